@@ -1,0 +1,48 @@
+"""Plain fp64 CPU oracle for paged decode attention.
+
+TEST INFRASTRUCTURE ONLY.  Only ``tests/``, ``__graft_entry__.smoke()`` and
+the ``cpu_baseline`` leg of ``bench.py`` may import, call or execute anything
+in this package.  The HIP library never links, imports or calls it, and it
+imports nothing from the HIP library: the two share no code.  The only module
+both consume is ``workloads`` (seeded input draws, no method arithmetic).
+
+Everything here is deliberately slow and obvious: numpy in float64, one
+sequence and one head at a time, no blocking, fusion or reordering beyond
+what the definitions state.  Stored f32/f16/bf16 inputs widen exactly to
+float64.
+
+Parity status of each function (what pins it is listed in the tests):
+
+* ``gather_rows``, ``decode``: pinned (dense-attention special case against
+  a library routine, pure-Python brute force, n = 1, constant keys,
+  permutation and shared-prefix invariance, write-then-read round trip).
+* ``ring_slot``, ``ring_cache_order``, ``ring_cache_index``: pinned (values
+  worked by hand from the sink + ring slot equation, brute-force last-writer
+  simulation).
+* ``rope_rotate_half``: pinned (complex-multiplication form, norm
+  preservation, relative-position invariance, identity at position 0).  The
+  pairing convention itself is a reading, not fixed by the pages.
+* ``reshape_and_cache``: pinned (write-then-gather round trip, untouched
+  rows keep their bytes).
+* ``BlockAllocatorModel``: pinned (lowest-free-id order, exhaustion, release
+  at the last reference, stats).
+* closed forms in ``sizes``: pinned against the numbers the pages print.
+"""
+from .paged_attention import (  # noqa: F401
+    to_f64,
+    gather_rows,
+    slot_of,
+    attention_one_group,
+    decode,
+    reshape_and_cache,
+    reshape_and_cache_,
+    build_pools,
+    ring_slot,
+    ring_cache_order,
+    ring_cache_index,
+    rope_inv_freq,
+    rope_rotate_half,
+    round_to_dtype,
+)
+from .allocator import BlockAllocatorModel  # noqa: F401
+from . import sizes  # noqa: F401

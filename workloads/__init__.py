@@ -1,0 +1,423 @@
+"""Seeded synthetic workloads for paged decode attention.
+
+This module only draws inputs: sequence lengths, physical block placement
+(block tables), query and key/value values, and the list of logical
+positions that each sequence writes into the cache.  It contains none of the
+method's arithmetic: no slot computation, no gather, no softmax, no RoPE.
+Both the CPU oracle (``oracle/``) and the HIP path consume what it returns,
+and each side computes slots, writes the cache and attends on its own.
+
+Value storage ("raw") conventions, shared by both sides as plain data:
+
+* ``f32``  -> numpy float32
+* ``f16``  -> numpy float16
+* ``bf16`` -> numpy uint16 holding the bfloat16 bit pattern (numpy has no
+  bfloat16); values are drawn in float32 and rounded to nearest-even.
+
+Every pool row that no write covers is NaN (f32 0x7FC00000, f16 0x7E00,
+bf16 0x7FC0), so any read outside a sequence's context poisons the result.
+Block-table entries past a sequence's last block point at a never-written
+(NaN) block, or hold -1 when ``pad_with_minus_one`` is set.
+
+Workload shapes follow the five configurations of the paged decode
+problem: a tiny fp32 case, one layer of a 1.1B embedded model
+(12 q heads / 2 KV heads, D 128, 16-token blocks, 680-block pool), a
+LLaMA-2-70B-shaped batch (64 q / 8 KV heads, bf16, mixed lengths 50..8000),
+a 32-sequence MHA batch sharing a 256-token prefix in 64-token blocks, and a
+sink + ring streaming cache (4 sink + 1020 ring slots, positions to 100k).
+"""
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass, field
+from typing import List, Optional
+
+import numpy as np
+
+SEED_BASE = 145_000
+
+RAW_DTYPES = {"f32": np.float32, "f16": np.float16, "bf16": np.uint16}
+ELEM_BYTES = {"f32": 4, "f16": 2, "bf16": 2}
+NAN_BITS = {"f32": 0x7FC00000, "f16": 0x7E00, "bf16": 0x7FC0}
+
+
+def round_f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """Round finite float32 values to bfloat16 (nearest-even); return bits."""
+    bits = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    bias = ((bits >> 16) & 1) + 0x7FFF
+    return ((bits + bias) >> 16).astype(np.uint16)
+
+
+def draw_values(rng: np.random.Generator, shape, dtype: str) -> np.ndarray:
+    """N(0, 1) draws in float32, stored in ``dtype``'s raw form."""
+    x = rng.standard_normal(shape, dtype=np.float32)
+    if dtype == "f32":
+        return x
+    if dtype == "f16":
+        return x.astype(np.float16)
+    if dtype == "bf16":
+        return round_f32_to_bf16_bits(x)
+    raise ValueError(f"unknown dtype {dtype!r}")
+
+
+def nan_array(shape, dtype: str) -> np.ndarray:
+    if dtype == "f32":
+        return np.full(shape, NAN_BITS["f32"], dtype=np.uint32).view(np.float32)
+    if dtype == "f16":
+        return np.full(shape, NAN_BITS["f16"], dtype=np.uint16).view(np.float16)
+    return np.full(shape, NAN_BITS["bf16"], dtype=np.uint16)
+
+
+@dataclass
+class RingSpec:
+    sink: int
+    window: int
+    rope_base: float = 10000.0
+
+
+@dataclass
+class WriteChunk:
+    """Logical positions of sequence ``seq`` and the K/V rows written there."""
+
+    seq: int
+    positions: np.ndarray  # int64 [m]
+    keys: np.ndarray  # raw [m, Hkv, D]
+    values: np.ndarray  # raw [m, Hkv, D]
+
+
+@dataclass
+class DecodeCase:
+    name: str
+    seed: int
+    dtype: str
+    num_blocks: int
+    block_size: int
+    num_kv_heads: int
+    num_q_heads: int
+    head_dim: int
+    scale: float
+    context_lens: np.ndarray  # int32 [B]
+    block_tables: np.ndarray  # int32 [B, max_blocks]
+    query: np.ndarray  # raw [B, Hq, D]
+    writes: List[WriteChunk]  # everything that fills the cache, in order
+    ring: Optional[RingSpec] = None
+    pad_block: int = -1  # block id used for table padding (-1: none)
+    notes: dict = field(default_factory=dict)
+
+    @property
+    def num_seqs(self) -> int:
+        return int(self.context_lens.shape[0])
+
+    @property
+    def max_blocks_per_seq(self) -> int:
+        return int(self.block_tables.shape[1])
+
+    def empty_pool(self) -> np.ndarray:
+        return nan_array(
+            (self.num_blocks, self.block_size, self.num_kv_heads, self.head_dim), self.dtype
+        )
+
+    def step_writes(self) -> List[WriteChunk]:
+        """The newest token of every sequence: what one decode step writes."""
+        out = []
+        last = {}
+        for ci, ch in enumerate(self.writes):
+            for j, p in enumerate(ch.positions):
+                last[ch.seq] = (ci, j, int(p))
+        for b in range(self.num_seqs):
+            n = int(self.context_lens[b])
+            if n == 0 or b not in last:
+                continue
+            ci, j, p = last[b]
+            ch = self.writes[ci]
+            out.append(
+                WriteChunk(b, np.array([p], dtype=np.int64), ch.keys[j : j + 1], ch.values[j : j + 1])
+            )
+        return out
+
+
+def _placement_tables(
+    rng: np.random.Generator,
+    blocks_per_seq: List[int],
+    num_blocks: int,
+    max_blocks: int,
+    pad_with_minus_one: bool,
+):
+    """Assign physical ids from one seeded permutation, in sequence order."""
+    perm = rng.permutation(num_blocks).astype(np.int32)
+    used = int(sum(blocks_per_seq))
+    if used > num_blocks:
+        raise ValueError("pool too small for placement")
+    spare = perm[used:]
+    pad = -1 if (pad_with_minus_one or spare.size == 0) else int(spare[0])
+    tables = np.full((len(blocks_per_seq), max_blocks), pad, dtype=np.int32)
+    cur = 0
+    for b, nb in enumerate(blocks_per_seq):
+        tables[b, :nb] = perm[cur : cur + nb]
+        cur += nb
+    return tables, pad
+
+
+def _ceil_div(a: int, b: int) -> int:
+    return -(-a // b)
+
+
+def _dense_writes(rng, lens, num_kv_heads, head_dim, dtype) -> List[WriteChunk]:
+    writes = []
+    for b, n in enumerate(lens):
+        n = int(n)
+        if n == 0:
+            continue
+        k = draw_values(rng, (n, num_kv_heads, head_dim), dtype)
+        v = draw_values(rng, (n, num_kv_heads, head_dim), dtype)
+        writes.append(WriteChunk(b, np.arange(n, dtype=np.int64), k, v))
+    return writes
+
+
+def make_paged_case(
+    name: str,
+    seed: int,
+    dtype: str,
+    lens,
+    num_q_heads: int,
+    num_kv_heads: int,
+    head_dim: int,
+    block_size: int,
+    num_blocks: Optional[int] = None,
+    pool_slack: float = 1.1,
+    max_blocks: Optional[int] = None,
+    pad_with_minus_one: bool = False,
+) -> DecodeCase:
+    """A generic plain-paging case: shuffled placement, N(0,1) values."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    lens = np.asarray(lens, dtype=np.int32)
+    bps = [_ceil_div(int(n), block_size) for n in lens]
+    need = int(sum(bps))
+    if num_blocks is None:
+        num_blocks = max(1, math.ceil(pool_slack * need))
+    if max_blocks is None:
+        max_blocks = max(1, max(bps) if bps else 1)
+    tables, pad = _placement_tables(rng, bps, num_blocks, max_blocks, pad_with_minus_one)
+    query = draw_values(rng, (len(lens), num_q_heads, head_dim), dtype)
+    writes = _dense_writes(rng, lens, num_kv_heads, head_dim, dtype)
+    return DecodeCase(
+        name=name, seed=seed, dtype=dtype, num_blocks=num_blocks, block_size=block_size,
+        num_kv_heads=num_kv_heads, num_q_heads=num_q_heads, head_dim=head_dim,
+        scale=1.0 / math.sqrt(head_dim), context_lens=lens, block_tables=tables,
+        query=query, writes=writes, pad_block=pad,
+    )
+
+
+# ---------------------------------------------------------------------------
+# The five workload configurations
+# ---------------------------------------------------------------------------
+
+def config_tiny_fp32(pad_with_minus_one: bool = False) -> DecodeCase:
+    """B 2, lengths {37, 70}, Hq 4, Hkv 2, D 64, fp32, 16-token blocks, 16-block pool."""
+    seed = SEED_BASE + 1
+    rng = np.random.Generator(np.random.PCG64(seed))
+    lens = np.array([37, 70], dtype=np.int32)
+    bs, nblk = 16, 16
+    tables, pad = _placement_tables(rng, [3, 5], nblk, 5, pad_with_minus_one)
+    query = draw_values(rng, (2, 4, 64), "f32")
+    writes = _dense_writes(rng, lens, 2, 64, "f32")
+    return DecodeCase(
+        name="tiny_fp32", seed=seed, dtype="f32", num_blocks=nblk, block_size=bs,
+        num_kv_heads=2, num_q_heads=4, head_dim=64, scale=1.0 / 8.0,
+        context_lens=lens, block_tables=tables, query=query, writes=writes, pad_block=pad,
+    )
+
+
+def config_embedded_1p1b(pad_with_minus_one: bool = False) -> DecodeCase:
+    """One layer of the 1.1B embedded shape: Hq 12, Hkv 2, D 128, fp16, bs 16, 680 blocks, B 8.
+
+    Lengths are uniform in [16, 2048] and redrawn (same seeded stream) until
+    the batch fits the 680-block pool.
+    """
+    seed = SEED_BASE + 2
+    rng = np.random.Generator(np.random.PCG64(seed))
+    bs, nblk = 16, 680
+    redraws = 0
+    while True:
+        lens = rng.integers(16, 2048, size=8, endpoint=True).astype(np.int32)
+        bps = [_ceil_div(int(n), bs) for n in lens]
+        if sum(bps) <= nblk:
+            break
+        redraws += 1
+    tables, pad = _placement_tables(rng, bps, nblk, max(bps), pad_with_minus_one)
+    query = draw_values(rng, (8, 12, 128), "f16")
+    writes = _dense_writes(rng, lens, 2, 128, "f16")
+    case = DecodeCase(
+        name="embedded_1p1b", seed=seed, dtype="f16", num_blocks=nblk, block_size=bs,
+        num_kv_heads=2, num_q_heads=12, head_dim=128, scale=1.0 / math.sqrt(128),
+        context_lens=lens, block_tables=tables, query=query, writes=writes, pad_block=pad,
+    )
+    case.notes["length_redraws"] = redraws
+    return case
+
+
+def llama70b_lengths(rng: np.random.Generator, batch: int = 64) -> np.ndarray:
+    """Mixed decode lengths: 50% U[50,500], 30% U[500,2000], 20% U[2000,8000].
+
+    The mixture is taken as fixed counts (32/19/13 of 64, rounded so they sum
+    to the batch), each length an inclusive integer draw, then shuffled.
+    """
+    n_short = int(round(0.5 * batch))
+    n_mid = int(round(0.3 * batch))
+    n_long = batch - n_short - n_mid
+    lens = np.concatenate([
+        rng.integers(50, 500, size=n_short, endpoint=True),
+        rng.integers(500, 2000, size=n_mid, endpoint=True),
+        rng.integers(2000, 8000, size=n_long, endpoint=True),
+    ]).astype(np.int32)
+    rng.shuffle(lens)
+    return lens
+
+
+def config_llama70b(pad_with_minus_one: bool = False, batch: int = 64) -> DecodeCase:
+    """LLaMA-2-70B-shaped decode on one GPU: Hq 64, Hkv 8, D 128, bf16, bs 16, B 64."""
+    seed = SEED_BASE + 3
+    rng = np.random.Generator(np.random.PCG64(seed))
+    lens = llama70b_lengths(rng, batch)
+    bs = 16
+    bps = [_ceil_div(int(n), bs) for n in lens]
+    need = int(sum(bps))
+    nblk = math.ceil(1.1 * need)
+    tables, pad = _placement_tables(rng, bps, nblk, max(bps), pad_with_minus_one)
+    query = draw_values(rng, (batch, 64, 128), "bf16")
+    writes = _dense_writes(rng, lens, 8, 128, "bf16")
+    return DecodeCase(
+        name="llama70b_b64", seed=seed, dtype="bf16", num_blocks=nblk, block_size=bs,
+        num_kv_heads=8, num_q_heads=64, head_dim=128, scale=1.0 / math.sqrt(128),
+        context_lens=lens, block_tables=tables, query=query, writes=writes, pad_block=pad,
+    )
+
+
+def config_shared_prefix(private_copies: bool = False, pad_with_minus_one: bool = False,
+                         batch: int = 32, prefix_tokens: int = 256) -> DecodeCase:
+    """MHA (Hq = Hkv = 32), D 128, fp16, bs 64; B sequences share a 256-token prefix.
+
+    With ``private_copies`` the same logical content is laid out with a
+    private copy of the prefix blocks per sequence (the twin layout); values,
+    lengths and queries are identical between the two layouts.
+    """
+    seed = SEED_BASE + 4
+    rng = np.random.Generator(np.random.PCG64(seed))
+    bs, hkv, d = 64, 32, 128
+    pblk = prefix_tokens // bs
+    suffix = rng.integers(16, 1024, size=batch, endpoint=True).astype(np.int32)
+    lens = (prefix_tokens + suffix).astype(np.int32)
+    sblk = [_ceil_div(int(s), bs) for s in suffix]
+    shared_need = pblk + int(sum(sblk))
+    private_need = pblk * batch + int(sum(sblk))
+    perm_shared = rng.permutation(math.ceil(1.1 * shared_need)).astype(np.int32)
+    perm_private = rng.permutation(math.ceil(1.1 * private_need)).astype(np.int32)
+    query = draw_values(rng, (batch, hkv, d), "f16")
+    prefix_k = draw_values(rng, (prefix_tokens, hkv, d), "f16")
+    prefix_v = draw_values(rng, (prefix_tokens, hkv, d), "f16")
+    suf = []
+    for b in range(batch):
+        s = int(suffix[b])
+        suf.append((draw_values(rng, (s, hkv, d), "f16"), draw_values(rng, (s, hkv, d), "f16")))
+    max_blocks = pblk + max(sblk)
+    perm = perm_private if private_copies else perm_shared
+    nblk = perm.size
+    used = private_need if private_copies else shared_need
+    spare = perm[used:]
+    pad = -1 if (pad_with_minus_one or spare.size == 0) else int(spare[0])
+    tables = np.full((batch, max_blocks), pad, dtype=np.int32)
+    cur = 0
+    if not private_copies:
+        prefix_ids = perm[:pblk]
+        cur = pblk
+    writes: List[WriteChunk] = []
+    for b in range(batch):
+        if private_copies:
+            tables[b, :pblk] = perm[cur : cur + pblk]
+            cur += pblk
+            writes.append(WriteChunk(b, np.arange(prefix_tokens, dtype=np.int64), prefix_k, prefix_v))
+        else:
+            tables[b, :pblk] = prefix_ids
+            if b == 0:
+                writes.append(WriteChunk(0, np.arange(prefix_tokens, dtype=np.int64), prefix_k, prefix_v))
+        tables[b, pblk : pblk + sblk[b]] = perm[cur : cur + sblk[b]]
+        cur += sblk[b]
+        k, v = suf[b]
+        writes.append(WriteChunk(b, np.arange(prefix_tokens, int(lens[b]), dtype=np.int64), k, v))
+    case = DecodeCase(
+        name="shared_prefix_private" if private_copies else "shared_prefix",
+        seed=seed, dtype="f16", num_blocks=nblk, block_size=bs, num_kv_heads=hkv,
+        num_q_heads=hkv, head_dim=d, scale=1.0 / math.sqrt(d), context_lens=lens,
+        block_tables=tables, query=query, writes=writes, pad_block=pad,
+    )
+    case.notes["prefix_blocks"] = pblk
+    case.notes["shared_prefix_ids"] = None if private_copies else [int(x) for x in perm[:pblk]]
+    return case
+
+
+RING_PARITY_LENGTHS = [1, 3, 4, 5, 17, 1000, 1023, 1024, 1025, 1026, 2044, 2045, 4096,
+                       50_000, 99_999, 100_000]
+
+
+def ring_survivor_positions(n: int, sink: int, window: int) -> np.ndarray:
+    """Logical positions still resident in a sink + ring cache after n appends.
+
+    This is the cache's retention policy (the first ``sink`` positions stay,
+    plus the newest ``window``), not its slot arithmetic.
+    """
+    if n <= sink + window:
+        return np.arange(n, dtype=np.int64)
+    return np.concatenate([np.arange(sink), np.arange(n - window, n)]).astype(np.int64)
+
+
+def config_sink_ring(lengths=None, seed_offset: int = 5, pad_with_minus_one: bool = False,
+                     sink: int = 4, window: int = 1020, block_size: int = 16,
+                     num_q_heads: int = 12, num_kv_heads: int = 2, head_dim: int = 128) -> DecodeCase:
+    """Sink + ring streaming cache: S 4 + W 1020 slots, bs 16, fp16, Hq 12, Hkv 2, D 128.
+
+    The K/V of logical position p of stream b are drawn from
+    ``default_rng([seed, b, p])`` so any survivor can be regenerated alone.
+    Only survivors are written (with distinct slots).  ``lengths`` defaults to
+    the 16 parity positions; the timing set is ``100_000 - 61 * b``.
+    """
+    seed = SEED_BASE + seed_offset
+    if lengths is None:
+        lengths = RING_PARITY_LENGTHS
+    lens = np.asarray(lengths, dtype=np.int64)
+    batch = lens.size
+    cap = sink + window
+    bps_cap = _ceil_div(cap, block_size)
+    rng = np.random.Generator(np.random.PCG64(seed))
+    nblk = math.ceil(1.1 * bps_cap * batch)
+    tables, pad = _placement_tables(rng, [bps_cap] * batch, nblk, bps_cap, pad_with_minus_one)
+    query = draw_values(rng, (batch, num_q_heads, head_dim), "f16")
+    writes = []
+    for b in range(batch):
+        pos = ring_survivor_positions(int(lens[b]), sink, window)
+        ks = np.empty((pos.size, num_kv_heads, head_dim), dtype=np.float16)
+        vs = np.empty_like(ks)
+        for i, p in enumerate(pos):
+            r = np.random.default_rng([seed, b, int(p)])
+            ks[i] = draw_values(r, (num_kv_heads, head_dim), "f16")
+            vs[i] = draw_values(r, (num_kv_heads, head_dim), "f16")
+        writes.append(WriteChunk(b, pos, ks, vs))
+    return DecodeCase(
+        name="sink_ring", seed=seed, dtype="f16", num_blocks=nblk, block_size=block_size,
+        num_kv_heads=num_kv_heads, num_q_heads=num_q_heads, head_dim=head_dim,
+        scale=1.0 / math.sqrt(head_dim), context_lens=lens.astype(np.int32),
+        block_tables=tables, query=query, writes=writes,
+        ring=RingSpec(sink, window, 10000.0), pad_block=pad,
+    )
+
+
+def ring_timing_lengths(batch: int = 16) -> List[int]:
+    return [100_000 - 61 * b for b in range(batch)]
+
+
+CONFIGS = {
+    "tiny_fp32": config_tiny_fp32,
+    "embedded_1p1b": config_embedded_1p1b,
+    "llama70b_b64": config_llama70b,
+    "shared_prefix": config_shared_prefix,
+    "sink_ring": config_sink_ring,
+}
