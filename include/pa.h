@@ -1,0 +1,211 @@
+/*
+ * pa.h -- C ABI of the MI355X (gfx950) paged decode-attention library.
+ *
+ * One hot path: single-token decode attention over a paged KV cache, plus
+ * its write side.  Every sequence's keys and values live in fixed-size
+ * physical blocks of one shared pool per layer and are reached only through
+ * that sequence's block table.
+ *
+ * Sources (web pages, cited by title and section):
+ *   [P1] "端侧 SLM 显存保活术：在 4GB 内存板卡上实现轻量 PagedAttention 与 KV 缓存分块"
+ *        (sheratonhq.com/news/141880): sections "嵌入式轻量 Block 分配器设计"
+ *        (pool of fixed-size blocks, free bitmap, lowest free id first, -1 when
+ *        exhausted), "注意力寻址：非连续物理块的间接寻址" (logical token ->
+ *        logical block and offset -> physical block via the block table) and
+ *        "共享前缀块" (several block tables point at the same resident prefix
+ *        blocks).
+ *   [P2] "Ollama的内存管理策略：从KV Cache Block分配到Prefix-aware内存复用的演进"
+ *        (xdnf.cn/news/5086), section "三、KV Cache内存管理的工程实现":
+ *        per-block reference counts, release at the last reference, pool
+ *        statistics (total / used / shared / free).
+ *   [P3] wzjinhao.cn/news/69573 (deferred speculative decoding with a
+ *        circular context), section "环形上下文与注意力沉淀机制": the sink +
+ *        ring slot equation; section "C++ 环形 KV 缓存管理内核实现": resident
+ *        keys in cache order (sinks, then the window oldest first).
+ *   [P4] "大模型推理内存优化：从 KV Cache 分页到连续批处理的工程实践"
+ *        (pwwt.cn/news/3010209), section "KV Cache 的内存开销与分页机制":
+ *        blocks of usually 16 tokens, one block table per request, a new
+ *        block when the last one fills, block sharing, and the decode kernel
+ *        reading K/V indirectly through the block table.
+ *
+ * Conventions
+ *   - Every int-returning call returns a pa_status (0 = PA_OK, < 0 = error)
+ *     unless noted otherwise.  pa_status_str() names a status.
+ *   - "device" pointers are HIP device memory owned by the caller (for
+ *     example PyTorch tensors); "host" pointers are ordinary host memory.
+ *     Device tensors are contiguous, row-major, 16-byte aligned.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *     Device work is enqueued asynchronously on it; no call synchronises,
+ *     so a fault caused by bad device-resident data (block ids, lengths,
+ *     slots) surfaces at the caller's next synchronisation.
+ *   - Device-resident contents (block ids in block tables, context lengths,
+ *     slots) are a caller contract and are not validated in the fast path.
+ *   - Host-side allocator calls are thread-safe (internal mutex).  Decode and
+ *     cache writes are re-entrant across streams; concurrent writes to the
+ *     same slot have unspecified results.
+ */
+#ifndef PA_H_
+#define PA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  PA_OK = 0,
+  PA_ERR_INVAL = -1,       /* invalid argument (shape, pointer, alignment, size) */
+  PA_ERR_NOMEM = -2,       /* host allocation failed / workspace too small */
+  PA_ERR_STATE = -3,       /* refcount misuse: the block is free */
+  PA_ERR_HIP = -4,         /* a HIP runtime call or kernel launch failed */
+  PA_ERR_UNSUPPORTED = -5  /* a combination the library has no kernel for */
+} pa_status;
+
+typedef enum { PA_F32 = 0, PA_F16 = 1, PA_BF16 = 2 } pa_dtype;
+
+/* Opaque pool handle: host-side state only (shapes, free list, refcounts). */
+typedef struct pa_pool pa_pool;
+
+typedef struct {
+  int32_t total;  /* blocks in the pool */
+  int32_t used;   /* blocks with refcount >= 1 */
+  int32_t shared; /* blocks with refcount >= 2 */
+  int32_t free;   /* total - used */
+} pa_pool_stats;
+
+/* Sink + ring mode [P3].  A stream of logical positions maps into
+ * sink + window ring slots; slot r of the ring is then addressed through the
+ * block table exactly like logical token r of a plain sequence.  Keys are
+ * stored un-rotated; decode rotates (rotate-half pairing: (x_i, x_{i+D/2}))
+ * the key at cache index j by j * theta_i and the query by (L - 1) * theta_i,
+ * theta_i = rope_base^(-2i/D), L = min(context_len, sink + window).
+ * `rope_table` is a device buffer of pa_rope_table_bytes() bytes filled by
+ * pa_rope_table_init() for the same (sink + window, head_dim, rope_base). */
+typedef struct {
+  int32_t sink;            /* S >= 0 */
+  int32_t window;          /* W >= 1 */
+  float rope_base;         /* e.g. 10000 */
+  int32_t rope_style;      /* 0 = rotate-half (the only style implemented) */
+  const float *rope_table; /* device, float2 (cos, sin) [S + W][D / 2] */
+} pa_ring;
+
+/* ---------------------------------------------------------------- pool --- */
+
+/* Describe one layer's K and V pools, each [num_blocks, block_size,
+ * num_kv_heads, head_dim] of `dtype`, in caller-owned device memory
+ * (k_cache, v_cache), and create the host-side allocator over its block ids
+ * [P1 allocator; P4].  block_size in {16, 64}; head_dim in {64, 128}.
+ * The handle never frees k_cache / v_cache.  *out is set on success. */
+int pa_create_pool(pa_pool **out, int32_t num_blocks, int32_t block_size, int32_t num_kv_heads,
+                   int32_t head_dim, pa_dtype dtype, void *k_cache, void *v_cache);
+
+/* Free the host-side state (NULL is a no-op).  Device memory is untouched. */
+void pa_destroy_pool(pa_pool *pool);
+
+/* Take the lowest free block id and set its refcount to 1 [P1 allocator].
+ * Returns the id, or -1 when the pool is exhausted or pool is NULL. */
+int32_t pa_alloc_block(pa_pool *pool);
+
+/* Add a reference to an allocated block (prefix sharing [P1 prefix; P2]).
+ * PA_ERR_INVAL for an id outside the pool, PA_ERR_STATE for a free block. */
+int pa_incref_block(pa_pool *pool, int32_t block_id);
+
+/* Drop a reference; at zero the block returns to the free set [P2].
+ * PA_ERR_INVAL for an id outside the pool, PA_ERR_STATE for a free block
+ * (double release). */
+int pa_decref_block(pa_pool *pool, int32_t block_id);
+
+/* Current reference count of a block (0 = free), or -1 for a bad id. */
+int32_t pa_get_refcount(const pa_pool *pool, int32_t block_id);
+
+/* Pool statistics [P2]. */
+int pa_get_stats(const pa_pool *pool, pa_pool_stats *out);
+
+/* ------------------------------------------------------------- mapping --- */
+
+/* Ring slot of a logical position [P3 slot equation]:
+ * pos if pos < sink, else sink + ((pos - sink) mod window).
+ * Returns -1 for pos < 0, sink < 0 or window < 1. */
+int32_t pa_ring_slot(int64_t pos, int32_t sink, int32_t window);
+
+/* Host: flat pool slots for (sequence, logical position) pairs [P1
+ * addressing; P4 paging]:  r = position (plain) or pa_ring_slot(position)
+ * (ring != NULL);  slot = block_tables[seq][r / block_size] * block_size +
+ * r % block_size.  block_tables is host int32 [num_seqs][max_blocks_per_seq];
+ * seq_ids host int32 [n]; positions host int64 [n]; out host int32 [n].
+ * PA_ERR_INVAL if an entry is out of range or the table holds a negative or
+ * out-of-pool id where a block is needed. */
+int pa_compute_slot_mapping(const pa_pool *pool, const int32_t *block_tables, int32_t num_seqs,
+                            int32_t max_blocks_per_seq, const int32_t *seq_ids,
+                            const int64_t *positions, int32_t n, const pa_ring *ring,
+                            int32_t *out);
+
+/* --------------------------------------------------------- write side --- */
+
+/* Device: copy token i's key and value rows ([num_kv_heads, head_dim] each,
+ * pool dtype, no conversion) into flat pool slot slot_mapping[i]
+ * (block = slot / block_size, row = slot % block_size).  key, value: device
+ * [num_tokens, num_kv_heads, head_dim]; slot_mapping: device int32
+ * [num_tokens]; a negative slot is padding and is skipped, and so is a slot
+ * at or beyond num_blocks * block_size.  Slots must be distinct (caller
+ * contract).  num_tokens == 0 is a no-op. */
+int pa_reshape_and_cache(pa_pool *pool, const void *key, const void *value,
+                         const int32_t *slot_mapping, int32_t num_tokens, void *stream);
+
+/* ------------------------------------------------------------- decode --- */
+
+/* Bytes of device workspace pa_decode needs for this batch shape (split-K
+ * partials).  ring may be NULL.  Returns 0 on invalid arguments. */
+size_t pa_decode_workspace_bytes(const pa_pool *pool, int32_t num_seqs, int32_t num_q_heads,
+                                 int32_t max_context_len, const pa_ring *ring);
+
+/* Bytes of the RoPE table for `capacity` = sink + window cached keys. */
+size_t pa_rope_table_bytes(int32_t capacity, int32_t head_dim);
+
+/* Device: fill table (float2 [capacity][head_dim / 2]) with
+ * (cos, sin)(j * rope_base^(-2i/head_dim)), computed in double precision and
+ * rounded to float. */
+int pa_rope_table_init(float *table, int32_t capacity, int32_t head_dim, float rope_base,
+                       void *stream);
+
+/* Device: single-token decode attention over the paged cache [P4 paging;
+ * P1 addressing; P3 ring].  For sequence b and query head h (KV head
+ * g = h / (num_q_heads / num_kv_heads)):
+ *   out[b,h,:] = sum_t softmax_t(scale * <q[b,h,:], K_t[g,:]>) * V_t[g,:]
+ * over the first context_lens[b] logical tokens (plain) or the resident ring
+ * keys (ring != NULL), each read through block_tables[b].
+ *   out:          device [num_seqs, num_q_heads, head_dim], query dtype
+ *                 (= pool dtype), rounded to nearest-even from fp32.
+ *   query:        device [num_seqs, num_q_heads, head_dim], pool dtype.
+ *   block_tables: device int32 [num_seqs, max_blocks_per_seq].
+ *   context_lens: device int32 [num_seqs]; 0 gives an all-zero output row.
+ *   max_context_len: host upper bound of context_lens (sizes the split-K
+ *                 grid); plain mode needs max_context_len <=
+ *                 max_blocks_per_seq * block_size.  Device lengths are
+ *                 clamped to [0, max_context_len]; block ids outside the
+ *                 pool are clamped into it (no fault; unspecified result).
+ *   workspace:    device, >= pa_decode_workspace_bytes(...) bytes, 256-byte
+ *                 aligned; its contents need no initialisation.  Concurrent
+ *                 calls need distinct workspaces.
+ * num_q_heads must be a multiple of the pool's num_kv_heads.  The reduction
+ * order depends only on logical positions and lengths, so the result is
+ * bit-identical under any relabelling of physical blocks and for shared
+ * versus private copies of the same blocks. */
+int pa_decode(pa_pool *pool, void *out, const void *query, const int32_t *block_tables,
+              int32_t max_blocks_per_seq, const int32_t *context_lens, int32_t num_seqs,
+              int32_t num_q_heads, int32_t max_context_len, float scale, const pa_ring *ring,
+              void *workspace, size_t workspace_bytes, void *stream);
+
+/* Name of a status code (static string). */
+const char *pa_status_str(int status);
+
+/* Text of the last HIP error seen by this thread in a pa_* call ("" if none). */
+const char *pa_last_hip_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PA_H_ */

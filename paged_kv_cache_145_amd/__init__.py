@@ -1,0 +1,197 @@
+"""Paged decode attention for AMD Instinct MI355X (gfx950).
+
+A thin Python binding over the C ABI of ``libpa_mi355x.so`` (declared in
+``include/pa.h``).  Functions here only marshal arguments: torch tensors are
+passed as raw device pointers with torch's current HIP stream; every step of
+the path runs in the library's HIP kernels or its host C++ allocator.
+"""
+from __future__ import annotations
+
+import ctypes
+from typing import Optional
+
+import numpy as np
+
+from . import _lib
+from ._lib import PaRing
+
+__all__ = [
+    "PaError", "Pool", "Ring", "ring_slot", "compute_slot_mapping", "reshape_and_cache",
+    "decode_workspace_bytes", "rope_table_bytes", "rope_table_init", "decode", "DTYPES",
+]
+
+DTYPES = {"f32": _lib.PA_F32, "f16": _lib.PA_F16, "bf16": _lib.PA_BF16}
+
+
+class PaError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        lib = _lib.load()
+        name = lib.pa_status_str(status).decode()
+        detail = lib.pa_last_hip_error().decode() if status == _lib.PA_ERR_HIP else ""
+        super().__init__(f"{what}: {name}" + (f" ({detail})" if detail else ""))
+        self.status = status
+
+
+def _check(status: int, what: str) -> None:
+    if status != _lib.PA_OK:
+        raise PaError(status, what)
+
+
+def _torch_dtype_name(t) -> str:
+    import torch
+
+    return {torch.float32: "f32", torch.float16: "f16", torch.bfloat16: "bf16"}[t.dtype]
+
+
+def _stream_ptr(stream) -> Optional[int]:
+    import torch
+
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _dev_ptr(t, name: str) -> ctypes.c_void_p:
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+class Ring:
+    """Sink + ring configuration with its device RoPE table."""
+
+    def __init__(self, sink: int, window: int, rope_base: float, rope_table):
+        self.sink, self.window, self.rope_base, self.rope_table = sink, window, rope_base, rope_table
+
+    def as_struct(self) -> PaRing:
+        ptr = self.rope_table.data_ptr() if self.rope_table is not None else None
+        return PaRing(self.sink, self.window, self.rope_base, 0, ptr)
+
+
+def _ring_ptr(ring: Optional[Ring]):
+    if ring is None:
+        return None
+    return ctypes.byref(ring.as_struct())
+
+
+class Pool:
+    """One layer's paged K/V pools (caller-owned device tensors) + allocator."""
+
+    def __init__(self, k_cache, v_cache, block_size: int):
+        lib = _lib.load()
+        if k_cache.shape != v_cache.shape or k_cache.dtype != v_cache.dtype or k_cache.dim() != 4:
+            raise ValueError("k_cache and v_cache must both be [num_blocks, block_size, Hkv, D]")
+        num_blocks, bs, hkv, d = k_cache.shape
+        if bs != block_size:
+            raise ValueError("block_size does not match the pool shape")
+        self.dtype = _torch_dtype_name(k_cache)
+        self.k_cache, self.v_cache = k_cache, v_cache
+        self.num_blocks, self.block_size, self.num_kv_heads, self.head_dim = num_blocks, bs, hkv, d
+        handle = ctypes.c_void_p()
+        _check(lib.pa_create_pool(ctypes.byref(handle), num_blocks, bs, hkv, d, DTYPES[self.dtype],
+                                  _dev_ptr(k_cache, "k_cache"), _dev_ptr(v_cache, "v_cache")),
+               "pa_create_pool")
+        self._h = handle
+        self._lib = lib
+
+    @property
+    def handle(self):
+        return self._h
+
+    def close(self) -> None:
+        if self._h:
+            self._lib.pa_destroy_pool(self._h)
+            self._h = ctypes.c_void_p()
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def alloc_block(self) -> int:
+        return self._lib.pa_alloc_block(self._h)
+
+    def incref(self, block_id: int) -> None:
+        _check(self._lib.pa_incref_block(self._h, block_id), "pa_incref_block")
+
+    def decref(self, block_id: int) -> None:
+        _check(self._lib.pa_decref_block(self._h, block_id), "pa_decref_block")
+
+    def refcount(self, block_id: int) -> int:
+        return self._lib.pa_get_refcount(self._h, block_id)
+
+    def stats(self) -> dict:
+        s = _lib.PaPoolStats()
+        _check(self._lib.pa_get_stats(self._h, ctypes.byref(s)), "pa_get_stats")
+        return {"total": s.total, "used": s.used, "shared": s.shared, "free": s.free}
+
+
+def ring_slot(pos: int, sink: int, window: int) -> int:
+    return _lib.load().pa_ring_slot(pos, sink, window)
+
+
+def compute_slot_mapping(pool: Pool, block_tables: np.ndarray, seq_ids, positions,
+                         ring: Optional[Ring] = None) -> np.ndarray:
+    """Host slot computation (int32 [n]) through the host copy of the tables."""
+    bt = np.ascontiguousarray(block_tables, dtype=np.int32)
+    sid = np.ascontiguousarray(seq_ids, dtype=np.int32)
+    pos = np.ascontiguousarray(positions, dtype=np.int64)
+    out = np.empty(sid.shape[0], dtype=np.int32)
+    _check(_lib.load().pa_compute_slot_mapping(
+        pool.handle, bt.ctypes.data_as(ctypes.c_void_p), bt.shape[0], bt.shape[1],
+        sid.ctypes.data_as(ctypes.c_void_p), pos.ctypes.data_as(ctypes.c_void_p), sid.shape[0],
+        _ring_ptr(ring), out.ctypes.data_as(ctypes.c_void_p)), "pa_compute_slot_mapping")
+    return out
+
+
+def reshape_and_cache(pool: Pool, key, value, slot_mapping, stream=None) -> None:
+    """Device scatter of key/value [N, Hkv, D] into the pool at slot_mapping [N] (int32)."""
+    n = int(slot_mapping.shape[0])
+    if n == 0:
+        return
+    if key.dtype != pool.k_cache.dtype or value.dtype != pool.k_cache.dtype:
+        raise ValueError("key/value dtype must match the pool")
+    if tuple(key.shape) != (n, pool.num_kv_heads, pool.head_dim) or key.shape != value.shape:
+        raise ValueError("key/value must be [N, Hkv, D]")
+    _check(_lib.load().pa_reshape_and_cache(
+        pool.handle, _dev_ptr(key, "key"), _dev_ptr(value, "value"),
+        _dev_ptr(slot_mapping, "slot_mapping"), n, _stream_ptr(stream)), "pa_reshape_and_cache")
+
+
+def decode_workspace_bytes(pool: Pool, num_seqs: int, num_q_heads: int, max_context_len: int,
+                           ring: Optional[Ring] = None) -> int:
+    return int(_lib.load().pa_decode_workspace_bytes(pool.handle, num_seqs, num_q_heads,
+                                                     max_context_len, _ring_ptr(ring)))
+
+
+def rope_table_bytes(capacity: int, head_dim: int) -> int:
+    return int(_lib.load().pa_rope_table_bytes(capacity, head_dim))
+
+
+def rope_table_init(table, capacity: int, head_dim: int, rope_base: float, stream=None) -> None:
+    if table.numel() * table.element_size() < rope_table_bytes(capacity, head_dim):
+        raise ValueError("rope table buffer too small")
+    _check(_lib.load().pa_rope_table_init(_dev_ptr(table, "rope_table"), capacity, head_dim,
+                                          rope_base, _stream_ptr(stream)), "pa_rope_table_init")
+
+
+def decode(pool: Pool, out, query, block_tables, context_lens, max_context_len: int,
+           scale: float, ring: Optional[Ring] = None, workspace=None, stream=None) -> None:
+    """Paged decode attention into ``out`` [B, Hq, D] (device tensors, async)."""
+    b, hq, d = query.shape
+    if tuple(out.shape) != (b, hq, d) or d != pool.head_dim:
+        raise ValueError("out/query must be [B, Hq, D] with D = the pool's head size")
+    if query.dtype != pool.k_cache.dtype or out.dtype != pool.k_cache.dtype:
+        raise ValueError("query/out dtype must match the pool")
+    ws_ptr, ws_bytes = None, 0
+    if workspace is not None:
+        ws_ptr = _dev_ptr(workspace, "workspace")
+        ws_bytes = workspace.numel() * workspace.element_size()
+    _check(_lib.load().pa_decode(
+        pool.handle, _dev_ptr(out, "out"), _dev_ptr(query, "query"),
+        _dev_ptr(block_tables, "block_tables"), int(block_tables.shape[1]),
+        _dev_ptr(context_lens, "context_lens"), b, hq, int(max_context_len), float(scale),
+        _ring_ptr(ring), ws_ptr, ws_bytes, _stream_ptr(stream)), "pa_decode")

@@ -1,0 +1,80 @@
+"""ctypes declarations of the C ABI in ``include/pa.h`` (libpa_mi355x.so).
+
+Loading fails loudly when the shared library has not been built: there is
+no fallback implementation.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+LIB_NAME = "libpa_mi355x.so"
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), LIB_NAME)
+
+PA_OK = 0
+PA_ERR_INVAL = -1
+PA_ERR_NOMEM = -2
+PA_ERR_STATE = -3
+PA_ERR_HIP = -4
+PA_ERR_UNSUPPORTED = -5
+
+PA_F32, PA_F16, PA_BF16 = 0, 1, 2
+
+
+class PaPoolStats(ctypes.Structure):
+    _fields_ = [("total", ctypes.c_int32), ("used", ctypes.c_int32),
+                ("shared", ctypes.c_int32), ("free", ctypes.c_int32)]
+
+
+class PaRing(ctypes.Structure):
+    _fields_ = [("sink", ctypes.c_int32), ("window", ctypes.c_int32),
+                ("rope_base", ctypes.c_float), ("rope_style", ctypes.c_int32),
+                ("rope_table", ctypes.c_void_p)]
+
+
+_p = ctypes.c_void_p
+_i32 = ctypes.c_int32
+_i64 = ctypes.c_int64
+_sz = ctypes.c_size_t
+
+# name -> (restype, argtypes); every symbol include/pa.h declares
+SIGNATURES = {
+    "pa_create_pool": (ctypes.c_int, [ctypes.POINTER(_p), _i32, _i32, _i32, _i32, ctypes.c_int, _p, _p]),
+    "pa_destroy_pool": (None, [_p]),
+    "pa_alloc_block": (_i32, [_p]),
+    "pa_incref_block": (ctypes.c_int, [_p, _i32]),
+    "pa_decref_block": (ctypes.c_int, [_p, _i32]),
+    "pa_get_refcount": (_i32, [_p, _i32]),
+    "pa_get_stats": (ctypes.c_int, [_p, ctypes.POINTER(PaPoolStats)]),
+    "pa_ring_slot": (_i32, [_i64, _i32, _i32]),
+    "pa_compute_slot_mapping": (ctypes.c_int, [_p, _p, _i32, _i32, _p, _p, _i32,
+                                               ctypes.POINTER(PaRing), _p]),
+    "pa_reshape_and_cache": (ctypes.c_int, [_p, _p, _p, _p, _i32, _p]),
+    "pa_decode_workspace_bytes": (_sz, [_p, _i32, _i32, _i32, ctypes.POINTER(PaRing)]),
+    "pa_rope_table_bytes": (_sz, [_i32, _i32]),
+    "pa_rope_table_init": (ctypes.c_int, [_p, _i32, _i32, ctypes.c_float, _p]),
+    "pa_decode": (ctypes.c_int, [_p, _p, _p, _p, _i32, _p, _i32, _i32, _i32, ctypes.c_float,
+                                 ctypes.POINTER(PaRing), _p, _sz, _p]),
+    "pa_status_str": (ctypes.c_char_p, [ctypes.c_int]),
+    "pa_last_hip_error": (ctypes.c_char_p, []),
+}
+
+_LIB = None
+
+
+def load() -> ctypes.CDLL:
+    """Load libpa_mi355x.so (raises if it is missing)."""
+    global _LIB
+    if _LIB is not None:
+        return _LIB
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(
+            f"{LIB_NAME} is not built at {LIB_PATH}; build it with "
+            "`python -c 'import __graft_entry__ as g; g.build()'` (no fallback exists)")
+    lib = ctypes.CDLL(LIB_PATH)
+    for name, (res, args) in SIGNATURES.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    _LIB = lib
+    return lib

@@ -1,0 +1,191 @@
+// C ABI entry points that enqueue device work: argument validation, kernel
+// choice, split-K sizing and launch.  The allocator entry points live in
+// pool.cpp.
+#include <cstdlib>
+#include <cstring>
+#include <string>
+
+#include "launch.h"
+#include "pool_internal.h"
+
+namespace pa {
+namespace {
+
+thread_local std::string g_last_hip_error;
+
+int hip_status(hipError_t err) {
+  if (err == hipSuccess) return PA_OK;
+  g_last_hip_error = hipGetErrorString(err);
+  return PA_ERR_HIP;
+}
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int env_int(const char *name, int fallback) {
+  const char *v = std::getenv(name);
+  if (v == nullptr || *v == '\0') return fallback;
+  return std::atoi(v);
+}
+
+int log2_exact(int v) {
+  int s = 0;
+  while ((1 << s) < v) ++s;
+  return s;
+}
+
+struct WorkspaceLayout {
+  int partition_tokens;
+  int max_parts;
+  size_t o_bytes;   // partial outputs
+  size_t ml_bytes;  // (max, sum) pairs
+  size_t total;
+};
+
+size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+WorkspaceLayout workspace_layout(const pa_pool *pool, int32_t num_seqs, int32_t num_q_heads,
+                                 int64_t eff_ctx) {
+  WorkspaceLayout w{};
+  w.partition_tokens = choose_partition_tokens(eff_ctx);
+  w.max_parts = eff_ctx > 0 ? (int)ceil_div(eff_ctx, w.partition_tokens) : 1;
+  if (w.max_parts <= 1) {
+    w.max_parts = 1;
+    return w;  // single partition: results go straight to the output
+  }
+  const size_t heads = (size_t)num_seqs * num_q_heads * w.max_parts;
+  w.o_bytes = round_up(heads * pool->head_dim * sizeof(float), 256);
+  w.ml_bytes = round_up(heads * 2 * sizeof(float), 256);
+  w.total = w.o_bytes + w.ml_bytes;
+  return w;
+}
+
+}  // namespace
+
+DecodeChoice choose_decode_kernel(pa_dtype dtype, int group) {
+  DecodeChoice c;
+  const bool force_valu = env_int("PA_FORCE_VALU", 0) != 0;
+  if (dtype != PA_F32 && group >= 4 && group <= 16 && !force_valu) {
+    c.kernel = DecodeKernel::kMfma;
+    c.heads_per_pass = group;
+    return c;
+  }
+  c.kernel = DecodeKernel::kValu;
+  c.heads_per_pass = group == 1 ? 1 : group == 2 ? 2 : 4;
+  return c;
+}
+
+int choose_partition_tokens(int64_t eff_ctx) {
+  const int forced = env_int("PA_PARTITION_TOKENS", 0);
+  if (forced >= kTileTokens && forced % kTileTokens == 0) return forced;
+  (void)eff_ctx;
+  return 512;
+}
+
+}  // namespace pa
+
+extern "C" {
+
+const char *pa_last_hip_error(void) { return pa::g_last_hip_error.c_str(); }
+
+int pa_reshape_and_cache(pa_pool *pool, const void *key, const void *value,
+                         const int32_t *slot_mapping, int32_t num_tokens, void *stream) {
+  if (pool == nullptr || num_tokens < 0) return PA_ERR_INVAL;
+  if (num_tokens == 0) return PA_OK;
+  if (key == nullptr || value == nullptr || slot_mapping == nullptr) return PA_ERR_INVAL;
+  if (!pa::aligned16(key) || !pa::aligned16(value)) return PA_ERR_INVAL;
+  if ((reinterpret_cast<uintptr_t>(slot_mapping) & 3u) != 0) return PA_ERR_INVAL;
+  return pa::hip_status(pa::launch_reshape_and_cache(
+      pool->dtype, pool->k_cache, pool->v_cache, key, value, slot_mapping, num_tokens,
+      pool->num_kv_heads * pool->head_dim, (int64_t)pool->num_blocks * pool->block_size,
+      static_cast<hipStream_t>(stream)));
+}
+
+size_t pa_decode_workspace_bytes(const pa_pool *pool, int32_t num_seqs, int32_t num_q_heads,
+                                 int32_t max_context_len, const pa_ring *ring) {
+  if (pool == nullptr || num_seqs < 0 || num_q_heads <= 0 || max_context_len < 0) return 0;
+  if (!pa::ring_valid(ring)) return 0;
+  const int64_t eff = pa::effective_context(max_context_len, ring);
+  return pa::workspace_layout(pool, num_seqs, num_q_heads, eff).total;
+}
+
+size_t pa_rope_table_bytes(int32_t capacity, int32_t head_dim) {
+  if (capacity <= 0 || head_dim <= 0 || (head_dim & 1)) return 0;
+  return (size_t)capacity * (size_t)(head_dim / 2) * 2 * sizeof(float);
+}
+
+int pa_rope_table_init(float *table, int32_t capacity, int32_t head_dim, float rope_base,
+                       void *stream) {
+  if (table == nullptr || capacity <= 0 || (head_dim != 64 && head_dim != 128)) return PA_ERR_INVAL;
+  if (!(rope_base > 0.0f) || !pa::aligned16(table)) return PA_ERR_INVAL;
+  return pa::hip_status(pa::launch_rope_table_init(table, capacity, head_dim, rope_base,
+                                                   static_cast<hipStream_t>(stream)));
+}
+
+int pa_decode(pa_pool *pool, void *out, const void *query, const int32_t *block_tables,
+              int32_t max_blocks_per_seq, const int32_t *context_lens, int32_t num_seqs,
+              int32_t num_q_heads, int32_t max_context_len, float scale, const pa_ring *ring,
+              void *workspace, size_t workspace_bytes, void *stream) {
+  if (pool == nullptr || num_seqs < 0 || num_q_heads <= 0 || max_context_len < 0 ||
+      max_blocks_per_seq <= 0)
+    return PA_ERR_INVAL;
+  if (num_q_heads % pool->num_kv_heads != 0) return PA_ERR_INVAL;
+  const int group = num_q_heads / pool->num_kv_heads;
+  if (!pa::ring_valid(ring)) return PA_ERR_INVAL;
+  if (num_seqs == 0) return PA_OK;
+  if (out == nullptr || query == nullptr || block_tables == nullptr || context_lens == nullptr)
+    return PA_ERR_INVAL;
+  if (!pa::aligned16(out) || !pa::aligned16(query)) return PA_ERR_INVAL;
+  if ((reinterpret_cast<uintptr_t>(block_tables) | reinterpret_cast<uintptr_t>(context_lens)) & 3u)
+    return PA_ERR_INVAL;
+  const int64_t table_tokens = (int64_t)max_blocks_per_seq * pool->block_size;
+  if (ring == nullptr) {
+    if (max_context_len > table_tokens) return PA_ERR_INVAL;
+  } else {
+    if ((int64_t)ring->sink + ring->window > table_tokens) return PA_ERR_INVAL;
+    if (ring->rope_table == nullptr || !pa::aligned16(ring->rope_table)) return PA_ERR_INVAL;
+  }
+  if (!(scale == scale)) return PA_ERR_INVAL;  // NaN scale
+
+  const int64_t eff = pa::effective_context(max_context_len, ring);
+  const pa::WorkspaceLayout w = pa::workspace_layout(pool, num_seqs, num_q_heads, eff);
+  if (w.total > 0) {
+    if (workspace == nullptr || workspace_bytes < w.total) return PA_ERR_NOMEM;
+    if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return PA_ERR_INVAL;
+  }
+  if ((int64_t)num_seqs > 65535 || (int64_t)w.max_parts > INT32_MAX) return PA_ERR_INVAL;
+
+  pa::DecodeArgs a{};
+  a.out = out;
+  a.query = query;
+  a.k_cache = pool->k_cache;
+  a.v_cache = pool->v_cache;
+  a.block_tables = block_tables;
+  a.context_lens = context_lens;
+  a.ws_o = w.total > 0 ? static_cast<float *>(workspace) : nullptr;
+  a.ws_ml = w.total > 0 ? reinterpret_cast<float *>(static_cast<char *>(workspace) + w.o_bytes)
+                        : nullptr;
+  a.rope = ring ? ring->rope_table : nullptr;
+  a.kv_block_stride = (int64_t)pool->block_size * pool->num_kv_heads * pool->head_dim;
+  a.num_blocks = pool->num_blocks;
+  a.max_context = max_context_len;
+  a.max_blocks_per_seq = max_blocks_per_seq;
+  a.num_q_heads = num_q_heads;
+  a.num_kv_heads = pool->num_kv_heads;
+  a.group = group;
+  a.block_shift = pa::log2_exact(pool->block_size);
+  a.partition_tokens = w.partition_tokens;
+  a.max_parts = w.max_parts;
+  a.ring_sink = ring ? ring->sink : 0;
+  a.ring_window = ring ? ring->window : 1;
+  a.scale_log2 = scale * pa::kLog2eHost;
+
+  const pa::DecodeChoice choice = pa::choose_decode_kernel(pool->dtype, group);
+  const int nchunk = choice.kernel == pa::DecodeKernel::kMfma
+                         ? 1
+                         : (group + choice.heads_per_pass - 1) / choice.heads_per_pass;
+  if ((int64_t)pool->num_kv_heads * nchunk > 65535) return PA_ERR_UNSUPPORTED;
+  return pa::hip_status(pa::launch_decode(a, pool->dtype, pool->head_dim, ring != nullptr, choice,
+                                          num_seqs, static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

@@ -1,0 +1,111 @@
+// Device helpers for the gfx950 kernels: storage-type tags, conversions,
+// 16-byte vector loads and wavefront (wave64) cross-lane reductions.
+#ifndef PA_DEVICE_COMMON_H_
+#define PA_DEVICE_COMMON_H_
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pa {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr int kWave = 64;
+
+// ------------------------------------------------------------ type tags ---
+// Storage is raw bits: uint16_t for f16/bf16, float for f32.
+struct F32 {
+  typedef float storage;
+  static constexpr int kBytes = 4;
+  static __device__ __forceinline__ float to_float(float x) { return x; }
+  static __device__ __forceinline__ float from_float(float x) { return x; }
+};
+
+struct F16 {
+  typedef uint16_t storage;
+  typedef f16x8 vec8;
+  typedef f16x4 vec4;
+  static constexpr int kBytes = 2;
+  static __device__ __forceinline__ float to_float(uint16_t b) {
+    return (float)__builtin_bit_cast(_Float16, b);
+  }
+  static __device__ __forceinline__ uint16_t from_float(float x) {
+    return __builtin_bit_cast(uint16_t, (_Float16)x);  // round to nearest even
+  }
+  static __device__ __forceinline__ f32x4 mfma_16x16x32(uint4 a, uint4 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a),
+                                                  __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ f32x4 mfma_16x16x16(uint2 a, uint2 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(f16x4, a),
+                                                 __builtin_bit_cast(f16x4, b), c, 0, 0, 0);
+  }
+};
+
+struct BF16 {
+  typedef uint16_t storage;
+  typedef bf16x8 vec8;
+  typedef bf16x4 vec4;
+  static constexpr int kBytes = 2;
+  static __device__ __forceinline__ float to_float(uint16_t b) {
+    return __uint_as_float(((uint32_t)b) << 16);
+  }
+  static __device__ __forceinline__ uint16_t from_float(float x) {
+    return __builtin_bit_cast(uint16_t, (__bf16)x);  // round to nearest even
+  }
+  static __device__ __forceinline__ f32x4 mfma_16x16x32(uint4 a, uint4 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ f32x4 mfma_16x16x16(uint2 a, uint2 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(bf16x4, a),
+                                                     __builtin_bit_cast(bf16x4, b), c, 0, 0, 0);
+  }
+};
+
+// Unpack the element e (0..7) of a 16-byte vector of 16-bit values.
+__device__ __forceinline__ uint16_t half_of(const uint4 &v, int e) {
+  const uint32_t w = e < 2 ? v.x : e < 4 ? v.y : e < 6 ? v.z : v.w;
+  return (uint16_t)((e & 1) ? (w >> 16) : (w & 0xffffu));
+}
+
+__device__ __forceinline__ uint32_t pack2(uint16_t lo, uint16_t hi) {
+  return (uint32_t)lo | ((uint32_t)hi << 16);
+}
+
+// ------------------------------------------------------------ cross-lane ---
+// DPP controls (GFX9 encoding).
+constexpr int kDppQuadXor1 = 0xB1;   // quad_perm [1,0,3,2]
+constexpr int kDppQuadXor2 = 0x4E;   // quad_perm [2,3,0,1]
+constexpr int kDppRowRor8 = 0x128;   // rotate right by 8 within a 16-lane row
+constexpr int kDppRowRor4 = 0x124;
+constexpr int kDppHalfMirror = 0x141;  // lane i <-> 7 - i within each 8 lanes
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+
+// Sum over aligned groups of N consecutive lanes (N in {4, 8, 16, 32, 64});
+// every lane of a group receives the group total.
+template <int N>
+__device__ __forceinline__ float group_sum(float x) {
+  x += dpp_f32<kDppQuadXor1>(x);
+  x += dpp_f32<kDppQuadXor2>(x);
+  if constexpr (N >= 8) x += dpp_f32<kDppHalfMirror>(x);
+  if constexpr (N >= 16) x += dpp_f32<kDppRowRor8>(x);
+  if constexpr (N >= 32) x += __shfl_xor(x, 16);
+  if constexpr (N >= 64) x += __shfl_xor(x, 32);
+  return x;
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+}  // namespace pa
+
+#endif  // PA_DEVICE_COMMON_H_

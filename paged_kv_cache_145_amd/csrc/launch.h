@@ -1,0 +1,67 @@
+// Internal (C++ linkage) launch interface between the C ABI entry points and
+// the kernels.  Host-side only types.
+#ifndef PA_LAUNCH_H_
+#define PA_LAUNCH_H_
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "pa.h"
+
+namespace pa {
+
+// Tokens of one split-K partition: one work-group of kDecodeWaves waves per
+// (partition, KV head [, head chunk], sequence); tiles of 16 tokens.
+constexpr int kTileTokens = 16;
+constexpr int kDecodeWaves = 4;
+constexpr float kLog2eHost = 1.4426950408889634f;
+
+struct DecodeArgs {
+  void *out;
+  const void *query;
+  const void *k_cache;
+  const void *v_cache;
+  const int32_t *block_tables;
+  const int32_t *context_lens;
+  float *ws_o;   // [B][Hq][max_parts][D]   partition-normalised outputs
+  float *ws_ml;  // [B][Hq][max_parts][2]   (running max in log2 units, sum)
+  const float *rope;  // float2 [S+W][D/2] or null
+  int64_t kv_block_stride;  // elements per physical block (block_size * Hkv * D)
+  int32_t num_blocks;
+  int32_t max_context;  // host bound of context_lens (lengths are clamped to it)
+  int32_t max_blocks_per_seq;
+  int32_t num_q_heads;
+  int32_t num_kv_heads;
+  int32_t group;        // Hq / Hkv
+  int32_t block_shift;  // log2(block_size)
+  int32_t partition_tokens;
+  int32_t max_parts;
+  int32_t ring_sink;
+  int32_t ring_window;
+  float scale_log2;  // scale * log2(e)
+};
+
+enum class DecodeKernel { kMfma, kValu };
+
+struct DecodeChoice {
+  DecodeKernel kernel;
+  int heads_per_pass;  // VALU: query heads handled per work-group (1, 2 or 4)
+};
+
+DecodeChoice choose_decode_kernel(pa_dtype dtype, int group);
+int choose_partition_tokens(int64_t effective_max_context);
+
+hipError_t launch_decode(const DecodeArgs &a, pa_dtype dtype, int head_dim, bool ring,
+                         DecodeChoice choice, int num_seqs, hipStream_t stream);
+
+hipError_t launch_reshape_and_cache(pa_dtype dtype, void *k_cache, void *v_cache,
+                                    const void *key, const void *value,
+                                    const int32_t *slot_mapping, int32_t num_tokens,
+                                    int32_t row_elems, int64_t num_slots, hipStream_t stream);
+
+hipError_t launch_rope_table_init(float *table, int32_t capacity, int32_t head_dim,
+                                  float rope_base, hipStream_t stream);
+
+}  // namespace pa
+
+#endif  // PA_LAUNCH_H_

@@ -1,0 +1,175 @@
+// Host side of the paged KV cache: pool description, block allocator with
+// reference counts, ring slot equation and slot mapping.  Plain C++17, no HIP.
+//
+// Allocation order follows the free-bitmap allocator of "端侧 SLM 显存保活术…"
+// (sheratonhq.com/news/141880), section "嵌入式轻量 Block 分配器设计": the
+// lowest free id is taken first (word scan + count trailing zeros) and -1
+// reports exhaustion.  Reference counts and release at the last reference
+// follow "Ollama的内存管理策略…" (xdnf.cn/news/5086), section
+// "三、KV Cache内存管理的工程实现"; misuse that page leaves unchecked
+// (release of a free block) is an error here.
+#include <cstring>
+#include <new>
+
+#include "pool_internal.h"
+
+namespace pa {
+
+bool ring_valid(const pa_ring *ring) {
+  if (ring == nullptr) return true;
+  if (ring->sink < 0 || ring->window < 1) return false;
+  if ((int64_t)ring->sink + ring->window > INT32_MAX) return false;
+  if (ring->rope_style != 0) return false;
+  if (!(ring->rope_base > 0.0f)) return false;
+  return true;
+}
+
+}  // namespace pa
+
+extern "C" {
+
+int pa_create_pool(pa_pool **out, int32_t num_blocks, int32_t block_size, int32_t num_kv_heads,
+                   int32_t head_dim, pa_dtype dtype, void *k_cache, void *v_cache) {
+  if (out == nullptr) return PA_ERR_INVAL;
+  *out = nullptr;
+  if (num_blocks <= 0 || num_kv_heads <= 0) return PA_ERR_INVAL;
+  if (block_size != 16 && block_size != 64) return PA_ERR_INVAL;
+  if (head_dim != 64 && head_dim != 128) return PA_ERR_INVAL;
+  if (!pa::valid_dtype((int)dtype)) return PA_ERR_INVAL;
+  if (k_cache == nullptr || v_cache == nullptr) return PA_ERR_INVAL;
+  if ((reinterpret_cast<uintptr_t>(k_cache) | reinterpret_cast<uintptr_t>(v_cache)) & 15u)
+    return PA_ERR_INVAL;
+  pa_pool *p = new (std::nothrow) pa_pool();
+  if (p == nullptr) return PA_ERR_NOMEM;
+  p->num_blocks = num_blocks;
+  p->block_size = block_size;
+  p->num_kv_heads = num_kv_heads;
+  p->head_dim = head_dim;
+  p->dtype = dtype;
+  p->k_cache = k_cache;
+  p->v_cache = v_cache;
+  try {
+    const size_t words = (size_t)pa::ceil_div(num_blocks, 64);
+    p->free_bits.assign(words, ~0ull);
+    const int tail = num_blocks % 64;
+    if (tail != 0) p->free_bits[words - 1] = (1ull << tail) - 1ull;
+    p->refcount.assign((size_t)num_blocks, 0);
+  } catch (...) {
+    delete p;
+    return PA_ERR_NOMEM;
+  }
+  p->used = 0;
+  p->shared = 0;
+  *out = p;
+  return PA_OK;
+}
+
+void pa_destroy_pool(pa_pool *pool) { delete pool; }
+
+int32_t pa_alloc_block(pa_pool *pool) {
+  if (pool == nullptr) return -1;
+  std::lock_guard<std::mutex> lock(pool->mu);
+  for (size_t w = 0; w < pool->free_bits.size(); ++w) {
+    const uint64_t bits = pool->free_bits[w];
+    if (bits != 0) {
+      const int bit = __builtin_ctzll(bits);
+      pool->free_bits[w] = bits & ~(1ull << bit);
+      const int32_t id = (int32_t)(w * 64 + (size_t)bit);
+      pool->refcount[(size_t)id] = 1;
+      pool->used += 1;
+      return id;
+    }
+  }
+  return -1;
+}
+
+int pa_incref_block(pa_pool *pool, int32_t block_id) {
+  if (pool == nullptr) return PA_ERR_INVAL;
+  std::lock_guard<std::mutex> lock(pool->mu);
+  if (block_id < 0 || block_id >= pool->num_blocks) return PA_ERR_INVAL;
+  int32_t &rc = pool->refcount[(size_t)block_id];
+  if (rc == 0) return PA_ERR_STATE;
+  if (rc == INT32_MAX) return PA_ERR_STATE;
+  rc += 1;
+  if (rc == 2) pool->shared += 1;
+  return PA_OK;
+}
+
+int pa_decref_block(pa_pool *pool, int32_t block_id) {
+  if (pool == nullptr) return PA_ERR_INVAL;
+  std::lock_guard<std::mutex> lock(pool->mu);
+  if (block_id < 0 || block_id >= pool->num_blocks) return PA_ERR_INVAL;
+  int32_t &rc = pool->refcount[(size_t)block_id];
+  if (rc == 0) return PA_ERR_STATE;
+  rc -= 1;
+  if (rc == 1) pool->shared -= 1;
+  if (rc == 0) {
+    pool->free_bits[(size_t)block_id / 64] |= 1ull << (block_id % 64);
+    pool->used -= 1;
+  }
+  return PA_OK;
+}
+
+int32_t pa_get_refcount(const pa_pool *pool, int32_t block_id) {
+  if (pool == nullptr) return -1;
+  std::lock_guard<std::mutex> lock(pool->mu);
+  if (block_id < 0 || block_id >= pool->num_blocks) return -1;
+  return pool->refcount[(size_t)block_id];
+}
+
+int pa_get_stats(const pa_pool *pool, pa_pool_stats *out) {
+  if (pool == nullptr || out == nullptr) return PA_ERR_INVAL;
+  std::lock_guard<std::mutex> lock(pool->mu);
+  out->total = pool->num_blocks;
+  out->used = pool->used;
+  out->shared = pool->shared;
+  out->free = pool->num_blocks - pool->used;
+  return PA_OK;
+}
+
+// Slot equation of wzjinhao.cn/news/69573, section "环形上下文与注意力沉淀机制".
+int32_t pa_ring_slot(int64_t pos, int32_t sink, int32_t window) {
+  if (pos < 0 || sink < 0 || window < 1) return -1;
+  if (pos < sink) return (int32_t)pos;
+  return (int32_t)(sink + (pos - sink) % window);
+}
+
+int pa_compute_slot_mapping(const pa_pool *pool, const int32_t *block_tables, int32_t num_seqs,
+                            int32_t max_blocks_per_seq, const int32_t *seq_ids,
+                            const int64_t *positions, int32_t n, const pa_ring *ring,
+                            int32_t *out) {
+  if (pool == nullptr || n < 0 || num_seqs < 0 || max_blocks_per_seq < 0) return PA_ERR_INVAL;
+  if (n == 0) return PA_OK;
+  if (block_tables == nullptr || seq_ids == nullptr || positions == nullptr || out == nullptr)
+    return PA_ERR_INVAL;
+  if (!pa::ring_valid(ring)) return PA_ERR_INVAL;
+  const int64_t bs = pool->block_size;
+  for (int32_t i = 0; i < n; ++i) {
+    const int32_t s = seq_ids[i];
+    const int64_t pos = positions[i];
+    if (s < 0 || s >= num_seqs || pos < 0) return PA_ERR_INVAL;
+    const int64_t r = ring ? (int64_t)pa_ring_slot(pos, ring->sink, ring->window) : pos;
+    const int64_t lb = r / bs;
+    if (lb >= max_blocks_per_seq) return PA_ERR_INVAL;
+    const int32_t phys = block_tables[(int64_t)s * max_blocks_per_seq + lb];
+    if (phys < 0 || phys >= pool->num_blocks) return PA_ERR_INVAL;
+    const int64_t slot = (int64_t)phys * bs + r % bs;
+    if (slot > INT32_MAX) return PA_ERR_INVAL;
+    out[i] = (int32_t)slot;
+  }
+  return PA_OK;
+}
+
+const char *pa_status_str(int status) {
+  switch (status) {
+    case PA_OK: return "PA_OK";
+    case PA_ERR_INVAL: return "PA_ERR_INVAL";
+    case PA_ERR_NOMEM: return "PA_ERR_NOMEM";
+    case PA_ERR_STATE: return "PA_ERR_STATE";
+    case PA_ERR_HIP: return "PA_ERR_HIP";
+    case PA_ERR_UNSUPPORTED: return "PA_ERR_UNSUPPORTED";
+    default: return "PA_ERR_UNKNOWN";
+  }
+}
+
+}  // extern "C"

@@ -1,0 +1,47 @@
+// Host-side pool state shared by the allocator (pool.cpp, plain C++) and the
+// HIP entry points (api.hip).  No HIP types here, so pool.cpp builds with g++.
+#ifndef PA_POOL_INTERNAL_H_
+#define PA_POOL_INTERNAL_H_
+
+#include <cstdint>
+#include <mutex>
+#include <vector>
+
+#include "pa.h"
+
+struct pa_pool {
+  int32_t num_blocks;
+  int32_t block_size;
+  int32_t num_kv_heads;
+  int32_t head_dim;
+  pa_dtype dtype;
+  void *k_cache;
+  void *v_cache;
+
+  // Allocator: one bit per block (1 = free), scanned lowest word first with a
+  // count-trailing-zeros step, plus a reference count per block.
+  mutable std::mutex mu;
+  std::vector<uint64_t> free_bits;
+  std::vector<int32_t> refcount;
+  int32_t used;
+  int32_t shared;
+};
+
+namespace pa {
+
+inline int dtype_bytes(pa_dtype t) { return t == PA_F32 ? 4 : 2; }
+inline bool valid_dtype(int t) { return t == PA_F32 || t == PA_F16 || t == PA_BF16; }
+inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// Effective number of cached keys a decode can read for a context bound.
+inline int64_t effective_context(int64_t max_context_len, const pa_ring *ring) {
+  if (ring == nullptr) return max_context_len;
+  int64_t cap = (int64_t)ring->sink + ring->window;
+  return max_context_len < cap ? max_context_len : cap;
+}
+
+bool ring_valid(const pa_ring *ring);
+
+}  // namespace pa
+
+#endif  // PA_POOL_INTERNAL_H_

@@ -1,0 +1,302 @@
+"""GPU parity: the HIP path through the C ABI against the fp64 oracle.
+
+Tolerances (stated for the decode output): fp32 KV max |err| <= 1e-4;
+fp16/bf16 KV max |err| / max |ref| <= 2e-2 with fp32 accumulation.
+Slot mappings and cache writes are bit-exact.  Invariances that the
+paging method implies are checked for bit identity on the GPU itself.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+from gpu_support import (DeviceCase, assert_parity, env, oracle_reference, raw_bits, raw_to_torch,
+                         torch_bits, torch_to_f64)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.fail("no GPU visible: the gpu tests need an MI355X")
+    import paged_kv_cache_145_amd._lib as L
+
+    L.load()
+    yield
+
+
+_REF_CACHE = {}
+
+
+def reference(name, maker):
+    if name not in _REF_CACHE:
+        case = maker()
+        _REF_CACHE[name] = (case, oracle_reference(case))
+    return _REF_CACHE[name]
+
+
+CONFIGS = {
+    "tiny_fp32": workloads.config_tiny_fp32,
+    "embedded_1p1b": workloads.config_embedded_1p1b,
+    "llama70b_b64": workloads.config_llama70b,
+    "shared_prefix": workloads.config_shared_prefix,
+    "sink_ring": workloads.config_sink_ring,
+}
+
+
+# ---------------------------------------------------------------- write side
+
+@pytest.mark.parametrize("name", list(CONFIGS))
+def test_reshape_and_cache_bit_exact(name):
+    case, (kp, vp, slots, _) = reference(name, CONFIGS[name])
+    dc = DeviceCase(case)
+    dc.write_all()
+    assert np.array_equal(dc.slot_chunks.astype(np.int64), np.concatenate(slots))
+    assert np.array_equal(torch_bits(dc.k_cache, case.dtype), raw_bits(kp, case.dtype))
+    assert np.array_equal(torch_bits(dc.v_cache, case.dtype), raw_bits(vp, case.dtype))
+    dc.close()
+
+
+def test_reshape_and_cache_skips_negative_slots():
+    case = workloads.config_tiny_fp32()
+    dc = DeviceCase(case)
+    before = torch_bits(dc.k_cache, "f32").copy()
+    keys = raw_to_torch(case.writes[0].keys[:4], "f32").cuda()
+    vals = raw_to_torch(case.writes[0].values[:4], "f32").cuda()
+    slots = torch.tensor([-1, 5, -7, 200], dtype=torch.int32, device="cuda")
+    import paged_kv_cache_145_amd as pk
+
+    pk.reshape_and_cache(dc.pool, keys, vals, slots)
+    torch.cuda.synchronize()
+    kp, _ = oracle.reshape_and_cache(case.empty_pool(), case.empty_pool(), case.writes[0].keys[:4],
+                                     case.writes[0].values[:4], [-1, 5, -7, 200], 16)
+    assert np.array_equal(torch_bits(dc.k_cache, "f32"), raw_bits(kp, "f32"))
+    assert not np.array_equal(torch_bits(dc.k_cache, "f32"), before)
+    dc.close()
+
+
+def test_ring_step_by_step_last_writer_state():
+    """One write per step into a 4 + 12 slot ring (one 16-token block); the
+    device pool must equal the oracle's last-writer pool after every step."""
+    sink, window = 4, 12
+    steps = 200
+    case = workloads.config_sink_ring(lengths=[steps], sink=sink, window=window, block_size=16,
+                                      num_q_heads=4, num_kv_heads=2, head_dim=64)
+    rng = np.random.default_rng(77)
+    keys = workloads.draw_values(rng, (steps, 2, 64), "f16")
+    vals = workloads.draw_values(rng, (steps, 2, 64), "f16")
+    case.writes = []
+    dc = DeviceCase(case)
+    kp, vp = case.empty_pool(), case.empty_pool()
+    import paged_kv_cache_145_amd as pk
+
+    for pos in range(steps):
+        ch = workloads.WriteChunk(0, np.array([pos], dtype=np.int64), keys[pos:pos + 1], vals[pos:pos + 1])
+        dc.write_all([ch])
+        r = oracle.ring_slot(pos, sink, window)
+        oracle.reshape_and_cache_(kp, vp, ch.keys, ch.values, [oracle.slot_of(case.block_tables[0], r, 16)], 16)
+        if pos % 17 == 0 or pos == steps - 1:
+            torch.cuda.synchronize()
+            assert np.array_equal(torch_bits(dc.k_cache, "f16"), raw_bits(kp, "f16"))
+            assert np.array_equal(torch_bits(dc.v_cache, "f16"), raw_bits(vp, "f16"))
+        if pos in (0, 10, 15, 16, 17, 50, steps - 1):
+            case.context_lens[:] = pos + 1
+            dc.context_lens.fill_(pos + 1)
+            out = dc.decode()
+            ref = oracle.decode(case.query, kp, vp, case.block_tables, case.context_lens, case.scale,
+                                "f16", 16, ring=case.ring)
+            assert_parity(out, ref, "f16")
+    dc.close()
+
+
+# ---------------------------------------------------------------- decode parity
+
+@pytest.mark.parametrize("kernel", ["auto", "valu"])
+@pytest.mark.parametrize("name", list(CONFIGS))
+def test_decode_parity_full_config(name, kernel):
+    case, (_, _, _, ref) = reference(name, CONFIGS[name])
+    dc = DeviceCase(case)
+    dc.write_all()
+    with env(PA_FORCE_VALU="1" if kernel == "valu" else None):
+        out = dc.decode()
+    err = assert_parity(out, ref, case.dtype)
+    print(f"{name} [{kernel}] parity error {err:.3e}")
+    dc.close()
+
+
+@pytest.mark.parametrize("partition", [16, 64, 256, 2048])
+def test_decode_partition_sizes(partition):
+    case, (_, _, _, ref) = reference("embedded_1p1b", CONFIGS["embedded_1p1b"])
+    dc = DeviceCase(case)
+    dc.write_all()
+    with env(PA_PARTITION_TOKENS=partition):
+        out = dc.decode()
+    assert_parity(out, ref, case.dtype)
+    dc.close()
+
+
+SHAPES = [
+    # dtype, Hq, Hkv, D, bs, lengths
+    ("f32", 4, 2, 64, 16, [1, 15, 16, 17, 100, 511, 513]),
+    ("f32", 8, 1, 128, 64, [3, 64, 65, 700]),
+    ("f16", 6, 6, 128, 64, [1, 63, 64, 65, 1030]),
+    ("bf16", 3, 1, 64, 16, [2, 31, 33, 600]),
+    ("f16", 4, 1, 64, 16, [5, 17, 512, 1025]),
+    ("bf16", 16, 2, 128, 16, [1, 16, 300, 2049]),
+    ("bf16", 32, 2, 64, 64, [7, 128, 1111]),
+    ("f16", 12, 2, 128, 16, [0, 1, 9, 4000]),
+    ("bf16", 40, 2, 128, 16, [250, 1300]),
+]
+
+
+@pytest.mark.parametrize("kernel", ["auto", "valu"])
+@pytest.mark.parametrize("shape", SHAPES, ids=lambda s: f"{s[0]}-G{s[1] // s[2]}-D{s[3]}-bs{s[4]}")
+def test_decode_ragged_shapes(shape, kernel):
+    dtype, hq, hkv, d, bs, lens = shape
+    case = workloads.make_paged_case("ragged", 4242 + hq + d + bs, dtype, lens, hq, hkv, d, bs)
+    _, _, _, ref = oracle_reference(case)
+    dc = DeviceCase(case)
+    dc.write_all()
+    with env(PA_FORCE_VALU="1" if kernel == "valu" else None, PA_PARTITION_TOKENS=256):
+        out = dc.decode()
+    assert_parity(out, ref, dtype)
+    for b, n in enumerate(lens):
+        if n == 0:
+            assert np.all(torch_bits(out[b], dtype) == 0)
+    dc.close()
+
+
+@pytest.mark.parametrize("kernel", ["auto", "valu"])
+@pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
+def test_single_token_is_v0_bit_exact(dtype, kernel):
+    case = workloads.make_paged_case("n1", 99, dtype, [1, 1, 1, 1], 16, 2, 128, 16)
+    dc = DeviceCase(case)
+    dc.write_all()
+    with env(PA_FORCE_VALU="1" if kernel == "valu" else None):
+        out = dc.decode()
+    got = torch_bits(out, dtype)
+    for b in range(4):
+        v0 = raw_bits(case.writes[b].values[0], dtype)  # [Hkv, D]
+        for h in range(16):
+            assert np.array_equal(got[b, h], v0[h // 8])
+    dc.close()
+
+
+@pytest.mark.parametrize("name", ["embedded_1p1b", "llama70b_b64"])
+def test_block_relabelling_bit_identical_on_gpu(name):
+    case, _ = reference(name, CONFIGS[name])
+    dc = DeviceCase(case)
+    dc.write_all()
+    base = torch_bits(dc.decode(), case.dtype)
+    perm = np.random.default_rng(123).permutation(case.num_blocks)
+    case2 = workloads.DecodeCase(**{**case.__dict__})
+    case2.block_tables = np.where(case.block_tables >= 0, perm[np.maximum(case.block_tables, 0)],
+                                  case.block_tables).astype(np.int32)
+    dc2 = DeviceCase(case2)
+    dc2.write_all()
+    moved = torch_bits(dc2.decode(), case.dtype)
+    assert np.array_equal(base, moved)
+    dc.close()
+    dc2.close()
+
+
+def test_shared_prefix_equals_private_copies_bit_identical_on_gpu():
+    shared, (_, _, _, ref) = reference("shared_prefix", CONFIGS["shared_prefix"])
+    private = workloads.config_shared_prefix(private_copies=True)
+    a = DeviceCase(shared)
+    a.write_all()
+    b = DeviceCase(private)
+    b.write_all()
+    out_a = a.decode()
+    out_b = b.decode()
+    assert np.array_equal(torch_bits(out_a, "f16"), torch_bits(out_b, "f16"))
+    assert_parity(out_a, ref, "f16")
+    a.close()
+    b.close()
+
+
+def test_allocator_built_tables_with_pinned_shared_prefix():
+    """Block tables produced by the library allocator: the 4 prefix blocks are
+    pinned (refcount 1) and referenced once more per sequence; suffix blocks
+    are private.  Decode matches the oracle on those tables; releasing every
+    sequence leaves only the pinned prefix allocated."""
+    import paged_kv_cache_145_amd as pk
+
+    base = workloads.config_shared_prefix(batch=8)
+    dc = DeviceCase(base)
+    pool = dc.pool
+    nb = base.notes["prefix_blocks"]
+    prefix = [pool.alloc_block() for _ in range(nb)]
+    tables = np.full_like(base.block_tables, -1)
+    for b in range(base.num_seqs):
+        for blk in prefix:
+            pool.incref(blk)
+        tables[b, :nb] = prefix
+        n = int(base.context_lens[b])
+        for j in range(nb, -(-n // base.block_size)):
+            tables[b, j] = pool.alloc_block()
+    assert min(tables[tables >= 0]) >= 0
+    st = pool.stats()
+    assert st["shared"] == nb
+    assert all(pool.refcount(blk) == base.num_seqs + 1 for blk in prefix)
+    case = workloads.DecodeCase(**{**base.__dict__})
+    case.block_tables = tables
+    dc.case = case
+    dc.block_tables = torch.from_numpy(tables).cuda()
+    dc.write_all()
+    _, _, _, ref = oracle_reference(case)
+    assert_parity(dc.decode(), ref, "f16")
+    for b in range(case.num_seqs):
+        for blk in tables[b]:
+            if blk >= 0:
+                pool.decref(int(blk))
+    st = pool.stats()
+    assert st["used"] == nb and st["shared"] == 0
+    assert all(pool.refcount(blk) == 1 for blk in prefix)
+    dc.close()
+
+
+def test_table_padding_never_read_on_gpu():
+    a_case = workloads.config_embedded_1p1b(pad_with_minus_one=False)
+    b_case = workloads.config_embedded_1p1b(pad_with_minus_one=True)
+    a = DeviceCase(a_case)
+    a.write_all()
+    b = DeviceCase(b_case)
+    b.write_all()
+    assert np.array_equal(torch_bits(a.decode(), "f16"), torch_bits(b.decode(), "f16"))
+    a.close()
+    b.close()
+
+
+def test_ring_parity_set_both_kernels_agree_with_oracle():
+    case, (_, _, _, ref) = reference("sink_ring", CONFIGS["sink_ring"])
+    dc = DeviceCase(case)
+    dc.write_all()
+    outs = {}
+    for kernel in ("auto", "valu"):
+        with env(PA_FORCE_VALU="1" if kernel == "valu" else None):
+            outs[kernel] = torch_to_f64(dc.decode())
+        assert_parity(torch.from_numpy(outs[kernel]), ref, "f16")
+    dc.close()
+
+
+def test_ring_timing_set_parity():
+    case = workloads.config_sink_ring(lengths=workloads.ring_timing_lengths(16))
+    _, _, _, ref = oracle_reference(case)
+    dc = DeviceCase(case)
+    dc.write_all()
+    out = dc.decode(max_context_len=100_000)
+    assert_parity(out, ref, "f16")
+    dc.close()
+
+
+def test_decode_is_deterministic_across_calls():
+    case, _ = reference("llama70b_b64", CONFIGS["llama70b_b64"])
+    dc = DeviceCase(case)
+    dc.write_all()
+    a = torch_bits(dc.decode(), "bf16")
+    b = torch_bits(dc.decode(), "bf16")
+    assert np.array_equal(a, b)
+    dc.close()

@@ -42,10 +42,16 @@ NAN_BITS = {"f32": 0x7FC00000, "f16": 0x7E00, "bf16": 0x7FC0}
 
 
 def round_f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
-    """Round finite float32 values to bfloat16 (nearest-even); return bits."""
-    bits = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32).astype(np.uint64)
-    bias = ((bits >> 16) & 1) + 0x7FFF
-    return ((bits + bias) >> 16).astype(np.uint16)
+    """Round finite float32 values to bfloat16 (nearest-even); return bits.
+
+    For finite inputs bits + 0x8000 stays below 2**32, so uint32 suffices.
+    """
+    bits = np.array(x, dtype=np.float32, copy=True).view(np.uint32)
+    lsb = (bits >> np.uint32(16)) & np.uint32(1)
+    bits += np.uint32(0x7FFF)
+    bits += lsb
+    bits >>= np.uint32(16)
+    return bits.astype(np.uint16)
 
 
 def draw_values(rng: np.random.Generator, shape, dtype: str) -> np.ndarray:
