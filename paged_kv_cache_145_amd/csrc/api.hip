@@ -3,6 +3,7 @@
 // pool.cpp.
 #include <cstdlib>
 #include <cstring>
+#include <algorithm>
 #include <string>
 
 #include "launch.h"
@@ -46,7 +47,8 @@ size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 WorkspaceLayout workspace_layout(const pa_pool *pool, int32_t num_seqs, int32_t num_q_heads,
                                  int64_t eff_ctx) {
   WorkspaceLayout w{};
-  w.partition_tokens = choose_partition_tokens(eff_ctx);
+  // a partition spans at most 64 blocks (its ids are staged one per lane)
+  w.partition_tokens = std::min(choose_partition_tokens(eff_ctx), 64 * pool->block_size);
   w.max_parts = eff_ctx > 0 ? (int)ceil_div(eff_ctx, w.partition_tokens) : 1;
   if (w.max_parts <= 1) {
     w.max_parts = 1;

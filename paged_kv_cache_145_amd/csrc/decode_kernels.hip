@@ -59,12 +59,39 @@ __device__ __forceinline__ int effective_len(const DecodeArgs &a, int n, bool ri
   return len > 0 ? len : 0;
 }
 
-// Physical block of a logical block.  Ids are a caller contract; an id
-// outside the pool is clamped into it so that the kernel never faults (the
-// result is then unspecified).
-__device__ __forceinline__ int block_id(const DecodeArgs &a, const int32_t *bt, int logical_block) {
-  const int phys = bt[logical_block];
-  return min(max(phys, 0), a.num_blocks - 1);
+// Physical block ids of one partition, staged once per wave in a VGPR:
+// lane i holds the id of the partition's i-th logical block (a partition
+// spans at most 64 blocks).  Ids outside the pool are clamped into it so
+// that the kernel never faults (the result is then unspecified).
+struct PartitionBlocks {
+  int ids;
+  int first;  // first logical block of the partition
+  int shift;
+  __device__ __forceinline__ PartitionBlocks(const DecodeArgs &a, const int32_t *bt, int begin, int end) {
+    shift = a.block_shift;
+    first = begin >> shift;
+    const int last = (end - 1) >> shift;
+    const int lane = threadIdx.x & 63;
+    const int phys = first + lane <= last ? bt[first + lane] : 0;
+    ids = min(max(phys, 0), a.num_blocks - 1);
+  }
+  // block id of the logical token r (wave-uniform r)
+  __device__ __forceinline__ int of_token(int r) const {
+    return __builtin_amdgcn_readlane(ids, (r >> shift) - first);
+  }
+};
+
+// Buffer descriptor over the rows [r0, r0 + valid) of one head in a block:
+// rows past `valid` are out of range, so their loads return zeros without
+// touching memory.  `head_base` already includes the head offset.
+template <int D, class st>
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const DecodeArgs &a, const char *head_base,
+                                                           int phys, int row_in_block, int valid,
+                                                           int64_t row_stride) {
+  const char *p = head_base + ((int64_t)phys * a.kv_block_stride + (int64_t)row_in_block * row_stride) *
+                                  (int64_t)sizeof(st);
+  const int nrec = valid > 0 ? (int)(((valid - 1) * row_stride + D) * sizeof(st)) : 0;
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<char *>(p), (short)0, nrec, kBufferWord3);
 }
 
 // Combine the per-wave (m, l, o) of one work-group and store either the
@@ -147,16 +174,26 @@ struct VChunk;
 template <>
 struct VChunk<128> {
   typedef uint4 type;
+  static __device__ __forceinline__ uint4 load(__amdgpu_buffer_rsrc_t r, int off) {
+    return buffer_load16(r, off);
+  }
   static __device__ __forceinline__ uint2 half(const uint4 &v, int h) {
     return h == 0 ? make_uint2(v.x, v.y) : make_uint2(v.z, v.w);
   }
-  static __device__ __forceinline__ uint4 zero() { return make_uint4(0, 0, 0, 0); }
+  static __device__ __forceinline__ uint4 select(bool keep, const uint4 &v) {
+    return make_uint4(keep ? v.x : 0u, keep ? v.y : 0u, keep ? v.z : 0u, keep ? v.w : 0u);
+  }
 };
 template <>
 struct VChunk<64> {
   typedef uint2 type;
+  static __device__ __forceinline__ uint2 load(__amdgpu_buffer_rsrc_t r, int off) {
+    return buffer_load8(r, off);
+  }
   static __device__ __forceinline__ uint2 half(const uint2 &v, int) { return v; }
-  static __device__ __forceinline__ uint2 zero() { return make_uint2(0, 0); }
+  static __device__ __forceinline__ uint2 select(bool keep, const uint2 &v) {
+    return make_uint2(keep ? v.x : 0u, keep ? v.y : 0u);
+  }
 };
 
 // ---------------------------------------------------------------------------
@@ -193,7 +230,9 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a) {
     zero_rows<T, D>(a, b, hq0, G);
     return;
   }
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  // wave-uniform (SGPR) so tile indices and block ids stay on the scalar path
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int row16 = lane & 15, grp = lane >> 4;
   const int begin = p * P;
   const int end = min(L, begin + P);
@@ -211,10 +250,10 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a) {
     if constexpr (RING) rope_frag16<T, KB>(qf, a.rope + (int64_t)(L - 1) * D, grp);
   }
 
-  const int64_t row_stride = (int64_t)a.num_kv_heads * D;
+  const int64_t row_stride = (int64_t)a.num_kv_heads * D;  // elements between token rows
   const int32_t *bt = a.block_tables + (int64_t)b * a.max_blocks_per_seq;
-  const st *kc = static_cast<const st *>(a.k_cache) + (int64_t)g * D;
-  const st *vc = static_cast<const st *>(a.v_cache) + (int64_t)g * D;
+  const char *kc = static_cast<const char *>(a.k_cache) + (int64_t)g * D * sizeof(st);
+  const char *vc = static_cast<const char *>(a.v_cache) + (int64_t)g * D * sizeof(st);
   const int bmask = (1 << a.block_shift) - 1;
 
   f32x4 acc[EV];
@@ -223,30 +262,30 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a) {
   float m_run = -INFINITY;
   float l_part = 0.f;
 
-  uint4 kf[KB];
-  vchunk vf[4];
+  // Per-lane byte offsets inside a tile (K: token row16, dims 8grp..+8 of
+  // each 32-dim chunk; V: token 4grp+tau, dims EV*row16..+EV).
+  const int k_off = (int)((row16 * row_stride + 8 * grp) * sizeof(st));
+  int v_off[4];
+#pragma unroll
+  for (int tau = 0; tau < 4; ++tau)
+    v_off[tau] = (int)(((4 * grp + tau) * row_stride + EV * row16) * sizeof(st));
+
+  const PartitionBlocks blocks(a, bt, begin, end);
   auto load_tile = [&](int t, uint4 (&k)[KB], vchunk (&v)[4]) {
-    const int r0 = begin + kTileTokens * t;
-    const int phys = block_id(a, bt, r0 >> a.block_shift);
-    const int64_t base = (int64_t)phys * a.kv_block_stride + (int64_t)(r0 & bmask) * row_stride;
-    const st *krow = kc + base + row16 * row_stride + 8 * grp;
+    const int r0 = begin + kTileTokens * min(t, ntiles - 1);
+    const int valid = t < ntiles ? min(kTileTokens, end - r0) : 0;
+    const int phys = blocks.of_token(r0);
+    const auto kr = tile_rsrc<D, st>(a, kc, phys, r0 & bmask, valid, row_stride);
+    const auto vr = tile_rsrc<D, st>(a, vc, phys, r0 & bmask, valid, row_stride);
 #pragma unroll
-    for (int kb = 0; kb < KB; ++kb) k[kb] = *reinterpret_cast<const uint4 *>(krow + 32 * kb);
+    for (int kb = 0; kb < KB; ++kb) k[kb] = buffer_load16(kr, k_off + 64 * kb);
 #pragma unroll
-    for (int tau = 0; tau < 4; ++tau)
-      v[tau] = *reinterpret_cast<const vchunk *>(vc + base + (4 * grp + tau) * row_stride + EV * row16);
+    for (int tau = 0; tau < 4; ++tau) v[tau] = VChunk<D>::load(vr, v_off[tau]);
   };
 
-  int t = wave;
-  if (t < ntiles) load_tile(t, kf, vf);
-  for (; t < ntiles; t += kNW) {
-    uint4 kn[KB];
-    vchunk vn[4];
-    const bool more = t + kNW < ntiles;
-    if (more) load_tile(t + kNW, kn, vn);
-
+  auto process_tile = [&](int t, uint4 (&kf)[KB], vchunk (&vf)[4]) {
     const int r0 = begin + kTileTokens * t;
-    const int valid = min(kTileTokens, end - r0);
+    const int valid = end - r0;  // <= 0 for a tile past the partition
     if constexpr (RING) {
       const int r = r0 + row16;
       const int j = r < L ? ring_cache_index(r, n, a.ring_sink, a.ring_window) : 0;
@@ -280,11 +319,8 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a) {
     for (int j = 0; j < 4; ++j) pj[j] = fast_exp2(sc[j] - m_run);
     l_part += (pj[0] + pj[1]) + (pj[2] + pj[3]);
 
-    if (valid < kTileTokens) {
-#pragma unroll
-      for (int tau = 0; tau < 4; ++tau)
-        if (4 * grp + tau >= valid) vf[tau] = VChunk<D>::zero();
-    }
+    // V rows past the context were loaded as zeros (out of the descriptor's
+    // range), so a zero weight never meets a NaN sentinel.
 #pragma unroll
     for (int tau = 0; tau < 4; ++tau) {
       const uint32_t x = T::from_float(pj[tau]);
@@ -294,11 +330,21 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a) {
       for (int e = 0; e < EV; ++e)
         acc[e] = T::mfma_16x16x16(op[e & 3], VChunk<D>::half(vf[tau], e >> 2), acc[e]);
     }
-    if (more) {
-#pragma unroll
-      for (int kb = 0; kb < KB; ++kb) kf[kb] = kn[kb];
-#pragma unroll
-      for (int tau = 0; tau < 4; ++tau) vf[tau] = vn[tau];
+  };
+
+  // Two register sets in ping-pong: while one tile is consumed the next
+  // one's loads are in flight, with no register copies and no branches
+  // around loads (so the hardware wait counts stay exact).  A tile past the
+  // partition loads nothing and contributes nothing.
+  uint4 ka[KB], kb2[KB];
+  vchunk va[4], vb[4];
+  if (wave < ntiles) {
+    load_tile(wave, ka, va);
+    for (int t = wave; t < ntiles; t += 2 * kNW) {
+      load_tile(t + kNW, kb2, vb);
+      process_tile(t, ka, va);
+      load_tile(t + 2 * kNW, ka, va);
+      process_tile(t + kNW, kb2, vb);
     }
   }
 
@@ -354,7 +400,8 @@ __global__ __launch_bounds__(256) void decode_valu_kernel(DecodeArgs a) {
     zero_rows<T, D>(a, b, hq0, nh);
     return;
   }
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int li = lane % LPR, rg = lane / LPR;
   const int begin = p * P;
   const int end = min(L, begin + P);
@@ -384,9 +431,13 @@ __global__ __launch_bounds__(256) void decode_valu_kernel(DecodeArgs a) {
 
   const int64_t row_stride = (int64_t)a.num_kv_heads * D;
   const int32_t *bt = a.block_tables + (int64_t)b * a.max_blocks_per_seq;
-  const st *kc = static_cast<const st *>(a.k_cache) + (int64_t)g * D + li * EPL;
-  const st *vc = static_cast<const st *>(a.v_cache) + (int64_t)g * D + li * EPL;
+  const char *kc = static_cast<const char *>(a.k_cache) + (int64_t)g * D * sizeof(st);
+  const char *vc = static_cast<const char *>(a.v_cache) + (int64_t)g * D * sizeof(st);
   const int bmask = (1 << a.block_shift) - 1;
+  const PartitionBlocks blocks(a, bt, begin, end);
+  int off[STEPS];  // byte offset of this lane's 16 bytes in step s of a tile
+#pragma unroll
+  for (int s = 0; s < STEPS; ++s) off[s] = (int)(((s * RPW + rg) * row_stride + li * EPL) * sizeof(st));
 
   float m[NH], l[NH], o[NH][EPL];
 #pragma unroll
@@ -397,22 +448,28 @@ __global__ __launch_bounds__(256) void decode_valu_kernel(DecodeArgs a) {
     for (int e = 0; e < EPL; ++e) o[hh][e] = 0.f;
   }
 
-  for (int t = wave; t < ntiles; t += kNW) {
+  auto load_tile = [&](int t, uint4 (&k)[STEPS], uint4 (&v)[STEPS]) {
+    const int r0 = begin + kTileTokens * min(t, ntiles - 1);
+    const int valid = t < ntiles ? min(kTileTokens, end - r0) : 0;
+    const int phys = blocks.of_token(r0);
+    const auto kr = tile_rsrc<D, st>(a, kc, phys, r0 & bmask, valid, row_stride);
+    const auto vr = tile_rsrc<D, st>(a, vc, phys, r0 & bmask, valid, row_stride);
+#pragma unroll
+    for (int s = 0; s < STEPS; ++s) {
+      k[s] = buffer_load16(kr, off[s]);
+      v[s] = buffer_load16(vr, off[s]);
+    }
+  };
+
+  auto process_tile = [&](int t, const uint4 (&kt)[STEPS], const uint4 (&vt)[STEPS]) {
     const int r0 = begin + kTileTokens * t;
-    const int valid = min(kTileTokens, end - r0);
-    const int phys = block_id(a, bt, r0 >> a.block_shift);
-    const int64_t base = (int64_t)phys * a.kv_block_stride + (int64_t)(r0 & bmask) * row_stride;
+    const int valid = end - r0;  // <= 0 past the partition
 #pragma unroll
     for (int s = 0; s < STEPS; ++s) {
       const int tok = s * RPW + rg;
       const bool ok = tok < valid;
-      uint4 kr = make_uint4(0, 0, 0, 0), vr = make_uint4(0, 0, 0, 0);
-      if (ok) {
-        kr = *reinterpret_cast<const uint4 *>(kc + base + tok * row_stride);
-        vr = *reinterpret_cast<const uint4 *>(vc + base + tok * row_stride);
-      }
-      const st *ke = reinterpret_cast<const st *>(&kr);
-      const st *ve = reinterpret_cast<const st *>(&vr);
+      const st *ke = reinterpret_cast<const st *>(&kt[s]);
+      const st *ve = reinterpret_cast<const st *>(&vt[s]);
       float kf[EPL], vf[EPL];
 #pragma unroll
       for (int e = 0; e < EPL; ++e) {
@@ -421,7 +478,7 @@ __global__ __launch_bounds__(256) void decode_valu_kernel(DecodeArgs a) {
       }
       if constexpr (RING) {
         const int r = r0 + tok;
-        const int j = r < L ? ring_cache_index(r, n, a.ring_sink, a.ring_window) : 0;
+        const int j = (ok && r < L) ? ring_cache_index(r, n, a.ring_sink, a.ring_window) : 0;
         const float *cs = a.rope + (int64_t)j * D + 2 * ridx;
 #pragma unroll
         for (int e = 0; e < EPL; ++e) {
@@ -446,6 +503,17 @@ __global__ __launch_bounds__(256) void decode_valu_kernel(DecodeArgs a) {
           m[hh] = mn;
         }
       }
+    }
+  };
+
+  uint4 ka[STEPS], va[STEPS], kb2[STEPS], vb[STEPS];
+  if (wave < ntiles) {
+    load_tile(wave, ka, va);
+    for (int t = wave; t < ntiles; t += 2 * kNW) {
+      load_tile(t + kNW, kb2, vb);
+      process_tile(t, ka, va);
+      load_tile(t + 2 * kNW, ka, va);
+      process_tile(t + kNW, kb2, vb);
     }
   }
 

@@ -106,6 +106,19 @@ __device__ __forceinline__ float group_sum(float x) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// ------------------------------------------------------- buffer loads ---
+// Raw (untyped) buffer descriptor word 3 for gfx9-family parts: 32-bit
+// data format, no swizzle.  Loads whose byte offset falls outside the
+// descriptor's num_records return zeros and access no memory.
+constexpr int kBufferWord3 = 0x00020000;
+
+__device__ __forceinline__ uint4 buffer_load16(__amdgpu_buffer_rsrc_t r, int off) {
+  return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+__device__ __forceinline__ uint2 buffer_load8(__amdgpu_buffer_rsrc_t r, int off) {
+  return __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0));
+}
+
 }  // namespace pa
 
 #endif  // PA_DEVICE_COMMON_H_
