@@ -37,8 +37,9 @@ int log2_exact(int v) {
 struct WorkspaceLayout {
   int partition_tokens;
   int max_parts;
-  size_t o_bytes;   // partial outputs
-  size_t ml_bytes;  // (max, sum) pairs
+  size_t sched_bytes;  // stream-K tile prefix (MFMA kernel)
+  size_t ml_bytes;     // (max, sum) pairs
+  size_t o_bytes;      // partial outputs
   size_t total;
 };
 
@@ -50,14 +51,26 @@ WorkspaceLayout workspace_layout(const pa_pool *pool, int32_t num_seqs, int32_t 
   // a partition spans at most 64 blocks (its ids are staged one per lane)
   w.partition_tokens = std::min(choose_partition_tokens(eff_ctx), 64 * pool->block_size);
   w.max_parts = eff_ctx > 0 ? (int)ceil_div(eff_ctx, w.partition_tokens) : 1;
+  const int group = num_q_heads / pool->num_kv_heads;
+  const int64_t slice = std::min<int64_t>(num_seqs, kMaxSchedSeqsHost);
+  if (choose_decode_kernel(pool->dtype, group).kernel == DecodeKernel::kMfma) {
+    // stream-K: one slot per wave plus one per (sequence, KV head)
+    const size_t waves = std::max<size_t>(kMaxPersistentWavesHost, (size_t)pool->num_kv_heads);
+    const size_t slots = waves + (size_t)slice * pool->num_kv_heads;
+    w.sched_bytes = round_up((size_t)(slice + 1) * sizeof(int32_t), 256);
+    w.ml_bytes = round_up(slots * group * 2 * sizeof(float), 256);
+    w.o_bytes = round_up(slots * group * pool->head_dim * sizeof(float), 256);
+    w.total = w.sched_bytes + w.ml_bytes + w.o_bytes;
+    return w;
+  }
   if (w.max_parts <= 1) {
     w.max_parts = 1;
     return w;  // single partition: results go straight to the output
   }
-  const size_t heads = (size_t)num_seqs * num_q_heads * w.max_parts;
-  w.o_bytes = round_up(heads * pool->head_dim * sizeof(float), 256);
+  const size_t heads = (size_t)slice * num_q_heads * w.max_parts;
   w.ml_bytes = round_up(heads * 2 * sizeof(float), 256);
-  w.total = w.o_bytes + w.ml_bytes;
+  w.o_bytes = round_up(heads * pool->head_dim * sizeof(float), 256);
+  w.total = w.ml_bytes + w.o_bytes;
   return w;
 }
 
@@ -154,7 +167,7 @@ int pa_decode(pa_pool *pool, void *out, const void *query, const int32_t *block_
     if (workspace == nullptr || workspace_bytes < w.total) return PA_ERR_NOMEM;
     if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return PA_ERR_INVAL;
   }
-  if ((int64_t)num_seqs > 65535 || (int64_t)w.max_parts > INT32_MAX) return PA_ERR_INVAL;
+  if ((int64_t)w.max_parts * num_seqs > INT32_MAX) return PA_ERR_UNSUPPORTED;
 
   pa::DecodeArgs a{};
   a.out = out;
@@ -163,11 +176,13 @@ int pa_decode(pa_pool *pool, void *out, const void *query, const int32_t *block_
   a.v_cache = pool->v_cache;
   a.block_tables = block_tables;
   a.context_lens = context_lens;
-  a.ws_o = w.total > 0 ? static_cast<float *>(workspace) : nullptr;
-  a.ws_ml = w.total > 0 ? reinterpret_cast<float *>(static_cast<char *>(workspace) + w.o_bytes)
-                        : nullptr;
+  char *ws = static_cast<char *>(workspace);
+  a.ws_sched = w.sched_bytes > 0 ? reinterpret_cast<int32_t *>(ws) : nullptr;
+  a.ws_ml = w.ml_bytes > 0 ? reinterpret_cast<float *>(ws + w.sched_bytes) : nullptr;
+  a.ws_o = w.o_bytes > 0 ? reinterpret_cast<float *>(ws + w.sched_bytes + w.ml_bytes) : nullptr;
   a.rope = ring ? ring->rope_table : nullptr;
   a.kv_block_stride = (int64_t)pool->block_size * pool->num_kv_heads * pool->head_dim;
+  a.num_seqs = num_seqs;
   a.num_blocks = pool->num_blocks;
   a.max_context = max_context_len;
   a.max_blocks_per_seq = max_blocks_per_seq;
@@ -185,7 +200,7 @@ int pa_decode(pa_pool *pool, void *out, const void *query, const int32_t *block_
   const int nchunk = choice.kernel == pa::DecodeKernel::kMfma
                          ? 1
                          : (group + choice.heads_per_pass - 1) / choice.heads_per_pass;
-  if ((int64_t)pool->num_kv_heads * nchunk > 65535) return PA_ERR_UNSUPPORTED;
+  if ((int64_t)pool->num_kv_heads * nchunk > INT32_MAX) return PA_ERR_UNSUPPORTED;
   return pa::hip_status(pa::launch_decode(a, pool->dtype, pool->head_dim, ring != nullptr, choice,
                                           num_seqs, static_cast<hipStream_t>(stream)));
 }

@@ -29,6 +29,8 @@
 //    decode_reduce combines them.
 //  * The summation order depends only on logical positions and lengths, so
 //    outputs are bit-identical under relabelling of physical blocks.
+#include <algorithm>
+
 #include "device_common.h"
 #include "launch.h"
 
@@ -57,6 +59,62 @@ __device__ __forceinline__ int effective_len(const DecodeArgs &a, int n, bool ri
     len = len < cap ? len : cap;
   }
   return len > 0 ? len : 0;
+}
+
+// ---------------------------------------------------------------------------
+// Persistent schedule.  Work items are (sequence b, partition p, KV head g)
+// with g fastest, so the heads of one partition run side by side.  Every
+// work-group derives the item list itself from the device-resident lengths
+// (no host synchronisation): s_first[b] = index of the first (b, p) pair of
+// sequence b (an exclusive prefix sum of its partition counts; an empty
+// sequence still owns one pair, which writes zeros).  Work-groups then take
+// items round-robin.
+// ---------------------------------------------------------------------------
+constexpr int kMaxSchedSeqs = kMaxSchedSeqsHost;
+
+__device__ int build_schedule(const DecodeArgs &a, bool ring, int *s_first, int *s_wsum) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int P = a.partition_tokens;
+  int carry = 0;
+  for (int base = 0; base < a.num_seqs; base += kNW * kWave) {
+    const int b = base + tid;
+    int v = 0;
+    if (b < a.num_seqs) {
+      const int L = effective_len(a, a.context_lens[b], ring);
+      v = L > 0 ? (L + P - 1) / P : 1;
+    }
+    int x = v;  // inclusive scan within the wave
+#pragma unroll
+    for (int off = 1; off < kWave; off <<= 1) {
+      const int y = __shfl_up(x, off);
+      if (lane >= off) x += y;
+    }
+    if (lane == kWave - 1) s_wsum[wave] = x;
+    __syncthreads();
+    int woff = 0, tot = 0;
+#pragma unroll
+    for (int w = 0; w < kNW; ++w) {
+      woff += w < wave ? s_wsum[w] : 0;
+      tot += s_wsum[w];
+    }
+    if (b < a.num_seqs) s_first[b] = carry + woff + x - v;
+    carry += tot;
+    __syncthreads();
+  }
+  if (tid == 0) s_first[a.num_seqs] = carry;
+  __syncthreads();
+  return carry;
+}
+
+// Sequence owning pair index bp (s_first is strictly increasing).
+__device__ __forceinline__ int find_seq(const int *s_first, int num_seqs, int bp) {
+  int lo = 0, hi = num_seqs;
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (s_first[mid] <= bp) lo = mid;
+    else hi = mid;
+  }
+  return lo;
 }
 
 // Physical block ids of one partition, staged once per wave in a VGPR:
@@ -100,7 +158,8 @@ template <class T, int D, int HMAX>
 __device__ __forceinline__ void finish_partition(const DecodeArgs &a, const float (*s_m)[HMAX],
                                                  const float (*s_l)[HMAX],
                                                  const float (*s_o)[HMAX][D], int nheads,
-                                                 int hq0, int b, int p, int parts) {
+                                                 int hq0, int b, int p, int parts,
+                                                 int wave_stride_bytes = HMAX * D * 4) {
   typedef typename T::storage st;
   for (int idx = threadIdx.x; idx < nheads * D; idx += blockDim.x) {
     const int h = idx / D;
@@ -113,7 +172,8 @@ __device__ __forceinline__ void finish_partition(const DecodeArgs &a, const floa
     for (int w = 0; w < kNW; ++w) {
       const float mw = s_m[w][h];
       const float wt = mw == -INFINITY ? 0.f : fast_exp2(mw - mx);
-      num += wt * s_o[w][h][d];
+      num += wt * reinterpret_cast<const float(*)[D]>(reinterpret_cast<const char *>(s_o) +
+                                                         w * wave_stride_bytes)[h][d];
       den += wt * s_l[w][h];
     }
     const int64_t head = (int64_t)b * a.num_q_heads + hq0 + h;
@@ -199,97 +259,207 @@ struct VChunk<64> {
 // ---------------------------------------------------------------------------
 // MFMA kernel: 16-bit K/V, GQA group G in [1, 16] (used for G >= 4).
 //
+// Work split (stream-K over tiles).  The batch is the flattened list of
+// (sequence b, 16-token tile t), T tiles in all.  Resident waves form groups
+// of Hkv consecutive waves; wave gw streams KV head gw % Hkv over the tile
+// range of its group gw / Hkv, ceil(T / groups) tiles.  So all waves carry
+// the same number of tiles, and the Hkv heads of one tile (one contiguous
+// run of every token row) are read at the same time.  Each wave runs a
+// two-deep load pipeline straight across sequence boundaries: no per-item
+// prologue and no cross-wave barrier.  A sequence that starts and ends
+// inside one range writes its final output rows directly; a sequence cut
+// by a range boundary leaves a partial (running max, sum and normalised
+// output) in slot (group + b) * Hkv + g, and decode_streamk_reduce combines
+// the partials.
+//
 // Scores: S[token][head] = K_tile[16 x D] . Q^T[D x 16] with
 //   v_mfma_f32_16x16x32_{bf16,f16}; A = K rows (lane: token row16, 8 dims),
 //   B = query (lane: head row16, the same 8 dims), so each lane's 16-byte K
 //   load is its A fragment.  Lane l receives S[4*(l/16) + j][l % 16].
 // Output: O[head][d] += P[head][token] V[token][d] with
-//   v_mfma_f32_16x16x16_{bf16,f16}.  V rows are d-contiguous, so instead of
-//   transposing V the contraction index k = (token group, slot) carries
-//   one token per lane group and P is placed in one of the four slots
-//   (zeros elsewhere): MFMA e accumulates O[head][EV*(l%16) + e] from the
-//   lane's own 16-byte V load, and its A operand is the lane's own score
-//   output.  No LDS traffic and no shuffles in the inner loop.
+//   v_mfma_f32_16x16x16_{bf16,f16}.  The A operand is the lane's own score
+//   output (head l%16, tokens 4*(l/16)..+3); V passes through a per-wave LDS
+//   tile and comes back as B operands through transposing LDS reads.
 // ---------------------------------------------------------------------------
+constexpr int kMaxPersistentWaves = kMaxPersistentWavesHost;
+
+// Per-wave LDS tile for V: row-major, rows padded so that the transposing
+// reads of one instruction spread over all banks.
+template <int D>
+struct MfmaLds {
+  static constexpr int kVRowBytes = D * 2 + 32;
+  static constexpr int kVBytes = kTileTokens * kVRowBytes;
+};
+
+// Tile schedule shared by a work-group: s_tfirst[b] = tiles of sequences
+// before b (exclusive prefix of ceil(L_b / 16)), s_len[b] = L_b.  Work-group
+// 0 also publishes s_tfirst to the workspace for the reduce kernel.
+__device__ int build_tile_schedule(const DecodeArgs &a, bool ring, int *s_tfirst, int *s_len,
+                                   int *s_wsum) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  int carry = 0;
+  for (int base = 0; base < a.num_seqs; base += kNW * kWave) {
+    const int b = base + tid;
+    int v = 0;
+    if (b < a.num_seqs) {
+      const int L = effective_len(a, a.context_lens[b], ring);
+      s_len[b] = L;
+      v = (L + kTileTokens - 1) / kTileTokens;
+    }
+    int x = v;
+#pragma unroll
+    for (int off = 1; off < kWave; off <<= 1) {
+      const int y = __shfl_up(x, off);
+      if (lane >= off) x += y;
+    }
+    if (lane == kWave - 1) s_wsum[wave] = x;
+    __syncthreads();
+    int woff = 0, tot = 0;
+#pragma unroll
+    for (int w = 0; w < kNW; ++w) {
+      woff += w < wave ? s_wsum[w] : 0;
+      tot += s_wsum[w];
+    }
+    if (b < a.num_seqs) s_tfirst[b] = carry + woff + x - v;
+    carry += tot;
+    __syncthreads();
+  }
+  if (tid == 0) s_tfirst[a.num_seqs] = carry;
+  __syncthreads();
+  if (blockIdx.x == 0)
+    for (int b = tid; b <= a.num_seqs; b += blockDim.x) a.ws_sched[b] = s_tfirst[b];
+  return carry;
+}
+
+// (b, t) of flattened tile y (y < s_tfirst[num_seqs]).
+__device__ __forceinline__ void locate_tile(const int *s_tfirst, int num_seqs, int y, int &b,
+                                            int &t, int &tiles) {
+  int lo = 0, hi = num_seqs;  // largest b with s_tfirst[b] <= y (it has tiles)
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (s_tfirst[mid] <= y) lo = mid;
+    else hi = mid;
+  }
+  b = lo;
+  tiles = s_tfirst[b + 1] - s_tfirst[b];
+  t = y - s_tfirst[b];
+}
+
 template <class T, int D, bool RING>
 __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a) {
   constexpr int KB = D / 32;  // score MFMAs per tile
   constexpr int EV = D / 16;  // V elements per lane per row
+  constexpr int NB = D / 16;  // output MFMAs per tile (16 dims each)
+  constexpr int kVRow = MfmaLds<D>::kVRowBytes;
   typedef typename T::storage st;
   typedef typename VChunk<D>::type vchunk;
 
-  const int p = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
-  const int n = a.context_lens[b];
-  const int L = effective_len(a, n, RING);
-  const int P = a.partition_tokens;
-  const int parts = L > 0 ? (L + P - 1) / P : 1;
-  if (p >= parts) return;
+  __shared__ int s_tfirst[kMaxSchedSeqs + 1];
+  __shared__ int s_len[kMaxSchedSeqs];
+  __shared__ int s_wsum[kNW];
+  __shared__ __align__(16) char s_vtiles[kNW][MfmaLds<D>::kVBytes];
+
+  const int total = build_tile_schedule(a, RING, s_tfirst, s_len, s_wsum);
+  const int hkv = a.num_kv_heads;
   const int G = a.group;
-  const int hq0 = g * G;
-  if (L == 0) {
-    zero_rows<T, D>(a, b, hq0, G);
-    return;
-  }
   const int lane = threadIdx.x & 63;
-  // wave-uniform (SGPR) so tile indices and block ids stay on the scalar path
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int row16 = lane & 15, grp = lane >> 4;
-  const int begin = p * P;
-  const int end = min(L, begin + P);
-  const int ntiles = (end - begin + kTileTokens - 1) / kTileTokens;
+  const int groups = (gridDim.x * kNW) / hkv;
+  const int gw = blockIdx.x * kNW + wave;
+  const int grp_id = gw / hkv;  // tile range of this wave
+  const int g = gw - grp_id * hkv;  // KV head of this wave
+  if (grp_id >= groups) return;
+  const int per = (total + groups - 1) / groups;
+  const int xbeg = grp_id * per;
+  const int xend = min(total, xbeg + per);
+  if (xbeg >= xend) return;  // no barriers follow
+  const int hq0 = g * G;
+  const int64_t head_off = (int64_t)g * D;
 
-  // Query fragment: head row16 of the group, dims 32kb + 8grp + [0, 8).
-  uint4 qf[KB];
-  const bool head_ok = row16 < G;
-  {
-    const st *qrow =
-        static_cast<const st *>(a.query) + ((int64_t)b * a.num_q_heads + hq0 + (head_ok ? row16 : 0)) * D;
-#pragma unroll
-    for (int kb = 0; kb < KB; ++kb)
-      qf[kb] = head_ok ? *reinterpret_cast<const uint4 *>(qrow + 32 * kb + 8 * grp) : make_uint4(0, 0, 0, 0);
-    if constexpr (RING) rope_frag16<T, KB>(qf, a.rope + (int64_t)(L - 1) * D, grp);
-  }
-
-  const int64_t row_stride = (int64_t)a.num_kv_heads * D;  // elements between token rows
-  const int32_t *bt = a.block_tables + (int64_t)b * a.max_blocks_per_seq;
-  const char *kc = static_cast<const char *>(a.k_cache) + (int64_t)g * D * sizeof(st);
-  const char *vc = static_cast<const char *>(a.v_cache) + (int64_t)g * D * sizeof(st);
+  const int64_t row_stride = (int64_t)hkv * D;  // elements between token rows
   const int bmask = (1 << a.block_shift) - 1;
-
-  f32x4 acc[EV];
-#pragma unroll
-  for (int e = 0; e < EV; ++e) acc[e] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m_run = -INFINITY;
-  float l_part = 0.f;
-
-  // Per-lane byte offsets inside a tile (K: token row16, dims 8grp..+8 of
-  // each 32-dim chunk; V: token 4grp+tau, dims EV*row16..+EV).
+  char *vt = s_vtiles[wave];
   const int k_off = (int)((row16 * row_stride + 8 * grp) * sizeof(st));
   int v_off[4];
 #pragma unroll
   for (int tau = 0; tau < 4; ++tau)
     v_off[tau] = (int)(((4 * grp + tau) * row_stride + EV * row16) * sizeof(st));
 
-  const PartitionBlocks blocks(a, bt, begin, end);
-  auto load_tile = [&](int t, uint4 (&k)[KB], vchunk (&v)[4]) {
-    const int r0 = begin + kTileTokens * min(t, ntiles - 1);
-    const int valid = t < ntiles ? min(kTileTokens, end - r0) : 0;
-    const int phys = blocks.of_token(r0);
-    const auto kr = tile_rsrc<D, st>(a, kc, phys, r0 & bmask, valid, row_stride);
-    const auto vr = tile_rsrc<D, st>(a, vc, phys, r0 & bmask, valid, row_stride);
+  // online-softmax state of the current (b, g) segment
+  f32x4 acc[NB];
+  float m_run = -INFINITY, l_part = 0.f;
+  uint4 qf[KB];
+  bool seg_whole = false;  // the segment began at tile 0 of its (b, g)
+
+  // Per-lane staged metadata of a chunk of up to 64 tiles: lane i describes
+  // tile c0 + i.  Read back with readlane (wave-uniform SGPR values).
+  int tb = 0, tt = 0, tphys = 0, tvalid = 0, tflag = 0;
+  int c0 = 0, cnt = 0;
+  auto stage = [&](int start) {
+    c0 = start;
+    cnt = min(kWave, xend - start);
+    tb = tt = tphys = tvalid = tflag = 0;
+    if (lane < cnt) {
+      int tiles;
+      locate_tile(s_tfirst, a.num_seqs, c0 + lane, tb, tt, tiles);
+      const int L = s_len[tb];
+      tvalid = min(kTileTokens, L - kTileTokens * tt);
+      const int r0 = kTileTokens * tt;
+      const int phys = a.block_tables[(int64_t)tb * a.max_blocks_per_seq + (r0 >> a.block_shift)];
+      tphys = min(max(phys, 0), a.num_blocks - 1);
+      tflag = (tt == 0 ? 1 : 0) | (tt == tiles - 1 ? 2 : 0);
+    }
+  };
+  auto rd = [&](int v, int j) { return __builtin_amdgcn_readlane(v, j); };
+
+  // Loads of staged tile j (j >= cnt: an empty tile, no memory access).
+  auto load_tile = [&](int j, uint4 (&k)[KB], vchunk (&v)[4]) {
+    const int jj = min(j, kWave - 1);
+    const int t = rd(tt, jj), phys = rd(tphys, jj);
+    const int valid = j < cnt ? rd(tvalid, jj) : 0;
+    const int r0 = kTileTokens * t;
+    const auto kr = tile_rsrc<D, st>(a, static_cast<const char *>(a.k_cache) + head_off * sizeof(st),
+                                     phys, r0 & bmask, valid, row_stride);
+    const auto vr = tile_rsrc<D, st>(a, static_cast<const char *>(a.v_cache) + head_off * sizeof(st),
+                                     phys, r0 & bmask, valid, row_stride);
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) k[kb] = buffer_load16(kr, k_off + 64 * kb);
 #pragma unroll
     for (int tau = 0; tau < 4; ++tau) v[tau] = VChunk<D>::load(vr, v_off[tau]);
   };
 
-  auto process_tile = [&](int t, uint4 (&kf)[KB], vchunk (&vf)[4]) {
-    const int r0 = begin + kTileTokens * t;
-    const int valid = end - r0;  // <= 0 for a tile past the partition
+  // Segment start: query fragment of (b, g) (issued before the next tile's
+  // loads so that the wait counts are the same whether or not it happens).
+  auto begin_segment = [&](int b, bool whole) {
+    const bool head_ok = row16 < G;
+    const st *qrow = static_cast<const st *>(a.query) +
+                     ((int64_t)b * a.num_q_heads + hq0 + (head_ok ? row16 : 0)) * D;
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) {  // unconditional load, then zero padded heads
+      const uint4 raw = *reinterpret_cast<const uint4 *>(qrow + 32 * kb + 8 * grp);
+      qf[kb] = make_uint4(head_ok ? raw.x : 0u, head_ok ? raw.y : 0u, head_ok ? raw.z : 0u,
+                          head_ok ? raw.w : 0u);
+    }
+    if constexpr (RING) rope_frag16<T, KB>(qf, a.rope + (int64_t)(s_len[b] - 1) * D, grp);
+    m_run = -INFINITY;
+    l_part = 0.f;
+#pragma unroll
+    for (int e = 0; e < NB; ++e) acc[e] = f32x4{0.f, 0.f, 0.f, 0.f};
+    seg_whole = whole;
+  };
+
+  auto process_tile = [&](int j, uint4 (&kf)[KB], vchunk (&vf)[4]) {
+    const int jj = min(j, kWave - 1);
+    const int valid = j < cnt ? rd(tvalid, jj) : 0;
     if constexpr (RING) {
-      const int r = r0 + row16;
-      const int j = r < L ? ring_cache_index(r, n, a.ring_sink, a.ring_window) : 0;
-      rope_frag16<T, KB>(kf, a.rope + (int64_t)j * D, grp);
+      // keys are stored un-rotated: rotate each by its cache-order index
+      const int b = rd(tb, jj), t = rd(tt, jj);
+      const int L = s_len[b];
+      const int n = a.context_lens[b];
+      const int r = kTileTokens * t + row16;
+      const int jc = (j < cnt && r < L) ? ring_cache_index(r, n, a.ring_sink, a.ring_window) : 0;
+      rope_frag16<T, KB>(kf, a.rope + (int64_t)jc * D, grp);
     }
     f32x4 s = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -297,7 +467,7 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a) {
 
     float sc[4];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) sc[j] = (4 * grp + j < valid) ? s[j] * a.scale_log2 : -INFINITY;
+    for (int r = 0; r < 4; ++r) sc[r] = (4 * grp + r < valid) ? s[r] * a.scale_log2 : -INFINITY;
     const float lmax = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
     if (__any(lmax > m_run + kRescaleSlack)) {
       float tmax = fmaxf(lmax, __shfl_xor(lmax, 16));
@@ -307,66 +477,177 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a) {
       l_part *= alpha;
       float ah[4];
 #pragma unroll
-      for (int jj = 0; jj < 4; ++jj) ah[jj] = __shfl(alpha, 4 * grp + jj);
+      for (int r = 0; r < 4; ++r) ah[r] = __shfl(alpha, 4 * grp + r);
 #pragma unroll
-      for (int e = 0; e < EV; ++e)
+      for (int e = 0; e < NB; ++e)
 #pragma unroll
-        for (int jj = 0; jj < 4; ++jj) acc[e][jj] *= ah[jj];
+        for (int r = 0; r < 4; ++r) acc[e][r] *= ah[r];
       m_run = m_new;
     }
+    // (an empty tile right after a reset sees m_run = -inf; keep exp2 finite)
+    const float m_ref = m_run == -INFINITY ? 0.f : m_run;
     float pj[4];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) pj[j] = fast_exp2(sc[j] - m_run);
+    for (int r = 0; r < 4; ++r) pj[r] = fast_exp2(sc[r] - m_ref);
     l_part += (pj[0] + pj[1]) + (pj[2] + pj[3]);
 
-    // V rows past the context were loaded as zeros (out of the descriptor's
+    // V rows past the context were loaded as zeros (outside the descriptor
     // range), so a zero weight never meets a NaN sentinel.
 #pragma unroll
-    for (int tau = 0; tau < 4; ++tau) {
-      const uint32_t x = T::from_float(pj[tau]);
-      const uint32_t y = x << 16;
-      const uint2 op[4] = {make_uint2(x, 0u), make_uint2(y, 0u), make_uint2(0u, x), make_uint2(0u, y)};
+    for (int tau = 0; tau < 4; ++tau)
+      *reinterpret_cast<vchunk *>(vt + (4 * grp + tau) * kVRow + sizeof(vchunk) * row16) = vf[tau];
+    const uint2 pa = make_uint2(pack2(T::from_float(pj[0]), T::from_float(pj[1])),
+                                pack2(T::from_float(pj[2]), T::from_float(pj[3])));
+    const char *vr = vt + (4 * grp + (row16 >> 2)) * kVRow + 8 * (row16 & 3);
 #pragma unroll
-      for (int e = 0; e < EV; ++e)
-        acc[e] = T::mfma_16x16x16(op[e & 3], VChunk<D>::half(vf[tau], e >> 2), acc[e]);
+    for (int jb = 0; jb < NB; ++jb)
+      acc[jb] = T::mfma_16x16x16(pa, lds_read_tr16_b64(vr + 32 * jb), acc[jb]);
+  };
+
+  // Segment end: final rows if the whole sequence was streamed here, else a
+  // partial in workspace slot (group + b) * Hkv + g.
+  auto end_segment = [&](int b, bool last_of_pair) {
+    float l_tot = l_part + __shfl_xor(l_part, 16);
+    l_tot += __shfl_xor(l_tot, 32);  // sum over the tile for head row16
+    float lh[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) lh[r] = __shfl(l_tot, 4 * grp + r);
+    if (seg_whole && last_of_pair) {
+      st *out = static_cast<st *>(a.out) + ((int64_t)b * a.num_q_heads + hq0) * D;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int h = 4 * grp + r;
+        if (h < G) {
+          const float inv = 1.f / lh[r];
+#pragma unroll
+          for (int e = 0; e < NB; ++e) out[h * D + 16 * e + row16] = T::from_float(acc[e][r] * inv);
+        }
+      }
+    } else {
+      const int64_t slot = ((int64_t)grp_id + b) * hkv + g;
+      float *po = a.ws_o + slot * G * D;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int h = 4 * grp + r;
+        if (h < G) {
+          const float inv = 1.f / lh[r];
+#pragma unroll
+          for (int e = 0; e < NB; ++e) po[h * D + 16 * e + row16] = acc[e][r] * inv;
+        }
+      }
+      if (grp == 0 && row16 < G) {
+        a.ws_ml[(slot * G + row16) * 2] = m_run;
+        a.ws_ml[(slot * G + row16) * 2 + 1] = l_tot;
+      }
     }
   };
 
-  // Two register sets in ping-pong: while one tile is consumed the next
-  // one's loads are in flight, with no register copies and no branches
-  // around loads (so the hardware wait counts stay exact).  A tile past the
-  // partition loads nothing and contributes nothing.
+  // One pipeline step: tile j (registers ka/va) is consumed while tile j+1
+  // loads into kb/vb.
+  auto step = [&](int j, uint4 (&kc)[KB], vchunk (&vc)[4], uint4 (&kn)[KB], vchunk (&vn)[4]) {
+    const int jj = min(j, kWave - 1);
+    const bool real = j < cnt;
+    const int b = rd(tb, jj), flag = rd(tflag, jj);
+    if (real && (flag & 1)) begin_segment(b, true);
+    load_tile(j + 1, kn, vn);
+    process_tile(j, kc, vc);
+    const bool last = c0 + j == xend - 1;
+    if (real && ((flag & 2) || last)) end_segment(b, (flag & 2) != 0);
+  };
+
   uint4 ka[KB], kb2[KB];
   vchunk va[4], vb[4];
-  if (wave < ntiles) {
-    load_tile(wave, ka, va);
-    for (int t = wave; t < ntiles; t += 2 * kNW) {
-      load_tile(t + kNW, kb2, vb);
-      process_tile(t, ka, va);
-      load_tile(t + 2 * kNW, ka, va);
-      process_tile(t + kNW, kb2, vb);
+  for (int start = xbeg; start < xend; start += kWave) {
+    stage(start);
+    if (start == xbeg && !(rd(tflag, 0) & 1))  // the range begins inside a sequence
+      begin_segment(rd(tb, 0), false);
+    load_tile(0, ka, va);
+    for (int j = 0; j < cnt; j += 2) {
+      step(j, ka, va, kb2, vb);
+      step(j + 1, kb2, vb, ka, va);
     }
   }
+}
 
-  float l_tot = l_part + __shfl_xor(l_part, 16);
-  l_tot += __shfl_xor(l_tot, 32);
-
-  __shared__ float s_m[kNW][16];
-  __shared__ float s_l[kNW][16];
-  __shared__ float s_o[kNW][16][D];
-  if (grp == 0) {
-    s_m[wave][row16] = m_run;
-    s_l[wave][row16] = l_tot;
+// ---------------------------------------------------------------------------
+// Stream-K combine, one work-group per (KV head g, sequence b): the cut
+// segments of sequence b sit in slots (q + b) * Hkv + g for the groups q
+// whose tile ranges intersect its tiles.
+// out = sum_q l_q 2^(m_q - M) o_q / sum_q l_q 2^(m_q - M).  An empty
+// sequence gets zero rows; a sequence streamed by one group was written
+// directly and is skipped.
+// ---------------------------------------------------------------------------
+template <class T, int D>
+__global__ __launch_bounds__(256) void decode_streamk_reduce_kernel(DecodeArgs a, int groups) {
+  typedef typename T::storage st;
+  constexpr int DPL = D / kWave;  // output elements per lane
+  const int lane = threadIdx.x & 63;
+  const int h = blockIdx.x * kNW + (threadIdx.x >> 6);  // query head within the group
+  const int g = blockIdx.y, b = blockIdx.z;
+  const int hkv = a.num_kv_heads, G = a.group;
+  if (h >= G) return;
+  const int t0 = a.ws_sched[b], t1 = a.ws_sched[b + 1];
+  const int total = a.ws_sched[a.num_seqs];
+  st *out = static_cast<st *>(a.out) + ((int64_t)b * a.num_q_heads + g * G + h) * D + lane;
+  if (t1 == t0) {
+#pragma unroll
+    for (int k = 0; k < DPL; ++k) out[k * kWave] = T::from_float(0.f);
+    return;
   }
+  const int per = (total + groups - 1) / groups;
+  const int q_lo = t0 / per, q_hi = (t1 - 1) / per;
+  if (q_lo == q_hi) return;
+  const int nseg = q_hi - q_lo + 1;
+  const int64_t slot0 = ((int64_t)q_lo + b) * hkv + g;  // slot of segment s: slot0 + s * hkv
+  float num[DPL];
 #pragma unroll
-  for (int e = 0; e < EV; ++e)
-#pragma unroll
-    for (int jj = 0; jj < 4; ++jj) {
-      const int h = 4 * grp + jj;
-      if (h < G) s_o[wave][h][EV * row16 + e] = acc[e][jj];
+  for (int k = 0; k < DPL; ++k) num[k] = 0.f;
+  float den = 0.f, mx = -INFINITY;
+  for (int s0 = 0; s0 < nseg; s0 += kWave) {  // chunks of 64 segments, online rescale
+    const int cnt = min(kWave, nseg - s0);
+    float ms = -INFINITY, ls = 0.f;
+    if (lane < cnt) {
+      const int64_t slot = slot0 + (int64_t)(s0 + lane) * hkv;
+      ms = a.ws_ml[(slot * G + h) * 2];
+      ls = a.ws_ml[(slot * G + h) * 2 + 1];
     }
-  __syncthreads();
-  finish_partition<T, D, 16>(a, s_m, s_l, s_o, G, hq0, b, p, parts);
+    float cmx = ms;
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) cmx = fmaxf(cmx, __shfl_xor(cmx, off));
+    const float m_new = fmaxf(mx, cmx);
+    const float scale_old = mx == -INFINITY ? 0.f : fast_exp2(mx - m_new);
+    den *= scale_old;
+#pragma unroll
+    for (int k = 0; k < DPL; ++k) num[k] *= scale_old;
+    mx = m_new;
+    const float wq = lane < cnt ? ls * fast_exp2(ms - mx) : 0.f;
+    const float *rows = a.ws_o + ((slot0 + (int64_t)s0 * hkv) * G + h) * D + lane;
+    const int64_t rstride = (int64_t)hkv * G * D;
+    int j = 0;
+    for (; j + 8 <= cnt; j += 8) {  // 8 segments of loads in flight
+      float v[8][DPL];
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+#pragma unroll
+        for (int k = 0; k < DPL; ++k) v[u][k] = rows[(j + u) * rstride + k * kWave];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const float w = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wq), j + u));
+        den += w;
+#pragma unroll
+        for (int k = 0; k < DPL; ++k) num[k] = fmaf(w, v[u][k], num[k]);
+      }
+    }
+    for (; j < cnt; ++j) {
+      const float w = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wq), j));
+      den += w;
+#pragma unroll
+      for (int k = 0; k < DPL; ++k) num[k] = fmaf(w, rows[j * rstride + k * kWave], num[k]);
+    }
+  }
+  const float inv = 1.f / den;
+#pragma unroll
+  for (int k = 0; k < DPL; ++k) out[k * kWave] = T::from_float(num[k] * inv);
 }
 
 // ---------------------------------------------------------------------------
@@ -376,7 +657,9 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a) {
 // state; dot products reduce within the row group with DPP.
 // ---------------------------------------------------------------------------
 template <class T, int D, bool RING, int NH>
-__global__ __launch_bounds__(256) void decode_valu_kernel(DecodeArgs a) {
+__device__ __forceinline__ void valu_partition(const DecodeArgs &a, int b, int p, int gc,
+                                               float (*s_m)[NH], float (*s_l)[NH],
+                                               float (*s_o)[NH][D]) {
   typedef typename T::storage st;
   constexpr int EPL = 16 / T::kBytes;  // elements per lane
   constexpr int LPR = D / EPL;         // lanes per row
@@ -384,11 +667,10 @@ __global__ __launch_bounds__(256) void decode_valu_kernel(DecodeArgs a) {
   constexpr int STEPS = kTileTokens / RPW;
   static_assert(LPR >= 4 && LPR <= 32, "row split");
 
-  const int p = blockIdx.x, b = blockIdx.z;
   const int G = a.group;
   const int nchunk = (G + NH - 1) / NH;
-  const int g = blockIdx.y / nchunk;
-  const int c = blockIdx.y - g * nchunk;
+  const int g = gc / nchunk;
+  const int c = gc - g * nchunk;
   const int hq0 = g * G + c * NH;
   const int nh = min(NH, G - c * NH);
   const int n = a.context_lens[b];
@@ -537,9 +819,6 @@ __global__ __launch_bounds__(256) void decode_valu_kernel(DecodeArgs a) {
     }
   }
 
-  __shared__ float s_m[kNW][NH];
-  __shared__ float s_l[kNW][NH];
-  __shared__ float s_o[kNW][NH][D];
   if (rg == 0) {
 #pragma unroll
     for (int hh = 0; hh < NH; ++hh) {
@@ -555,16 +834,41 @@ __global__ __launch_bounds__(256) void decode_valu_kernel(DecodeArgs a) {
   finish_partition<T, D, NH>(a, s_m, s_l, s_o, nh, hq0, b, p, parts);
 }
 
+template <class T, int D, bool RING, int NH>
+__global__ __launch_bounds__(256) void decode_valu_kernel(DecodeArgs a) {
+  __shared__ int s_first[kMaxSchedSeqs + 1];
+  __shared__ int s_wsum[kNW];
+  __shared__ float s_m[kNW][NH];
+  __shared__ float s_l[kNW][NH];
+  __shared__ float s_o[kNW][NH][D];
+  const int nchunk = (a.group + NH - 1) / NH;
+  const int per_pair = a.num_kv_heads * nchunk;
+  const int pairs = build_schedule(a, RING, s_first, s_wsum);
+  const int items = pairs * per_pair;
+  for (int it = blockIdx.x; it < items; it += gridDim.x) {
+    const int bp = it / per_pair;
+    const int gc = it - bp * per_pair;
+    const int b = find_seq(s_first, a.num_seqs, bp);
+    valu_partition<T, D, RING, NH>(a, b, bp - s_first[b], gc, s_m, s_l, s_o);
+    __syncthreads();  // the next item reuses the merge buffers
+  }
+}
+
 // ---------------------------------------------------------------------------
 // Split-K combine: out = sum_p w_p o_p / sum_p w_p, w_p = l_p 2^(m_p - M).
-// One work-group per (query head, sequence); only multi-partition sequences.
+// One wave per (query head, sequence), four heads per work-group; only
+// multi-partition sequences.  Lanes load the partition weights in parallel;
+// the partial outputs are then streamed with independent loads.
 // ---------------------------------------------------------------------------
 template <class T, int D>
-__global__ __launch_bounds__(D) void decode_reduce_kernel(DecodeArgs a, int ring) {
+__global__ __launch_bounds__(256) void decode_reduce_kernel(DecodeArgs a, int ring) {
   typedef typename T::storage st;
-  const int h = blockIdx.x, b = blockIdx.y;
-  const int n = a.context_lens[b];
-  const int L = effective_len(a, n, ring != 0);
+  constexpr int DPL = D / kWave;  // output elements per lane
+  const int lane = threadIdx.x & 63;
+  const int h = blockIdx.x * kNW + (threadIdx.x >> 6);
+  const int b = blockIdx.y;
+  if (h >= a.num_q_heads) return;
+  const int L = effective_len(a, a.context_lens[b], ring != 0);
   const int P = a.partition_tokens;
   const int parts = min((L + P - 1) / P, a.max_parts);
   if (parts <= 1) return;
@@ -572,42 +876,91 @@ __global__ __launch_bounds__(D) void decode_reduce_kernel(DecodeArgs a, int ring
   const float *ml = a.ws_ml + head * a.max_parts * 2;
   const float *po = a.ws_o + head * a.max_parts * D;
   float mx = -INFINITY;
-  for (int q = 0; q < parts; ++q) mx = fmaxf(mx, ml[2 * q]);
-  const int d = threadIdx.x;
-  float num = 0.f, den = 0.f;
-  for (int q = 0; q < parts; ++q) {
-    const float w = ml[2 * q + 1] * fast_exp2(ml[2 * q] - mx);
-    num += w * po[(int64_t)q * D + d];
-    den += w;
+  for (int q = lane; q < parts; q += kWave) mx = fmaxf(mx, ml[2 * q]);
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
+  float num[DPL];
+#pragma unroll
+  for (int k = 0; k < DPL; ++k) num[k] = 0.f;
+  float den = 0.f;
+  for (int q0 = 0; q0 < parts; q0 += kWave) {
+    const int q = q0 + lane;
+    const float wq = q < parts ? ml[2 * q + 1] * fast_exp2(ml[2 * q] - mx) : 0.f;
+    const int cnt = min(kWave, parts - q0);
+#pragma unroll 8
+    for (int j = 0; j < cnt; ++j) {
+      const float w = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wq), j));
+      den += w;
+      const float *row = po + (int64_t)(q0 + j) * D + lane;
+#pragma unroll
+      for (int k = 0; k < DPL; ++k) num[k] = fmaf(w, row[k * kWave], num[k]);
+    }
   }
-  static_cast<st *>(a.out)[head * D + d] = T::from_float(num / den);
+  st *out = static_cast<st *>(a.out) + head * D + lane;
+#pragma unroll
+  for (int k = 0; k < DPL; ++k) out[k * kWave] = T::from_float(num[k] / den);
+}
+
+// Work-groups per CU the device can keep resident for a kernel, times the
+// CU count: the persistent grid.
+int persistent_grid(const void *kernel, int64_t max_items) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) dev = 0;
+  int cus = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+    cus = 256;
+  int per_cu = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, kNW * kWave, 0) != hipSuccess ||
+      per_cu <= 0)
+    per_cu = 1;
+  const int64_t g = (int64_t)cus * per_cu;
+  return (int)std::max<int64_t>(1, std::min<int64_t>(g, max_items));
 }
 
 template <class T, int D, bool RING>
-hipError_t launch_typed(const DecodeArgs &a, DecodeChoice choice, int num_seqs, hipStream_t stream) {
+hipError_t launch_typed(const DecodeArgs &a, DecodeChoice choice, hipStream_t stream) {
   const dim3 block(kNW * kWave);
-  bool launched = false;
   if constexpr (T::kBytes == 2) {
     if (choice.kernel == DecodeKernel::kMfma) {
-      const dim3 grid(a.max_parts, a.num_kv_heads, num_seqs);
-      hipLaunchKernelGGL((decode_mfma_kernel<T, D, RING>), grid, block, 0, stream, a);
-      launched = true;
+      static const int grid_max = std::min(
+          persistent_grid(reinterpret_cast<const void *>(&decode_mfma_kernel<T, D, RING>), INT32_MAX),
+          kMaxPersistentWaves / kNW);
+      // at least one group of Hkv waves
+      const int grid = std::max(grid_max, (a.num_kv_heads + kNW - 1) / kNW);
+      hipLaunchKernelGGL((decode_mfma_kernel<T, D, RING>), dim3(grid), block, 0, stream, a);
+      hipError_t err = hipGetLastError();
+      if (err != hipSuccess) return err;
+      hipLaunchKernelGGL((decode_streamk_reduce_kernel<T, D>),
+                         dim3((a.group + kNW - 1) / kNW, a.num_kv_heads, a.num_seqs), block, 0, stream,
+                         a, (grid * kNW) / a.num_kv_heads);
+      return hipGetLastError();
     }
   }
-  if (!launched) {
-    const int nchunk = (a.group + choice.heads_per_pass - 1) / choice.heads_per_pass;
-    const dim3 grid(a.max_parts, a.num_kv_heads * nchunk, num_seqs);
-    switch (choice.heads_per_pass) {
-      case 1: hipLaunchKernelGGL((decode_valu_kernel<T, D, RING, 1>), grid, block, 0, stream, a); break;
-      case 2: hipLaunchKernelGGL((decode_valu_kernel<T, D, RING, 2>), grid, block, 0, stream, a); break;
-      default: hipLaunchKernelGGL((decode_valu_kernel<T, D, RING, 4>), grid, block, 0, stream, a); break;
+  const int64_t pairs_bound = (int64_t)a.num_seqs * a.max_parts;
+  const int nchunk = (a.group + choice.heads_per_pass - 1) / choice.heads_per_pass;
+  const int64_t items = pairs_bound * a.num_kv_heads * nchunk;
+  switch (choice.heads_per_pass) {
+    case 1: {
+      static const int gmax = persistent_grid(reinterpret_cast<const void *>(&decode_valu_kernel<T, D, RING, 1>), INT32_MAX);
+      hipLaunchKernelGGL((decode_valu_kernel<T, D, RING, 1>), dim3((int)std::min<int64_t>(gmax, items)), block, 0, stream, a);
+      break;
+    }
+    case 2: {
+      static const int gmax = persistent_grid(reinterpret_cast<const void *>(&decode_valu_kernel<T, D, RING, 2>), INT32_MAX);
+      hipLaunchKernelGGL((decode_valu_kernel<T, D, RING, 2>), dim3((int)std::min<int64_t>(gmax, items)), block, 0, stream, a);
+      break;
+    }
+    default: {
+      static const int gmax = persistent_grid(reinterpret_cast<const void *>(&decode_valu_kernel<T, D, RING, 4>), INT32_MAX);
+      hipLaunchKernelGGL((decode_valu_kernel<T, D, RING, 4>), dim3((int)std::min<int64_t>(gmax, items)), block, 0, stream, a);
+      break;
     }
   }
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   if (a.max_parts > 1) {
-    const dim3 rgrid(a.num_q_heads, num_seqs);
-    hipLaunchKernelGGL((decode_reduce_kernel<T, D>), rgrid, dim3(D), 0, stream, a, RING ? 1 : 0);
+    const dim3 rgrid((a.num_q_heads + kNW - 1) / kNW, a.num_seqs);
+    hipLaunchKernelGGL((decode_reduce_kernel<T, D>), rgrid, block, 0, stream, a, RING ? 1 : 0);
     err = hipGetLastError();
   }
   return err;
@@ -615,25 +968,40 @@ hipError_t launch_typed(const DecodeArgs &a, DecodeChoice choice, int num_seqs, 
 
 template <class T>
 hipError_t launch_dtype(const DecodeArgs &a, int head_dim, bool ring, DecodeChoice choice,
-                        int num_seqs, hipStream_t stream) {
+                        hipStream_t stream) {
   if (head_dim == 128)
-    return ring ? launch_typed<T, 128, true>(a, choice, num_seqs, stream)
-                : launch_typed<T, 128, false>(a, choice, num_seqs, stream);
-  return ring ? launch_typed<T, 64, true>(a, choice, num_seqs, stream)
-              : launch_typed<T, 64, false>(a, choice, num_seqs, stream);
+    return ring ? launch_typed<T, 128, true>(a, choice, stream)
+                : launch_typed<T, 128, false>(a, choice, stream);
+  return ring ? launch_typed<T, 64, true>(a, choice, stream)
+              : launch_typed<T, 64, false>(a, choice, stream);
 }
 
 }  // namespace
 
-hipError_t launch_decode(const DecodeArgs &a, pa_dtype dtype, int head_dim, bool ring,
+hipError_t launch_decode(const DecodeArgs &args, pa_dtype dtype, int head_dim, bool ring,
                          DecodeChoice choice, int num_seqs, hipStream_t stream) {
-  switch (dtype) {
-    case PA_F16: return launch_dtype<F16>(a, head_dim, ring, choice, num_seqs, stream);
-    case PA_BF16: return launch_dtype<BF16>(a, head_dim, ring, choice, num_seqs, stream);
-    default: break;
+  if (dtype == PA_F32) choice.kernel = DecodeKernel::kValu;  // no fp32 MFMA kernel
+  // The device-side schedule holds up to kMaxSchedSeqs sequences; larger
+  // batches run as consecutive slices on the same stream (each slice reuses
+  // the workspace).
+  const size_t esz = dtype == PA_F32 ? 4 : 2;
+  for (int s0 = 0; s0 < num_seqs; s0 += kMaxSchedSeqs) {
+    DecodeArgs a = args;
+    a.num_seqs = std::min(kMaxSchedSeqs, num_seqs - s0);
+    const int64_t qo = (int64_t)s0 * a.num_q_heads * head_dim;
+    a.out = static_cast<char *>(args.out) + qo * esz;
+    a.query = static_cast<const char *>(args.query) + qo * esz;
+    a.block_tables = args.block_tables + (int64_t)s0 * a.max_blocks_per_seq;
+    a.context_lens = args.context_lens + s0;
+    hipError_t err;
+    switch (dtype) {
+      case PA_F16: err = launch_dtype<F16>(a, head_dim, ring, choice, stream); break;
+      case PA_BF16: err = launch_dtype<BF16>(a, head_dim, ring, choice, stream); break;
+      default: err = launch_dtype<F32>(a, head_dim, ring, choice, stream); break;
+    }
+    if (err != hipSuccess) return err;
   }
-  choice.kernel = DecodeKernel::kValu;  // fp32 always takes the VALU kernel
-  return launch_dtype<F32>(a, head_dim, ring, choice, num_seqs, stream);
+  return hipSuccess;
 }
 
 }  // namespace pa

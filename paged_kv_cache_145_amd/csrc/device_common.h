@@ -106,6 +106,21 @@ __device__ __forceinline__ float group_sum(float x) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// ------------------------------------------------------------- LDS ------
+// gfx950 transposing LDS read of 16-bit data.  Within each group of 16
+// lanes, lane i receives element (i % 4) of the 8 bytes that lanes
+// 4k + i / 4 (k = 0..3) address, i.e. result[i][k] = supplied[4k + i/4][i%4].
+// Reading a row-major [token][d] tile with lane s addressing row
+// (4 g + s / 4), column (n0 + 4 (s % 4)) therefore yields, in lane i, the
+// four consecutive tokens 4 g .. 4 g + 3 of column n0 + i.
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint2 lds_read_tr16_b64(const void *lds_addr) {
+  typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+  const s16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (lds_s16x4 *)(__attribute__((address_space(3))) char *)(uintptr_t)lds_addr);
+  return __builtin_bit_cast(uint2, r);
+}
+
 // ------------------------------------------------------- buffer loads ---
 // Raw (untyped) buffer descriptor word 3 for gfx9-family parts: 32-bit
 // data format, no swizzle.  Loads whose byte offset falls outside the

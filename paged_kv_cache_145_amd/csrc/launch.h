@@ -23,10 +23,14 @@ struct DecodeArgs {
   const void *v_cache;
   const int32_t *block_tables;
   const int32_t *context_lens;
-  float *ws_o;   // [B][Hq][max_parts][D]   partition-normalised outputs
-  float *ws_ml;  // [B][Hq][max_parts][2]   (running max in log2 units, sum)
+  // split-K partials.  MFMA kernel: slots [waves + B * Hkv][G][D] and
+  // [..][G][2]; VALU kernel: [B][Hq][max_parts][D] and [..][2].
+  float *ws_o;   // partition-normalised outputs
+  float *ws_ml;  // (running max in log2 units, sum)
+  int32_t *ws_sched;  // MFMA kernel: tile prefix per sequence [B + 1]
   const float *rope;  // float2 [S+W][D/2] or null
   int64_t kv_block_stride;  // elements per physical block (block_size * Hkv * D)
+  int32_t num_seqs;    // sequences of this launch (at most the schedule capacity)
   int32_t num_blocks;
   int32_t max_context;  // host bound of context_lens (lengths are clamped to it)
   int32_t max_blocks_per_seq;
@@ -42,6 +46,10 @@ struct DecodeArgs {
 };
 
 enum class DecodeKernel { kMfma, kValu };
+
+// Upper bounds the host uses to size the workspace.
+constexpr int kMaxSchedSeqsHost = 1024;      // sequences per launch slice
+constexpr int kMaxPersistentWavesHost = 8192;  // waves of the stream-K grid
 
 struct DecodeChoice {
   DecodeKernel kernel;

@@ -209,7 +209,10 @@ def test_decode_and_write_argument_validation(lib):
     assert lib.pa_decode(h, dev, dev, dev, 256, dev, 2, 4, 4096, 0.1, None, None, 0, None) == -2
     assert lib.pa_decode(h, dev, dev, dev, 256, dev, 2, 4, 4096, 0.1, None, dev, need - 1, None) == -2
     # short context fits one partition: no workspace needed
+    # group 2 (VALU kernel): a context inside one partition needs no workspace
     assert lib.pa_decode_workspace_bytes(h, 2, 4, 100, None) == 0
+    # group 8 (MFMA kernel, stream-K): partial slots are always reserved
+    assert lib.pa_decode_workspace_bytes(h, 2, 16, 100, None) > 0
     # zero sequences is a no-op
     assert lib.pa_decode(h, None, None, None, 4, None, 0, 4, 10, 0.1, None, None, 0, None) == 0
     # writes
