@@ -282,6 +282,10 @@ struct VChunk<64> {
 //   tile and comes back as B operands through transposing LDS reads.
 // ---------------------------------------------------------------------------
 constexpr int kMaxPersistentWaves = kMaxPersistentWavesHost;
+// Depth of the per-wave tile pipeline (tiles in flight + the one consumed).
+constexpr int kStages = 4;
+// Segment-opening tiles per staged chunk (query fragments kept in LDS).
+constexpr int kQSlots = 4;
 
 // Per-wave LDS tile for V: row-major, rows padded so that the transposing
 // reads of one instruction spread over all banks.
@@ -346,7 +350,8 @@ __device__ __forceinline__ void locate_tile(const int *s_tfirst, int num_seqs, i
 }
 
 template <class T, int D, bool RING>
-__global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void decode_mfma_kernel(DecodeArgs a) {
   constexpr int KB = D / 32;  // score MFMAs per tile
   constexpr int EV = D / 16;  // V elements per lane per row
   constexpr int NB = D / 16;  // output MFMAs per tile (16 dims each)
@@ -358,6 +363,7 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a) {
   __shared__ int s_len[kMaxSchedSeqs];
   __shared__ int s_wsum[kNW];
   __shared__ __align__(16) char s_vtiles[kNW][MfmaLds<D>::kVBytes];
+  __shared__ uint4 s_q[kNW][kQSlots * KB * kWave];  // query fragments, lane-major
 
   const int total = build_tile_schedule(a, RING, s_tfirst, s_len, s_wsum);
   const int hkv = a.num_kv_heads;
@@ -380,7 +386,9 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a) {
   const int64_t row_stride = (int64_t)hkv * D;  // elements between token rows
   const int bmask = (1 << a.block_shift) - 1;
   char *vt = s_vtiles[wave];
+  uint4 *qs = s_q[wave];
   const int k_off = (int)((row16 * row_stride + 8 * grp) * sizeof(st));
+  const int q_off = (int)((row16 * D + 8 * grp) * sizeof(st));
   int v_off[4];
 #pragma unroll
   for (int tau = 0; tau < 4; ++tau)
@@ -394,12 +402,15 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a) {
 
   // Per-lane staged metadata of a chunk of up to 64 tiles: lane i describes
   // tile c0 + i.  Read back with readlane (wave-uniform SGPR values).
-  int tb = 0, tt = 0, tphys = 0, tvalid = 0, tflag = 0;
+  auto rd = [&](int v, int j) { return __builtin_amdgcn_readlane(v, j); };
+  // toff: byte offset of the tile's first row of head g from the pool base
+  // (the same for K and V); tnrec: bytes the tile's valid rows span.
+  int tb = 0, tt = 0, tvalid = 0, tflag = 0, toff_lo = 0, toff_hi = 0, tnrec = 0, tslot = 0;
   int c0 = 0, cnt = 0;
   auto stage = [&](int start) {
     c0 = start;
     cnt = min(kWave, xend - start);
-    tb = tt = tphys = tvalid = tflag = 0;
+    tb = tt = tvalid = tflag = toff_lo = toff_hi = tnrec = 0;
     if (lane < cnt) {
       int tiles;
       locate_tile(s_tfirst, a.num_seqs, c0 + lane, tb, tt, tiles);
@@ -407,40 +418,68 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a) {
       tvalid = min(kTileTokens, L - kTileTokens * tt);
       const int r0 = kTileTokens * tt;
       const int phys = a.block_tables[(int64_t)tb * a.max_blocks_per_seq + (r0 >> a.block_shift)];
-      tphys = min(max(phys, 0), a.num_blocks - 1);
+      const int64_t off = ((int64_t)min(max(phys, 0), a.num_blocks - 1) * a.kv_block_stride +
+                           (int64_t)(r0 & bmask) * row_stride + head_off) *
+                          (int64_t)sizeof(st);
+      toff_lo = (int)(uint32_t)off;
+      toff_hi = (int)(off >> 32);
+      tnrec = (int)(((tvalid - 1) * row_stride + D) * sizeof(st));  // tvalid >= 1 here
       tflag = (tt == 0 ? 1 : 0) | (tt == tiles - 1 ? 2 : 0);
     }
+    // Tiles that open a segment (first tile of a sequence, or the first
+    // tile of this wave's range) get a query slot in LDS; a chunk ends
+    // before its (kQSlots + 1)-th opening tile.
+    const bool opens = lane < cnt && ((tflag & 1) || c0 + lane == xbeg);
+    unsigned long long m = __ballot(opens);
+    if (__popcll(m) > kQSlots) {
+      unsigned long long r = m;
+      for (int i = 0; i < kQSlots; ++i) r &= r - 1;
+      cnt = __ffsll((long long)r) - 1;
+      m &= (1ull << cnt) - 1;
+    }
+    tslot = opens && lane < cnt ? __popcll(m & ((1ull << lane) - 1)) : 0;
+    // fetch the query fragments of the opening tiles (all loads first)
+    uint4 qtmp[kQSlots][KB];
+    unsigned long long mm = m;
+#pragma unroll
+    for (int s2 = 0; s2 < kQSlots; ++s2) {
+      const int i = mm ? __ffsll((long long)mm) - 1 : 0;
+      const int64_t qoff = ((int64_t)rd(tb, i) * a.num_q_heads + hq0) * D * (int64_t)sizeof(st);
+      // lanes of padded heads (row16 >= G) fall outside the record range
+      const auto qr = __builtin_amdgcn_make_buffer_rsrc(
+          const_cast<char *>(static_cast<const char *>(a.query) + qoff), (short)0,
+          mm ? G * D * (int)sizeof(st) : 0, kBufferWord3);
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) qtmp[s2][kb] = buffer_load16(qr, q_off + 64 * kb);
+      mm &= mm - 1;
+    }
+#pragma unroll
+    for (int s2 = 0; s2 < kQSlots; ++s2)
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) qs[(s2 * KB + kb) * kWave + lane] = qtmp[s2][kb];
   };
-  auto rd = [&](int v, int j) { return __builtin_amdgcn_readlane(v, j); };
 
   // Loads of staged tile j (j >= cnt: an empty tile, no memory access).
+  // They are unconditional so that every step has the same wait counts.
   auto load_tile = [&](int j, uint4 (&k)[KB], vchunk (&v)[4]) {
     const int jj = min(j, kWave - 1);
-    const int t = rd(tt, jj), phys = rd(tphys, jj);
-    const int valid = j < cnt ? rd(tvalid, jj) : 0;
-    const int r0 = kTileTokens * t;
-    const auto kr = tile_rsrc<D, st>(a, static_cast<const char *>(a.k_cache) + head_off * sizeof(st),
-                                     phys, r0 & bmask, valid, row_stride);
-    const auto vr = tile_rsrc<D, st>(a, static_cast<const char *>(a.v_cache) + head_off * sizeof(st),
-                                     phys, r0 & bmask, valid, row_stride);
+    const uint64_t off = ((uint64_t)(uint32_t)rd(toff_hi, jj) << 32) | (uint32_t)rd(toff_lo, jj);
+    const int nrec = j < cnt ? rd(tnrec, jj) : 0;
+    const auto kr = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<char *>(static_cast<const char *>(a.k_cache) + off), (short)0, nrec, kBufferWord3);
+    const auto vr = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<char *>(static_cast<const char *>(a.v_cache) + off), (short)0, nrec, kBufferWord3);
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) k[kb] = buffer_load16(kr, k_off + 64 * kb);
 #pragma unroll
     for (int tau = 0; tau < 4; ++tau) v[tau] = VChunk<D>::load(vr, v_off[tau]);
   };
 
-  // Segment start: query fragment of (b, g) (issued before the next tile's
-  // loads so that the wait counts are the same whether or not it happens).
-  auto begin_segment = [&](int b, bool whole) {
-    const bool head_ok = row16 < G;
-    const st *qrow = static_cast<const st *>(a.query) +
-                     ((int64_t)b * a.num_q_heads + hq0 + (head_ok ? row16 : 0)) * D;
+  // Segment start: the query fragment of the tile's sequence from its slot.
+  auto begin_segment = [&](int j, int b, bool whole) {
+    const int slot = rd(tslot, j);
 #pragma unroll
-    for (int kb = 0; kb < KB; ++kb) {  // unconditional load, then zero padded heads
-      const uint4 raw = *reinterpret_cast<const uint4 *>(qrow + 32 * kb + 8 * grp);
-      qf[kb] = make_uint4(head_ok ? raw.x : 0u, head_ok ? raw.y : 0u, head_ok ? raw.z : 0u,
-                          head_ok ? raw.w : 0u);
-    }
+    for (int kb = 0; kb < KB; ++kb) qf[kb] = qs[(slot * KB + kb) * kWave + lane];
     if constexpr (RING) rope_frag16<T, KB>(qf, a.rope + (int64_t)(s_len[b] - 1) * D, grp);
     m_run = -INFINITY;
     l_part = 0.f;
@@ -499,9 +538,13 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a) {
     const uint2 pa = make_uint2(pack2(T::from_float(pj[0]), T::from_float(pj[1])),
                                 pack2(T::from_float(pj[2]), T::from_float(pj[3])));
     const char *vr = vt + (4 * grp + (row16 >> 2)) * kVRow + 8 * (row16 & 3);
+    uint2 vtr[NB];
 #pragma unroll
-    for (int jb = 0; jb < NB; ++jb)
-      acc[jb] = T::mfma_16x16x16(pa, lds_read_tr16_b64(vr + 32 * jb), acc[jb]);
+    for (int jb = 0; jb < NB; ++jb) vtr[jb] = lds_read_tr16_b64(vr + 32 * jb);
+#pragma unroll
+    for (int jb = 0; jb < NB; ++jb) acc[jb] = T::mfma_16x16x16(pa, vtr[jb], acc[jb]);
+    __builtin_amdgcn_sched_group_barrier(0x100, NB, 0);  // all transposing reads first
+    __builtin_amdgcn_sched_group_barrier(0x008, NB, 0);  // then the MFMAs
   };
 
   // Segment end: final rows if the whole sequence was streamed here, else a
@@ -542,29 +585,30 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a) {
     }
   };
 
-  // One pipeline step: tile j (registers ka/va) is consumed while tile j+1
-  // loads into kb/vb.
+  // Pipeline of kStages register buffers: tile j is consumed from buffer
+  // j % kStages while tiles j+1 .. j+kStages-1 are in flight.
+  constexpr int S = kStages;
+  uint4 kbuf[S][KB];
+  vchunk vbuf[S][4];
   auto step = [&](int j, uint4 (&kc)[KB], vchunk (&vc)[4], uint4 (&kn)[KB], vchunk (&vn)[4]) {
-    const int jj = min(j, kWave - 1);
-    const bool real = j < cnt;
-    const int b = rd(tb, jj), flag = rd(tflag, jj);
-    if (real && (flag & 1)) begin_segment(b, true);
-    load_tile(j + 1, kn, vn);
-    process_tile(j, kc, vc);
-    const bool last = c0 + j == xend - 1;
-    if (real && ((flag & 2) || last)) end_segment(b, (flag & 2) != 0);
+    load_tile(j + S - 1, kn, vn);
+    if (j < cnt) {
+      const int b = rd(tb, j), flag = rd(tflag, j);
+      if ((flag & 1) || c0 + j == xbeg) begin_segment(j, b, (flag & 1) != 0);
+      process_tile(j, kc, vc);
+      const bool last = c0 + j == xend - 1;
+      if ((flag & 2) || last) end_segment(b, (flag & 2) != 0);
+    }
   };
 
-  uint4 ka[KB], kb2[KB];
-  vchunk va[4], vb[4];
-  for (int start = xbeg; start < xend; start += kWave) {
-    stage(start);
-    if (start == xbeg && !(rd(tflag, 0) & 1))  // the range begins inside a sequence
-      begin_segment(rd(tb, 0), false);
-    load_tile(0, ka, va);
-    for (int j = 0; j < cnt; j += 2) {
-      step(j, ka, va, kb2, vb);
-      step(j + 1, kb2, vb, ka, va);
+  for (int start = xbeg; start < xend; start += cnt) {
+    stage(start);  // sets cnt
+#pragma unroll
+    for (int u = 0; u < S - 1; ++u) load_tile(u, kbuf[u], vbuf[u]);
+    for (int j = 0; j < cnt; j += S) {
+#pragma unroll
+      for (int u = 0; u < S; ++u)
+        step(j + u, kbuf[u], vbuf[u], kbuf[(u + S - 1) % S], vbuf[(u + S - 1) % S]);
     }
   }
 }
@@ -901,9 +945,9 @@ __global__ __launch_bounds__(256) void decode_reduce_kernel(DecodeArgs a, int ri
   for (int k = 0; k < DPL; ++k) out[k * kWave] = T::from_float(num[k] / den);
 }
 
-// Work-groups per CU the device can keep resident for a kernel, times the
-// CU count: the persistent grid.
-int persistent_grid(const void *kernel, int64_t max_items) {
+// Work-groups per CU the device can keep resident for a kernel (at most
+// per_cu_cap), times the CU count: the persistent grid.
+int persistent_grid(const void *kernel, int per_cu_cap) {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) dev = 0;
   int cus = 0;
@@ -913,8 +957,7 @@ int persistent_grid(const void *kernel, int64_t max_items) {
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, kNW * kWave, 0) != hipSuccess ||
       per_cu <= 0)
     per_cu = 1;
-  const int64_t g = (int64_t)cus * per_cu;
-  return (int)std::max<int64_t>(1, std::min<int64_t>(g, max_items));
+  return cus * std::max(1, std::min(per_cu, per_cu_cap));
 }
 
 template <class T, int D, bool RING>
@@ -922,8 +965,11 @@ hipError_t launch_typed(const DecodeArgs &a, DecodeChoice choice, hipStream_t st
   const dim3 block(kNW * kWave);
   if constexpr (T::kBytes == 2) {
     if (choice.kernel == DecodeKernel::kMfma) {
+      // one work-group (one wave per SIMD) per CU: a lone wave per SIMD is
+      // never starved by an older neighbour, so equal tile counts finish
+      // at nearly equal times
       static const int grid_max = std::min(
-          persistent_grid(reinterpret_cast<const void *>(&decode_mfma_kernel<T, D, RING>), INT32_MAX),
+          persistent_grid(reinterpret_cast<const void *>(&decode_mfma_kernel<T, D, RING>), 1),
           kMaxPersistentWaves / kNW);
       // at least one group of Hkv waves
       const int grid = std::max(grid_max, (a.num_kv_heads + kNW - 1) / kNW);
