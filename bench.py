@@ -3,10 +3,11 @@
 
 One step = the whole hot path over one batch: the cache write of every
 sequence's newest token (pa_reshape_and_cache) followed by single-token
-paged decode attention (pa_decode: split-K partition kernel + reduce).
-Workload: the LLaMA-2-70B-shaped batch (B 64, Hq 64, Hkv 8, D 128, bf16,
-16-token blocks, mixed lengths 50..8000, shuffled physical blocks), seeded
-and synthetic, resident in HBM before the timed region starts.
+paged decode attention (pa_decode: stream-K kernel + combine kernel).
+Default workload: the LLaMA-2-70B-shaped batch (B 64, Hq 64, Hkv 8, D 128,
+bf16, 16-token blocks, mixed lengths 50..8000, shuffled physical blocks),
+seeded and synthetic, resident in HBM before the timed region starts;
+--config picks one of the other parity workloads instead.
 
 Prints one JSON line.  `value` is effective GB/s over the whole step
 (algorithmic bytes / step time); `roofline` reports the decode call against
@@ -31,6 +32,8 @@ if ROOT not in sys.path:
 HBM_PEAK_GBS = 8000.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_decode_llama70b_b64.json")
 KERNEL_SOURCES = ["decode_kernels.hip", "device_common.h", "launch.h", "api.hip"]
+DECODE_KERNELS = ("decode_mfma_kernel", "decode_streamk_reduce_kernel")
+CALIBRATION_BYTES = 1 << 30  # the plain copy run after the profiled decode calls
 
 
 def algorithmic_bytes(case) -> dict:
@@ -40,11 +43,24 @@ def algorithmic_bytes(case) -> dict:
     lens = case.context_lens.astype(np.int64)
     if case.ring is not None:
         lens = np.minimum(lens, case.ring.sink + case.ring.window)
-    kv = int(lens.sum()) * case.num_kv_heads * case.head_dim * 2 * s_kv
+    row = case.num_kv_heads * case.head_dim * 2 * s_kv  # one token's K and V rows, all KV heads
+    kv = int(lens.sum()) * row
+    # rows that several sequences reach through the same physical block (a
+    # shared prefix) are counted once in the unique figure
+    seen = set()
+    for b, n in enumerate(lens):
+        for blk in range(-(-int(n) // case.block_size)):
+            rows = min(case.block_size, int(n) - blk * case.block_size)
+            seen.add((int(case.block_tables[b, blk]), rows))
+    unique_rows = {}
+    for phys, rows in seen:
+        unique_rows[phys] = max(rows, unique_rows.get(phys, 0))
+    kv_unique = sum(unique_rows.values()) * row
     qo = case.num_seqs * case.num_q_heads * case.head_dim * 2 * s_kv
     tables = int(sum(-(-int(n) // case.block_size) for n in lens)) * 4 + case.num_seqs * 4
-    write = case.num_seqs * case.num_kv_heads * case.head_dim * 2 * s_kv * 2  # read + write, K and V
-    return {"decode": kv + qo + tables, "kv": kv, "write": write, "tokens": int(lens.sum())}
+    write = case.num_seqs * row * 2  # read + write of the new token's K and V
+    return {"decode": kv_unique + qo + tables, "decode_logical": kv + qo + tables, "kv": kv,
+            "kv_unique": kv_unique, "write": write, "tokens": int(lens.sum())}
 
 
 def kernel_hash() -> str:
@@ -67,7 +83,43 @@ def read_traffic():
     return t.get("bytes_per_call")
 
 
-def cpu_baseline(case, repeats: int = 3) -> dict:
+def _counter_rows(path):
+    import csv
+
+    with open(path, newline="") as fh:
+        return list(csv.DictReader(fh))
+
+
+def summarize_counters(fetch_csv: str, write_csv: str, command: str) -> dict:
+    """HBM bytes per decode call from two rocprofv3 --pmc runs of
+    ``bench.py --profile-calls N`` (FETCH_SIZE, then WRITE_SIZE; KiB per
+    dispatch).  Each counter is scaled by what it reads for the 1 GiB copy
+    that the profiled run ends with."""
+    out = {"kernel_hash": kernel_hash(), "command": command}
+    per_kernel = {}
+    for counter, path in (("FETCH_SIZE", fetch_csv), ("WRITE_SIZE", write_csv)):
+        rows = [r for r in _counter_rows(path) if r["Counter_Name"] == counter]
+        copies = [r for r in rows if "copy" in r["Kernel_Name"].lower()
+                  and float(r["Counter_Value"]) * 1024 > CALIBRATION_BYTES / 4]
+        if not copies:
+            raise SystemExit(f"{path}: no calibration copy dispatch found")
+        cal_kib = float(copies[-1]["Counter_Value"])
+        factor = CALIBRATION_BYTES / (cal_kib * 1024.0)
+        out[f"{counter.lower()}_copy_kib"] = cal_kib
+        out[f"{counter.lower()}_factor"] = round(factor, 4)
+        for name in DECODE_KERNELS:
+            vals = [float(r["Counter_Value"]) for r in rows if name in r["Kernel_Name"]]
+            if vals:
+                d = per_kernel.setdefault(name, {"dispatches": len(vals)})
+                d[f"{counter.lower()}_kib_mean"] = round(statistics.mean(vals), 1)
+                d[f"{counter.lower()}_bytes"] = round(statistics.mean(vals) * 1024.0 * factor)
+    out["per_kernel"] = per_kernel
+    out["bytes_per_call"] = int(sum(d.get("fetch_size_bytes", 0) + d.get("write_size_bytes", 0)
+                                    for d in per_kernel.values()))
+    return out
+
+
+def cpu_baseline(case, repeats: int = 2) -> dict:
     """The fp64 oracle (gather through block tables + naive softmax) on host cores."""
     import oracle
 
@@ -76,24 +128,29 @@ def cpu_baseline(case, repeats: int = 3) -> dict:
     except ImportError:  # pragma: no cover
         threadpool_limits = None
     kp, vp, _ = oracle.build_pools(case)
-    times = []
+    times, cpu_s = [], []
     ctx = threadpool_limits(limits=1) if threadpool_limits else None
     try:
         if ctx:
             ctx.__enter__()
         for _ in range(repeats):
             t0 = time.perf_counter()
+            c0 = time.process_time()
             oracle.decode(case.query, kp, vp, case.block_tables, case.context_lens, case.scale,
                           case.dtype, case.block_size, ring=case.ring)
             times.append(time.perf_counter() - t0)
+            cpu_s.append(time.process_time() - c0)
     finally:
         if ctx:
             ctx.__exit__(None, None, None)
     t = statistics.median(times)
+    # threads actually busy: process CPU time over wall time (BLAS limited to one)
+    cores = max(1, round(sum(cpu_s) / sum(times)))
     ab = algorithmic_bytes(case)
-    return {"value": round(ab["decode"] / t / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+    return {"value": round(ab["decode"] / t / 1e9, 4), "unit": "GB/s", "cores": cores, "kind": "oracle",
             "sample": f"whole workload ({case.num_seqs} sequences, {ab['tokens']} cached tokens), "
-                      f"decode only, median of {repeats}; {t:.3f} s per call",
+                      f"decode only (fp64 gather + softmax), median of {repeats}; {t:.3f} s per call, "
+                      f"cpu/wall {sum(cpu_s) / sum(times):.2f}",
             "seconds_per_call": round(t, 4)}
 
 
@@ -103,9 +160,24 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--cold-steps", type=int, default=50,
-                    help="extra decode calls each preceded by a 1 GiB cache scrub (0 = skip)")
+                    help="extra decode calls each preceded by a 1 GiB read that evicts the caches (0 = skip)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--config", default="llama70b_b64", choices=sorted(__import__("workloads").CONFIGS),
+                    help="workload (default: the 70B-shaped batch the metric is quoted on; the others "
+                         "are the parity configurations, timed the same way)")
+    ap.add_argument("--profile-calls", type=int, default=0,
+                    help="only run this many decode calls, then a 1 GiB copy (for rocprofv3 counter runs)")
+    ap.add_argument("--write-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="turn two rocprofv3 counter_collection.csv files into the traffic record")
+    ap.add_argument("--traffic-command", default="",
+                    help="the profiling command line recorded with --write-traffic")
     args = ap.parse_args()
+    if args.write_traffic:
+        rec = summarize_counters(args.write_traffic[0], args.write_traffic[1], args.traffic_command)
+        with open(TRAFFIC_FILE, "w") as fh:
+            json.dump(rec, fh, indent=1)
+        print(json.dumps(rec))
+        return 0
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (this path has no multi-GPU mode); got --gpus {args.gpus}",
               file=sys.stderr)
@@ -126,29 +198,42 @@ def main() -> int:
     _lib.load()
     dev = "cuda:0"
     torch.cuda.set_device(0)
-    print("bench: generating the seeded 70B-shaped batch", file=sys.stderr, flush=True)
-    case = workloads.config_llama70b()
+    print(f"bench: generating the seeded workload {args.config}", file=sys.stderr, flush=True)
+    if args.config == "sink_ring":  # timing set: full windows at distinct ring phases near 100k
+        case = workloads.config_sink_ring(lengths=workloads.ring_timing_lengths())
+    else:
+        case = workloads.CONFIGS[args.config]()
     ab = algorithmic_bytes(case)
-    tdt = torch.bfloat16
+    tdt = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}[case.dtype]
+    ibits = torch.int32 if case.dtype == "f32" else torch.int16
+    raw_view = np.int32 if case.dtype == "f32" else np.int16
 
     def to_dev(raw):
-        return torch.from_numpy(np.ascontiguousarray(raw).view(np.int16)).view(tdt).to(dev)
+        return torch.from_numpy(np.ascontiguousarray(raw).view(raw_view)).view(tdt).to(dev)
 
     shape = (case.num_blocks, case.block_size, case.num_kv_heads, case.head_dim)
     k_cache = torch.empty(shape, dtype=tdt, device=dev)
     v_cache = torch.empty(shape, dtype=tdt, device=dev)
-    k_cache.view(torch.int16).fill_(workloads.NAN_BITS["bf16"])
-    v_cache.view(torch.int16).fill_(workloads.NAN_BITS["bf16"])
+    nan_bits = int(np.array(workloads.NAN_BITS[case.dtype],
+                            dtype=np.uint32 if case.dtype == "f32" else np.uint16).view(raw_view))
+    k_cache.view(ibits).fill_(nan_bits)
+    v_cache.view(ibits).fill_(nan_bits)
     pool = pk.Pool(k_cache, v_cache, case.block_size)
+    ring = None
+    if case.ring is not None:
+        cap = case.ring.sink + case.ring.window
+        table = torch.empty(pk.rope_table_bytes(cap, case.head_dim) // 4, dtype=torch.float32, device=dev)
+        pk.rope_table_init(table, cap, case.head_dim, case.ring.rope_base)
+        ring = pk.Ring(case.ring.sink, case.ring.window, case.ring.rope_base, table)
 
     # fill the cache through the library's own write path
     for ch in case.writes:
         sid = np.full(ch.positions.shape, ch.seq, dtype=np.int32)
-        slots = pk.compute_slot_mapping(pool, case.block_tables, sid, ch.positions)
+        slots = pk.compute_slot_mapping(pool, case.block_tables, sid, ch.positions, ring)
         pk.reshape_and_cache(pool, to_dev(ch.keys), to_dev(ch.values), torch.from_numpy(slots).to(dev))
     step_chunks = case.step_writes()
     step_slots = np.concatenate([pk.compute_slot_mapping(
-        pool, case.block_tables, np.full(1, ch.seq, dtype=np.int32), ch.positions) for ch in step_chunks])
+        pool, case.block_tables, np.full(1, ch.seq, dtype=np.int32), ch.positions, ring) for ch in step_chunks])
     step_keys = to_dev(np.concatenate([ch.keys for ch in step_chunks]))
     step_vals = to_dev(np.concatenate([ch.values for ch in step_chunks]))
     step_slots_d = torch.from_numpy(step_slots).to(dev)
@@ -158,15 +243,32 @@ def main() -> int:
     lens = torch.from_numpy(case.context_lens).to(dev)
     max_ctx = int(case.context_lens.max())
     out = torch.empty((case.num_seqs, case.num_q_heads, case.head_dim), dtype=tdt, device=dev)
-    ws_bytes = pk.decode_workspace_bytes(pool, case.num_seqs, case.num_q_heads, max_ctx)
+    ws_bytes = pk.decode_workspace_bytes(pool, case.num_seqs, case.num_q_heads, max_ctx, ring)
     ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
     torch.cuda.synchronize()
+
+    def decode():
+        pk.decode(pool, out, query, tables, lens, max_ctx, case.scale, ring=ring, workspace=ws)
+
+    if args.profile_calls > 0:
+        for _ in range(args.profile_calls):
+            decode()
+        torch.cuda.synchronize()
+        src = torch.empty(CALIBRATION_BYTES, dtype=torch.uint8, device=dev)
+        src.fill_(3)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)  # calibration: reads and writes exactly 1 GiB
+        torch.cuda.synchronize()
+        print(f"bench: profiled {args.profile_calls} decode calls and a 1 GiB copy", file=sys.stderr)
+        pool.close()
+        return 0
 
     def step(ev_decode=None):
         pk.reshape_and_cache(pool, step_keys, step_vals, step_slots_d)
         if ev_decode is not None:
             ev_decode[0].record()
-        pk.decode(pool, out, query, tables, lens, max_ctx, case.scale, workspace=ws)
+        decode()
         if ev_decode is not None:
             ev_decode[1].record()
 
@@ -188,12 +290,15 @@ def main() -> int:
 
     cold_ms = []
     if args.cold_steps > 0:
-        scrub = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        # read (not write) 1 GiB between calls: the caches end up holding
+        # clean unrelated lines, so the call finds neither its data cached
+        # nor dirty lines to write back
+        scrub = torch.ones(1 << 28, dtype=torch.float32, device=dev)
         for _ in range(args.cold_steps):
-            scrub.fill_(1)
+            scrub.sum()
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             e0.record()
-            pk.decode(pool, out, query, tables, lens, max_ctx, case.scale, workspace=ws)
+            decode()
             e1.record()
             e1.synchronize()
             cold_ms.append(e0.elapsed_time(e1))
@@ -204,7 +309,19 @@ def main() -> int:
     value = step_bytes / (ms_per_step * 1e-3) / 1e9
     dec_avg_ms = statistics.mean(decode_ms)
     achieved = ab["decode"] / (dec_avg_ms * 1e-3) / 1e9
-    traffic = read_traffic()
+    traffic = read_traffic() if args.config == "llama70b_b64" else None
+    group = case.num_q_heads // case.num_kv_heads
+    mfma = case.dtype != "f32" and 4 <= group <= 16 and os.environ.get("PA_FORCE_VALU", "0") in ("", "0")
+    kernel = ("pa_decode call: decode_mfma_kernel + decode_streamk_reduce_kernel" if mfma else
+              "pa_decode call: decode_valu_kernel (+ decode_reduce_kernel when a context is split)")
+    if args.config == "llama70b_b64":
+        workload = ("llama70b_b64: paged decode, B 64, Hq 64, Hkv 8 (GQA 8), D 128, bf16 KV, "
+                    "block 16, lengths 32xU[50,500] + 19xU[500,2000] + 13xU[2000,8000], "
+                    "shuffled blocks, pool 1.1x need")
+    else:
+        workload = (f"{args.config}: paged decode, B {case.num_seqs}, Hq {case.num_q_heads}, "
+                    f"Hkv {case.num_kv_heads}, D {case.head_dim}, {case.dtype} KV, block {case.block_size}"
+                    + (f", sink {case.ring.sink} + ring {case.ring.window}" if case.ring else ""))
     result = {
         "metric": "paged decode attention: effective KV GB/s (% of HBM peak) and tokens/s",
         "value": round(value, 2),
@@ -216,12 +333,10 @@ def main() -> int:
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": case.dtype,
         "data": "synthetic",
         "config": {
-            "workload": "llama70b_b64: paged decode, B 64, Hq 64, Hkv 8 (GQA 8), D 128, bf16 KV, "
-                        "block 16, lengths 32xU[50,500] + 19xU[500,2000] + 13xU[2000,8000], "
-                        "shuffled blocks, pool 1.1x need",
+            "workload": workload,
             "global_batch": case.num_seqs,
             "cached_tokens": ab["tokens"],
             "max_context_len": max_ctx,
@@ -239,13 +354,14 @@ def main() -> int:
                            if cold_ms else None),
         "roofline": {
             "bound": "hbm",
-            "kernel": "pa_decode (decode_mfma_kernel + decode_reduce_kernel)",
+            "kernel": kernel + " (HIP events bracket the call)",
             "achieved": round(achieved, 1),
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
             "traffic": traffic,
             "algorithmic_bytes": ab["decode"],
+            "algorithmic_bytes_logical": ab["decode_logical"],
         },
     }
     pool.close()
