@@ -16,17 +16,15 @@
 //    order so RoPE keeps relative distances as the ring slides.
 //
 // Work decomposition (MI355X-first, not the pages' CUDA design):
-//  * One work-group of 4 wave64s per (split-K partition, KV head, sequence).
-//    A partition is a contiguous run of `partition_tokens` logical tokens;
-//    its 16-token tiles are dealt round-robin to the 4 waves, each keeping
-//    its own online-softmax state; the waves merge through LDS at the end.
-//  * The block id of a tile is wave-uniform, so it is fetched through the
-//    scalar path (one SGPR load per tile) rather than staged in LDS.
-//  * A tile's 16 K rows (head g) are read with 16-byte loads; for the MFMA
-//    kernel each lane's 16 bytes are exactly its A-operand fragment.
-//  * Sequences whose context fits one partition write the final output
-//    directly; longer ones write (max, sum, normalised partial) and
-//    decode_reduce combines them.
+//  * decode_mfma_kernel (16-bit K/V, GQA group 4..16): stream-K over
+//    16-token tiles, one work-group of 4 waves per CU, one KV head per
+//    wave; both contractions on MFMA; a separate combine kernel merges the
+//    partials of sequences cut by a range boundary.
+//  * decode_valu_kernel (any dtype, any group): persistent work-groups over
+//    (partition, KV head, head chunk, sequence) items with VALU dot
+//    products; decode_reduce_kernel merges partitions.
+//  * Block ids are never staged in LDS: they are wave-uniform per tile and
+//    travel through lanes and v_readlane into scalar registers.
 //  * The summation order depends only on logical positions and lengths, so
 //    outputs are bit-identical under relabelling of physical blocks.
 #include <algorithm>
