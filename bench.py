@@ -165,6 +165,9 @@ def main() -> int:
     ap.add_argument("--config", default="llama70b_b64", choices=sorted(__import__("workloads").CONFIGS),
                     help="workload (default: the 70B-shaped batch the metric is quoted on; the others "
                          "are the parity configurations, timed the same way)")
+    ap.add_argument("--launch", choices=("eager", "graph"), default="eager",
+                    help="launch eagerly (default) or replay captured HIP graphs of the write and the "
+                         "decode call (one replay each per step)")
     ap.add_argument("--profile-calls", type=int, default=0,
                     help="only run this many decode calls, then a 1 GiB copy (for rocprofv3 counter runs)")
     ap.add_argument("--write-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
@@ -264,8 +267,11 @@ def main() -> int:
         pool.close()
         return 0
 
-    def step(ev_decode=None):
+    def write():
         pk.reshape_and_cache(pool, step_keys, step_vals, step_slots_d)
+
+    def step(ev_decode=None):
+        write()
         if ev_decode is not None:
             ev_decode[0].record()
         decode()
@@ -276,6 +282,21 @@ def main() -> int:
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
+    if args.launch == "graph":
+        # a decode loop replays captured launches: one graph for the cache
+        # write, one for the decode call (both kernels)
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        g_write, g_decode = torch.cuda.CUDAGraph(), torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g_write, stream=side):
+            write()
+        with torch.cuda.graph(g_decode, stream=side):
+            decode()
+        torch.cuda.synchronize()
+        write, decode = g_write.replay, g_decode.replay
+        for _ in range(max(1, args.warmup // 4)):
+            step()
+        torch.cuda.synchronize()
 
     events = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
               for _ in range(args.steps)]
@@ -342,6 +363,8 @@ def main() -> int:
             "max_context_len": max_ctx,
             "num_blocks": case.num_blocks,
             "seed": case.seed,
+            "launch": ("hip graph replay (cache write graph + decode call graph)" if args.launch == "graph"
+                       else "eager launches"),
         },
         "tokens_per_s": round(case.num_seqs / (ms_per_step * 1e-3), 1),
         "step_bytes": step_bytes,

@@ -192,6 +192,9 @@ int pa_decode(pa_pool *pool, void *out, const void *query, const int32_t *block_
   a.block_shift = pa::log2_exact(pool->block_size);
   a.partition_tokens = w.partition_tokens;
   a.max_parts = w.max_parts;
+  // Plain tiles are cheap, so short ranges lose to start-up and merging;
+  // ring tiles also rotate every key and gain from spreading out.
+  a.min_range_tiles = ring ? 1 : 4;
   a.ring_sink = ring ? ring->sink : 0;
   a.ring_window = ring ? ring->window : 1;
   a.scale_log2 = scale * pa::kLog2eHost;

@@ -333,6 +333,14 @@ __device__ int build_tile_schedule(const DecodeArgs &a, bool ring, int *s_tfirst
   return carry;
 }
 
+// Groups that get a tile range.  Ranges shorter than a.min_range_tiles
+// cost more in start-up and partial merging than they gain in parallelism,
+// so small batches leave some groups idle.
+__device__ __forceinline__ int active_groups(const DecodeArgs &a, int total_tiles, int groups) {
+  const int m = max(1, a.min_range_tiles);
+  return max(1, min(groups, (total_tiles + m - 1) / m));
+}
+
 // (b, t) of flattened tile y (y < s_tfirst[num_seqs]).
 __device__ __forceinline__ void locate_tile(const int *s_tfirst, int num_seqs, int y, int &b,
                                             int &t, int &tiles) {
@@ -369,7 +377,7 @@ void decode_mfma_kernel(DecodeArgs a) {
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int row16 = lane & 15, grp = lane >> 4;
-  const int groups = (gridDim.x * kNW) / hkv;
+  const int groups = active_groups(a, total, (gridDim.x * kNW) / hkv);
   const int gw = blockIdx.x * kNW + wave;
   const int grp_id = gw / hkv;  // tile range of this wave
   const int g = gw - grp_id * hkv;  // KV head of this wave
@@ -409,19 +417,14 @@ void decode_mfma_kernel(DecodeArgs a) {
     c0 = start;
     cnt = min(kWave, xend - start);
     tb = tt = tvalid = tflag = toff_lo = toff_hi = tnrec = 0;
+    int tiles = 0;
+    if (lane < cnt) locate_tile(s_tfirst, a.num_seqs, c0 + lane, tb, tt, tiles);
+    const int r0 = kTileTokens * tt;
+    // block id of the tile, loaded before the query fragments are fetched so
+    // that both are in flight together (lanes past cnt read entry 0)
+    const int phys = a.block_tables[(int64_t)tb * a.max_blocks_per_seq + (r0 >> a.block_shift)];
     if (lane < cnt) {
-      int tiles;
-      locate_tile(s_tfirst, a.num_seqs, c0 + lane, tb, tt, tiles);
-      const int L = s_len[tb];
-      tvalid = min(kTileTokens, L - kTileTokens * tt);
-      const int r0 = kTileTokens * tt;
-      const int phys = a.block_tables[(int64_t)tb * a.max_blocks_per_seq + (r0 >> a.block_shift)];
-      const int64_t off = ((int64_t)min(max(phys, 0), a.num_blocks - 1) * a.kv_block_stride +
-                           (int64_t)(r0 & bmask) * row_stride + head_off) *
-                          (int64_t)sizeof(st);
-      toff_lo = (int)(uint32_t)off;
-      toff_hi = (int)(off >> 32);
-      tnrec = (int)(((tvalid - 1) * row_stride + D) * sizeof(st));  // tvalid >= 1 here
+      tvalid = min(kTileTokens, s_len[tb] - r0);
       tflag = (tt == 0 ? 1 : 0) | (tt == tiles - 1 ? 2 : 0);
     }
     // Tiles that open a segment (first tile of a sequence, or the first
@@ -450,6 +453,14 @@ void decode_mfma_kernel(DecodeArgs a) {
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb) qtmp[s2][kb] = buffer_load16(qr, q_off + 64 * kb);
       mm &= mm - 1;
+    }
+    if (lane < cnt) {
+      const int64_t off = ((int64_t)min(max(phys, 0), a.num_blocks - 1) * a.kv_block_stride +
+                           (int64_t)(r0 & bmask) * row_stride + head_off) *
+                          (int64_t)sizeof(st);
+      toff_lo = (int)(uint32_t)off;
+      toff_hi = (int)(off >> 32);
+      tnrec = (int)(((tvalid - 1) * row_stride + D) * sizeof(st));  // tvalid >= 1 here
     }
 #pragma unroll
     for (int s2 = 0; s2 < kQSlots; ++s2)
@@ -636,17 +647,27 @@ __global__ __launch_bounds__(256) void decode_streamk_reduce_kernel(DecodeArgs a
     for (int k = 0; k < DPL; ++k) out[k * kWave] = T::from_float(0.f);
     return;
   }
-  const int per = (total + groups - 1) / groups;
+  const int active = active_groups(a, total, groups);
+  const int per = (total + active - 1) / active;
   const int q_lo = t0 / per, q_hi = (t1 - 1) / per;
   if (q_lo == q_hi) return;
   const int nseg = q_hi - q_lo + 1;
   const int64_t slot0 = ((int64_t)q_lo + b) * hkv + g;  // slot of segment s: slot0 + s * hkv
+  const int64_t rstride = (int64_t)hkv * G * D;  // between consecutive segments' rows
   float num[DPL];
 #pragma unroll
   for (int k = 0; k < DPL; ++k) num[k] = 0.f;
   float den = 0.f, mx = -INFINITY;
   for (int s0 = 0; s0 < nseg; s0 += kWave) {  // chunks of 64 segments, online rescale
     const int cnt = min(kWave, nseg - s0);
+    const float *rows = a.ws_o + ((slot0 + (int64_t)s0 * hkv) * G + h) * D + lane;
+    // the rows of the first 8 segments are requested together with the
+    // (m, l) pairs (indices clamped into the chunk; extra copies unused)
+    float v[8][DPL];
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+#pragma unroll
+      for (int k = 0; k < DPL; ++k) v[u][k] = rows[min(u, cnt - 1) * rstride + k * kWave];
     float ms = -INFINITY, ls = 0.f;
     if (lane < cnt) {
       const int64_t slot = slot0 + (int64_t)(s0 + lane) * hkv;
@@ -663,28 +684,29 @@ __global__ __launch_bounds__(256) void decode_streamk_reduce_kernel(DecodeArgs a
     for (int k = 0; k < DPL; ++k) num[k] *= scale_old;
     mx = m_new;
     const float wq = lane < cnt ? ls * fast_exp2(ms - mx) : 0.f;
-    const float *rows = a.ws_o + ((slot0 + (int64_t)s0 * hkv) * G + h) * D + lane;
-    const int64_t rstride = (int64_t)hkv * G * D;
-    int j = 0;
-    for (; j + 8 <= cnt; j += 8) {  // 8 segments of loads in flight
-      float v[8][DPL];
 #pragma unroll
-      for (int u = 0; u < 8; ++u)
-#pragma unroll
-        for (int k = 0; k < DPL; ++k) v[u][k] = rows[(j + u) * rstride + k * kWave];
-#pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const float w = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wq), j + u));
+    for (int u = 0; u < 8; ++u) {
+      if (u < cnt) {
+        const float w = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wq), u));
         den += w;
 #pragma unroll
         for (int k = 0; k < DPL; ++k) num[k] = fmaf(w, v[u][k], num[k]);
       }
     }
-    for (; j < cnt; ++j) {
-      const float w = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wq), j));
-      den += w;
+    for (int j = 8; j < cnt; j += 8) {  // rarely: more than 8 segments, 8 rows in flight
 #pragma unroll
-      for (int k = 0; k < DPL; ++k) num[k] = fmaf(w, rows[j * rstride + k * kWave], num[k]);
+      for (int u = 0; u < 8; ++u)
+#pragma unroll
+        for (int k = 0; k < DPL; ++k) v[u][k] = rows[min(j + u, cnt - 1) * rstride + k * kWave];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        if (j + u < cnt) {
+          const float w = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wq), j + u));
+          den += w;
+#pragma unroll
+          for (int k = 0; k < DPL; ++k) num[k] = fmaf(w, v[u][k], num[k]);
+        }
+      }
     }
   }
   const float inv = 1.f / den;

@@ -40,6 +40,7 @@ struct DecodeArgs {
   int32_t block_shift;  // log2(block_size)
   int32_t partition_tokens;
   int32_t max_parts;
+  int32_t min_range_tiles;  // MFMA kernel: shortest stream-K range worth a group
   int32_t ring_sink;
   int32_t ring_window;
   float scale_log2;  // scale * log2(e)

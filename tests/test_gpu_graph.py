@@ -1,0 +1,73 @@
+"""Captured HIP graphs of the hot path replay to the eager result.
+
+A decode loop captures the cache write and the decode call once and
+replays them every step.  Each replay here is followed by unrelated eager
+work and a synchronisation, and every replay must equal the eager call bit
+for bit (same kernels, same inputs, no memset nodes in the graph).
+"""
+import numpy as np
+import pytest
+import torch
+
+import workloads
+from gpu_support import DeviceCase, raw_to_torch, torch_bits
+
+pytestmark = pytest.mark.gpu
+
+
+def _case(name):
+    if name == "sink_ring":
+        return workloads.config_sink_ring(lengths=workloads.ring_timing_lengths())
+    return workloads.CONFIGS[name]()
+
+
+@pytest.mark.parametrize("name", ["llama70b_b64", "shared_prefix", "sink_ring", "tiny_fp32"])
+def test_graph_replays_equal_eager(name):
+    case = _case(name)
+    dc = DeviceCase(case)
+    dc.write_all()
+    c = case
+    mcl = int(c.context_lens.max())
+    ws = dc.workspace(mcl)
+    out_eager = torch.empty((c.num_seqs, c.num_q_heads, c.head_dim), dtype=dc.k_cache.dtype,
+                            device=dc.device)
+    out_graph = torch.empty_like(out_eager)
+
+    step = c.step_writes()
+    slots = torch.from_numpy(np.concatenate([dc.slots_for(ch) for ch in step])).to(dc.device)
+    keys = raw_to_torch(np.concatenate([ch.keys for ch in step]), c.dtype).to(dc.device)
+    vals = raw_to_torch(np.concatenate([ch.values for ch in step]), c.dtype).to(dc.device)
+
+    import paged_kv_cache_145_amd as pk
+
+    def write():
+        pk.reshape_and_cache(dc.pool, keys, vals, slots)
+
+    def decode(out):
+        pk.decode(dc.pool, out, dc.query, dc.block_tables, dc.context_lens, mcl, c.scale,
+                  ring=dc.ring, workspace=ws)
+
+    write()
+    decode(out_eager)
+    torch.cuda.synchronize()
+    k_ref, v_ref = torch_bits(dc.k_cache, c.dtype), torch_bits(dc.v_cache, c.dtype)
+    ref = torch_bits(out_eager, c.dtype)
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=side):
+        write()
+        decode(out_graph)
+    torch.cuda.synchronize()
+
+    scratch = torch.ones(1 << 20, device=dc.device)
+    for rep in range(4):
+        out_graph.fill_(0)
+        g.replay()
+        scratch.mul_(1.0001).add_(rep)  # unrelated eager work between replays
+        torch.cuda.synchronize()
+        assert np.array_equal(torch_bits(out_graph, c.dtype), ref), f"replay {rep} differs from eager"
+        assert np.array_equal(torch_bits(dc.k_cache, c.dtype), k_ref)
+        assert np.array_equal(torch_bits(dc.v_cache, c.dtype), v_ref)
+    dc.pool.close()
