@@ -22,12 +22,17 @@ __global__ __launch_bounds__(256) void reshape_and_cache_kernel(
     int64_t num_slots) {
   const int64_t i = blockIdx.x;
   const int32_t slot = slot_mapping[i];
-  if (slot < 0 || slot >= num_slots) return;  // padding; out-of-pool slots are dropped
+  // padding (negative) and out-of-pool slots are dropped; the rows are read
+  // regardless, so their loads overlap the slot load
+  const bool keep = slot >= 0 && slot < num_slots;
   const int64_t src = i * chunks;
-  const int64_t dst = (int64_t)slot * chunks;
+  const int64_t dst = (int64_t)(keep ? slot : 0) * chunks;
   for (int c = threadIdx.x; c < chunks; c += blockDim.x) {
-    k_cache[dst + c] = key[src + c];
-    v_cache[dst + c] = value[src + c];
+    const uint4 kx = key[src + c], vx = value[src + c];
+    if (keep) {
+      k_cache[dst + c] = kx;
+      v_cache[dst + c] = vx;
+    }
   }
 }
 
