@@ -27,8 +27,15 @@ Parity status of each function (what pins it is listed in the tests):
 * ``BlockAllocatorModel``: pinned (lowest-free-id order, exhaustion, release
   at the last reference, stats).
 * closed forms in ``sizes``: pinned against the numbers the pages print.
+* ``fp8`` (E4M3 values, nearest-even encoding with saturation, per-head
+  scaling) and ``quantize_for_cache``: pinned (codes worked by hand from the
+  format definition, every code round-trips, rounding is monotone and
+  nearest, ties go to the even code); the format and scaling rule are
+  readings, the page names FP8 storage without fixing either.
 """
+from . import fp8  # noqa: F401
 from .paged_attention import (  # noqa: F401
+    quantize_for_cache,
     to_f64,
     gather_rows,
     slot_of,

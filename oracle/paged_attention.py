@@ -28,6 +28,8 @@ from __future__ import annotations
 
 import numpy as np
 
+from . import fp8
+
 # ---------------------------------------------------------------------------
 # dtype handling (exact widening of stored values)
 # ---------------------------------------------------------------------------
@@ -166,14 +168,15 @@ def attention_one_group(q: np.ndarray, keys: np.ndarray, values: np.ndarray, sca
 
 
 def decode(query, k_pool, v_pool, block_tables, context_lens, scale, dtype, block_size,
-           ring=None) -> np.ndarray:
+           ring=None, kv_dtype=None, k_scale=None, v_scale=None) -> np.ndarray:
     """Single-token decode attention over a paged KV cache (float64 output).
 
     query [B, Hq, D]; pools [num_blocks, block_size, Hkv, D]; block_tables
     [B, max_blocks] int; context_lens [B].  q head h reads KV head h // G with
     G = Hq / Hkv.  ``ring`` (object with sink, window, rope_base) switches to
     the sink + ring cache: the resident keys in cache order j = 0..L-1 are
-    rotated by j, the query by L - 1.
+    rotated by j, the query by L - 1.  ``kv_dtype`` "fp8_e4m3": the pools hold
+    E4M3 codes whose values are scaled per KV head by k_scale / v_scale.
     """
     q_all = to_f64(query, dtype)
     b_count, hq, d = q_all.shape
@@ -190,8 +193,12 @@ def decode(query, k_pool, v_pool, block_tables, context_lens, scale, dtype, bloc
             idx = np.arange(n)
         else:
             idx = np.asarray(ring_cache_order(n, ring.sink, ring.window), dtype=np.int64)
-        keys = to_f64(gather_rows(k_pool, block_tables[b], idx, block_size), dtype)  # [L, Hkv, D]
-        vals = to_f64(gather_rows(v_pool, block_tables[b], idx, block_size), dtype)
+        if kv_dtype == "fp8_e4m3":
+            keys = fp8.dequantize_rows(gather_rows(k_pool, block_tables[b], idx, block_size), k_scale)
+            vals = fp8.dequantize_rows(gather_rows(v_pool, block_tables[b], idx, block_size), v_scale)
+        else:
+            keys = to_f64(gather_rows(k_pool, block_tables[b], idx, block_size), dtype)  # [L, Hkv, D]
+            vals = to_f64(gather_rows(v_pool, block_tables[b], idx, block_size), dtype)
         q_b = q_all[b]
         if ring is not None:
             length = idx.size
@@ -238,6 +245,11 @@ def reshape_and_cache(k_pool, v_pool, keys, values, slot_mapping, block_size):
     return k_out, v_out
 
 
+def quantize_for_cache(rows_raw, act_dtype, scale) -> np.ndarray:
+    """E4M3 codes of raw activation rows [m, Hkv, D] (f16/bf16/f32 storage)."""
+    return fp8.quantize_rows(to_f64(rows_raw, act_dtype).astype(np.float32), scale)
+
+
 def build_pools(case):
     """Fill a NaN pool with every write of a ``workloads.DecodeCase``.
 
@@ -256,6 +268,10 @@ def build_pools(case):
             r = p if case.ring is None else ring_slot(p, case.ring.sink, case.ring.window)
             slots.append(slot_of(row, r, case.block_size))
         slots = np.asarray(slots, dtype=np.int64)
-        reshape_and_cache_(k_pool, v_pool, ch.keys, ch.values, slots, case.block_size)
+        keys, values = ch.keys, ch.values
+        if getattr(case, "kv_dtype", None) == "fp8_e4m3":
+            keys = quantize_for_cache(keys, case.dtype, case.k_scale)
+            values = quantize_for_cache(values, case.dtype, case.v_scale)
+        reshape_and_cache_(k_pool, v_pool, keys, values, slots, case.block_size)
         slot_lists.append(slots)
     return k_pool, v_pool, slot_lists

@@ -462,3 +462,100 @@ def test_closed_forms_match_printed_sizes():
     assert abs(100 * sz.preallocation_waste(200, 4096) - s["waste_200_of_4096_pct"][0]) <= 0.05
     assert sz.preallocation_waste(8000, 4096) == 0.0
     assert [sz.blocks_needed(n, 16) for n in (0, 1, 16, 17, 8000)] == [0, 1, 1, 2, 500]
+
+
+# ---------------------------------------------------------------------------
+# FP8 (E4M3) KV storage
+# ---------------------------------------------------------------------------
+
+def _e4m3_golden():
+    rows = []
+    with open(os.path.join(GOLDEN, "e4m3_codes.txt")) as fh:
+        for line in fh:
+            line = line.strip()
+            if not line or line.startswith("#"):
+                continue
+            x, code, value = line.split()[:3]
+            rows.append((float(x), int(code, 16), float(value)))
+    return rows
+
+
+def test_e4m3_codes_worked_by_hand():
+    from oracle import fp8
+
+    rows = _e4m3_golden()
+    assert len(rows) >= 20
+    for x, code, value in rows:
+        assert fp8.e4m3_encode_one(np.float32(x)) == code, (x, hex(code))
+        got = fp8.e4m3_value(code)
+        assert got == value or (got == 0.0 and value == 0.0 and np.signbit(got) == np.signbit(value)), (x, got)
+    assert np.isnan(fp8.e4m3_value(0x7F)) and np.isnan(fp8.e4m3_value(0xFF))
+    assert fp8.e4m3_encode_one(np.float32("nan")) == 0x7F
+
+
+def test_e4m3_every_finite_code_round_trips_and_order_is_kept():
+    from oracle import fp8
+
+    finite = [c for c in range(256) if not np.isnan(fp8.e4m3_value(c))]
+    assert len(finite) == 254
+    for c in finite:
+        assert fp8.e4m3_value(fp8.e4m3_encode_one(np.float32(fp8.e4m3_value(c)))) == fp8.e4m3_value(c)
+    # the positive codes 0x00..0x7e are strictly increasing in value
+    pos = [fp8.e4m3_value(c) for c in range(0x7F)]
+    assert all(a < b for a, b in zip(pos, pos[1:]))
+    rng = np.random.default_rng(7)
+    xs = np.sort(rng.uniform(-500, 500, 4000).astype(np.float32))
+    dec = fp8.e4m3_decode(fp8.e4m3_encode(xs))
+    assert np.all(np.diff(dec) >= 0)
+
+
+def test_e4m3_rounding_is_to_a_neighbour_within_half_a_step():
+    """Independent of the encoder's search: the result must be one of the two
+    representable neighbours, within half their spacing."""
+    from oracle import fp8
+
+    rng = np.random.default_rng(8)
+    xs = np.concatenate([rng.uniform(-448, 448, 3000), rng.normal(0, 0.01, 1000)]).astype(np.float32)
+    for x in xs:
+        a = abs(float(x))
+        # neighbours from the format: exponent of a, step 2^(e-3), subnormal step 2^-9
+        if a < 2.0 ** -6:
+            step = 2.0 ** -9
+        else:
+            step = 2.0 ** (np.floor(np.log2(a)) - 3)
+        lo = np.floor(a / step) * step
+        got = abs(fp8.e4m3_value(fp8.e4m3_encode_one(x)))
+        assert got in (lo, lo + step) or (a >= 448 and got == 448.0)
+        assert abs(got - a) <= step / 2 + 1e-300
+
+
+def test_fp8_decode_equals_attention_on_dequantised_pools():
+    """The fp8 path of decode is attention on scale[h] * value(code): build a
+    float64 pool from the codes by hand and compare."""
+    from oracle import fp8
+
+    case = workloads.config_fp8(workloads.config_tiny_fp32)
+    kp, vp, _ = oracle.build_pools(case)
+    assert kp.dtype == np.uint8
+    ref_k = fp8.E4M3_TABLE[kp] * case.k_scale.astype(np.float64)[None, None, :, None]
+    ref_v = fp8.E4M3_TABLE[vp] * case.v_scale.astype(np.float64)[None, None, :, None]
+    got = oracle.decode(case.query, kp, vp, case.block_tables, case.context_lens, case.scale, case.dtype,
+                        case.block_size, kv_dtype=case.kv_dtype, k_scale=case.k_scale, v_scale=case.v_scale)
+    q = oracle.to_f64(case.query, case.dtype)
+    g = case.num_q_heads // case.num_kv_heads
+    for b in range(case.num_seqs):
+        n = int(case.context_lens[b])
+        rows_k = np.stack([ref_k[case.block_tables[b, t // case.block_size], t % case.block_size] for t in range(n)])
+        rows_v = np.stack([ref_v[case.block_tables[b, t // case.block_size], t % case.block_size] for t in range(n)])
+        for h in range(case.num_q_heads):
+            s = case.scale * rows_k[:, h // g, :] @ q[b, h]
+            p = np.exp(s - s.max())
+            np.testing.assert_allclose(got[b, h], (p / p.sum()) @ rows_v[:, h // g, :], rtol=0, atol=1e-12)
+    # the quantisation is a float32 product with 1/scale, then nearest-even E4M3
+    ch = case.writes[0]
+    x = oracle.to_f64(ch.keys, case.dtype).astype(np.float32)
+    inv = (np.float32(1) / case.k_scale.astype(np.float32)).astype(np.float32)
+    codes = oracle.quantize_for_cache(ch.keys, case.dtype, case.k_scale)
+    for idx in [(0, 0, 0), (3, 1, 17), (10, 1, 63)]:
+        prod = np.float32(x[idx] * inv[idx[1]])
+        assert codes[idx] == fp8.e4m3_encode_one(prod)

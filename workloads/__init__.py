@@ -37,6 +37,7 @@ import numpy as np
 SEED_BASE = 145_000
 
 RAW_DTYPES = {"f32": np.float32, "f16": np.float16, "bf16": np.uint16}
+FP8_NAN_CODE = 0x7F  # E4M3 NaN (S.1111.111)
 ELEM_BYTES = {"f32": 4, "f16": 2, "bf16": 2}
 NAN_BITS = {"f32": 0x7FC00000, "f16": 0x7E00, "bf16": 0x7FC0}
 
@@ -109,6 +110,12 @@ class DecodeCase:
     ring: Optional[RingSpec] = None
     pad_block: int = -1  # block id used for table padding (-1: none)
     notes: dict = field(default_factory=dict)
+    # 8-bit KV storage: "fp8_e4m3" pools hold codes, dequantised per KV head
+    # by k_scale / v_scale (float32 [Hkv]); ``dtype`` is then the dtype of
+    # the query, the output and the key/value rows handed to the cache write
+    kv_dtype: Optional[str] = None
+    k_scale: Optional[np.ndarray] = None
+    v_scale: Optional[np.ndarray] = None
 
     @property
     def num_seqs(self) -> int:
@@ -119,9 +126,10 @@ class DecodeCase:
         return int(self.block_tables.shape[1])
 
     def empty_pool(self) -> np.ndarray:
-        return nan_array(
-            (self.num_blocks, self.block_size, self.num_kv_heads, self.head_dim), self.dtype
-        )
+        shape = (self.num_blocks, self.block_size, self.num_kv_heads, self.head_dim)
+        if self.kv_dtype == "fp8_e4m3":
+            return np.full(shape, FP8_NAN_CODE, dtype=np.uint8)
+        return nan_array(shape, self.dtype)
 
     def step_writes(self) -> List[WriteChunk]:
         """The newest token of every sequence: what one decode step writes."""
@@ -418,6 +426,63 @@ def config_sink_ring(lengths=None, seed_offset: int = 5, pad_with_minus_one: boo
 
 def ring_timing_lengths(batch: int = 16) -> List[int]:
     return [100_000 - 61 * b for b in range(batch)]
+
+
+def fp8_scales(num_kv_heads: int):
+    """Per-KV-head K and V scales: N(0,1) rows reach |x| ~ 5, so
+    (5 + h/4) / 448 keeps them inside the E4M3 range; distinct per head so a
+    wrong head mapping shows."""
+    h = np.arange(num_kv_heads, dtype=np.float64)
+    k = ((5.0 + h / 4.0) / 448.0).astype(np.float32)
+    v = ((4.0 + h / 3.0) / 448.0).astype(np.float32)
+    return k, v
+
+
+def _requantise_f32(case: DecodeCase) -> DecodeCase:
+    """fp32 draws re-stored as bf16 raw rows (8-bit pools take 16-bit rows)."""
+    conv = lambda a: round_f32_to_bf16_bits(np.asarray(a, dtype=np.float32))
+    case.query = conv(case.query)
+    for ch in case.writes:
+        ch.keys, ch.values = conv(ch.keys), conv(ch.values)
+    case.dtype = "bf16"
+    return case
+
+
+def config_fp8(base=None, **kw) -> DecodeCase:
+    """A workload with 8-bit (E4M3) KV storage: the base configuration's
+    lengths, placement and values, the pools holding scaled E4M3 codes."""
+    case = (base or config_llama70b)(**kw)
+    if case.ring is not None:
+        raise ValueError("8-bit KV storage is not combined with the ring cache")
+    if case.dtype == "f32":
+        case = _requantise_f32(case)
+    case.kv_dtype = "fp8_e4m3"
+    case.k_scale, case.v_scale = fp8_scales(case.num_kv_heads)
+    case.name = case.name + "_fp8"
+    return case
+
+
+def config_tiny_fp8() -> DecodeCase:
+    """The tiny case (B 2, lengths 37 / 70, Hq 8, Hkv 2) with E4M3 pools and
+    bf16 activations; GQA 4 so the MFMA kernel serves it."""
+    seed = SEED_BASE + 11
+    case = make_paged_case("tiny", seed, "bf16", [37, 70], 8, 2, 128, 16)
+    return config_fp8(lambda: case)
+
+
+def config_llama70b_fp8() -> DecodeCase:
+    return config_fp8(config_llama70b)
+
+
+def config_embedded_1p1b_fp8() -> DecodeCase:
+    return config_fp8(config_embedded_1p1b)
+
+
+FP8_CONFIGS = {
+    "tiny_fp8": config_tiny_fp8,
+    "embedded_1p1b_fp8": config_embedded_1p1b_fp8,
+    "llama70b_b64_fp8": config_llama70b_fp8,
+}
 
 
 CONFIGS = {
