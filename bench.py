@@ -39,7 +39,8 @@ CALIBRATION_BYTES = 1 << 30  # the plain copy run after the profiled decode call
 def algorithmic_bytes(case) -> dict:
     """Bytes the decode must move at minimum: every resident K and V row once,
     query in, output out, block-table entries and lengths."""
-    s_kv = {"f32": 4, "f16": 2, "bf16": 2}[case.dtype]
+    s_act = {"f32": 4, "f16": 2, "bf16": 2}[case.dtype]
+    s_kv = 1 if getattr(case, "kv_dtype", None) == "fp8_e4m3" else s_act
     lens = case.context_lens.astype(np.int64)
     if case.ring is not None:
         lens = np.minimum(lens, case.ring.sink + case.ring.window)
@@ -56,9 +57,9 @@ def algorithmic_bytes(case) -> dict:
     for phys, rows in seen:
         unique_rows[phys] = max(rows, unique_rows.get(phys, 0))
     kv_unique = sum(unique_rows.values()) * row
-    qo = case.num_seqs * case.num_q_heads * case.head_dim * 2 * s_kv
+    qo = case.num_seqs * case.num_q_heads * case.head_dim * 2 * s_act
     tables = int(sum(-(-int(n) // case.block_size) for n in lens)) * 4 + case.num_seqs * 4
-    write = case.num_seqs * row * 2  # read + write of the new token's K and V
+    write = case.num_seqs * case.num_kv_heads * case.head_dim * 2 * (s_act + s_kv)  # K and V rows in + codes out
     return {"decode": kv_unique + qo + tables, "decode_logical": kv + qo + tables, "kv": kv,
             "kv_unique": kv_unique, "write": write, "tokens": int(lens.sum())}
 
@@ -137,7 +138,8 @@ def cpu_baseline(case, repeats: int = 2) -> dict:
             t0 = time.perf_counter()
             c0 = time.process_time()
             oracle.decode(case.query, kp, vp, case.block_tables, case.context_lens, case.scale,
-                          case.dtype, case.block_size, ring=case.ring)
+                          case.dtype, case.block_size, ring=case.ring, kv_dtype=case.kv_dtype,
+                          k_scale=case.k_scale, v_scale=case.v_scale)
             times.append(time.perf_counter() - t0)
             cpu_s.append(time.process_time() - c0)
     finally:
@@ -162,7 +164,8 @@ def main() -> int:
     ap.add_argument("--cold-steps", type=int, default=50,
                     help="extra decode calls each preceded by a 1 GiB read that evicts the caches (0 = skip)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--config", default="llama70b_b64", choices=sorted(__import__("workloads").CONFIGS),
+    ap.add_argument("--config", default="llama70b_b64",
+                    choices=sorted(list(__import__("workloads").CONFIGS) + list(__import__("workloads").FP8_CONFIGS)),
                     help="workload (default: the 70B-shaped batch the metric is quoted on; the others "
                          "are the parity configurations, timed the same way)")
     ap.add_argument("--launch", choices=("eager", "graph"), default="eager",
@@ -205,7 +208,7 @@ def main() -> int:
     if args.config == "sink_ring":  # timing set: full windows at distinct ring phases near 100k
         case = workloads.config_sink_ring(lengths=workloads.ring_timing_lengths())
     else:
-        case = workloads.CONFIGS[args.config]()
+        case = {**workloads.CONFIGS, **workloads.FP8_CONFIGS}[args.config]()
     ab = algorithmic_bytes(case)
     tdt = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}[case.dtype]
     ibits = torch.int32 if case.dtype == "f32" else torch.int16
@@ -215,13 +218,19 @@ def main() -> int:
         return torch.from_numpy(np.ascontiguousarray(raw).view(raw_view)).view(tdt).to(dev)
 
     shape = (case.num_blocks, case.block_size, case.num_kv_heads, case.head_dim)
-    k_cache = torch.empty(shape, dtype=tdt, device=dev)
-    v_cache = torch.empty(shape, dtype=tdt, device=dev)
-    nan_bits = int(np.array(workloads.NAN_BITS[case.dtype],
-                            dtype=np.uint32 if case.dtype == "f32" else np.uint16).view(raw_view))
-    k_cache.view(ibits).fill_(nan_bits)
-    v_cache.view(ibits).fill_(nan_bits)
-    pool = pk.Pool(k_cache, v_cache, case.block_size)
+    if case.kv_dtype == "fp8_e4m3":
+        k_cache = torch.full(shape, workloads.FP8_NAN_CODE, dtype=torch.uint8, device=dev)
+        v_cache = torch.full(shape, workloads.FP8_NAN_CODE, dtype=torch.uint8, device=dev)
+        pool = pk.Pool(k_cache, v_cache, case.block_size, act_dtype=tdt, k_scale=case.k_scale,
+                       v_scale=case.v_scale)
+    else:
+        k_cache = torch.empty(shape, dtype=tdt, device=dev)
+        v_cache = torch.empty(shape, dtype=tdt, device=dev)
+        nan_bits = int(np.array(workloads.NAN_BITS[case.dtype],
+                                dtype=np.uint32 if case.dtype == "f32" else np.uint16).view(raw_view))
+        k_cache.view(ibits).fill_(nan_bits)
+        v_cache.view(ibits).fill_(nan_bits)
+        pool = pk.Pool(k_cache, v_cache, case.block_size)
     ring = None
     if case.ring is not None:
         cap = case.ring.sink + case.ring.window
@@ -340,8 +349,10 @@ def main() -> int:
                     "block 16, lengths 32xU[50,500] + 19xU[500,2000] + 13xU[2000,8000], "
                     "shuffled blocks, pool 1.1x need")
     else:
+        kv_name = "E4M3 (8-bit, per-head scales)" if case.kv_dtype == "fp8_e4m3" else case.dtype
         workload = (f"{args.config}: paged decode, B {case.num_seqs}, Hq {case.num_q_heads}, "
-                    f"Hkv {case.num_kv_heads}, D {case.head_dim}, {case.dtype} KV, block {case.block_size}"
+                    f"Hkv {case.num_kv_heads}, D {case.head_dim}, {kv_name} KV, {case.dtype} query, "
+                    f"block {case.block_size}"
                     + (f", sink {case.ring.sink} + ring {case.ring.window}" if case.ring else ""))
     result = {
         "metric": "paged decode attention: effective KV GB/s (% of HBM peak) and tokens/s",
@@ -363,6 +374,7 @@ def main() -> int:
             "max_context_len": max_ctx,
             "num_blocks": case.num_blocks,
             "seed": case.seed,
+            "kv_storage": "e4m3 codes, per-head scales" if case.kv_dtype == "fp8_e4m3" else case.dtype,
             "launch": ("hip graph replay (cache write graph + decode call graph)" if args.launch == "graph"
                        else "eager launches"),
         },

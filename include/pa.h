@@ -63,7 +63,9 @@ typedef enum {
   PA_ERR_UNSUPPORTED = -5  /* a combination the library has no kernel for */
 } pa_status;
 
-typedef enum { PA_F32 = 0, PA_F16 = 1, PA_BF16 = 2 } pa_dtype;
+/* PA_FP8_E4M3 is a storage type of K/V pools only: such pools are made by
+ * pa_create_pool_fp8, and pa_create_pool rejects it. */
+typedef enum { PA_F32 = 0, PA_F16 = 1, PA_BF16 = 2, PA_FP8_E4M3 = 3 } pa_dtype;
 
 /* Opaque pool handle: host-side state only (shapes, free list, refcounts). */
 typedef struct pa_pool pa_pool;
@@ -100,6 +102,22 @@ typedef struct {
  * The handle never frees k_cache / v_cache.  *out is set on success. */
 int pa_create_pool(pa_pool **out, int32_t num_blocks, int32_t block_size, int32_t num_kv_heads,
                    int32_t head_dim, pa_dtype dtype, void *k_cache, void *v_cache);
+
+/* Pools of 8-bit K/V [P4, section "工程边界与架构取舍": FP8 storage halves
+ * the KV cache].  k_cache / v_cache hold E4M3 codes (OCP 8-bit float: 4
+ * exponent bits, bias 7, 3 mantissa bits, largest finite 448, S.1111.111 =
+ * NaN), [num_blocks, block_size, num_kv_heads, head_dim] bytes each.  A code
+ * c of KV head h stands for k_scale[h] * value(c) (V: v_scale[h]).
+ * act_dtype (PA_F16 or PA_BF16) is the dtype of the query, the output and
+ * the key/value rows handed to pa_reshape_and_cache, which stores
+ * nearest-even E4M3 codes of fp32(x) * fp32(1 / scale[h]), saturating at
+ * +-448.  k_scale, v_scale: host float [num_kv_heads], finite and > 0,
+ * copied into the handle; num_kv_heads <= 64.  Decode on such a pool needs
+ * 4 <= Hq / Hkv <= 16 and no ring (else PA_ERR_UNSUPPORTED).  Other
+ * arguments and errors as pa_create_pool. */
+int pa_create_pool_fp8(pa_pool **out, int32_t num_blocks, int32_t block_size,
+                       int32_t num_kv_heads, int32_t head_dim, pa_dtype act_dtype,
+                       const float *k_scale, const float *v_scale, void *k_cache, void *v_cache);
 
 /* Free the host-side state (NULL is a no-op).  Device memory is untouched. */
 void pa_destroy_pool(pa_pool *pool);
@@ -145,7 +163,8 @@ int pa_compute_slot_mapping(const pa_pool *pool, const int32_t *block_tables, in
 /* --------------------------------------------------------- write side --- */
 
 /* Device: copy token i's key and value rows ([num_kv_heads, head_dim] each,
- * pool dtype, no conversion) into flat pool slot slot_mapping[i]
+ * pool dtype, no conversion; for an 8-bit pool the rows are in its act_dtype
+ * and are stored as scaled E4M3 codes) into flat pool slot slot_mapping[i]
  * (block = slot / block_size, row = slot % block_size).  key, value: device
  * [num_tokens, num_kv_heads, head_dim]; slot_mapping: device int32
  * [num_tokens]; a negative slot is padding and is skipped, and so is a slot

@@ -72,9 +72,21 @@ def e4m3_encode_one(x: float) -> int:
 
 
 def e4m3_encode(x: np.ndarray) -> np.ndarray:
+    """Array form of ``e4m3_encode_one``: the two finite magnitudes around
+    |x| (the table is sorted), the nearer one, ties to the even code."""
     x = np.asarray(x, dtype=np.float32)
-    flat = np.array([e4m3_encode_one(v) for v in x.reshape(-1)], dtype=np.uint8)
-    return flat.reshape(x.shape)
+    a = np.abs(x.astype(np.float64))
+    hi = np.clip(np.searchsorted(_MAGNITUDES, a, side="left"), 0, 0x7E)  # first magnitude >= a
+    lo = np.clip(hi - 1, 0, 0x7E)
+    d_lo = np.abs(a - _MAGNITUDES[lo])
+    d_hi = np.abs(_MAGNITUDES[hi] - a)
+    code = np.where(d_lo < d_hi, lo, hi)
+    tie = d_lo == d_hi
+    code = np.where(tie, np.where(lo % 2 == 0, lo, hi), code)
+    code = np.where(a >= MAX_FINITE, 0x7E, code)
+    code = code | np.where(np.signbit(x), 0x80, 0)
+    code = np.where(np.isnan(x), NAN_CODE, code)
+    return code.astype(np.uint8)
 
 
 def inverse_scale(scale: np.ndarray) -> np.ndarray:

@@ -79,20 +79,43 @@ def _ring_ptr(ring: Optional[Ring]):
 class Pool:
     """One layer's paged K/V pools (caller-owned device tensors) + allocator."""
 
-    def __init__(self, k_cache, v_cache, block_size: int):
+    def __init__(self, k_cache, v_cache, block_size: int, act_dtype=None, k_scale=None, v_scale=None):
+        """``k_cache``/``v_cache`` of dtype uint8 make an 8-bit (E4M3) pool:
+        ``act_dtype`` (torch.float16 / torch.bfloat16) is then the dtype of
+        queries, outputs and written rows, and ``k_scale``/``v_scale`` hold
+        one float per KV head."""
+        import torch
+
         lib = _lib.load()
         if k_cache.shape != v_cache.shape or k_cache.dtype != v_cache.dtype or k_cache.dim() != 4:
             raise ValueError("k_cache and v_cache must both be [num_blocks, block_size, Hkv, D]")
         num_blocks, bs, hkv, d = k_cache.shape
         if bs != block_size:
             raise ValueError("block_size does not match the pool shape")
-        self.dtype = _torch_dtype_name(k_cache)
         self.k_cache, self.v_cache = k_cache, v_cache
         self.num_blocks, self.block_size, self.num_kv_heads, self.head_dim = num_blocks, bs, hkv, d
         handle = ctypes.c_void_p()
-        _check(lib.pa_create_pool(ctypes.byref(handle), num_blocks, bs, hkv, d, DTYPES[self.dtype],
-                                  _dev_ptr(k_cache, "k_cache"), _dev_ptr(v_cache, "v_cache")),
-               "pa_create_pool")
+        self.kv_fp8 = k_cache.dtype == torch.uint8
+        if self.kv_fp8:
+            if act_dtype not in (torch.float16, torch.bfloat16) or k_scale is None or v_scale is None:
+                raise ValueError("an 8-bit pool needs act_dtype (f16/bf16) and per-head k_scale, v_scale")
+            self.act_dtype = act_dtype
+            self.dtype = {torch.float16: "f16", torch.bfloat16: "bf16"}[act_dtype]
+            ks = np.ascontiguousarray(k_scale, dtype=np.float32)
+            vs = np.ascontiguousarray(v_scale, dtype=np.float32)
+            if ks.shape != (hkv,) or vs.shape != (hkv,):
+                raise ValueError("k_scale and v_scale need one value per KV head")
+            fp = ctypes.POINTER(ctypes.c_float)
+            _check(lib.pa_create_pool_fp8(ctypes.byref(handle), num_blocks, bs, hkv, d, DTYPES[self.dtype],
+                                          ks.ctypes.data_as(fp), vs.ctypes.data_as(fp),
+                                          _dev_ptr(k_cache, "k_cache"), _dev_ptr(v_cache, "v_cache")),
+                   "pa_create_pool_fp8")
+        else:
+            self.act_dtype = k_cache.dtype
+            self.dtype = _torch_dtype_name(k_cache)
+            _check(lib.pa_create_pool(ctypes.byref(handle), num_blocks, bs, hkv, d, DTYPES[self.dtype],
+                                      _dev_ptr(k_cache, "k_cache"), _dev_ptr(v_cache, "v_cache")),
+                   "pa_create_pool")
         self._h = handle
         self._lib = lib
 
@@ -152,7 +175,7 @@ def reshape_and_cache(pool: Pool, key, value, slot_mapping, stream=None) -> None
     n = int(slot_mapping.shape[0])
     if n == 0:
         return
-    if key.dtype != pool.k_cache.dtype or value.dtype != pool.k_cache.dtype:
+    if key.dtype != pool.act_dtype or value.dtype != pool.act_dtype:
         raise ValueError("key/value dtype must match the pool")
     if tuple(key.shape) != (n, pool.num_kv_heads, pool.head_dim) or key.shape != value.shape:
         raise ValueError("key/value must be [N, Hkv, D]")
@@ -184,7 +207,7 @@ def decode(pool: Pool, out, query, block_tables, context_lens, max_context_len: 
     b, hq, d = query.shape
     if tuple(out.shape) != (b, hq, d) or d != pool.head_dim:
         raise ValueError("out/query must be [B, Hq, D] with D = the pool's head size")
-    if query.dtype != pool.k_cache.dtype or out.dtype != pool.k_cache.dtype:
+    if query.dtype != pool.act_dtype or out.dtype != pool.act_dtype:
         raise ValueError("query/out dtype must match the pool")
     ws_ptr, ws_bytes = None, 0
     if workspace is not None:

@@ -109,6 +109,17 @@ int pa_reshape_and_cache(pa_pool *pool, const void *key, const void *value,
   if (key == nullptr || value == nullptr || slot_mapping == nullptr) return PA_ERR_INVAL;
   if (!pa::aligned16(key) || !pa::aligned16(value)) return PA_ERR_INVAL;
   if ((reinterpret_cast<uintptr_t>(slot_mapping) & 3u) != 0) return PA_ERR_INVAL;
+  if (pool->kv_fp8) {
+    pa::KvScales inv{};
+    for (int h = 0; h < pool->num_kv_heads; ++h) {
+      inv.k[h] = pool->k_inv[h];
+      inv.v[h] = pool->v_inv[h];
+    }
+    return pa::hip_status(pa::launch_reshape_and_cache_fp8(
+        pool->dtype, pool->k_cache, pool->v_cache, key, value, slot_mapping, num_tokens,
+        pool->num_kv_heads, pool->head_dim, (int64_t)pool->num_blocks * pool->block_size, inv,
+        static_cast<hipStream_t>(stream)));
+  }
   return pa::hip_status(pa::launch_reshape_and_cache(
       pool->dtype, pool->k_cache, pool->v_cache, key, value, slot_mapping, num_tokens,
       pool->num_kv_heads * pool->head_dim, (int64_t)pool->num_blocks * pool->block_size,
@@ -146,6 +157,9 @@ int pa_decode(pa_pool *pool, void *out, const void *query, const int32_t *block_
   if (num_q_heads % pool->num_kv_heads != 0) return PA_ERR_INVAL;
   const int group = num_q_heads / pool->num_kv_heads;
   if (!pa::ring_valid(ring)) return PA_ERR_INVAL;
+  if (pool->kv_fp8 &&
+      (ring != nullptr || pa::choose_decode_kernel(pool->dtype, group).kernel != pa::DecodeKernel::kMfma))
+    return PA_ERR_UNSUPPORTED;
   if (num_seqs == 0) return PA_OK;
   if (out == nullptr || query == nullptr || block_tables == nullptr || context_lens == nullptr)
     return PA_ERR_INVAL;
@@ -198,14 +212,20 @@ int pa_decode(pa_pool *pool, void *out, const void *query, const int32_t *block_
   a.ring_sink = ring ? ring->sink : 0;
   a.ring_window = ring ? ring->window : 1;
   a.scale_log2 = scale * pa::kLog2eHost;
+  if (pool->kv_fp8)
+    for (int h = 0; h < pool->num_kv_heads; ++h) {
+      a.kv_scale.k[h] = pool->k_scale[h];
+      a.kv_scale.v[h] = pool->v_scale[h];
+    }
 
   const pa::DecodeChoice choice = pa::choose_decode_kernel(pool->dtype, group);
   const int nchunk = choice.kernel == pa::DecodeKernel::kMfma
                          ? 1
                          : (group + choice.heads_per_pass - 1) / choice.heads_per_pass;
   if ((int64_t)pool->num_kv_heads * nchunk > INT32_MAX) return PA_ERR_UNSUPPORTED;
-  return pa::hip_status(pa::launch_decode(a, pool->dtype, pool->head_dim, ring != nullptr, choice,
-                                          num_seqs, static_cast<hipStream_t>(stream)));
+  return pa::hip_status(pa::launch_decode(a, pool->dtype, pool->head_dim, ring != nullptr,
+                                          pool->kv_fp8, choice, num_seqs,
+                                          static_cast<hipStream_t>(stream)));
 }
 
 }  // extern "C"

@@ -28,6 +28,7 @@
 //  * The summation order depends only on logical positions and lengths, so
 //    outputs are bit-identical under relabelling of physical blocks.
 #include <algorithm>
+#include <type_traits>
 
 #include "device_common.h"
 #include "launch.h"
@@ -227,6 +228,29 @@ __device__ __forceinline__ void rope_frag16(uint4 (&f)[KB], const float *cs, int
   }
 }
 
+// 8-bit pools: one lane's V codes for one row (D/16 codes), loaded raw and
+// widened to the 16-bit chunk the LDS tile holds.
+template <int D>
+struct V8Chunk;
+template <>
+struct V8Chunk<128> {
+  typedef uint2 type;
+  static __device__ __forceinline__ uint2 load(__amdgpu_buffer_rsrc_t r, int off) {
+    return buffer_load8(r, off);
+  }
+  template <class T>
+  static __device__ __forceinline__ uint4 widen(const uint2 &v) { return fp8x8_to_16<T>(v); }
+};
+template <>
+struct V8Chunk<64> {
+  typedef uint32_t type;
+  static __device__ __forceinline__ uint32_t load(__amdgpu_buffer_rsrc_t r, int off) {
+    return buffer_load4(r, off);
+  }
+  template <class T>
+  static __device__ __forceinline__ uint2 widen(const uint32_t &v) { return fp8x4_to_16<T>(v); }
+};
+
 template <int D>
 struct VChunk;
 template <>
@@ -355,7 +379,7 @@ __device__ __forceinline__ void locate_tile(const int *s_tfirst, int num_seqs, i
   t = y - s_tfirst[b];
 }
 
-template <class T, int D, bool RING>
+template <class T, int D, bool RING, bool KV8>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void decode_mfma_kernel(DecodeArgs a) {
   constexpr int KB = D / 32;  // score MFMAs per tile
@@ -364,6 +388,13 @@ void decode_mfma_kernel(DecodeArgs a) {
   constexpr int kVRow = MfmaLds<D>::kVRowBytes;
   typedef typename T::storage st;
   typedef typename VChunk<D>::type vchunk;
+  // 8-bit pools (KV8): one byte per K/V element.  A lane's 16-byte K load
+  // then carries 16 dimensions, the A operands of two score MFMAs; the
+  // query fragments follow the same dimension order.
+  static_assert(!(KV8 && RING), "8-bit pools have no ring mode");
+  constexpr int KVB = KV8 ? 1 : (int)sizeof(st);  // bytes per K/V element
+  constexpr int KLD = KV8 ? D / 64 : KB;          // 16-byte K loads per lane per tile
+  typedef typename std::conditional<KV8, typename V8Chunk<D>::type, vchunk>::type vload;
 
   __shared__ int s_tfirst[kMaxSchedSeqs + 1];
   __shared__ int s_len[kMaxSchedSeqs];
@@ -393,12 +424,16 @@ void decode_mfma_kernel(DecodeArgs a) {
   const int bmask = (1 << a.block_shift) - 1;
   char *vt = s_vtiles[wave];
   uint4 *qs = s_q[wave];
-  const int k_off = (int)((row16 * row_stride + 8 * grp) * sizeof(st));
-  const int q_off = (int)((row16 * D + 8 * grp) * sizeof(st));
+  const int k_off = (int)((row16 * row_stride + (KV8 ? 16 : 8) * grp) * KVB);
+  // query dimension of element 0 of score MFMA kb's fragment in this lane
+  auto q_dim = [&](int kb) { return KV8 ? 64 * (kb >> 1) + 16 * grp + 8 * (kb & 1) : 32 * kb + 8 * grp; };
   int v_off[4];
 #pragma unroll
   for (int tau = 0; tau < 4; ++tau)
-    v_off[tau] = (int)(((4 * grp + tau) * row_stride + EV * row16) * sizeof(st));
+    v_off[tau] = (int)(((4 * grp + tau) * row_stride + EV * row16) * KVB);
+  // dequantisation of 8-bit pools: scores by k_scale, outputs by v_scale
+  const float sl2 = KV8 ? a.scale_log2 * a.kv_scale.k[g] : a.scale_log2;
+  const float vscale = KV8 ? a.kv_scale.v[g] : 1.f;
 
   // online-softmax state of the current (b, g) segment
   f32x4 acc[NB];
@@ -451,16 +486,17 @@ void decode_mfma_kernel(DecodeArgs a) {
           const_cast<char *>(static_cast<const char *>(a.query) + qoff), (short)0,
           mm ? G * D * (int)sizeof(st) : 0, kBufferWord3);
 #pragma unroll
-      for (int kb = 0; kb < KB; ++kb) qtmp[s2][kb] = buffer_load16(qr, q_off + 64 * kb);
+      for (int kb = 0; kb < KB; ++kb)
+        qtmp[s2][kb] = buffer_load16(qr, (int)((row16 * D + q_dim(kb)) * sizeof(st)));
       mm &= mm - 1;
     }
     if (lane < cnt) {
       const int64_t off = ((int64_t)min(max(phys, 0), a.num_blocks - 1) * a.kv_block_stride +
                            (int64_t)(r0 & bmask) * row_stride + head_off) *
-                          (int64_t)sizeof(st);
+                          (int64_t)KVB;
       toff_lo = (int)(uint32_t)off;
       toff_hi = (int)(off >> 32);
-      tnrec = (int)(((tvalid - 1) * row_stride + D) * sizeof(st));  // tvalid >= 1 here
+      tnrec = (int)(((tvalid - 1) * row_stride + D) * KVB);  // tvalid >= 1 here
     }
 #pragma unroll
     for (int s2 = 0; s2 < kQSlots; ++s2)
@@ -470,7 +506,7 @@ void decode_mfma_kernel(DecodeArgs a) {
 
   // Loads of staged tile j (j >= cnt: an empty tile, no memory access).
   // They are unconditional so that every step has the same wait counts.
-  auto load_tile = [&](int j, uint4 (&k)[KB], vchunk (&v)[4]) {
+  auto load_tile = [&](int j, uint4 (&k)[KLD], vload (&v)[4]) {
     const int jj = min(j, kWave - 1);
     const uint64_t off = ((uint64_t)(uint32_t)rd(toff_hi, jj) << 32) | (uint32_t)rd(toff_lo, jj);
     const int nrec = j < cnt ? rd(tnrec, jj) : 0;
@@ -479,9 +515,12 @@ void decode_mfma_kernel(DecodeArgs a) {
     const auto vr = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<char *>(static_cast<const char *>(a.v_cache) + off), (short)0, nrec, kBufferWord3);
 #pragma unroll
-    for (int kb = 0; kb < KB; ++kb) k[kb] = buffer_load16(kr, k_off + 64 * kb);
+    for (int kb = 0; kb < KLD; ++kb) k[kb] = buffer_load16(kr, k_off + 64 * kb);
 #pragma unroll
-    for (int tau = 0; tau < 4; ++tau) v[tau] = VChunk<D>::load(vr, v_off[tau]);
+    for (int tau = 0; tau < 4; ++tau) {
+      if constexpr (KV8) v[tau] = V8Chunk<D>::load(vr, v_off[tau]);
+      else v[tau] = VChunk<D>::load(vr, v_off[tau]);
+    }
   };
 
   // Segment start: the query fragment of the tile's sequence from its slot.
@@ -497,7 +536,23 @@ void decode_mfma_kernel(DecodeArgs a) {
     seg_whole = whole;
   };
 
-  auto process_tile = [&](int j, uint4 (&kf)[KB], vchunk (&vf)[4]) {
+  auto process_tile = [&](int j, uint4 (&kraw)[KLD], vload (&vraw)[4]) {
+    uint4 kf[KB];
+    vchunk vf[4];
+    if constexpr (KV8) {
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) {
+        const uint4 w = kraw[kb >> 1];
+        kf[kb] = fp8x8_to_16<T>((kb & 1) ? make_uint2(w.z, w.w) : make_uint2(w.x, w.y));
+      }
+#pragma unroll
+      for (int tau = 0; tau < 4; ++tau) vf[tau] = V8Chunk<D>::template widen<T>(vraw[tau]);
+    } else {
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) kf[kb] = kraw[kb];
+#pragma unroll
+      for (int tau = 0; tau < 4; ++tau) vf[tau] = vraw[tau];
+    }
     const int jj = min(j, kWave - 1);
     const int valid = j < cnt ? rd(tvalid, jj) : 0;
     if constexpr (RING) {
@@ -515,7 +570,7 @@ void decode_mfma_kernel(DecodeArgs a) {
 
     float sc[4];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) sc[r] = (4 * grp + r < valid) ? s[r] * a.scale_log2 : -INFINITY;
+    for (int r = 0; r < 4; ++r) sc[r] = (4 * grp + r < valid) ? s[r] * sl2 : -INFINITY;
     const float lmax = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
     if (__any(lmax > m_run + kRescaleSlack)) {
       float tmax = fmaxf(lmax, __shfl_xor(lmax, 16));
@@ -570,7 +625,7 @@ void decode_mfma_kernel(DecodeArgs a) {
       for (int r = 0; r < 4; ++r) {
         const int h = 4 * grp + r;
         if (h < G) {
-          const float inv = 1.f / lh[r];
+          const float inv = vscale / lh[r];
 #pragma unroll
           for (int e = 0; e < NB; ++e) out[h * D + 16 * e + row16] = T::from_float(acc[e][r] * inv);
         }
@@ -582,7 +637,7 @@ void decode_mfma_kernel(DecodeArgs a) {
       for (int r = 0; r < 4; ++r) {
         const int h = 4 * grp + r;
         if (h < G) {
-          const float inv = 1.f / lh[r];
+          const float inv = vscale / lh[r];
 #pragma unroll
           for (int e = 0; e < NB; ++e) po[h * D + 16 * e + row16] = acc[e][r] * inv;
         }
@@ -597,9 +652,9 @@ void decode_mfma_kernel(DecodeArgs a) {
   // Pipeline of kStages register buffers: tile j is consumed from buffer
   // j % kStages while tiles j+1 .. j+kStages-1 are in flight.
   constexpr int S = kStages;
-  uint4 kbuf[S][KB];
-  vchunk vbuf[S][4];
-  auto step = [&](int j, uint4 (&kc)[KB], vchunk (&vc)[4], uint4 (&kn)[KB], vchunk (&vn)[4]) {
+  uint4 kbuf[S][KLD];
+  vload vbuf[S][4];
+  auto step = [&](int j, uint4 (&kc)[KLD], vload (&vc)[4], uint4 (&kn)[KLD], vload (&vn)[4]) {
     load_tile(j + S - 1, kn, vn);
     if (j < cnt) {
       const int b = rd(tb, j), flag = rd(tflag, j);
@@ -980,20 +1035,23 @@ int persistent_grid(const void *kernel, int per_cu_cap) {
   return cus * std::max(1, std::min(per_cu, per_cu_cap));
 }
 
-template <class T, int D, bool RING>
+template <class T, int D, bool RING, bool KV8 = false>
 hipError_t launch_typed(const DecodeArgs &a, DecodeChoice choice, hipStream_t stream) {
   const dim3 block(kNW * kWave);
+  if constexpr (KV8) {  // 8-bit pools: the MFMA kernel only
+    if (choice.kernel != DecodeKernel::kMfma) return hipErrorInvalidValue;
+  }
   if constexpr (T::kBytes == 2) {
     if (choice.kernel == DecodeKernel::kMfma) {
       // one work-group (one wave per SIMD) per CU: a lone wave per SIMD is
       // never starved by an older neighbour, so equal tile counts finish
       // at nearly equal times
       static const int grid_max = std::min(
-          persistent_grid(reinterpret_cast<const void *>(&decode_mfma_kernel<T, D, RING>), 1),
+          persistent_grid(reinterpret_cast<const void *>(&decode_mfma_kernel<T, D, RING, KV8>), 1),
           kMaxPersistentWaves / kNW);
       // at least one group of Hkv waves
       const int grid = std::max(grid_max, (a.num_kv_heads + kNW - 1) / kNW);
-      hipLaunchKernelGGL((decode_mfma_kernel<T, D, RING>), dim3(grid), block, 0, stream, a);
+      hipLaunchKernelGGL((decode_mfma_kernel<T, D, RING, KV8>), dim3(grid), block, 0, stream, a);
       hipError_t err = hipGetLastError();
       if (err != hipSuccess) return err;
       hipLaunchKernelGGL((decode_streamk_reduce_kernel<T, D>),
@@ -1002,6 +1060,7 @@ hipError_t launch_typed(const DecodeArgs &a, DecodeChoice choice, hipStream_t st
       return hipGetLastError();
     }
   }
+  if constexpr (KV8) return hipErrorInvalidValue;
   const int64_t pairs_bound = (int64_t)a.num_seqs * a.max_parts;
   const int nchunk = (a.group + choice.heads_per_pass - 1) / choice.heads_per_pass;
   const int64_t items = pairs_bound * a.num_kv_heads * nchunk;
@@ -1033,8 +1092,15 @@ hipError_t launch_typed(const DecodeArgs &a, DecodeChoice choice, hipStream_t st
 }
 
 template <class T>
-hipError_t launch_dtype(const DecodeArgs &a, int head_dim, bool ring, DecodeChoice choice,
-                        hipStream_t stream) {
+hipError_t launch_dtype(const DecodeArgs &a, int head_dim, bool ring, bool kv_fp8,
+                        DecodeChoice choice, hipStream_t stream) {
+  if constexpr (T::kBytes == 2) {
+    if (kv_fp8) {
+      if (ring) return hipErrorInvalidValue;
+      return head_dim == 128 ? launch_typed<T, 128, false, true>(a, choice, stream)
+                             : launch_typed<T, 64, false, true>(a, choice, stream);
+    }
+  }
   if (head_dim == 128)
     return ring ? launch_typed<T, 128, true>(a, choice, stream)
                 : launch_typed<T, 128, false>(a, choice, stream);
@@ -1045,7 +1111,7 @@ hipError_t launch_dtype(const DecodeArgs &a, int head_dim, bool ring, DecodeChoi
 }  // namespace
 
 hipError_t launch_decode(const DecodeArgs &args, pa_dtype dtype, int head_dim, bool ring,
-                         DecodeChoice choice, int num_seqs, hipStream_t stream) {
+                         bool kv_fp8, DecodeChoice choice, int num_seqs, hipStream_t stream) {
   if (dtype == PA_F32) choice.kernel = DecodeKernel::kValu;  // no fp32 MFMA kernel
   // The device-side schedule holds up to kMaxSchedSeqs sequences; larger
   // batches run as consecutive slices on the same stream (each slice reuses
@@ -1061,9 +1127,9 @@ hipError_t launch_decode(const DecodeArgs &args, pa_dtype dtype, int head_dim, b
     a.context_lens = args.context_lens + s0;
     hipError_t err;
     switch (dtype) {
-      case PA_F16: err = launch_dtype<F16>(a, head_dim, ring, choice, stream); break;
-      case PA_BF16: err = launch_dtype<BF16>(a, head_dim, ring, choice, stream); break;
-      default: err = launch_dtype<F32>(a, head_dim, ring, choice, stream); break;
+      case PA_F16: err = launch_dtype<F16>(a, head_dim, ring, kv_fp8, choice, stream); break;
+      case PA_BF16: err = launch_dtype<BF16>(a, head_dim, ring, kv_fp8, choice, stream); break;
+      default: err = launch_dtype<F32>(a, head_dim, ring, kv_fp8, choice, stream); break;
     }
     if (err != hipSuccess) return err;
   }

@@ -45,6 +45,11 @@ struct F16 {
     return __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(f16x4, a),
                                                  __builtin_bit_cast(f16x4, b), c, 0, 0, 0);
   }
+  // Two E4M3 codes (bytes 2 HI, 2 HI + 1 of w) to two f16 values, exactly.
+  template <bool HI>
+  static __device__ __forceinline__ uint32_t from_fp8_pair(uint32_t w) {
+    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, HI));
+  }
 };
 
 struct BF16 {
@@ -65,6 +70,12 @@ struct BF16 {
   static __device__ __forceinline__ f32x4 mfma_16x16x16(uint2 a, uint2 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(bf16x4, a),
                                                      __builtin_bit_cast(bf16x4, b), c, 0, 0, 0);
+  }
+  // Two E4M3 codes (bytes 2 HI, 2 HI + 1 of w) to two bf16 values, exactly
+  // (every E4M3 value, subnormals included, is a bf16 value).
+  template <bool HI>
+  static __device__ __forceinline__ uint32_t from_fp8_pair(uint32_t w) {
+    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, HI));
   }
 };
 
@@ -132,6 +143,21 @@ __device__ __forceinline__ uint4 buffer_load16(__amdgpu_buffer_rsrc_t r, int off
 }
 __device__ __forceinline__ uint2 buffer_load8(__amdgpu_buffer_rsrc_t r, int off) {
   return __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0));
+}
+__device__ __forceinline__ uint32_t buffer_load4(__amdgpu_buffer_rsrc_t r, int off) {
+  return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
+}
+
+// Eight / four E4M3 codes to 16-bit values of the tag T (little-endian
+// order kept: code e lands in 16-bit element e).
+template <class T>
+__device__ __forceinline__ uint4 fp8x8_to_16(uint2 v) {
+  return make_uint4(T::template from_fp8_pair<false>(v.x), T::template from_fp8_pair<true>(v.x),
+                    T::template from_fp8_pair<false>(v.y), T::template from_fp8_pair<true>(v.y));
+}
+template <class T>
+__device__ __forceinline__ uint2 fp8x4_to_16(uint32_t v) {
+  return make_uint2(T::template from_fp8_pair<false>(v), T::template from_fp8_pair<true>(v));
 }
 
 }  // namespace pa

@@ -16,6 +16,14 @@ constexpr int kTileTokens = 16;
 constexpr int kDecodeWaves = 4;
 constexpr float kLog2eHost = 1.4426950408889634f;
 
+// Per-KV-head factors of 8-bit pools, passed by value in kernel arguments:
+// the decode kernels take the scales, the cache write the inverse scales.
+constexpr int kMaxFp8HeadsHost = 64;
+struct KvScales {
+  float k[kMaxFp8HeadsHost];
+  float v[kMaxFp8HeadsHost];
+};
+
 struct DecodeArgs {
   void *out;
   const void *query;
@@ -44,6 +52,7 @@ struct DecodeArgs {
   int32_t ring_sink;
   int32_t ring_window;
   float scale_log2;  // scale * log2(e)
+  KvScales kv_scale;  // 8-bit pools: dequantisation scales per KV head
 };
 
 enum class DecodeKernel { kMfma, kValu };
@@ -60,13 +69,21 @@ struct DecodeChoice {
 DecodeChoice choose_decode_kernel(pa_dtype dtype, int group);
 int choose_partition_tokens(int64_t effective_max_context);
 
-hipError_t launch_decode(const DecodeArgs &a, pa_dtype dtype, int head_dim, bool ring,
+// dtype: the query/output dtype; kv_fp8: the pools hold E4M3 codes.
+hipError_t launch_decode(const DecodeArgs &a, pa_dtype dtype, int head_dim, bool ring, bool kv_fp8,
                          DecodeChoice choice, int num_seqs, hipStream_t stream);
 
 hipError_t launch_reshape_and_cache(pa_dtype dtype, void *k_cache, void *v_cache,
                                     const void *key, const void *value,
                                     const int32_t *slot_mapping, int32_t num_tokens,
                                     int32_t row_elems, int64_t num_slots, hipStream_t stream);
+
+// 8-bit pools: quantise rows of act dtype (F16/BF16) with inverse scales.
+hipError_t launch_reshape_and_cache_fp8(pa_dtype act_dtype, void *k_cache, void *v_cache,
+                                        const void *key, const void *value,
+                                        const int32_t *slot_mapping, int32_t num_tokens,
+                                        int32_t num_kv_heads, int32_t head_dim, int64_t num_slots,
+                                        const KvScales &inv, hipStream_t stream);
 
 hipError_t launch_rope_table_init(float *table, int32_t capacity, int32_t head_dim,
                                   float rope_base, hipStream_t stream);

@@ -11,6 +11,8 @@
 #include <cstring>
 #include <new>
 
+#include <cmath>
+
 #include "pool_internal.h"
 
 namespace pa {
@@ -46,6 +48,7 @@ int pa_create_pool(pa_pool **out, int32_t num_blocks, int32_t block_size, int32_
   p->num_kv_heads = num_kv_heads;
   p->head_dim = head_dim;
   p->dtype = dtype;
+  p->kv_fp8 = false;
   p->k_cache = k_cache;
   p->v_cache = v_cache;
   try {
@@ -60,6 +63,41 @@ int pa_create_pool(pa_pool **out, int32_t num_blocks, int32_t block_size, int32_
   }
   p->used = 0;
   p->shared = 0;
+  *out = p;
+  return PA_OK;
+}
+
+int pa_create_pool_fp8(pa_pool **out, int32_t num_blocks, int32_t block_size,
+                       int32_t num_kv_heads, int32_t head_dim, pa_dtype act_dtype,
+                       const float *k_scale, const float *v_scale, void *k_cache, void *v_cache) {
+  if (out == nullptr) return PA_ERR_INVAL;
+  *out = nullptr;
+  if (act_dtype != PA_F16 && act_dtype != PA_BF16) return PA_ERR_INVAL;
+  if (num_kv_heads <= 0 || num_kv_heads > pa::kMaxFp8Heads) return PA_ERR_INVAL;
+  if (k_scale == nullptr || v_scale == nullptr) return PA_ERR_INVAL;
+  for (int h = 0; h < num_kv_heads; ++h) {
+    if (!(std::isfinite(k_scale[h]) && k_scale[h] > 0.f)) return PA_ERR_INVAL;
+    if (!(std::isfinite(v_scale[h]) && v_scale[h] > 0.f)) return PA_ERR_INVAL;
+  }
+  pa_pool *p = nullptr;
+  const int rc = pa_create_pool(&p, num_blocks, block_size, num_kv_heads, head_dim, act_dtype,
+                                k_cache, v_cache);
+  if (rc != PA_OK) return rc;
+  try {
+    p->k_scale.assign(k_scale, k_scale + num_kv_heads);
+    p->v_scale.assign(v_scale, v_scale + num_kv_heads);
+    p->k_inv.resize(num_kv_heads);
+    p->v_inv.resize(num_kv_heads);
+  } catch (...) {
+    delete p;
+    return PA_ERR_NOMEM;
+  }
+  for (int h = 0; h < num_kv_heads; ++h) {  // float division, rounded once
+    volatile float one = 1.0f;
+    p->k_inv[h] = one / k_scale[h];
+    p->v_inv[h] = one / v_scale[h];
+  }
+  p->kv_fp8 = true;
   *out = p;
   return PA_OK;
 }

@@ -14,7 +14,10 @@ struct pa_pool {
   int32_t block_size;
   int32_t num_kv_heads;
   int32_t head_dim;
-  pa_dtype dtype;
+  pa_dtype dtype;  // element type of K/V rows, or the activation type of an 8-bit pool
+  bool kv_fp8;     // pools hold E4M3 codes scaled per KV head
+  std::vector<float> k_scale, v_scale;  // 8-bit pools: per-head scales
+  std::vector<float> k_inv, v_inv;      // fp32(1 / scale)
   void *k_cache;
   void *v_cache;
 
@@ -30,6 +33,7 @@ struct pa_pool {
 namespace pa {
 
 inline int dtype_bytes(pa_dtype t) { return t == PA_F32 ? 4 : 2; }
+constexpr int kMaxFp8Heads = 64;  // per-head scales travel in kernel arguments
 inline bool valid_dtype(int t) { return t == PA_F32 || t == PA_F16 || t == PA_BF16; }
 inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 

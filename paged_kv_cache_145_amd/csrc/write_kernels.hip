@@ -36,6 +36,66 @@ __global__ __launch_bounds__(256) void reshape_and_cache_kernel(
   }
 }
 
+// Nearest E4M3 code of a float, ties to the even code, magnitudes of 448
+// and above saturating to 448, NaN to the NaN code (OCP 8-bit float: bias
+// 7, 3 mantissa bits, exponent field 0 = subnormals of step 2^-9).
+__device__ __forceinline__ uint32_t e4m3_code(float x) {
+  const uint32_t bits = __float_as_uint(x);
+  const uint32_t sign = (bits >> 24) & 0x80u;
+  const float a = fabsf(x);
+  if (a != a) return 0x7Fu;
+  if (a >= 448.0f) return sign | 0x7Eu;
+  if (a < 0.015625f) {  // below 2^-6: a * 2^9 is exact; round it to an integer
+    return sign | (uint32_t)__builtin_rintf(a * 512.0f);  // 8 -> code 8 = 2^-6
+  }
+  // normal: drop 20 of the 23 fraction bits with round-to-nearest-even
+  const uint32_t ab = __float_as_uint(a);
+  const uint32_t r = (ab + 0x7FFFFu + ((ab >> 20) & 1u)) & 0xFFF00000u;
+  const uint32_t code = ((((r >> 23) - 127u + 7u) & 0xFu) << 3) | ((r >> 20) & 7u);
+  return sign | (code > 0x7Eu ? 0x7Eu : code);
+}
+
+// 8-bit pools: one work-group per token; each thread turns 16 activations
+// (one 16-element run inside one head) into 16 codes: x * inv_scale[head]
+// in float, then E4M3.
+template <class T>
+__global__ __launch_bounds__(256) void reshape_and_cache_fp8_kernel(
+    uint4 *__restrict__ k_cache, uint4 *__restrict__ v_cache, const uint4 *__restrict__ key,
+    const uint4 *__restrict__ value, const int32_t *__restrict__ slot_mapping, int32_t chunks,
+    int32_t head_dim, int64_t num_slots, KvScales inv) {
+  const int64_t i = blockIdx.x;
+  const int32_t slot = slot_mapping[i];
+  const bool keep = slot >= 0 && slot < num_slots;
+  const int64_t dst = (int64_t)(keep ? slot : 0) * chunks;  // 16 codes per chunk
+  for (int c = threadIdx.x; c < chunks; c += blockDim.x) {
+    const int h = (c * 16) / head_dim;
+    const uint4 k0 = key[(i * chunks + c) * 2], k1 = key[(i * chunks + c) * 2 + 1];
+    const uint4 v0 = value[(i * chunks + c) * 2], v1 = value[(i * chunks + c) * 2 + 1];
+    auto quant = [&](const uint4 &lo, const uint4 &hi, float s) {
+      const uint32_t w[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+      uint32_t o[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        uint32_t packed = 0;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const uint32_t word = w[(4 * q + e) / 2];
+          const uint16_t b = (uint16_t)(((4 * q + e) & 1) ? (word >> 16) : (word & 0xFFFFu));
+          packed |= e4m3_code(T::to_float(b) * s) << (8 * e);
+        }
+        o[q] = packed;
+      }
+      return make_uint4(o[0], o[1], o[2], o[3]);
+    };
+    const uint4 kq = quant(k0, k1, inv.k[h]);
+    const uint4 vq = quant(v0, v1, inv.v[h]);
+    if (keep) {
+      k_cache[dst + c] = kq;
+      v_cache[dst + c] = vq;
+    }
+  }
+}
+
 // table[j][i] = (cos, sin)(j * base^(-2i/D)), double precision, rounded to float.
 __global__ __launch_bounds__(256) void rope_table_kernel(float2 *table, int32_t capacity,
                                                          int32_t half_dim, double base) {
@@ -62,6 +122,26 @@ hipError_t launch_reshape_and_cache(pa_dtype dtype, void *k_cache, void *v_cache
                      static_cast<uint4 *>(k_cache), static_cast<uint4 *>(v_cache),
                      static_cast<const uint4 *>(key), static_cast<const uint4 *>(value),
                      slot_mapping, chunks, num_slots);
+  return hipGetLastError();
+}
+
+hipError_t launch_reshape_and_cache_fp8(pa_dtype act_dtype, void *k_cache, void *v_cache,
+                                        const void *key, const void *value,
+                                        const int32_t *slot_mapping, int32_t num_tokens,
+                                        int32_t num_kv_heads, int32_t head_dim, int64_t num_slots,
+                                        const KvScales &inv, hipStream_t stream) {
+  const int32_t chunks = num_kv_heads * head_dim / 16;
+  const int threads = chunks >= 256 ? 256 : ((chunks + 63) / 64) * 64;
+  auto *kc = static_cast<uint4 *>(k_cache);
+  auto *vc = static_cast<uint4 *>(v_cache);
+  auto *kk = static_cast<const uint4 *>(key);
+  auto *vv = static_cast<const uint4 *>(value);
+  if (act_dtype == PA_BF16)
+    hipLaunchKernelGGL(reshape_and_cache_fp8_kernel<BF16>, dim3(num_tokens), dim3(threads), 0, stream,
+                       kc, vc, kk, vv, slot_mapping, chunks, head_dim, num_slots, inv);
+  else
+    hipLaunchKernelGGL(reshape_and_cache_fp8_kernel<F16>, dim3(num_tokens), dim3(threads), 0, stream,
+                       kc, vc, kk, vv, slot_mapping, chunks, head_dim, num_slots, inv);
   return hipGetLastError();
 }
 

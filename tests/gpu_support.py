@@ -63,16 +63,22 @@ class DeviceCase:
         self.device = device
         dt = case.dtype
         shape = (case.num_blocks, case.block_size, case.num_kv_heads, case.head_dim)
-        self.k_cache = torch.empty(shape, dtype=TORCH_DTYPES[dt], device=device)
-        self.v_cache = torch.empty_like(self.k_cache)
-        nan = workloads.NAN_BITS[dt]
-        if dt == "f32":
-            nan = int(np.array(nan, dtype=np.uint32).view(np.int32))
+        if case.kv_dtype == "fp8_e4m3":
+            self.k_cache = torch.full(shape, workloads.FP8_NAN_CODE, dtype=torch.uint8, device=device)
+            self.v_cache = torch.full(shape, workloads.FP8_NAN_CODE, dtype=torch.uint8, device=device)
+            self.pool = pk.Pool(self.k_cache, self.v_cache, case.block_size, act_dtype=TORCH_DTYPES[dt],
+                                k_scale=case.k_scale, v_scale=case.v_scale)
         else:
-            nan = int(np.array(nan, dtype=np.uint16).view(np.int16))
-        self.k_cache.view(INT_VIEW[dt]).fill_(nan)
-        self.v_cache.view(INT_VIEW[dt]).fill_(nan)
-        self.pool = pk.Pool(self.k_cache, self.v_cache, case.block_size)
+            self.k_cache = torch.empty(shape, dtype=TORCH_DTYPES[dt], device=device)
+            self.v_cache = torch.empty_like(self.k_cache)
+            nan = workloads.NAN_BITS[dt]
+            if dt == "f32":
+                nan = int(np.array(nan, dtype=np.uint32).view(np.int32))
+            else:
+                nan = int(np.array(nan, dtype=np.uint16).view(np.int16))
+            self.k_cache.view(INT_VIEW[dt]).fill_(nan)
+            self.v_cache.view(INT_VIEW[dt]).fill_(nan)
+            self.pool = pk.Pool(self.k_cache, self.v_cache, case.block_size)
         self.ring = None
         if case.ring is not None:
             cap = case.ring.sink + case.ring.window
@@ -129,7 +135,8 @@ class DeviceCase:
 def oracle_reference(case):
     kp, vp, slots = oracle.build_pools(case)
     ref = oracle.decode(case.query, kp, vp, case.block_tables, case.context_lens, case.scale,
-                        case.dtype, case.block_size, ring=case.ring)
+                        case.dtype, case.block_size, ring=case.ring, kv_dtype=case.kv_dtype,
+                        k_scale=case.k_scale, v_scale=case.v_scale)
     return kp, vp, slots, ref
 
 

@@ -1,0 +1,95 @@
+"""8-bit (E4M3) KV pools on the GPU against the oracle.
+
+The cache write quantises each activation row with the pool's per-head
+inverse scales and must store exactly the oracle's codes; decode
+dequantises in the kernel and must match the oracle's attention over
+scale[h] * value(code) to the 16-bit tolerance.  The format and scaling
+follow the reading of "大模型推理内存优化：从 KV Cache 分页到连续批处理的工程实践",
+section "工程边界与架构取舍" (FP8 storage of the KV cache) described in the
+oracle's fp8 module.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import paged_kv_cache_145_amd as pk
+import workloads
+from gpu_support import DeviceCase, assert_parity, oracle_reference
+
+pytestmark = pytest.mark.gpu
+
+FP8_CASES = ["tiny_fp8", "embedded_1p1b_fp8", "llama70b_b64_fp8"]
+
+
+@pytest.mark.parametrize("name", FP8_CASES)
+def test_fp8_cache_write_bit_exact(name):
+    case = workloads.FP8_CONFIGS[name]()
+    dc = DeviceCase(case)
+    dc.write_all()
+    torch.cuda.synchronize()
+    kp, vp, _ = oracle.build_pools(case)
+    assert np.array_equal(dc.k_cache.cpu().numpy(), kp)
+    assert np.array_equal(dc.v_cache.cpu().numpy(), vp)
+    dc.close()
+
+
+@pytest.mark.parametrize("name", FP8_CASES)
+def test_fp8_decode_parity(name):
+    case = workloads.FP8_CONFIGS[name]()
+    dc = DeviceCase(case)
+    dc.write_all()
+    out = dc.decode()
+    _, _, _, ref = oracle_reference(case)
+    assert_parity(out, ref, case.dtype)
+    dc.close()
+
+
+def test_fp8_ragged_and_empty_sequences():
+    """Empty sequences, one token, every tail length, 64-token blocks, D 64."""
+    base = workloads.make_paged_case("ragged", 145_077, "f16", [0, 1, 15, 16, 17, 33, 250, 0, 1000],
+                                     8, 2, 64, 64)
+    case = workloads.config_fp8(lambda: base)
+    dc = DeviceCase(case)
+    dc.write_all()
+    out = dc.decode()
+    _, _, _, ref = oracle_reference(case)
+    assert_parity(out, ref, case.dtype)
+    got = out.float().cpu().numpy()
+    assert np.all(got[0] == 0) and np.all(got[7] == 0)
+    dc.close()
+
+
+def test_fp8_relabelling_bit_identical():
+    case = workloads.FP8_CONFIGS["tiny_fp8"]()
+    a = DeviceCase(case)
+    a.write_all()
+    out_a = a.decode().cpu()
+    perm = np.random.default_rng(3).permutation(case.num_blocks).astype(np.int32)
+    case_b = workloads.FP8_CONFIGS["tiny_fp8"]()
+    case_b.block_tables = np.where(case_b.block_tables >= 0, perm[np.maximum(case_b.block_tables, 0)], -1)
+    b = DeviceCase(case_b)
+    b.write_all()
+    out_b = b.decode().cpu()
+    assert torch.equal(out_a.view(torch.int16), out_b.view(torch.int16))
+    a.close()
+    b.close()
+
+
+def test_fp8_unsupported_combinations_are_rejected():
+    case = workloads.FP8_CONFIGS["tiny_fp8"]()
+    dc = DeviceCase(case)
+    out = torch.empty((case.num_seqs, case.num_q_heads, case.head_dim), dtype=torch.bfloat16, device="cuda")
+    # a group of 1 (MHA) has no 8-bit kernel
+    q1 = torch.zeros((case.num_seqs, case.num_kv_heads, case.head_dim), dtype=torch.bfloat16, device="cuda")
+    o1 = torch.empty_like(q1)
+    with pytest.raises(pk.PaError) as e:
+        pk.decode(dc.pool, o1, q1, dc.block_tables, dc.context_lens, int(case.context_lens.max()), 0.1)
+    assert e.value.status == -5
+    # the ring cache is not combined with 8-bit pools
+    table = torch.empty(pk.rope_table_bytes(64, case.head_dim) // 4, dtype=torch.float32, device="cuda")
+    ring = pk.Ring(4, 60, 10000.0, table)
+    with pytest.raises(pk.PaError) as e:
+        pk.decode(dc.pool, out, dc.query, dc.block_tables, dc.context_lens, 64, 0.1, ring=ring)
+    assert e.value.status == -5
+    dc.close()

@@ -509,6 +509,19 @@ def test_e4m3_every_finite_code_round_trips_and_order_is_kept():
     assert np.all(np.diff(dec) >= 0)
 
 
+def test_e4m3_array_encoder_equals_the_scalar_search():
+    from oracle import fp8
+
+    rng = np.random.default_rng(9)
+    xs = np.concatenate([rng.uniform(-500, 500, 3000), rng.normal(0, 0.02, 3000),
+                         fp8.E4M3_TABLE[np.isfinite(fp8.E4M3_TABLE)],
+                         (fp8._MAGNITUDES[:-1] + fp8._MAGNITUDES[1:]) / 2,  # every midpoint (ties)
+                         [0.0, -0.0, 448.0, 449.0, -1e9, np.nan]]).astype(np.float32)
+    got = fp8.e4m3_encode(xs)
+    want = np.array([fp8.e4m3_encode_one(v) for v in xs], dtype=np.uint8)
+    assert np.array_equal(got, want)
+
+
 def test_e4m3_rounding_is_to_a_neighbour_within_half_a_step():
     """Independent of the encoder's search: the result must be one of the two
     representable neighbours, within half their spacing."""
