@@ -306,8 +306,10 @@ struct VChunk<64> {
 constexpr int kMaxPersistentWaves = kMaxPersistentWavesHost;
 // Depth of the per-wave tile pipeline (tiles in flight + the one consumed).
 constexpr int kStages = 4;
-// Segment-opening tiles per staged chunk (query fragments kept in LDS).
-constexpr int kQSlots = 4;
+// Segment-opening tiles per staged chunk (query fragments kept in LDS);
+// 8-bit pools keep two so that two work-groups fit a CU's LDS.
+template <bool KV8>
+constexpr int kQSlotsFor = KV8 ? 2 : 4;
 
 // Per-wave LDS tile for V: row-major, rows padded so that the transposing
 // reads of one instruction spread over all banks.
@@ -379,8 +381,11 @@ __device__ __forceinline__ void locate_tile(const int *s_tfirst, int num_seqs, i
   t = y - s_tfirst[b];
 }
 
+// 16-bit pools: one wave per SIMD (a memory-bound wave paired with an older
+// neighbour falls behind it).  8-bit pools halve the bytes per tile and the
+// per-tile arithmetic then dominates, so two waves per SIMD overlap it.
 template <class T, int D, bool RING, bool KV8>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, KV8 ? 2 : 1)))
 void decode_mfma_kernel(DecodeArgs a) {
   constexpr int KB = D / 32;  // score MFMAs per tile
   constexpr int EV = D / 16;  // V elements per lane per row
@@ -392,6 +397,7 @@ void decode_mfma_kernel(DecodeArgs a) {
   // then carries 16 dimensions, the A operands of two score MFMAs; the
   // query fragments follow the same dimension order.
   static_assert(!(KV8 && RING), "8-bit pools have no ring mode");
+  constexpr int kQSlots = kQSlotsFor<KV8>;
   constexpr int KVB = KV8 ? 1 : (int)sizeof(st);  // bytes per K/V element
   constexpr int KLD = KV8 ? D / 64 : KB;          // 16-byte K loads per lane per tile
   typedef typename std::conditional<KV8, typename V8Chunk<D>::type, vchunk>::type vload;
@@ -1047,7 +1053,8 @@ hipError_t launch_typed(const DecodeArgs &a, DecodeChoice choice, hipStream_t st
       // never starved by an older neighbour, so equal tile counts finish
       // at nearly equal times
       static const int grid_max = std::min(
-          persistent_grid(reinterpret_cast<const void *>(&decode_mfma_kernel<T, D, RING, KV8>), 1),
+          persistent_grid(reinterpret_cast<const void *>(&decode_mfma_kernel<T, D, RING, KV8>),
+                          KV8 ? 2 : 1),
           kMaxPersistentWaves / kNW);
       // at least one group of Hkv waves
       const int grid = std::max(grid_max, (a.num_kv_heads + kNW - 1) / kNW);
