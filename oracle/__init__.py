@@ -32,8 +32,17 @@ Parity status of each function (what pins it is listed in the tests):
   format definition, every code round-trips, rounding is monotone and
   nearest, ties go to the even code); the format and scaling rule are
   readings, the page names FP8 storage without fixing either.
+* ``prefix`` (chained FNV-1a block keys, the prefix index with token
+  verification, copy-on-write, least-recent leaf eviction, block copy):
+  pinned (published FNV-1a test vectors, chaining identity, the prime's
+  2^40 + 0x1b3 split, a birthday-built key collision refused by
+  verification, scenarios worked by hand, reference counts equal to holders
+  under random operations, copy round trips).  Chaining, verification
+  against the parent entry, the index's own reference and tail entries are
+  readings: the page's listing leaves them open or gets them wrong.
 """
 from . import fp8  # noqa: F401
+from . import prefix  # noqa: F401
 from .paged_attention import (  # noqa: F401
     quantize_for_cache,
     to_f64,
