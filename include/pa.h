@@ -132,7 +132,8 @@ int pa_incref_block(pa_pool *pool, int32_t block_id);
 
 /* Drop a reference; at zero the block returns to the free set [P2].
  * PA_ERR_INVAL for an id outside the pool, PA_ERR_STATE for a free block
- * (double release). */
+ * (double release) or when the one reference left is the prefix index's
+ * (only eviction or pa_prefix_clear drops that one). */
 int pa_decref_block(pa_pool *pool, int32_t block_id);
 
 /* Current reference count of a block (0 = free), or -1 for a bad id. */
@@ -140,6 +141,106 @@ int32_t pa_get_refcount(const pa_pool *pool, int32_t block_id);
 
 /* Pool statistics [P2]. */
 int pa_get_stats(const pa_pool *pool, pa_pool_stats *out);
+
+/* ------------------------------------------- prefix reuse, copy-on-write --- */
+
+/* Prefix-aware reuse of cached blocks [P2, sections "三、KV Cache内存管理的
+ * 工程实现" and "四、内存管理策略的边界"; P1, section "共享前缀块"].
+ * Token ids are uint32.  A full block (block_size ids) is keyed by a 64-bit
+ * FNV-1a fold of its ids, one id per step (h ^= id; h *= 0x100000001b3 mod
+ * 2^64), continued from the previous block's key (the first block starts
+ * from 0xcbf29ce484222325): the key of block i covers every id up to its
+ * end.  The index lists blocks whose contents are the K/V of known ids and
+ * holds one reference on each; a key hit counts only when the ids match and
+ * the entry hangs off the entry matched for the previous block, so hash
+ * collisions never join different prefixes.  A partial last block (a
+ * "tail", fewer ids than a block) may be listed too and is found under its
+ * parent.  Listed blocks are read-only: a caller writes into a block only
+ * after pa_cow_block.  Host-only state under the pool's mutex; nothing here
+ * touches device memory. */
+typedef enum {
+  PA_PREFIX_TAIL = 1,     /* also list the partial last block */
+  PA_PREFIX_RESIDENT = 2  /* the listed blocks are never evicted */
+} pa_prefix_flags;
+
+typedef struct {
+  int32_t entries;      /* listed blocks */
+  int32_t tail_entries; /* of which partial */
+  int32_t resident;     /* of which resident */
+  int32_t index_only;   /* listed blocks no caller holds (refcount 1) */
+} pa_prefix_stats;
+
+/* Host: keys of the num_tokens / block_size full blocks of `tokens` (host
+ * uint32 [num_tokens]) into out (host uint64, one per full block); a
+ * trailing partial block gets no key.  block_size >= 1 (any value: this
+ * call needs no pool).  PA_ERR_INVAL for num_tokens < 0, block_size < 1 or
+ * NULL pointers where a key is due. */
+int pa_block_hashes(const uint32_t *tokens, int64_t num_tokens, int32_t block_size,
+                    uint64_t *out);
+
+/* Host: the longest cached prefix of `tokens` (host uint32 [num_tokens]).
+ * Walks full blocks by key while they verify, then takes the longest tail
+ * listed under the last matched entry whose ids all lie within the request.
+ * Each returned block gains one reference for the caller (release with
+ * pa_decref_block); blocks_out (host int32 [max_blocks]) gets them in
+ * logical order, *num_blocks_out their count and *num_tokens_matched the
+ * ids they cover (a multiple of block_size unless the last one is a tail).
+ * At most max_blocks are returned.  Every entry walked counts as used now
+ * for eviction order. */
+int pa_prefix_match(pa_pool *pool, const uint32_t *tokens, int64_t num_tokens,
+                    int32_t *blocks_out, int32_t max_blocks, int32_t *num_blocks_out,
+                    int64_t *num_tokens_matched);
+
+/* Host: list a sequence's blocks: blocks[i] (host int32, allocated, caller
+ * holds a reference) holds the K/V of ids [i * block_size, (i+1) *
+ * block_size) of `tokens`.  Every full block is listed; with PA_PREFIX_TAIL
+ * the partial last block too.  A block whose (previous entry, ids) is listed
+ * already is skipped (the caller keeps its own copy); each new entry takes
+ * one reference on its block.  PA_PREFIX_RESIDENT marks every entry walked
+ * (new or known) as never evicted.  *num_new (may be NULL) = entries made.
+ * PA_ERR_INVAL: num_blocks short of the blocks needed, unknown flags, or a
+ * new entry's id outside the pool; PA_ERR_STATE: a new entry's block is
+ * free, listed already under other ids, or given twice.  On error nothing
+ * changes. */
+int pa_prefix_insert(pa_pool *pool, const uint32_t *tokens, int64_t num_tokens,
+                     const int32_t *blocks, int32_t num_blocks, uint32_t flags, int32_t *num_new);
+
+/* Host: free up to max_blocks blocks that only the index still holds
+ * (refcount 1), taking leaf entries (none listed after them), never
+ * resident ones, least recently used first (ties: the older entry); a
+ * parent whose last child goes becomes a candidate in turn.  freed (host
+ * int32 [max_blocks], may be NULL) gets the freed ids in order and
+ * *num_freed their count. */
+int pa_prefix_evict(pa_pool *pool, int32_t max_blocks, int32_t *freed, int32_t *num_freed);
+
+/* Host: drop every entry, resident ones too, and the index's references. */
+int pa_prefix_clear(pa_pool *pool);
+
+/* Host: counts of the prefix index. */
+int pa_prefix_get_stats(const pa_pool *pool, pa_prefix_stats *out);
+
+/* Host: copy-on-write [P2, section "三、KV Cache内存管理的工程实现": a
+ * shared block is read-only and is copied before it is modified].  The
+ * caller holds a reference on block_id and wants to write into it.  With
+ * refcount 1 *out_block = block_id and nothing changes.  Otherwise the
+ * lowest free block is allocated for the caller (refcount 1), block_id
+ * loses the caller's reference, and *out_block = the new id: the caller
+ * then enqueues pa_copy_blocks(block_id -> *out_block) before writing and
+ * puts the new id in its block table.  PA_ERR_NOMEM (*out_block = -1,
+ * nothing changed) when no block is free; PA_ERR_STATE for a free block or
+ * one only the index holds; PA_ERR_INVAL for an id outside the pool. */
+int pa_cow_block(pa_pool *pool, int32_t block_id, int32_t *out_block);
+
+/* Device: for each pair i, block dst_blocks[i] of both the K and the V pool
+ * takes the contents of block src_blocks[i] (every byte: block_size rows
+ * of num_kv_heads * head_dim elements, or codes for an 8-bit pool).
+ * src_blocks, dst_blocks: device int32 [num_pairs]; a pair with either id
+ * outside [0, num_blocks) is skipped (negative ids are padding).
+ * Destinations must be distinct and no destination may be a source (caller
+ * contract; otherwise the result is unspecified).  num_pairs == 0 is a
+ * no-op. */
+int pa_copy_blocks(pa_pool *pool, const int32_t *src_blocks, const int32_t *dst_blocks,
+                   int32_t num_pairs, void *stream);
 
 /* ------------------------------------------------------------- mapping --- */
 

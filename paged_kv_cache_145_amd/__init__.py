@@ -18,6 +18,7 @@ from ._lib import PaRing
 __all__ = [
     "PaError", "Pool", "Ring", "ring_slot", "compute_slot_mapping", "reshape_and_cache",
     "decode_workspace_bytes", "rope_table_bytes", "rope_table_init", "decode", "DTYPES",
+    "block_hashes", "copy_blocks",
 ]
 
 DTYPES = {"f32": _lib.PA_F32, "f16": _lib.PA_F16, "bf16": _lib.PA_BF16}
@@ -150,6 +151,86 @@ class Pool:
         s = _lib.PaPoolStats()
         _check(self._lib.pa_get_stats(self._h, ctypes.byref(s)), "pa_get_stats")
         return {"total": s.total, "used": s.used, "shared": s.shared, "free": s.free}
+
+    # -- prefix reuse and copy-on-write (host state only) --------------------
+    def prefix_match(self, tokens, max_blocks: Optional[int] = None):
+        """Longest cached prefix of ``tokens``: (block ids, tokens covered);
+        each block gains a reference for the caller."""
+        t = _tokens(tokens)
+        cap = (t.shape[0] // self.block_size + 1) if max_blocks is None else int(max_blocks)
+        out = np.empty(max(cap, 1), dtype=np.int32)
+        nb, nt = ctypes.c_int32(), ctypes.c_int64()
+        _check(self._lib.pa_prefix_match(self._h, t.ctypes.data_as(ctypes.c_void_p), t.shape[0],
+                                         out.ctypes.data_as(ctypes.c_void_p), cap, ctypes.byref(nb),
+                                         ctypes.byref(nt)), "pa_prefix_match")
+        return [int(x) for x in out[: nb.value]], int(nt.value)
+
+    def prefix_insert(self, tokens, blocks, tail: bool = False, resident: bool = False) -> int:
+        """List ``blocks`` (block i holds tokens [i*bs, (i+1)*bs)); returns new entries."""
+        t = _tokens(tokens)
+        b = np.ascontiguousarray(blocks, dtype=np.int32)
+        flags = (_lib.PA_PREFIX_TAIL if tail else 0) | (_lib.PA_PREFIX_RESIDENT if resident else 0)
+        made = ctypes.c_int32()
+        _check(self._lib.pa_prefix_insert(self._h, t.ctypes.data_as(ctypes.c_void_p), t.shape[0],
+                                          b.ctypes.data_as(ctypes.c_void_p), b.shape[0], flags,
+                                          ctypes.byref(made)), "pa_prefix_insert")
+        return int(made.value)
+
+    def prefix_evict(self, max_blocks: int):
+        """Free up to ``max_blocks`` index-only blocks; returns their ids in order."""
+        out = np.empty(max(int(max_blocks), 1), dtype=np.int32)
+        n = ctypes.c_int32()
+        _check(self._lib.pa_prefix_evict(self._h, int(max_blocks), out.ctypes.data_as(ctypes.c_void_p),
+                                         ctypes.byref(n)), "pa_prefix_evict")
+        return [int(x) for x in out[: n.value]]
+
+    def prefix_clear(self) -> None:
+        _check(self._lib.pa_prefix_clear(self._h), "pa_prefix_clear")
+
+    def prefix_stats(self) -> dict:
+        s = _lib.PaPrefixStats()
+        _check(self._lib.pa_prefix_get_stats(self._h, ctypes.byref(s)), "pa_prefix_get_stats")
+        return {"entries": s.entries, "tail_entries": s.tail_entries, "resident": s.resident,
+                "index_only": s.index_only}
+
+    def cow_block(self, block_id: int):
+        """(block to write, whether its old contents must be copied over)."""
+        out = ctypes.c_int32()
+        _check(self._lib.pa_cow_block(self._h, int(block_id), ctypes.byref(out)), "pa_cow_block")
+        return int(out.value), int(out.value) != int(block_id)
+
+
+def _tokens(tokens) -> np.ndarray:
+    t = np.asarray(tokens)
+    if t.size and (t.min() < 0 or t.max() > 0xFFFFFFFF):
+        raise ValueError("token ids must fit in uint32")
+    return np.ascontiguousarray(t, dtype=np.uint32).reshape(-1)
+
+
+def block_hashes(tokens, block_size: int) -> list:
+    """Chained 64-bit keys of the full blocks of ``tokens``."""
+    t = _tokens(tokens)
+    out = np.zeros(max(t.shape[0] // max(int(block_size), 1), 1), dtype=np.uint64)
+    _check(_lib.load().pa_block_hashes(t.ctypes.data_as(ctypes.c_void_p), t.shape[0], int(block_size),
+                                       out.ctypes.data_as(ctypes.c_void_p)), "pa_block_hashes")
+    return [int(x) for x in out[: t.shape[0] // int(block_size)]]
+
+
+def copy_blocks(pool: Pool, src_blocks, dst_blocks, stream=None) -> None:
+    """Device: block dst[i] of both pools takes block src[i]'s contents
+    (device int32 tensors of equal length; negative ids are padding)."""
+    n = int(src_blocks.shape[0])
+    if tuple(dst_blocks.shape) != (n,):
+        raise ValueError("src_blocks and dst_blocks must have the same length")
+    if n == 0:
+        return
+    import torch
+
+    if src_blocks.dtype != torch.int32 or dst_blocks.dtype != torch.int32:
+        raise ValueError("block ids must be int32")
+    _check(_lib.load().pa_copy_blocks(pool.handle, _dev_ptr(src_blocks, "src_blocks"),
+                                      _dev_ptr(dst_blocks, "dst_blocks"), n, _stream_ptr(stream)),
+           "pa_copy_blocks")
 
 
 def ring_slot(pos: int, sink: int, window: int) -> int:

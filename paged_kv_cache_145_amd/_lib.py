@@ -26,6 +26,15 @@ class PaPoolStats(ctypes.Structure):
                 ("shared", ctypes.c_int32), ("free", ctypes.c_int32)]
 
 
+class PaPrefixStats(ctypes.Structure):
+    _fields_ = [("entries", ctypes.c_int32), ("tail_entries", ctypes.c_int32),
+                ("resident", ctypes.c_int32), ("index_only", ctypes.c_int32)]
+
+
+PA_PREFIX_TAIL = 1
+PA_PREFIX_RESIDENT = 2
+
+
 class PaRing(ctypes.Structure):
     _fields_ = [("sink", ctypes.c_int32), ("window", ctypes.c_int32),
                 ("rope_base", ctypes.c_float), ("rope_style", ctypes.c_int32),
@@ -49,6 +58,14 @@ SIGNATURES = {
     "pa_decref_block": (ctypes.c_int, [_p, _i32]),
     "pa_get_refcount": (_i32, [_p, _i32]),
     "pa_get_stats": (ctypes.c_int, [_p, ctypes.POINTER(PaPoolStats)]),
+    "pa_block_hashes": (ctypes.c_int, [_p, _i64, _i32, _p]),
+    "pa_prefix_match": (ctypes.c_int, [_p, _p, _i64, _p, _i32, ctypes.POINTER(_i32), ctypes.POINTER(_i64)]),
+    "pa_prefix_insert": (ctypes.c_int, [_p, _p, _i64, _p, _i32, ctypes.c_uint32, ctypes.POINTER(_i32)]),
+    "pa_prefix_evict": (ctypes.c_int, [_p, _i32, _p, ctypes.POINTER(_i32)]),
+    "pa_prefix_clear": (ctypes.c_int, [_p]),
+    "pa_prefix_get_stats": (ctypes.c_int, [_p, ctypes.POINTER(PaPrefixStats)]),
+    "pa_cow_block": (ctypes.c_int, [_p, _i32, ctypes.POINTER(_i32)]),
+    "pa_copy_blocks": (ctypes.c_int, [_p, _p, _p, _i32, _p]),
     "pa_ring_slot": (_i32, [_i64, _i32, _i32]),
     "pa_compute_slot_mapping": (ctypes.c_int, [_p, _p, _i32, _i32, _p, _p, _i32,
                                                ctypes.POINTER(PaRing), _p]),

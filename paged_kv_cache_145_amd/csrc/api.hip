@@ -126,6 +126,23 @@ int pa_reshape_and_cache(pa_pool *pool, const void *key, const void *value,
       static_cast<hipStream_t>(stream)));
 }
 
+int pa_copy_blocks(pa_pool *pool, const int32_t *src_blocks, const int32_t *dst_blocks,
+                   int32_t num_pairs, void *stream) {
+  if (pool == nullptr || num_pairs < 0) return PA_ERR_INVAL;
+  if (num_pairs == 0) return PA_OK;
+  if (src_blocks == nullptr || dst_blocks == nullptr) return PA_ERR_INVAL;
+  if ((reinterpret_cast<uintptr_t>(src_blocks) | reinterpret_cast<uintptr_t>(dst_blocks)) & 3u)
+    return PA_ERR_INVAL;
+  const int64_t elem = pool->kv_fp8 ? 1 : pa::dtype_bytes(pool->dtype);
+  const int64_t block_bytes =
+      (int64_t)pool->block_size * pool->num_kv_heads * pool->head_dim * elem;
+  const int64_t segs = pa::ceil_div(block_bytes / 16, pa::kCopySegChunks);
+  if ((int64_t)num_pairs * segs > INT32_MAX) return PA_ERR_UNSUPPORTED;
+  return pa::hip_status(pa::launch_copy_blocks(pool->k_cache, pool->v_cache, src_blocks,
+                                               dst_blocks, num_pairs, pool->num_blocks, block_bytes,
+                                               static_cast<hipStream_t>(stream)));
+}
+
 size_t pa_decode_workspace_bytes(const pa_pool *pool, int32_t num_seqs, int32_t num_q_heads,
                                  int32_t max_context_len, const pa_ring *ring) {
   if (pool == nullptr || num_seqs < 0 || num_q_heads <= 0 || max_context_len < 0) return 0;

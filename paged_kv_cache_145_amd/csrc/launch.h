@@ -85,6 +85,13 @@ hipError_t launch_reshape_and_cache_fp8(pa_dtype act_dtype, void *k_cache, void 
                                         int32_t num_kv_heads, int32_t head_dim, int64_t num_slots,
                                         const KvScales &inv, hipStream_t stream);
 
+// Copy whole blocks (block_bytes each, a multiple of 16) of both pools; one
+// work-group per kCopySegChunks 16-byte chunks of a block.
+constexpr int kCopySegChunks = 1024;
+hipError_t launch_copy_blocks(void *k_cache, void *v_cache, const int32_t *src_blocks,
+                              const int32_t *dst_blocks, int32_t num_pairs, int32_t num_blocks,
+                              int64_t block_bytes, hipStream_t stream);
+
 hipError_t launch_rope_table_init(float *table, int32_t capacity, int32_t head_dim,
                                   float rope_base, hipStream_t stream);
 

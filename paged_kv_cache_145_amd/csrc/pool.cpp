@@ -17,6 +17,37 @@
 
 namespace pa {
 
+int32_t alloc_block_locked(pa_pool *pool) {
+  for (size_t w = 0; w < pool->free_bits.size(); ++w) {
+    const uint64_t bits = pool->free_bits[w];
+    if (bits != 0) {
+      const int bit = __builtin_ctzll(bits);
+      pool->free_bits[w] = bits & ~(1ull << bit);
+      const int32_t id = (int32_t)(w * 64 + (size_t)bit);
+      pool->refcount[(size_t)id] = 1;
+      pool->used += 1;
+      return id;
+    }
+  }
+  return -1;
+}
+
+void add_ref_locked(pa_pool *pool, int32_t block_id) {
+  int32_t &rc = pool->refcount[(size_t)block_id];
+  rc += 1;
+  if (rc == 2) pool->shared += 1;
+}
+
+void drop_ref_locked(pa_pool *pool, int32_t block_id) {
+  int32_t &rc = pool->refcount[(size_t)block_id];
+  rc -= 1;
+  if (rc == 1) pool->shared -= 1;
+  if (rc == 0) {
+    pool->free_bits[(size_t)block_id / 64] |= 1ull << (block_id % 64);
+    pool->used -= 1;
+  }
+}
+
 bool ring_valid(const pa_ring *ring) {
   if (ring == nullptr) return true;
   if (ring->sink < 0 || ring->window < 1) return false;
@@ -57,6 +88,7 @@ int pa_create_pool(pa_pool **out, int32_t num_blocks, int32_t block_size, int32_
     const int tail = num_blocks % 64;
     if (tail != 0) p->free_bits[words - 1] = (1ull << tail) - 1ull;
     p->refcount.assign((size_t)num_blocks, 0);
+    p->prefix.block_entry.assign((size_t)num_blocks, -1);
   } catch (...) {
     delete p;
     return PA_ERR_NOMEM;
@@ -107,29 +139,16 @@ void pa_destroy_pool(pa_pool *pool) { delete pool; }
 int32_t pa_alloc_block(pa_pool *pool) {
   if (pool == nullptr) return -1;
   std::lock_guard<std::mutex> lock(pool->mu);
-  for (size_t w = 0; w < pool->free_bits.size(); ++w) {
-    const uint64_t bits = pool->free_bits[w];
-    if (bits != 0) {
-      const int bit = __builtin_ctzll(bits);
-      pool->free_bits[w] = bits & ~(1ull << bit);
-      const int32_t id = (int32_t)(w * 64 + (size_t)bit);
-      pool->refcount[(size_t)id] = 1;
-      pool->used += 1;
-      return id;
-    }
-  }
-  return -1;
+  return pa::alloc_block_locked(pool);
 }
 
 int pa_incref_block(pa_pool *pool, int32_t block_id) {
   if (pool == nullptr) return PA_ERR_INVAL;
   std::lock_guard<std::mutex> lock(pool->mu);
   if (block_id < 0 || block_id >= pool->num_blocks) return PA_ERR_INVAL;
-  int32_t &rc = pool->refcount[(size_t)block_id];
-  if (rc == 0) return PA_ERR_STATE;
-  if (rc == INT32_MAX) return PA_ERR_STATE;
-  rc += 1;
-  if (rc == 2) pool->shared += 1;
+  const int32_t rc = pool->refcount[(size_t)block_id];
+  if (rc == 0 || rc == INT32_MAX) return PA_ERR_STATE;
+  pa::add_ref_locked(pool, block_id);
   return PA_OK;
 }
 
@@ -137,14 +156,11 @@ int pa_decref_block(pa_pool *pool, int32_t block_id) {
   if (pool == nullptr) return PA_ERR_INVAL;
   std::lock_guard<std::mutex> lock(pool->mu);
   if (block_id < 0 || block_id >= pool->num_blocks) return PA_ERR_INVAL;
-  int32_t &rc = pool->refcount[(size_t)block_id];
+  const int32_t rc = pool->refcount[(size_t)block_id];
   if (rc == 0) return PA_ERR_STATE;
-  rc -= 1;
-  if (rc == 1) pool->shared -= 1;
-  if (rc == 0) {
-    pool->free_bits[(size_t)block_id / 64] |= 1ull << (block_id % 64);
-    pool->used -= 1;
-  }
+  // the prefix index's own reference is dropped by eviction, not here
+  if (rc == 1 && pool->prefix.block_entry[(size_t)block_id] >= 0) return PA_ERR_STATE;
+  pa::drop_ref_locked(pool, block_id);
   return PA_OK;
 }
 

@@ -5,9 +5,44 @@
 
 #include <cstdint>
 #include <mutex>
+#include <unordered_map>
 #include <vector>
 
 #include "pa.h"
+
+namespace pa {
+
+// One listed block of the prefix index.  A full entry covers block_size
+// token ids and is found by its chained key; a tail entry covers fewer and
+// is found under its parent.  Entries form a forest: `parent` is the slot of
+// the entry for the previous block (-1 for the first block).
+struct PrefixEntry {
+  bool live = false;
+  bool full = false;
+  bool resident = false;
+  int32_t block = -1;
+  int32_t parent = -1;
+  int32_t children = 0;
+  uint64_t key = 0;
+  uint64_t serial = 0;    // creation order
+  uint64_t last_use = 0;  // use clock of the last match / insert that walked it
+  std::vector<uint32_t> tokens;
+};
+
+struct PrefixIndex {
+  std::vector<PrefixEntry> entries;  // slots; dead slots are reused
+  std::vector<int32_t> free_slots;
+  std::unordered_multimap<uint64_t, int32_t> by_key;  // chained key -> full entry slot
+  std::unordered_multimap<int32_t, int32_t> tails;    // parent slot -> tail entry slot
+  std::vector<int32_t> block_entry;                   // block id -> slot, or -1
+  uint64_t clock = 0;
+  uint64_t next_serial = 0;
+  int32_t live = 0;
+  int32_t tail_entries = 0;
+  int32_t resident = 0;
+};
+
+}  // namespace pa
 
 struct pa_pool {
   int32_t num_blocks;
@@ -28,6 +63,8 @@ struct pa_pool {
   std::vector<int32_t> refcount;
   int32_t used;
   int32_t shared;
+  // Blocks listed by the prefix index, each holding one reference.
+  pa::PrefixIndex prefix;
 };
 
 namespace pa {
@@ -45,6 +82,11 @@ inline int64_t effective_context(int64_t max_context_len, const pa_ring *ring) {
 }
 
 bool ring_valid(const pa_ring *ring);
+
+// Allocator steps with pool->mu held (pool.cpp).
+int32_t alloc_block_locked(pa_pool *pool);
+void add_ref_locked(pa_pool *pool, int32_t block_id);   // refcount >= 1
+void drop_ref_locked(pa_pool *pool, int32_t block_id);  // refcount >= 1
 
 }  // namespace pa
 

@@ -96,6 +96,43 @@ __global__ __launch_bounds__(256) void reshape_and_cache_fp8_kernel(
   }
 }
 
+// Block copy that completes a copy-on-write: a shared block is copied to a
+// private one before the private one is written ("Ollama的内存管理策略…"
+// (xdnf.cn/news/5086), section "三、KV Cache内存管理的工程实现").  Grid: x =
+// (pair, segment), y = pool (0 = K, 1 = V).  A work-group moves one
+// kCopySegChunks * 16-byte segment of one block: four independent 16-byte
+// loads per thread in flight, then four stores, so each wave keeps 4 KiB of
+// reads outstanding on this purely HBM-bound move.
+constexpr int kCopyThreads = 256;
+constexpr int kCopyUnroll = 4;
+static_assert(kCopySegChunks == kCopyThreads * kCopyUnroll, "copy segment size");
+
+__global__ __launch_bounds__(kCopyThreads) void copy_blocks_kernel(
+    uint4 *k_cache, uint4 *v_cache, const int32_t *__restrict__ src_blocks,
+    const int32_t *__restrict__ dst_blocks, int32_t num_blocks, int64_t block_chunks,
+    int32_t segs) {
+  const int64_t pair = blockIdx.x / segs;
+  const int64_t seg = blockIdx.x - pair * segs;
+  const int32_t s = src_blocks[pair];
+  const int32_t d = dst_blocks[pair];
+  if (s < 0 || s >= num_blocks || d < 0 || d >= num_blocks) return;
+  uint4 *pool = blockIdx.y == 0 ? k_cache : v_cache;
+  const uint4 *from = pool + (int64_t)s * block_chunks;
+  uint4 *to = pool + (int64_t)d * block_chunks;
+  const int64_t base = seg * kCopySegChunks + threadIdx.x;
+  uint4 r[kCopyUnroll];
+#pragma unroll
+  for (int j = 0; j < kCopyUnroll; ++j) {
+    const int64_t c = base + j * kCopyThreads;
+    if (c < block_chunks) r[j] = from[c];
+  }
+#pragma unroll
+  for (int j = 0; j < kCopyUnroll; ++j) {
+    const int64_t c = base + j * kCopyThreads;
+    if (c < block_chunks) to[c] = r[j];
+  }
+}
+
 // table[j][i] = (cos, sin)(j * base^(-2i/D)), double precision, rounded to float.
 __global__ __launch_bounds__(256) void rope_table_kernel(float2 *table, int32_t capacity,
                                                          int32_t half_dim, double base) {
@@ -142,6 +179,17 @@ hipError_t launch_reshape_and_cache_fp8(pa_dtype act_dtype, void *k_cache, void 
   else
     hipLaunchKernelGGL(reshape_and_cache_fp8_kernel<F16>, dim3(num_tokens), dim3(threads), 0, stream,
                        kc, vc, kk, vv, slot_mapping, chunks, head_dim, num_slots, inv);
+  return hipGetLastError();
+}
+
+hipError_t launch_copy_blocks(void *k_cache, void *v_cache, const int32_t *src_blocks,
+                              const int32_t *dst_blocks, int32_t num_pairs, int32_t num_blocks,
+                              int64_t block_bytes, hipStream_t stream) {
+  const int64_t chunks = block_bytes / 16;
+  const int32_t segs = (int32_t)((chunks + kCopySegChunks - 1) / kCopySegChunks);
+  hipLaunchKernelGGL(copy_blocks_kernel, dim3((unsigned)((int64_t)num_pairs * segs), 2),
+                     dim3(kCopyThreads), 0, stream, static_cast<uint4 *>(k_cache),
+                     static_cast<uint4 *>(v_cache), src_blocks, dst_blocks, num_blocks, chunks, segs);
   return hipGetLastError();
 }
 

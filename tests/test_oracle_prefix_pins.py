@@ -106,6 +106,8 @@ def test_hand_worked_scenario():
     assert m.stats() == {"entries": 3, "tail_entries": 1, "resident": 3, "index_only": 3}
     with pytest.raises(AllocatorError):  # the index's reference is not the caller's
         m.release(0)
+    with pytest.raises(AllocatorError):  # nor may a caller write through it
+        m.cow(0)
 
     # B extends the prompt: both full blocks and the tail are reused
     blocks_b, covered = m.match(a + [50, 51], 16)

@@ -492,3 +492,114 @@ CONFIGS = {
     "shared_prefix": config_shared_prefix,
     "sink_ring": config_sink_ring,
 }
+
+
+# ---------------------------------------------------------------------------
+# Prefix reuse: a resident system prompt that does not end on a block
+# boundary, and requests that share all of it, part of it or none of it
+# ---------------------------------------------------------------------------
+
+@dataclass
+class PrefixRequest:
+    """A request's prompt ids and the K/V rows of every position.  The first
+    ``shared`` ids (and rows) are the system prompt's; the rest are its own."""
+
+    tokens: np.ndarray  # uint32 [n]
+    shared: int
+    keys: np.ndarray  # raw [n, Hkv, D]
+    values: np.ndarray
+
+
+@dataclass
+class PrefixScenario:
+    name: str
+    seed: int
+    dtype: str
+    num_blocks: int
+    block_size: int
+    num_kv_heads: int
+    num_q_heads: int
+    head_dim: int
+    scale: float
+    system_tokens: np.ndarray  # uint32 [P]
+    system_keys: np.ndarray  # raw [P, Hkv, D]
+    system_values: np.ndarray
+    requests: List[PrefixRequest]
+    query: np.ndarray  # raw [B, Hq, D]
+    kv_dtype: Optional[str] = None
+    k_scale: Optional[np.ndarray] = None
+    v_scale: Optional[np.ndarray] = None
+
+    @property
+    def num_seqs(self) -> int:
+        return len(self.requests)
+
+    def empty_pool(self) -> np.ndarray:
+        shape = (self.num_blocks, self.block_size, self.num_kv_heads, self.head_dim)
+        if self.kv_dtype == "fp8_e4m3":
+            return np.full(shape, FP8_NAN_CODE, dtype=np.uint8)
+        return nan_array(shape, self.dtype)
+
+
+def prefix_scenario(name: str, seed: int, dtype: str, system_len: int, shares, own_lens,
+                    num_q_heads: int, num_kv_heads: int, head_dim: int, block_size: int,
+                    duplicate_of: Optional[int] = None, kv_fp8: bool = False) -> PrefixScenario:
+    """Requests b take ``shares[b]`` leading ids of the system prompt and then
+    ``own_lens[b]`` ids of their own (the first differing from the system
+    prompt's next id); ``duplicate_of`` appends a copy of that request."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    hkv, d = num_kv_heads, head_dim
+    sys_tok = rng.integers(0, 1 << 32, size=system_len, dtype=np.uint64).astype(np.uint32)
+    sys_k = draw_values(rng, (system_len, hkv, d), dtype)
+    sys_v = draw_values(rng, (system_len, hkv, d), dtype)
+    reqs = []
+    for share, own in zip(shares, own_lens):
+        share, own = int(share), int(own)
+        own_tok = rng.integers(0, 1 << 32, size=own, dtype=np.uint64).astype(np.uint32)
+        if own and share < system_len and own_tok[0] == sys_tok[share]:
+            own_tok[0] ^= np.uint32(1)
+        k = np.concatenate([sys_k[:share], draw_values(rng, (own, hkv, d), dtype)])
+        v = np.concatenate([sys_v[:share], draw_values(rng, (own, hkv, d), dtype)])
+        reqs.append(PrefixRequest(np.concatenate([sys_tok[:share], own_tok]), share, k, v))
+    if duplicate_of is not None:
+        r = reqs[duplicate_of]
+        reqs.append(PrefixRequest(r.tokens.copy(), r.shared, r.keys.copy(), r.values.copy()))
+    query = draw_values(rng, (len(reqs), num_q_heads, d), dtype)
+    need = _ceil_div(system_len, block_size) + sum(_ceil_div(len(r.tokens), block_size) + 1 for r in reqs)
+    sc = PrefixScenario(
+        name=name, seed=seed, dtype=dtype, num_blocks=math.ceil(1.25 * need), block_size=block_size,
+        num_kv_heads=hkv, num_q_heads=num_q_heads, head_dim=d, scale=1.0 / math.sqrt(d),
+        system_tokens=sys_tok, system_keys=sys_k, system_values=sys_v, requests=reqs, query=query,
+    )
+    if kv_fp8:
+        sc.kv_dtype = "fp8_e4m3"
+        sc.k_scale, sc.v_scale = fp8_scales(hkv)
+    return sc
+
+
+def config_prefix_unaligned(kv_fp8: bool = False) -> PrefixScenario:
+    """70B attention heads (Hq 64, Hkv 8, D 128, bf16, 16-token blocks); a
+    600-token system prompt (37 full blocks and a tail of 8); 12 requests:
+    six extend the whole prompt, two leave it 3 ids before its end (inside
+    the tail), one after 200 ids (inside a full block), one shares nothing,
+    one is the prompt alone, one repeats the first request."""
+    shares = [600] * 6 + [597, 597, 200, 0, 600]
+    own = [1, 8, 9, 57, 250, 431, 3, 120, 77, 300, 0]
+    return prefix_scenario("prefix_unaligned" + ("_fp8" if kv_fp8 else ""), SEED_BASE + 20, "bf16", 600,
+                           shares, own, 64, 8, 128, 16, duplicate_of=4, kv_fp8=kv_fp8)
+
+
+def config_prefix_unaligned_small() -> PrefixScenario:
+    """fp32, Hq 4, Hkv 2, D 64, 64-token blocks, a 150-token system prompt
+    (two full blocks and a tail of 22)."""
+    shares = [150, 150, 149, 128, 10, 0, 150]
+    own = [5, 42, 1, 64, 100, 7, 0]
+    return prefix_scenario("prefix_unaligned_small", SEED_BASE + 21, "f32", 150, shares, own,
+                           4, 2, 64, 64, duplicate_of=1)
+
+
+PREFIX_CONFIGS = {
+    "prefix_unaligned": config_prefix_unaligned,
+    "prefix_unaligned_fp8": lambda: config_prefix_unaligned(kv_fp8=True),
+    "prefix_unaligned_small": config_prefix_unaligned_small,
+}
