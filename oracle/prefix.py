@@ -225,12 +225,15 @@ class PrefixCacheModel:
         """A block the caller may write: the block itself when the caller
         holds its only reference, else a fresh block that replaces it (the
         caller copies the old contents).  Returns (-1, False) and changes
-        nothing when no block is free."""
+        nothing when no block is free.  The caller must hold a reference, so
+        a block held by the index alone is refused."""
         if not 0 <= block < self.alloc.num_blocks:
             raise AllocatorError("inval", f"block id {block} outside the pool")
         rc = self.alloc.refcount[block]
         if rc == 0:
             raise AllocatorError("state", f"block {block} is free")
+        if rc == 1 and block in self.indexed_blocks():
+            raise AllocatorError("state", f"block {block} is held only by the prefix index")
         if rc == 1:
             return block, False
         fresh = self.alloc.alloc()
