@@ -156,6 +156,239 @@ def cpu_baseline(case, repeats: int = 2) -> dict:
             "seconds_per_call": round(t, 4)}
 
 
+def _nan_pools(workloads, torch, shape, dtype, dev):
+    tdt = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}[dtype]
+    ibits = torch.int32 if dtype == "f32" else torch.int16
+    raw = np.array(workloads.NAN_BITS[dtype], dtype=np.uint32 if dtype == "f32" else np.uint16)
+    bits = int(raw.view(np.int32 if dtype == "f32" else np.int16))
+    k = torch.empty(shape, dtype=tdt, device=dev)
+    v = torch.empty(shape, dtype=tdt, device=dev)
+    k.view(ibits).fill_(bits)
+    v.view(ibits).fill_(bits)
+    return k, v
+
+
+def _event_us(torch, fn, calls: int):
+    """Mean and median microseconds of ``fn`` bracketed by events on the
+    current stream (the stream the library launches on)."""
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(calls)]
+    for a, b in evs:
+        a.record()
+        fn()
+        b.record()
+    torch.cuda.synchronize()
+    ts = [a.elapsed_time(b) * 1e3 for a, b in evs]
+    return statistics.mean(ts), statistics.median(ts)
+
+
+def prefix_cpu_baseline(prompt, block_size: int, reps: int = 20) -> dict:
+    """The oracle's prefix model answering the same 2048-id match."""
+    from oracle.allocator import BlockAllocatorModel
+    from oracle.prefix import PrefixCacheModel
+
+    ids = [int(x) for x in prompt]
+    model = PrefixCacheModel(BlockAllocatorModel(256), block_size)
+    model.insert(ids, [model.alloc.alloc() for _ in range(len(ids) // block_size)])
+    t0, c0 = time.perf_counter(), time.process_time()
+    for _ in range(reps):
+        got, _ = model.match(ids, 1 << 20)
+        for blk in got:
+            model.release(blk)
+    wall = (time.perf_counter() - t0) / reps
+    cores = max(1, round((time.process_time() - c0) / (wall * reps)))
+    return {"value": round(wall * 1e6, 1), "unit": "us per 2048-id match", "cores": cores, "kind": "oracle",
+            "sample": f"the oracle's prefix model matching the same 2048-id prompt, {reps} times"}
+
+
+def measure_prefix(args) -> int:
+    """Prefix reuse with copy-on-write, measured on the 70B-head workload of
+    a 600-token resident system prompt (37 full 16-token blocks and a tail
+    of 8) and 12 requests: host admission through the library's prefix index
+    (match, copy-on-write, allocate, list), the tail copies, decode over the
+    shared blocks, and the block copy kernel at one admission wave and in
+    bulk.  Prints one JSON line; ``roofline`` is the copy kernel's."""
+    import torch
+
+    import paged_kv_cache_145_amd as pk
+    import workloads
+
+    dev = "cuda:0"
+    torch.cuda.set_device(0)
+    sc = workloads.config_prefix_unaligned()
+    bs, hkv, d = sc.block_size, sc.num_kv_heads, sc.head_dim
+    tdt = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}[sc.dtype]
+    raw_view = np.int32 if sc.dtype == "f32" else np.int16
+
+    def to_dev(raw):
+        return torch.from_numpy(np.ascontiguousarray(raw).view(raw_view)).view(tdt).to(dev)
+
+    k, v = _nan_pools(workloads, torch, (sc.num_blocks, bs, hkv, d), sc.dtype, dev)
+    pool = pk.Pool(k, v, bs)
+    print("bench: admitting the prefix workload through the prefix index", file=sys.stderr, flush=True)
+    p = len(sc.system_tokens)
+    sys_blocks = [pool.alloc_block() for _ in range(-(-p // bs))]
+    pool.prefix_insert(sc.system_tokens, sys_blocks, tail=True, resident=True)
+    for blk in sys_blocks:
+        pool.decref(blk)
+    tables, covered, copies, admit_us = [], [], [], []
+    for r in sc.requests:
+        n = len(r.tokens)
+        t0 = time.perf_counter()
+        blocks, cov = pool.prefix_match(r.tokens)
+        if cov % bs and cov < n:
+            new, copied = pool.cow_block(blocks[-1])
+            if copied:
+                copies.append((blocks[-1], new))
+            blocks[-1] = new
+        while len(blocks) * bs < n:
+            blocks.append(pool.alloc_block())
+        pool.prefix_insert(r.tokens, blocks)
+        admit_us.append((time.perf_counter() - t0) * 1e6)
+        tables.append(blocks)
+        covered.append(cov)
+    if min(min(t) for t in tables) < 0:
+        raise SystemExit("pool too small for the prefix workload")
+
+    def write_rows(rows_tables, positions, keys, values):
+        bt = np.full((len(rows_tables), max(len(t) for t in rows_tables)), -1, dtype=np.int32)
+        for i, t in enumerate(rows_tables):
+            bt[i, : len(t)] = t
+        sid = np.concatenate([np.full(len(q), i, dtype=np.int32) for i, q in enumerate(positions)])
+        pos = np.concatenate([np.asarray(q, dtype=np.int64) for q in positions])
+        slots = pk.compute_slot_mapping(pool, bt, sid, pos)
+        pk.reshape_and_cache(pool, to_dev(keys), to_dev(values), torch.from_numpy(slots).to(dev))
+
+    write_rows([sys_blocks], [np.arange(p)], sc.system_keys, sc.system_values)
+    src = torch.tensor([a for a, _ in copies], dtype=torch.int32, device=dev)
+    dst = torch.tensor([b for _, b in copies], dtype=torch.int32, device=dev)
+    pk.copy_blocks(pool, src, dst)
+    write_rows(tables, [np.arange(c, len(r.tokens)) for c, r in zip(covered, sc.requests)],
+               np.concatenate([r.keys[c:] for c, r in zip(covered, sc.requests)]),
+               np.concatenate([r.values[c:] for c, r in zip(covered, sc.requests)]))
+    bt = np.full((sc.num_seqs, max(len(t) for t in tables)), -1, dtype=np.int32)
+    for i, t in enumerate(tables):
+        bt[i, : len(t)] = t
+    lens = np.array([len(r.tokens) for r in sc.requests], dtype=np.int32)
+    query, tables_d, lens_d = to_dev(sc.query), torch.from_numpy(bt).to(dev), torch.from_numpy(lens).to(dev)
+    out = torch.empty((sc.num_seqs, sc.num_q_heads, d), dtype=tdt, device=dev)
+    mcl = int(lens.max())
+    ws = torch.empty(max(pk.decode_workspace_bytes(pool, sc.num_seqs, sc.num_q_heads, mcl), 1),
+                     dtype=torch.uint8, device=dev)
+
+    def decode():
+        pk.decode(pool, out, query, tables_d, lens_d, mcl, sc.scale, workspace=ws)
+
+    row = hkv * d * 2 * 2  # one token's K and V rows
+    unique_blocks = {}
+    for t, n in zip(tables, lens):
+        for j, blk in enumerate(t):
+            unique_blocks[blk] = max(unique_blocks.get(blk, 0), min(bs, int(n) - j * bs))
+    dec_bytes = sum(unique_blocks.values()) * row + sc.num_seqs * sc.num_q_heads * d * 2 * 2
+    for _ in range(args.warmup):
+        decode()
+    torch.cuda.synchronize()
+    dec_mean, dec_med = _event_us(torch, decode, args.steps)
+    block_bytes = bs * hkv * d * 2
+    wave = (src, dst)
+
+    def copy_wave():
+        pk.copy_blocks(pool, *wave)
+
+    for _ in range(args.warmup):
+        copy_wave()
+    wave_mean, wave_med = _event_us(torch, copy_wave, args.steps)
+    pool.close()
+
+    # bulk: 4096 pairs of 70B-shaped blocks (256 MiB read, 256 MiB written)
+    pairs = 4096
+    print(f"bench: timing the block copy in bulk ({pairs} pairs)", file=sys.stderr, flush=True)
+    bk = torch.zeros((2 * pairs, bs, hkv, d), dtype=tdt, device=dev)
+    bv = torch.zeros_like(bk)
+    bulk = pk.Pool(bk, bv, bs)
+    perm = np.random.default_rng(sc.seed).permutation(2 * pairs).astype(np.int32)
+    bsrc, bdst = torch.from_numpy(perm[:pairs]).to(dev), torch.from_numpy(perm[pairs:]).to(dev)
+
+    def copy_bulk():
+        pk.copy_blocks(bulk, bsrc, bdst)
+
+    for _ in range(args.warmup):
+        copy_bulk()
+    bulk_mean, bulk_med = _event_us(torch, copy_bulk, args.steps)
+    bulk.close()
+    del bk, bv
+    bulk_bytes = pairs * block_bytes * 2 * 2  # K and V, read and written
+    achieved = bulk_bytes / (bulk_mean * 1e-6) / 1e9
+
+    # host side of the index: keys and a full-prompt match of 2048 ids
+    rng = np.random.default_rng(sc.seed + 1)
+    prompt = rng.integers(0, 1 << 32, size=2048, dtype=np.uint64).astype(np.uint32)
+    hk, hv = torch.zeros((256, bs, hkv, d), dtype=tdt, device=dev), None
+    hv = torch.zeros_like(hk)
+    host_pool = pk.Pool(hk, hv, bs)
+    hb = [host_pool.alloc_block() for _ in range(2048 // bs)]
+    host_pool.prefix_insert(prompt, hb)
+    long_ids = rng.integers(0, 1 << 32, size=1 << 22, dtype=np.uint64).astype(np.uint32)
+    t0 = time.perf_counter()
+    pk.block_hashes(long_ids, bs)  # one call over 2^22 ids: the binding's cost is negligible
+    hash_ns = (time.perf_counter() - t0) / (long_ids.size // bs) * 1e9
+    reps = 2000
+    t0 = time.perf_counter()
+    for _ in range(reps):  # each match takes a reference per block; all are dropped below
+        host_pool.prefix_match(prompt)
+    match_us = (time.perf_counter() - t0) / reps * 1e6
+    for blk in hb:
+        for _ in range(reps):
+            host_pool.decref(blk)
+    host_pool.close()
+    cpu = prefix_cpu_baseline(prompt, bs) if not args.no_cpu_baseline else None
+
+    result = {
+        "metric": "prefix reuse: copy-on-write block copy bandwidth (bulk) with admission and shared-prefix decode",
+        "value": round(achieved, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(bulk_mean / 1e3, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": sc.dtype,
+        "data": "synthetic",
+        "config": {
+            "workload": ("prefix_unaligned: Hq 64, Hkv 8, D 128, bf16, block 16; 600-token resident system "
+                         "prompt (37 full blocks + tail of 8); 12 requests (6 extend it, 2 leave it inside "
+                         "the tail, 1 inside a full block, 1 share nothing, 1 prompt only, 1 repeat); bulk "
+                         f"copy of {pairs} block pairs"),
+            "global_batch": sc.num_seqs,
+            "seed": sc.seed,
+        },
+        "admission": {"host_us_per_request_median": round(statistics.median(admit_us), 2),
+                      "covered_tokens": covered, "tail_copies": len(copies)},
+        "copy_wave": {"pairs": len(copies), "us_mean": round(wave_mean, 2), "us_median": round(wave_med, 2),
+                      "bytes": len(copies) * block_bytes * 2 * 2},
+        "decode_shared": {"us_mean": round(dec_mean, 2), "us_median": round(dec_med, 2),
+                          "unique_bytes": dec_bytes,
+                          "gbs_unique": round(dec_bytes / (dec_mean * 1e-6) / 1e9, 1),
+                          "cached_tokens": int(lens.sum())},
+        "host_index": {"block_key_ns_per_block16": round(hash_ns, 1),
+                       "match_2048_ids_us": round(match_us, 2)},
+        "roofline": {
+            "bound": "hbm",
+            "kernel": "pa_copy_blocks: copy_blocks_kernel (HIP events bracket the call)",
+            "achieved": round(achieved, 1),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": None,
+            "algorithmic_bytes": bulk_bytes,
+        },
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(result), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[1])
     ap.add_argument("--gpus", type=int, default=1)
@@ -175,6 +408,9 @@ def main() -> int:
                     help="only run this many decode calls, then a 1 GiB copy (for rocprofv3 counter runs)")
     ap.add_argument("--write-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="turn two rocprofv3 counter_collection.csv files into the traffic record")
+    ap.add_argument("--measure", choices=("decode", "prefix"), default="decode",
+                    help="decode (default): the hot-path step; prefix: prefix reuse with copy-on-write "
+                         "(admission, tail copies, shared-prefix decode, bulk block copy)")
     ap.add_argument("--traffic-command", default="",
                     help="the profiling command line recorded with --write-traffic")
     args = ap.parse_args()
@@ -202,6 +438,8 @@ def main() -> int:
         print("bench.py needs a GPU", file=sys.stderr)
         return 2
     _lib.load()
+    if args.measure == "prefix":
+        return measure_prefix(args)
     dev = "cuda:0"
     torch.cuda.set_device(0)
     print(f"bench: generating the seeded workload {args.config}", file=sys.stderr, flush=True)
