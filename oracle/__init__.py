@@ -16,6 +16,11 @@ Parity status of each function (what pins it is listed in the tests):
 * ``gather_rows``, ``decode``: pinned (dense-attention special case against
   a library routine, pure-Python brute force, n = 1, constant keys,
   permutation and shared-prefix invariance, write-then-read round trip).
+* ``decode_multi`` (several new tokens per sequence, causal): pinned
+  (q_len = 1 equals ``decode``; each new token equals ``decode`` over its
+  own prefix; dense causal attention against torch's
+  scaled_dot_product_attention with an explicit mask; keys after a token's
+  position never change its row; tokens before position 0 give zeros).
 * ``ring_slot``, ``ring_cache_order``, ``ring_cache_index``: pinned (values
   worked by hand from the sink + ring slot equation, brute-force last-writer
   simulation).
@@ -50,6 +55,7 @@ from .paged_attention import (  # noqa: F401
     slot_of,
     attention_one_group,
     decode,
+    decode_multi,
     reshape_and_cache,
     reshape_and_cache_,
     build_pools,

@@ -210,6 +210,50 @@ def decode(query, k_pool, v_pool, block_tables, context_lens, scale, dtype, bloc
     return out
 
 
+def decode_multi(query, k_pool, v_pool, block_tables, context_lens, scale, dtype, block_size,
+                 q_len, kv_dtype=None, k_scale=None, v_scale=None) -> np.ndarray:
+    """Attention of ``q_len`` new tokens per sequence over the paged cache
+    (float64 output [B, q_len, Hq, D]).
+
+    Speculative verification ("推迟投机解码" of wzjinhao.cn/news/69573,
+    section "嵌入式流式推理的访存墙与投机瓶颈": the target model scores a
+    batch of draft tokens at once) and chunked prefill ("大模型推理内存优化…",
+    pwwt.cn/news/3010209, section "工程边界与架构取舍": a long prompt is
+    processed in pieces between decode steps) both attend with several new
+    tokens whose K/V are already in the cache.
+    Reading: ``context_lens[b]`` counts them; new token i of sequence b sits
+    at position p = context_lens[b] - q_len + i and attends causally to the
+    cached positions 0..p; a token with p < 0 attends to nothing and gives
+    zeros.  query [B, q_len, Hq, D]; the GQA map is that of ``decode``.
+    """
+    q_all = to_f64(query, dtype)
+    b_count, ql, hq, d = q_all.shape
+    if ql != q_len:
+        raise ValueError("query must be [B, q_len, Hq, D]")
+    hkv = k_pool.shape[2]
+    if hq % hkv != 0:
+        raise ValueError("Hq must be a multiple of Hkv")
+    group = hq // hkv
+    out = np.zeros((b_count, q_len, hq, d), dtype=np.float64)
+    for b in range(b_count):
+        n_ctx = int(context_lens[b])
+        for i in range(q_len):
+            n = n_ctx - q_len + i + 1  # keys visible to new token i
+            if n <= 0:
+                continue
+            idx = np.arange(n)
+            if kv_dtype == "fp8_e4m3":
+                keys = fp8.dequantize_rows(gather_rows(k_pool, block_tables[b], idx, block_size), k_scale)
+                vals = fp8.dequantize_rows(gather_rows(v_pool, block_tables[b], idx, block_size), v_scale)
+            else:
+                keys = to_f64(gather_rows(k_pool, block_tables[b], idx, block_size), dtype)
+                vals = to_f64(gather_rows(v_pool, block_tables[b], idx, block_size), dtype)
+            for g in range(hkv):
+                heads = slice(g * group, (g + 1) * group)
+                out[b, i, heads] = attention_one_group(q_all[b, i, heads], keys[:, g, :], vals[:, g, :], scale)
+    return out
+
+
 # ---------------------------------------------------------------------------
 # write side
 # ---------------------------------------------------------------------------

@@ -116,6 +116,10 @@ class DecodeCase:
     kv_dtype: Optional[str] = None
     k_scale: Optional[np.ndarray] = None
     v_scale: Optional[np.ndarray] = None
+    # several new tokens per sequence (speculative verification, chunked
+    # prefill): query is then [B, q_len, Hq, D] and the last q_len positions
+    # of each sequence are its new tokens; None for single-token decode
+    q_len: Optional[int] = None
 
     @property
     def num_seqs(self) -> int:
@@ -476,6 +480,50 @@ def config_llama70b_fp8() -> DecodeCase:
 
 def config_embedded_1p1b_fp8() -> DecodeCase:
     return config_fp8(config_embedded_1p1b)
+
+
+def make_multi_case(name: str, seed: int, dtype: str, lens, q_len: int, num_q_heads: int,
+                    num_kv_heads: int, head_dim: int, block_size: int, **kw) -> DecodeCase:
+    """A plain-paging case whose sequences each end with ``q_len`` new tokens
+    (already written); the query holds one row per new token."""
+    case = make_paged_case(name, seed, dtype, lens, num_q_heads, num_kv_heads, head_dim, block_size, **kw)
+    rng = np.random.Generator(np.random.PCG64([seed, 1]))
+    case.query = draw_values(rng, (case.num_seqs, q_len, num_q_heads, head_dim), dtype)
+    case.q_len = q_len
+    return case
+
+
+def config_spec_verify_tiny() -> DecodeCase:
+    """Speculative verification, small: q_len 5 (four drafts and the last
+    accepted token), B 4 with lengths 3 (shorter than q_len), 5, 37, 70;
+    Hq 8, Hkv 2, D 128, bf16, 16-token blocks."""
+    return make_multi_case("spec_verify_tiny", SEED_BASE + 30, "bf16", [3, 5, 37, 70], 5, 8, 2, 128, 16)
+
+
+def config_spec_verify_llama70b() -> DecodeCase:
+    """Speculative verification on the 70B-shaped batch: the lengths,
+    placement and K/V of the single-token workload, q_len 5 per sequence."""
+    case = config_llama70b()
+    rng = np.random.Generator(np.random.PCG64([case.seed, 5]))
+    case.query = draw_values(rng, (case.num_seqs, 5, case.num_q_heads, case.head_dim), case.dtype)
+    case.q_len = 5
+    case.name = "spec_verify_llama70b"
+    return case
+
+
+def config_chunked_prefill() -> DecodeCase:
+    """Chunked prefill with 70B heads: four sequences with 0, 1000, 3000 and
+    7000 earlier tokens each take a 256-token chunk (q_len 256, Hq 64,
+    Hkv 8, D 128, bf16, 16-token blocks)."""
+    return make_multi_case("chunked_prefill", SEED_BASE + 31, "bf16", [256, 1256, 3256, 7256], 256,
+                           64, 8, 128, 16)
+
+
+MULTI_CONFIGS = {
+    "spec_verify_tiny": config_spec_verify_tiny,
+    "spec_verify_llama70b": config_spec_verify_llama70b,
+    "chunked_prefill": config_chunked_prefill,
+}
 
 
 FP8_CONFIGS = {
