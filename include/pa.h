@@ -318,6 +318,35 @@ int pa_decode(pa_pool *pool, void *out, const void *query, const int32_t *block_
               int32_t num_q_heads, int32_t max_context_len, float scale, const pa_ring *ring,
               void *workspace, size_t workspace_bytes, void *stream);
 
+/* Bytes of device workspace pa_decode_multi needs (split partials); 0 when
+ * none is needed or on invalid arguments. */
+size_t pa_decode_multi_workspace_bytes(const pa_pool *pool, int32_t num_seqs, int32_t q_len,
+                                       int32_t num_q_heads, int32_t max_context_len);
+
+/* Device: attention of q_len new tokens per sequence over the paged cache,
+ * for the batched check of draft tokens in speculative decoding [P3,
+ * section "嵌入式流式推理的访存墙与投机瓶颈": a step of draft tokens is scored
+ * in one pass] and for chunked prefill [P4, section "工程边界与架构取舍": a
+ * long prompt is processed in pieces].  The new tokens' K/V are already in
+ * the cache (pa_reshape_and_cache) and counted in context_lens.  New token i
+ * of sequence b sits at position p = context_lens[b] - q_len + i and attends
+ * causally to positions 0..p; p < 0 gives an all-zero row.  For query head h
+ * (KV head h / G):
+ *   out[b,i,h,:] = sum_{t<=p} softmax_t(scale * <q[b,i,h,:], K_t>) * V_t
+ *   out, query:   device [num_seqs, q_len, num_q_heads, head_dim], pool dtype
+ *                 (16-bit pools only), rounded to nearest-even from fp32.
+ *   block_tables, context_lens, max_context_len, workspace: as pa_decode
+ *                 (workspace >= pa_decode_multi_workspace_bytes).
+ *   q_len:        1 .. 4096; q_len * G <= 2^20.
+ * q_len = 1 is single-token decode by another kernel (same result within
+ * rounding).  Rejecting draft tokens needs no call: lowering context_lens
+ * hides their rows, and the next write overwrites them.  PA_ERR_UNSUPPORTED
+ * for fp32 and 8-bit pools. */
+int pa_decode_multi(pa_pool *pool, void *out, const void *query, const int32_t *block_tables,
+                    int32_t max_blocks_per_seq, const int32_t *context_lens, int32_t num_seqs,
+                    int32_t q_len, int32_t num_q_heads, int32_t max_context_len, float scale,
+                    void *workspace, size_t workspace_bytes, void *stream);
+
 /* Name of a status code (static string). */
 const char *pa_status_str(int status);
 

@@ -18,7 +18,7 @@ from ._lib import PaRing
 __all__ = [
     "PaError", "Pool", "Ring", "ring_slot", "compute_slot_mapping", "reshape_and_cache",
     "decode_workspace_bytes", "rope_table_bytes", "rope_table_init", "decode", "DTYPES",
-    "block_hashes", "copy_blocks",
+    "block_hashes", "copy_blocks", "decode_multi_workspace_bytes", "decode_multi",
 ]
 
 DTYPES = {"f32": _lib.PA_F32, "f16": _lib.PA_F16, "bf16": _lib.PA_BF16}
@@ -299,3 +299,29 @@ def decode(pool: Pool, out, query, block_tables, context_lens, max_context_len: 
         _dev_ptr(block_tables, "block_tables"), int(block_tables.shape[1]),
         _dev_ptr(context_lens, "context_lens"), b, hq, int(max_context_len), float(scale),
         _ring_ptr(ring), ws_ptr, ws_bytes, _stream_ptr(stream)), "pa_decode")
+
+
+def decode_multi_workspace_bytes(pool: Pool, num_seqs: int, q_len: int, num_q_heads: int,
+                                 max_context_len: int) -> int:
+    return int(_lib.load().pa_decode_multi_workspace_bytes(pool.handle, num_seqs, q_len, num_q_heads,
+                                                           max_context_len))
+
+
+def decode_multi(pool: Pool, out, query, block_tables, context_lens, max_context_len: int,
+                 scale: float, workspace=None, stream=None) -> None:
+    """Causal attention of q_len new tokens per sequence: ``query``/``out``
+    [B, q_len, Hq, D] (device tensors, async)."""
+    b, ql, hq, d = query.shape
+    if tuple(out.shape) != (b, ql, hq, d) or d != pool.head_dim:
+        raise ValueError("out/query must be [B, q_len, Hq, D] with D = the pool's head size")
+    if query.dtype != pool.act_dtype or out.dtype != pool.act_dtype:
+        raise ValueError("query/out dtype must match the pool")
+    ws_ptr, ws_bytes = None, 0
+    if workspace is not None:
+        ws_ptr = _dev_ptr(workspace, "workspace")
+        ws_bytes = workspace.numel() * workspace.element_size()
+    _check(_lib.load().pa_decode_multi(
+        pool.handle, _dev_ptr(out, "out"), _dev_ptr(query, "query"),
+        _dev_ptr(block_tables, "block_tables"), int(block_tables.shape[1]),
+        _dev_ptr(context_lens, "context_lens"), b, ql, hq, int(max_context_len), float(scale),
+        ws_ptr, ws_bytes, _stream_ptr(stream)), "pa_decode_multi")

@@ -19,7 +19,7 @@ BUILD_DIR = os.path.join(ROOT, "_build")
 LIB_NAME = "libpa_mi355x.so"
 LIB_PATH = os.path.join(PKG, LIB_NAME)
 
-HIP_SOURCES = ["decode_kernels.hip", "write_kernels.hip", "api.hip"]
+HIP_SOURCES = ["decode_kernels.hip", "multi_kernels.hip", "write_kernels.hip", "api.hip"]
 CPP_SOURCES = ["pool.cpp", "prefix.cpp"]
 ARCH = "gfx950"
 

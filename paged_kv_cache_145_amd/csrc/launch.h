@@ -55,6 +55,35 @@ struct DecodeArgs {
   KvScales kv_scale;  // 8-bit pools: dequantisation scales per KV head
 };
 
+// Multi-token decode (several new tokens per sequence, causal).
+struct MultiArgs {
+  void *out;          // [B, q_len, Hq, D]
+  const void *query;  // [B, q_len, Hq, D]
+  const void *k_cache;
+  const void *v_cache;
+  const int32_t *block_tables;
+  const int32_t *context_lens;
+  float *ws_o;   // split partials [B][passes][max_splits][Hkv][pass_rows][D]
+  float *ws_ml;  // (running max in log2 units, sum) per partial row
+  int64_t kv_block_stride;  // elements per physical block
+  int32_t num_seqs;
+  int32_t num_blocks;
+  int32_t max_context;
+  int32_t max_blocks_per_seq;
+  int32_t num_q_heads;
+  int32_t num_kv_heads;
+  int32_t group;        // Hq / Hkv
+  int32_t q_len;
+  int32_t rows;         // q_len * group query rows per KV head
+  int32_t pass_rows;    // 16 * (row tiles per wave)
+  int32_t passes;       // ceil(rows / pass_rows)
+  int32_t head_groups;  // ceil(Hkv / 4)
+  int32_t block_shift;
+  int32_t split_tiles;  // 16-token tiles per split, at most 64
+  int32_t max_splits;   // splits of the longest (sequence, pass)
+  float scale_log2;
+};
+
 enum class DecodeKernel { kMfma, kValu };
 
 // Upper bounds the host uses to size the workspace.
@@ -72,6 +101,8 @@ int choose_partition_tokens(int64_t effective_max_context);
 // dtype: the query/output dtype; kv_fp8: the pools hold E4M3 codes.
 hipError_t launch_decode(const DecodeArgs &a, pa_dtype dtype, int head_dim, bool ring, bool kv_fp8,
                          DecodeChoice choice, int num_seqs, hipStream_t stream);
+
+hipError_t launch_decode_multi(const MultiArgs &a, pa_dtype dtype, int head_dim, hipStream_t stream);
 
 hipError_t launch_reshape_and_cache(pa_dtype dtype, void *k_cache, void *v_cache,
                                     const void *key, const void *value,
