@@ -389,6 +389,137 @@ def measure_prefix(args) -> int:
     return 0
 
 
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # dense bf16/f16 MFMA peak of MI355X
+
+
+def multi_costs(case) -> dict:
+    """Algorithmic bytes and flops of one pa_decode_multi call: every K/V
+    row the longest query row of each sequence sees, once; the queries and
+    outputs; table entries.  Flops: 4 * D per (query row, visible key)."""
+    s = {"f32": 4, "f16": 2, "bf16": 2}[case.dtype]
+    lens = case.context_lens.astype(np.int64)
+    row = case.num_kv_heads * case.head_dim * 2 * s
+    kv = int(lens.sum()) * row
+    qo = case.num_seqs * case.q_len * case.num_q_heads * case.head_dim * 2 * s
+    tables = int(sum(-(-int(n) // case.block_size) for n in lens)) * 4 + case.num_seqs * 4
+    keys_seen = sum(max(0, int(n) - case.q_len + i + 1) for n in lens for i in range(case.q_len))
+    flops = 4 * case.head_dim * case.num_q_heads * keys_seen
+    return {"bytes": kv + qo + tables, "flops": flops, "tokens": int(lens.sum())}
+
+
+def measure_multi(args) -> int:
+    """Multi-token paged decode (speculative verification, chunked prefill)
+    on one of the multi-token workloads; one JSON line."""
+    import torch
+
+    import paged_kv_cache_145_amd as pk
+    import workloads
+
+    dev = "cuda:0"
+    torch.cuda.set_device(0)
+    name = args.config if args.config in workloads.MULTI_CONFIGS else "spec_verify_llama70b"
+    print(f"bench: generating the seeded workload {name}", file=sys.stderr, flush=True)
+    case = workloads.MULTI_CONFIGS[name]()
+    tdt = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}[case.dtype]
+    raw_view = np.int32 if case.dtype == "f32" else np.int16
+
+    def to_dev(raw):
+        return torch.from_numpy(np.ascontiguousarray(raw).view(raw_view)).view(tdt).to(dev)
+
+    k, v = _nan_pools(workloads, torch, (case.num_blocks, case.block_size, case.num_kv_heads, case.head_dim),
+                      case.dtype, dev)
+    pool = pk.Pool(k, v, case.block_size)
+    for ch in case.writes:
+        sid = np.full(ch.positions.shape, ch.seq, dtype=np.int32)
+        slots = pk.compute_slot_mapping(pool, case.block_tables, sid, ch.positions)
+        pk.reshape_and_cache(pool, to_dev(ch.keys), to_dev(ch.values), torch.from_numpy(slots).to(dev))
+    query = to_dev(case.query)
+    tables = torch.from_numpy(case.block_tables).to(dev)
+    lens = torch.from_numpy(case.context_lens).to(dev)
+    mcl = int(case.context_lens.max())
+    out = torch.empty(tuple(case.query.shape), dtype=tdt, device=dev)
+    ws = torch.empty(max(pk.decode_multi_workspace_bytes(pool, case.num_seqs, case.q_len, case.num_q_heads, mcl), 1),
+                     dtype=torch.uint8, device=dev)
+
+    def call():
+        pk.decode_multi(pool, out, query, tables, lens, mcl, case.scale, workspace=ws)
+
+    for _ in range(args.warmup):
+        call()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    mean_us, med_us = _event_us(torch, call, args.steps)
+    wall = time.perf_counter() - t0
+    pool.close()
+    c = multi_costs(case)
+    gbs = c["bytes"] / (mean_us * 1e-6) / 1e9
+    tflops = c["flops"] / (mean_us * 1e-6) / 1e12
+    # the bound is the resource whose ideal time is longer
+    mfma_bound = c["flops"] / (MFMA_BF16_PEAK_TFLOPS * 1e12) > c["bytes"] / (HBM_PEAK_GBS * 1e9)
+    roof = ({"bound": "mfma", "achieved": round(tflops, 1), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+             "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4), "algorithmic_flops": c["flops"]}
+            if mfma_bound else
+            {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+             "frac": round(gbs / HBM_PEAK_GBS, 4), "algorithmic_bytes": c["bytes"]})
+    roof["kernel"] = "pa_decode_multi call: decode_multi_kernel (+ decode_multi_reduce_kernel) (HIP events)"
+    roof["traffic"] = None
+    new_tokens = case.num_seqs * case.q_len
+    result = {
+        "metric": "multi-token paged decode: new tokens attended per second",
+        "value": round(new_tokens / (mean_us * 1e-6), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall / args.steps * 1e3, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": case.dtype,
+        "data": "synthetic",
+        "config": {"workload": (f"{name}: B {case.num_seqs}, q_len {case.q_len}, Hq {case.num_q_heads}, "
+                                f"Hkv {case.num_kv_heads}, D {case.head_dim}, {case.dtype}, block {case.block_size}, "
+                                f"{c['tokens']} cached tokens (the new ones included)"),
+                   "global_batch": case.num_seqs, "q_len": case.q_len, "seed": case.seed},
+        "call_us": {"mean": round(mean_us, 2), "median": round(med_us, 2)},
+        "effective_gbs": round(gbs, 1),
+        "effective_tflops": round(tflops, 2),
+        "roofline": roof,
+        "cpu_baseline": None if args.no_cpu_baseline else multi_cpu_baseline(case),
+    }
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+def multi_cpu_baseline(case, max_rows: int = 64) -> dict:
+    """The oracle's decode_multi on a bounded sample: the new tokens of the
+    first sequences, up to ``max_rows`` (sequence, token) rows."""
+    import oracle
+
+    try:
+        from threadpoolctl import threadpool_limits
+    except ImportError:  # pragma: no cover
+        threadpool_limits = None
+    nseq = max(1, min(case.num_seqs, max_rows // case.q_len))
+    kp, vp, _ = oracle.build_pools(case)
+    ctx = threadpool_limits(limits=1) if threadpool_limits else None
+    if ctx:
+        ctx.__enter__()
+    try:
+        t0, c0 = time.perf_counter(), time.process_time()
+        oracle.decode_multi(case.query[:nseq], kp, vp, case.block_tables[:nseq], case.context_lens[:nseq],
+                            case.scale, case.dtype, case.block_size, case.q_len)
+        wall = time.perf_counter() - t0
+    finally:
+        if ctx:
+            ctx.__exit__(None, None, None)
+    cores = max(1, round((time.process_time() - c0) / wall))
+    rows = nseq * case.q_len
+    return {"value": round(rows / wall, 2), "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "sample": f"the new tokens of the first {nseq} sequences ({rows} rows), fp64 gather + softmax, "
+                      f"{wall:.2f} s"}
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[1])
     ap.add_argument("--gpus", type=int, default=1)
@@ -398,7 +529,8 @@ def main() -> int:
                     help="extra decode calls each preceded by a 1 GiB read that evicts the caches (0 = skip)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--config", default="llama70b_b64",
-                    choices=sorted(list(__import__("workloads").CONFIGS) + list(__import__("workloads").FP8_CONFIGS)),
+                    choices=sorted(list(__import__("workloads").CONFIGS) + list(__import__("workloads").FP8_CONFIGS)
+                                   + list(__import__("workloads").MULTI_CONFIGS)),
                     help="workload (default: the 70B-shaped batch the metric is quoted on; the others "
                          "are the parity configurations, timed the same way)")
     ap.add_argument("--launch", choices=("eager", "graph"), default="eager",
@@ -408,9 +540,10 @@ def main() -> int:
                     help="only run this many decode calls, then a 1 GiB copy (for rocprofv3 counter runs)")
     ap.add_argument("--write-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="turn two rocprofv3 counter_collection.csv files into the traffic record")
-    ap.add_argument("--measure", choices=("decode", "prefix"), default="decode",
+    ap.add_argument("--measure", choices=("decode", "prefix", "multi"), default="decode",
                     help="decode (default): the hot-path step; prefix: prefix reuse with copy-on-write "
-                         "(admission, tail copies, shared-prefix decode, bulk block copy)")
+                         "(admission, tail copies, shared-prefix decode, bulk block copy); multi: "
+                         "multi-token decode on --config spec_verify_llama70b (default) or chunked_prefill")
     ap.add_argument("--traffic-command", default="",
                     help="the profiling command line recorded with --write-traffic")
     args = ap.parse_args()
@@ -440,6 +573,11 @@ def main() -> int:
     _lib.load()
     if args.measure == "prefix":
         return measure_prefix(args)
+    if args.measure == "multi":
+        return measure_multi(args)
+    if args.config in workloads.MULTI_CONFIGS:
+        print("multi-token workloads run with --measure multi", file=sys.stderr)
+        return 2
     dev = "cuda:0"
     torch.cuda.set_device(0)
     print(f"bench: generating the seeded workload {args.config}", file=sys.stderr, flush=True)

@@ -318,8 +318,8 @@ int pa_decode(pa_pool *pool, void *out, const void *query, const int32_t *block_
               int32_t num_q_heads, int32_t max_context_len, float scale, const pa_ring *ring,
               void *workspace, size_t workspace_bytes, void *stream);
 
-/* Bytes of device workspace pa_decode_multi needs (split partials); 0 when
- * none is needed or on invalid arguments. */
+/* Bytes of device workspace pa_decode_multi needs (tile schedule and
+ * stream-K partials); 0 for num_seqs == 0 or invalid arguments. */
 size_t pa_decode_multi_workspace_bytes(const pa_pool *pool, int32_t num_seqs, int32_t q_len,
                                        int32_t num_q_heads, int32_t max_context_len);
 
@@ -337,7 +337,8 @@ size_t pa_decode_multi_workspace_bytes(const pa_pool *pool, int32_t num_seqs, in
  *                 (16-bit pools only), rounded to nearest-even from fp32.
  *   block_tables, context_lens, max_context_len, workspace: as pa_decode
  *                 (workspace >= pa_decode_multi_workspace_bytes).
- *   q_len:        1 .. 4096; q_len * G <= 2^20.
+ *   q_len:        1 .. 4096; q_len * G <= 49152 (D = 128) or 65536 (D = 64),
+ *                 else PA_ERR_UNSUPPORTED.
  * q_len = 1 is single-token decode by another kernel (same result within
  * rounding).  Rejecting draft tokens needs no call: lowering context_lens
  * hides their rows, and the next write overwrites them.  PA_ERR_UNSUPPORTED

@@ -75,28 +75,27 @@ WorkspaceLayout workspace_layout(const pa_pool *pool, int32_t num_seqs, int32_t 
 }
 
 struct MultiLayout {
-  int mt, pass_rows, passes, split_tiles, max_splits;
-  size_t ml_bytes, o_bytes, total;
+  int mt, pass_rows, passes, seqs_per_launch, groups;
+  size_t sched_bytes, ml_bytes, o_bytes, total;
 };
 
-MultiLayout multi_layout(const pa_pool *pool, int32_t num_seqs, int32_t q_len, int32_t num_q_heads,
-                         int32_t max_context_len) {
+// Sizes of one launch slice (at most kMaxMultiSeqsHost (sequence, pass)
+// pairs); slices run one after another and reuse the workspace.
+MultiLayout multi_layout(const pa_pool *pool, int32_t num_seqs, int32_t q_len, int32_t num_q_heads) {
   MultiLayout m{};
   const int group = num_q_heads / pool->num_kv_heads;
   const int64_t rows = (int64_t)q_len * group;
-  m.mt = (int)std::min<int64_t>(4, ceil_div(rows, 16));
+  m.mt = (int)std::min<int64_t>(kMultiMaxRowTiles(pool->head_dim), ceil_div(rows, 16));
   m.pass_rows = 16 * m.mt;
   m.passes = (int)ceil_div(rows, m.pass_rows);
-  const int forced = env_int("PA_MULTI_SPLIT_TILES", 0);
-  m.split_tiles = forced >= 1 && forced <= 64 ? forced : 32;
-  const int64_t tiles = ceil_div(max_context_len, kTileTokens);
-  m.max_splits = (int)std::max<int64_t>(1, ceil_div(tiles, m.split_tiles));
-  if (m.max_splits > 1) {
-    const size_t items = (size_t)num_seqs * m.passes * m.max_splits * pool->num_kv_heads * m.pass_rows;
-    m.ml_bytes = round_up(items * 2 * sizeof(float), 256);
-    m.o_bytes = round_up(items * pool->head_dim * sizeof(float), 256);
-  }
-  m.total = m.ml_bytes + m.o_bytes;
+  m.seqs_per_launch = std::max(1, std::min(num_seqs, kMaxMultiSeqsHost / std::max(1, m.passes)));
+  m.groups = std::max(1, (multi_grid() * 4) / pool->num_kv_heads);
+  const size_t nv = (size_t)m.seqs_per_launch * m.passes;
+  const size_t rows_total = (m.groups + nv) * pool->num_kv_heads * m.pass_rows;
+  m.sched_bytes = round_up((nv + 1) * sizeof(int32_t), 256);
+  m.ml_bytes = round_up(rows_total * 2 * sizeof(float), 256);
+  m.o_bytes = round_up(rows_total * pool->head_dim * sizeof(float), 256);
+  m.total = m.sched_bytes + m.ml_bytes + m.o_bytes;
   return m;
 }
 
@@ -176,7 +175,8 @@ size_t pa_decode_multi_workspace_bytes(const pa_pool *pool, int32_t num_seqs, in
   if (pool == nullptr || num_seqs < 0 || q_len < 1 || q_len > pa::kMaxMultiQLen || num_q_heads <= 0 ||
       max_context_len < 0 || num_q_heads % pool->num_kv_heads != 0)
     return 0;
-  return pa::multi_layout(pool, num_seqs, q_len, num_q_heads, max_context_len).total;
+  if (num_seqs == 0) return 0;
+  return pa::multi_layout(pool, num_seqs, q_len, num_q_heads).total;
 }
 
 int pa_decode_multi(pa_pool *pool, void *out, const void *query, const int32_t *block_tables,
@@ -187,7 +187,11 @@ int pa_decode_multi(pa_pool *pool, void *out, const void *query, const int32_t *
       max_context_len < 0 || max_blocks_per_seq <= 0)
     return PA_ERR_INVAL;
   if (num_q_heads % pool->num_kv_heads != 0) return PA_ERR_INVAL;
-  if ((int64_t)q_len * (num_q_heads / pool->num_kv_heads) > (1 << 20)) return PA_ERR_UNSUPPORTED;
+  const int group = num_q_heads / pool->num_kv_heads;
+  // one launch slice must hold every pass of a sequence
+  if (pa::ceil_div((int64_t)q_len * group, 16 * pa::kMultiMaxRowTiles(pool->head_dim)) >
+      pa::kMaxMultiSeqsHost)
+    return PA_ERR_UNSUPPORTED;
   if (pool->kv_fp8 || (pool->dtype != PA_F16 && pool->dtype != PA_BF16)) return PA_ERR_UNSUPPORTED;
   if (num_seqs == 0) return PA_OK;
   if (out == nullptr || query == nullptr || block_tables == nullptr || context_lens == nullptr)
@@ -197,45 +201,47 @@ int pa_decode_multi(pa_pool *pool, void *out, const void *query, const int32_t *
     return PA_ERR_INVAL;
   if (max_context_len > (int64_t)max_blocks_per_seq * pool->block_size) return PA_ERR_INVAL;
   if (!(scale == scale)) return PA_ERR_INVAL;
-  const pa::MultiLayout m = pa::multi_layout(pool, num_seqs, q_len, num_q_heads, max_context_len);
-  if (m.total > 0) {
-    if (workspace == nullptr || workspace_bytes < m.total) return PA_ERR_NOMEM;
-    if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return PA_ERR_INVAL;
-  }
-  const int head_groups = (pool->num_kv_heads + 3) / 4;
-  if ((int64_t)num_seqs * m.max_splits > INT32_MAX / 256 || (int64_t)head_groups * m.passes > 65535 ||
-      (int64_t)num_seqs * m.passes * pool->num_kv_heads > INT32_MAX / 256)
-    return PA_ERR_UNSUPPORTED;
+  const pa::MultiLayout m = pa::multi_layout(pool, num_seqs, q_len, num_q_heads);
+  if (workspace == nullptr || workspace_bytes < m.total) return PA_ERR_NOMEM;
+  if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return PA_ERR_INVAL;
 
   pa::MultiArgs a{};
-  a.out = out;
-  a.query = query;
   a.k_cache = pool->k_cache;
   a.v_cache = pool->v_cache;
-  a.block_tables = block_tables;
-  a.context_lens = context_lens;
   char *ws = static_cast<char *>(workspace);
-  a.ws_ml = m.ml_bytes > 0 ? reinterpret_cast<float *>(ws) : nullptr;
-  a.ws_o = m.o_bytes > 0 ? reinterpret_cast<float *>(ws + m.ml_bytes) : nullptr;
+  a.ws_sched = reinterpret_cast<int32_t *>(ws);
+  a.ws_ml = reinterpret_cast<float *>(ws + m.sched_bytes);
+  a.ws_o = reinterpret_cast<float *>(ws + m.sched_bytes + m.ml_bytes);
   a.kv_block_stride = (int64_t)pool->block_size * pool->num_kv_heads * pool->head_dim;
-  a.num_seqs = num_seqs;
   a.num_blocks = pool->num_blocks;
   a.max_context = max_context_len;
   a.max_blocks_per_seq = max_blocks_per_seq;
   a.num_q_heads = num_q_heads;
   a.num_kv_heads = pool->num_kv_heads;
-  a.group = num_q_heads / pool->num_kv_heads;
+  a.group = group;
   a.q_len = q_len;
-  a.rows = q_len * a.group;
+  a.rows = q_len * group;
   a.pass_rows = m.pass_rows;
   a.passes = m.passes;
-  a.head_groups = head_groups;
+  a.groups = m.groups;
+  const int forced_range = pa::env_int("PA_MULTI_MIN_RANGE", 0);
+  a.min_range_tiles = forced_range >= 1 ? forced_range : 4;
   a.block_shift = pa::log2_exact(pool->block_size);
-  a.split_tiles = m.split_tiles;
-  a.max_splits = m.max_splits;
   a.scale_log2 = scale * pa::kLog2eHost;
-  return pa::hip_status(pa::launch_decode_multi(a, pool->dtype, pool->head_dim,
-                                                static_cast<hipStream_t>(stream)));
+  const int64_t row_elems = (int64_t)q_len * num_q_heads * pool->head_dim;
+  const int esize = pa::dtype_bytes(pool->dtype);
+  const int grid = pa::multi_grid();
+  for (int32_t s0 = 0; s0 < num_seqs; s0 += m.seqs_per_launch) {
+    a.num_seqs = std::min(m.seqs_per_launch, num_seqs - s0);
+    a.out = static_cast<char *>(out) + s0 * row_elems * esize;
+    a.query = static_cast<const char *>(query) + s0 * row_elems * esize;
+    a.block_tables = block_tables + (int64_t)s0 * max_blocks_per_seq;
+    a.context_lens = context_lens + s0;
+    const int rc = pa::hip_status(pa::launch_decode_multi(a, pool->dtype, pool->head_dim, grid,
+                                                          static_cast<hipStream_t>(stream)));
+    if (rc != PA_OK) return rc;
+  }
+  return PA_OK;
 }
 
 size_t pa_decode_workspace_bytes(const pa_pool *pool, int32_t num_seqs, int32_t num_q_heads,

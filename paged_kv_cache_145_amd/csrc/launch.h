@@ -56,6 +56,7 @@ struct DecodeArgs {
 };
 
 // Multi-token decode (several new tokens per sequence, causal).
+constexpr int kMaxMultiSeqsHost = 1024;  // (sequence, pass) pairs per launch slice
 struct MultiArgs {
   void *out;          // [B, q_len, Hq, D]
   const void *query;  // [B, q_len, Hq, D]
@@ -63,8 +64,11 @@ struct MultiArgs {
   const void *v_cache;
   const int32_t *block_tables;
   const int32_t *context_lens;
-  float *ws_o;   // split partials [B][passes][max_splits][Hkv][pass_rows][D]
-  float *ws_ml;  // (running max in log2 units, sum) per partial row
+  // stream-K partials: slots [(groups + B * passes) * Hkv][pass_rows][D]
+  // and [..][pass_rows][2]; tile prefix per (sequence, pass) [B * passes + 1]
+  float *ws_o;
+  float *ws_ml;
+  int32_t *ws_sched;
   int64_t kv_block_stride;  // elements per physical block
   int32_t num_seqs;
   int32_t num_blocks;
@@ -72,17 +76,22 @@ struct MultiArgs {
   int32_t max_blocks_per_seq;
   int32_t num_q_heads;
   int32_t num_kv_heads;
-  int32_t group;        // Hq / Hkv
+  int32_t group;      // Hq / Hkv
   int32_t q_len;
-  int32_t rows;         // q_len * group query rows per KV head
-  int32_t pass_rows;    // 16 * (row tiles per wave)
-  int32_t passes;       // ceil(rows / pass_rows)
-  int32_t head_groups;  // ceil(Hkv / 4)
+  int32_t rows;       // q_len * group query rows per KV head
+  int32_t pass_rows;  // 16 * (row tiles per wave)
+  int32_t passes;     // ceil(rows / pass_rows)
+  int32_t groups;     // wave groups of the persistent grid
+  int32_t min_range_tiles;
   int32_t block_shift;
-  int32_t split_tiles;  // 16-token tiles per split, at most 64
-  int32_t max_splits;   // splits of the longest (sequence, pass)
   float scale_log2;
 };
+
+// Work-groups of the multi-token kernel's persistent grid (one per CU).
+int multi_grid();
+// Row tiles of 16 query rows one wave holds: registers allow four at
+// D = 64 and three at D = 128 (with a four-deep load pipeline).
+constexpr int kMultiMaxRowTiles(int head_dim) { return head_dim == 128 ? 3 : 4; }
 
 enum class DecodeKernel { kMfma, kValu };
 
@@ -102,7 +111,8 @@ int choose_partition_tokens(int64_t effective_max_context);
 hipError_t launch_decode(const DecodeArgs &a, pa_dtype dtype, int head_dim, bool ring, bool kv_fp8,
                          DecodeChoice choice, int num_seqs, hipStream_t stream);
 
-hipError_t launch_decode_multi(const MultiArgs &a, pa_dtype dtype, int head_dim, hipStream_t stream);
+hipError_t launch_decode_multi(const MultiArgs &a, pa_dtype dtype, int head_dim, int grid,
+                               hipStream_t stream);
 
 hipError_t launch_reshape_and_cache(pa_dtype dtype, void *k_cache, void *v_cache,
                                     const void *key, const void *value,

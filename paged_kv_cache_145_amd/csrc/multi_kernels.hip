@@ -8,23 +8,28 @@
 //
 // New token i of sequence b sits at position p = L_b - q_len + i (its K/V
 // are already cached) and sees positions 0..p.  The q_len * G query rows of
-// one KV head (row r = i * G + h) are the M dimension of the MFMA tiles.
+// one KV head (row r = i * G + h) are the M dimension of the MFMA tiles; a
+// wave holds MT row tiles (16 * MT rows, a "pass") and longer row sets take
+// several passes.
 //
-// Work split.  Grid (sequence x KV split, 1, head group x row pass): a
-// work-group of 4 waves takes 4 consecutive KV heads (so the waves read the
-// same token rows side by side), one split of at most split_tiles 16-token
-// tiles, and one pass of 16 * MT query rows; each wave keeps its MT row
-// tiles in registers and streams its head's K/V tiles once for all of them.
-// A (sequence, pass) with one split writes its output rows directly;
-// otherwise each split leaves normalised partials and
-// decode_multi_reduce_kernel merges them in split order.
+// Work split (stream-K, as in the single-token kernel).  A virtual sequence
+// is a (sequence, pass) pair; its tiles are the 16-token tiles up to the
+// last key its rows see.  The flattened list of (virtual sequence, tile)
+// is cut into equal ranges, one per group of Hkv waves; wave g of a group
+// streams KV head g over the range, so all waves carry the same number of
+// tiles and the heads of a token row are read side by side.  A virtual
+// sequence that starts and ends inside one range writes its output rows
+// directly; one cut by range boundaries leaves normalised partials in slots
+// (group + v) * Hkv + g, merged by decode_multi_reduce_kernel.
 //
-// Per 16-token tile, as in the single-token kernel but with MT query tiles:
+// Per 16-token tile:
 //   S[token][row] = K_tile . Q^T with v_mfma_f32_16x16x32 (A = the lane's
 //   own K row fragment, B = query rows); lane l gets S[4(l/16)+j][l%16];
 //   O[row][d] += P[row][token] V[token][d] with v_mfma_f32_16x16x16; V goes
 //   through a per-wave LDS tile and returns as B operands through
-//   transposing LDS reads (shared by the MT row tiles).
+//   transposing LDS reads, shared by the MT row tiles.
+#include <algorithm>
+
 #include "device_common.h"
 #include "launch.h"
 
@@ -32,7 +37,13 @@ namespace pa {
 namespace {
 
 constexpr int kMqWaves = 4;
-constexpr float kMqRescaleSlack = 8.0f;  // log2 units the running max may lag
+constexpr int kMaxMqSeqs = kMaxMultiSeqsHost;  // virtual sequences per launch
+constexpr float kMqRescaleSlack = 8.0f;        // log2 units the running max may lag
+constexpr int kMqQSlots = 2;                   // segment-opening tiles per staged chunk
+
+// Depth of the per-wave tile pipeline.
+template <int D, int MT>
+constexpr int kMqStagesFor = 4;
 
 // One lane's share of a V row: D / 16 elements, 16 or 8 bytes.
 template <int D>
@@ -60,96 +71,197 @@ struct MqLds {
   static constexpr int kVBytes = kTileTokens * kVRowBytes;
 };
 
-// Key range and split count of (sequence, pass); identical in both kernels.
-struct MqRange {
-  int L, row0, row_end, kv_end, tiles_end, splits;
-};
-__device__ __forceinline__ MqRange mq_range(const MultiArgs &a, int b, int pass) {
-  MqRange r;
-  r.L = min(max(a.context_lens[b], 0), a.max_context);
-  r.row0 = pass * a.pass_rows;
-  r.row_end = min(a.rows, r.row0 + a.pass_rows);
-  // the last row of the pass sees the most keys
-  r.kv_end = min(max(r.L - a.q_len + (r.row_end - 1) / a.group + 1, 0), r.L);
-  r.tiles_end = (r.kv_end + kTileTokens - 1) / kTileTokens;
-  r.splits = max(1, (r.tiles_end + a.split_tiles - 1) / a.split_tiles);
-  return r;
+// Rows of pass p and the last key position + 1 that its rows see.
+__device__ __forceinline__ void mq_pass(const MultiArgs &a, int L, int p, int &row0, int &row_end,
+                                        int &kv_end) {
+  row0 = p * a.pass_rows;
+  row_end = min(a.rows, row0 + a.pass_rows);
+  kv_end = min(max(L - a.q_len + (row_end - 1) / a.group + 1, 0), L);
 }
 
-// Partial slot of (sequence, pass, split, KV head, row within the pass).
-__device__ __forceinline__ int64_t mq_slot(const MultiArgs &a, int b, int pass, int s, int g, int row) {
-  return ((((int64_t)b * a.passes + pass) * a.max_splits + s) * a.num_kv_heads + g) * a.pass_rows + row;
+__device__ __forceinline__ int mq_len(const MultiArgs &a, int b) {
+  return min(max(a.context_lens[b], 0), a.max_context);
+}
+
+// Groups that get a tile range (short ranges cost more than they gain).
+__device__ __forceinline__ int mq_active_groups(const MultiArgs &a, int total) {
+  const int m = max(1, a.min_range_tiles);
+  return max(1, min(a.groups, (total + m - 1) / m));
+}
+
+// Tile schedule of the launch: s_tfirst[v] = tiles of virtual sequences
+// before v, s_kvend[v] = key positions v's rows see.  Work-group 0 also
+// publishes s_tfirst to the workspace for the merge kernel.
+__device__ int mq_schedule(const MultiArgs &a, int *s_tfirst, int *s_kvend, int *s_wsum) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int nv = a.num_seqs * a.passes;
+  int carry = 0;
+  for (int base = 0; base < nv; base += kMqWaves * kWave) {
+    const int v = base + tid;
+    int n = 0;
+    if (v < nv) {
+      const int b = v / a.passes;
+      int row0, row_end, kv_end;
+      mq_pass(a, mq_len(a, b), v - b * a.passes, row0, row_end, kv_end);
+      s_kvend[v] = kv_end;
+      n = (kv_end + kTileTokens - 1) / kTileTokens;
+    }
+    int x = n;  // inclusive scan within the wave
+#pragma unroll
+    for (int off = 1; off < kWave; off <<= 1) {
+      const int y = __shfl_up(x, off);
+      if (lane >= off) x += y;
+    }
+    if (lane == kWave - 1) s_wsum[wave] = x;
+    __syncthreads();
+    int woff = 0, tot = 0;
+#pragma unroll
+    for (int w = 0; w < kMqWaves; ++w) {
+      woff += w < wave ? s_wsum[w] : 0;
+      tot += s_wsum[w];
+    }
+    if (v < nv) s_tfirst[v] = carry + woff + x - n;
+    carry += tot;
+    __syncthreads();
+  }
+  if (tid == 0) s_tfirst[nv] = carry;
+  __syncthreads();
+  if (blockIdx.x == 0)
+    for (int v = tid; v <= nv; v += blockDim.x) a.ws_sched[v] = s_tfirst[v];
+  return carry;
 }
 
 template <class T, int D, int MT>
-__global__ __launch_bounds__(256) void decode_multi_kernel(MultiArgs a) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void decode_multi_kernel(MultiArgs a) {
   constexpr int KB = D / 32;  // score MFMAs per row tile and key tile
   constexpr int EV = D / 16;  // V elements per lane per row
   constexpr int NB = D / 16;  // output MFMAs per row tile (16 dims each)
   constexpr int kVRow = MqLds<D>::kVRowBytes;
+  constexpr int QF = MT * KB;  // query fragments per lane per segment
   typedef typename T::storage st;
   typedef typename MqV<D>::type vchunk;
+  __shared__ int s_tfirst[kMaxMqSeqs + 1];
+  __shared__ int s_kvend[kMaxMqSeqs];
+  __shared__ int s_wsum[kMqWaves];
   __shared__ __align__(16) char s_vt[kMqWaves][MqLds<D>::kVBytes];
+  __shared__ uint4 s_q[kMqWaves][kMqQSlots * QF * kWave];  // query fragments, lane-major
 
+  const int nv = a.num_seqs * a.passes;
+  const int total = mq_schedule(a, s_tfirst, s_kvend, s_wsum);
+  const int hkv = a.num_kv_heads, G = a.group, ql = a.q_len;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int row16 = lane & 15, grp = lane >> 4;
-  const int b = blockIdx.x / a.max_splits;
-  const int s = blockIdx.x - b * a.max_splits;
-  const int hg = blockIdx.z % a.head_groups;
-  const int pass = blockIdx.z / a.head_groups;
-  const int g = hg * kMqWaves + wave;
-  if (g >= a.num_kv_heads) return;  // no barriers in this kernel
-  const MqRange rg = mq_range(a, b, pass);
-  if (s >= rg.splits) return;
-  const int G = a.group, ql = a.q_len;
-  const int t_beg = s * a.split_tiles;
-  const int ntiles = max(0, min(t_beg + a.split_tiles, rg.tiles_end) - t_beg);  // <= 64
+  const int groups = mq_active_groups(a, total);
+  const int gw = blockIdx.x * kMqWaves + wave;
+  const int grp_id = gw / hkv;      // tile range of this wave
+  const int g = gw - grp_id * hkv;  // KV head of this wave
+  if (grp_id >= groups) return;     // no barriers follow
+  const int per = (total + groups - 1) / groups;
+  const int xbeg = grp_id * per;
+  const int xend = min(total, xbeg + per);
+  if (xbeg >= xend) return;
 
-  const int64_t row_stride = (int64_t)a.num_kv_heads * D;  // elements between token rows
+  const int64_t row_stride = (int64_t)hkv * D;  // elements between token rows
   const int bmask = (1 << a.block_shift) - 1;
   char *vt = s_vt[wave];
-
-  // This lane's query row in each row tile: row16 (the S column it holds).
-  int limit[MT];  // last key position the row sees (-1: none)
-  uint4 qf[MT][KB];
-#pragma unroll
-  for (int mt = 0; mt < MT; ++mt) {
-    const int r = rg.row0 + 16 * mt + row16;
-    const bool ok = r < rg.row_end;
-    const int i = ok ? r / G : 0;
-    const int h = ok ? r - i * G : 0;
-    limit[mt] = ok ? rg.L - ql + i : -1;
-    const st *q = static_cast<const st *>(a.query) +
-                  (((int64_t)b * ql + i) * a.num_q_heads + (int64_t)g * G + h) * D + 8 * grp;
-#pragma unroll
-    for (int kb = 0; kb < KB; ++kb)
-      qf[mt][kb] = ok ? *reinterpret_cast<const uint4 *>(q + 32 * kb) : make_uint4(0u, 0u, 0u, 0u);
-  }
-
-  // block id of tile t_beg + lane, read back per tile with readlane
-  int tblk = 0;
-  if (lane < ntiles) {
-    const int t = t_beg + lane;
-    tblk = a.block_tables[(int64_t)b * a.max_blocks_per_seq + ((kTileTokens * t) >> a.block_shift)];
-    tblk = min(max(tblk, 0), a.num_blocks - 1);
-  }
+  uint4 *qs = s_q[wave];
   const int k_off = (int)((row16 * row_stride + 8 * grp) * (int64_t)sizeof(st));
   int v_off[4];
 #pragma unroll
   for (int tau = 0; tau < 4; ++tau)
     v_off[tau] = (int)(((4 * grp + tau) * row_stride + EV * row16) * (int64_t)sizeof(st));
 
-  // Loads of tile j; past ntiles the record range is empty and nothing is read.
+  // segment state
+  f32x4 acc[MT][NB];
+  float m_run[MT], l_part[MT];
+  int limit[MT];  // last key position this lane's row sees in each row tile (-1: none)
+  uint4 qf[MT][KB];
+  int seg_row0 = 0, seg_row_end = 0;
+  bool seg_whole = false;
+
+  // Staged metadata of a chunk of up to 64 tiles (lane i: tile c0 + i),
+  // read back with readlane.
+  auto rd = [&](int x, int j) { return __builtin_amdgcn_readlane(x, j); };
+  int tv = 0, tt = 0, tvalid = 0, tflag = 0, toff_lo = 0, toff_hi = 0, tnrec = 0, tslot = 0;
+  int c0 = 0, cnt = 0;
+  auto stage = [&](int start) {
+    c0 = start;
+    cnt = min(kWave, xend - start);
+    tv = tt = tvalid = tflag = toff_lo = toff_hi = tnrec = 0;
+    int blk = 0;
+    if (lane < cnt) {
+      const int y = c0 + lane;
+      int lo = 0, hi = nv;  // largest v with s_tfirst[v] <= y (it has tiles)
+      while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (s_tfirst[mid] <= y) lo = mid;
+        else hi = mid;
+      }
+      tv = lo;
+      tt = y - s_tfirst[lo];
+      const int tiles = s_tfirst[lo + 1] - s_tfirst[lo];
+      const int b = lo / a.passes;
+      blk = a.block_tables[(int64_t)b * a.max_blocks_per_seq + ((kTileTokens * tt) >> a.block_shift)];
+      blk = min(max(blk, 0), a.num_blocks - 1);
+      tvalid = min(kTileTokens, s_kvend[lo] - kTileTokens * tt);
+      tflag = (tt == 0 ? 1 : 0) | (tt == tiles - 1 ? 2 : 0);
+    }
+    // tiles that open a segment get a query slot in LDS; the chunk ends
+    // before its (kMqQSlots + 1)-th opening tile
+    const bool opens = lane < cnt && ((tflag & 1) || c0 + lane == xbeg);
+    unsigned long long m = __ballot(opens);
+    if (__popcll(m) > kMqQSlots) {
+      unsigned long long r = m;
+      for (int i = 0; i < kMqQSlots; ++i) r &= r - 1;
+      cnt = __ffsll((long long)r) - 1;
+      m &= (1ull << cnt) - 1;
+    }
+    tslot = opens && lane < cnt ? __popcll(m & ((1ull << lane) - 1)) : 0;
+    uint4 qtmp[kMqQSlots][QF];
+    unsigned long long mm = m;
+#pragma unroll
+    for (int s2 = 0; s2 < kMqQSlots; ++s2) {
+      const int i = mm ? __ffsll((long long)mm) - 1 : 0;
+      const int v = rd(tv, i);
+      const int b = v / a.passes;
+      const int p = v - b * a.passes;
+      const int row_end = min(a.rows, (p + 1) * a.pass_rows);
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        const int r = p * a.pass_rows + 16 * mt + row16;
+        const bool ok = mm != 0 && r < row_end;
+        const int qi = ok ? r / G : 0;
+        const int h = ok ? r - qi * G : 0;
+        const st *q = static_cast<const st *>(a.query) +
+                      (((int64_t)b * ql + qi) * a.num_q_heads + (int64_t)g * G + h) * D + 8 * grp;
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb)
+          qtmp[s2][mt * KB + kb] =
+              ok ? *reinterpret_cast<const uint4 *>(q + 32 * kb) : make_uint4(0u, 0u, 0u, 0u);
+      }
+      mm &= mm - 1;
+    }
+    if (lane < cnt) {
+      const int64_t off = ((int64_t)blk * a.kv_block_stride +
+                           (int64_t)((kTileTokens * tt) & bmask) * row_stride + (int64_t)g * D) *
+                          (int64_t)sizeof(st);
+      toff_lo = (int)(uint32_t)off;
+      toff_hi = (int)(off >> 32);
+      tnrec = (int)(((tvalid - 1) * row_stride + D) * (int64_t)sizeof(st));  // tvalid >= 1 here
+    }
+#pragma unroll
+    for (int s2 = 0; s2 < kMqQSlots; ++s2)
+#pragma unroll
+      for (int f = 0; f < QF; ++f) qs[(s2 * QF + f) * kWave + lane] = qtmp[s2][f];
+  };
+
+  // Loads of staged tile j (j >= cnt: empty record range, no memory access).
   auto load_tile = [&](int j, uint4 (&k)[KB], vchunk (&v)[4]) {
     const int jj = min(j, kWave - 1);
-    const int t = t_beg + j;
-    const int blk = __builtin_amdgcn_readlane(tblk, jj);
-    const int valid = j < ntiles ? min(kTileTokens, rg.kv_end - kTileTokens * t) : 0;
-    const int64_t off = ((int64_t)blk * a.kv_block_stride +
-                         (int64_t)((kTileTokens * t) & bmask) * row_stride + (int64_t)g * D) *
-                        (int64_t)sizeof(st);
-    const int nrec = valid > 0 ? (int)(((valid - 1) * row_stride + D) * (int64_t)sizeof(st)) : 0;
+    const uint64_t off = ((uint64_t)(uint32_t)rd(toff_hi, jj) << 32) | (uint32_t)rd(toff_lo, jj);
+    const int nrec = j < cnt ? rd(tnrec, jj) : 0;
     const auto kr = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<char *>(static_cast<const char *>(a.k_cache) + off), (short)0, nrec, kBufferWord3);
     const auto vr = __builtin_amdgcn_make_buffer_rsrc(
@@ -160,19 +272,31 @@ __global__ __launch_bounds__(256) void decode_multi_kernel(MultiArgs a) {
     for (int tau = 0; tau < 4; ++tau) v[tau] = MqV<D>::load(vr, v_off[tau]);
   };
 
-  f32x4 acc[MT][NB];
-  float m_run[MT], l_part[MT];
+  auto begin_segment = [&](int j, int v, bool whole) {
+    const int slot = rd(tslot, j);
 #pragma unroll
-  for (int mt = 0; mt < MT; ++mt) {
-    m_run[mt] = -INFINITY;
-    l_part[mt] = 0.f;
+    for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-    for (int e = 0; e < NB; ++e) acc[mt][e] = f32x4{0.f, 0.f, 0.f, 0.f};
-  }
-  const float sl2 = a.scale_log2;
+      for (int kb = 0; kb < KB; ++kb) qf[mt][kb] = qs[(slot * QF + mt * KB + kb) * kWave + lane];
+    const int b = v / a.passes;
+    const int L = mq_len(a, b);
+    int kv_end;
+    mq_pass(a, L, v - b * a.passes, seg_row0, seg_row_end, kv_end);
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      const int r = seg_row0 + 16 * mt + row16;
+      limit[mt] = r < seg_row_end ? L - ql + r / G : -1;
+      m_run[mt] = -INFINITY;
+      l_part[mt] = 0.f;
+#pragma unroll
+      for (int e = 0; e < NB; ++e) acc[mt][e] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+    seg_whole = whole;
+  };
 
+  const float sl2 = a.scale_log2;
   auto process_tile = [&](int j, const uint4 (&kf)[KB], const vchunk (&vf)[4]) {
-    const int kp0 = kTileTokens * (t_beg + j) + 4 * grp;  // key position of S element 0
+    const int kp0 = kTileTokens * rd(tt, j) + 4 * grp;  // key position of S element 0
     f32x4 sv[MT];
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
@@ -181,8 +305,8 @@ __global__ __launch_bounds__(256) void decode_multi_kernel(MultiArgs a) {
       for (int kb = 0; kb < KB; ++kb) sacc = T::mfma_16x16x32(kf[kb], qf[mt][kb], sacc);
       sv[mt] = sacc;
     }
-    // V rows past kv_end were loaded as zeros, so a zero weight never meets
-    // a NaN sentinel; rows before it hold written values.
+    // V rows past the keys the pass sees were loaded as zeros, so a zero
+    // weight never meets a NaN sentinel; rows before hold written values.
 #pragma unroll
     for (int tau = 0; tau < 4; ++tau)
       *reinterpret_cast<vchunk *>(vt + (4 * grp + tau) * kVRow + sizeof(vchunk) * row16) = vf[tau];
@@ -224,123 +348,169 @@ __global__ __launch_bounds__(256) void decode_multi_kernel(MultiArgs a) {
     }
   };
 
-  // two register buffers: tile j + 1 is in flight while tile j is consumed
-  uint4 ka[KB], kb2[KB];
-  vchunk va[4], vb[4];
-  load_tile(0, ka, va);
-  for (int j = 0; j < ntiles; j += 2) {
-    load_tile(j + 1, kb2, vb);
-    process_tile(j, ka, va);
-    if (j + 1 < ntiles) {
-      load_tile(j + 2, ka, va);
-      process_tile(j + 1, kb2, vb);
-    }
-  }
-
-  // Rows of this lane's output fragments: 4 grp + r of each row tile.
-  const bool whole = rg.splits == 1;
+  // Segment end: final rows if the whole virtual sequence was streamed here,
+  // else partials in slot (group + v) * Hkv + g.
+  auto end_segment = [&](int v, bool last_tile) {
+    const bool whole = seg_whole && last_tile;
+    const int b = v / a.passes;
+    const int64_t slot = ((int64_t)grp_id + v) * hkv + g;
 #pragma unroll
-  for (int mt = 0; mt < MT; ++mt) {
-    float l_tot = l_part[mt] + __shfl_xor(l_part[mt], 16);
-    l_tot += __shfl_xor(l_tot, 32);  // the row16 row's sum over this split
-    float lh[4];
+    for (int mt = 0; mt < MT; ++mt) {
+      float l_tot = l_part[mt] + __shfl_xor(l_part[mt], 16);
+      l_tot += __shfl_xor(l_tot, 32);  // the row16 row's sum over this segment
+      float lh[4];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) lh[r] = __shfl(l_tot, 4 * grp + r);
+      for (int r = 0; r < 4; ++r) lh[r] = __shfl(l_tot, 4 * grp + r);
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int rr = rg.row0 + 16 * mt + 4 * grp + r;
-      if (rr >= rg.row_end) continue;
-      const float inv = lh[r] > 0.f ? 1.f / lh[r] : 0.f;
-      if (whole) {
-        const int i = rr / G, h = rr - (rr / G) * G;
-        st *out = static_cast<st *>(a.out) + (((int64_t)b * ql + i) * a.num_q_heads + (int64_t)g * G + h) * D;
+      for (int r = 0; r < 4; ++r) {
+        const int rr = seg_row0 + 16 * mt + 4 * grp + r;
+        if (rr >= seg_row_end) continue;
+        const float inv = lh[r] > 0.f ? 1.f / lh[r] : 0.f;
+        if (whole) {
+          const int i = rr / G, h = rr - (rr / G) * G;
+          st *out = static_cast<st *>(a.out) +
+                    (((int64_t)b * ql + i) * a.num_q_heads + (int64_t)g * G + h) * D;
 #pragma unroll
-        for (int e = 0; e < NB; ++e) out[16 * e + row16] = T::from_float(acc[mt][e][r] * inv);
-      } else {
-        float *po = a.ws_o + mq_slot(a, b, pass, s, g, rr - rg.row0) * D;
+          for (int e = 0; e < NB; ++e) out[16 * e + row16] = T::from_float(acc[mt][e][r] * inv);
+        } else {
+          float *po = a.ws_o + (slot * a.pass_rows + (rr - seg_row0)) * D;
 #pragma unroll
-        for (int e = 0; e < NB; ++e) po[16 * e + row16] = acc[mt][e][r] * inv;
+          for (int e = 0; e < NB; ++e) po[16 * e + row16] = acc[mt][e][r] * inv;
+        }
+      }
+      if (!whole && grp == 0) {
+        const int rr = seg_row0 + 16 * mt + row16;
+        if (rr < seg_row_end) {
+          a.ws_ml[(slot * a.pass_rows + (rr - seg_row0)) * 2] = m_run[mt];
+          a.ws_ml[(slot * a.pass_rows + (rr - seg_row0)) * 2 + 1] = l_tot;
+        }
       }
     }
-    if (!whole && grp == 0) {
-      const int rr = rg.row0 + 16 * mt + row16;
-      if (rr < rg.row_end) {
-        const int64_t slot = mq_slot(a, b, pass, s, g, rr - rg.row0);
-        a.ws_ml[slot * 2] = m_run[mt];
-        a.ws_ml[slot * 2 + 1] = l_tot;
+  };
+
+  auto step = [&](int j, const uint4 (&kc)[KB], const vchunk (&vc)[4]) {
+    const int v = rd(tv, j), flag = rd(tflag, j);
+    if ((flag & 1) || c0 + j == xbeg) begin_segment(j, v, (flag & 1) != 0);
+    process_tile(j, kc, vc);
+    if ((flag & 2) || c0 + j == xend - 1) end_segment(v, (flag & 2) != 0);
+  };
+
+  // S register buffers: tile j is consumed from buffer j % S while the next
+  // S - 1 tiles are in flight.  Loads are unconditional (empty past cnt) so
+  // every step sees the same loads in flight and the same wait counts.
+  constexpr int S = kMqStagesFor<D, MT>;
+  uint4 kbuf[S][KB];
+  vchunk vbuf[S][4];
+  for (int start = xbeg; start < xend; start += cnt) {
+    stage(start);  // sets cnt
+#pragma unroll
+    for (int u = 0; u < S - 1; ++u) load_tile(u, kbuf[u], vbuf[u]);
+    for (int j = 0; j < cnt; j += S) {
+#pragma unroll
+      for (int u = 0; u < S; ++u) {
+        load_tile(j + u + S - 1, kbuf[(u + S - 1) % S], vbuf[(u + S - 1) % S]);
+        if (j + u < cnt) step(j + u, kbuf[u], vbuf[u]);  // wave-uniform
       }
     }
   }
 }
 
-// Merge the splits of every (sequence, pass, KV head) that had more than
-// one: out = sum_s w_s o_s / sum_s w_s with w_s = l_s 2^(m_s - max m), in
-// split order.  One work-group per (sequence, pass, KV head).
+// Merge of the virtual sequences cut by range boundaries: out = sum_k w_k
+// o_k / sum_k w_k, w_k = l_k 2^(m_k - max m), over the groups k that
+// covered v, in group order; virtual sequences with no tile get zero rows.
+// A thread owns one row and four output dimensions.
 template <class T, int D>
 __global__ __launch_bounds__(256) void decode_multi_reduce_kernel(MultiArgs a) {
   typedef typename T::storage st;
-  const int per_seq = a.passes * a.num_kv_heads;
-  const int b = blockIdx.x / per_seq;
-  const int z = blockIdx.x - b * per_seq;
-  const int pass = z / a.num_kv_heads;
-  const int g = z - pass * a.num_kv_heads;
-  const MqRange rg = mq_range(a, b, pass);
-  if (rg.splits <= 1) return;  // written by the main kernel
-  const int nrows = rg.row_end - rg.row0;
-  const int G = a.group;
-  for (int e = threadIdx.x; e < nrows * D; e += blockDim.x) {
-    const int row = e / D, d = e - (e / D) * D;
+  constexpr int QPR = D / 4;      // threads per row
+  constexpr int RPB = 256 / QPR;  // rows per work-group
+  const int bpv = (a.pass_rows + RPB - 1) / RPB;  // work-groups per (v, head)
+  const int rb = blockIdx.x % bpv;
+  const int g = (blockIdx.x / bpv) % a.num_kv_heads;
+  const int v = blockIdx.x / (bpv * a.num_kv_heads);
+  const int nv = a.num_seqs * a.passes;
+  const int total = a.ws_sched[nv];
+  const int t0 = a.ws_sched[v], t1 = a.ws_sched[v + 1];
+  const int groups = mq_active_groups(a, total);
+  const int per = (total + groups - 1) / groups;
+  const int ga = t1 > t0 ? t0 / per : 0, gb = t1 > t0 ? (t1 - 1) / per : 0;
+  if (t1 > t0 && ga == gb) return;  // written by the main kernel
+  const int b = v / a.passes;
+  const int row0 = (v - b * a.passes) * a.pass_rows;
+  const int row_end = min(a.rows, row0 + a.pass_rows);
+  const int row = rb * RPB + (int)threadIdx.x / QPR;
+  const int q4 = (int)threadIdx.x % QPR;
+  if (row0 + row >= row_end) return;  // no barriers follow
+  float wsum = 0.f;
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  if (t1 > t0) {
     float m_max = -INFINITY;
-    for (int s = 0; s < rg.splits; ++s) m_max = fmaxf(m_max, a.ws_ml[mq_slot(a, b, pass, s, g, row) * 2]);
-    float wsum = 0.f, acc = 0.f;
-    for (int s = 0; s < rg.splits; ++s) {
-      const int64_t slot = mq_slot(a, b, pass, s, g, row);
-      const float l = a.ws_ml[slot * 2 + 1];
-      if (l > 0.f) {
-        const float w = l * fast_exp2(a.ws_ml[slot * 2] - m_max);
-        wsum += w;
-        acc += w * a.ws_o[slot * D + d];
-      }
+    for (int k = ga; k <= gb; ++k)
+      m_max = fmaxf(m_max, a.ws_ml[((((int64_t)k + v) * a.num_kv_heads + g) * a.pass_rows + row) * 2]);
+#pragma unroll 4
+    for (int k = ga; k <= gb; ++k) {
+      const int64_t r = (((int64_t)k + v) * a.num_kv_heads + g) * a.pass_rows + row;
+      const float m = a.ws_ml[r * 2], l = a.ws_ml[r * 2 + 1];
+      const float4 o = reinterpret_cast<const float4 *>(a.ws_o + r * D)[q4];
+      const float w = l > 0.f ? l * fast_exp2(m - m_max) : 0.f;
+      wsum += w;
+      acc.x += w * o.x;
+      acc.y += w * o.y;
+      acc.z += w * o.z;
+      acc.w += w * o.w;
     }
-    const int rr = rg.row0 + row;
-    const int i = rr / G, h = rr - (rr / G) * G;
-    st *out = static_cast<st *>(a.out) + (((int64_t)b * a.q_len + i) * a.num_q_heads + (int64_t)g * G + h) * D;
-    out[d] = T::from_float(wsum > 0.f ? acc / wsum : 0.f);
   }
+  const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
+  const int rr = row0 + row;
+  const int i = rr / a.group, h = rr - (rr / a.group) * a.group;
+  st *out = static_cast<st *>(a.out) +
+            (((int64_t)b * a.q_len + i) * a.num_q_heads + (int64_t)g * a.group + h) * D + 4 * q4;
+  out[0] = T::from_float(acc.x * inv);
+  out[1] = T::from_float(acc.y * inv);
+  out[2] = T::from_float(acc.z * inv);
+  out[3] = T::from_float(acc.w * inv);
 }
 
 template <class T, int D, int MT>
-hipError_t launch_mt(const MultiArgs &a, hipStream_t stream) {
-  const dim3 grid((unsigned)(a.num_seqs * a.max_splits), 1, (unsigned)(a.head_groups * a.passes));
-  hipLaunchKernelGGL((decode_multi_kernel<T, D, MT>), grid, dim3(256), 0, stream, a);
+hipError_t launch_mt(const MultiArgs &a, int grid, hipStream_t stream) {
+  hipLaunchKernelGGL((decode_multi_kernel<T, D, MT>), dim3(grid), dim3(kMqWaves * kWave), 0, stream, a);
   hipError_t err = hipGetLastError();
-  if (err != hipSuccess || a.max_splits == 1) return err;
+  if (err != hipSuccess) return err;
+  constexpr int rpb = 256 / (D / 4);
+  const int bpv = (a.pass_rows + rpb - 1) / rpb;
   hipLaunchKernelGGL((decode_multi_reduce_kernel<T, D>),
-                     dim3((unsigned)(a.num_seqs * a.passes * a.num_kv_heads)), dim3(256), 0, stream, a);
+                     dim3((unsigned)(a.num_seqs * a.passes * a.num_kv_heads * bpv)), dim3(256), 0, stream, a);
   return hipGetLastError();
 }
 
 template <class T, int D>
-hipError_t launch_d(const MultiArgs &a, int mt, hipStream_t stream) {
+hipError_t launch_d(const MultiArgs &a, int mt, int grid, hipStream_t stream) {
   switch (mt) {
-    case 1: return launch_mt<T, D, 1>(a, stream);
-    case 2: return launch_mt<T, D, 2>(a, stream);
-    case 3: return launch_mt<T, D, 3>(a, stream);
-    default: return launch_mt<T, D, 4>(a, stream);
+    case 1: return launch_mt<T, D, 1>(a, grid, stream);
+    case 2: return launch_mt<T, D, 2>(a, grid, stream);
+    case 3: return launch_mt<T, D, 3>(a, grid, stream);
+    default: return launch_mt<T, D, kMultiMaxRowTiles(D)>(a, grid, stream);
   }
-}
-
-template <class T>
-hipError_t launch_t(const MultiArgs &a, int head_dim, int mt, hipStream_t stream) {
-  return head_dim == 128 ? launch_d<T, 128>(a, mt, stream) : launch_d<T, 64>(a, mt, stream);
 }
 
 }  // namespace
 
-hipError_t launch_decode_multi(const MultiArgs &a, pa_dtype dtype, int head_dim, hipStream_t stream) {
+// One work-group (four waves, one per SIMD) per CU.
+int multi_grid() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) dev = 0;
+  int cus = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+    cus = 256;
+  return cus;
+}
+
+hipError_t launch_decode_multi(const MultiArgs &a, pa_dtype dtype, int head_dim, int grid,
+                               hipStream_t stream) {
   const int mt = a.pass_rows / 16;
-  if (dtype == PA_BF16) return launch_t<BF16>(a, head_dim, mt, stream);
-  return launch_t<F16>(a, head_dim, mt, stream);
+  if (dtype == PA_BF16)
+    return head_dim == 128 ? launch_d<BF16, 128>(a, mt, grid, stream) : launch_d<BF16, 64>(a, mt, grid, stream);
+  return head_dim == 128 ? launch_d<F16, 128>(a, mt, grid, stream) : launch_d<F16, 64>(a, mt, grid, stream);
 }
 
 }  // namespace pa

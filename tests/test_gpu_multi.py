@@ -1,7 +1,7 @@
 """GPU parity of multi-token paged decode (pa_decode_multi) against the
 oracle's ``decode_multi``: speculative verification (q_len 5), ragged and
-short contexts, every supported GQA width and head size, forced KV splits
-(the merge kernel), q_len = 1 against single-token decode, the 70B-shaped
+short contexts, every supported GQA width and head size, stream-K cuts
+(the merge kernel, through the shortest stream-K range), q_len = 1 against single-token decode, the 70B-shaped
 verification batch in full, chunked prefill on sampled rows, and a
 rejected-draft rollback followed by new writes.
 """
@@ -61,15 +61,17 @@ SHAPES = [
 ]
 
 
-@pytest.mark.parametrize("split", [None, 1, 3])
+@pytest.mark.parametrize("min_range", [None, 1, 64])
 @pytest.mark.parametrize("shape", SHAPES, ids=[f"s{i}" for i in range(len(SHAPES))])
-def test_multi_parity_shapes(shape, split):
+def test_multi_parity_shapes(shape, min_range):
+    """min_range sets the shortest stream-K range: 1 cuts sequences into
+    many merged pieces, 64 leaves most of them whole."""
     dtype, lens, q, hq, hkv, d, bs = shape
-    print(f"multi shape {shape} split={split}", flush=True)
+    print(f"multi shape {shape} min_range={min_range}", flush=True)
     case = workloads.make_multi_case("multi_shape", 7100 + len(lens) + q, dtype, lens, q, hq, hkv, d, bs)
     dc = DeviceCase(case)
     dc.write_all()
-    with env(PA_MULTI_SPLIT_TILES=split):
+    with env(PA_MULTI_MIN_RANGE=min_range):
         out = _run(dc, case)
     assert_parity(out, _ref(case), dtype)
     dc.close()
