@@ -31,6 +31,10 @@ Parity status of each function (what pins it is listed in the tests):
   rows keep their bytes).
 * ``BlockAllocatorModel``: pinned (lowest-free-id order, exhaustion, release
   at the last reference, stats).
+* ``batching`` (continuous-batching scheduler over the pool): pinned
+  (iterations worked by hand from the page's three steps, preemption and
+  resumption, refusals, invariants under random traffic).  Visiting order,
+  allocation order and token positions are readings.
 * closed forms in ``sizes``: pinned against the numbers the pages print.
 * ``fp8`` (E4M3 values, nearest-even encoding with saturation, per-head
   scaling) and ``quantize_for_cache``: pinned (codes worked by hand from the
@@ -48,6 +52,7 @@ Parity status of each function (what pins it is listed in the tests):
 """
 from . import fp8  # noqa: F401
 from . import prefix  # noqa: F401
+from . import batching  # noqa: F401
 from .paged_attention import (  # noqa: F401
     quantize_for_cache,
     to_f64,
