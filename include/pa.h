@@ -242,6 +242,69 @@ int pa_cow_block(pa_pool *pool, int32_t block_id, int32_t *out_block);
 int pa_copy_blocks(pa_pool *pool, const int32_t *src_blocks, const int32_t *dst_blocks,
                    int32_t num_pairs, void *stream);
 
+/* ------------------------------------------------- continuous batching --- */
+
+/* Host-side continuous-batching driver over a pool [P4, the scheduler of
+ * its continuous-batching section]: it decides every iteration which
+ * requests run and holds their block tables.  One pa_batcher_schedule call
+ * takes three steps in this order:
+ *   1. every decoding request stays; when the tokens it holds (prompt +
+ *      generated) need more blocks than its table has, it gets one block
+ *      (pa_alloc_block), and when none is free it sits this iteration out
+ *      ("preempted", keeping its blocks);
+ *   2. waiting requests are admitted first come, first served while the
+ *      batch is below max_batch and the pool's free blocks cover
+ *      ceil(prompt / block_size); the first that does not fit stays at the
+ *      head of the queue and admission stops;
+ *   3. requests that generated max_tokens tokens leave; their blocks lose
+ *      the batcher's reference (pa_decref_block).
+ * Decoding requests are visited in admission order.  The admission
+ * iteration is the prefill: it writes positions 0 .. prompt - 1.  Every
+ * later iteration of a request writes the K/V of its last generated token
+ * at position prompt + generated - 1 and attends over prompt + generated
+ * positions.  After running an iteration the caller calls pa_batcher_step
+ * once per scheduled request.  Host state under the batcher's mutex; other
+ * users of the same pool should not allocate while a schedule call runs. */
+typedef struct pa_batcher pa_batcher;
+
+typedef struct {
+  int32_t scheduled;      /* requests in this iteration's batch */
+  int32_t prefill;        /* of which admitted now */
+  int32_t preempted;      /* decoding requests left out for want of a block */
+  int32_t freed_requests; /* finished requests released at step 3 */
+  int32_t freed_blocks;   /* their blocks */
+  int32_t waiting;        /* queue length after the call */
+  int32_t active;         /* admitted requests after the call */
+} pa_batch_info;
+
+/* Create a driver over `pool` with at most max_batch requests per
+ * iteration and block tables of max_blocks_per_seq entries. */
+int pa_batcher_create(pa_pool *pool, int32_t max_batch, int32_t max_blocks_per_seq, pa_batcher **out);
+
+/* Free the driver and drop its references on every block it holds. */
+void pa_batcher_destroy(pa_batcher *batcher);
+
+/* Queue a request.  PA_ERR_INVAL: prompt_len < 1, max_tokens < 1, or
+ * prompt_len + max_tokens tokens need more than max_blocks_per_seq blocks;
+ * PA_ERR_STATE: the id is waiting or active already. */
+int pa_batcher_add(pa_batcher *batcher, uint64_t request_id, int32_t prompt_len, int32_t max_tokens);
+
+/* One scheduling call (the three steps above).  Outputs, host arrays of
+ * max_batch entries (block_tables: [max_batch][max_blocks_per_seq], rows
+ * padded with -1), filled for the info->scheduled requests in batch order
+ * (decoding requests in admission order, then the admitted ones): ids,
+ * the table, context_lens (positions attended after this iteration's
+ * writes), write_start / write_count (positions written now), prefill
+ * (1 for a request admitted now). */
+int pa_batcher_schedule(pa_batcher *batcher, uint64_t *ids, int32_t *block_tables, int32_t *context_lens,
+                        int32_t *write_start, int32_t *write_count, int32_t *prefill,
+                        pa_batch_info *info);
+
+/* Advance a scheduled request by one generated token; at max_tokens it is
+ * finished and the next schedule call releases it.  PA_ERR_INVAL for an id
+ * that is not active, PA_ERR_STATE for a finished request. */
+int pa_batcher_step(pa_batcher *batcher, uint64_t request_id);
+
 /* ------------------------------------------------------------- mapping --- */
 
 /* Ring slot of a logical position [P3 slot equation]:

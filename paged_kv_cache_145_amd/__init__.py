@@ -18,7 +18,7 @@ from ._lib import PaRing
 __all__ = [
     "PaError", "Pool", "Ring", "ring_slot", "compute_slot_mapping", "reshape_and_cache",
     "decode_workspace_bytes", "rope_table_bytes", "rope_table_init", "decode", "DTYPES",
-    "block_hashes", "copy_blocks", "decode_multi_workspace_bytes", "decode_multi",
+    "block_hashes", "copy_blocks", "decode_multi_workspace_bytes", "decode_multi", "Batcher",
 ]
 
 DTYPES = {"f32": _lib.PA_F32, "f16": _lib.PA_F16, "bf16": _lib.PA_BF16}
@@ -325,3 +325,54 @@ def decode_multi(pool: Pool, out, query, block_tables, context_lens, max_context
         _dev_ptr(block_tables, "block_tables"), int(block_tables.shape[1]),
         _dev_ptr(context_lens, "context_lens"), b, ql, hq, int(max_context_len), float(scale),
         ws_ptr, ws_bytes, _stream_ptr(stream)), "pa_decode_multi")
+
+
+class Batcher:
+    """Continuous-batching driver over a pool (host state in the library)."""
+
+    def __init__(self, pool: Pool, max_batch: int, max_blocks_per_seq: int):
+        self._lib = _lib.load()
+        self.pool = pool  # keeps the pool alive while the driver holds its blocks
+        self.max_batch, self.max_blocks_per_seq = int(max_batch), int(max_blocks_per_seq)
+        h = ctypes.c_void_p()
+        _check(self._lib.pa_batcher_create(pool.handle, self.max_batch, self.max_blocks_per_seq,
+                                           ctypes.byref(h)), "pa_batcher_create")
+        self._h = h
+        n, mb = self.max_batch, self.max_blocks_per_seq
+        self._ids = np.empty(n, dtype=np.uint64)
+        self._tables = np.empty((n, mb), dtype=np.int32)
+        self._ctx = np.empty(n, dtype=np.int32)
+        self._ws = np.empty(n, dtype=np.int32)
+        self._wc = np.empty(n, dtype=np.int32)
+        self._pre = np.empty(n, dtype=np.int32)
+
+    def close(self) -> None:
+        if self._h:
+            self._lib.pa_batcher_destroy(self._h)
+            self._h = ctypes.c_void_p()
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def add(self, request_id: int, prompt_len: int, max_tokens: int) -> None:
+        _check(self._lib.pa_batcher_add(self._h, int(request_id), int(prompt_len), int(max_tokens)),
+               "pa_batcher_add")
+
+    def schedule(self):
+        """One iteration's batch: dict of arrays (ids, tables, context_lens,
+        write_start, write_count, prefill) and the info counters."""
+        info = _lib.PaBatchInfo()
+        p = lambda a: a.ctypes.data_as(ctypes.c_void_p)
+        _check(self._lib.pa_batcher_schedule(self._h, p(self._ids), p(self._tables), p(self._ctx), p(self._ws),
+                                             p(self._wc), p(self._pre), ctypes.byref(info)), "pa_batcher_schedule")
+        n = info.scheduled
+        batch = {"ids": self._ids[:n].copy(), "tables": self._tables[:n].copy(),
+                 "context_lens": self._ctx[:n].copy(), "write_start": self._ws[:n].copy(),
+                 "write_count": self._wc[:n].copy(), "prefill": self._pre[:n].astype(bool)}
+        return batch, {f: getattr(info, f) for f, _ in _lib.PaBatchInfo._fields_}
+
+    def step(self, request_id: int) -> None:
+        _check(self._lib.pa_batcher_step(self._h, int(request_id)), "pa_batcher_step")

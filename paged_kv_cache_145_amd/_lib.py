@@ -35,6 +35,12 @@ PA_PREFIX_TAIL = 1
 PA_PREFIX_RESIDENT = 2
 
 
+class PaBatchInfo(ctypes.Structure):
+    _fields_ = [("scheduled", ctypes.c_int32), ("prefill", ctypes.c_int32), ("preempted", ctypes.c_int32),
+                ("freed_requests", ctypes.c_int32), ("freed_blocks", ctypes.c_int32),
+                ("waiting", ctypes.c_int32), ("active", ctypes.c_int32)]
+
+
 class PaRing(ctypes.Structure):
     _fields_ = [("sink", ctypes.c_int32), ("window", ctypes.c_int32),
                 ("rope_base", ctypes.c_float), ("rope_style", ctypes.c_int32),
@@ -66,6 +72,11 @@ SIGNATURES = {
     "pa_prefix_get_stats": (ctypes.c_int, [_p, ctypes.POINTER(PaPrefixStats)]),
     "pa_cow_block": (ctypes.c_int, [_p, _i32, ctypes.POINTER(_i32)]),
     "pa_copy_blocks": (ctypes.c_int, [_p, _p, _p, _i32, _p]),
+    "pa_batcher_create": (ctypes.c_int, [_p, _i32, _i32, ctypes.POINTER(_p)]),
+    "pa_batcher_destroy": (None, [_p]),
+    "pa_batcher_add": (ctypes.c_int, [_p, ctypes.c_uint64, _i32, _i32]),
+    "pa_batcher_schedule": (ctypes.c_int, [_p, _p, _p, _p, _p, _p, _p, ctypes.POINTER(PaBatchInfo)]),
+    "pa_batcher_step": (ctypes.c_int, [_p, ctypes.c_uint64]),
     "pa_ring_slot": (_i32, [_i64, _i32, _i32]),
     "pa_compute_slot_mapping": (ctypes.c_int, [_p, _p, _i32, _i32, _p, _p, _i32,
                                                ctypes.POINTER(PaRing), _p]),

@@ -20,7 +20,7 @@ LIB_NAME = "libpa_mi355x.so"
 LIB_PATH = os.path.join(PKG, LIB_NAME)
 
 HIP_SOURCES = ["decode_kernels.hip", "multi_kernels.hip", "write_kernels.hip", "api.hip"]
-CPP_SOURCES = ["pool.cpp", "prefix.cpp"]
+CPP_SOURCES = ["pool.cpp", "prefix.cpp", "batching.cpp"]
 ARCH = "gfx950"
 
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-Wall", f"-I{INCLUDE}", f"-I{CSRC}"]

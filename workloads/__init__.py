@@ -651,3 +651,40 @@ PREFIX_CONFIGS = {
     "prefix_unaligned_fp8": lambda: config_prefix_unaligned(kv_fp8=True),
     "prefix_unaligned_small": config_prefix_unaligned_small,
 }
+
+
+# ---------------------------------------------------------------------------
+# Continuous batching: a stream of requests and the K/V rows they write
+# ---------------------------------------------------------------------------
+
+def batching_requests(seed: int, count: int, block_size: int, max_blocks: int, prompt_lo: int = 50,
+                      prompt_hi: int = 500, gen_lo: int = 16, gen_hi: int = 256):
+    """``count`` requests (id, prompt_len, max_tokens, arrival iteration):
+    prompts U[prompt_lo, prompt_hi], generations U[gen_lo, gen_hi] (clipped to
+    the table's room), arrivals spread over the first iterations."""
+    rng = np.random.Generator(np.random.PCG64([seed, 40]))
+    reqs = []
+    room = max_blocks * block_size
+    for i in range(count):
+        p = int(rng.integers(prompt_lo, prompt_hi, endpoint=True))
+        g = int(min(rng.integers(gen_lo, gen_hi, endpoint=True), room - p))
+        reqs.append((i, p, max(1, g), int(rng.integers(0, max(1, count // 4)))))
+    return reqs
+
+
+def request_rows(seed: int, rid: int, positions, num_kv_heads: int, head_dim: int, dtype: str):
+    """K and V rows of request ``rid`` at ``positions`` (each row drawn from
+    its own (seed, request, position) stream, so any row can be redrawn)."""
+    pos = list(positions)
+    k = np.empty((len(pos), num_kv_heads, head_dim), dtype=RAW_DTYPES[dtype])
+    v = np.empty_like(k)
+    for j, p in enumerate(pos):
+        r = np.random.default_rng([seed, rid, int(p)])
+        k[j] = draw_values(r, (num_kv_heads, head_dim), dtype)
+        v[j] = draw_values(r, (num_kv_heads, head_dim), dtype)
+    return k, v
+
+
+def request_query(seed: int, rid: int, iteration: int, num_q_heads: int, head_dim: int, dtype: str):
+    r = np.random.default_rng([seed, rid, 1 << 30, iteration])
+    return draw_values(r, (num_q_heads, head_dim), dtype)
