@@ -520,6 +520,143 @@ def multi_cpu_baseline(case, max_rows: int = 64) -> dict:
                       f"{wall:.2f} s"}
 
 
+def batching_cpu_baseline(reqs, block_size, num_blocks, max_batch, max_blocks, iters: int) -> dict:
+    """The oracle's scheduler model driving the same request stream."""
+    from oracle.allocator import BlockAllocatorModel
+    from oracle.batching import ContinuousBatchingModel
+
+    m = ContinuousBatchingModel(BlockAllocatorModel(num_blocks), block_size, max_batch, max_blocks)
+    t0, c0 = time.perf_counter(), time.process_time()
+    for it in range(iters):
+        for rid, p, g, arrival in reqs:
+            if arrival == it:
+                m.add(rid, p, g)
+        batch, _ = m.schedule()
+        for s in batch:
+            m.step(s.rid)
+    wall = time.perf_counter() - t0
+    cores = max(1, round((time.process_time() - c0) / wall))
+    return {"value": round(wall / iters * 1e6, 1), "unit": "us per scheduling iteration", "cores": cores,
+            "kind": "oracle", "sample": f"the oracle's scheduler model over the first {iters} iterations of the "
+                                        f"same request stream (host bookkeeping only, no attention)"}
+
+
+def measure_batching(args) -> int:
+    """Continuous batching driven by the library's batcher over the 70B-head
+    pool: every iteration schedules (host C++), writes the new K/V rows and
+    decodes the decoding requests.  One JSON line; ``roofline`` is the
+    decode calls' (their algorithmic bytes over their event time)."""
+    import torch
+
+    import paged_kv_cache_145_amd as pk
+    import workloads
+
+    dev = "cuda:0"
+    torch.cuda.set_device(0)
+    bs, hkv, hq, d, nb, max_batch = 16, 8, 64, 128, 6841, 64
+    max_blocks = -(-(2000 + 256) // bs)
+    reqs = workloads.batching_requests(145050, 384, bs, max_blocks, prompt_lo=50, prompt_hi=2000,
+                                       gen_lo=16, gen_hi=256)
+    tdt = torch.bfloat16
+    k = torch.zeros((nb, bs, hkv, d), dtype=tdt, device=dev)
+    v = torch.zeros_like(k)
+    pool = pk.Pool(k, v, bs)
+    batcher = pk.Batcher(pool, max_batch, max_blocks)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(145050)
+    rows_cap = max_batch * 2000
+    rows_k = torch.randn((rows_cap, hkv, d), generator=gen, device=dev).to(tdt)
+    rows_v = torch.randn((rows_cap, hkv, d), generator=gen, device=dev).to(tdt)
+    query = torch.randn((max_batch, hq, d), generator=gen, device=dev).to(tdt)
+    out = torch.empty((max_batch, hq, d), dtype=tdt, device=dev)
+    ws = torch.empty(max(pk.decode_workspace_bytes(pool, max_batch, hq, max_blocks * bs), 1), dtype=torch.uint8,
+                     device=dev)
+    scale = 1.0 / np.sqrt(d)
+    row_bytes = hkv * d * 2 * 2
+    total_iters = args.warmup + args.steps
+    host_s, it_s, sched_us = [], [], []
+    dec_ev, dec_bytes, dec_tokens = [], [], []
+    stats = {"prefill": 0, "preempted": 0, "freed_requests": 0, "written_rows": 0}
+    print(f"bench: continuous batching, {total_iters} iterations", file=sys.stderr, flush=True)
+    for it in range(total_iters):
+        t0 = time.perf_counter()
+        for rid, p, g, arrival in reqs:
+            if arrival == it:
+                batcher.add(rid, p, g)
+        ts = time.perf_counter()
+        batch, info = batcher.schedule()
+        sched_s = time.perf_counter() - ts
+        n = info["scheduled"]
+        if n == 0:
+            continue
+        ws_, wc = batch["write_start"], batch["write_count"]
+        sid = np.repeat(np.arange(n, dtype=np.int32), wc)
+        pos = np.concatenate([np.arange(a, a + c, dtype=np.int64) for a, c in zip(ws_, wc)])
+        slots = pk.compute_slot_mapping(pool, batch["tables"], sid, pos)
+        dec = np.flatnonzero(~batch["prefill"])
+        tables = torch.from_numpy(np.ascontiguousarray(batch["tables"][dec])).to(dev, non_blocking=False)
+        lens_np = np.ascontiguousarray(batch["context_lens"][dec])
+        lens = torch.from_numpy(lens_np).to(dev)
+        slots_d = torch.from_numpy(slots).to(dev)
+        t1 = time.perf_counter()
+        m = slots.shape[0]
+        pk.reshape_and_cache(pool, rows_k[:m], rows_v[:m], slots_d)
+        if dec.size:
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            pk.decode(pool, out[: dec.size], query[: dec.size], tables, lens, int(lens_np.max()), scale, workspace=ws)
+            e1.record()
+        for rid in batch["ids"]:
+            batcher.step(int(rid))
+        torch.cuda.synchronize()
+        t2 = time.perf_counter()
+        if it >= args.warmup:
+            sched_us.append(sched_s * 1e6)
+            host_s.append(t1 - t0)
+            it_s.append(t2 - t0)
+            if dec.size:
+                dec_ev.append(e0.elapsed_time(e1) * 1e-3)
+                dec_bytes.append(int(lens_np.sum()) * row_bytes + dec.size * hq * d * 2 * 2)
+                dec_tokens.append(int(dec.size))
+            for key in ("prefill", "preempted", "freed_requests"):
+                stats[key] += info[key]
+            stats["written_rows"] += m
+    batcher.close()
+    pool.close()
+    wall = sum(it_s)
+    achieved = sum(dec_bytes) / sum(dec_ev) / 1e9 if dec_ev else 0.0
+    result = {
+        "metric": "continuous batching: decoded tokens per second (host scheduling, cache writes and decode)",
+        "value": round(sum(dec_tokens) / wall, 1) if wall else 0.0,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": len(it_s),
+        "warmup": args.warmup,
+        "ms_per_step": round(wall / max(1, len(it_s)) * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": (f"continuous batching over a {nb}-block pool (Hq {hq}, Hkv {hkv}, D {d}, bf16, "
+                                f"block {bs}), batch <= {max_batch}, 384 requests: prompts U[50,2000], "
+                                f"generations U[16,256], arrivals over the first 96 iterations"),
+                   "global_batch": max_batch, "seed": 145050},
+        "iteration_ms": {"mean": round(statistics.mean(it_s) * 1e3, 4), "host_mean": round(statistics.mean(host_s) * 1e3, 4),
+                         "schedule_call_us": round(statistics.mean(sched_us), 2)},
+        "decode_us_mean": round(statistics.mean(dec_ev) * 1e6, 2) if dec_ev else None,
+        "decode_batch_mean": round(statistics.mean(dec_tokens), 1) if dec_tokens else 0,
+        "scheduler": stats,
+        "roofline": {"bound": "hbm", "kernel": "pa_decode calls of the loop (HIP events)", "achieved": round(achieved, 1),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": None, "algorithmic_bytes_per_call": int(statistics.mean(dec_bytes)) if dec_bytes else 0},
+        "cpu_baseline": None if args.no_cpu_baseline else batching_cpu_baseline(reqs, bs, nb, max_batch, max_blocks,
+                                                                                 min(total_iters, 200)),
+    }
+    print(json.dumps(result), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[1])
     ap.add_argument("--gpus", type=int, default=1)
@@ -540,10 +677,11 @@ def main() -> int:
                     help="only run this many decode calls, then a 1 GiB copy (for rocprofv3 counter runs)")
     ap.add_argument("--write-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="turn two rocprofv3 counter_collection.csv files into the traffic record")
-    ap.add_argument("--measure", choices=("decode", "prefix", "multi"), default="decode",
+    ap.add_argument("--measure", choices=("decode", "prefix", "multi", "batching"), default="decode",
                     help="decode (default): the hot-path step; prefix: prefix reuse with copy-on-write "
                          "(admission, tail copies, shared-prefix decode, bulk block copy); multi: "
-                         "multi-token decode on --config spec_verify_llama70b (default) or chunked_prefill")
+                         "multi-token decode on --config spec_verify_llama70b (default) or chunked_prefill; "
+                         "batching: the continuous-batching driver looping over schedule, writes and decode")
     ap.add_argument("--traffic-command", default="",
                     help="the profiling command line recorded with --write-traffic")
     args = ap.parse_args()
@@ -575,6 +713,8 @@ def main() -> int:
         return measure_prefix(args)
     if args.measure == "multi":
         return measure_multi(args)
+    if args.measure == "batching":
+        return measure_batching(args)
     if args.config in workloads.MULTI_CONFIGS:
         print("multi-token workloads run with --measure multi", file=sys.stderr)
         return 2
