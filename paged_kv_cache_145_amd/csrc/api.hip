@@ -75,23 +75,33 @@ WorkspaceLayout workspace_layout(const pa_pool *pool, int32_t num_seqs, int32_t 
 }
 
 struct MultiLayout {
-  int mt, pass_rows, passes, seqs_per_launch, groups;
+  int mt, pass_rows, passes, pass_group, pgroups, seqs_per_launch, grid, groups;
   size_t sched_bytes, ml_bytes, o_bytes, total;
 };
 
-// Sizes of one launch slice (at most kMaxMultiSeqsHost (sequence, pass)
-// pairs); slices run one after another and reuse the workspace.
+// Sizes of one launch slice (at most kMaxMultiSeqsHost (sequence, pass
+// group) pairs); slices run one after another and reuse the workspace.
 MultiLayout multi_layout(const pa_pool *pool, int32_t num_seqs, int32_t q_len, int32_t num_q_heads) {
   MultiLayout m{};
-  const int group = num_q_heads / pool->num_kv_heads;
+  const int hkv = pool->num_kv_heads;
+  const int group = num_q_heads / hkv;
   const int64_t rows = (int64_t)q_len * group;
-  m.mt = (int)std::min<int64_t>(kMultiMaxRowTiles(pool->head_dim), ceil_div(rows, 16));
+  const int max_mt = kMultiMaxRowTiles(pool->head_dim);
+  const int forced_mt = env_int("PA_MULTI_ROW_TILES", 0);
+  m.mt = (int)std::min<int64_t>(forced_mt >= 1 && forced_mt <= max_mt ? forced_mt : max_mt, ceil_div(rows, 16));
   m.pass_rows = 16 * m.mt;
   m.passes = (int)ceil_div(rows, m.pass_rows);
-  m.seqs_per_launch = std::max(1, std::min(num_seqs, kMaxMultiSeqsHost / std::max(1, m.passes)));
-  m.groups = std::max(1, (multi_grid() * 4) / pool->num_kv_heads);
-  const size_t nv = (size_t)m.seqs_per_launch * m.passes;
-  const size_t rows_total = (m.groups + nv) * pool->num_kv_heads * m.pass_rows;
+  // passes of one head share K/V tiles through L2 when a work-group takes several
+  const int forced = env_int("PA_MULTI_PASS_GROUP", 0);
+  m.pass_group = (forced == 1 || forced == 2 || forced == 4) ? forced
+                 : m.passes >= 4 ? 4 : m.passes >= 2 ? 2 : 1;
+  m.pgroups = (int)ceil_div(m.passes, m.pass_group);
+  m.seqs_per_launch = std::max(1, std::min(num_seqs, kMaxMultiSeqsHost / std::max(1, m.pgroups)));
+  const int waves_per_group = hkv * m.pass_group;
+  m.grid = std::max(multi_grid(), (int)ceil_div(waves_per_group, 4));  // at least one group
+  m.groups = (m.grid * 4) / waves_per_group;
+  const size_t nv = (size_t)m.seqs_per_launch * m.pgroups;
+  const size_t rows_total = (m.groups + nv) * (size_t)waves_per_group * m.pass_rows;
   m.sched_bytes = round_up((nv + 1) * sizeof(int32_t), 256);
   m.ml_bytes = round_up(rows_total * 2 * sizeof(float), 256);
   m.o_bytes = round_up(rows_total * pool->head_dim * sizeof(float), 256);
@@ -223,6 +233,8 @@ int pa_decode_multi(pa_pool *pool, void *out, const void *query, const int32_t *
   a.rows = q_len * group;
   a.pass_rows = m.pass_rows;
   a.passes = m.passes;
+  a.pass_group = m.pass_group;
+  a.pgroups = m.pgroups;
   a.groups = m.groups;
   const int forced_range = pa::env_int("PA_MULTI_MIN_RANGE", 0);
   a.min_range_tiles = forced_range >= 1 ? forced_range : 4;
@@ -230,7 +242,7 @@ int pa_decode_multi(pa_pool *pool, void *out, const void *query, const int32_t *
   a.scale_log2 = scale * pa::kLog2eHost;
   const int64_t row_elems = (int64_t)q_len * num_q_heads * pool->head_dim;
   const int esize = pa::dtype_bytes(pool->dtype);
-  const int grid = pa::multi_grid();
+  const int grid = m.grid;
   for (int32_t s0 = 0; s0 < num_seqs; s0 += m.seqs_per_launch) {
     a.num_seqs = std::min(m.seqs_per_launch, num_seqs - s0);
     a.out = static_cast<char *>(out) + s0 * row_elems * esize;

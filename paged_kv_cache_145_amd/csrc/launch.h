@@ -56,7 +56,7 @@ struct DecodeArgs {
 };
 
 // Multi-token decode (several new tokens per sequence, causal).
-constexpr int kMaxMultiSeqsHost = 1024;  // (sequence, pass) pairs per launch slice
+constexpr int kMaxMultiSeqsHost = 1024;  // (sequence, pass group) pairs per launch slice
 struct MultiArgs {
   void *out;          // [B, q_len, Hq, D]
   const void *query;  // [B, q_len, Hq, D]
@@ -64,8 +64,9 @@ struct MultiArgs {
   const void *v_cache;
   const int32_t *block_tables;
   const int32_t *context_lens;
-  // stream-K partials: slots [(groups + B * passes) * Hkv][pass_rows][D]
-  // and [..][pass_rows][2]; tile prefix per (sequence, pass) [B * passes + 1]
+  // stream-K partials: slots [(groups + B * pgroups) * Hkv * pass_group]
+  // [pass_rows][D] and [..][pass_rows][2]; tile prefix per (sequence, pass
+  // group) [B * pgroups + 1]
   float *ws_o;
   float *ws_ml;
   int32_t *ws_sched;
@@ -81,7 +82,9 @@ struct MultiArgs {
   int32_t rows;       // q_len * group query rows per KV head
   int32_t pass_rows;  // 16 * (row tiles per wave)
   int32_t passes;     // ceil(rows / pass_rows)
-  int32_t groups;     // wave groups of the persistent grid
+  int32_t pass_group; // passes one work-group's waves take together (1, 2 or 4)
+  int32_t pgroups;    // ceil(passes / pass_group)
+  int32_t groups;     // wave groups (Hkv * pass_group waves each) of the grid
   int32_t min_range_tiles;
   int32_t block_shift;
   float scale_log2;

@@ -12,15 +12,19 @@
 // wave holds MT row tiles (16 * MT rows, a "pass") and longer row sets take
 // several passes.
 //
-// Work split (stream-K, as in the single-token kernel).  A virtual sequence
-// is a (sequence, pass) pair; its tiles are the 16-token tiles up to the
-// last key its rows see.  The flattened list of (virtual sequence, tile)
-// is cut into equal ranges, one per group of Hkv waves; wave g of a group
-// streams KV head g over the range, so all waves carry the same number of
-// tiles and the heads of a token row are read side by side.  A virtual
-// sequence that starts and ends inside one range writes its output rows
-// directly; one cut by range boundaries leaves normalised partials in slots
-// (group + v) * Hkv + g, merged by decode_multi_reduce_kernel.
+// Work split (stream-K, as in the single-token kernel).  Passes are taken
+// PG at a time (PG = 1, 2 or 4): a virtual sequence is a (sequence, pass
+// group) pair; its tiles are the 16-token tiles up to the last key its rows
+// see.  The flattened list of (virtual sequence, tile) is cut into equal
+// ranges, one per group of Hkv * PG waves; wave (g, w) of a group streams
+// KV head g over the range for pass w of each pass group.  With PG = 1 the
+// four waves of a work-group are four heads, so a token row's heads are
+// read side by side; with PG = 4 they are four passes of one head over the
+// same tiles, so the K/V a pass re-reads comes from the CU's L2 instead of
+// HBM.  A virtual sequence that starts and ends inside one range writes its
+// output rows directly; one cut by range boundaries leaves normalised
+// partials in slots ((group + v) * Hkv + g) * PG + w, merged by
+// decode_multi_reduce_kernel.
 //
 // Per 16-token tile:
 //   S[token][row] = K_tile . Q^T with v_mfma_f32_16x16x32 (A = the lane's
@@ -90,19 +94,20 @@ __device__ __forceinline__ int mq_active_groups(const MultiArgs &a, int total) {
 }
 
 // Tile schedule of the launch: s_tfirst[v] = tiles of virtual sequences
-// before v, s_kvend[v] = key positions v's rows see.  Work-group 0 also
+// before v, s_kvend[v] = key positions the rows of v's pass group see.  Work-group 0 also
 // publishes s_tfirst to the workspace for the merge kernel.
 __device__ int mq_schedule(const MultiArgs &a, int *s_tfirst, int *s_kvend, int *s_wsum) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int nv = a.num_seqs * a.passes;
+  const int nv = a.num_seqs * a.pgroups;
   int carry = 0;
   for (int base = 0; base < nv; base += kMqWaves * kWave) {
     const int v = base + tid;
     int n = 0;
     if (v < nv) {
-      const int b = v / a.passes;
-      int row0, row_end, kv_end;
-      mq_pass(a, mq_len(a, b), v - b * a.passes, row0, row_end, kv_end);
+      const int b = v / a.pgroups;
+      const int last = min(a.passes - 1, (v - b * a.pgroups) * a.pass_group + a.pass_group - 1);
+      int row0, row_end, kv_end;  // the group's last pass sees the most keys
+      mq_pass(a, mq_len(a, b), last, row0, row_end, kv_end);
       s_kvend[v] = kv_end;
       n = (kv_end + kTileTokens - 1) / kTileTokens;
     }
@@ -147,17 +152,19 @@ void decode_multi_kernel(MultiArgs a) {
   __shared__ __align__(16) char s_vt[kMqWaves][MqLds<D>::kVBytes];
   __shared__ uint4 s_q[kMqWaves][kMqQSlots * QF * kWave];  // query fragments, lane-major
 
-  const int nv = a.num_seqs * a.passes;
+  const int nv = a.num_seqs * a.pgroups;
   const int total = mq_schedule(a, s_tfirst, s_kvend, s_wsum);
-  const int hkv = a.num_kv_heads, G = a.group, ql = a.q_len;
+  const int hkv = a.num_kv_heads, G = a.group, ql = a.q_len, PG = a.pass_group;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int row16 = lane & 15, grp = lane >> 4;
   const int groups = mq_active_groups(a, total);
   const int gw = blockIdx.x * kMqWaves + wave;
-  const int grp_id = gw / hkv;      // tile range of this wave
-  const int g = gw - grp_id * hkv;  // KV head of this wave
-  if (grp_id >= groups) return;     // no barriers follow
+  const int grp_id = gw / (hkv * PG);  // tile range of this wave
+  const int within = gw - grp_id * hkv * PG;
+  const int g = within / PG;           // KV head of this wave
+  const int w = within - g * PG;       // pass of each pass group
+  if (grp_id >= groups) return;        // no barriers follow
   const int per = (total + groups - 1) / groups;
   const int xbeg = grp_id * per;
   const int xend = min(total, xbeg + per);
@@ -202,7 +209,7 @@ void decode_multi_kernel(MultiArgs a) {
       tv = lo;
       tt = y - s_tfirst[lo];
       const int tiles = s_tfirst[lo + 1] - s_tfirst[lo];
-      const int b = lo / a.passes;
+      const int b = lo / a.pgroups;
       blk = a.block_tables[(int64_t)b * a.max_blocks_per_seq + ((kTileTokens * tt) >> a.block_shift)];
       blk = min(max(blk, 0), a.num_blocks - 1);
       tvalid = min(kTileTokens, s_kvend[lo] - kTileTokens * tt);
@@ -225,8 +232,8 @@ void decode_multi_kernel(MultiArgs a) {
     for (int s2 = 0; s2 < kMqQSlots; ++s2) {
       const int i = mm ? __ffsll((long long)mm) - 1 : 0;
       const int v = rd(tv, i);
-      const int b = v / a.passes;
-      const int p = v - b * a.passes;
+      const int b = v / a.pgroups;
+      const int p = (v - b * a.pgroups) * PG + w;  // this wave's pass (none if >= passes)
       const int row_end = min(a.rows, (p + 1) * a.pass_rows);
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
@@ -278,10 +285,10 @@ void decode_multi_kernel(MultiArgs a) {
     for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb) qf[mt][kb] = qs[(slot * QF + mt * KB + kb) * kWave + lane];
-    const int b = v / a.passes;
+    const int b = v / a.pgroups;
     const int L = mq_len(a, b);
     int kv_end;
-    mq_pass(a, L, v - b * a.passes, seg_row0, seg_row_end, kv_end);
+    mq_pass(a, L, (v - b * a.pgroups) * PG + w, seg_row0, seg_row_end, kv_end);  // no rows past the last pass
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
       const int r = seg_row0 + 16 * mt + row16;
@@ -349,11 +356,11 @@ void decode_multi_kernel(MultiArgs a) {
   };
 
   // Segment end: final rows if the whole virtual sequence was streamed here,
-  // else partials in slot (group + v) * Hkv + g.
+  // else partials in slot ((group + v) * Hkv + g) * PG + w.
   auto end_segment = [&](int v, bool last_tile) {
     const bool whole = seg_whole && last_tile;
-    const int b = v / a.passes;
-    const int64_t slot = ((int64_t)grp_id + v) * hkv + g;
+    const int b = v / a.pgroups;
+    const int64_t slot = (((int64_t)grp_id + v) * hkv + g) * PG + w;
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
       float l_tot = l_part[mt] + __shfl_xor(l_part[mt], 16);
@@ -415,28 +422,32 @@ void decode_multi_kernel(MultiArgs a) {
   }
 }
 
-// Merge of the virtual sequences cut by range boundaries: out = sum_k w_k
-// o_k / sum_k w_k, w_k = l_k 2^(m_k - max m), over the groups k that
-// covered v, in group order; virtual sequences with no tile get zero rows.
-// A thread owns one row and four output dimensions.
+// Merge of the passes whose virtual sequence was cut by range boundaries:
+// out = sum_k w_k o_k / sum_k w_k, w_k = l_k 2^(m_k - max m), over the
+// groups k that covered it, in group order; virtual sequences with no tile
+// get zero rows.  A thread owns one row and four output dimensions.
 template <class T, int D>
 __global__ __launch_bounds__(256) void decode_multi_reduce_kernel(MultiArgs a) {
   typedef typename T::storage st;
   constexpr int QPR = D / 4;      // threads per row
   constexpr int RPB = 256 / QPR;  // rows per work-group
-  const int bpv = (a.pass_rows + RPB - 1) / RPB;  // work-groups per (v, head)
+  const int bpv = (a.pass_rows + RPB - 1) / RPB;  // work-groups per (sequence, pass, head)
   const int rb = blockIdx.x % bpv;
   const int g = (blockIdx.x / bpv) % a.num_kv_heads;
-  const int v = blockIdx.x / (bpv * a.num_kv_heads);
-  const int nv = a.num_seqs * a.passes;
+  const int bp = blockIdx.x / (bpv * a.num_kv_heads);  // b * passes + pass
+  const int b = bp / a.passes;
+  const int pass = bp - b * a.passes;
+  const int PG = a.pass_group;
+  const int v = b * a.pgroups + pass / PG;
+  const int w = pass - (pass / PG) * PG;
+  const int nv = a.num_seqs * a.pgroups;
   const int total = a.ws_sched[nv];
   const int t0 = a.ws_sched[v], t1 = a.ws_sched[v + 1];
   const int groups = mq_active_groups(a, total);
   const int per = (total + groups - 1) / groups;
   const int ga = t1 > t0 ? t0 / per : 0, gb = t1 > t0 ? (t1 - 1) / per : 0;
   if (t1 > t0 && ga == gb) return;  // written by the main kernel
-  const int b = v / a.passes;
-  const int row0 = (v - b * a.passes) * a.pass_rows;
+  const int row0 = pass * a.pass_rows;
   const int row_end = min(a.rows, row0 + a.pass_rows);
   const int row = rb * RPB + (int)threadIdx.x / QPR;
   const int q4 = (int)threadIdx.x % QPR;
@@ -446,10 +457,11 @@ __global__ __launch_bounds__(256) void decode_multi_reduce_kernel(MultiArgs a) {
   if (t1 > t0) {
     float m_max = -INFINITY;
     for (int k = ga; k <= gb; ++k)
-      m_max = fmaxf(m_max, a.ws_ml[((((int64_t)k + v) * a.num_kv_heads + g) * a.pass_rows + row) * 2]);
+      m_max = fmaxf(m_max,
+                    a.ws_ml[(((((int64_t)k + v) * a.num_kv_heads + g) * PG + w) * a.pass_rows + row) * 2]);
 #pragma unroll 4
     for (int k = ga; k <= gb; ++k) {
-      const int64_t r = (((int64_t)k + v) * a.num_kv_heads + g) * a.pass_rows + row;
+      const int64_t r = ((((int64_t)k + v) * a.num_kv_heads + g) * PG + w) * a.pass_rows + row;
       const float m = a.ws_ml[r * 2], l = a.ws_ml[r * 2 + 1];
       const float4 o = reinterpret_cast<const float4 *>(a.ws_o + r * D)[q4];
       const float w = l > 0.f ? l * fast_exp2(m - m_max) : 0.f;

@@ -77,6 +77,22 @@ def test_multi_parity_shapes(shape, min_range):
     dc.close()
 
 
+@pytest.mark.parametrize("pass_group", [1, 2, 4])
+@pytest.mark.parametrize("shape", SHAPES[:5], ids=[f"s{i}" for i in range(5)])
+def test_multi_parity_pass_groups(shape, pass_group):
+    """Several passes of one head per work-group (sharing K/V tiles through
+    L2), including pass groups with fewer real passes than waves."""
+    dtype, lens, q, hq, hkv, d, bs = shape
+    print(f"multi shape {shape} pass_group={pass_group}", flush=True)
+    case = workloads.make_multi_case("multi_shape", 7100 + len(lens) + q, dtype, lens, q, hq, hkv, d, bs)
+    dc = DeviceCase(case)
+    dc.write_all()
+    with env(PA_MULTI_PASS_GROUP=pass_group, PA_MULTI_MIN_RANGE=1):
+        out = _run(dc, case)
+    assert_parity(out, _ref(case), dtype)
+    dc.close()
+
+
 def test_q_len_one_matches_single_token_decode():
     case = workloads.make_multi_case("multi_q1", 7200, "bf16", [1, 50, 333, 4000], 1, 64, 8, 128, 16)
     dc = DeviceCase(case)
