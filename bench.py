@@ -397,8 +397,9 @@ def multi_costs(case) -> dict:
     row the longest query row of each sequence sees, once; the queries and
     outputs; table entries.  Flops: 4 * D per (query row, visible key)."""
     s = {"f32": 4, "f16": 2, "bf16": 2}[case.dtype]
+    s_kv = 1 if case.kv_dtype == "fp8_e4m3" else s
     lens = case.context_lens.astype(np.int64)
-    row = case.num_kv_heads * case.head_dim * 2 * s
+    row = case.num_kv_heads * case.head_dim * 2 * s_kv
     kv = int(lens.sum()) * row
     qo = case.num_seqs * case.q_len * case.num_q_heads * case.head_dim * 2 * s
     tables = int(sum(-(-int(n) // case.block_size) for n in lens)) * 4 + case.num_seqs * 4
@@ -426,9 +427,14 @@ def measure_multi(args) -> int:
     def to_dev(raw):
         return torch.from_numpy(np.ascontiguousarray(raw).view(raw_view)).view(tdt).to(dev)
 
-    k, v = _nan_pools(workloads, torch, (case.num_blocks, case.block_size, case.num_kv_heads, case.head_dim),
-                      case.dtype, dev)
-    pool = pk.Pool(k, v, case.block_size)
+    shape = (case.num_blocks, case.block_size, case.num_kv_heads, case.head_dim)
+    if case.kv_dtype == "fp8_e4m3":
+        k = torch.full(shape, workloads.FP8_NAN_CODE, dtype=torch.uint8, device=dev)
+        v = torch.full(shape, workloads.FP8_NAN_CODE, dtype=torch.uint8, device=dev)
+        pool = pk.Pool(k, v, case.block_size, act_dtype=tdt, k_scale=case.k_scale, v_scale=case.v_scale)
+    else:
+        k, v = _nan_pools(workloads, torch, shape, case.dtype, dev)
+        pool = pk.Pool(k, v, case.block_size)
     for ch in case.writes:
         sid = np.full(ch.positions.shape, ch.seq, dtype=np.int32)
         slots = pk.compute_slot_mapping(pool, case.block_tables, sid, ch.positions)
@@ -478,7 +484,8 @@ def measure_multi(args) -> int:
         "dtype": case.dtype,
         "data": "synthetic",
         "config": {"workload": (f"{name}: B {case.num_seqs}, q_len {case.q_len}, Hq {case.num_q_heads}, "
-                                f"Hkv {case.num_kv_heads}, D {case.head_dim}, {case.dtype}, block {case.block_size}, "
+                                f"Hkv {case.num_kv_heads}, D {case.head_dim}, "
+                                f"{'E4M3 KV, ' if case.kv_dtype else ''}{case.dtype}, block {case.block_size}, "
                                 f"{c['tokens']} cached tokens (the new ones included)"),
                    "global_batch": case.num_seqs, "q_len": case.q_len, "seed": case.seed},
         "call_us": {"mean": round(mean_us, 2), "median": round(med_us, 2)},

@@ -397,15 +397,17 @@ size_t pa_decode_multi_workspace_bytes(const pa_pool *pool, int32_t num_seqs, in
  * (KV head h / G):
  *   out[b,i,h,:] = sum_{t<=p} softmax_t(scale * <q[b,i,h,:], K_t>) * V_t
  *   out, query:   device [num_seqs, q_len, num_q_heads, head_dim], pool dtype
- *                 (16-bit pools only), rounded to nearest-even from fp32.
+ *                 (an 8-bit pool's act_dtype), rounded to nearest-even from
+ *                 fp32.
  *   block_tables, context_lens, max_context_len, workspace: as pa_decode
  *                 (workspace >= pa_decode_multi_workspace_bytes).
  *   q_len:        1 .. 4096; q_len * G <= 49152 (D = 128) or 65536 (D = 64),
  *                 else PA_ERR_UNSUPPORTED.
  * q_len = 1 is single-token decode by another kernel (same result within
  * rounding).  Rejecting draft tokens needs no call: lowering context_lens
- * hides their rows, and the next write overwrites them.  PA_ERR_UNSUPPORTED
- * for fp32 and 8-bit pools. */
+ * hides their rows, and the next write overwrites them.  8-bit pools are
+ * dequantised in registers (k_scale on scores, v_scale on outputs).
+ * PA_ERR_UNSUPPORTED for fp32 pools. */
 int pa_decode_multi(pa_pool *pool, void *out, const void *query, const int32_t *block_tables,
                     int32_t max_blocks_per_seq, const int32_t *context_lens, int32_t num_seqs,
                     int32_t q_len, int32_t num_q_heads, int32_t max_context_len, float scale,

@@ -202,7 +202,7 @@ int pa_decode_multi(pa_pool *pool, void *out, const void *query, const int32_t *
   if (pa::ceil_div((int64_t)q_len * group, 16 * pa::kMultiMaxRowTiles(pool->head_dim)) >
       pa::kMaxMultiSeqsHost)
     return PA_ERR_UNSUPPORTED;
-  if (pool->kv_fp8 || (pool->dtype != PA_F16 && pool->dtype != PA_BF16)) return PA_ERR_UNSUPPORTED;
+  if (pool->dtype != PA_F16 && pool->dtype != PA_BF16) return PA_ERR_UNSUPPORTED;
   if (num_seqs == 0) return PA_OK;
   if (out == nullptr || query == nullptr || block_tables == nullptr || context_lens == nullptr)
     return PA_ERR_INVAL;
@@ -240,6 +240,11 @@ int pa_decode_multi(pa_pool *pool, void *out, const void *query, const int32_t *
   a.min_range_tiles = forced_range >= 1 ? forced_range : 4;
   a.block_shift = pa::log2_exact(pool->block_size);
   a.scale_log2 = scale * pa::kLog2eHost;
+  if (pool->kv_fp8)
+    for (int h = 0; h < pool->num_kv_heads; ++h) {
+      a.kv_scale.k[h] = pool->k_scale[h];
+      a.kv_scale.v[h] = pool->v_scale[h];
+    }
   const int64_t row_elems = (int64_t)q_len * num_q_heads * pool->head_dim;
   const int esize = pa::dtype_bytes(pool->dtype);
   const int grid = m.grid;
@@ -249,7 +254,7 @@ int pa_decode_multi(pa_pool *pool, void *out, const void *query, const int32_t *
     a.query = static_cast<const char *>(query) + s0 * row_elems * esize;
     a.block_tables = block_tables + (int64_t)s0 * max_blocks_per_seq;
     a.context_lens = context_lens + s0;
-    const int rc = pa::hip_status(pa::launch_decode_multi(a, pool->dtype, pool->head_dim, grid,
+    const int rc = pa::hip_status(pa::launch_decode_multi(a, pool->dtype, pool->head_dim, pool->kv_fp8, grid,
                                                           static_cast<hipStream_t>(stream)));
     if (rc != PA_OK) return rc;
   }

@@ -88,6 +88,7 @@ struct MultiArgs {
   int32_t min_range_tiles;
   int32_t block_shift;
   float scale_log2;
+  KvScales kv_scale;  // 8-bit pools: dequantisation scales per KV head
 };
 
 // Work-groups of the multi-token kernel's persistent grid (one per CU).
@@ -114,7 +115,7 @@ int choose_partition_tokens(int64_t effective_max_context);
 hipError_t launch_decode(const DecodeArgs &a, pa_dtype dtype, int head_dim, bool ring, bool kv_fp8,
                          DecodeChoice choice, int num_seqs, hipStream_t stream);
 
-hipError_t launch_decode_multi(const MultiArgs &a, pa_dtype dtype, int head_dim, int grid,
+hipError_t launch_decode_multi(const MultiArgs &a, pa_dtype dtype, int head_dim, bool kv_fp8, int grid,
                                hipStream_t stream);
 
 hipError_t launch_reshape_and_cache(pa_dtype dtype, void *k_cache, void *v_cache,

@@ -33,6 +33,7 @@
 //   through a per-wave LDS tile and returns as B operands through
 //   transposing LDS reads, shared by the MT row tiles.
 #include <algorithm>
+#include <type_traits>
 
 #include "device_common.h"
 #include "launch.h"
@@ -65,6 +66,29 @@ struct MqV<64> {
   static __device__ __forceinline__ uint2 load(__amdgpu_buffer_rsrc_t r, int off) {
     return buffer_load8(r, off);
   }
+};
+
+// 8-bit pools: one lane's V codes for a row (D / 16 codes), widened to the
+// 16-bit piece the LDS tile holds.
+template <int D>
+struct MqV8;
+template <>
+struct MqV8<128> {
+  typedef uint2 type;
+  static __device__ __forceinline__ uint2 load(__amdgpu_buffer_rsrc_t r, int off) {
+    return buffer_load8(r, off);
+  }
+  template <class T>
+  static __device__ __forceinline__ uint4 widen(const uint2 &v) { return fp8x8_to_16<T>(v); }
+};
+template <>
+struct MqV8<64> {
+  typedef uint32_t type;
+  static __device__ __forceinline__ uint32_t load(__amdgpu_buffer_rsrc_t r, int off) {
+    return buffer_load4(r, off);
+  }
+  template <class T>
+  static __device__ __forceinline__ uint2 widen(const uint32_t &v) { return fp8x4_to_16<T>(v); }
 };
 
 // Per-wave V tile: row-major, rows padded so the transposing reads of one
@@ -136,7 +160,11 @@ __device__ int mq_schedule(const MultiArgs &a, int *s_tfirst, int *s_kvend, int 
   return carry;
 }
 
-template <class T, int D, int MT>
+// KV8: the pools hold E4M3 codes scaled per KV head.  A lane's 16-byte K
+// load then carries 16 dimensions, the A operands of two score MFMAs, and
+// the query fragments follow that dimension order; codes widen exactly to
+// 16-bit values before the MFMAs and the LDS tile.
+template <class T, int D, int MT, bool KV8>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void decode_multi_kernel(MultiArgs a) {
   constexpr int KB = D / 32;  // score MFMAs per row tile and key tile
@@ -146,6 +174,9 @@ void decode_multi_kernel(MultiArgs a) {
   constexpr int QF = MT * KB;  // query fragments per lane per segment
   typedef typename T::storage st;
   typedef typename MqV<D>::type vchunk;
+  constexpr int KVB = KV8 ? 1 : (int)sizeof(st);  // bytes per K/V element
+  constexpr int KLD = KV8 ? D / 64 : KB;          // 16-byte K loads per lane per tile
+  typedef typename std::conditional<KV8, typename MqV8<D>::type, vchunk>::type vload;
   __shared__ int s_tfirst[kMaxMqSeqs + 1];
   __shared__ int s_kvend[kMaxMqSeqs];
   __shared__ int s_wsum[kMqWaves];
@@ -174,11 +205,16 @@ void decode_multi_kernel(MultiArgs a) {
   const int bmask = (1 << a.block_shift) - 1;
   char *vt = s_vt[wave];
   uint4 *qs = s_q[wave];
-  const int k_off = (int)((row16 * row_stride + 8 * grp) * (int64_t)sizeof(st));
+  const int k_off = (int)((row16 * row_stride + (KV8 ? 16 : 8) * grp) * (int64_t)KVB);
+  // query dimension of element 0 of score MFMA kb's fragment in this lane
+  auto q_dim = [&](int kb) { return KV8 ? 64 * (kb >> 1) + 16 * grp + 8 * (kb & 1) : 32 * kb + 8 * grp; };
   int v_off[4];
 #pragma unroll
   for (int tau = 0; tau < 4; ++tau)
-    v_off[tau] = (int)(((4 * grp + tau) * row_stride + EV * row16) * (int64_t)sizeof(st));
+    v_off[tau] = (int)(((4 * grp + tau) * row_stride + EV * row16) * (int64_t)KVB);
+  // dequantisation of 8-bit pools: scores by k_scale, outputs by v_scale
+  const float kscale = KV8 ? a.kv_scale.k[g] : 1.f;
+  const float vscale = KV8 ? a.kv_scale.v[g] : 1.f;
 
   // segment state
   f32x4 acc[MT][NB];
@@ -242,21 +278,21 @@ void decode_multi_kernel(MultiArgs a) {
         const int qi = ok ? r / G : 0;
         const int h = ok ? r - qi * G : 0;
         const st *q = static_cast<const st *>(a.query) +
-                      (((int64_t)b * ql + qi) * a.num_q_heads + (int64_t)g * G + h) * D + 8 * grp;
+                      (((int64_t)b * ql + qi) * a.num_q_heads + (int64_t)g * G + h) * D;
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb)
           qtmp[s2][mt * KB + kb] =
-              ok ? *reinterpret_cast<const uint4 *>(q + 32 * kb) : make_uint4(0u, 0u, 0u, 0u);
+              ok ? *reinterpret_cast<const uint4 *>(q + q_dim(kb)) : make_uint4(0u, 0u, 0u, 0u);
       }
       mm &= mm - 1;
     }
     if (lane < cnt) {
       const int64_t off = ((int64_t)blk * a.kv_block_stride +
                            (int64_t)((kTileTokens * tt) & bmask) * row_stride + (int64_t)g * D) *
-                          (int64_t)sizeof(st);
+                          (int64_t)KVB;
       toff_lo = (int)(uint32_t)off;
       toff_hi = (int)(off >> 32);
-      tnrec = (int)(((tvalid - 1) * row_stride + D) * (int64_t)sizeof(st));  // tvalid >= 1 here
+      tnrec = (int)(((tvalid - 1) * row_stride + D) * (int64_t)KVB);  // tvalid >= 1 here
     }
 #pragma unroll
     for (int s2 = 0; s2 < kMqQSlots; ++s2)
@@ -265,7 +301,7 @@ void decode_multi_kernel(MultiArgs a) {
   };
 
   // Loads of staged tile j (j >= cnt: empty record range, no memory access).
-  auto load_tile = [&](int j, uint4 (&k)[KB], vchunk (&v)[4]) {
+  auto load_tile = [&](int j, uint4 (&k)[KLD], vload (&v)[4]) {
     const int jj = min(j, kWave - 1);
     const uint64_t off = ((uint64_t)(uint32_t)rd(toff_hi, jj) << 32) | (uint32_t)rd(toff_lo, jj);
     const int nrec = j < cnt ? rd(tnrec, jj) : 0;
@@ -274,9 +310,12 @@ void decode_multi_kernel(MultiArgs a) {
     const auto vr = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<char *>(static_cast<const char *>(a.v_cache) + off), (short)0, nrec, kBufferWord3);
 #pragma unroll
-    for (int kb = 0; kb < KB; ++kb) k[kb] = buffer_load16(kr, k_off + 64 * kb);
+    for (int kb = 0; kb < KLD; ++kb) k[kb] = buffer_load16(kr, k_off + 64 * kb);
 #pragma unroll
-    for (int tau = 0; tau < 4; ++tau) v[tau] = MqV<D>::load(vr, v_off[tau]);
+    for (int tau = 0; tau < 4; ++tau) {
+      if constexpr (KV8) v[tau] = MqV8<D>::load(vr, v_off[tau]);
+      else v[tau] = MqV<D>::load(vr, v_off[tau]);
+    }
   };
 
   auto begin_segment = [&](int j, int v, bool whole) {
@@ -301,8 +340,24 @@ void decode_multi_kernel(MultiArgs a) {
     seg_whole = whole;
   };
 
-  const float sl2 = a.scale_log2;
-  auto process_tile = [&](int j, const uint4 (&kf)[KB], const vchunk (&vf)[4]) {
+  const float sl2 = a.scale_log2 * kscale;
+  auto process_tile = [&](int j, const uint4 (&kraw)[KLD], const vload (&vraw)[4]) {
+    uint4 kf[KB];
+    vchunk vf[4];
+    if constexpr (KV8) {
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) {
+        const uint4 w8 = kraw[kb >> 1];
+        kf[kb] = fp8x8_to_16<T>((kb & 1) ? make_uint2(w8.z, w8.w) : make_uint2(w8.x, w8.y));
+      }
+#pragma unroll
+      for (int tau = 0; tau < 4; ++tau) vf[tau] = MqV8<D>::template widen<T>(vraw[tau]);
+    } else {
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) kf[kb] = kraw[kb];
+#pragma unroll
+      for (int tau = 0; tau < 4; ++tau) vf[tau] = vraw[tau];
+    }
     const int kp0 = kTileTokens * rd(tt, j) + 4 * grp;  // key position of S element 0
     f32x4 sv[MT];
 #pragma unroll
@@ -372,7 +427,7 @@ void decode_multi_kernel(MultiArgs a) {
       for (int r = 0; r < 4; ++r) {
         const int rr = seg_row0 + 16 * mt + 4 * grp + r;
         if (rr >= seg_row_end) continue;
-        const float inv = lh[r] > 0.f ? 1.f / lh[r] : 0.f;
+        const float inv = lh[r] > 0.f ? vscale / lh[r] : 0.f;
         if (whole) {
           const int i = rr / G, h = rr - (rr / G) * G;
           st *out = static_cast<st *>(a.out) +
@@ -395,7 +450,7 @@ void decode_multi_kernel(MultiArgs a) {
     }
   };
 
-  auto step = [&](int j, const uint4 (&kc)[KB], const vchunk (&vc)[4]) {
+  auto step = [&](int j, const uint4 (&kc)[KLD], const vload (&vc)[4]) {
     const int v = rd(tv, j), flag = rd(tflag, j);
     if ((flag & 1) || c0 + j == xbeg) begin_segment(j, v, (flag & 1) != 0);
     process_tile(j, kc, vc);
@@ -406,8 +461,8 @@ void decode_multi_kernel(MultiArgs a) {
   // S - 1 tiles are in flight.  Loads are unconditional (empty past cnt) so
   // every step sees the same loads in flight and the same wait counts.
   constexpr int S = kMqStagesFor<D, MT>;
-  uint4 kbuf[S][KB];
-  vchunk vbuf[S][4];
+  uint4 kbuf[S][KLD];
+  vload vbuf[S][4];
   for (int start = xbeg; start < xend; start += cnt) {
     stage(start);  // sets cnt
 #pragma unroll
@@ -483,9 +538,9 @@ __global__ __launch_bounds__(256) void decode_multi_reduce_kernel(MultiArgs a) {
   out[3] = T::from_float(acc.w * inv);
 }
 
-template <class T, int D, int MT>
+template <class T, int D, int MT, bool KV8>
 hipError_t launch_mt(const MultiArgs &a, int grid, hipStream_t stream) {
-  hipLaunchKernelGGL((decode_multi_kernel<T, D, MT>), dim3(grid), dim3(kMqWaves * kWave), 0, stream, a);
+  hipLaunchKernelGGL((decode_multi_kernel<T, D, MT, KV8>), dim3(grid), dim3(kMqWaves * kWave), 0, stream, a);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   constexpr int rpb = 256 / (D / 4);
@@ -495,14 +550,19 @@ hipError_t launch_mt(const MultiArgs &a, int grid, hipStream_t stream) {
   return hipGetLastError();
 }
 
-template <class T, int D>
+template <class T, int D, bool KV8>
 hipError_t launch_d(const MultiArgs &a, int mt, int grid, hipStream_t stream) {
   switch (mt) {
-    case 1: return launch_mt<T, D, 1>(a, grid, stream);
-    case 2: return launch_mt<T, D, 2>(a, grid, stream);
-    case 3: return launch_mt<T, D, 3>(a, grid, stream);
-    default: return launch_mt<T, D, kMultiMaxRowTiles(D)>(a, grid, stream);
+    case 1: return launch_mt<T, D, 1, KV8>(a, grid, stream);
+    case 2: return launch_mt<T, D, 2, KV8>(a, grid, stream);
+    case 3: return launch_mt<T, D, 3, KV8>(a, grid, stream);
+    default: return launch_mt<T, D, kMultiMaxRowTiles(D), KV8>(a, grid, stream);
   }
+}
+
+template <class T, bool KV8>
+hipError_t launch_h(const MultiArgs &a, int head_dim, int mt, int grid, hipStream_t stream) {
+  return head_dim == 128 ? launch_d<T, 128, KV8>(a, mt, grid, stream) : launch_d<T, 64, KV8>(a, mt, grid, stream);
 }
 
 }  // namespace
@@ -517,12 +577,14 @@ int multi_grid() {
   return cus;
 }
 
-hipError_t launch_decode_multi(const MultiArgs &a, pa_dtype dtype, int head_dim, int grid,
+hipError_t launch_decode_multi(const MultiArgs &a, pa_dtype dtype, int head_dim, bool kv_fp8, int grid,
                                hipStream_t stream) {
   const int mt = a.pass_rows / 16;
   if (dtype == PA_BF16)
-    return head_dim == 128 ? launch_d<BF16, 128>(a, mt, grid, stream) : launch_d<BF16, 64>(a, mt, grid, stream);
-  return head_dim == 128 ? launch_d<F16, 128>(a, mt, grid, stream) : launch_d<F16, 64>(a, mt, grid, stream);
+    return kv_fp8 ? launch_h<BF16, true>(a, head_dim, mt, grid, stream)
+                  : launch_h<BF16, false>(a, head_dim, mt, grid, stream);
+  return kv_fp8 ? launch_h<F16, true>(a, head_dim, mt, grid, stream)
+                : launch_h<F16, false>(a, head_dim, mt, grid, stream);
 }
 
 }  // namespace pa

@@ -34,7 +34,8 @@ def _ref(case, kp=None, vp=None):
     if kp is None:
         kp, vp, _ = oracle.build_pools(case)
     return oracle.decode_multi(case.query, kp, vp, case.block_tables, case.context_lens, case.scale,
-                               case.dtype, case.block_size, case.q_len)
+                               case.dtype, case.block_size, case.q_len, kv_dtype=case.kv_dtype,
+                               k_scale=case.k_scale, v_scale=case.v_scale)
 
 
 def test_spec_verify_tiny():
@@ -164,12 +165,37 @@ def test_rejected_drafts_roll_back():
     dc.close()
 
 
+@pytest.mark.parametrize("min_range", [None, 1])
+@pytest.mark.parametrize("shape", [SHAPES[0], SHAPES[1], SHAPES[3], SHAPES[4]], ids=["s0", "s1", "s3", "s4"])
+def test_multi_parity_fp8_pools(shape, min_range):
+    """8-bit (E4M3) pools: codes widened in registers, per-head scales."""
+    dtype, lens, q, hq, hkv, d, bs = shape
+    print(f"multi fp8 shape {shape} min_range={min_range}", flush=True)
+    case = workloads.config_fp8(lambda: workloads.make_multi_case("multi_fp8", 7400 + len(lens) + q, dtype, lens,
+                                                                  q, hq, hkv, d, bs))
+    dc = DeviceCase(case)
+    dc.write_all()
+    with env(PA_MULTI_MIN_RANGE=min_range):
+        out = _run(dc, case)
+    assert_parity(out, _ref(case), dtype)
+    dc.close()
+
+
+def test_spec_verify_llama70b_fp8():
+    case = workloads.config_fp8(workloads.config_spec_verify_llama70b)
+    print("multi spec_verify_llama70b fp8", flush=True)
+    dc = DeviceCase(case)
+    dc.write_all()
+    out = _run(dc, case)
+    assert_parity(out, _ref(case), case.dtype)
+    dc.close()
+
+
 def test_unsupported_pools():
-    for case in (workloads.make_multi_case("m32", 7300, "f32", [10], 2, 4, 2, 64, 16),
-                 workloads.config_fp8(lambda: workloads.make_multi_case("m8", 7301, "bf16", [10], 2, 8, 2, 128, 16))):
-        dc = DeviceCase(case)
-        out = torch.empty((1, 2, case.num_q_heads, case.head_dim), dtype=TORCH_DTYPES[case.dtype], device=dc.device)
-        with pytest.raises(pk.PaError) as e:
-            pk.decode_multi(dc.pool, out, dc.query, dc.block_tables, dc.context_lens, 10, case.scale)
-        assert e.value.status == -5
-        dc.close()
+    case = workloads.make_multi_case("m32", 7300, "f32", [10], 2, 4, 2, 64, 16)
+    dc = DeviceCase(case)
+    out = torch.empty((1, 2, case.num_q_heads, case.head_dim), dtype=TORCH_DTYPES[case.dtype], device=dc.device)
+    with pytest.raises(pk.PaError) as e:
+        pk.decode_multi(dc.pool, out, dc.query, dc.block_tables, dc.context_lens, 10, case.scale)
+    assert e.value.status == -5
+    dc.close()

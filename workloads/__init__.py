@@ -523,6 +523,8 @@ MULTI_CONFIGS = {
     "spec_verify_tiny": config_spec_verify_tiny,
     "spec_verify_llama70b": config_spec_verify_llama70b,
     "chunked_prefill": config_chunked_prefill,
+    # resolved at call time: config_fp8 is defined further down
+    "spec_verify_llama70b_fp8": lambda: config_fp8(config_spec_verify_llama70b),
 }
 
 
