@@ -498,7 +498,7 @@ def measure_multi(args) -> int:
     return 0
 
 
-def multi_cpu_baseline(case, max_rows: int = 64) -> dict:
+def multi_cpu_baseline(case, max_rows: int = 800) -> dict:
     """The oracle's decode_multi on a bounded sample: the new tokens of the
     first sequences, up to ``max_rows`` (sequence, token) rows."""
     import oracle

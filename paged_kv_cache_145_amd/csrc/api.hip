@@ -75,7 +75,7 @@ WorkspaceLayout workspace_layout(const pa_pool *pool, int32_t num_seqs, int32_t 
 }
 
 struct MultiLayout {
-  int mt, pass_rows, passes, pass_group, pgroups, seqs_per_launch, grid, groups;
+  int waves, mt, pass_rows, passes, pass_group, pgroups, seqs_per_launch, grid, groups;
   size_t sched_bytes, ml_bytes, o_bytes, total;
 };
 
@@ -87,8 +87,13 @@ MultiLayout multi_layout(const pa_pool *pool, int32_t num_seqs, int32_t q_len, i
   const int group = num_q_heads / hkv;
   const int64_t rows = (int64_t)q_len * group;
   const int max_mt = kMultiMaxRowTiles(pool->head_dim);
+  // Many passes (chunked prefill) are bound by the per-tile arithmetic: two
+  // waves per SIMD with two row tiles each; otherwise one wave per SIMD.
+  const int forced_w = env_int("PA_MULTI_WAVES", 0);
+  m.waves = (forced_w == 1 || forced_w == 2) ? forced_w : rows > 3 * 16 * max_mt ? 2 : 1;
+  const int wave_mt = m.waves == 2 ? 2 : max_mt;
   const int forced_mt = env_int("PA_MULTI_ROW_TILES", 0);
-  m.mt = (int)std::min<int64_t>(forced_mt >= 1 && forced_mt <= max_mt ? forced_mt : max_mt, ceil_div(rows, 16));
+  m.mt = (int)std::min<int64_t>(forced_mt >= 1 && forced_mt <= wave_mt ? forced_mt : wave_mt, ceil_div(rows, 16));
   m.pass_rows = 16 * m.mt;
   m.passes = (int)ceil_div(rows, m.pass_rows);
   // passes of one head share K/V tiles through L2 when a work-group takes several
@@ -98,7 +103,7 @@ MultiLayout multi_layout(const pa_pool *pool, int32_t num_seqs, int32_t q_len, i
   m.pgroups = (int)ceil_div(m.passes, m.pass_group);
   m.seqs_per_launch = std::max(1, std::min(num_seqs, kMaxMultiSeqsHost / std::max(1, m.pgroups)));
   const int waves_per_group = hkv * m.pass_group;
-  m.grid = std::max(multi_grid(), (int)ceil_div(waves_per_group, 4));  // at least one group
+  m.grid = std::max(m.waves * multi_grid(), (int)ceil_div(waves_per_group, 4));  // at least one group
   m.groups = (m.grid * 4) / waves_per_group;
   const size_t nv = (size_t)m.seqs_per_launch * m.pgroups;
   const size_t rows_total = (m.groups + nv) * (size_t)waves_per_group * m.pass_rows;
@@ -254,8 +259,8 @@ int pa_decode_multi(pa_pool *pool, void *out, const void *query, const int32_t *
     a.query = static_cast<const char *>(query) + s0 * row_elems * esize;
     a.block_tables = block_tables + (int64_t)s0 * max_blocks_per_seq;
     a.context_lens = context_lens + s0;
-    const int rc = pa::hip_status(pa::launch_decode_multi(a, pool->dtype, pool->head_dim, pool->kv_fp8, grid,
-                                                          static_cast<hipStream_t>(stream)));
+    const int rc = pa::hip_status(pa::launch_decode_multi(a, pool->dtype, pool->head_dim, pool->kv_fp8, m.waves,
+                                                          grid, static_cast<hipStream_t>(stream)));
     if (rc != PA_OK) return rc;
   }
   return PA_OK;

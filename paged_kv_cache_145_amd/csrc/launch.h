@@ -91,7 +91,8 @@ struct MultiArgs {
   KvScales kv_scale;  // 8-bit pools: dequantisation scales per KV head
 };
 
-// Work-groups of the multi-token kernel's persistent grid (one per CU).
+// CUs of the current device: the multi-token kernel's persistent grid is
+// waves-per-SIMD (1 or 2) work-groups per CU.
 int multi_grid();
 // Row tiles of 16 query rows one wave holds: registers allow four at
 // D = 64 and three at D = 128 (with a four-deep load pipeline).
@@ -115,8 +116,8 @@ int choose_partition_tokens(int64_t effective_max_context);
 hipError_t launch_decode(const DecodeArgs &a, pa_dtype dtype, int head_dim, bool ring, bool kv_fp8,
                          DecodeChoice choice, int num_seqs, hipStream_t stream);
 
-hipError_t launch_decode_multi(const MultiArgs &a, pa_dtype dtype, int head_dim, bool kv_fp8, int grid,
-                               hipStream_t stream);
+hipError_t launch_decode_multi(const MultiArgs &a, pa_dtype dtype, int head_dim, bool kv_fp8, int waves,
+                               int grid, hipStream_t stream);
 
 hipError_t launch_reshape_and_cache(pa_dtype dtype, void *k_cache, void *v_cache,
                                     const void *key, const void *value,

@@ -44,11 +44,15 @@ namespace {
 constexpr int kMqWaves = 4;
 constexpr int kMaxMqSeqs = kMaxMultiSeqsHost;  // virtual sequences per launch
 constexpr float kMqRescaleSlack = 8.0f;        // log2 units the running max may lag
-constexpr int kMqQSlots = 2;                   // segment-opening tiles per staged chunk
-
-// Depth of the per-wave tile pipeline.
-template <int D, int MT>
-constexpr int kMqStagesFor = 4;
+// Two configurations.  W = 1 (one wave per SIMD, up to three row tiles, a
+// four-deep load pipeline): memory-bound calls such as draft verification.
+// W = 2 (two waves per SIMD, at most two row tiles, two stages, one query
+// slot, so two work-groups fit a CU): calls with many row passes, where a
+// second wave hides the per-tile MFMA -> softmax -> MFMA chain.
+template <int W>
+constexpr int kMqStagesFor = W == 2 ? 2 : 4;  // depth of the per-wave tile pipeline
+template <int W>
+constexpr int kMqQSlotsFor = W == 2 ? 1 : 2;  // segment-opening tiles per staged chunk
 
 // One lane's share of a V row: D / 16 elements, 16 or 8 bytes.
 template <int D>
@@ -164,9 +168,10 @@ __device__ int mq_schedule(const MultiArgs &a, int *s_tfirst, int *s_kvend, int 
 // load then carries 16 dimensions, the A operands of two score MFMAs, and
 // the query fragments follow that dimension order; codes widen exactly to
 // 16-bit values before the MFMAs and the LDS tile.
-template <class T, int D, int MT, bool KV8>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+template <class T, int D, int MT, bool KV8, int W>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(W, W)))
 void decode_multi_kernel(MultiArgs a) {
+  constexpr int kMqQSlots = kMqQSlotsFor<W>;
   constexpr int KB = D / 32;  // score MFMAs per row tile and key tile
   constexpr int EV = D / 16;  // V elements per lane per row
   constexpr int NB = D / 16;  // output MFMAs per row tile (16 dims each)
@@ -460,7 +465,7 @@ void decode_multi_kernel(MultiArgs a) {
   // S register buffers: tile j is consumed from buffer j % S while the next
   // S - 1 tiles are in flight.  Loads are unconditional (empty past cnt) so
   // every step sees the same loads in flight and the same wait counts.
-  constexpr int S = kMqStagesFor<D, MT>;
+  constexpr int S = kMqStagesFor<W>;
   uint4 kbuf[S][KLD];
   vload vbuf[S][4];
   for (int start = xbeg; start < xend; start += cnt) {
@@ -538,9 +543,9 @@ __global__ __launch_bounds__(256) void decode_multi_reduce_kernel(MultiArgs a) {
   out[3] = T::from_float(acc.w * inv);
 }
 
-template <class T, int D, int MT, bool KV8>
+template <class T, int D, int MT, bool KV8, int W>
 hipError_t launch_mt(const MultiArgs &a, int grid, hipStream_t stream) {
-  hipLaunchKernelGGL((decode_multi_kernel<T, D, MT, KV8>), dim3(grid), dim3(kMqWaves * kWave), 0, stream, a);
+  hipLaunchKernelGGL((decode_multi_kernel<T, D, MT, KV8, W>), dim3(grid), dim3(kMqWaves * kWave), 0, stream, a);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   constexpr int rpb = 256 / (D / 4);
@@ -551,23 +556,27 @@ hipError_t launch_mt(const MultiArgs &a, int grid, hipStream_t stream) {
 }
 
 template <class T, int D, bool KV8>
-hipError_t launch_d(const MultiArgs &a, int mt, int grid, hipStream_t stream) {
+hipError_t launch_d(const MultiArgs &a, int mt, int waves, int grid, hipStream_t stream) {
+  if (waves == 2) return mt == 1 ? launch_mt<T, D, 1, KV8, 2>(a, grid, stream)
+                                 : launch_mt<T, D, 2, KV8, 2>(a, grid, stream);
   switch (mt) {
-    case 1: return launch_mt<T, D, 1, KV8>(a, grid, stream);
-    case 2: return launch_mt<T, D, 2, KV8>(a, grid, stream);
-    case 3: return launch_mt<T, D, 3, KV8>(a, grid, stream);
-    default: return launch_mt<T, D, kMultiMaxRowTiles(D), KV8>(a, grid, stream);
+    case 1: return launch_mt<T, D, 1, KV8, 1>(a, grid, stream);
+    case 2: return launch_mt<T, D, 2, KV8, 1>(a, grid, stream);
+    case 3: return launch_mt<T, D, 3, KV8, 1>(a, grid, stream);
+    default: return launch_mt<T, D, kMultiMaxRowTiles(D), KV8, 1>(a, grid, stream);
   }
 }
 
 template <class T, bool KV8>
-hipError_t launch_h(const MultiArgs &a, int head_dim, int mt, int grid, hipStream_t stream) {
-  return head_dim == 128 ? launch_d<T, 128, KV8>(a, mt, grid, stream) : launch_d<T, 64, KV8>(a, mt, grid, stream);
+hipError_t launch_h(const MultiArgs &a, int head_dim, int mt, int waves, int grid, hipStream_t stream) {
+  return head_dim == 128 ? launch_d<T, 128, KV8>(a, mt, waves, grid, stream)
+                         : launch_d<T, 64, KV8>(a, mt, waves, grid, stream);
 }
 
 }  // namespace
 
-// One work-group (four waves, one per SIMD) per CU.
+// CUs of the current device (one work-group of four waves per CU and per
+// wave-per-SIMD of the configuration).
 int multi_grid() {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) dev = 0;
@@ -577,14 +586,14 @@ int multi_grid() {
   return cus;
 }
 
-hipError_t launch_decode_multi(const MultiArgs &a, pa_dtype dtype, int head_dim, bool kv_fp8, int grid,
-                               hipStream_t stream) {
+hipError_t launch_decode_multi(const MultiArgs &a, pa_dtype dtype, int head_dim, bool kv_fp8, int waves,
+                               int grid, hipStream_t stream) {
   const int mt = a.pass_rows / 16;
   if (dtype == PA_BF16)
-    return kv_fp8 ? launch_h<BF16, true>(a, head_dim, mt, grid, stream)
-                  : launch_h<BF16, false>(a, head_dim, mt, grid, stream);
-  return kv_fp8 ? launch_h<F16, true>(a, head_dim, mt, grid, stream)
-                : launch_h<F16, false>(a, head_dim, mt, grid, stream);
+    return kv_fp8 ? launch_h<BF16, true>(a, head_dim, mt, waves, grid, stream)
+                  : launch_h<BF16, false>(a, head_dim, mt, waves, grid, stream);
+  return kv_fp8 ? launch_h<F16, true>(a, head_dim, mt, waves, grid, stream)
+                : launch_h<F16, false>(a, head_dim, mt, waves, grid, stream);
 }
 
 }  // namespace pa

@@ -78,17 +78,19 @@ def test_multi_parity_shapes(shape, min_range):
     dc.close()
 
 
+@pytest.mark.parametrize("waves", [1, 2])
 @pytest.mark.parametrize("pass_group", [1, 2, 4])
 @pytest.mark.parametrize("shape", SHAPES[:5], ids=[f"s{i}" for i in range(5)])
-def test_multi_parity_pass_groups(shape, pass_group):
+def test_multi_parity_pass_groups(shape, pass_group, waves):
     """Several passes of one head per work-group (sharing K/V tiles through
-    L2), including pass groups with fewer real passes than waves."""
+    L2), including pass groups with fewer real passes than waves, in both
+    kernel configurations (one and two waves per SIMD)."""
     dtype, lens, q, hq, hkv, d, bs = shape
-    print(f"multi shape {shape} pass_group={pass_group}", flush=True)
+    print(f"multi shape {shape} pass_group={pass_group} waves={waves}", flush=True)
     case = workloads.make_multi_case("multi_shape", 7100 + len(lens) + q, dtype, lens, q, hq, hkv, d, bs)
     dc = DeviceCase(case)
     dc.write_all()
-    with env(PA_MULTI_PASS_GROUP=pass_group, PA_MULTI_MIN_RANGE=1):
+    with env(PA_MULTI_PASS_GROUP=pass_group, PA_MULTI_MIN_RANGE=1, PA_MULTI_WAVES=waves):
         out = _run(dc, case)
     assert_parity(out, _ref(case), dtype)
     dc.close()
@@ -165,17 +167,18 @@ def test_rejected_drafts_roll_back():
     dc.close()
 
 
+@pytest.mark.parametrize("waves", [None, 2])
 @pytest.mark.parametrize("min_range", [None, 1])
 @pytest.mark.parametrize("shape", [SHAPES[0], SHAPES[1], SHAPES[3], SHAPES[4]], ids=["s0", "s1", "s3", "s4"])
-def test_multi_parity_fp8_pools(shape, min_range):
+def test_multi_parity_fp8_pools(shape, min_range, waves):
     """8-bit (E4M3) pools: codes widened in registers, per-head scales."""
     dtype, lens, q, hq, hkv, d, bs = shape
-    print(f"multi fp8 shape {shape} min_range={min_range}", flush=True)
+    print(f"multi fp8 shape {shape} min_range={min_range} waves={waves}", flush=True)
     case = workloads.config_fp8(lambda: workloads.make_multi_case("multi_fp8", 7400 + len(lens) + q, dtype, lens,
                                                                   q, hq, hkv, d, bs))
     dc = DeviceCase(case)
     dc.write_all()
-    with env(PA_MULTI_MIN_RANGE=min_range):
+    with env(PA_MULTI_MIN_RANGE=min_range, PA_MULTI_WAVES=waves):
         out = _run(dc, case)
     assert_parity(out, _ref(case), dtype)
     dc.close()
