@@ -30,7 +30,9 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_decode_llama70b_b64.json")
+def traffic_file(config: str) -> str:
+    """Counter-derived HBM traffic record of the decode call on a workload."""
+    return os.path.join(ROOT, "profiles", f"traffic_decode_{config}.json")
 KERNEL_SOURCES = ["decode_kernels.hip", "device_common.h", "launch.h", "api.hip"]
 DECODE_KERNELS = ("decode_mfma_kernel", "decode_streamk_reduce_kernel")
 CALIBRATION_BYTES = 1 << 30  # the plain copy run after the profiled decode calls
@@ -72,10 +74,10 @@ def kernel_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def read_traffic():
+def read_traffic(config: str):
     """Counter-derived HBM bytes per decode call, if taken on the current kernels."""
     try:
-        with open(TRAFFIC_FILE) as fh:
+        with open(traffic_file(config)) as fh:
             t = json.load(fh)
     except (OSError, ValueError):
         return None
@@ -694,7 +696,7 @@ def main() -> int:
     args = ap.parse_args()
     if args.write_traffic:
         rec = summarize_counters(args.write_traffic[0], args.write_traffic[1], args.traffic_command)
-        with open(TRAFFIC_FILE, "w") as fh:
+        with open(traffic_file(args.config), "w") as fh:
             json.dump(rec, fh, indent=1)
         print(json.dumps(rec))
         return 0
@@ -862,7 +864,7 @@ def main() -> int:
     value = step_bytes / (ms_per_step * 1e-3) / 1e9
     dec_avg_ms = statistics.mean(decode_ms)
     achieved = ab["decode"] / (dec_avg_ms * 1e-3) / 1e9
-    traffic = read_traffic() if args.config == "llama70b_b64" else None
+    traffic = read_traffic(args.config)
     group = case.num_q_heads // case.num_kv_heads
     mfma = case.dtype != "f32" and 4 <= group <= 16 and os.environ.get("PA_FORCE_VALU", "0") in ("", "0")
     kernel = ("pa_decode call: decode_mfma_kernel + decode_streamk_reduce_kernel" if mfma else
