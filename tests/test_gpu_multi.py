@@ -202,3 +202,31 @@ def test_unsupported_pools():
         pk.decode_multi(dc.pool, out, dc.query, dc.block_tables, dc.context_lens, 10, case.scale)
     assert e.value.status == -5
     dc.close()
+
+
+def test_more_sequences_than_one_launch_slice():
+    """1,300 sequences: the single-token decode schedules at most 1,024
+    sequences per launch and the multi-token decode at most 1,024 (sequence,
+    pass group) pairs, so both run as consecutive slices."""
+    rng = np.random.default_rng(77)
+    lens = [int(x) for x in rng.integers(1, 41, size=1300)]
+    print("slices: 1300 sequences", flush=True)
+    for q in (1, 9):
+        case = workloads.make_multi_case("slices", 7500 + q, "bf16", lens, q, 16, 2, 64, 16)
+        dc = DeviceCase(case)
+        dc.write_all()
+        out = _run(dc, case)
+        assert_parity(out, _ref(case), case.dtype)
+        if q == 1:
+            single = torch.empty((case.num_seqs, 16, 64), dtype=torch.bfloat16, device=dc.device)
+            mcl = int(case.context_lens.max())
+            ws = torch.empty(max(pk.decode_workspace_bytes(dc.pool, case.num_seqs, 16, mcl), 1), dtype=torch.uint8,
+                             device=dc.device)
+            pk.decode(dc.pool, single, dc.query[:, 0].contiguous(), dc.block_tables, dc.context_lens, mcl,
+                      case.scale, workspace=ws)
+            torch.cuda.synchronize()
+            kp, vp, _ = oracle.build_pools(case)
+            ref = oracle.decode(case.query[:, 0], kp, vp, case.block_tables, case.context_lens, case.scale,
+                                case.dtype, case.block_size)
+            assert_parity(single, ref, case.dtype)
+        dc.close()
