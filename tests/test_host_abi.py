@@ -310,3 +310,39 @@ int main() {
     run = subprocess.run([str(exe)], capture_output=True, text=True, timeout=120)
     assert run.returncode == 0, run.stdout + run.stderr
     assert run.stdout.split() == ["1000", "0", "0", "1000"]
+
+
+def test_decode_multi_argument_validation(lib):
+    """pa_decode_multi rejects bad arguments before any device call."""
+    h = fake_pool(lib, 64, 16, 2, 128, 2)  # bf16
+    dev = ctypes.c_void_p(1 << 24)
+    odd = ctypes.c_void_p((1 << 24) + 2)
+    need = lib.pa_decode_multi_workspace_bytes(h, 3, 5, 16, 500)
+    assert need > 0
+    assert lib.pa_decode_multi_workspace_bytes(h, 0, 5, 16, 500) == 0
+    assert lib.pa_decode_multi_workspace_bytes(h, 3, 0, 16, 500) == 0  # q_len 0
+    assert lib.pa_decode_multi_workspace_bytes(h, 3, 5, 15, 500) == 0  # Hq not a multiple of Hkv
+    call = lambda *a: lib.pa_decode_multi(*a)
+    # q_len outside 1 .. 4096, Hq not a multiple of Hkv, negative sizes
+    assert call(h, dev, dev, dev, 40, dev, 3, 0, 16, 500, 0.1, dev, need, None) == -1
+    assert call(h, dev, dev, dev, 40, dev, 3, 4097, 16, 500, 0.1, dev, need, None) == -1
+    assert call(h, dev, dev, dev, 40, dev, 3, 5, 15, 500, 0.1, dev, need, None) == -1
+    assert call(h, dev, dev, dev, 40, dev, -1, 5, 16, 500, 0.1, dev, need, None) == -1
+    # context beyond the table, misaligned pointers, NaN scale
+    assert call(h, dev, dev, dev, 4, dev, 3, 5, 16, 500, 0.1, dev, need, None) == -1
+    assert call(h, odd, dev, dev, 40, dev, 3, 5, 16, 500, 0.1, dev, need, None) == -1
+    assert call(h, dev, dev, odd, 40, dev, 3, 5, 16, 500, 0.1, dev, need, None) == -1
+    assert call(h, dev, dev, dev, 40, dev, 3, 5, 16, 500, float("nan"), dev, need, None) == -1
+    # workspace missing or short, misaligned workspace
+    assert call(h, dev, dev, dev, 40, dev, 3, 5, 16, 500, 0.1, None, 0, None) == -2
+    assert call(h, dev, dev, dev, 40, dev, 3, 5, 16, 500, 0.1, dev, need - 1, None) == -2
+    assert call(h, dev, dev, dev, 40, dev, 3, 5, 16, 500, 0.1, ctypes.c_void_p((1 << 24) + 16), need, None) == -1
+    # too many rows for one launch slice
+    assert call(h, dev, dev, dev, 40, dev, 3, 4096, 64, 500, 0.1, dev, need, None) == -5
+    # zero sequences is a no-op
+    assert call(h, None, None, None, 40, None, 0, 5, 16, 500, 0.1, None, 0, None) == 0
+    lib.pa_destroy_pool(h)
+    # fp32 pools have no multi-token kernel
+    h32 = fake_pool(lib, 64, 16, 2, 128, 0)
+    assert call(h32, dev, dev, dev, 40, dev, 3, 5, 16, 500, 0.1, dev, need, None) == -5
+    lib.pa_destroy_pool(h32)
