@@ -245,23 +245,30 @@ int pa_prefix_insert(pa_pool *pool, const uint32_t *tokens, int64_t num_tokens,
     for (size_t b = a + 1; b < plan.size(); ++b)
       if (plan[b].existing < 0 && plan[b].block == plan[a].block) return PA_ERR_STATE;
   }
-  int32_t created = 0;
+  // Phase 1: every allocation the insert may need except the map nodes.
+  size_t new_count = 0;
+  for (const pa::Step &st : plan) new_count += st.existing < 0 ? 1 : 0;
+  std::vector<std::vector<uint32_t>> toks;
+  std::vector<int32_t> made, path;
   try {
-    // reserve the slots first so a failed allocation leaves the index as it was
-    size_t new_count = 0;
-    for (const pa::Step &st : plan) new_count += st.existing < 0 ? 1 : 0;
-    if (new_count > ix.free_slots.size())
-      ix.entries.reserve(ix.entries.size() + new_count - ix.free_slots.size());
-    ix.by_key.reserve(ix.by_key.size() + new_count);
-    ix.tails.reserve(ix.tails.size() + new_count);
-    std::vector<std::vector<uint32_t>> toks(new_count);
+    toks.resize(new_count);
     size_t k = 0;
     for (const pa::Step &st : plan)
       if (st.existing < 0) toks[k++].assign(tokens + st.first, tokens + st.first + st.count);
-
-    ix.clock += 1;
+    made.reserve(new_count);
+    path.reserve(plan.size());
+    ix.entries.reserve(ix.entries.size() + new_count);
+    ix.free_slots.reserve(ix.free_slots.size() + new_count);  // room to give slots back
+    ix.by_key.reserve(ix.by_key.size() + new_count);
+    ix.tails.reserve(ix.tails.size() + new_count);
+  } catch (...) {
+    return PA_ERR_NOMEM;  // nothing changed
+  }
+  // Phase 2: the new entries and their map nodes; a failed node allocation
+  // takes every new entry back out.
+  try {
     parent = -1;
-    k = 0;
+    size_t k = 0;
     for (const pa::Step &st : plan) {
       int32_t slot = st.existing;
       if (slot < 0) {
@@ -270,41 +277,59 @@ int pa_prefix_insert(pa_pool *pool, const uint32_t *tokens, int64_t num_tokens,
           ix.free_slots.pop_back();
         } else {
           slot = (int32_t)ix.entries.size();
-          ix.entries.emplace_back();
+          ix.entries.emplace_back();  // within the reserved capacity
         }
+        made.push_back(slot);
         pa::PrefixEntry &e = ix.entries[(size_t)slot];
-        e.live = true;
         e.full = st.full;
         e.block = st.block;
         e.parent = parent;
         e.children = 0;
         e.key = st.key;
-        e.serial = ix.next_serial++;
         e.tokens = std::move(toks[k++]);
         if (st.full)
           ix.by_key.emplace(st.key, slot);
-        else {
+        else
           ix.tails.emplace(parent, slot);
-          ix.tail_entries += 1;
-        }
-        if (parent >= 0) ix.entries[(size_t)parent].children += 1;
-        ix.block_entry[(size_t)st.block] = slot;
-        pa::add_ref_locked(pool, st.block);
-        ix.live += 1;
-        created += 1;
+        e.live = true;
       }
-      pa::PrefixEntry &e = ix.entries[(size_t)slot];
-      e.last_use = ix.clock;
-      if (resident && !e.resident) {
-        e.resident = true;
-        ix.resident += 1;
-      }
+      path.push_back(slot);
       parent = slot;
     }
   } catch (...) {
-    return PA_ERR_NOMEM;  // only reachable before the first entry is made
+    for (auto it = made.rbegin(); it != made.rend(); ++it) {
+      pa::PrefixEntry &e = ix.entries[(size_t)*it];
+      if (e.live) {
+        if (e.full)
+          pa::erase_pair(ix.by_key, e.key, *it);
+        else
+          pa::erase_pair(ix.tails, e.parent, *it);
+      }
+      e = pa::PrefixEntry();
+      ix.free_slots.push_back(*it);  // within the reserved capacity
+    }
+    return PA_ERR_NOMEM;
   }
-  if (num_new != nullptr) *num_new = created;
+  // Phase 3: counts, references and use stamps (nothing allocates).
+  for (int32_t slot : made) {
+    pa::PrefixEntry &e = ix.entries[(size_t)slot];
+    e.serial = ix.next_serial++;
+    if (!e.full) ix.tail_entries += 1;
+    if (e.parent >= 0) ix.entries[(size_t)e.parent].children += 1;
+    ix.block_entry[(size_t)e.block] = slot;
+    pa::add_ref_locked(pool, e.block);
+    ix.live += 1;
+  }
+  ix.clock += 1;
+  for (int32_t slot : path) {
+    pa::PrefixEntry &e = ix.entries[(size_t)slot];
+    e.last_use = ix.clock;
+    if (resident && !e.resident) {
+      e.resident = true;
+      ix.resident += 1;
+    }
+  }
+  if (num_new != nullptr) *num_new = (int32_t)made.size();
   return PA_OK;
 }
 
