@@ -866,7 +866,7 @@ def main() -> int:
     achieved = ab["decode"] / (dec_avg_ms * 1e-3) / 1e9
     traffic = read_traffic(args.config)
     group = case.num_q_heads // case.num_kv_heads
-    mfma = case.dtype != "f32" and 4 <= group <= 16 and os.environ.get("PA_FORCE_VALU", "0") in ("", "0")
+    mfma = case.dtype != "f32" and 1 <= group <= 16 and os.environ.get("PA_FORCE_VALU", "0") in ("", "0")
     kernel = ("pa_decode call: decode_mfma_kernel + decode_streamk_reduce_kernel" if mfma else
               "pa_decode call: decode_valu_kernel (+ decode_reduce_kernel when a context is split)")
     if args.config == "llama70b_b64":

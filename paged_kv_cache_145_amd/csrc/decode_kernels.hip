@@ -279,7 +279,7 @@ struct VChunk<64> {
 };
 
 // ---------------------------------------------------------------------------
-// MFMA kernel: 16-bit K/V, GQA group G in [1, 16] (used for G >= 4).
+// MFMA kernel: 16-bit K/V (or 8-bit codes), GQA group G in [1, 16].
 //
 // Work split (stream-K over tiles).  The batch is the flattened list of
 // (sequence b, 16-token tile t), T tiles in all.  Resident waves form groups

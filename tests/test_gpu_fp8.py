@@ -80,8 +80,8 @@ def test_fp8_unsupported_combinations_are_rejected():
     case = workloads.FP8_CONFIGS["tiny_fp8"]()
     dc = DeviceCase(case)
     out = torch.empty((case.num_seqs, case.num_q_heads, case.head_dim), dtype=torch.bfloat16, device="cuda")
-    # a group of 1 (MHA) has no 8-bit kernel
-    q1 = torch.zeros((case.num_seqs, case.num_kv_heads, case.head_dim), dtype=torch.bfloat16, device="cuda")
+    # a group above 16 has no 8-bit kernel
+    q1 = torch.zeros((case.num_seqs, 32 * case.num_kv_heads, case.head_dim), dtype=torch.bfloat16, device="cuda")
     o1 = torch.empty_like(q1)
     with pytest.raises(pk.PaError) as e:
         pk.decode(dc.pool, o1, q1, dc.block_tables, dc.context_lens, int(case.context_lens.max()), 0.1)
@@ -92,4 +92,19 @@ def test_fp8_unsupported_combinations_are_rejected():
     with pytest.raises(pk.PaError) as e:
         pk.decode(dc.pool, out, dc.query, dc.block_tables, dc.context_lens, 64, 0.1, ring=ring)
     assert e.value.status == -5
+    dc.close()
+
+
+@pytest.mark.parametrize("hq,hkv,d", [(4, 4, 128), (4, 2, 64), (6, 2, 128)], ids=["G1-D128", "G2-D64", "G3-D128"])
+def test_fp8_small_groups(hq, hkv, d):
+    """GQA groups below 4 (MHA included) on 8-bit pools, several tile ranges."""
+    base = workloads.make_paged_case("small_group", 145_090 + hq + d, "bf16", [700, 3, 2100, 64, 0, 1300],
+                                     hq, hkv, d, 16)
+    case = workloads.config_fp8(lambda: base)
+    dc = DeviceCase(case)
+    dc.write_all()
+    out = dc.decode()
+    _, _, _, ref = oracle_reference(case)
+    assert_parity(out, ref, case.dtype)
+    assert np.all(out.float().cpu().numpy()[4] == 0)
     dc.close()

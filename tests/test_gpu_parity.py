@@ -148,6 +148,8 @@ SHAPES = [
     ("bf16", 32, 2, 64, 64, [7, 128, 1111]),
     ("f16", 12, 2, 128, 16, [0, 1, 9, 4000]),
     ("bf16", 40, 2, 128, 16, [250, 1300]),
+    ("bf16", 8, 4, 128, 16, [0, 5, 16, 700, 2900]),
+    ("f16", 2, 2, 64, 64, [1, 64, 1500, 33]),
 ]
 
 
@@ -299,4 +301,69 @@ def test_decode_is_deterministic_across_calls():
     a = torch_bits(dc.decode(), "bf16")
     b = torch_bits(dc.decode(), "bf16")
     assert np.array_equal(a, b)
+    dc.close()
+
+
+LONG_SHAPES = [
+    # dtype, Hq, Hkv, D, bs, lengths: one context spans hundreds of tile ranges
+    ("bf16", 16, 2, 128, 16, [40000, 7]),
+    ("f16", 16, 1, 128, 16, [20000]),        # G 16: two passes of 8 heads per merge
+    ("bf16", 32, 4, 64, 16, [9000, 3000, 1]),
+]
+
+
+@pytest.mark.parametrize("shape", LONG_SHAPES, ids=lambda s: f"{s[0]}-G{s[1] // s[2]}-D{s[3]}-n{s[5][0]}")
+def test_long_context_merges_many_segments(shape):
+    """A context cut into hundreds of stream-K segments (more than the
+    combine takes in one chunk of 64) still matches the oracle, and repeats
+    bit for bit."""
+    dtype, hq, hkv, d, bs, lens = shape
+    case = workloads.make_paged_case("long", 7100 + hq + d, dtype, lens, hq, hkv, d, bs)
+    _, _, _, ref = oracle_reference(case)
+    dc = DeviceCase(case)
+    dc.write_all()
+    out = dc.decode()
+    assert_parity(out, ref, dtype)
+    again = dc.decode()
+    assert np.array_equal(torch_bits(out, dtype), torch_bits(again, dtype))
+    dc.close()
+
+
+def test_workspace_reused_across_shapes():
+    """One workspace, never initialised (filled with 0xFF bytes here), serves
+    calls of different shapes in turn; each equals a call with its own."""
+    import paged_kv_cache_145_amd as pk
+
+    cases = [workloads.config_llama70b(),
+             workloads.make_paged_case("reuse", 7301, "bf16", [5000, 60, 2100, 900], 64, 8, 128, 16)]
+    dcs = [DeviceCase(c) for c in cases]
+    for dc in dcs:
+        dc.write_all()
+    fresh = [torch_bits(dc.decode(), "bf16") for dc in dcs]
+    nbytes = max(pk.decode_workspace_bytes(dc.pool, dc.case.num_seqs, dc.case.num_q_heads,
+                                           int(dc.case.context_lens.max())) for dc in dcs)
+    ws = torch.full((nbytes,), 0xFF, dtype=torch.uint8, device="cuda:0")
+    for i in [0, 1, 0, 1, 1, 0]:
+        dc, c = dcs[i], dcs[i].case
+        out = torch.empty((c.num_seqs, c.num_q_heads, c.head_dim), dtype=torch.bfloat16, device="cuda:0")
+        pk.decode(dc.pool, out, dc.query, dc.block_tables, dc.context_lens, int(c.context_lens.max()),
+                  c.scale, workspace=ws)
+        torch.cuda.synchronize()
+        assert np.array_equal(torch_bits(out, "bf16"), fresh[i]), f"call on case {i} differs"
+    for dc in dcs:
+        dc.close()
+
+
+@pytest.mark.parametrize("kernel", ["auto", "valu"])
+@pytest.mark.parametrize("hq,hkv", [(2, 2), (4, 2)], ids=["G1", "G2"])
+def test_ring_small_groups(hq, hkv, kernel):
+    """The sink + ring cache with in-kernel RoPE at GQA groups 1 and 2."""
+    case = workloads.config_sink_ring(lengths=[1, 5, 1023, 1025, 2045, 50_000], num_q_heads=hq,
+                                      num_kv_heads=hkv)
+    _, _, _, ref = oracle_reference(case)
+    dc = DeviceCase(case)
+    dc.write_all()
+    with env(PA_FORCE_VALU="1" if kernel == "valu" else None):
+        out = dc.decode(max_context_len=100_000)
+    assert_parity(out, ref, "f16")
     dc.close()

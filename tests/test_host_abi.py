@@ -157,7 +157,8 @@ def test_create_pool_fp8_validation(lib):
 
     ring = PaRing(4, 60, 10000.0, 0, dev)
     assert lib.pa_decode(h, dev, dev, dev, 8, dev, 2, 8, 64, 0.1, ctypes.byref(ring), None, 0, None) == -5
-    assert lib.pa_decode(h, dev, dev, dev, 8, dev, 2, 2, 64, 0.1, None, None, 0, None) == -5
+    # GQA group 32 (above the 8-bit kernel's 16)
+    assert lib.pa_decode(h, dev, dev, dev, 8, dev, 2, 64, 64, 0.1, None, None, 0, None) == -5
     lib.pa_destroy_pool(h)
 
 
@@ -238,8 +239,8 @@ def test_decode_and_write_argument_validation(lib):
     assert lib.pa_decode(h, dev, dev, dev, 256, dev, 2, 4, 4096, 0.1, None, None, 0, None) == -2
     assert lib.pa_decode(h, dev, dev, dev, 256, dev, 2, 4, 4096, 0.1, None, dev, need - 1, None) == -2
     # short context fits one partition: no workspace needed
-    # group 2 (VALU kernel): a context inside one partition needs no workspace
-    assert lib.pa_decode_workspace_bytes(h, 2, 4, 100, None) == 0
+    # group 20 (VALU kernel): a context inside one partition needs no workspace
+    assert lib.pa_decode_workspace_bytes(h, 2, 40, 100, None) == 0
     # group 8 (MFMA kernel, stream-K): partial slots are always reserved
     assert lib.pa_decode_workspace_bytes(h, 2, 16, 100, None) > 0
     # zero sequences is a no-op
