@@ -287,7 +287,7 @@ struct VChunk<64> {
 // range of its group gw / Hkv, ceil(T / groups) tiles.  So all waves carry
 // the same number of tiles, and the Hkv heads of one tile (one contiguous
 // run of every token row) are read at the same time.  Each wave runs a
-// two-deep load pipeline straight across sequence boundaries: no per-item
+// shallow load pipeline straight across sequence boundaries: no per-item
 // prologue and no cross-wave barrier.  A sequence that starts and ends
 // inside one range writes its final output rows directly; a sequence cut
 // by a range boundary leaves a partial (running max, sum and normalised
@@ -305,7 +305,14 @@ struct VChunk<64> {
 // ---------------------------------------------------------------------------
 constexpr int kMaxPersistentWaves = kMaxPersistentWavesHost;
 // Depth of the per-wave tile pipeline (tiles in flight + the one consumed).
-constexpr int kStages = 4;
+// HBM saturates with one tile in flight per wave (1024 waves x 8 KiB at
+// 16 bits); more only lengthens the queues.  16-bit pools keep one tile
+// ahead (the 70B-shaped batch: 85.0 us against 85.6 us at four stages, the
+// MHA shared-prefix batch 60.4 against 61.4), 8-bit pools, two waves per
+// SIMD with twice the per-byte arithmetic, issue each tile's loads just
+// before consuming it (47.0 us against 54.9 us at four stages).
+template <bool KV8>
+constexpr int kStagesFor = KV8 ? 1 : 2;
 // Segment-opening tiles per staged chunk (query fragments kept in LDS);
 // 8-bit pools keep two so that two work-groups fit a CU's LDS.
 template <bool KV8>
@@ -655,9 +662,9 @@ void decode_mfma_kernel(DecodeArgs a) {
     }
   };
 
-  // Pipeline of kStages register buffers: tile j is consumed from buffer
-  // j % kStages while tiles j+1 .. j+kStages-1 are in flight.
-  constexpr int S = kStages;
+  // Pipeline of S register buffers: tile j is consumed from buffer j % S
+  // while tiles j+1 .. j+S-1 are in flight.
+  constexpr int S = kStagesFor<KV8>;
   uint4 kbuf[S][KLD];
   vload vbuf[S][4];
   auto step = [&](int j, uint4 (&kc)[KLD], vload (&vc)[4], uint4 (&kn)[KLD], vload (&vn)[4]) {
