@@ -122,8 +122,10 @@ def summarize_counters(fetch_csv: str, write_csv: str, command: str) -> dict:
     return out
 
 
-def cpu_baseline(case, repeats: int = 2) -> dict:
-    """The fp64 oracle (gather through block tables + naive softmax) on host cores."""
+def cpu_baseline(case, min_seconds: float = 10.0, max_repeats: int = 40) -> dict:
+    """The fp64 oracle (gather through block tables + naive softmax) on host
+    cores, repeated over the whole workload until about ``min_seconds`` of
+    CPU work (at least two calls); the median call is reported."""
     import oracle
 
     try:
@@ -136,7 +138,7 @@ def cpu_baseline(case, repeats: int = 2) -> dict:
     try:
         if ctx:
             ctx.__enter__()
-        for _ in range(repeats):
+        while len(times) < 2 or (sum(times) < min_seconds and len(times) < max_repeats):
             t0 = time.perf_counter()
             c0 = time.process_time()
             oracle.decode(case.query, kp, vp, case.block_tables, case.context_lens, case.scale,
@@ -153,7 +155,8 @@ def cpu_baseline(case, repeats: int = 2) -> dict:
     ab = algorithmic_bytes(case)
     return {"value": round(ab["decode"] / t / 1e9, 4), "unit": "GB/s", "cores": cores, "kind": "oracle",
             "sample": f"whole workload ({case.num_seqs} sequences, {ab['tokens']} cached tokens), "
-                      f"decode only (fp64 gather + softmax), median of {repeats}; {t:.3f} s per call, "
+                      f"decode only (fp64 gather + softmax), median of {len(times)} calls ({sum(times):.1f} s); "
+                      f"{t:.3f} s per call, "
                       f"cpu/wall {sum(cpu_s) / sum(times):.2f}",
             "seconds_per_call": round(t, 4)}
 
