@@ -515,21 +515,54 @@ __global__ __launch_bounds__(256) void decode_multi_reduce_kernel(MultiArgs a) {
   float wsum = 0.f;
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
   if (t1 > t0) {
+    // Segments k = ga..gb in windows of kWin: every (m, l) pair and row of a
+    // window is requested before the first is used (one round trip per
+    // window, not one per segment); windows after the first rescale the
+    // running sums to the new maximum.
+    constexpr int kWin = 16;
+    const int64_t rstep = (int64_t)a.num_kv_heads * PG * a.pass_rows;  // rows between segments
+    const int64_t r0 = ((((int64_t)ga + v) * a.num_kv_heads + g) * PG + w) * a.pass_rows + row;
     float m_max = -INFINITY;
-    for (int k = ga; k <= gb; ++k)
-      m_max = fmaxf(m_max,
-                    a.ws_ml[(((((int64_t)k + v) * a.num_kv_heads + g) * PG + w) * a.pass_rows + row) * 2]);
-#pragma unroll 4
-    for (int k = ga; k <= gb; ++k) {
-      const int64_t r = ((((int64_t)k + v) * a.num_kv_heads + g) * PG + w) * a.pass_rows + row;
-      const float m = a.ws_ml[r * 2], l = a.ws_ml[r * 2 + 1];
-      const float4 o = reinterpret_cast<const float4 *>(a.ws_o + r * D)[q4];
-      const float w = l > 0.f ? l * fast_exp2(m - m_max) : 0.f;
-      wsum += w;
-      acc.x += w * o.x;
-      acc.y += w * o.y;
-      acc.z += w * o.z;
-      acc.w += w * o.w;
+    for (int k0 = ga; k0 <= gb; k0 += kWin) {
+      const int cnt = min(kWin, gb - k0 + 1);
+      float mk[kWin], lk[kWin];
+      float4 ok[kWin];
+#pragma unroll
+      for (int u = 0; u < kWin; ++u) {
+        if (u < cnt) {
+          const int64_t r = r0 + (int64_t)(k0 - ga + u) * rstep;
+          mk[u] = a.ws_ml[r * 2];
+          lk[u] = a.ws_ml[r * 2 + 1];
+          ok[u] = reinterpret_cast<const float4 *>(a.ws_o + r * D)[q4];
+        } else {
+          mk[u] = -INFINITY;
+          lk[u] = 0.f;
+          ok[u] = make_float4(0.f, 0.f, 0.f, 0.f);
+        }
+      }
+      float m_new = m_max;
+#pragma unroll
+      for (int u = 0; u < kWin; ++u) m_new = fmaxf(m_new, mk[u]);
+      if (k0 > ga && m_new > m_max) {
+        const float f = fast_exp2(m_max - m_new);
+        wsum *= f;
+        acc.x *= f;
+        acc.y *= f;
+        acc.z *= f;
+        acc.w *= f;
+      }
+      m_max = m_new;
+#pragma unroll
+      for (int u = 0; u < kWin; ++u) {
+        if (u < cnt) {
+          const float wk = lk[u] > 0.f ? lk[u] * fast_exp2(mk[u] - m_max) : 0.f;
+          wsum += wk;
+          acc.x += wk * ok[u].x;
+          acc.y += wk * ok[u].y;
+          acc.z += wk * ok[u].z;
+          acc.w += wk * ok[u].w;
+        }
+      }
     }
   }
   const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
