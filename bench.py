@@ -2,8 +2,11 @@
 """Benchmark: paged decode attention on one MI355X.
 
 One step = the whole hot path over one batch: the cache write of every
-sequence's newest token (pa_reshape_and_cache) followed by single-token
-paged decode attention (pa_decode: stream-K kernel + combine kernel).
+sequence's newest token and single-token paged decode attention over the
+cache that holds it.  By default one pa_decode_append call does both (the
+stream-K kernel stores each new token just before it streams that tile,
+then the combine kernel); --step separate runs pa_reshape_and_cache, then
+pa_decode.
 Default workload: the LLaMA-2-70B-shaped batch (B 64, Hq 64, Hkv 8, D 128,
 bf16, 16-token blocks, mixed lengths 50..8000, shuffled physical blocks),
 seeded and synthetic, resident in HBM before the timed region starts;
@@ -62,8 +65,11 @@ def algorithmic_bytes(case) -> dict:
     qo = case.num_seqs * case.num_q_heads * case.head_dim * 2 * s_act
     tables = int(sum(-(-int(n) // case.block_size) for n in lens)) * 4 + case.num_seqs * 4
     write = case.num_seqs * case.num_kv_heads * case.head_dim * 2 * (s_act + s_kv)  # K and V rows in + codes out
+    # a decode call that also stores the new rows reads them once (from the
+    # inputs) and writes them once on top of the decode's own bytes
+    write_out = case.num_seqs * case.num_kv_heads * case.head_dim * 2 * s_kv
     return {"decode": kv_unique + qo + tables, "decode_logical": kv + qo + tables, "kv": kv,
-            "kv_unique": kv_unique, "write": write, "tokens": int(lens.sum())}
+            "kv_unique": kv_unique, "write": write, "write_out": write_out, "tokens": int(lens.sum())}
 
 
 def kernel_hash() -> str:
@@ -74,14 +80,15 @@ def kernel_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def read_traffic(config: str):
-    """Counter-derived HBM bytes per decode call, if taken on the current kernels."""
+def read_traffic(config: str, step: str):
+    """Counter-derived HBM bytes per decode call, if taken on the current
+    kernels with the same kind of step."""
     try:
         with open(traffic_file(config)) as fh:
             t = json.load(fh)
     except (OSError, ValueError):
         return None
-    if t.get("kernel_hash") != kernel_hash():
+    if t.get("kernel_hash") != kernel_hash() or t.get("step", "separate") != step:
         return None
     return t.get("bytes_per_call")
 
@@ -98,7 +105,8 @@ def summarize_counters(fetch_csv: str, write_csv: str, command: str) -> dict:
     ``bench.py --profile-calls N`` (FETCH_SIZE, then WRITE_SIZE; KiB per
     dispatch).  Each counter is scaled by what it reads for the 1 GiB copy
     that the profiled run ends with."""
-    out = {"kernel_hash": kernel_hash(), "command": command}
+    out = {"kernel_hash": kernel_hash(), "command": command,
+           "step": "separate" if "--step separate" in command else "fused"}
     per_kernel = {}
     for counter, path in (("FETCH_SIZE", fetch_csv), ("WRITE_SIZE", write_csv)):
         rows = [r for r in _counter_rows(path) if r["Counter_Name"] == counter]
@@ -685,6 +693,9 @@ def main() -> int:
     ap.add_argument("--launch", choices=("eager", "graph"), default="eager",
                     help="launch eagerly (default) or replay captured HIP graphs of the write and the "
                          "decode call (one replay each per step)")
+    ap.add_argument("--step", choices=("fused", "separate"), default="fused",
+                    help="fused (default): one pa_decode_append call stores the new tokens and decodes; "
+                         "separate: pa_reshape_and_cache, then pa_decode")
     ap.add_argument("--profile-calls", type=int, default=0,
                     help="only run this many decode calls, then a 1 GiB copy (for rocprofv3 counter runs)")
     ap.add_argument("--write-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
@@ -787,8 +798,17 @@ def main() -> int:
     ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
     torch.cuda.synchronize()
 
+    fused = args.step == "fused" and ring is None
+
     def decode():
-        pk.decode(pool, out, query, tables, lens, max_ctx, case.scale, ring=ring, workspace=ws)
+        if fused:  # stores the step's new tokens and decodes in one call
+            pk.decode_append(pool, out, query, step_keys, step_vals, step_slots_d, tables, lens, max_ctx,
+                             case.scale, workspace=ws)
+        else:
+            pk.decode(pool, out, query, tables, lens, max_ctx, case.scale, ring=ring, workspace=ws)
+
+    # algorithmic bytes of the call the events bracket
+    call_bytes = ab["decode"] + (ab["write_out"] if fused else 0)
 
     if args.profile_calls > 0:
         for _ in range(args.profile_calls):
@@ -805,7 +825,8 @@ def main() -> int:
         return 0
 
     def write():
-        pk.reshape_and_cache(pool, step_keys, step_vals, step_slots_d)
+        if not fused:
+            pk.reshape_and_cache(pool, step_keys, step_vals, step_slots_d)
 
     def step(ev_decode=None):
         write()
@@ -825,12 +846,15 @@ def main() -> int:
         side = torch.cuda.Stream()
         side.wait_stream(torch.cuda.current_stream())
         g_write, g_decode = torch.cuda.CUDAGraph(), torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g_write, stream=side):
-            write()
+        if not fused:
+            with torch.cuda.graph(g_write, stream=side):
+                write()
         with torch.cuda.graph(g_decode, stream=side):
             decode()
         torch.cuda.synchronize()
-        write, decode = g_write.replay, g_decode.replay
+        if not fused:
+            write = g_write.replay
+        decode = g_decode.replay
         for _ in range(max(1, args.warmup // 4)):
             step()
         torch.cuda.synchronize()
@@ -866,12 +890,21 @@ def main() -> int:
     step_bytes = ab["decode"] + ab["write"]
     value = step_bytes / (ms_per_step * 1e-3) / 1e9
     dec_avg_ms = statistics.mean(decode_ms)
-    achieved = ab["decode"] / (dec_avg_ms * 1e-3) / 1e9
-    traffic = read_traffic(args.config)
+    achieved = call_bytes / (dec_avg_ms * 1e-3) / 1e9
+    traffic = read_traffic(args.config, "fused" if fused else "separate")
     group = case.num_q_heads // case.num_kv_heads
     mfma = case.dtype != "f32" and 1 <= group <= 16 and os.environ.get("PA_FORCE_VALU", "0") in ("", "0")
-    kernel = ("pa_decode call: decode_mfma_kernel + decode_streamk_reduce_kernel" if mfma else
-              "pa_decode call: decode_valu_kernel (+ decode_reduce_kernel when a context is split)")
+    fused_launch = fused and mfma and case.kv_dtype != "fp8_e4m3"
+    if fused_launch:
+        kernel = ("pa_decode_append call: decode_mfma_kernel (variant that also stores the new tokens) + "
+                  "decode_streamk_reduce_kernel")
+    elif mfma:
+        kernel = ("pa_decode_append call: pa_reshape_and_cache + " if fused else "pa_decode call: ") + \
+            "decode_mfma_kernel + decode_streamk_reduce_kernel"
+    else:
+        kernel = ("pa_decode_append call: pa_reshape_and_cache + " if fused else "pa_decode call: ") + \
+            "decode_valu_kernel (+ decode_reduce_kernel when a context is split)"
+
     if args.config == "llama70b_b64":
         workload = ("llama70b_b64: paged decode, B 64, Hq 64, Hkv 8 (GQA 8), D 128, bf16 KV, "
                     "block 16, lengths 32xU[50,500] + 19xU[500,2000] + 13xU[2000,8000], "
@@ -903,7 +936,10 @@ def main() -> int:
             "num_blocks": case.num_blocks,
             "seed": case.seed,
             "kv_storage": "e4m3 codes, per-head scales" if case.kv_dtype == "fp8_e4m3" else case.dtype,
-            "launch": ("hip graph replay (cache write graph + decode call graph)" if args.launch == "graph"
+            "step": ("one pa_decode_append call (stores the new tokens, then attends)" if fused
+                     else "pa_reshape_and_cache, then pa_decode"),
+            "launch": (("hip graph replay of the call" if fused else
+                        "hip graph replay (cache write graph + decode call graph)") if args.launch == "graph"
                        else "eager launches"),
         },
         "tokens_per_s": round(case.num_seqs / (ms_per_step * 1e-3), 1),
@@ -913,7 +949,7 @@ def main() -> int:
                       "p10": round(float(np.percentile(decode_ms, 10)) * 1e3, 2),
                       "p90": round(float(np.percentile(decode_ms, 90)) * 1e3, 2)},
         "decode_cold_us": ({"median": round(statistics.median(cold_ms) * 1e3, 2),
-                            "gbs": round(ab["decode"] / (statistics.median(cold_ms) * 1e-3) / 1e9, 1)}
+                            "gbs": round(call_bytes / (statistics.median(cold_ms) * 1e-3) / 1e9, 1)}
                            if cold_ms else None),
         "roofline": {
             "bound": "hbm",
@@ -923,8 +959,8 @@ def main() -> int:
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
             "traffic": traffic,
-            "algorithmic_bytes": ab["decode"],
-            "algorithmic_bytes_logical": ab["decode_logical"],
+            "algorithmic_bytes": call_bytes,
+            "algorithmic_bytes_logical": ab["decode_logical"] + (ab["write_out"] if fused else 0),
         },
     }
     pool.close()

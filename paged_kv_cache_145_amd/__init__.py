@@ -17,7 +17,7 @@ from ._lib import PaRing
 
 __all__ = [
     "PaError", "Pool", "Ring", "ring_slot", "compute_slot_mapping", "reshape_and_cache",
-    "decode_workspace_bytes", "rope_table_bytes", "rope_table_init", "decode", "DTYPES",
+    "decode_workspace_bytes", "rope_table_bytes", "rope_table_init", "decode", "decode_append", "DTYPES",
     "block_hashes", "copy_blocks", "decode_multi_workspace_bytes", "decode_multi", "Batcher",
 ]
 
@@ -299,6 +299,35 @@ def decode(pool: Pool, out, query, block_tables, context_lens, max_context_len: 
         _dev_ptr(block_tables, "block_tables"), int(block_tables.shape[1]),
         _dev_ptr(context_lens, "context_lens"), b, hq, int(max_context_len), float(scale),
         _ring_ptr(ring), ws_ptr, ws_bytes, _stream_ptr(stream)), "pa_decode")
+
+
+def decode_append(pool: Pool, out, query, key, value, slot_mapping, block_tables, context_lens,
+                  max_context_len: int, scale: float, workspace=None, stream=None) -> None:
+    """One decode step that also stores each sequence's new token: key/value
+    [B, Hkv, D] go to slot_mapping [B] (the slot of position
+    context_lens[b] - 1) and ``out`` [B, Hq, D] is the decode attention over
+    the cache including them."""
+    b, hq, d = query.shape
+    if tuple(out.shape) != (b, hq, d) or d != pool.head_dim:
+        raise ValueError("out/query must be [B, Hq, D] with D = the pool's head size")
+    if query.dtype != pool.act_dtype or out.dtype != pool.act_dtype:
+        raise ValueError("query/out dtype must match the pool")
+    if key.dtype != pool.act_dtype or value.dtype != pool.act_dtype:
+        raise ValueError("key/value dtype must match the pool")
+    if tuple(key.shape) != (b, pool.num_kv_heads, d) or key.shape != value.shape:
+        raise ValueError("key/value must be [B, Hkv, D]")
+    if tuple(slot_mapping.shape) != (b,):
+        raise ValueError("slot_mapping must be [B]")
+    ws_ptr, ws_bytes = None, 0
+    if workspace is not None:
+        ws_ptr = _dev_ptr(workspace, "workspace")
+        ws_bytes = workspace.numel() * workspace.element_size()
+    _check(_lib.load().pa_decode_append(
+        pool.handle, _dev_ptr(out, "out"), _dev_ptr(query, "query"), _dev_ptr(key, "key"),
+        _dev_ptr(value, "value"), _dev_ptr(slot_mapping, "slot_mapping"),
+        _dev_ptr(block_tables, "block_tables"), int(block_tables.shape[1]),
+        _dev_ptr(context_lens, "context_lens"), b, hq, int(max_context_len), float(scale),
+        ws_ptr, ws_bytes, _stream_ptr(stream)), "pa_decode_append")
 
 
 def decode_multi_workspace_bytes(pool: Pool, num_seqs: int, q_len: int, num_q_heads: int,

@@ -294,10 +294,22 @@ int pa_rope_table_init(float *table, int32_t capacity, int32_t head_dim, float r
                                                    static_cast<hipStream_t>(stream)));
 }
 
-int pa_decode(pa_pool *pool, void *out, const void *query, const int32_t *block_tables,
-              int32_t max_blocks_per_seq, const int32_t *context_lens, int32_t num_seqs,
-              int32_t num_q_heads, int32_t max_context_len, float scale, const pa_ring *ring,
-              void *workspace, size_t workspace_bytes, void *stream) {
+}  // extern "C"
+
+namespace pa {
+namespace {
+
+// New tokens a decode call appends (one per sequence), or none.
+struct AppendInputs {
+  const void *key;
+  const void *value;
+  const int32_t *slots;
+};
+
+int decode_impl(pa_pool *pool, void *out, const void *query, const int32_t *block_tables,
+                int32_t max_blocks_per_seq, const int32_t *context_lens, int32_t num_seqs,
+                int32_t num_q_heads, int32_t max_context_len, float scale, const pa_ring *ring,
+                void *workspace, size_t workspace_bytes, void *stream, const AppendInputs *app) {
   if (pool == nullptr || num_seqs < 0 || num_q_heads <= 0 || max_context_len < 0 ||
       max_blocks_per_seq <= 0)
     return PA_ERR_INVAL;
@@ -370,9 +382,53 @@ int pa_decode(pa_pool *pool, void *out, const void *query, const int32_t *block_
                          ? 1
                          : (group + choice.heads_per_pass - 1) / choice.heads_per_pass;
   if ((int64_t)pool->num_kv_heads * nchunk > INT32_MAX) return PA_ERR_UNSUPPORTED;
+  if (app != nullptr) {
+    // the MFMA kernel appends in the same launch; other paths write first
+    const bool fused = choice.kernel == pa::DecodeKernel::kMfma && ring == nullptr && !pool->kv_fp8 &&
+                       pool->dtype != PA_F32;
+    if (fused) {
+      a.app_key = app->key;
+      a.app_value = app->value;
+      a.app_slots = app->slots;
+      a.num_slots = (int64_t)pool->num_blocks * pool->block_size;
+    } else {
+      const int rc = pa_reshape_and_cache(pool, app->key, app->value, app->slots, num_seqs, stream);
+      if (rc != PA_OK) return rc;
+    }
+  }
   return pa::hip_status(pa::launch_decode(a, pool->dtype, pool->head_dim, ring != nullptr,
                                           pool->kv_fp8, choice, num_seqs,
                                           static_cast<hipStream_t>(stream)));
+}
+
+}  // namespace
+}  // namespace pa
+
+extern "C" {
+
+int pa_decode(pa_pool *pool, void *out, const void *query, const int32_t *block_tables,
+              int32_t max_blocks_per_seq, const int32_t *context_lens, int32_t num_seqs,
+              int32_t num_q_heads, int32_t max_context_len, float scale, const pa_ring *ring,
+              void *workspace, size_t workspace_bytes, void *stream) {
+  return pa::decode_impl(pool, out, query, block_tables, max_blocks_per_seq, context_lens, num_seqs,
+                         num_q_heads, max_context_len, scale, ring, workspace, workspace_bytes, stream,
+                         nullptr);
+}
+
+int pa_decode_append(pa_pool *pool, void *out, const void *query, const void *key, const void *value,
+                     const int32_t *slot_mapping, const int32_t *block_tables, int32_t max_blocks_per_seq,
+                     const int32_t *context_lens, int32_t num_seqs, int32_t num_q_heads,
+                     int32_t max_context_len, float scale, void *workspace, size_t workspace_bytes,
+                     void *stream) {
+  if (pool == nullptr || num_seqs < 0) return PA_ERR_INVAL;
+  if (num_seqs == 0) return PA_OK;
+  if (key == nullptr || value == nullptr || slot_mapping == nullptr) return PA_ERR_INVAL;
+  if (!pa::aligned16(key) || !pa::aligned16(value)) return PA_ERR_INVAL;
+  if ((reinterpret_cast<uintptr_t>(slot_mapping) & 3u) != 0) return PA_ERR_INVAL;
+  const pa::AppendInputs app{key, value, slot_mapping};
+  return pa::decode_impl(pool, out, query, block_tables, max_blocks_per_seq, context_lens, num_seqs,
+                         num_q_heads, max_context_len, scale, nullptr, workspace, workspace_bytes, stream,
+                         &app);
 }
 
 }  // extern "C"

@@ -391,7 +391,9 @@ __device__ __forceinline__ void locate_tile(const int *s_tfirst, int num_seqs, i
 // 16-bit pools: one wave per SIMD (a memory-bound wave paired with an older
 // neighbour falls behind it).  8-bit pools halve the bytes per tile and the
 // per-tile arithmetic then dominates, so two waves per SIMD overlap it.
-template <class T, int D, bool RING, bool KV8>
+// APP: the launch also stores each sequence's new token (16-bit pools, no
+// ring); a separate instantiation, so plain decode carries none of it.
+template <class T, int D, bool RING, bool KV8, bool APP = false>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, KV8 ? 2 : 1)))
 void decode_mfma_kernel(DecodeArgs a) {
   constexpr int KB = D / 32;  // score MFMAs per tile
@@ -461,12 +463,74 @@ void decode_mfma_kernel(DecodeArgs a) {
   // (the same for K and V); tnrec: bytes the tile's valid rows span.
   int tb = 0, tt = 0, tvalid = 0, tflag = 0, toff_lo = 0, toff_hi = 0, tnrec = 0, tslot = 0;
   int c0 = 0, cnt = 0;
+  int app_hi = 0;  // tiles below this index had their new token stored
+
+  // Append (16-bit pools, no ring): the new token of a sequence sits in its
+  // last tile, and the wave that streams that tile for head g stores the
+  // token's K and V rows of head g (from the inputs) when it stages the
+  // tile, before any load of it: the wave's own later loads of those
+  // addresses are ordered after its stores, so the result equals a cache
+  // write followed by the decode.  A lane group of 2 * D * 2 / 16 lanes
+  // carries one sequence's two rows in 16-byte pieces (K first).
+  static_assert(!APP || (!KV8 && !RING), "appending needs a 16-bit pool without ring");
+  constexpr int kPiecesPerRow = D * (int)sizeof(st) / 16;
+  constexpr int kLanesPerEnd = 2 * kPiecesPerRow;
+  constexpr int kEndsPerRound = kWave / kLanesPerEnd;
+  constexpr int kAppRounds = 4;  // rounds whose loads are issued together
+  const int app_e = lane / kLanesPerEnd;
+  const bool app_v = lane % kLanesPerEnd >= kPiecesPerRow;
+  const int app_piece = lane % kPiecesPerRow;
+  // Loads the rows of the next kAppRounds * kEndsPerRound sequences ending in
+  // the staged chunk (bits of `em`, which are consumed); bsel = -1 where none.
+  auto app_load = [&](unsigned long long &em, u32x4 (&row)[kAppRounds], int (&slot)[kAppRounds],
+                      int (&bsel)[kAppRounds]) {
+#pragma unroll
+    for (int r = 0; r < kAppRounds; ++r) {
+      int bs = -1;
+#pragma unroll
+      for (int e = 0; e < kEndsPerRound; ++e) {
+        const int j = em ? __ffsll((long long)em) - 1 : -1;
+        em &= em - 1;
+        const int be = j >= 0 ? rd(tb, j) : -1;
+        if (e == app_e) bs = be;
+      }
+      const int b = max(bs, 0);  // in range for every lane
+      bsel[r] = bs;
+      slot[r] = a.app_slots[b];
+      const char *src = static_cast<const char *>(app_v ? a.app_value : a.app_key) +
+                        (((int64_t)b * hkv + g) * D) * (int64_t)sizeof(st) + 16 * app_piece;
+      row[r] = *reinterpret_cast<const u32x4 *>(src);
+    }
+  };
+  auto app_store = [&](const u32x4 (&row)[kAppRounds], const int (&slot)[kAppRounds],
+                       const int (&bsel)[kAppRounds]) {
+#pragma unroll
+    for (int r = 0; r < kAppRounds; ++r) {
+      if (bsel[r] >= 0 && slot[r] >= 0 && slot[r] < a.num_slots) {
+        char *dst = static_cast<char *>(const_cast<void *>(app_v ? a.v_cache : a.k_cache)) +
+                    (((int64_t)slot[r] * hkv + g) * D) * (int64_t)sizeof(st) + 16 * app_piece;
+        *reinterpret_cast<u32x4 *>(dst) = row[r];
+      }
+    }
+  };
+
   auto stage = [&](int start) {
     c0 = start;
     cnt = min(kWave, xend - start);
     tb = tt = tvalid = tflag = toff_lo = toff_hi = tnrec = 0;
     int tiles = 0;
     if (lane < cnt) locate_tile(s_tfirst, a.num_seqs, c0 + lane, tb, tt, tiles);
+    // new-token rows of the sequences ending in this chunk (not yet stored
+    // by an earlier, truncated chunk): requested first, so they have arrived
+    // by the time the block ids have
+    unsigned long long ends = 0;
+    u32x4 arow[kAppRounds];
+    int aslot[kAppRounds], absel[kAppRounds];
+    if constexpr (APP) {
+      ends = __ballot(lane < cnt && c0 + lane >= app_hi && tt == tiles - 1);
+      app_hi = c0 + cnt;
+      app_load(ends, arow, aslot, absel);
+    }
     const int r0 = kTileTokens * tt;
     // block id of the tile, loaded before the query fragments are fetched so
     // that both are in flight together (lanes past cnt read entry 0)
@@ -510,6 +574,15 @@ void decode_mfma_kernel(DecodeArgs a) {
       toff_lo = (int)(uint32_t)off;
       toff_hi = (int)(off >> 32);
       tnrec = (int)(((tvalid - 1) * row_stride + D) * KVB);  // tvalid >= 1 here
+    }
+    if constexpr (APP) {
+      app_store(arow, aslot, absel);
+      while (ends) {  // more sequence ends than one batch (short contexts)
+        app_load(ends, arow, aslot, absel);
+        app_store(arow, aslot, absel);
+      }
+      // keep the chunk's tile loads after the stores
+      __asm__ volatile("" ::: "memory");
     }
 #pragma unroll
     for (int s2 = 0; s2 < kQSlots; ++s2)
@@ -1065,7 +1138,12 @@ hipError_t launch_typed(const DecodeArgs &a, DecodeChoice choice, hipStream_t st
           kMaxPersistentWaves / kNW);
       // at least one group of Hkv waves
       const int grid = std::max(grid_max, (a.num_kv_heads + kNW - 1) / kNW);
-      hipLaunchKernelGGL((decode_mfma_kernel<T, D, RING, KV8>), dim3(grid), block, 0, stream, a);
+      if (a.app_key != nullptr) {
+        if constexpr (RING || KV8) return hipErrorInvalidValue;
+        else hipLaunchKernelGGL((decode_mfma_kernel<T, D, false, false, true>), dim3(grid), block, 0, stream, a);
+      } else {
+        hipLaunchKernelGGL((decode_mfma_kernel<T, D, RING, KV8>), dim3(grid), block, 0, stream, a);
+      }
       hipError_t err = hipGetLastError();
       if (err != hipSuccess) return err;
       hipLaunchKernelGGL((decode_streamk_reduce_kernel<T, D>),
@@ -1139,6 +1217,12 @@ hipError_t launch_decode(const DecodeArgs &args, pa_dtype dtype, int head_dim, b
     a.query = static_cast<const char *>(args.query) + qo * esz;
     a.block_tables = args.block_tables + (int64_t)s0 * a.max_blocks_per_seq;
     a.context_lens = args.context_lens + s0;
+    if (args.app_key != nullptr) {
+      const int64_t ko = (int64_t)s0 * a.num_kv_heads * head_dim;
+      a.app_key = static_cast<const char *>(args.app_key) + ko * esz;
+      a.app_value = static_cast<const char *>(args.app_value) + ko * esz;
+      a.app_slots = args.app_slots + s0;
+    }
     hipError_t err;
     switch (dtype) {
       case PA_F16: err = launch_dtype<F16>(a, head_dim, ring, kv_fp8, choice, stream); break;

@@ -9,6 +9,9 @@
 namespace pa {
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+// 16 bytes as a vector type: arrays of it stay in registers where arrays of
+// the uint4 struct can be placed in memory
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));

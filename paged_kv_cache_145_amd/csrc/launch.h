@@ -36,6 +36,13 @@ struct DecodeArgs {
   float *ws_o;   // partition-normalised outputs
   float *ws_ml;  // (running max in log2 units, sum)
   int32_t *ws_sched;  // MFMA kernel: tile prefix per sequence [B + 1]
+  // Append mode (MFMA kernel, plain paging, 16-bit pools): the new token of
+  // each sequence, key/value [B][Hkv][D], is written to app_slots[b] and
+  // attended from these inputs; the cache supplies the other L_b - 1 keys.
+  const void *app_key;
+  const void *app_value;
+  const int32_t *app_slots;
+  int64_t num_slots;  // num_blocks * block_size (slots past it are not written)
   const float *rope;  // float2 [S+W][D/2] or null
   int64_t kv_block_stride;  // elements per physical block (block_size * Hkv * D)
   int32_t num_seqs;    // sequences of this launch (at most the schedule capacity)

@@ -108,7 +108,6 @@ __global__ __launch_bounds__(256) void reshape_and_cache_fp8_kernel(
 constexpr int kCopyThreads = 256;
 constexpr int kCopyUnroll = 4;
 static_assert(kCopySegChunks == kCopyThreads * kCopyUnroll, "copy segment size");
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 __global__ __launch_bounds__(kCopyThreads) void copy_blocks_kernel(
     u32x4 *k_cache, u32x4 *v_cache, const int32_t *__restrict__ src_blocks,
