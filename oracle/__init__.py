@@ -36,10 +36,11 @@ Parity status of each function (what pins it is listed in the tests):
   resumption, refusals, invariants under random traffic).  Visiting order,
   allocation order and token positions are readings.
 * closed forms in ``sizes``: pinned against the numbers the pages print.
-* ``fp8`` (E4M3 values, nearest-even encoding with saturation, per-head
-  scaling) and ``quantize_for_cache``: pinned (codes worked by hand from the
-  format definition, every code round-trips, rounding is monotone and
-  nearest, ties go to the even code); the format and scaling rule are
+* ``fp8`` (E4M3 and E5M2 values, nearest-even encoding with saturation,
+  per-head scaling) and ``quantize_for_cache``: pinned (codes worked by hand
+  from the format definitions, every code round-trips, rounding is monotone
+  and nearest, ties go to the even code, E5M2 values equal IEEE binary16
+  numbers with the code as top byte); the formats and scaling rule are
   readings, the page names FP8 storage without fixing either.
 * ``prefix`` (chained FNV-1a block keys, the prefix index with token
   verification, copy-on-write, least-recent leaf eviction, block copy):

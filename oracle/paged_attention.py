@@ -175,8 +175,9 @@ def decode(query, k_pool, v_pool, block_tables, context_lens, scale, dtype, bloc
     [B, max_blocks] int; context_lens [B].  q head h reads KV head h // G with
     G = Hq / Hkv.  ``ring`` (object with sink, window, rope_base) switches to
     the sink + ring cache: the resident keys in cache order j = 0..L-1 are
-    rotated by j, the query by L - 1.  ``kv_dtype`` "fp8_e4m3": the pools hold
-    E4M3 codes whose values are scaled per KV head by k_scale / v_scale.
+    rotated by j, the query by L - 1.  ``kv_dtype`` "fp8_e4m3" / "fp8_e5m2":
+    the pools hold E4M3 / E5M2 codes whose values are scaled per KV head by
+    k_scale / v_scale.
     """
     q_all = to_f64(query, dtype)
     b_count, hq, d = q_all.shape
@@ -193,9 +194,10 @@ def decode(query, k_pool, v_pool, block_tables, context_lens, scale, dtype, bloc
             idx = np.arange(n)
         else:
             idx = np.asarray(ring_cache_order(n, ring.sink, ring.window), dtype=np.int64)
-        if kv_dtype == "fp8_e4m3":
-            keys = fp8.dequantize_rows(gather_rows(k_pool, block_tables[b], idx, block_size), k_scale)
-            vals = fp8.dequantize_rows(gather_rows(v_pool, block_tables[b], idx, block_size), v_scale)
+        if kv_dtype in fp8.KV_FORMATS:
+            fmt = fp8.KV_FORMATS[kv_dtype]
+            keys = fp8.dequantize_rows(gather_rows(k_pool, block_tables[b], idx, block_size), k_scale, fmt)
+            vals = fp8.dequantize_rows(gather_rows(v_pool, block_tables[b], idx, block_size), v_scale, fmt)
         else:
             keys = to_f64(gather_rows(k_pool, block_tables[b], idx, block_size), dtype)  # [L, Hkv, D]
             vals = to_f64(gather_rows(v_pool, block_tables[b], idx, block_size), dtype)
@@ -242,9 +244,10 @@ def decode_multi(query, k_pool, v_pool, block_tables, context_lens, scale, dtype
             if n <= 0:
                 continue
             idx = np.arange(n)
-            if kv_dtype == "fp8_e4m3":
-                keys = fp8.dequantize_rows(gather_rows(k_pool, block_tables[b], idx, block_size), k_scale)
-                vals = fp8.dequantize_rows(gather_rows(v_pool, block_tables[b], idx, block_size), v_scale)
+            if kv_dtype in fp8.KV_FORMATS:
+                fmt = fp8.KV_FORMATS[kv_dtype]
+                keys = fp8.dequantize_rows(gather_rows(k_pool, block_tables[b], idx, block_size), k_scale, fmt)
+                vals = fp8.dequantize_rows(gather_rows(v_pool, block_tables[b], idx, block_size), v_scale, fmt)
             else:
                 keys = to_f64(gather_rows(k_pool, block_tables[b], idx, block_size), dtype)
                 vals = to_f64(gather_rows(v_pool, block_tables[b], idx, block_size), dtype)
@@ -289,9 +292,10 @@ def reshape_and_cache(k_pool, v_pool, keys, values, slot_mapping, block_size):
     return k_out, v_out
 
 
-def quantize_for_cache(rows_raw, act_dtype, scale) -> np.ndarray:
-    """E4M3 codes of raw activation rows [m, Hkv, D] (f16/bf16/f32 storage)."""
-    return fp8.quantize_rows(to_f64(rows_raw, act_dtype).astype(np.float32), scale)
+def quantize_for_cache(rows_raw, act_dtype, scale, kv_dtype: str = "fp8_e4m3") -> np.ndarray:
+    """8-bit codes (E4M3 or E5M2, by ``kv_dtype``) of raw activation rows
+    [m, Hkv, D] (f16/bf16/f32 storage)."""
+    return fp8.quantize_rows(to_f64(rows_raw, act_dtype).astype(np.float32), scale, fp8.KV_FORMATS[kv_dtype])
 
 
 def build_pools(case):
@@ -313,9 +317,9 @@ def build_pools(case):
             slots.append(slot_of(row, r, case.block_size))
         slots = np.asarray(slots, dtype=np.int64)
         keys, values = ch.keys, ch.values
-        if getattr(case, "kv_dtype", None) == "fp8_e4m3":
-            keys = quantize_for_cache(keys, case.dtype, case.k_scale)
-            values = quantize_for_cache(values, case.dtype, case.v_scale)
+        if getattr(case, "kv_dtype", None) in fp8.KV_FORMATS:
+            keys = quantize_for_cache(keys, case.dtype, case.k_scale, case.kv_dtype)
+            values = quantize_for_cache(values, case.dtype, case.v_scale, case.kv_dtype)
         reshape_and_cache_(k_pool, v_pool, keys, values, slots, case.block_size)
         slot_lists.append(slots)
     return k_pool, v_pool, slot_lists

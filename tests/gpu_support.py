@@ -63,7 +63,7 @@ class DeviceCase:
         self.device = device
         dt = case.dtype
         shape = (case.num_blocks, case.block_size, case.num_kv_heads, case.head_dim)
-        if case.kv_dtype == "fp8_e4m3":
+        if workloads.is_kv8(case.kv_dtype):
             self.k_cache = torch.full(shape, workloads.FP8_NAN_CODE, dtype=torch.uint8, device=device)
             self.v_cache = torch.full(shape, workloads.FP8_NAN_CODE, dtype=torch.uint8, device=device)
             self.pool = pk.Pool(self.k_cache, self.v_cache, case.block_size, act_dtype=TORCH_DTYPES[dt],

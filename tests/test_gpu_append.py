@@ -60,7 +60,7 @@ def _append(dc, case, slots, keys, vals, max_ctx=None):
 
 
 def _same_pools(a, b, dtype):
-    view = torch.uint8 if a.case.kv_dtype == "fp8_e4m3" else INT_VIEW[dtype]
+    view = torch.uint8 if workloads.is_kv8(a.case.kv_dtype) else INT_VIEW[dtype]
     assert torch.equal(a.k_cache.view(view), b.k_cache.view(view)), "key pool differs"
     assert torch.equal(a.v_cache.view(view), b.v_cache.view(view)), "value pool differs"
 

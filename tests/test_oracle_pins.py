@@ -542,16 +542,119 @@ def test_e4m3_rounding_is_to_a_neighbour_within_half_a_step():
         assert abs(got - a) <= step / 2 + 1e-300
 
 
-def test_fp8_decode_equals_attention_on_dequantised_pools():
-    """The fp8 path of decode is attention on scale[h] * value(code): build a
-    float64 pool from the codes by hand and compare."""
+# ---------------------------------------------------------------------------
+# FP8 (E5M2) KV storage
+# ---------------------------------------------------------------------------
+
+def _e5m2_golden():
+    rows = []
+    with open(os.path.join(GOLDEN, "e5m2_codes.txt")) as fh:
+        for line in fh:
+            line = line.strip()
+            if not line or line.startswith("#"):
+                continue
+            x, code, value = line.split()[:3]
+            rows.append((float(x), int(code, 16), float(value)))
+    return rows
+
+
+def test_e5m2_codes_worked_by_hand():
     from oracle import fp8
 
-    case = workloads.config_fp8(workloads.config_tiny_fp32)
+    rows = _e5m2_golden()
+    assert len(rows) >= 25
+    for x, code, value in rows:
+        assert fp8.e5m2_encode_one(np.float32(x)) == code, (x, hex(code))
+        got = fp8.e5m2_value(code)
+        assert got == value or (got == 0.0 and value == 0.0 and np.signbit(got) == np.signbit(value)), (x, got)
+    for c in (0x7D, 0x7E, 0x7F, 0xFD, 0xFE, 0xFF):
+        assert np.isnan(fp8.e5m2_value(c))
+    assert fp8.e5m2_value(0x7C) == np.inf and fp8.e5m2_value(0xFC) == -np.inf
+    assert fp8.e5m2_encode_one(np.float32("nan")) == 0x7F
+
+
+def test_e5m2_is_the_top_byte_of_ieee_half():
+    """E5M2 shares binary16's sign, exponent width and bias; its 2 mantissa
+    bits are binary16's top 2.  So code c is the half-precision number with
+    bits c << 8 (numpy's float16, an independent implementation of IEEE
+    binary16), for every code: zeros, subnormals, normals, infinities, NaN."""
+    from oracle import fp8
+
+    halves = (np.arange(256, dtype=np.uint16) << 8).view(np.float16).astype(np.float64)
+    for c in range(256):
+        h, v = halves[c], fp8.e5m2_value(c)
+        assert (np.isnan(h) and np.isnan(v)) or (h == v and np.signbit(h) == np.signbit(v)), (hex(c), h, v)
+
+
+def test_e5m2_every_finite_code_round_trips_and_order_is_kept():
+    from oracle import fp8
+
+    finite = [c for c in range(256) if np.isfinite(fp8.e5m2_value(c))]
+    assert len(finite) == 248  # 256 - 2 infinities - 6 NaNs
+    for c in finite:
+        assert fp8.e5m2_value(fp8.e5m2_encode_one(np.float32(fp8.e5m2_value(c)))) == fp8.e5m2_value(c)
+    pos = [fp8.e5m2_value(c) for c in range(0x7C)]
+    assert all(a < b for a, b in zip(pos, pos[1:]))
+    rng = np.random.default_rng(17)
+    xs = np.sort(rng.uniform(-60000, 60000, 4000).astype(np.float32))
+    dec = fp8.e5m2_decode(fp8.e5m2_encode(xs))
+    assert np.all(np.diff(dec) >= 0)
+
+
+def test_e5m2_array_encoder_equals_the_scalar_search():
+    from oracle import fp8
+
+    rng = np.random.default_rng(19)
+    mags = fp8._E5M2_MAGNITUDES
+    xs = np.concatenate([rng.uniform(-60000, 60000, 3000), rng.normal(0, 0.02, 3000),
+                         rng.normal(0, 1e-4, 1000),
+                         fp8.E5M2_TABLE[np.isfinite(fp8.E5M2_TABLE)],
+                         (mags[:-1] + mags[1:]) / 2,  # every midpoint (ties)
+                         [0.0, -0.0, 57344.0, 61440.0, -1e9, np.inf, -np.inf, np.nan]]).astype(np.float32)
+    got = fp8.e5m2_encode(xs)
+    want = np.array([fp8.e5m2_encode_one(v) for v in xs], dtype=np.uint8)
+    assert np.array_equal(got, want)
+
+
+def test_e5m2_rounding_is_to_a_neighbour_within_half_a_step():
+    """Independent of the encoder's search: one of the two representable
+    neighbours (spacing 2^(e-2), subnormal spacing 2^-16), within half a
+    step; the tie goes to the even code."""
+    from oracle import fp8
+
+    rng = np.random.default_rng(18)
+    xs = np.concatenate([rng.uniform(-57344, 57344, 3000), rng.normal(0, 0.01, 1000),
+                         rng.normal(0, 3e-5, 1000)]).astype(np.float32)
+    for x in xs:
+        a = abs(float(x))
+        step = 2.0 ** -16 if a < 2.0 ** -14 else 2.0 ** (np.floor(np.log2(a)) - 2)
+        lo = np.floor(a / step) * step
+        code = fp8.e5m2_encode_one(x)
+        got = abs(fp8.e5m2_value(code))
+        assert got in (lo, lo + step), (x, got)
+        assert abs(got - a) <= step / 2
+        if abs(got - a) == step / 2:
+            assert code % 2 == 0, (x, hex(code))
+
+
+@pytest.mark.parametrize("kv_format", ["e4m3", "e5m2"])
+def test_fp8_decode_equals_attention_on_dequantised_pools(kv_format):
+    """The fp8 path of decode is attention on scale[h] * value(code): build a
+    float64 pool from the codes by hand and compare (E5M2 values through
+    numpy's binary16, of which E5M2 is the top byte)."""
+    from oracle import fp8
+
+    case = workloads.config_fp8(workloads.config_tiny_fp32, kv_format=kv_format)
     kp, vp, _ = oracle.build_pools(case)
     assert kp.dtype == np.uint8
-    ref_k = fp8.E4M3_TABLE[kp] * case.k_scale.astype(np.float64)[None, None, :, None]
-    ref_v = fp8.E4M3_TABLE[vp] * case.v_scale.astype(np.float64)[None, None, :, None]
+    if kv_format == "e4m3":
+        table = fp8.E4M3_TABLE
+        encode_one = fp8.e4m3_encode_one
+    else:
+        table = (np.arange(256, dtype=np.uint16) << 8).view(np.float16).astype(np.float64)
+        encode_one = fp8.e5m2_encode_one
+    ref_k = table[kp] * case.k_scale.astype(np.float64)[None, None, :, None]
+    ref_v = table[vp] * case.v_scale.astype(np.float64)[None, None, :, None]
     got = oracle.decode(case.query, kp, vp, case.block_tables, case.context_lens, case.scale, case.dtype,
                         case.block_size, kv_dtype=case.kv_dtype, k_scale=case.k_scale, v_scale=case.v_scale)
     q = oracle.to_f64(case.query, case.dtype)
@@ -564,11 +667,12 @@ def test_fp8_decode_equals_attention_on_dequantised_pools():
             s = case.scale * rows_k[:, h // g, :] @ q[b, h]
             p = np.exp(s - s.max())
             np.testing.assert_allclose(got[b, h], (p / p.sum()) @ rows_v[:, h // g, :], rtol=0, atol=1e-12)
-    # the quantisation is a float32 product with 1/scale, then nearest-even E4M3
+    # the quantisation is a float32 product with 1/scale, then the nearest
+    # code (ties to even) of the format
     ch = case.writes[0]
     x = oracle.to_f64(ch.keys, case.dtype).astype(np.float32)
     inv = (np.float32(1) / case.k_scale.astype(np.float32)).astype(np.float32)
-    codes = oracle.quantize_for_cache(ch.keys, case.dtype, case.k_scale)
+    codes = oracle.quantize_for_cache(ch.keys, case.dtype, case.k_scale, case.kv_dtype)
     for idx in [(0, 0, 0), (3, 1, 17), (10, 1, 63)]:
         prod = np.float32(x[idx] * inv[idx[1]])
-        assert codes[idx] == fp8.e4m3_encode_one(prod)
+        assert codes[idx] == encode_one(prod)

@@ -37,9 +37,17 @@ import numpy as np
 SEED_BASE = 145_000
 
 RAW_DTYPES = {"f32": np.float32, "f16": np.float16, "bf16": np.uint16}
-FP8_NAN_CODE = 0x7F  # E4M3 NaN (S.1111.111)
+FP8_NAN_CODE = 0x7F  # NaN in both 8-bit formats (E4M3 S.1111.111, E5M2 S.11111.11)
 ELEM_BYTES = {"f32": 4, "f16": 2, "bf16": 2}
 NAN_BITS = {"f32": 0x7FC00000, "f16": 0x7E00, "bf16": 0x7FC0}
+
+
+KV8_DTYPES = ("fp8_e4m3", "fp8_e5m2")
+
+
+def is_kv8(kv_dtype) -> bool:
+    """True for the 8-bit KV storage types."""
+    return kv_dtype in KV8_DTYPES
 
 
 def round_f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
@@ -110,7 +118,7 @@ class DecodeCase:
     ring: Optional[RingSpec] = None
     pad_block: int = -1  # block id used for table padding (-1: none)
     notes: dict = field(default_factory=dict)
-    # 8-bit KV storage: "fp8_e4m3" pools hold codes, dequantised per KV head
+    # 8-bit KV storage: "fp8_e4m3" / "fp8_e5m2" pools hold codes, dequantised per KV head
     # by k_scale / v_scale (float32 [Hkv]); ``dtype`` is then the dtype of
     # the query, the output and the key/value rows handed to the cache write
     kv_dtype: Optional[str] = None
@@ -131,7 +139,7 @@ class DecodeCase:
 
     def empty_pool(self) -> np.ndarray:
         shape = (self.num_blocks, self.block_size, self.num_kv_heads, self.head_dim)
-        if self.kv_dtype == "fp8_e4m3":
+        if is_kv8(self.kv_dtype):
             return np.full(shape, FP8_NAN_CODE, dtype=np.uint8)
         return nan_array(shape, self.dtype)
 
@@ -452,17 +460,20 @@ def _requantise_f32(case: DecodeCase) -> DecodeCase:
     return case
 
 
-def config_fp8(base=None, **kw) -> DecodeCase:
-    """A workload with 8-bit (E4M3) KV storage: the base configuration's
-    lengths, placement and values, the pools holding scaled E4M3 codes."""
+def config_fp8(base=None, kv_format: str = "e4m3", **kw) -> DecodeCase:
+    """A workload with 8-bit KV storage (``kv_format`` "e4m3" or "e5m2"):
+    the base configuration's lengths, placement and values, the pools
+    holding scaled codes of that format."""
+    if kv_format not in ("e4m3", "e5m2"):
+        raise ValueError(f"unknown 8-bit format {kv_format!r}")
     case = (base or config_llama70b)(**kw)
     if case.ring is not None:
         raise ValueError("8-bit KV storage is not combined with the ring cache")
     if case.dtype == "f32":
         case = _requantise_f32(case)
-    case.kv_dtype = "fp8_e4m3"
+    case.kv_dtype = "fp8_" + kv_format
     case.k_scale, case.v_scale = fp8_scales(case.num_kv_heads)
-    case.name = case.name + "_fp8"
+    case.name = case.name + ("_fp8" if kv_format == "e4m3" else "_e5m2")
     return case
 
 
@@ -586,7 +597,7 @@ class PrefixScenario:
 
     def empty_pool(self) -> np.ndarray:
         shape = (self.num_blocks, self.block_size, self.num_kv_heads, self.head_dim)
-        if self.kv_dtype == "fp8_e4m3":
+        if is_kv8(self.kv_dtype):
             return np.full(shape, FP8_NAN_CODE, dtype=np.uint8)
         return nan_array(shape, self.dtype)
 
