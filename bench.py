@@ -41,11 +41,16 @@ DECODE_KERNELS = ("decode_mfma_kernel", "decode_streamk_reduce_kernel")
 CALIBRATION_BYTES = 1 << 30  # the plain copy run after the profiled decode calls
 
 
+def workloads_is_kv8(kv_dtype) -> bool:
+    """8-bit KV storage types (E4M3 or E5M2 codes)."""
+    return kv_dtype in ("fp8_e4m3", "fp8_e5m2")
+
+
 def algorithmic_bytes(case) -> dict:
     """Bytes the decode must move at minimum: every resident K and V row once,
     query in, output out, block-table entries and lengths."""
     s_act = {"f32": 4, "f16": 2, "bf16": 2}[case.dtype]
-    s_kv = 1 if getattr(case, "kv_dtype", None) == "fp8_e4m3" else s_act
+    s_kv = 1 if workloads_is_kv8(getattr(case, "kv_dtype", None)) else s_act
     lens = case.context_lens.astype(np.int64)
     if case.ring is not None:
         lens = np.minimum(lens, case.ring.sink + case.ring.window)
@@ -410,7 +415,7 @@ def multi_costs(case) -> dict:
     row the longest query row of each sequence sees, once; the queries and
     outputs; table entries.  Flops: 4 * D per (query row, visible key)."""
     s = {"f32": 4, "f16": 2, "bf16": 2}[case.dtype]
-    s_kv = 1 if case.kv_dtype == "fp8_e4m3" else s
+    s_kv = 1 if workloads_is_kv8(case.kv_dtype) else s
     lens = case.context_lens.astype(np.int64)
     row = case.num_kv_heads * case.head_dim * 2 * s_kv
     kv = int(lens.sum()) * row
@@ -441,10 +446,11 @@ def measure_multi(args) -> int:
         return torch.from_numpy(np.ascontiguousarray(raw).view(raw_view)).view(tdt).to(dev)
 
     shape = (case.num_blocks, case.block_size, case.num_kv_heads, case.head_dim)
-    if case.kv_dtype == "fp8_e4m3":
+    if workloads_is_kv8(case.kv_dtype):
         k = torch.full(shape, workloads.FP8_NAN_CODE, dtype=torch.uint8, device=dev)
         v = torch.full(shape, workloads.FP8_NAN_CODE, dtype=torch.uint8, device=dev)
-        pool = pk.Pool(k, v, case.block_size, act_dtype=tdt, k_scale=case.k_scale, v_scale=case.v_scale)
+        pool = pk.Pool(k, v, case.block_size, act_dtype=tdt, k_scale=case.k_scale, v_scale=case.v_scale,
+                       kv_format=case.kv_dtype[4:])
     else:
         k, v = _nan_pools(workloads, torch, shape, case.dtype, dev)
         pool = pk.Pool(k, v, case.block_size)
@@ -757,11 +763,11 @@ def main() -> int:
         return torch.from_numpy(np.ascontiguousarray(raw).view(raw_view)).view(tdt).to(dev)
 
     shape = (case.num_blocks, case.block_size, case.num_kv_heads, case.head_dim)
-    if case.kv_dtype == "fp8_e4m3":
+    if workloads_is_kv8(case.kv_dtype):
         k_cache = torch.full(shape, workloads.FP8_NAN_CODE, dtype=torch.uint8, device=dev)
         v_cache = torch.full(shape, workloads.FP8_NAN_CODE, dtype=torch.uint8, device=dev)
         pool = pk.Pool(k_cache, v_cache, case.block_size, act_dtype=tdt, k_scale=case.k_scale,
-                       v_scale=case.v_scale)
+                       v_scale=case.v_scale, kv_format=case.kv_dtype[4:])
     else:
         k_cache = torch.empty(shape, dtype=tdt, device=dev)
         v_cache = torch.empty(shape, dtype=tdt, device=dev)
@@ -798,7 +804,12 @@ def main() -> int:
     ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
     torch.cuda.synchronize()
 
-    fused = args.step == "fused" and ring is None
+    group = case.num_q_heads // case.num_kv_heads
+    # the one-call step is a single launch on 16-bit pools with groups up to
+    # 16 and no ring; elsewhere the library would run the two calls in turn,
+    # so the bench times them as two calls
+    mfma = case.dtype != "f32" and 1 <= group <= 16 and os.environ.get("PA_FORCE_VALU", "0") in ("", "0")
+    fused = args.step == "fused" and ring is None and mfma and not workloads_is_kv8(case.kv_dtype)
 
     def decode():
         if fused:  # stores the step's new tokens and decodes in one call
@@ -892,25 +903,21 @@ def main() -> int:
     dec_avg_ms = statistics.mean(decode_ms)
     achieved = call_bytes / (dec_avg_ms * 1e-3) / 1e9
     traffic = read_traffic(args.config, "fused" if fused else "separate")
-    group = case.num_q_heads // case.num_kv_heads
-    mfma = case.dtype != "f32" and 1 <= group <= 16 and os.environ.get("PA_FORCE_VALU", "0") in ("", "0")
-    fused_launch = fused and mfma and case.kv_dtype != "fp8_e4m3"
-    if fused_launch:
+    if fused:
         kernel = ("pa_decode_append call: decode_mfma_kernel (variant that also stores the new tokens) + "
                   "decode_streamk_reduce_kernel")
     elif mfma:
-        kernel = ("pa_decode_append call: pa_reshape_and_cache + " if fused else "pa_decode call: ") + \
-            "decode_mfma_kernel + decode_streamk_reduce_kernel"
+        kernel = "pa_decode call: decode_mfma_kernel + decode_streamk_reduce_kernel"
     else:
-        kernel = ("pa_decode_append call: pa_reshape_and_cache + " if fused else "pa_decode call: ") + \
-            "decode_valu_kernel (+ decode_reduce_kernel when a context is split)"
+        kernel = "pa_decode call: decode_valu_kernel (+ decode_reduce_kernel when a context is split)"
 
     if args.config == "llama70b_b64":
         workload = ("llama70b_b64: paged decode, B 64, Hq 64, Hkv 8 (GQA 8), D 128, bf16 KV, "
                     "block 16, lengths 32xU[50,500] + 19xU[500,2000] + 13xU[2000,8000], "
                     "shuffled blocks, pool 1.1x need")
     else:
-        kv_name = "E4M3 (8-bit, per-head scales)" if case.kv_dtype == "fp8_e4m3" else case.dtype
+        kv_name = (f"{case.kv_dtype[4:].upper()} (8-bit, per-head scales)" if workloads_is_kv8(case.kv_dtype)
+                   else case.dtype)
         workload = (f"{args.config}: paged decode, B {case.num_seqs}, Hq {case.num_q_heads}, "
                     f"Hkv {case.num_kv_heads}, D {case.head_dim}, {kv_name} KV, {case.dtype} query, "
                     f"block {case.block_size}"
@@ -935,7 +942,8 @@ def main() -> int:
             "max_context_len": max_ctx,
             "num_blocks": case.num_blocks,
             "seed": case.seed,
-            "kv_storage": "e4m3 codes, per-head scales" if case.kv_dtype == "fp8_e4m3" else case.dtype,
+            "kv_storage": (f"{case.kv_dtype[4:]} codes, per-head scales" if workloads_is_kv8(case.kv_dtype)
+                           else case.dtype),
             "step": ("one pa_decode_append call (stores the new tokens, then attends)" if fused
                      else "pa_reshape_and_cache, then pa_decode"),
             "launch": (("hip graph replay of the call" if fused else

@@ -63,9 +63,10 @@ typedef enum {
   PA_ERR_UNSUPPORTED = -5  /* a combination the library has no kernel for */
 } pa_status;
 
-/* PA_FP8_E4M3 is a storage type of K/V pools only: such pools are made by
- * pa_create_pool_fp8, and pa_create_pool rejects it. */
-typedef enum { PA_F32 = 0, PA_F16 = 1, PA_BF16 = 2, PA_FP8_E4M3 = 3 } pa_dtype;
+/* PA_FP8_E4M3 and PA_FP8_E5M2 are storage types of K/V pools only: such
+ * pools are made by pa_create_pool_kv8 (or pa_create_pool_fp8 for E4M3), and
+ * pa_create_pool rejects them. */
+typedef enum { PA_F32 = 0, PA_F16 = 1, PA_BF16 = 2, PA_FP8_E4M3 = 3, PA_FP8_E5M2 = 4 } pa_dtype;
 
 /* Opaque pool handle: host-side state only (shapes, free list, refcounts). */
 typedef struct pa_pool pa_pool;
@@ -113,11 +114,26 @@ int pa_create_pool(pa_pool **out, int32_t num_blocks, int32_t block_size, int32_
  * nearest-even E4M3 codes of fp32(x) * fp32(1 / scale[h]), saturating at
  * +-448.  k_scale, v_scale: host float [num_kv_heads], finite and > 0,
  * copied into the handle; num_kv_heads <= 64.  Decode on such a pool needs
- * 4 <= Hq / Hkv <= 16 and no ring (else PA_ERR_UNSUPPORTED).  Other
- * arguments and errors as pa_create_pool. */
+ * 1 <= Hq / Hkv <= 16 and no ring (else PA_ERR_UNSUPPORTED).  Other
+ * arguments and errors as pa_create_pool.  Same as pa_create_pool_kv8 with
+ * kv_dtype = PA_FP8_E4M3. */
 int pa_create_pool_fp8(pa_pool **out, int32_t num_blocks, int32_t block_size,
                        int32_t num_kv_heads, int32_t head_dim, pa_dtype act_dtype,
                        const float *k_scale, const float *v_scale, void *k_cache, void *v_cache);
+
+/* Pools of 8-bit K/V in either OCP 8-bit float format [P4, section
+ * "工程边界与架构取舍"; the page names FP8 storage without fixing a
+ * format]: kv_dtype PA_FP8_E4M3 (as pa_create_pool_fp8) or PA_FP8_E5M2
+ * (5 exponent bits, bias 15, 2 mantissa bits; exponent field 0 subnormal,
+ * 31 infinity or NaN; largest finite 57344 = 1.75 * 2^15; the code is the
+ * top byte of the IEEE binary16 number it stands for).  pa_reshape_and_cache
+ * stores nearest-even codes of fp32(x) * fp32(1 / scale[h]) in that format,
+ * magnitudes beyond the largest finite one (infinities too) saturating to
+ * it, NaN to 0x7F.  Everything else as pa_create_pool_fp8; PA_ERR_INVAL for
+ * any other kv_dtype. */
+int pa_create_pool_kv8(pa_pool **out, int32_t num_blocks, int32_t block_size, int32_t num_kv_heads,
+                       int32_t head_dim, pa_dtype kv_dtype, pa_dtype act_dtype, const float *k_scale,
+                       const float *v_scale, void *k_cache, void *v_cache);
 
 /* Free the host-side state (NULL is a no-op).  Device memory is untouched. */
 void pa_destroy_pool(pa_pool *pool);

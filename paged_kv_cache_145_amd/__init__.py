@@ -22,6 +22,7 @@ __all__ = [
 ]
 
 DTYPES = {"f32": _lib.PA_F32, "f16": _lib.PA_F16, "bf16": _lib.PA_BF16}
+KV8_FORMATS = {"e4m3": _lib.PA_FP8_E4M3, "e5m2": _lib.PA_FP8_E5M2}
 
 
 class PaError(RuntimeError):
@@ -80,11 +81,12 @@ def _ring_ptr(ring: Optional[Ring]):
 class Pool:
     """One layer's paged K/V pools (caller-owned device tensors) + allocator."""
 
-    def __init__(self, k_cache, v_cache, block_size: int, act_dtype=None, k_scale=None, v_scale=None):
-        """``k_cache``/``v_cache`` of dtype uint8 make an 8-bit (E4M3) pool:
-        ``act_dtype`` (torch.float16 / torch.bfloat16) is then the dtype of
-        queries, outputs and written rows, and ``k_scale``/``v_scale`` hold
-        one float per KV head."""
+    def __init__(self, k_cache, v_cache, block_size: int, act_dtype=None, k_scale=None, v_scale=None,
+                 kv_format: str = "e4m3"):
+        """``k_cache``/``v_cache`` of dtype uint8 make an 8-bit pool of codes
+        in ``kv_format`` ("e4m3" or "e5m2"): ``act_dtype`` (torch.float16 /
+        torch.bfloat16) is then the dtype of queries, outputs and written
+        rows, and ``k_scale``/``v_scale`` hold one float per KV head."""
         import torch
 
         lib = _lib.load()
@@ -106,12 +108,16 @@ class Pool:
             vs = np.ascontiguousarray(v_scale, dtype=np.float32)
             if ks.shape != (hkv,) or vs.shape != (hkv,):
                 raise ValueError("k_scale and v_scale need one value per KV head")
+            if kv_format not in KV8_FORMATS:
+                raise ValueError(f"kv_format must be one of {sorted(KV8_FORMATS)}")
+            self.kv_format = kv_format
             fp = ctypes.POINTER(ctypes.c_float)
-            _check(lib.pa_create_pool_fp8(ctypes.byref(handle), num_blocks, bs, hkv, d, DTYPES[self.dtype],
-                                          ks.ctypes.data_as(fp), vs.ctypes.data_as(fp),
+            _check(lib.pa_create_pool_kv8(ctypes.byref(handle), num_blocks, bs, hkv, d, KV8_FORMATS[kv_format],
+                                          DTYPES[self.dtype], ks.ctypes.data_as(fp), vs.ctypes.data_as(fp),
                                           _dev_ptr(k_cache, "k_cache"), _dev_ptr(v_cache, "v_cache")),
-                   "pa_create_pool_fp8")
+                   "pa_create_pool_kv8")
         else:
+            self.kv_format = None
             self.act_dtype = k_cache.dtype
             self.dtype = _torch_dtype_name(k_cache)
             _check(lib.pa_create_pool(ctypes.byref(handle), num_blocks, bs, hkv, d, DTYPES[self.dtype],

@@ -18,7 +18,7 @@ PA_ERR_STATE = -3
 PA_ERR_HIP = -4
 PA_ERR_UNSUPPORTED = -5
 
-PA_F32, PA_F16, PA_BF16, PA_FP8_E4M3 = 0, 1, 2, 3
+PA_F32, PA_F16, PA_BF16, PA_FP8_E4M3, PA_FP8_E5M2 = 0, 1, 2, 3, 4
 
 
 class PaPoolStats(ctypes.Structure):
@@ -56,6 +56,9 @@ _sz = ctypes.c_size_t
 SIGNATURES = {
     "pa_create_pool": (ctypes.c_int, [ctypes.POINTER(_p), _i32, _i32, _i32, _i32, ctypes.c_int, _p, _p]),
     "pa_create_pool_fp8": (ctypes.c_int, [ctypes.POINTER(_p), _i32, _i32, _i32, _i32, ctypes.c_int,
+                                          ctypes.POINTER(ctypes.c_float), ctypes.POINTER(ctypes.c_float),
+                                          _p, _p]),
+    "pa_create_pool_kv8": (ctypes.c_int, [ctypes.POINTER(_p), _i32, _i32, _i32, _i32, ctypes.c_int, ctypes.c_int,
                                           ctypes.POINTER(ctypes.c_float), ctypes.POINTER(ctypes.c_float),
                                           _p, _p]),
     "pa_destroy_pool": (None, [_p]),

@@ -12,6 +12,13 @@
 namespace pa {
 namespace {
 
+// Kernel-side format of a pool's K/V storage: 0 for 16-bit (or fp32) rows,
+// kKvE4M3 / kKvE5M2 for 8-bit codes.
+int kv8_format(const pa_pool *pool) {
+  if (!pool->kv_fp8) return 0;
+  return pool->kv_dtype == PA_FP8_E5M2 ? kKvE5M2 : kKvE4M3;
+}
+
 thread_local std::string g_last_hip_error;
 
 int hip_status(hipError_t err) {
@@ -165,7 +172,7 @@ int pa_reshape_and_cache(pa_pool *pool, const void *key, const void *value,
       inv.v[h] = pool->v_inv[h];
     }
     return pa::hip_status(pa::launch_reshape_and_cache_fp8(
-        pool->dtype, pool->k_cache, pool->v_cache, key, value, slot_mapping, num_tokens,
+        pool->dtype, pa::kv8_format(pool), pool->k_cache, pool->v_cache, key, value, slot_mapping, num_tokens,
         pool->num_kv_heads, pool->head_dim, (int64_t)pool->num_blocks * pool->block_size, inv,
         static_cast<hipStream_t>(stream)));
   }
@@ -266,7 +273,7 @@ int pa_decode_multi(pa_pool *pool, void *out, const void *query, const int32_t *
     a.query = static_cast<const char *>(query) + s0 * row_elems * esize;
     a.block_tables = block_tables + (int64_t)s0 * max_blocks_per_seq;
     a.context_lens = context_lens + s0;
-    const int rc = pa::hip_status(pa::launch_decode_multi(a, pool->dtype, pool->head_dim, pool->kv_fp8, m.waves,
+    const int rc = pa::hip_status(pa::launch_decode_multi(a, pool->dtype, pool->head_dim, pa::kv8_format(pool), m.waves,
                                                           grid, static_cast<hipStream_t>(stream)));
     if (rc != PA_OK) return rc;
   }
@@ -397,7 +404,7 @@ int decode_impl(pa_pool *pool, void *out, const void *query, const int32_t *bloc
     }
   }
   return pa::hip_status(pa::launch_decode(a, pool->dtype, pool->head_dim, ring != nullptr,
-                                          pool->kv_fp8, choice, num_seqs,
+                                          pa::kv8_format(pool), choice, num_seqs,
                                           static_cast<hipStream_t>(stream)));
 }
 

@@ -238,8 +238,8 @@ struct V8Chunk<128> {
   static __device__ __forceinline__ uint2 load(__amdgpu_buffer_rsrc_t r, int off) {
     return buffer_load8(r, off);
   }
-  template <class T>
-  static __device__ __forceinline__ uint4 widen(const uint2 &v) { return fp8x8_to_16<T>(v); }
+  template <class T, int F>
+  static __device__ __forceinline__ uint4 widen(const uint2 &v) { return fp8x8_to_16<T, F>(v); }
 };
 template <>
 struct V8Chunk<64> {
@@ -247,8 +247,8 @@ struct V8Chunk<64> {
   static __device__ __forceinline__ uint32_t load(__amdgpu_buffer_rsrc_t r, int off) {
     return buffer_load4(r, off);
   }
-  template <class T>
-  static __device__ __forceinline__ uint2 widen(const uint32_t &v) { return fp8x4_to_16<T>(v); }
+  template <class T, int F>
+  static __device__ __forceinline__ uint2 widen(const uint32_t &v) { return fp8x4_to_16<T, F>(v); }
 };
 
 template <int D>
@@ -393,9 +393,11 @@ __device__ __forceinline__ void locate_tile(const int *s_tfirst, int num_seqs, i
 // per-tile arithmetic then dominates, so two waves per SIMD overlap it.
 // APP: the launch also stores each sequence's new token (16-bit pools, no
 // ring); a separate instantiation, so plain decode carries none of it.
-template <class T, int D, bool RING, bool KV8, bool APP = false>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, KV8 ? 2 : 1)))
+// KVF: 0 for 16-bit pools, else the 8-bit format (kKvE4M3 or kKvE5M2).
+template <class T, int D, bool RING, int KVF, bool APP = false>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, KVF != 0 ? 2 : 1)))
 void decode_mfma_kernel(DecodeArgs a) {
+  constexpr bool KV8 = KVF != 0;
   constexpr int KB = D / 32;  // score MFMAs per tile
   constexpr int EV = D / 16;  // V elements per lane per row
   constexpr int NB = D / 16;  // output MFMAs per tile (16 dims each)
@@ -629,10 +631,10 @@ void decode_mfma_kernel(DecodeArgs a) {
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb) {
         const uint4 w = kraw[kb >> 1];
-        kf[kb] = fp8x8_to_16<T>((kb & 1) ? make_uint2(w.z, w.w) : make_uint2(w.x, w.y));
+        kf[kb] = fp8x8_to_16<T, KVF>((kb & 1) ? make_uint2(w.z, w.w) : make_uint2(w.x, w.y));
       }
 #pragma unroll
-      for (int tau = 0; tau < 4; ++tau) vf[tau] = V8Chunk<D>::template widen<T>(vraw[tau]);
+      for (int tau = 0; tau < 4; ++tau) vf[tau] = V8Chunk<D>::template widen<T, KVF>(vraw[tau]);
     } else {
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb) kf[kb] = kraw[kb];
@@ -1121,8 +1123,9 @@ int persistent_grid(const void *kernel, int per_cu_cap) {
   return cus * std::max(1, std::min(per_cu, per_cu_cap));
 }
 
-template <class T, int D, bool RING, bool KV8 = false>
+template <class T, int D, bool RING, int KVF = 0>
 hipError_t launch_typed(const DecodeArgs &a, DecodeChoice choice, hipStream_t stream) {
+  constexpr bool KV8 = KVF != 0;
   const dim3 block(kNW * kWave);
   if constexpr (KV8) {  // 8-bit pools: the MFMA kernel only
     if (choice.kernel != DecodeKernel::kMfma) return hipErrorInvalidValue;
@@ -1133,16 +1136,16 @@ hipError_t launch_typed(const DecodeArgs &a, DecodeChoice choice, hipStream_t st
       // never starved by an older neighbour, so equal tile counts finish
       // at nearly equal times
       static const int grid_max = std::min(
-          persistent_grid(reinterpret_cast<const void *>(&decode_mfma_kernel<T, D, RING, KV8>),
+          persistent_grid(reinterpret_cast<const void *>(&decode_mfma_kernel<T, D, RING, KVF>),
                           KV8 ? 2 : 1),
           kMaxPersistentWaves / kNW);
       // at least one group of Hkv waves
       const int grid = std::max(grid_max, (a.num_kv_heads + kNW - 1) / kNW);
       if (a.app_key != nullptr) {
         if constexpr (RING || KV8) return hipErrorInvalidValue;
-        else hipLaunchKernelGGL((decode_mfma_kernel<T, D, false, false, true>), dim3(grid), block, 0, stream, a);
+        else hipLaunchKernelGGL((decode_mfma_kernel<T, D, false, 0, true>), dim3(grid), block, 0, stream, a);
       } else {
-        hipLaunchKernelGGL((decode_mfma_kernel<T, D, RING, KV8>), dim3(grid), block, 0, stream, a);
+        hipLaunchKernelGGL((decode_mfma_kernel<T, D, RING, KVF>), dim3(grid), block, 0, stream, a);
       }
       hipError_t err = hipGetLastError();
       if (err != hipSuccess) return err;
@@ -1184,15 +1187,19 @@ hipError_t launch_typed(const DecodeArgs &a, DecodeChoice choice, hipStream_t st
 }
 
 template <class T>
-hipError_t launch_dtype(const DecodeArgs &a, int head_dim, bool ring, bool kv_fp8,
+hipError_t launch_dtype(const DecodeArgs &a, int head_dim, bool ring, int kv8,
                         DecodeChoice choice, hipStream_t stream) {
   if constexpr (T::kBytes == 2) {
-    if (kv_fp8) {
+    if (kv8 == kKvE4M3 || kv8 == kKvE5M2) {
       if (ring) return hipErrorInvalidValue;
-      return head_dim == 128 ? launch_typed<T, 128, false, true>(a, choice, stream)
-                             : launch_typed<T, 64, false, true>(a, choice, stream);
+      if (kv8 == kKvE5M2)
+        return head_dim == 128 ? launch_typed<T, 128, false, kKvE5M2>(a, choice, stream)
+                               : launch_typed<T, 64, false, kKvE5M2>(a, choice, stream);
+      return head_dim == 128 ? launch_typed<T, 128, false, kKvE4M3>(a, choice, stream)
+                             : launch_typed<T, 64, false, kKvE4M3>(a, choice, stream);
     }
   }
+  if (kv8 != 0) return hipErrorInvalidValue;
   if (head_dim == 128)
     return ring ? launch_typed<T, 128, true>(a, choice, stream)
                 : launch_typed<T, 128, false>(a, choice, stream);
@@ -1203,7 +1210,7 @@ hipError_t launch_dtype(const DecodeArgs &a, int head_dim, bool ring, bool kv_fp
 }  // namespace
 
 hipError_t launch_decode(const DecodeArgs &args, pa_dtype dtype, int head_dim, bool ring,
-                         bool kv_fp8, DecodeChoice choice, int num_seqs, hipStream_t stream) {
+                         int kv8, DecodeChoice choice, int num_seqs, hipStream_t stream) {
   if (dtype == PA_F32) choice.kernel = DecodeKernel::kValu;  // no fp32 MFMA kernel
   // The device-side schedule holds up to kMaxSchedSeqs sequences; larger
   // batches run as consecutive slices on the same stream (each slice reuses
@@ -1225,9 +1232,9 @@ hipError_t launch_decode(const DecodeArgs &args, pa_dtype dtype, int head_dim, b
     }
     hipError_t err;
     switch (dtype) {
-      case PA_F16: err = launch_dtype<F16>(a, head_dim, ring, kv_fp8, choice, stream); break;
-      case PA_BF16: err = launch_dtype<BF16>(a, head_dim, ring, kv_fp8, choice, stream); break;
-      default: err = launch_dtype<F32>(a, head_dim, ring, kv_fp8, choice, stream); break;
+      case PA_F16: err = launch_dtype<F16>(a, head_dim, ring, kv8, choice, stream); break;
+      case PA_BF16: err = launch_dtype<BF16>(a, head_dim, ring, kv8, choice, stream); break;
+      default: err = launch_dtype<F32>(a, head_dim, ring, kv8, choice, stream); break;
     }
     if (err != hipSuccess) return err;
   }

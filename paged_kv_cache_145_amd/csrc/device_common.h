@@ -6,6 +6,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "launch.h"  // kKvE4M3, kKvE5M2
+
 namespace pa {
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
@@ -53,6 +55,11 @@ struct F16 {
   static __device__ __forceinline__ uint32_t from_fp8_pair(uint32_t w) {
     return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, HI));
   }
+  // Two E5M2 codes to two f16 values, exactly (E5M2 is f16's top byte).
+  template <bool HI>
+  static __device__ __forceinline__ uint32_t from_bf8_pair(uint32_t w) {
+    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_bf8(w, 1.0f, HI));
+  }
 };
 
 struct BF16 {
@@ -79,6 +86,12 @@ struct BF16 {
   template <bool HI>
   static __device__ __forceinline__ uint32_t from_fp8_pair(uint32_t w) {
     return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, HI));
+  }
+  // Two E5M2 codes to two bf16 values, exactly (2^-16 .. 57344 lie well
+  // inside bf16's range and 3 significant bits fit its 8).
+  template <bool HI>
+  static __device__ __forceinline__ uint32_t from_bf8_pair(uint32_t w) {
+    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_bf8(w, 1.0f, HI));
   }
 };
 
@@ -151,16 +164,23 @@ __device__ __forceinline__ uint32_t buffer_load4(__amdgpu_buffer_rsrc_t r, int o
   return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
 }
 
-// Eight / four E4M3 codes to 16-bit values of the tag T (little-endian
-// order kept: code e lands in 16-bit element e).
-template <class T>
-__device__ __forceinline__ uint4 fp8x8_to_16(uint2 v) {
-  return make_uint4(T::template from_fp8_pair<false>(v.x), T::template from_fp8_pair<true>(v.x),
-                    T::template from_fp8_pair<false>(v.y), T::template from_fp8_pair<true>(v.y));
+template <class T, int F, bool HI>
+__device__ __forceinline__ uint32_t code_pair_to_16(uint32_t w) {
+  static_assert(F == kKvE4M3 || F == kKvE5M2, "8-bit format");
+  if constexpr (F == kKvE5M2) return T::template from_bf8_pair<HI>(w);
+  else return T::template from_fp8_pair<HI>(w);
 }
-template <class T>
+
+// Eight / four 8-bit codes of format F to 16-bit values of the tag T
+// (little-endian order kept: code e lands in 16-bit element e).
+template <class T, int F>
+__device__ __forceinline__ uint4 fp8x8_to_16(uint2 v) {
+  return make_uint4(code_pair_to_16<T, F, false>(v.x), code_pair_to_16<T, F, true>(v.x),
+                    code_pair_to_16<T, F, false>(v.y), code_pair_to_16<T, F, true>(v.y));
+}
+template <class T, int F>
 __device__ __forceinline__ uint2 fp8x4_to_16(uint32_t v) {
-  return make_uint2(T::template from_fp8_pair<false>(v), T::template from_fp8_pair<true>(v));
+  return make_uint2(code_pair_to_16<T, F, false>(v), code_pair_to_16<T, F, true>(v));
 }
 
 }  // namespace pa

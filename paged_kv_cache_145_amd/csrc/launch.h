@@ -19,6 +19,11 @@ constexpr float kLog2eHost = 1.4426950408889634f;
 // Per-KV-head factors of 8-bit pools, passed by value in kernel arguments:
 // the decode kernels take the scales, the cache write the inverse scales.
 constexpr int kMaxFp8HeadsHost = 64;
+
+// Formats of 8-bit pools, as the launch functions and the kernels' KVF
+// template argument name them (0 = 16-bit pools).
+constexpr int kKvE4M3 = 1;
+constexpr int kKvE5M2 = 2;
 struct KvScales {
   float k[kMaxFp8HeadsHost];
   float v[kMaxFp8HeadsHost];
@@ -119,11 +124,12 @@ struct DecodeChoice {
 DecodeChoice choose_decode_kernel(pa_dtype dtype, int group);
 int choose_partition_tokens(int64_t effective_max_context);
 
-// dtype: the query/output dtype; kv_fp8: the pools hold E4M3 codes.
-hipError_t launch_decode(const DecodeArgs &a, pa_dtype dtype, int head_dim, bool ring, bool kv_fp8,
+// dtype: the query/output dtype; kv8: 0 for 16-bit pools, else the format
+// of their 8-bit codes (kKvE4M3 = 1, kKvE5M2 = 2).
+hipError_t launch_decode(const DecodeArgs &a, pa_dtype dtype, int head_dim, bool ring, int kv8,
                          DecodeChoice choice, int num_seqs, hipStream_t stream);
 
-hipError_t launch_decode_multi(const MultiArgs &a, pa_dtype dtype, int head_dim, bool kv_fp8, int waves,
+hipError_t launch_decode_multi(const MultiArgs &a, pa_dtype dtype, int head_dim, int kv8, int waves,
                                int grid, hipStream_t stream);
 
 hipError_t launch_reshape_and_cache(pa_dtype dtype, void *k_cache, void *v_cache,
@@ -131,8 +137,9 @@ hipError_t launch_reshape_and_cache(pa_dtype dtype, void *k_cache, void *v_cache
                                     const int32_t *slot_mapping, int32_t num_tokens,
                                     int32_t row_elems, int64_t num_slots, hipStream_t stream);
 
-// 8-bit pools: quantise rows of act dtype (F16/BF16) with inverse scales.
-hipError_t launch_reshape_and_cache_fp8(pa_dtype act_dtype, void *k_cache, void *v_cache,
+// 8-bit pools: quantise rows of act dtype (F16/BF16) with inverse scales to
+// codes of format kv8 (1 = E4M3, 2 = E5M2).
+hipError_t launch_reshape_and_cache_fp8(pa_dtype act_dtype, int kv8, void *k_cache, void *v_cache,
                                         const void *key, const void *value,
                                         const int32_t *slot_mapping, int32_t num_tokens,
                                         int32_t num_kv_heads, int32_t head_dim, int64_t num_slots,

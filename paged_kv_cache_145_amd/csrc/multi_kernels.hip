@@ -82,8 +82,8 @@ struct MqV8<128> {
   static __device__ __forceinline__ uint2 load(__amdgpu_buffer_rsrc_t r, int off) {
     return buffer_load8(r, off);
   }
-  template <class T>
-  static __device__ __forceinline__ uint4 widen(const uint2 &v) { return fp8x8_to_16<T>(v); }
+  template <class T, int F>
+  static __device__ __forceinline__ uint4 widen(const uint2 &v) { return fp8x8_to_16<T, F>(v); }
 };
 template <>
 struct MqV8<64> {
@@ -91,8 +91,8 @@ struct MqV8<64> {
   static __device__ __forceinline__ uint32_t load(__amdgpu_buffer_rsrc_t r, int off) {
     return buffer_load4(r, off);
   }
-  template <class T>
-  static __device__ __forceinline__ uint2 widen(const uint32_t &v) { return fp8x4_to_16<T>(v); }
+  template <class T, int F>
+  static __device__ __forceinline__ uint2 widen(const uint32_t &v) { return fp8x4_to_16<T, F>(v); }
 };
 
 // Per-wave V tile: row-major, rows padded so the transposing reads of one
@@ -164,13 +164,15 @@ __device__ int mq_schedule(const MultiArgs &a, int *s_tfirst, int *s_kvend, int 
   return carry;
 }
 
-// KV8: the pools hold E4M3 codes scaled per KV head.  A lane's 16-byte K
-// load then carries 16 dimensions, the A operands of two score MFMAs, and
-// the query fragments follow that dimension order; codes widen exactly to
-// 16-bit values before the MFMAs and the LDS tile.
-template <class T, int D, int MT, bool KV8, int W>
+// KVF != 0: the pools hold 8-bit codes of that format (kKvE4M3, kKvE5M2)
+// scaled per KV head.  A lane's 16-byte K load then carries 16 dimensions,
+// the A operands of two score MFMAs, and the query fragments follow that
+// dimension order; codes widen exactly to 16-bit values before the MFMAs and
+// the LDS tile.
+template <class T, int D, int MT, int KVF, int W>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(W, W)))
 void decode_multi_kernel(MultiArgs a) {
+  constexpr bool KV8 = KVF != 0;
   constexpr int kMqQSlots = kMqQSlotsFor<W>;
   constexpr int KB = D / 32;  // score MFMAs per row tile and key tile
   constexpr int EV = D / 16;  // V elements per lane per row
@@ -353,10 +355,10 @@ void decode_multi_kernel(MultiArgs a) {
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb) {
         const uint4 w8 = kraw[kb >> 1];
-        kf[kb] = fp8x8_to_16<T>((kb & 1) ? make_uint2(w8.z, w8.w) : make_uint2(w8.x, w8.y));
+        kf[kb] = fp8x8_to_16<T, KVF>((kb & 1) ? make_uint2(w8.z, w8.w) : make_uint2(w8.x, w8.y));
       }
 #pragma unroll
-      for (int tau = 0; tau < 4; ++tau) vf[tau] = MqV8<D>::template widen<T>(vraw[tau]);
+      for (int tau = 0; tau < 4; ++tau) vf[tau] = MqV8<D>::template widen<T, KVF>(vraw[tau]);
     } else {
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb) kf[kb] = kraw[kb];
@@ -576,9 +578,9 @@ __global__ __launch_bounds__(256) void decode_multi_reduce_kernel(MultiArgs a) {
   out[3] = T::from_float(acc.w * inv);
 }
 
-template <class T, int D, int MT, bool KV8, int W>
+template <class T, int D, int MT, int KVF, int W>
 hipError_t launch_mt(const MultiArgs &a, int grid, hipStream_t stream) {
-  hipLaunchKernelGGL((decode_multi_kernel<T, D, MT, KV8, W>), dim3(grid), dim3(kMqWaves * kWave), 0, stream, a);
+  hipLaunchKernelGGL((decode_multi_kernel<T, D, MT, KVF, W>), dim3(grid), dim3(kMqWaves * kWave), 0, stream, a);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   constexpr int rpb = 256 / (D / 4);
@@ -588,22 +590,33 @@ hipError_t launch_mt(const MultiArgs &a, int grid, hipStream_t stream) {
   return hipGetLastError();
 }
 
-template <class T, int D, bool KV8>
+template <class T, int D, int KVF>
 hipError_t launch_d(const MultiArgs &a, int mt, int waves, int grid, hipStream_t stream) {
-  if (waves == 2) return mt == 1 ? launch_mt<T, D, 1, KV8, 2>(a, grid, stream)
-                                 : launch_mt<T, D, 2, KV8, 2>(a, grid, stream);
+  if (waves == 2) return mt == 1 ? launch_mt<T, D, 1, KVF, 2>(a, grid, stream)
+                                 : launch_mt<T, D, 2, KVF, 2>(a, grid, stream);
   switch (mt) {
-    case 1: return launch_mt<T, D, 1, KV8, 1>(a, grid, stream);
-    case 2: return launch_mt<T, D, 2, KV8, 1>(a, grid, stream);
-    case 3: return launch_mt<T, D, 3, KV8, 1>(a, grid, stream);
-    default: return launch_mt<T, D, kMultiMaxRowTiles(D), KV8, 1>(a, grid, stream);
+    case 1: return launch_mt<T, D, 1, KVF, 1>(a, grid, stream);
+    case 2: return launch_mt<T, D, 2, KVF, 1>(a, grid, stream);
+    case 3: return launch_mt<T, D, 3, KVF, 1>(a, grid, stream);
+    default: return launch_mt<T, D, kMultiMaxRowTiles(D), KVF, 1>(a, grid, stream);
   }
 }
 
-template <class T, bool KV8>
+template <class T, int KVF>
 hipError_t launch_h(const MultiArgs &a, int head_dim, int mt, int waves, int grid, hipStream_t stream) {
-  return head_dim == 128 ? launch_d<T, 128, KV8>(a, mt, waves, grid, stream)
-                         : launch_d<T, 64, KV8>(a, mt, waves, grid, stream);
+  return head_dim == 128 ? launch_d<T, 128, KVF>(a, mt, waves, grid, stream)
+                         : launch_d<T, 64, KVF>(a, mt, waves, grid, stream);
+}
+
+template <class T>
+hipError_t launch_t(const MultiArgs &a, int head_dim, int kv8, int mt, int waves, int grid,
+                    hipStream_t stream) {
+  switch (kv8) {
+    case 0: return launch_h<T, 0>(a, head_dim, mt, waves, grid, stream);
+    case kKvE4M3: return launch_h<T, kKvE4M3>(a, head_dim, mt, waves, grid, stream);
+    case kKvE5M2: return launch_h<T, kKvE5M2>(a, head_dim, mt, waves, grid, stream);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 }  // namespace
@@ -619,14 +632,11 @@ int multi_grid() {
   return cus;
 }
 
-hipError_t launch_decode_multi(const MultiArgs &a, pa_dtype dtype, int head_dim, bool kv_fp8, int waves,
+hipError_t launch_decode_multi(const MultiArgs &a, pa_dtype dtype, int head_dim, int kv8, int waves,
                                int grid, hipStream_t stream) {
   const int mt = a.pass_rows / 16;
-  if (dtype == PA_BF16)
-    return kv_fp8 ? launch_h<BF16, true>(a, head_dim, mt, waves, grid, stream)
-                  : launch_h<BF16, false>(a, head_dim, mt, waves, grid, stream);
-  return kv_fp8 ? launch_h<F16, true>(a, head_dim, mt, waves, grid, stream)
-                : launch_h<F16, false>(a, head_dim, mt, waves, grid, stream);
+  if (dtype == PA_BF16) return launch_t<BF16>(a, head_dim, kv8, mt, waves, grid, stream);
+  return launch_t<F16>(a, head_dim, kv8, mt, waves, grid, stream);
 }
 
 }  // namespace pa

@@ -80,6 +80,7 @@ int pa_create_pool(pa_pool **out, int32_t num_blocks, int32_t block_size, int32_
   p->head_dim = head_dim;
   p->dtype = dtype;
   p->kv_fp8 = false;
+  p->kv_dtype = dtype;
   p->k_cache = k_cache;
   p->v_cache = v_cache;
   try {
@@ -102,8 +103,16 @@ int pa_create_pool(pa_pool **out, int32_t num_blocks, int32_t block_size, int32_
 int pa_create_pool_fp8(pa_pool **out, int32_t num_blocks, int32_t block_size,
                        int32_t num_kv_heads, int32_t head_dim, pa_dtype act_dtype,
                        const float *k_scale, const float *v_scale, void *k_cache, void *v_cache) {
+  return pa_create_pool_kv8(out, num_blocks, block_size, num_kv_heads, head_dim, PA_FP8_E4M3, act_dtype,
+                            k_scale, v_scale, k_cache, v_cache);
+}
+
+int pa_create_pool_kv8(pa_pool **out, int32_t num_blocks, int32_t block_size, int32_t num_kv_heads,
+                       int32_t head_dim, pa_dtype kv_dtype, pa_dtype act_dtype, const float *k_scale,
+                       const float *v_scale, void *k_cache, void *v_cache) {
   if (out == nullptr) return PA_ERR_INVAL;
   *out = nullptr;
+  if (kv_dtype != PA_FP8_E4M3 && kv_dtype != PA_FP8_E5M2) return PA_ERR_INVAL;
   if (act_dtype != PA_F16 && act_dtype != PA_BF16) return PA_ERR_INVAL;
   if (num_kv_heads <= 0 || num_kv_heads > pa::kMaxFp8Heads) return PA_ERR_INVAL;
   if (k_scale == nullptr || v_scale == nullptr) return PA_ERR_INVAL;
@@ -130,6 +139,7 @@ int pa_create_pool_fp8(pa_pool **out, int32_t num_blocks, int32_t block_size,
     p->v_inv[h] = one / v_scale[h];
   }
   p->kv_fp8 = true;
+  p->kv_dtype = kv_dtype;
   *out = p;
   return PA_OK;
 }

@@ -50,7 +50,8 @@ struct pa_pool {
   int32_t num_kv_heads;
   int32_t head_dim;
   pa_dtype dtype;  // element type of K/V rows, or the activation type of an 8-bit pool
-  bool kv_fp8;     // pools hold E4M3 codes scaled per KV head
+  bool kv_fp8;     // pools hold 8-bit codes scaled per KV head
+  pa_dtype kv_dtype;  // storage type of K/V rows: dtype, or PA_FP8_E4M3 / PA_FP8_E5M2
   std::vector<float> k_scale, v_scale;  // 8-bit pools: per-head scales
   std::vector<float> k_inv, v_inv;      // fp32(1 / scale)
   void *k_cache;

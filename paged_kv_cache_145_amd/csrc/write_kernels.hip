@@ -55,10 +55,30 @@ __device__ __forceinline__ uint32_t e4m3_code(float x) {
   return sign | (code > 0x7Eu ? 0x7Eu : code);
 }
 
+// Nearest E5M2 code of a float, ties to the even code, magnitudes of 57344
+// and above (infinities too) saturating to 57344, NaN to 0x7F (OCP 8-bit
+// float: bias 15, 2 mantissa bits, exponent field 0 = subnormals of step
+// 2^-16, exponent field 31 = infinity / NaN, never produced here).
+__device__ __forceinline__ uint32_t e5m2_code(float x) {
+  const uint32_t bits = __float_as_uint(x);
+  const uint32_t sign = (bits >> 24) & 0x80u;
+  const float a = fabsf(x);
+  if (a != a) return 0x7Fu;
+  if (a >= 57344.0f) return sign | 0x7Bu;
+  if (a < 6.103515625e-05f) {  // below 2^-14: a * 2^16 is exact; round it to an integer
+    return sign | (uint32_t)__builtin_rintf(a * 65536.0f);  // 4 -> code 4 = 2^-14
+  }
+  // normal: drop 21 of the 23 fraction bits with round-to-nearest-even
+  const uint32_t ab = __float_as_uint(a);
+  const uint32_t r = (ab + 0xFFFFFu + ((ab >> 21) & 1u)) & 0xFFE00000u;
+  const uint32_t code = ((((r >> 23) - 127u + 15u) & 0x1Fu) << 2) | ((r >> 21) & 3u);
+  return sign | (code > 0x7Bu ? 0x7Bu : code);
+}
+
 // 8-bit pools: one work-group per token; each thread turns 16 activations
 // (one 16-element run inside one head) into 16 codes: x * inv_scale[head]
-// in float, then E4M3.
-template <class T>
+// in float, then the code of format F (kKvE4M3 or kKvE5M2).
+template <class T, int F>
 __global__ __launch_bounds__(256) void reshape_and_cache_fp8_kernel(
     uint4 *__restrict__ k_cache, uint4 *__restrict__ v_cache, const uint4 *__restrict__ key,
     const uint4 *__restrict__ value, const int32_t *__restrict__ slot_mapping, int32_t chunks,
@@ -81,7 +101,8 @@ __global__ __launch_bounds__(256) void reshape_and_cache_fp8_kernel(
         for (int e = 0; e < 4; ++e) {
           const uint32_t word = w[(4 * q + e) / 2];
           const uint16_t b = (uint16_t)(((4 * q + e) & 1) ? (word >> 16) : (word & 0xFFFFu));
-          packed |= e4m3_code(T::to_float(b) * s) << (8 * e);
+          const float xs = T::to_float(b) * s;
+          packed |= (F == kKvE5M2 ? e5m2_code(xs) : e4m3_code(xs)) << (8 * e);
         }
         o[q] = packed;
       }
@@ -164,23 +185,24 @@ hipError_t launch_reshape_and_cache(pa_dtype dtype, void *k_cache, void *v_cache
   return hipGetLastError();
 }
 
-hipError_t launch_reshape_and_cache_fp8(pa_dtype act_dtype, void *k_cache, void *v_cache,
+hipError_t launch_reshape_and_cache_fp8(pa_dtype act_dtype, int kv8, void *k_cache, void *v_cache,
                                         const void *key, const void *value,
                                         const int32_t *slot_mapping, int32_t num_tokens,
                                         int32_t num_kv_heads, int32_t head_dim, int64_t num_slots,
                                         const KvScales &inv, hipStream_t stream) {
+  if (kv8 != kKvE4M3 && kv8 != kKvE5M2) return hipErrorInvalidValue;
   const int32_t chunks = num_kv_heads * head_dim / 16;
   const int threads = chunks >= 256 ? 256 : ((chunks + 63) / 64) * 64;
   auto *kc = static_cast<uint4 *>(k_cache);
   auto *vc = static_cast<uint4 *>(v_cache);
   auto *kk = static_cast<const uint4 *>(key);
   auto *vv = static_cast<const uint4 *>(value);
-  if (act_dtype == PA_BF16)
-    hipLaunchKernelGGL(reshape_and_cache_fp8_kernel<BF16>, dim3(num_tokens), dim3(threads), 0, stream,
-                       kc, vc, kk, vv, slot_mapping, chunks, head_dim, num_slots, inv);
-  else
-    hipLaunchKernelGGL(reshape_and_cache_fp8_kernel<F16>, dim3(num_tokens), dim3(threads), 0, stream,
-                       kc, vc, kk, vv, slot_mapping, chunks, head_dim, num_slots, inv);
+  const bool e5 = kv8 == kKvE5M2;
+  auto kernel = act_dtype == PA_BF16
+                    ? (e5 ? reshape_and_cache_fp8_kernel<BF16, kKvE5M2> : reshape_and_cache_fp8_kernel<BF16, kKvE4M3>)
+                    : (e5 ? reshape_and_cache_fp8_kernel<F16, kKvE5M2> : reshape_and_cache_fp8_kernel<F16, kKvE4M3>);
+  hipLaunchKernelGGL(kernel, dim3(num_tokens), dim3(threads), 0, stream, kc, vc, kk, vv, slot_mapping, chunks,
+                     head_dim, num_slots, inv);
   return hipGetLastError();
 }
 

@@ -67,7 +67,8 @@ class DeviceCase:
             self.k_cache = torch.full(shape, workloads.FP8_NAN_CODE, dtype=torch.uint8, device=device)
             self.v_cache = torch.full(shape, workloads.FP8_NAN_CODE, dtype=torch.uint8, device=device)
             self.pool = pk.Pool(self.k_cache, self.v_cache, case.block_size, act_dtype=TORCH_DTYPES[dt],
-                                k_scale=case.k_scale, v_scale=case.v_scale)
+                                k_scale=case.k_scale, v_scale=case.v_scale,
+                                kv_format=case.kv_dtype.split("_")[1])
         else:
             self.k_cache = torch.empty(shape, dtype=TORCH_DTYPES[dt], device=device)
             self.v_cache = torch.empty_like(self.k_cache)

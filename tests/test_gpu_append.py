@@ -166,10 +166,12 @@ def test_append_two_step_paths(shape):
     _check(workloads.make_paged_case("append_fb", 8400 + hq, dtype, lens, hq, hkv, d, bs))
 
 
-def test_append_fp8_pool():
-    print("append fp8", flush=True)
+@pytest.mark.parametrize("kv_format", ["e4m3", "e5m2"])
+def test_append_fp8_pool(kv_format):
+    print(f"append {kv_format}", flush=True)
     case = workloads.config_fp8(lambda: workloads.make_paged_case("append_fp8", 8500, "bf16",
-                                                                  [1, 2, 16, 17, 1000], 32, 4, 128, 16))
+                                                                  [1, 2, 16, 17, 1000], 32, 4, 128, 16),
+                                kv_format=kv_format)
     _check(case)
 
 

@@ -1,4 +1,4 @@
-"""8-bit (E4M3) KV pools on the GPU against the oracle.
+"""8-bit (E4M3 and E5M2) KV pools on the GPU against the oracle.
 
 The cache write quantises each activation row with the pool's per-head
 inverse scales and must store exactly the oracle's codes; decode
@@ -19,12 +19,20 @@ from gpu_support import DeviceCase, assert_parity, oracle_reference
 
 pytestmark = pytest.mark.gpu
 
-FP8_CASES = ["tiny_fp8", "embedded_1p1b_fp8", "llama70b_b64_fp8"]
+FP8_CASES = ["tiny_fp8", "embedded_1p1b_fp8", "llama70b_b64_fp8", "llama70b_b64_e5m2",
+             "tiny_e5m2", "embedded_1p1b_e5m2"]
+
+
+def _case(name):
+    if name in workloads.FP8_CONFIGS:
+        return workloads.FP8_CONFIGS[name]()
+    base = {"tiny_e5m2": workloads.config_tiny_fp32, "embedded_1p1b_e5m2": workloads.config_embedded_1p1b}[name]
+    return workloads.config_fp8(base, kv_format="e5m2")
 
 
 @pytest.mark.parametrize("name", FP8_CASES)
 def test_fp8_cache_write_bit_exact(name):
-    case = workloads.FP8_CONFIGS[name]()
+    case = _case(name)
     dc = DeviceCase(case)
     dc.write_all()
     torch.cuda.synchronize()
@@ -36,7 +44,7 @@ def test_fp8_cache_write_bit_exact(name):
 
 @pytest.mark.parametrize("name", FP8_CASES)
 def test_fp8_decode_parity(name):
-    case = workloads.FP8_CONFIGS[name]()
+    case = _case(name)
     dc = DeviceCase(case)
     dc.write_all()
     out = dc.decode()
@@ -45,11 +53,68 @@ def test_fp8_decode_parity(name):
     dc.close()
 
 
-def test_fp8_ragged_and_empty_sequences():
+def _act_bits(x: np.ndarray, act: str) -> np.ndarray:
+    """Raw 16-bit rows of float64 values in the activation dtype (nearest-even)."""
+    if act == "f16":
+        with np.errstate(over="ignore"):
+            return x.astype(np.float16).view(np.uint16)
+    raw = workloads.round_f32_to_bf16_bits(np.where(np.isfinite(x), x, 0).astype(np.float32)).astype(np.uint16)
+    raw[np.isnan(x)] = 0x7FC0
+    raw[x == np.inf] = 0x7F80
+    raw[x == -np.inf] = 0xFF80
+    return raw
+
+
+@pytest.mark.parametrize("kv_format", ["e4m3", "e5m2"])
+def test_fp8_write_special_values(kv_format):
+    """The cache write's encoder on values chosen to hit its branches: zeros
+    of both signs, subnormals, every tie between neighbouring codes (to the
+    even code), every code's value, values between, the largest finite
+    value and values past it, both infinities, NaN; scales of 1, so the
+    quantised product is the value itself."""
+    from oracle import fp8
+
+    if kv_format == "e4m3":
+        mags, top, act = fp8._MAGNITUDES, 448.0, "f16"
+    else:
+        mags, top, act = fp8._E5M2_MAGNITUDES, 57344.0, "bf16"
+    mids = (mags[:-1] + mags[1:]) / 2
+    special = np.array([0.0, -0.0, top, -top, 1.1 * top, 1e30, -1e30, np.inf, -np.inf, np.nan])
+    vals = np.concatenate([special, mids, -mids, mags, -mags, 1.3 * mags, 0.9 * mags])
+    hkv, d = 2, 128
+    per_row = hkv * d
+    rows = -(-vals.size // per_row)
+    x = np.zeros(rows * per_row)
+    x[: vals.size] = vals
+    raw = _act_bits(x, act)
+    # the ties survive the activation dtype exactly (4 / 3 significant bits)
+    back = raw.view(np.float16).astype(np.float64) if act == "f16" else \
+        (raw.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    n_sp = special.size
+    assert np.array_equal(back[n_sp: n_sp + mids.size], mids)
+    raw = raw.reshape(rows, hkv, d)
+    if act == "f16":  # raw f16 rows are float16 arrays, bf16 rows their uint16 bits
+        raw = raw.view(np.float16)
+    base = workloads.make_paged_case("special", 145_095, act, [rows], 4, hkv, d, 16)
+    base.writes = [workloads.WriteChunk(0, np.arange(rows, dtype=np.int64), raw.copy(), raw[::-1].copy())]
+    case = workloads.config_fp8(lambda: base, kv_format=kv_format)
+    case.k_scale = np.ones(hkv, dtype=np.float32)
+    case.v_scale = np.ones(hkv, dtype=np.float32)
+    dc = DeviceCase(case)
+    dc.write_all()
+    torch.cuda.synchronize()
+    kp, vp, _ = oracle.build_pools(case)
+    assert np.array_equal(dc.k_cache.cpu().numpy(), kp)
+    assert np.array_equal(dc.v_cache.cpu().numpy(), vp)
+    dc.close()
+
+
+@pytest.mark.parametrize("kv_format", ["e4m3", "e5m2"])
+def test_fp8_ragged_and_empty_sequences(kv_format):
     """Empty sequences, one token, every tail length, 64-token blocks, D 64."""
     base = workloads.make_paged_case("ragged", 145_077, "f16", [0, 1, 15, 16, 17, 33, 250, 0, 1000],
                                      8, 2, 64, 64)
-    case = workloads.config_fp8(lambda: base)
+    case = workloads.config_fp8(lambda: base, kv_format=kv_format)
     dc = DeviceCase(case)
     dc.write_all()
     out = dc.decode()
@@ -95,12 +160,13 @@ def test_fp8_unsupported_combinations_are_rejected():
     dc.close()
 
 
+@pytest.mark.parametrize("kv_format", ["e4m3", "e5m2"])
 @pytest.mark.parametrize("hq,hkv,d", [(4, 4, 128), (4, 2, 64), (6, 2, 128)], ids=["G1-D128", "G2-D64", "G3-D128"])
-def test_fp8_small_groups(hq, hkv, d):
+def test_fp8_small_groups(hq, hkv, d, kv_format):
     """GQA groups below 4 (MHA included) on 8-bit pools, several tile ranges."""
     base = workloads.make_paged_case("small_group", 145_090 + hq + d, "bf16", [700, 3, 2100, 64, 0, 1300],
                                      hq, hkv, d, 16)
-    case = workloads.config_fp8(lambda: base)
+    case = workloads.config_fp8(lambda: base, kv_format=kv_format)
     dc = DeviceCase(case)
     dc.write_all()
     out = dc.decode()

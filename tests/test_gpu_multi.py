@@ -184,6 +184,23 @@ def test_multi_parity_fp8_pools(shape, min_range, waves):
     dc.close()
 
 
+@pytest.mark.parametrize("min_range", [None, 1])
+@pytest.mark.parametrize("shape", [SHAPES[0], SHAPES[3], SHAPES[5]], ids=["s0", "s3", "s5"])
+def test_multi_parity_e5m2_pools(shape, min_range):
+    """8-bit pools in the E5M2 format: the same kernels with the other
+    widening."""
+    dtype, lens, q, hq, hkv, d, bs = shape
+    print(f"multi e5m2 shape {shape} min_range={min_range}", flush=True)
+    case = workloads.config_fp8(lambda: workloads.make_multi_case("multi_e5m2", 7450 + len(lens) + q, dtype, lens,
+                                                                  q, hq, hkv, d, bs), kv_format="e5m2")
+    dc = DeviceCase(case)
+    dc.write_all()
+    with env(PA_MULTI_MIN_RANGE=min_range):
+        out = _run(dc, case)
+    assert_parity(out, _ref(case), dtype)
+    dc.close()
+
+
 def test_spec_verify_llama70b_fp8():
     case = workloads.config_fp8(workloads.config_spec_verify_llama70b)
     print("multi spec_verify_llama70b fp8", flush=True)

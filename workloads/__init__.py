@@ -493,6 +493,10 @@ def config_embedded_1p1b_fp8() -> DecodeCase:
     return config_fp8(config_embedded_1p1b)
 
 
+def config_llama70b_e5m2() -> DecodeCase:
+    return config_fp8(config_llama70b, kv_format="e5m2")
+
+
 def make_multi_case(name: str, seed: int, dtype: str, lens, q_len: int, num_q_heads: int,
                     num_kv_heads: int, head_dim: int, block_size: int, **kw) -> DecodeCase:
     """A plain-paging case whose sequences each end with ``q_len`` new tokens
@@ -536,6 +540,7 @@ MULTI_CONFIGS = {
     "chunked_prefill": config_chunked_prefill,
     # resolved at call time: config_fp8 is defined further down
     "spec_verify_llama70b_fp8": lambda: config_fp8(config_spec_verify_llama70b),
+    "spec_verify_llama70b_e5m2": lambda: config_fp8(config_spec_verify_llama70b, kv_format="e5m2"),
 }
 
 
@@ -543,6 +548,7 @@ FP8_CONFIGS = {
     "tiny_fp8": config_tiny_fp8,
     "embedded_1p1b_fp8": config_embedded_1p1b_fp8,
     "llama70b_b64_fp8": config_llama70b_fp8,
+    "llama70b_b64_e5m2": config_llama70b_e5m2,
 }
 
 
