@@ -805,11 +805,11 @@ def main() -> int:
     torch.cuda.synchronize()
 
     group = case.num_q_heads // case.num_kv_heads
-    # the one-call step is a single launch on 16-bit pools with groups up to
-    # 16 and no ring; elsewhere the library would run the two calls in turn,
-    # so the bench times them as two calls
+    # the one-call step is a single launch on the MFMA path (f16/bf16 or
+    # 8-bit pools, groups up to 16) without the ring; elsewhere the library
+    # would run the two calls in turn, so the bench times them as two calls
     mfma = case.dtype != "f32" and 1 <= group <= 16 and os.environ.get("PA_FORCE_VALU", "0") in ("", "0")
-    fused = args.step == "fused" and ring is None and mfma and not workloads_is_kv8(case.kv_dtype)
+    fused = args.step == "fused" and ring is None and mfma
 
     def decode():
         if fused:  # stores the step's new tokens and decodes in one call

@@ -410,10 +410,12 @@ int pa_decode(pa_pool *pool, void *out, const void *query, const int32_t *block_
  * slot_mapping[b] is the slot of position context_lens[b] - 1 through
  * block_tables[b] (or padding), it is -1 where context_lens[b] == 0, no
  * other sequence of the call reads it, and slots are distinct; otherwise
- * the result is unspecified (no fault).  On 16-bit pools with num_q_heads /
- * num_kv_heads <= 16 both happen in the decode launch: the wave that streams
- * a sequence's last tile for KV head g stores the new rows of head g just
- * before it loads that tile.  Other pools run the two calls in turn.  Other
+ * the result is unspecified (no fault).  On f16/bf16 and 8-bit pools with
+ * num_q_heads / num_kv_heads <= 16 both happen in the decode launch: the
+ * wave that streams a sequence's last tile for KV head g stores the new rows
+ * of head g (8-bit pools: quantised exactly as pa_reshape_and_cache does)
+ * just before it loads that tile.  Other pools (fp32, wider groups) run the
+ * two calls in turn.  Other
  * arguments, the workspace size (pa_decode_workspace_bytes with ring =
  * NULL) and errors are those of pa_decode; key and value must be 16-byte
  * aligned and slot_mapping 4-byte aligned (PA_ERR_INVAL otherwise). */

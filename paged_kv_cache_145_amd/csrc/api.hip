@@ -382,6 +382,8 @@ int decode_impl(pa_pool *pool, void *out, const void *query, const int32_t *bloc
     for (int h = 0; h < pool->num_kv_heads; ++h) {
       a.kv_scale.k[h] = pool->k_scale[h];
       a.kv_scale.v[h] = pool->v_scale[h];
+      a.kv_inv.k[h] = pool->k_inv[h];
+      a.kv_inv.v[h] = pool->v_inv[h];
     }
 
   const pa::DecodeChoice choice = pa::choose_decode_kernel(pool->dtype, group);
@@ -391,8 +393,7 @@ int decode_impl(pa_pool *pool, void *out, const void *query, const int32_t *bloc
   if ((int64_t)pool->num_kv_heads * nchunk > INT32_MAX) return PA_ERR_UNSUPPORTED;
   if (app != nullptr) {
     // the MFMA kernel appends in the same launch; other paths write first
-    const bool fused = choice.kernel == pa::DecodeKernel::kMfma && ring == nullptr && !pool->kv_fp8 &&
-                       pool->dtype != PA_F32;
+    const bool fused = choice.kernel == pa::DecodeKernel::kMfma && ring == nullptr && pool->dtype != PA_F32;
     if (fused) {
       a.app_key = app->key;
       a.app_value = app->value;

@@ -467,14 +467,15 @@ void decode_mfma_kernel(DecodeArgs a) {
   int c0 = 0, cnt = 0;
   int app_hi = 0;  // tiles below this index had their new token stored
 
-  // Append (16-bit pools, no ring): the new token of a sequence sits in its
-  // last tile, and the wave that streams that tile for head g stores the
-  // token's K and V rows of head g (from the inputs) when it stages the
-  // tile, before any load of it: the wave's own later loads of those
-  // addresses are ordered after its stores, so the result equals a cache
-  // write followed by the decode.  A lane group of 2 * D * 2 / 16 lanes
-  // carries one sequence's two rows in 16-byte pieces (K first).
-  static_assert(!APP || (!KV8 && !RING), "appending needs a 16-bit pool without ring");
+  // Append (no ring): the new token of a sequence sits in its last tile, and
+  // the wave that streams that tile for head g stores the token's K and V
+  // rows of head g (from the inputs; 8-bit pools: quantised exactly as the
+  // cache write does) when it stages the tile, before any load of it: the
+  // wave's own later loads of those addresses are ordered after its stores,
+  // so the result equals a cache write followed by the decode.  A lane
+  // group of 2 * D * 2 / 16 lanes carries one sequence's two input rows in
+  // 16-byte pieces (K first); a piece stores 16 bytes, or 8 codes.
+  static_assert(!APP || !RING, "appending needs plain paging");
   constexpr int kPiecesPerRow = D * (int)sizeof(st) / 16;
   constexpr int kLanesPerEnd = 2 * kPiecesPerRow;
   constexpr int kEndsPerRound = kWave / kLanesPerEnd;
@@ -510,8 +511,25 @@ void decode_mfma_kernel(DecodeArgs a) {
     for (int r = 0; r < kAppRounds; ++r) {
       if (bsel[r] >= 0 && slot[r] >= 0 && slot[r] < a.num_slots) {
         char *dst = static_cast<char *>(const_cast<void *>(app_v ? a.v_cache : a.k_cache)) +
-                    (((int64_t)slot[r] * hkv + g) * D) * (int64_t)sizeof(st) + 16 * app_piece;
-        *reinterpret_cast<u32x4 *>(dst) = row[r];
+                    (((int64_t)slot[r] * hkv + g) * D) * (int64_t)KVB + (16 / (int)sizeof(st)) * KVB * app_piece;
+        if constexpr (KV8) {
+          const float inv = app_v ? a.kv_inv.v[g] : a.kv_inv.k[g];
+          uint32_t c[2];
+#pragma unroll
+          for (int w = 0; w < 2; ++w) {
+            uint32_t packed = 0;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const uint32_t word = row[r][(4 * w + e) / 2];
+              const uint16_t b = (uint16_t)(((4 * w + e) & 1) ? (word >> 16) : (word & 0xFFFFu));
+              packed |= fp8_code<KVF>(T::to_float(b) * inv) << (8 * e);
+            }
+            c[w] = packed;
+          }
+          *reinterpret_cast<uint2 *>(dst) = make_uint2(c[0], c[1]);
+        } else {
+          *reinterpret_cast<u32x4 *>(dst) = row[r];
+        }
       }
     }
   };
@@ -1142,8 +1160,8 @@ hipError_t launch_typed(const DecodeArgs &a, DecodeChoice choice, hipStream_t st
       // at least one group of Hkv waves
       const int grid = std::max(grid_max, (a.num_kv_heads + kNW - 1) / kNW);
       if (a.app_key != nullptr) {
-        if constexpr (RING || KV8) return hipErrorInvalidValue;
-        else hipLaunchKernelGGL((decode_mfma_kernel<T, D, false, 0, true>), dim3(grid), block, 0, stream, a);
+        if constexpr (RING) return hipErrorInvalidValue;
+        else hipLaunchKernelGGL((decode_mfma_kernel<T, D, false, KVF, true>), dim3(grid), block, 0, stream, a);
       } else {
         hipLaunchKernelGGL((decode_mfma_kernel<T, D, RING, KVF>), dim3(grid), block, 0, stream, a);
       }

@@ -164,6 +164,53 @@ __device__ __forceinline__ uint32_t buffer_load4(__amdgpu_buffer_rsrc_t r, int o
   return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
 }
 
+// Nearest E4M3 code of a float, ties to the even code, magnitudes of 448
+// and above saturating to 448, NaN to the NaN code (OCP 8-bit float: bias
+// 7, 3 mantissa bits, exponent field 0 = subnormals of step 2^-9).
+__device__ __forceinline__ uint32_t e4m3_code(float x) {
+  const uint32_t bits = __float_as_uint(x);
+  const uint32_t sign = (bits >> 24) & 0x80u;
+  const float a = fabsf(x);
+  if (a != a) return 0x7Fu;
+  if (a >= 448.0f) return sign | 0x7Eu;
+  if (a < 0.015625f) {  // below 2^-6: a * 2^9 is exact; round it to an integer
+    return sign | (uint32_t)__builtin_rintf(a * 512.0f);  // 8 -> code 8 = 2^-6
+  }
+  // normal: drop 20 of the 23 fraction bits with round-to-nearest-even
+  const uint32_t ab = __float_as_uint(a);
+  const uint32_t r = (ab + 0x7FFFFu + ((ab >> 20) & 1u)) & 0xFFF00000u;
+  const uint32_t code = ((((r >> 23) - 127u + 7u) & 0xFu) << 3) | ((r >> 20) & 7u);
+  return sign | (code > 0x7Eu ? 0x7Eu : code);
+}
+
+// Nearest E5M2 code of a float, ties to the even code, magnitudes of 57344
+// and above (infinities too) saturating to 57344, NaN to 0x7F (OCP 8-bit
+// float: bias 15, 2 mantissa bits, exponent field 0 = subnormals of step
+// 2^-16, exponent field 31 = infinity / NaN, never produced here).
+__device__ __forceinline__ uint32_t e5m2_code(float x) {
+  const uint32_t bits = __float_as_uint(x);
+  const uint32_t sign = (bits >> 24) & 0x80u;
+  const float a = fabsf(x);
+  if (a != a) return 0x7Fu;
+  if (a >= 57344.0f) return sign | 0x7Bu;
+  if (a < 6.103515625e-05f) {  // below 2^-14: a * 2^16 is exact; round it to an integer
+    return sign | (uint32_t)__builtin_rintf(a * 65536.0f);  // 4 -> code 4 = 2^-14
+  }
+  // normal: drop 21 of the 23 fraction bits with round-to-nearest-even
+  const uint32_t ab = __float_as_uint(a);
+  const uint32_t r = (ab + 0xFFFFFu + ((ab >> 21) & 1u)) & 0xFFE00000u;
+  const uint32_t code = ((((r >> 23) - 127u + 15u) & 0x1Fu) << 2) | ((r >> 21) & 3u);
+  return sign | (code > 0x7Bu ? 0x7Bu : code);
+}
+
+// Code of format F (kKvE4M3 or kKvE5M2) of a float.
+template <int F>
+__device__ __forceinline__ uint32_t fp8_code(float x) {
+  static_assert(F == kKvE4M3 || F == kKvE5M2, "8-bit format");
+  if constexpr (F == kKvE5M2) return e5m2_code(x);
+  else return e4m3_code(x);
+}
+
 template <class T, int F, bool HI>
 __device__ __forceinline__ uint32_t code_pair_to_16(uint32_t w) {
   static_assert(F == kKvE4M3 || F == kKvE5M2, "8-bit format");

@@ -41,9 +41,10 @@ struct DecodeArgs {
   float *ws_o;   // partition-normalised outputs
   float *ws_ml;  // (running max in log2 units, sum)
   int32_t *ws_sched;  // MFMA kernel: tile prefix per sequence [B + 1]
-  // Append mode (MFMA kernel, plain paging, 16-bit pools): the new token of
-  // each sequence, key/value [B][Hkv][D], is written to app_slots[b] and
-  // attended from these inputs; the cache supplies the other L_b - 1 keys.
+  // Append mode (MFMA kernel, plain paging): the new token of each
+  // sequence, key/value [B][Hkv][D] in the activation dtype, is stored at
+  // app_slots[b] (8-bit pools: quantised with kv_inv) by the wave that
+  // streams the sequence's last tile, before it loads that tile.
   const void *app_key;
   const void *app_value;
   const int32_t *app_slots;
@@ -65,6 +66,7 @@ struct DecodeArgs {
   int32_t ring_window;
   float scale_log2;  // scale * log2(e)
   KvScales kv_scale;  // 8-bit pools: dequantisation scales per KV head
+  KvScales kv_inv;    // 8-bit pools in append mode: fp32(1 / scale), as the cache write uses
 };
 
 // Multi-token decode (several new tokens per sequence, causal).

@@ -4,9 +4,9 @@ token but the newest is written beforehand, the newest one's slot holds a
 NaN sentinel, and one call must both store the new rows (bit for bit, as
 pa_reshape_and_cache would) and attend over the full context, giving the
 same bits as pa_reshape_and_cache followed by pa_decode.  Covers the fused
-single-launch path (16-bit pools, GQA groups up to 16) on ragged, short,
-long and shared-prefix batches and on batches larger than one launch slice,
-and the two-step path (fp32 pools, wider groups, 8-bit pools).
+single-launch path (16-bit and 8-bit pools, GQA groups up to 16) on ragged,
+short, long and shared-prefix batches and on batches larger than one launch
+slice, and the two-step path (fp32 pools, wider groups).
 """
 import numpy as np
 import pytest
@@ -167,12 +167,21 @@ def test_append_two_step_paths(shape):
 
 
 @pytest.mark.parametrize("kv_format", ["e4m3", "e5m2"])
-def test_append_fp8_pool(kv_format):
-    print(f"append {kv_format}", flush=True)
-    case = workloads.config_fp8(lambda: workloads.make_paged_case("append_fp8", 8500, "bf16",
-                                                                  [1, 2, 16, 17, 1000], 32, 4, 128, 16),
-                                kv_format=kv_format)
+@pytest.mark.parametrize("shape", [("bf16", 32, 4, 128, [1, 2, 16, 17, 1000, 0, 5000]),
+                                   ("f16", 8, 8, 64, [3, 64, 65, 2000])], ids=["bf16-G8-D128", "f16-G1-D64"])
+def test_append_fp8_pool(kv_format, shape):
+    """8-bit pools: the launch quantises the new rows as the cache write does
+    (bit-exact pools) and attends over them."""
+    dtype, hq, hkv, d, lens = shape
+    print(f"append {kv_format} {shape}", flush=True)
+    case = workloads.config_fp8(lambda: workloads.make_paged_case("append_fp8", 8500 + hq, dtype, lens, hq, hkv, d,
+                                                                  16), kv_format=kv_format)
     _check(case)
+
+
+def test_append_fp8_llama70b():
+    print("append llama70b e4m3", flush=True)
+    _check(workloads.config_llama70b_fp8())
 
 
 def test_append_rejects_misaligned_inputs():
