@@ -504,7 +504,7 @@ def measure_multi(args) -> int:
         "data": "synthetic",
         "config": {"workload": (f"{name}: B {case.num_seqs}, q_len {case.q_len}, Hq {case.num_q_heads}, "
                                 f"Hkv {case.num_kv_heads}, D {case.head_dim}, "
-                                f"{'E4M3 KV, ' if case.kv_dtype else ''}{case.dtype}, block {case.block_size}, "
+                                f"{case.kv_dtype[4:].upper() + ' KV, ' if case.kv_dtype else ''}{case.dtype}, block {case.block_size}, "
                                 f"{c['tokens']} cached tokens (the new ones included)"),
                    "global_batch": case.num_seqs, "q_len": case.q_len, "seed": case.seed},
         "call_us": {"mean": round(mean_us, 2), "median": round(med_us, 2)},
