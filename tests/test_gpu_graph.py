@@ -71,3 +71,55 @@ def test_graph_replays_equal_eager(name):
         assert np.array_equal(torch_bits(dc.k_cache, c.dtype), k_ref)
         assert np.array_equal(torch_bits(dc.v_cache, c.dtype), v_ref)
     dc.pool.close()
+
+
+@pytest.mark.parametrize("name", ["llama70b_b64", "shared_prefix", "llama70b_b64_fp8"])
+def test_graph_of_the_one_call_step(name):
+    """pa_decode_append (the new tokens stored inside the decode launch)
+    captured once: every replay equals the eager call and the two-call step
+    bit for bit, cache included."""
+    import paged_kv_cache_145_amd as pk
+
+    case = workloads.FP8_CONFIGS[name]() if name in workloads.FP8_CONFIGS else workloads.CONFIGS[name]()
+    c = case
+    dc = DeviceCase(case)
+    dc.write_all()
+    mcl = int(c.context_lens.max())
+    ws = dc.workspace(mcl)
+    dt = torch.bfloat16 if c.dtype == "bf16" else torch.float16
+    step = c.step_writes()
+    slots = torch.from_numpy(np.concatenate([dc.slots_for(ch) for ch in step])).to(dc.device)
+    keys = raw_to_torch(np.concatenate([ch.keys for ch in step]), c.dtype).to(dc.device)
+    vals = raw_to_torch(np.concatenate([ch.values for ch in step]), c.dtype).to(dc.device)
+    out_two = torch.empty((c.num_seqs, c.num_q_heads, c.head_dim), dtype=dt, device=dc.device)
+    out_eager = torch.empty_like(out_two)
+    out_graph = torch.empty_like(out_two)
+    pk.reshape_and_cache(dc.pool, keys, vals, slots)
+    pk.decode(dc.pool, out_two, dc.query, dc.block_tables, dc.context_lens, mcl, c.scale, workspace=ws)
+
+    def step_call(out):
+        pk.decode_append(dc.pool, out, dc.query, keys, vals, slots, dc.block_tables, dc.context_lens, mcl,
+                         c.scale, workspace=ws)
+
+    step_call(out_eager)
+    torch.cuda.synchronize()
+    ref = torch_bits(out_two, c.dtype)
+    assert np.array_equal(torch_bits(out_eager, c.dtype), ref)
+    view = torch.uint8 if workloads.is_kv8(c.kv_dtype) else torch.int16
+    k_ref, v_ref = dc.k_cache.view(view).clone(), dc.v_cache.view(view).clone()
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=side):
+        step_call(out_graph)
+    torch.cuda.synchronize()
+    scratch = torch.ones(1 << 20, device=dc.device)
+    for rep in range(4):
+        out_graph.fill_(0)
+        g.replay()
+        scratch.mul_(1.0001).add_(rep)
+        torch.cuda.synchronize()
+        assert np.array_equal(torch_bits(out_graph, c.dtype), ref), f"replay {rep} differs"
+        assert torch.equal(dc.k_cache.view(view), k_ref) and torch.equal(dc.v_cache.view(view), v_ref)
+    dc.pool.close()
