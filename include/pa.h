@@ -425,6 +425,26 @@ int pa_decode_append(pa_pool *pool, void *out, const void *query, const void *ke
                      int32_t max_context_len, float scale, void *workspace, size_t workspace_bytes,
                      void *stream);
 
+/* Device: debug checks of the device-resident inputs that pa_decode,
+ * pa_decode_append and pa_reshape_and_cache trust without checking (their
+ * caller contract [P1 addressing: a block id must name a block of the
+ * pool; P4 paging: the table row maps each logical block]; the fast path
+ * clamps instead, so bad data gives an unspecified result but no fault).
+ * One small launch on `stream` writes counts (device int32 [4], 4-byte
+ * aligned; overwritten, need not be zeroed, no memset, safe to capture in
+ * a graph): counts[0] = lengths outside [0, max_context_len]; counts[1] =
+ * block-table entries that a decode reads (the first ceil(L / block_size)
+ * of row b, L = context_lens[b] clamped into [0, max_context_len], or
+ * min(L, sink + window) with ring != NULL) outside [0, num_blocks);
+ * counts[2] = slot_mapping entries at or beyond num_blocks * block_size
+ * (negative slots are padding, not errors); counts[3] = 0.  slot_mapping
+ * may be NULL when num_slot_entries == 0.  PA_ERR_INVAL on NULL or
+ * misaligned pointers or negative sizes. */
+int pa_check_decode_inputs(const pa_pool *pool, const int32_t *block_tables, int32_t max_blocks_per_seq,
+                           const int32_t *context_lens, int32_t num_seqs, int32_t max_context_len,
+                           const pa_ring *ring, const int32_t *slot_mapping, int32_t num_slot_entries,
+                           int32_t *counts, void *stream);
+
 /* Bytes of device workspace pa_decode_multi needs (tile schedule and
  * stream-K partials); 0 for num_seqs == 0 or invalid arguments. */
 size_t pa_decode_multi_workspace_bytes(const pa_pool *pool, int32_t num_seqs, int32_t q_len,

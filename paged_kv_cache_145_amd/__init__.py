@@ -17,7 +17,8 @@ from ._lib import PaRing
 
 __all__ = [
     "PaError", "Pool", "Ring", "ring_slot", "compute_slot_mapping", "reshape_and_cache",
-    "decode_workspace_bytes", "rope_table_bytes", "rope_table_init", "decode", "decode_append", "DTYPES",
+    "decode_workspace_bytes", "rope_table_bytes", "rope_table_init", "decode", "decode_append",
+    "check_decode_inputs", "DTYPES",
     "block_hashes", "copy_blocks", "decode_multi_workspace_bytes", "decode_multi", "Batcher",
 ]
 
@@ -334,6 +335,23 @@ def decode_append(pool: Pool, out, query, key, value, slot_mapping, block_tables
         _dev_ptr(block_tables, "block_tables"), int(block_tables.shape[1]),
         _dev_ptr(context_lens, "context_lens"), b, hq, int(max_context_len), float(scale),
         ws_ptr, ws_bytes, _stream_ptr(stream)), "pa_decode_append")
+
+
+def check_decode_inputs(pool: Pool, block_tables, context_lens, max_context_len: int,
+                        ring: Optional[Ring] = None, slot_mapping=None, counts=None, stream=None):
+    """Debug counts (device int32 [4]) of out-of-range lengths, block ids a
+    decode reads, and slots; see pa_check_decode_inputs.  Asynchronous."""
+    import torch
+
+    if counts is None:
+        counts = torch.empty(4, dtype=torch.int32, device=block_tables.device)
+    n_slots = 0 if slot_mapping is None else int(slot_mapping.shape[0])
+    _check(_lib.load().pa_check_decode_inputs(
+        pool.handle, _dev_ptr(block_tables, "block_tables"), int(block_tables.shape[1]),
+        _dev_ptr(context_lens, "context_lens"), int(context_lens.shape[0]), int(max_context_len),
+        _ring_ptr(ring), None if slot_mapping is None else _dev_ptr(slot_mapping, "slot_mapping"), n_slots,
+        _dev_ptr(counts, "counts"), _stream_ptr(stream)), "pa_check_decode_inputs")
+    return counts
 
 
 def decode_multi_workspace_bytes(pool: Pool, num_seqs: int, q_len: int, num_q_heads: int,

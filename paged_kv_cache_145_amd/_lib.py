@@ -94,6 +94,8 @@ SIGNATURES = {
     "pa_decode_multi_workspace_bytes": (_sz, [_p, _i32, _i32, _i32, _i32]),
     "pa_decode_multi": (ctypes.c_int, [_p, _p, _p, _p, _i32, _p, _i32, _i32, _i32, _i32, ctypes.c_float,
                                        _p, _sz, _p]),
+    "pa_check_decode_inputs": (ctypes.c_int, [_p, _p, _i32, _p, _i32, _i32, ctypes.POINTER(PaRing), _p, _i32,
+                                              _p, _p]),
     "pa_status_str": (ctypes.c_char_p, [ctypes.c_int]),
     "pa_last_hip_error": (ctypes.c_char_p, []),
 }

@@ -293,6 +293,27 @@ size_t pa_rope_table_bytes(int32_t capacity, int32_t head_dim) {
   return (size_t)capacity * (size_t)(head_dim / 2) * 2 * sizeof(float);
 }
 
+int pa_check_decode_inputs(const pa_pool *pool, const int32_t *block_tables, int32_t max_blocks_per_seq,
+                           const int32_t *context_lens, int32_t num_seqs, int32_t max_context_len,
+                           const pa_ring *ring, const int32_t *slot_mapping, int32_t num_slot_entries,
+                           int32_t *counts, void *stream) {
+  if (pool == nullptr || counts == nullptr || num_seqs < 0 || num_slot_entries < 0 || max_context_len < 0 ||
+      max_blocks_per_seq < 0)
+    return PA_ERR_INVAL;
+  if (num_seqs > 0 && (block_tables == nullptr || context_lens == nullptr || max_blocks_per_seq == 0))
+    return PA_ERR_INVAL;
+  if (num_slot_entries > 0 && slot_mapping == nullptr) return PA_ERR_INVAL;
+  if ((reinterpret_cast<uintptr_t>(counts) | reinterpret_cast<uintptr_t>(block_tables) |
+       reinterpret_cast<uintptr_t>(context_lens) | reinterpret_cast<uintptr_t>(slot_mapping)) & 3u)
+    return PA_ERR_INVAL;
+  if (ring != nullptr && (ring->sink < 0 || ring->window < 1)) return PA_ERR_INVAL;
+  const int32_t capacity = ring != nullptr ? ring->sink + ring->window : 0;
+  return pa::hip_status(pa::launch_check_inputs(
+      block_tables, max_blocks_per_seq, context_lens, num_seqs, max_context_len, pool->block_size,
+      pool->num_blocks, capacity, slot_mapping, num_slot_entries, (int64_t)pool->num_blocks * pool->block_size,
+      counts, static_cast<hipStream_t>(stream)));
+}
+
 int pa_rope_table_init(float *table, int32_t capacity, int32_t head_dim, float rope_base,
                        void *stream) {
   if (table == nullptr || capacity <= 0 || (head_dim != 64 && head_dim != 128)) return PA_ERR_INVAL;

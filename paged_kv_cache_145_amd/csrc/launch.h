@@ -154,6 +154,13 @@ hipError_t launch_copy_blocks(void *k_cache, void *v_cache, const int32_t *src_b
                               const int32_t *dst_blocks, int32_t num_pairs, int32_t num_blocks,
                               int64_t block_bytes, hipStream_t stream);
 
+// Debug checks of device-resident decode inputs (counts[4], see pa.h).
+hipError_t launch_check_inputs(const int32_t *block_tables, int32_t max_blocks_per_seq,
+                               const int32_t *context_lens, int32_t num_seqs, int32_t max_context,
+                               int32_t block_size, int32_t num_blocks, int32_t ring_capacity,
+                               const int32_t *slots, int32_t num_slot_entries, int64_t num_slots,
+                               int32_t *counts, hipStream_t stream);
+
 hipError_t launch_rope_table_init(float *table, int32_t capacity, int32_t head_dim,
                                   float rope_base, hipStream_t stream);
 

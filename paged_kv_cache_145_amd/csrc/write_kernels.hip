@@ -177,6 +177,65 @@ hipError_t launch_copy_blocks(void *k_cache, void *v_cache, const int32_t *src_b
   return hipGetLastError();
 }
 
+// Checks of the device-resident inputs the fast path trusts, one work-group:
+// counts of lengths outside [0, max_context], of block-table entries a
+// decode reads (the first ceil(L / block_size) of each row, L the resident
+// key count) outside [0, num_blocks), and of slots at or beyond num_slots.
+// Thread 0 stores the three counts and a zero; no atomics, no memset.
+__global__ __launch_bounds__(256) void check_inputs_kernel(
+    const int32_t *__restrict__ block_tables, int32_t max_blocks_per_seq,
+    const int32_t *__restrict__ context_lens, int32_t num_seqs, int32_t max_context,
+    int32_t block_size, int32_t num_blocks, int32_t ring_capacity,
+    const int32_t *__restrict__ slots, int32_t num_slot_entries, int64_t num_slots,
+    int32_t *__restrict__ counts) {
+  __shared__ int32_t s_red[3][256];
+  int32_t bad_len = 0, bad_block = 0, bad_slot = 0;
+  for (int b = threadIdx.x; b < num_seqs; b += blockDim.x) {
+    const int32_t n = context_lens[b];
+    if (n < 0 || n > max_context) ++bad_len;
+  }
+  // rows of the tables: one sequence at a time, its entries across threads
+  for (int b = 0; b < num_seqs; ++b) {
+    int32_t n = context_lens[b];
+    n = n < 0 ? 0 : (n > max_context ? max_context : n);
+    const int32_t keys = ring_capacity > 0 && n > ring_capacity ? ring_capacity : n;
+    const int32_t need = (keys + block_size - 1) / block_size;
+    const int32_t lim = need < max_blocks_per_seq ? need : max_blocks_per_seq;
+    for (int j = threadIdx.x; j < lim; j += blockDim.x) {
+      const int32_t id = block_tables[(int64_t)b * max_blocks_per_seq + j];
+      if (id < 0 || id >= num_blocks) ++bad_block;
+    }
+  }
+  for (int i = threadIdx.x; i < num_slot_entries; i += blockDim.x)
+    if ((int64_t)slots[i] >= num_slots) ++bad_slot;
+  s_red[0][threadIdx.x] = bad_len;
+  s_red[1][threadIdx.x] = bad_block;
+  s_red[2][threadIdx.x] = bad_slot;
+  __syncthreads();
+  for (int w = 128; w > 0; w >>= 1) {
+    if ((int)threadIdx.x < w)
+      for (int k = 0; k < 3; ++k) s_red[k][threadIdx.x] += s_red[k][threadIdx.x + w];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) {
+    counts[0] = s_red[0][0];
+    counts[1] = s_red[1][0];
+    counts[2] = s_red[2][0];
+    counts[3] = 0;
+  }
+}
+
+hipError_t launch_check_inputs(const int32_t *block_tables, int32_t max_blocks_per_seq,
+                               const int32_t *context_lens, int32_t num_seqs, int32_t max_context,
+                               int32_t block_size, int32_t num_blocks, int32_t ring_capacity,
+                               const int32_t *slots, int32_t num_slot_entries, int64_t num_slots,
+                               int32_t *counts, hipStream_t stream) {
+  hipLaunchKernelGGL(check_inputs_kernel, dim3(1), dim3(256), 0, stream, block_tables, max_blocks_per_seq,
+                     context_lens, num_seqs, max_context, block_size, num_blocks, ring_capacity, slots,
+                     num_slot_entries, num_slots, counts);
+  return hipGetLastError();
+}
+
 hipError_t launch_rope_table_init(float *table, int32_t capacity, int32_t head_dim,
                                   float rope_base, hipStream_t stream) {
   const int64_t total = (int64_t)capacity * (head_dim / 2);

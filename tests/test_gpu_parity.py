@@ -367,3 +367,45 @@ def test_ring_small_groups(hq, hkv, kernel):
         out = dc.decode(max_context_len=100_000)
     assert_parity(out, ref, "f16")
     dc.close()
+
+
+@pytest.mark.parametrize("ring", [False, True])
+def test_input_checks_count_exactly_the_planted_errors(ring):
+    """pa_check_decode_inputs reads zeros on valid inputs; with two bad
+    lengths, two bad block ids among the entries a decode reads, one bad id
+    past them, one padding slot and one slot past the pool it reads exactly
+    [2, 2, 1, 0]."""
+    import paged_kv_cache_145_amd as pk
+
+    if ring:  # 1,024 resident keys: a 3,000-token row reads 64 entries
+        case = workloads.config_sink_ring(lengths=[5, 1030, 3000, 0])
+        long_row, reads = 2, 64
+    else:
+        case = workloads.make_paged_case("checks", 7700, "bf16", [0, 5, 40, 700, 33], 8, 2, 64, 16)
+        long_row, reads = 2, 3  # 40 tokens: 3 entries
+    dc = DeviceCase(case)
+    mcl = int(case.context_lens.max())
+    slots = np.concatenate([dc.slots_for(ch) for ch in case.step_writes()]).astype(np.int32)
+    counts = pk.check_decode_inputs(dc.pool, dc.block_tables, dc.context_lens, mcl, ring=dc.ring,
+                                    slot_mapping=torch.from_numpy(slots).to(dc.device))
+    torch.cuda.synchronize()
+    assert counts.cpu().tolist() == [0, 0, 0, 0]
+    lens = case.context_lens.copy()
+    tables = case.block_tables.copy()
+    last = case.num_seqs - 1
+    lens[0] = -3                    # bad length; read as 0 (no entries)
+    lens[last] = mcl + 9            # bad length; read as max_context_len
+    tables[last, :] = 0             # so the clamped read of that row finds valid ids
+    tables[long_row, 0] = case.num_blocks  # read by a decode: counted
+    tables[long_row, reads - 1] = -7       # the last entry read: counted
+    if reads < tables.shape[1]:
+        tables[long_row, reads] = 10 ** 6  # past the entries read: not counted
+    bad_slots = slots.copy()
+    bad_slots[0] = -1               # padding: not counted
+    bad_slots[-1] = case.num_blocks * case.block_size  # past the pool: counted
+    counts = pk.check_decode_inputs(dc.pool, torch.from_numpy(tables).to(dc.device),
+                                    torch.from_numpy(lens).to(dc.device), mcl, ring=dc.ring,
+                                    slot_mapping=torch.from_numpy(bad_slots).to(dc.device))
+    torch.cuda.synchronize()
+    assert counts.cpu().tolist() == [2, 2, 1, 0]
+    dc.close()

@@ -259,6 +259,15 @@ def test_decode_and_write_argument_validation(lib):
     assert lib.pa_decode_workspace_bytes(h, 2, 16, 100, None) > 0
     # zero sequences is a no-op
     assert lib.pa_decode(h, None, None, None, 4, None, 0, 4, 10, 0.1, None, None, 0, None) == 0
+    # debug input checks: pointer, alignment and size validation on the host
+    cnt = ctypes.c_void_p((1 << 24) + 64)
+    assert lib.pa_check_decode_inputs(None, dev, 4, dev, 2, 10, None, None, 0, cnt, None) == -1
+    assert lib.pa_check_decode_inputs(h, dev, 4, dev, 2, 10, None, None, 0, None, None) == -1
+    assert lib.pa_check_decode_inputs(h, None, 4, dev, 2, 10, None, None, 0, cnt, None) == -1
+    assert lib.pa_check_decode_inputs(h, dev, 4, dev, -1, 10, None, None, 0, cnt, None) == -1
+    assert lib.pa_check_decode_inputs(h, dev, 4, dev, 2, 10, None, None, 3, cnt, None) == -1  # slots missing
+    assert lib.pa_check_decode_inputs(h, dev, 4, dev, 2, 10, None, None, 0, ctypes.c_void_p((1 << 24) + 2),
+                                      None) == -1
     # decode with append: the decode's checks, plus the new rows' pointers
     mis = ctypes.c_void_p((1 << 24) + 8)
     args = (4, dev, 2, 4, 10, 0.1)
