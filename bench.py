@@ -806,15 +806,15 @@ def main() -> int:
 
     group = case.num_q_heads // case.num_kv_heads
     # the one-call step is a single launch on the MFMA path (f16/bf16 or
-    # 8-bit pools, groups up to 16) without the ring; elsewhere the library
-    # would run the two calls in turn, so the bench times them as two calls
+    # 8-bit pools, groups up to 16); elsewhere the library would run the
+    # two calls in turn, so the bench times them as two calls
     mfma = case.dtype != "f32" and 1 <= group <= 16 and os.environ.get("PA_FORCE_VALU", "0") in ("", "0")
-    fused = args.step == "fused" and ring is None and mfma
+    fused = args.step == "fused" and mfma
 
     def decode():
         if fused:  # stores the step's new tokens and decodes in one call
             pk.decode_append(pool, out, query, step_keys, step_vals, step_slots_d, tables, lens, max_ctx,
-                             case.scale, workspace=ws)
+                             case.scale, ring=ring, workspace=ws)
         else:
             pk.decode(pool, out, query, tables, lens, max_ctx, case.scale, ring=ring, workspace=ws)
 

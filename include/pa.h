@@ -405,25 +405,27 @@ int pa_decode(pa_pool *pool, void *out, const void *query, const int32_t *block_
  * context_lens[b] tokens, the last of which (position context_lens[b] - 1)
  * is that new token.  The result, cache contents and output, is bit for bit
  * that of pa_reshape_and_cache(key, value, slot_mapping, num_seqs) followed
- * by pa_decode (ring = NULL), including padding: a negative slot, or one at
+ * by pa_decode (same ring), including padding: a negative slot, or one at
  * or beyond num_blocks * block_size, stores nothing.  Caller contract:
  * slot_mapping[b] is the slot of position context_lens[b] - 1 through
- * block_tables[b] (or padding), it is -1 where context_lens[b] == 0, no
+ * block_tables[b] (ring != NULL: of its ring slot Slot(context_lens[b] - 1))
+ * (or padding), it is -1 where context_lens[b] == 0, no
  * other sequence of the call reads it, and slots are distinct; otherwise
  * the result is unspecified (no fault).  On f16/bf16 and 8-bit pools with
  * num_q_heads / num_kv_heads <= 16 both happen in the decode launch: the
- * wave that streams a sequence's last tile for KV head g stores the new rows
- * of head g (8-bit pools: quantised exactly as pa_reshape_and_cache does)
- * just before it loads that tile.  Other pools (fp32, wider groups) run the
- * two calls in turn.  Other
- * arguments, the workspace size (pa_decode_workspace_bytes with ring =
- * NULL) and errors are those of pa_decode; key and value must be 16-byte
+ * wave that streams the tile holding a sequence's newest token for KV head
+ * g (its last tile; ring mode: the tile of its ring slot) stores the new
+ * rows of head g (8-bit pools: quantised exactly as pa_reshape_and_cache
+ * does) just before it loads that tile.  Other pools (fp32, wider groups)
+ * run the two calls in turn.  Other
+ * arguments, the workspace size (pa_decode_workspace_bytes with the same
+ * ring) and errors are those of pa_decode; key and value must be 16-byte
  * aligned and slot_mapping 4-byte aligned (PA_ERR_INVAL otherwise). */
 int pa_decode_append(pa_pool *pool, void *out, const void *query, const void *key, const void *value,
                      const int32_t *slot_mapping, const int32_t *block_tables, int32_t max_blocks_per_seq,
                      const int32_t *context_lens, int32_t num_seqs, int32_t num_q_heads,
-                     int32_t max_context_len, float scale, void *workspace, size_t workspace_bytes,
-                     void *stream);
+                     int32_t max_context_len, float scale, const pa_ring *ring, void *workspace,
+                     size_t workspace_bytes, void *stream);
 
 /* Device: debug checks of the device-resident inputs that pa_decode,
  * pa_decode_append and pa_reshape_and_cache trust without checking (their

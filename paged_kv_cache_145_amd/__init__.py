@@ -309,7 +309,8 @@ def decode(pool: Pool, out, query, block_tables, context_lens, max_context_len: 
 
 
 def decode_append(pool: Pool, out, query, key, value, slot_mapping, block_tables, context_lens,
-                  max_context_len: int, scale: float, workspace=None, stream=None) -> None:
+                  max_context_len: int, scale: float, ring: Optional[Ring] = None, workspace=None,
+                  stream=None) -> None:
     """One decode step that also stores each sequence's new token: key/value
     [B, Hkv, D] go to slot_mapping [B] (the slot of position
     context_lens[b] - 1) and ``out`` [B, Hq, D] is the decode attention over
@@ -334,7 +335,7 @@ def decode_append(pool: Pool, out, query, key, value, slot_mapping, block_tables
         _dev_ptr(value, "value"), _dev_ptr(slot_mapping, "slot_mapping"),
         _dev_ptr(block_tables, "block_tables"), int(block_tables.shape[1]),
         _dev_ptr(context_lens, "context_lens"), b, hq, int(max_context_len), float(scale),
-        ws_ptr, ws_bytes, _stream_ptr(stream)), "pa_decode_append")
+        _ring_ptr(ring), ws_ptr, ws_bytes, _stream_ptr(stream)), "pa_decode_append")
 
 
 def check_decode_inputs(pool: Pool, block_tables, context_lens, max_context_len: int,

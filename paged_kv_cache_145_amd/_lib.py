@@ -90,7 +90,7 @@ SIGNATURES = {
     "pa_decode": (ctypes.c_int, [_p, _p, _p, _p, _i32, _p, _i32, _i32, _i32, ctypes.c_float,
                                  ctypes.POINTER(PaRing), _p, _sz, _p]),
     "pa_decode_append": (ctypes.c_int, [_p, _p, _p, _p, _p, _p, _p, _i32, _p, _i32, _i32, _i32,
-                                        ctypes.c_float, _p, _sz, _p]),
+                                        ctypes.c_float, ctypes.POINTER(PaRing), _p, _sz, _p]),
     "pa_decode_multi_workspace_bytes": (_sz, [_p, _i32, _i32, _i32, _i32]),
     "pa_decode_multi": (ctypes.c_int, [_p, _p, _p, _p, _i32, _p, _i32, _i32, _i32, _i32, ctypes.c_float,
                                        _p, _sz, _p]),

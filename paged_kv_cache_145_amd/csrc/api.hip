@@ -414,7 +414,7 @@ int decode_impl(pa_pool *pool, void *out, const void *query, const int32_t *bloc
   if ((int64_t)pool->num_kv_heads * nchunk > INT32_MAX) return PA_ERR_UNSUPPORTED;
   if (app != nullptr) {
     // the MFMA kernel appends in the same launch; other paths write first
-    const bool fused = choice.kernel == pa::DecodeKernel::kMfma && ring == nullptr && pool->dtype != PA_F32;
+    const bool fused = choice.kernel == pa::DecodeKernel::kMfma && pool->dtype != PA_F32;
     if (fused) {
       a.app_key = app->key;
       a.app_value = app->value;
@@ -447,8 +447,8 @@ int pa_decode(pa_pool *pool, void *out, const void *query, const int32_t *block_
 int pa_decode_append(pa_pool *pool, void *out, const void *query, const void *key, const void *value,
                      const int32_t *slot_mapping, const int32_t *block_tables, int32_t max_blocks_per_seq,
                      const int32_t *context_lens, int32_t num_seqs, int32_t num_q_heads,
-                     int32_t max_context_len, float scale, void *workspace, size_t workspace_bytes,
-                     void *stream) {
+                     int32_t max_context_len, float scale, const pa_ring *ring, void *workspace,
+                     size_t workspace_bytes, void *stream) {
   if (pool == nullptr || num_seqs < 0) return PA_ERR_INVAL;
   if (num_seqs == 0) return PA_OK;
   if (key == nullptr || value == nullptr || slot_mapping == nullptr) return PA_ERR_INVAL;
@@ -456,7 +456,7 @@ int pa_decode_append(pa_pool *pool, void *out, const void *query, const void *ke
   if ((reinterpret_cast<uintptr_t>(slot_mapping) & 3u) != 0) return PA_ERR_INVAL;
   const pa::AppendInputs app{key, value, slot_mapping};
   return pa::decode_impl(pool, out, query, block_tables, max_blocks_per_seq, context_lens, num_seqs,
-                         num_q_heads, max_context_len, scale, nullptr, workspace, workspace_bytes, stream,
+                         num_q_heads, max_context_len, scale, ring, workspace, workspace_bytes, stream,
                          &app);
 }
 

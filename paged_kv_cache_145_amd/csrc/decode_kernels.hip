@@ -330,16 +330,23 @@ struct MfmaLds {
 // before b (exclusive prefix of ceil(L_b / 16)), s_len[b] = L_b.  Work-group
 // 0 also publishes s_tfirst to the workspace for the reduce kernel.
 __device__ int build_tile_schedule(const DecodeArgs &a, bool ring, int *s_tfirst, int *s_len,
-                                   int *s_wsum) {
+                                   int *s_wsum, int *s_newslot = nullptr) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   int carry = 0;
   for (int base = 0; base < a.num_seqs; base += kNW * kWave) {
     const int b = base + tid;
     int v = 0;
     if (b < a.num_seqs) {
-      const int L = effective_len(a, a.context_lens[b], ring);
+      const int n = a.context_lens[b];
+      const int L = effective_len(a, n, ring);
       s_len[b] = L;
       v = (L + kTileTokens - 1) / kTileTokens;
+      if (s_newslot != nullptr) {  // ring slot of the newest resident token (-1: none)
+        const int pos = (n < a.max_context ? n : a.max_context) - 1;
+        s_newslot[b] = L <= 0 ? -1
+                       : pos < a.ring_sink ? pos
+                                           : a.ring_sink + (pos - a.ring_sink) % a.ring_window;
+      }
     }
     int x = v;
 #pragma unroll
@@ -415,11 +422,12 @@ void decode_mfma_kernel(DecodeArgs a) {
 
   __shared__ int s_tfirst[kMaxSchedSeqs + 1];
   __shared__ int s_len[kMaxSchedSeqs];
+  __shared__ int s_newslot[(RING && APP) ? kMaxSchedSeqs : 1];  // ring append only
   __shared__ int s_wsum[kNW];
   __shared__ __align__(16) char s_vtiles[kNW][MfmaLds<D>::kVBytes];
   __shared__ uint4 s_q[kNW][kQSlots * KB * kWave];  // query fragments, lane-major
 
-  const int total = build_tile_schedule(a, RING, s_tfirst, s_len, s_wsum);
+  const int total = build_tile_schedule(a, RING, s_tfirst, s_len, s_wsum, (RING && APP) ? s_newslot : nullptr);
   const int hkv = a.num_kv_heads;
   const int G = a.group;
   const int lane = threadIdx.x & 63;
@@ -475,7 +483,8 @@ void decode_mfma_kernel(DecodeArgs a) {
   // so the result equals a cache write followed by the decode.  A lane
   // group of 2 * D * 2 / 16 lanes carries one sequence's two input rows in
   // 16-byte pieces (K first); a piece stores 16 bytes, or 8 codes.
-  static_assert(!APP || !RING, "appending needs plain paging");
+  // Ring mode: the newest token's ring slot Slot(n - 1) picks its tile,
+  // which need not be the sequence's last.
   constexpr int kPiecesPerRow = D * (int)sizeof(st) / 16;
   constexpr int kLanesPerEnd = 2 * kPiecesPerRow;
   constexpr int kEndsPerRound = kWave / kLanesPerEnd;
@@ -547,7 +556,8 @@ void decode_mfma_kernel(DecodeArgs a) {
     u32x4 arow[kAppRounds];
     int aslot[kAppRounds], absel[kAppRounds];
     if constexpr (APP) {
-      ends = __ballot(lane < cnt && c0 + lane >= app_hi && tt == tiles - 1);
+      const bool holds_new = RING ? (s_newslot[tb] >= 0 && s_newslot[tb] / kTileTokens == tt) : tt == tiles - 1;
+      ends = __ballot(lane < cnt && c0 + lane >= app_hi && holds_new);
       app_hi = c0 + cnt;
       app_load(ends, arow, aslot, absel);
     }
@@ -1160,8 +1170,8 @@ hipError_t launch_typed(const DecodeArgs &a, DecodeChoice choice, hipStream_t st
       // at least one group of Hkv waves
       const int grid = std::max(grid_max, (a.num_kv_heads + kNW - 1) / kNW);
       if (a.app_key != nullptr) {
-        if constexpr (RING) return hipErrorInvalidValue;
-        else hipLaunchKernelGGL((decode_mfma_kernel<T, D, false, KVF, true>), dim3(grid), block, 0, stream, a);
+        if constexpr (RING && KV8) return hipErrorInvalidValue;
+        else hipLaunchKernelGGL((decode_mfma_kernel<T, D, RING, KVF, true>), dim3(grid), block, 0, stream, a);
       } else {
         hipLaunchKernelGGL((decode_mfma_kernel<T, D, RING, KVF>), dim3(grid), block, 0, stream, a);
       }

@@ -49,12 +49,12 @@ def _append(dc, case, slots, keys, vals, max_ctx=None):
     mcl = int(case.context_lens.max()) if max_ctx is None else max_ctx
     out = torch.full((case.num_seqs, case.num_q_heads, case.head_dim), float("nan"), dtype=TORCH_DTYPES[dt],
                      device=dc.device)
-    nbytes = pk.decode_workspace_bytes(dc.pool, case.num_seqs, case.num_q_heads, mcl)
+    nbytes = pk.decode_workspace_bytes(dc.pool, case.num_seqs, case.num_q_heads, mcl, dc.ring)
     ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dc.device)
     ws.fill_(0xFF)  # the workspace needs no initialisation
     pk.decode_append(dc.pool, out, dc.query, raw_to_torch(keys, dt).to(dc.device),
                      raw_to_torch(vals, dt).to(dc.device), torch.from_numpy(slots).to(dc.device),
-                     dc.block_tables, dc.context_lens, mcl, case.scale, workspace=ws)
+                     dc.block_tables, dc.context_lens, mcl, case.scale, ring=dc.ring, workspace=ws)
     torch.cuda.synchronize()
     return out
 
@@ -144,6 +144,14 @@ def test_append_padding_slot_writes_nothing():
     _same_pools(dc, dc2, dt)
     for x in (dc, full, dc2, full2):
         x.close()
+
+
+def test_append_sink_ring():
+    """Ring mode: the newest token's ring slot picks the tile that stores it
+    (not the last tile once a context has wrapped), lengths from 1 to 100,000
+    around every wrap boundary."""
+    print("append sink ring", flush=True)
+    _check(workloads.config_sink_ring())
 
 
 def test_append_more_sequences_than_one_launch_slice():

@@ -73,14 +73,14 @@ def test_graph_replays_equal_eager(name):
     dc.pool.close()
 
 
-@pytest.mark.parametrize("name", ["llama70b_b64", "shared_prefix", "llama70b_b64_fp8"])
+@pytest.mark.parametrize("name", ["llama70b_b64", "shared_prefix", "llama70b_b64_fp8", "sink_ring"])
 def test_graph_of_the_one_call_step(name):
     """pa_decode_append (the new tokens stored inside the decode launch)
     captured once: every replay equals the eager call and the two-call step
     bit for bit, cache included."""
     import paged_kv_cache_145_amd as pk
 
-    case = workloads.FP8_CONFIGS[name]() if name in workloads.FP8_CONFIGS else workloads.CONFIGS[name]()
+    case = workloads.FP8_CONFIGS[name]() if name in workloads.FP8_CONFIGS else _case(name)
     c = case
     dc = DeviceCase(case)
     dc.write_all()
@@ -95,11 +95,12 @@ def test_graph_of_the_one_call_step(name):
     out_eager = torch.empty_like(out_two)
     out_graph = torch.empty_like(out_two)
     pk.reshape_and_cache(dc.pool, keys, vals, slots)
-    pk.decode(dc.pool, out_two, dc.query, dc.block_tables, dc.context_lens, mcl, c.scale, workspace=ws)
+    pk.decode(dc.pool, out_two, dc.query, dc.block_tables, dc.context_lens, mcl, c.scale, ring=dc.ring,
+              workspace=ws)
 
     def step_call(out):
         pk.decode_append(dc.pool, out, dc.query, keys, vals, slots, dc.block_tables, dc.context_lens, mcl,
-                         c.scale, workspace=ws)
+                         c.scale, ring=dc.ring, workspace=ws)
 
     step_call(out_eager)
     torch.cuda.synchronize()

@@ -270,7 +270,7 @@ def test_decode_and_write_argument_validation(lib):
                                       None) == -1
     # decode with append: the decode's checks, plus the new rows' pointers
     mis = ctypes.c_void_p((1 << 24) + 8)
-    args = (4, dev, 2, 4, 10, 0.1)
+    args = (4, dev, 2, 4, 10, 0.1, None)
     assert lib.pa_decode_append(None, dev, dev, dev, dev, dev, dev, *args, None, 0, None) == -1
     assert lib.pa_decode_append(h, dev, dev, None, dev, dev, dev, *args, None, 0, None) == -1
     assert lib.pa_decode_append(h, dev, dev, dev, None, dev, dev, *args, None, 0, None) == -1
@@ -279,9 +279,11 @@ def test_decode_and_write_argument_validation(lib):
     assert lib.pa_decode_append(h, dev, dev, dev, mis, dev, dev, *args, None, 0, None) == -1
     assert lib.pa_decode_append(h, dev, dev, dev, dev, ctypes.c_void_p((1 << 24) + 2), dev, *args,
                                 None, 0, None) == -1
-    assert lib.pa_decode_append(h, dev, dev, dev, dev, dev, dev, 4, dev, 2, 3, 10, 0.1, None, 0, None) == -1
-    assert lib.pa_decode_append(h, dev, dev, dev, dev, dev, dev, 256, dev, 2, 4, 4096, 0.1, None, 0, None) == -2
-    assert lib.pa_decode_append(h, None, None, None, None, None, None, 4, None, 0, 4, 10, 0.1, None, 0, None) == 0
+    assert lib.pa_decode_append(h, dev, dev, dev, dev, dev, dev, 4, dev, 2, 3, 10, 0.1, None, None, 0, None) == -1
+    assert lib.pa_decode_append(h, dev, dev, dev, dev, dev, dev, 256, dev, 2, 4, 4096, 0.1, None, None, 0,
+                                None) == -2
+    assert lib.pa_decode_append(h, None, None, None, None, None, None, 4, None, 0, 4, 10, 0.1, None, None, 0,
+                                None) == 0
     # writes
     assert lib.pa_reshape_and_cache(h, None, None, None, 0, None) == 0
     assert lib.pa_reshape_and_cache(h, None, dev, dev, 3, None) == -1
