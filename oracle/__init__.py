@@ -70,7 +70,7 @@ from .paged_attention import (  # noqa: F401
     ring_cache_index,
     rope_inv_freq,
     rope_rotate_half,
-    round_to_dtype,
+    ring_writer,
 )
 from .allocator import BlockAllocatorModel  # noqa: F401
 from . import sizes  # noqa: F401

@@ -15,10 +15,11 @@ Sources (web pages; cited by title and section):
   each request has its own table; blocks may be shared.
 * Page "wzjinhao.cn/news/69573" (deferred speculative decoding with a
   circular context), section "环形上下文与注意力沉淀机制", the Slot(pos)
-  equation: slot = pos for pos < S, else S + ((pos - S) mod W); and the
-  C++ ring-cache listing's valid-index enumeration (sinks first, then the
-  window oldest first); keys must be rotated so that RoPE keeps the right
-  relative distance as the ring slides.
+  equation: slot = pos for pos < S, else S + ((pos - S) mod W); section
+  "C++ 环形 KV 缓存管理内核实现": the resident keys are taken in cache order
+  (sinks first, then the window oldest first), which here follows from the
+  last position written to each slot; keys must be rotated so that RoPE
+  keeps the right relative distance as the ring slides.
 
 The pages do not define the softmax itself; decode here is the textbook
 single-query attention: scores s_t = scale * <q, k_t>, weights
@@ -42,25 +43,6 @@ def to_f64(raw: np.ndarray, dtype: str) -> np.ndarray:
     if dtype == "bf16":
         bits = np.asarray(raw).astype(np.uint32) << np.uint32(16)
         return bits.view(np.float32).astype(np.float64)
-    raise ValueError(f"unknown dtype {dtype!r}")
-
-
-def round_to_dtype(x: np.ndarray, dtype: str) -> np.ndarray:
-    """Round float64 values to the storage dtype (nearest-even), as float64.
-
-    Used only to model the final cast of an output to the query dtype.
-    bf16: round the float32 value to the upper 16 bits, ties to even.
-    """
-    if dtype == "f32":
-        return np.asarray(x, dtype=np.float32).astype(np.float64)
-    if dtype == "f16":
-        return np.asarray(x, dtype=np.float16).astype(np.float64)
-    if dtype == "bf16":
-        f = np.asarray(x, dtype=np.float32)
-        bits = f.view(np.uint32).astype(np.uint64)
-        lsb = (bits >> np.uint64(16)) & np.uint64(1)
-        rounded = ((bits + np.uint64(0x7FFF) + lsb) >> np.uint64(16)) << np.uint64(16)
-        return rounded.astype(np.uint32).view(np.float32).astype(np.float64)
     raise ValueError(f"unknown dtype {dtype!r}")
 
 
@@ -106,21 +88,32 @@ def ring_slot(pos: int, sink: int, window: int) -> int:
     return int(sink + (pos - sink) % window)
 
 
+def ring_writer(slot: int, n: int, sink: int, window: int) -> int:
+    """Logical position whose key a ring slot holds after positions 0..n-1
+    were written in order, or -1 if no position has reached the slot.
+
+    By the Slot(pos) equation a sink slot r < S is written only by position
+    r, and a window slot r >= S by the positions r, r + W, r + 2W, ...; the
+    slot keeps the last of them below n.
+    """
+    if slot < 0 or slot >= sink + window or slot > n - 1:
+        return -1
+    if slot < sink:
+        return int(slot)
+    return int(slot + window * ((n - 1 - slot) // window))
+
+
 def ring_cache_order(n: int, sink: int, window: int) -> list:
     """Ring slots of the resident keys in cache order after n appends.
 
-    Up to S + W appends nothing has been overwritten: slots 0..n-1.  Beyond
-    that, the sink slots come first, then the window's slots from the oldest
-    resident position (n - W) to the newest (n - 1).
+    Cache order is the order of the logical positions the resident keys
+    hold (so the sink keys, positions 0..S-1, come first, then the window
+    from its oldest surviving position to the newest): every slot that a
+    position has reached is resident, sorted by the position of its last
+    writer.
     """
-    capacity = sink + window
-    if n <= capacity:
-        return list(range(n))
-    order = list(range(sink))
-    oldest = n - window
-    for i in range(window):
-        order.append(ring_slot(oldest + i, sink, window))
-    return order
+    resident = [r for r in range(min(n, sink + window))]
+    return sorted(resident, key=lambda r: ring_writer(r, n, sink, window))
 
 
 def ring_cache_index(slot: int, n: int, sink: int, window: int) -> int:

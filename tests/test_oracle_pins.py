@@ -253,6 +253,42 @@ def test_unwritten_rows_are_nan_and_unread():
 
 
 # --------------------------------------------------------------------------
+# exact widening of stored 16-bit values
+# --------------------------------------------------------------------------
+
+def test_bf16_widening_every_bit_pattern():
+    """bf16 bits widen as torch's own bfloat16 -> float64 conversion does,
+    for all 65,536 patterns (NaN payloads compared as NaN)."""
+    bits = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    got = oracle.to_f64(bits, "bf16")
+    ref = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(torch.float64).numpy()
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(got), nan)
+    assert np.array_equal(got[~nan], ref[~nan])
+    assert np.array_equal(np.signbit(got[~nan]), np.signbit(ref[~nan]))
+
+
+@pytest.mark.parametrize("bits,value", [
+    (0x3F80, 1.0), (0xC000, -2.0), (0x0001, 2.0 ** -133), (0x7F80, math.inf),
+    (0xFF80, -math.inf), (0x8000, -0.0), (0x4049, 3.140625), (0x0080, 2.0 ** -126),
+    (0x7F7F, (2 - 2.0 ** -7) * 2.0 ** 127),
+])
+def test_bf16_widening_hand_values(bits, value):
+    """bf16 is the top half of a binary32: sign, 8 exponent bits (bias 127),
+    7 fraction bits; values worked by hand from that layout."""
+    got = float(oracle.to_f64(np.array([bits], dtype=np.uint16), "bf16")[0])
+    assert got == value and math.copysign(1.0, got) == math.copysign(1.0, value)
+
+
+def test_f16_widening_hand_values():
+    """binary16: 5 exponent bits (bias 15), 10 fraction bits."""
+    for bits, value in [(0x3C00, 1.0), (0xC000, -2.0), (0x0001, 2.0 ** -24), (0x7BFF, 65504.0),
+                        (0x3555, 0.333251953125)]:
+        raw = np.array([bits], dtype=np.uint16).view(np.float16)
+        assert float(oracle.to_f64(raw, "f16")[0]) == value
+
+
+# --------------------------------------------------------------------------
 # ring mapping
 # --------------------------------------------------------------------------
 
@@ -290,6 +326,12 @@ def test_ring_last_writer_simulation(sink, window):
         assert [slot for slot, _ in by_age] == oracle.ring_cache_order(n, sink, window)
         survivors = [pos for _, pos in by_age]
         assert survivors == list(workloads.ring_survivor_positions(n, sink, window))
+        # each slot's last writer, as the simulation kept it
+        for slot, pos in holder.items():
+            assert oracle.ring_writer(slot, n, sink, window) == pos
+        for slot in range(sink + window):
+            if slot not in holder:
+                assert oracle.ring_writer(slot, n, sink, window) == -1
         # closed-form inverse: cache index of ring slot r
         for j, (slot, _) in enumerate(by_age):
             if n <= sink + window or slot < sink:
