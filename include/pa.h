@@ -84,14 +84,20 @@ typedef struct {
  * stored un-rotated; decode rotates (rotate-half pairing: (x_i, x_{i+D/2}))
  * the key at cache index j by j * theta_i and the query by (L - 1) * theta_i,
  * theta_i = rope_base^(-2i/D), L = min(context_len, sink + window).
- * `rope_table` is a device buffer of pa_rope_table_bytes() bytes filled by
- * pa_rope_table_init() for the same (sink + window, head_dim, rope_base). */
+ * `rope_table` is a device buffer of pa_rope_table_bytes(rope_capacity,
+ * rope_head_dim) bytes filled by pa_rope_table_init() with the same
+ * (rope_capacity, rope_head_dim, rope_base).  Decode refuses (PA_ERR_INVAL)
+ * a table that holds fewer than sink + window positions or was built for
+ * another head size than the pool's: the kernels index it by cache position
+ * and head size, so a smaller table would be read past its end. */
 typedef struct {
   int32_t sink;            /* S >= 0 */
   int32_t window;          /* W >= 1 */
   float rope_base;         /* e.g. 10000 */
   int32_t rope_style;      /* 0 = rotate-half (the only style implemented) */
-  const float *rope_table; /* device, float2 (cos, sin) [S + W][D / 2] */
+  const float *rope_table; /* device, float2 (cos, sin) [rope_capacity][rope_head_dim / 2] */
+  int32_t rope_capacity;   /* positions the table holds, >= S + W */
+  int32_t rope_head_dim;   /* head size the table was built for (= the pool's) */
 } pa_ring;
 
 /* ---------------------------------------------------------------- pool --- */
@@ -427,6 +433,7 @@ int pa_decode_append(pa_pool *pool, void *out, const void *query, const void *ke
                      int32_t max_context_len, float scale, const pa_ring *ring, void *workspace,
                      size_t workspace_bytes, void *stream);
 
+
 /* Device: debug checks of the device-resident inputs that pa_decode,
  * pa_decode_append and pa_reshape_and_cache trust without checking (their
  * caller contract [P1 addressing: a block id must name a block of the
@@ -484,6 +491,32 @@ const char *pa_status_str(int status);
 
 /* Text of the last HIP error seen by this thread in a pa_* call ("" if none). */
 const char *pa_last_hip_error(void);
+
+/* Kernel-configuration overrides, for tests and measurements only (not
+ * defined by the pages).  Each option starts from the environment variable
+ * of the same name (PA_FORCE_VALU, ...), read once when the library is
+ * loaded; value 0 means the library's own choice.
+ *   PA_OPT_FORCE_VALU        nonzero: decode uses the VALU kernel for every dtype
+ *   PA_OPT_PARTITION_TOKENS  VALU kernel partition size (a multiple of 16)
+ *   PA_OPT_MULTI_WAVES       multi-token decode: waves per SIMD (1 or 2)
+ *   PA_OPT_MULTI_ROW_TILES   multi-token decode: 16-row tiles per wave
+ *   PA_OPT_MULTI_PASS_GROUP  multi-token decode: passes per work-group (1, 2, 4)
+ *   PA_OPT_MULTI_MIN_RANGE   multi-token decode: shortest stream-K range (tiles)
+ * Options change the kernel choice and the workspace size: set them before
+ * pa_*_workspace_bytes and keep them until the matching call has been
+ * enqueued.  pa_set_option returns PA_ERR_INVAL for an unknown option or a
+ * negative value; pa_get_option returns -1 for an unknown option. */
+typedef enum {
+  PA_OPT_FORCE_VALU = 0,
+  PA_OPT_PARTITION_TOKENS = 1,
+  PA_OPT_MULTI_WAVES = 2,
+  PA_OPT_MULTI_ROW_TILES = 3,
+  PA_OPT_MULTI_PASS_GROUP = 4,
+  PA_OPT_MULTI_MIN_RANGE = 5,
+  PA_OPT_COUNT = 6
+} pa_option;
+int pa_set_option(pa_option opt, int32_t value);
+int32_t pa_get_option(pa_option opt);
 
 #ifdef __cplusplus
 }

@@ -19,7 +19,7 @@ __all__ = [
     "PaError", "Pool", "Ring", "ring_slot", "compute_slot_mapping", "reshape_and_cache",
     "decode_workspace_bytes", "rope_table_bytes", "rope_table_init", "decode", "decode_append",
     "check_decode_inputs", "DTYPES",
-    "block_hashes", "copy_blocks", "decode_multi_workspace_bytes", "decode_multi", "Batcher",
+    "block_hashes", "copy_blocks", "set_option", "decode_multi_workspace_bytes", "decode_multi", "Batcher",
 ]
 
 DTYPES = {"f32": _lib.PA_F32, "f16": _lib.PA_F16, "bf16": _lib.PA_BF16}
@@ -62,15 +62,50 @@ def _dev_ptr(t, name: str) -> ctypes.c_void_p:
     return ctypes.c_void_p(t.data_ptr())
 
 
-class Ring:
-    """Sink + ring configuration with its device RoPE table."""
+def _index_tensor(t, name: str, shape=None, min_rows=None) -> None:
+    """Device-resident index data is read by the kernels as int32: refuse
+    any other dtype or a shape the call does not expect."""
+    import torch
 
-    def __init__(self, sink: int, window: int, rope_base: float, rope_table):
+    if t.dtype != torch.int32:
+        raise ValueError(f"{name} must be int32 (got {t.dtype})")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)} (got {tuple(t.shape)})")
+    if min_rows is not None and (t.dim() != 2 or t.shape[0] < min_rows or t.shape[1] < 1):
+        raise ValueError(f"{name} must be [>= {min_rows}, max_blocks] (got {tuple(t.shape)})")
+
+
+class Ring:
+    """Sink + ring configuration with its device RoPE table (float32, filled
+    by ``rope_table_init`` for ``capacity`` >= sink + window positions and
+    head size ``head_dim``)."""
+
+    def __init__(self, sink: int, window: int, rope_base: float, rope_table, head_dim: Optional[int] = None,
+                 capacity: Optional[int] = None):
+        import torch
+
         self.sink, self.window, self.rope_base, self.rope_table = sink, window, rope_base, rope_table
+        self.capacity = int(sink + window if capacity is None else capacity)
+        if rope_table is None:
+            self.head_dim = int(head_dim or 0)
+            return
+        if not rope_table.is_cuda or not rope_table.is_contiguous() or rope_table.dtype != torch.float32:
+            raise ValueError("rope_table must be a contiguous float32 device tensor")
+        if head_dim is None:  # the table holds capacity rows of head_dim floats
+            if self.capacity <= 0 or rope_table.numel() % self.capacity:
+                raise ValueError("cannot infer head_dim from the rope table; pass head_dim")
+            head_dim = rope_table.numel() // self.capacity
+        self.head_dim = int(head_dim)
+        need = rope_table_bytes(self.capacity, self.head_dim)
+        if need == 0 or rope_table.numel() * 4 < need:
+            raise ValueError(f"rope_table holds {rope_table.numel() * 4} bytes; "
+                             f"{self.capacity} positions at head_dim {self.head_dim} need {need}")
+        if self.capacity < sink + window:
+            raise ValueError("rope table capacity is below sink + window")
 
     def as_struct(self) -> PaRing:
         ptr = self.rope_table.data_ptr() if self.rope_table is not None else None
-        return PaRing(self.sink, self.window, self.rope_base, 0, ptr)
+        return PaRing(self.sink, self.window, self.rope_base, 0, ptr, self.capacity, self.head_dim)
 
 
 def _ring_ptr(ring: Optional[Ring]):
@@ -240,6 +275,17 @@ def copy_blocks(pool: Pool, src_blocks, dst_blocks, stream=None) -> None:
            "pa_copy_blocks")
 
 
+def set_option(name: str, value: int) -> int:
+    """Set a kernel-configuration override (``PA_FORCE_VALU``, ...; 0 = the
+    library's choice); returns the previous value.  For tests and
+    measurements."""
+    lib = _lib.load()
+    opt = _lib.PA_OPTIONS[name]
+    old = int(lib.pa_get_option(opt))
+    _check(lib.pa_set_option(opt, int(value)), "pa_set_option")
+    return old
+
+
 def ring_slot(pos: int, sink: int, window: int) -> int:
     return _lib.load().pa_ring_slot(pos, sink, window)
 
@@ -267,6 +313,7 @@ def reshape_and_cache(pool: Pool, key, value, slot_mapping, stream=None) -> None
         raise ValueError("key/value dtype must match the pool")
     if tuple(key.shape) != (n, pool.num_kv_heads, pool.head_dim) or key.shape != value.shape:
         raise ValueError("key/value must be [N, Hkv, D]")
+    _index_tensor(slot_mapping, "slot_mapping", shape=(n,))
     _check(_lib.load().pa_reshape_and_cache(
         pool.handle, _dev_ptr(key, "key"), _dev_ptr(value, "value"),
         _dev_ptr(slot_mapping, "slot_mapping"), n, _stream_ptr(stream)), "pa_reshape_and_cache")
@@ -289,6 +336,13 @@ def rope_table_init(table, capacity: int, head_dim: int, rope_base: float, strea
                                           rope_base, _stream_ptr(stream)), "pa_rope_table_init")
 
 
+def _check_tables(pool: Pool, block_tables, context_lens, num_seqs: int, ring: Optional[Ring]) -> None:
+    _index_tensor(context_lens, "context_lens", shape=(num_seqs,))
+    _index_tensor(block_tables, "block_tables", min_rows=num_seqs)
+    if ring is not None and ring.rope_table is not None and ring.head_dim != pool.head_dim:
+        raise ValueError(f"the ring's rope table is for head_dim {ring.head_dim}, the pool's is {pool.head_dim}")
+
+
 def decode(pool: Pool, out, query, block_tables, context_lens, max_context_len: int,
            scale: float, ring: Optional[Ring] = None, workspace=None, stream=None) -> None:
     """Paged decode attention into ``out`` [B, Hq, D] (device tensors, async)."""
@@ -297,6 +351,7 @@ def decode(pool: Pool, out, query, block_tables, context_lens, max_context_len: 
         raise ValueError("out/query must be [B, Hq, D] with D = the pool's head size")
     if query.dtype != pool.act_dtype or out.dtype != pool.act_dtype:
         raise ValueError("query/out dtype must match the pool")
+    _check_tables(pool, block_tables, context_lens, b, ring)
     ws_ptr, ws_bytes = None, 0
     if workspace is not None:
         ws_ptr = _dev_ptr(workspace, "workspace")
@@ -308,13 +363,8 @@ def decode(pool: Pool, out, query, block_tables, context_lens, max_context_len: 
         _ring_ptr(ring), ws_ptr, ws_bytes, _stream_ptr(stream)), "pa_decode")
 
 
-def decode_append(pool: Pool, out, query, key, value, slot_mapping, block_tables, context_lens,
-                  max_context_len: int, scale: float, ring: Optional[Ring] = None, workspace=None,
-                  stream=None) -> None:
-    """One decode step that also stores each sequence's new token: key/value
-    [B, Hkv, D] go to slot_mapping [B] (the slot of position
-    context_lens[b] - 1) and ``out`` [B, Hq, D] is the decode attention over
-    the cache including them."""
+def _check_append(pool: Pool, out, query, key, value, slot_mapping, block_tables, context_lens,
+                  ring: Optional[Ring]) -> int:
     b, hq, d = query.shape
     if tuple(out.shape) != (b, hq, d) or d != pool.head_dim:
         raise ValueError("out/query must be [B, Hq, D] with D = the pool's head size")
@@ -324,8 +374,19 @@ def decode_append(pool: Pool, out, query, key, value, slot_mapping, block_tables
         raise ValueError("key/value dtype must match the pool")
     if tuple(key.shape) != (b, pool.num_kv_heads, d) or key.shape != value.shape:
         raise ValueError("key/value must be [B, Hkv, D]")
-    if tuple(slot_mapping.shape) != (b,):
-        raise ValueError("slot_mapping must be [B]")
+    _index_tensor(slot_mapping, "slot_mapping", shape=(b,))
+    _check_tables(pool, block_tables, context_lens, b, ring)
+    return b
+
+
+def decode_append(pool: Pool, out, query, key, value, slot_mapping, block_tables, context_lens,
+                  max_context_len: int, scale: float, ring: Optional[Ring] = None, workspace=None,
+                  stream=None) -> None:
+    """One decode step that also stores each sequence's new token: key/value
+    [B, Hkv, D] go to slot_mapping [B] (the slot of position
+    context_lens[b] - 1) and ``out`` [B, Hq, D] is the decode attention over
+    the cache including them."""
+    b = _check_append(pool, out, query, key, value, slot_mapping, block_tables, context_lens, ring)
     ws_ptr, ws_bytes = None, 0
     if workspace is not None:
         ws_ptr = _dev_ptr(workspace, "workspace")
@@ -334,7 +395,7 @@ def decode_append(pool: Pool, out, query, key, value, slot_mapping, block_tables
         pool.handle, _dev_ptr(out, "out"), _dev_ptr(query, "query"), _dev_ptr(key, "key"),
         _dev_ptr(value, "value"), _dev_ptr(slot_mapping, "slot_mapping"),
         _dev_ptr(block_tables, "block_tables"), int(block_tables.shape[1]),
-        _dev_ptr(context_lens, "context_lens"), b, hq, int(max_context_len), float(scale),
+        _dev_ptr(context_lens, "context_lens"), b, query.shape[1], int(max_context_len), float(scale),
         _ring_ptr(ring), ws_ptr, ws_bytes, _stream_ptr(stream)), "pa_decode_append")
 
 
@@ -370,6 +431,7 @@ def decode_multi(pool: Pool, out, query, block_tables, context_lens, max_context
         raise ValueError("out/query must be [B, q_len, Hq, D] with D = the pool's head size")
     if query.dtype != pool.act_dtype or out.dtype != pool.act_dtype:
         raise ValueError("query/out dtype must match the pool")
+    _check_tables(pool, block_tables, context_lens, b, None)
     ws_ptr, ws_bytes = None, 0
     if workspace is not None:
         ws_ptr = _dev_ptr(workspace, "workspace")

@@ -31,6 +31,10 @@ class PaPrefixStats(ctypes.Structure):
                 ("resident", ctypes.c_int32), ("index_only", ctypes.c_int32)]
 
 
+# kernel-configuration overrides (pa_set_option), for tests and measurements
+PA_OPTIONS = {"PA_FORCE_VALU": 0, "PA_PARTITION_TOKENS": 1, "PA_MULTI_WAVES": 2, "PA_MULTI_ROW_TILES": 3,
+              "PA_MULTI_PASS_GROUP": 4, "PA_MULTI_MIN_RANGE": 5}
+
 PA_PREFIX_TAIL = 1
 PA_PREFIX_RESIDENT = 2
 
@@ -44,7 +48,8 @@ class PaBatchInfo(ctypes.Structure):
 class PaRing(ctypes.Structure):
     _fields_ = [("sink", ctypes.c_int32), ("window", ctypes.c_int32),
                 ("rope_base", ctypes.c_float), ("rope_style", ctypes.c_int32),
-                ("rope_table", ctypes.c_void_p)]
+                ("rope_table", ctypes.c_void_p), ("rope_capacity", ctypes.c_int32),
+                ("rope_head_dim", ctypes.c_int32)]
 
 
 _p = ctypes.c_void_p
@@ -98,6 +103,8 @@ SIGNATURES = {
                                               _p, _p]),
     "pa_status_str": (ctypes.c_char_p, [ctypes.c_int]),
     "pa_last_hip_error": (ctypes.c_char_p, []),
+    "pa_set_option": (ctypes.c_int, [ctypes.c_int, _i32]),
+    "pa_get_option": (_i32, [ctypes.c_int]),
 }
 
 _LIB = None

@@ -4,6 +4,7 @@
 #include <cstdlib>
 #include <cstring>
 #include <algorithm>
+#include <atomic>
 #include <string>
 
 #include "launch.h"
@@ -35,6 +36,22 @@ int env_int(const char *name, int fallback) {
   return std::atoi(v);
 }
 
+// Overrides of the kernel configuration for tests and measurements
+// (pa_set_option).  Each starts from its environment variable, read once
+// when the library is loaded; 0 means "the library's own choice".
+std::atomic<int32_t> g_options[PA_OPT_COUNT];
+
+int32_t option(pa_option o) { return g_options[o].load(std::memory_order_relaxed); }
+
+struct OptionInit {
+  OptionInit() {
+    static const char *const names[PA_OPT_COUNT] = {"PA_FORCE_VALU",      "PA_PARTITION_TOKENS",
+                                                    "PA_MULTI_WAVES",     "PA_MULTI_ROW_TILES",
+                                                    "PA_MULTI_PASS_GROUP", "PA_MULTI_MIN_RANGE"};
+    for (int i = 0; i < PA_OPT_COUNT; ++i) g_options[i].store(env_int(names[i], 0));
+  }
+} g_option_init;
+
 int log2_exact(int v) {
   int s = 0;
   while ((1 << s) < v) ++s;
@@ -53,7 +70,7 @@ struct WorkspaceLayout {
 size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
 WorkspaceLayout workspace_layout(const pa_pool *pool, int32_t num_seqs, int32_t num_q_heads,
-                                 int64_t eff_ctx) {
+                                 int64_t eff_ctx, bool ring) {
   WorkspaceLayout w{};
   // a partition spans at most 64 blocks (its ids are staged one per lane)
   w.partition_tokens = std::min(choose_partition_tokens(eff_ctx), 64 * pool->block_size);
@@ -62,7 +79,8 @@ WorkspaceLayout workspace_layout(const pa_pool *pool, int32_t num_seqs, int32_t 
   const int64_t slice = std::min<int64_t>(num_seqs, kMaxSchedSeqsHost);
   if (choose_decode_kernel(pool->dtype, group).kernel == DecodeKernel::kMfma) {
     // stream-K: one slot per wave plus one per (sequence, KV head)
-    const size_t waves = std::max<size_t>(kMaxPersistentWavesHost, (size_t)pool->num_kv_heads);
+    const size_t waves = (size_t)decode_mfma_waves(pool->dtype, pool->head_dim, ring, kv8_format(pool),
+                                                   pool->num_kv_heads);
     const size_t slots = waves + (size_t)slice * pool->num_kv_heads;
     w.sched_bytes = round_up((size_t)(slice + 1) * sizeof(int32_t), 256);
     w.ml_bytes = round_up(slots * group * 2 * sizeof(float), 256);
@@ -98,16 +116,16 @@ MultiLayout multi_layout(const pa_pool *pool, int32_t num_seqs, int32_t q_len, i
   // arithmetic: verification of the 70B-shaped batch 87.9 us against 99.2 us
   // with one wave) are bound by the per-tile arithmetic: two waves per SIMD
   // with two row tiles each; otherwise one wave per SIMD.
-  const int forced_w = env_int("PA_MULTI_WAVES", 0);
+  const int forced_w = option(PA_OPT_MULTI_WAVES);
   m.waves = (forced_w == 1 || forced_w == 2) ? forced_w
             : (pool->kv_fp8 || rows > 3 * 16 * max_mt) ? 2 : 1;
   const int wave_mt = m.waves == 2 ? 2 : max_mt;
-  const int forced_mt = env_int("PA_MULTI_ROW_TILES", 0);
+  const int forced_mt = option(PA_OPT_MULTI_ROW_TILES);
   m.mt = (int)std::min<int64_t>(forced_mt >= 1 && forced_mt <= wave_mt ? forced_mt : wave_mt, ceil_div(rows, 16));
   m.pass_rows = 16 * m.mt;
   m.passes = (int)ceil_div(rows, m.pass_rows);
   // passes of one head share K/V tiles through L2 when a work-group takes several
-  const int forced = env_int("PA_MULTI_PASS_GROUP", 0);
+  const int forced = option(PA_OPT_MULTI_PASS_GROUP);
   m.pass_group = (forced == 1 || forced == 2 || forced == 4) ? forced
                  : m.passes >= 4 ? 4 : m.passes >= 2 ? 2 : 1;
   m.pgroups = (int)ceil_div(m.passes, m.pass_group);
@@ -130,7 +148,7 @@ constexpr int kMaxMultiQLen = 4096;
 
 DecodeChoice choose_decode_kernel(pa_dtype dtype, int group) {
   DecodeChoice c;
-  const bool force_valu = env_int("PA_FORCE_VALU", 0) != 0;
+  const bool force_valu = (option(PA_OPT_FORCE_VALU) != 0);
   // 16-bit and 8-bit pools stream through the MFMA kernel for any group up
   // to 16: it is bound by HBM, so the unused score columns of a small group
   // cost no time (the shared-prefix MHA batch: 61.8 us against 67.1 us for
@@ -146,7 +164,7 @@ DecodeChoice choose_decode_kernel(pa_dtype dtype, int group) {
 }
 
 int choose_partition_tokens(int64_t eff_ctx) {
-  const int forced = env_int("PA_PARTITION_TOKENS", 0);
+  const int forced = option(PA_OPT_PARTITION_TOKENS);
   if (forced >= kTileTokens && forced % kTileTokens == 0) return forced;
   (void)eff_ctx;
   return 512;
@@ -157,6 +175,17 @@ int choose_partition_tokens(int64_t eff_ctx) {
 extern "C" {
 
 const char *pa_last_hip_error(void) { return pa::g_last_hip_error.c_str(); }
+
+int pa_set_option(pa_option opt, int32_t value) {
+  if ((int)opt < 0 || (int)opt >= PA_OPT_COUNT || value < 0) return PA_ERR_INVAL;
+  pa::g_options[opt].store(value, std::memory_order_relaxed);
+  return PA_OK;
+}
+
+int32_t pa_get_option(pa_option opt) {
+  if ((int)opt < 0 || (int)opt >= PA_OPT_COUNT) return -1;
+  return pa::option(opt);
+}
 
 int pa_reshape_and_cache(pa_pool *pool, const void *key, const void *value,
                          const int32_t *slot_mapping, int32_t num_tokens, void *stream) {
@@ -255,7 +284,7 @@ int pa_decode_multi(pa_pool *pool, void *out, const void *query, const int32_t *
   a.pass_group = m.pass_group;
   a.pgroups = m.pgroups;
   a.groups = m.groups;
-  const int forced_range = pa::env_int("PA_MULTI_MIN_RANGE", 0);
+  const int forced_range = pa::option(PA_OPT_MULTI_MIN_RANGE);
   a.min_range_tiles = forced_range >= 1 ? forced_range : 4;
   a.block_shift = pa::log2_exact(pool->block_size);
   a.scale_log2 = scale * pa::kLog2eHost;
@@ -285,7 +314,7 @@ size_t pa_decode_workspace_bytes(const pa_pool *pool, int32_t num_seqs, int32_t 
   if (pool == nullptr || num_seqs < 0 || num_q_heads <= 0 || max_context_len < 0) return 0;
   if (!pa::ring_valid(ring)) return 0;
   const int64_t eff = pa::effective_context(max_context_len, ring);
-  return pa::workspace_layout(pool, num_seqs, num_q_heads, eff).total;
+  return pa::workspace_layout(pool, num_seqs, num_q_heads, eff, ring != nullptr).total;
 }
 
 size_t pa_rope_table_bytes(int32_t capacity, int32_t head_dim) {
@@ -321,7 +350,6 @@ int pa_rope_table_init(float *table, int32_t capacity, int32_t head_dim, float r
   return pa::hip_status(pa::launch_rope_table_init(table, capacity, head_dim, rope_base,
                                                    static_cast<hipStream_t>(stream)));
 }
-
 }  // extern "C"
 
 namespace pa {
@@ -359,11 +387,15 @@ int decode_impl(pa_pool *pool, void *out, const void *query, const int32_t *bloc
   } else {
     if ((int64_t)ring->sink + ring->window > table_tokens) return PA_ERR_INVAL;
     if (ring->rope_table == nullptr || !pa::aligned16(ring->rope_table)) return PA_ERR_INVAL;
+    // the kernels read table rows 0 .. S+W-1 of head_dim floats each
+    if ((int64_t)ring->rope_capacity < (int64_t)ring->sink + ring->window ||
+        ring->rope_head_dim != pool->head_dim)
+      return PA_ERR_INVAL;
   }
   if (!(scale == scale)) return PA_ERR_INVAL;  // NaN scale
 
   const int64_t eff = pa::effective_context(max_context_len, ring);
-  const pa::WorkspaceLayout w = pa::workspace_layout(pool, num_seqs, num_q_heads, eff);
+  const pa::WorkspaceLayout w = pa::workspace_layout(pool, num_seqs, num_q_heads, eff, ring != nullptr);
   if (w.total > 0) {
     if (workspace == nullptr || workspace_bytes < w.total) return PA_ERR_NOMEM;
     if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return PA_ERR_INVAL;

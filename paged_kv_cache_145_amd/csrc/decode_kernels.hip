@@ -236,7 +236,7 @@ template <>
 struct V8Chunk<128> {
   typedef uint2 type;
   static __device__ __forceinline__ uint2 load(__amdgpu_buffer_rsrc_t r, int off) {
-    return buffer_load8(r, off);
+    return buffer_load8<kCacheStream>(r, off);
   }
   template <class T, int F>
   static __device__ __forceinline__ uint4 widen(const uint2 &v) { return fp8x8_to_16<T, F>(v); }
@@ -245,7 +245,7 @@ template <>
 struct V8Chunk<64> {
   typedef uint32_t type;
   static __device__ __forceinline__ uint32_t load(__amdgpu_buffer_rsrc_t r, int off) {
-    return buffer_load4(r, off);
+    return buffer_load4<kCacheStream>(r, off);
   }
   template <class T, int F>
   static __device__ __forceinline__ uint2 widen(const uint32_t &v) { return fp8x4_to_16<T, F>(v); }
@@ -257,7 +257,7 @@ template <>
 struct VChunk<128> {
   typedef uint4 type;
   static __device__ __forceinline__ uint4 load(__amdgpu_buffer_rsrc_t r, int off) {
-    return buffer_load16(r, off);
+    return buffer_load16<kCacheStream>(r, off);
   }
   static __device__ __forceinline__ uint2 half(const uint4 &v, int h) {
     return h == 0 ? make_uint2(v.x, v.y) : make_uint2(v.z, v.w);
@@ -270,7 +270,7 @@ template <>
 struct VChunk<64> {
   typedef uint2 type;
   static __device__ __forceinline__ uint2 load(__amdgpu_buffer_rsrc_t r, int off) {
-    return buffer_load8(r, off);
+    return buffer_load8<kCacheStream>(r, off);
   }
   static __device__ __forceinline__ uint2 half(const uint2 &v, int) { return v; }
   static __device__ __forceinline__ uint2 select(bool keep, const uint2 &v) {
@@ -631,7 +631,7 @@ void decode_mfma_kernel(DecodeArgs a) {
     const auto vr = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<char *>(static_cast<const char *>(a.v_cache) + off), (short)0, nrec, kBufferWord3);
 #pragma unroll
-    for (int kb = 0; kb < KLD; ++kb) k[kb] = buffer_load16(kr, k_off + 64 * kb);
+    for (int kb = 0; kb < KLD; ++kb) k[kb] = buffer_load16<kCacheStream>(kr, k_off + 64 * kb);
 #pragma unroll
     for (int tau = 0; tau < 4; ++tau) {
       if constexpr (KV8) v[tau] = V8Chunk<D>::load(vr, v_off[tau]);
@@ -973,8 +973,8 @@ __device__ __forceinline__ void valu_partition(const DecodeArgs &a, int b, int p
     const auto vr = tile_rsrc<D, st>(a, vc, phys, r0 & bmask, valid, row_stride);
 #pragma unroll
     for (int s = 0; s < STEPS; ++s) {
-      k[s] = buffer_load16(kr, off[s]);
-      v[s] = buffer_load16(vr, off[s]);
+      k[s] = buffer_load16<kCacheStream>(kr, off[s]);
+      v[s] = buffer_load16<kCacheStream>(vr, off[s]);
     }
   };
 
@@ -1151,6 +1151,18 @@ int persistent_grid(const void *kernel, int per_cu_cap) {
   return cus * std::max(1, std::min(per_cu, per_cu_cap));
 }
 
+// Persistent grid of the MFMA decode kernel: one work-group per CU for
+// 16-bit pools (a lone wave per SIMD is never starved by an older
+// neighbour, so equal tile counts finish at nearly equal times), two for
+// 8-bit pools; at least one group of Hkv waves.
+template <class T, int D, bool RING, int KVF>
+int mfma_grid(int num_kv_heads) {
+  static const int grid_max = std::min(
+      persistent_grid(reinterpret_cast<const void *>(&decode_mfma_kernel<T, D, RING, KVF>), KVF != 0 ? 2 : 1),
+      kMaxPersistentWaves / kNW);
+  return std::max(grid_max, (num_kv_heads + kNW - 1) / kNW);
+}
+
 template <class T, int D, bool RING, int KVF = 0>
 hipError_t launch_typed(const DecodeArgs &a, DecodeChoice choice, hipStream_t stream) {
   constexpr bool KV8 = KVF != 0;
@@ -1160,15 +1172,7 @@ hipError_t launch_typed(const DecodeArgs &a, DecodeChoice choice, hipStream_t st
   }
   if constexpr (T::kBytes == 2) {
     if (choice.kernel == DecodeKernel::kMfma) {
-      // one work-group (one wave per SIMD) per CU: a lone wave per SIMD is
-      // never starved by an older neighbour, so equal tile counts finish
-      // at nearly equal times
-      static const int grid_max = std::min(
-          persistent_grid(reinterpret_cast<const void *>(&decode_mfma_kernel<T, D, RING, KVF>),
-                          KV8 ? 2 : 1),
-          kMaxPersistentWaves / kNW);
-      // at least one group of Hkv waves
-      const int grid = std::max(grid_max, (a.num_kv_heads + kNW - 1) / kNW);
+      const int grid = mfma_grid<T, D, RING, KVF>(a.num_kv_heads);
       if (a.app_key != nullptr) {
         if constexpr (RING && KV8) return hipErrorInvalidValue;
         else hipLaunchKernelGGL((decode_mfma_kernel<T, D, RING, KVF, true>), dim3(grid), block, 0, stream, a);
@@ -1235,7 +1239,32 @@ hipError_t launch_dtype(const DecodeArgs &a, int head_dim, bool ring, int kv8,
               : launch_typed<T, 64, false>(a, choice, stream);
 }
 
+template <class T, bool RING, int KVF>
+int mfma_waves_t(int head_dim, int num_kv_heads) {
+  return kNW * (head_dim == 128 ? mfma_grid<T, 128, RING, KVF>(num_kv_heads)
+                                : mfma_grid<T, 64, RING, KVF>(num_kv_heads));
+}
+
+template <class T, bool RING>
+int mfma_waves_r(int head_dim, int kv8, int num_kv_heads) {
+  if constexpr (!RING) {
+    if (kv8 == kKvE4M3) return mfma_waves_t<T, false, kKvE4M3>(head_dim, num_kv_heads);
+    if (kv8 == kKvE5M2) return mfma_waves_t<T, false, kKvE5M2>(head_dim, num_kv_heads);
+  }
+  return mfma_waves_t<T, RING, 0>(head_dim, num_kv_heads);
+}
+
 }  // namespace
+
+int decode_mfma_waves(pa_dtype dtype, int head_dim, bool ring, int kv8, int num_kv_heads) {
+  if (dtype == PA_BF16)
+    return ring ? mfma_waves_r<BF16, true>(head_dim, kv8, num_kv_heads)
+                : mfma_waves_r<BF16, false>(head_dim, kv8, num_kv_heads);
+  if (dtype == PA_F16)
+    return ring ? mfma_waves_r<F16, true>(head_dim, kv8, num_kv_heads)
+                : mfma_waves_r<F16, false>(head_dim, kv8, num_kv_heads);
+  return 0;
+}
 
 hipError_t launch_decode(const DecodeArgs &args, pa_dtype dtype, int head_dim, bool ring,
                          int kv8, DecodeChoice choice, int num_seqs, hipStream_t stream) {

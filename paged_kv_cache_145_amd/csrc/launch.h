@@ -124,6 +124,9 @@ struct DecodeChoice {
 };
 
 DecodeChoice choose_decode_kernel(pa_dtype dtype, int group);
+// Waves of the MFMA decode kernel's persistent grid on the current device
+// (16-bit query/output dtype; kv8 as in launch_decode).
+int decode_mfma_waves(pa_dtype dtype, int head_dim, bool ring, int kv8, int num_kv_heads);
 int choose_partition_tokens(int64_t effective_max_context);
 
 // dtype: the query/output dtype; kv8: 0 for 16-bit pools, else the format

@@ -38,21 +38,17 @@ def torch_to_f64(t: torch.Tensor) -> np.ndarray:
 
 
 @contextlib.contextmanager
-def env(**kv):
-    old = {k: os.environ.get(k) for k in kv}
+def options(**kv):
+    """Kernel-configuration overrides for the duration of a block (None or 0:
+    the library's own choice); previous values are restored afterwards."""
+    old = {}
     try:
         for k, v in kv.items():
-            if v is None:
-                os.environ.pop(k, None)
-            else:
-                os.environ[k] = str(v)
+            old[k] = pk.set_option(k, 0 if v is None else int(v))
         yield
     finally:
         for k, v in old.items():
-            if v is None:
-                os.environ.pop(k, None)
-            else:
-                os.environ[k] = v
+            pk.set_option(k, v)
 
 
 class DeviceCase:

@@ -12,7 +12,7 @@ import torch
 import oracle
 import paged_kv_cache_145_amd as pk
 import workloads
-from gpu_support import TORCH_DTYPES, DeviceCase, assert_parity, env, raw_to_torch, torch_to_f64
+from gpu_support import TORCH_DTYPES, DeviceCase, assert_parity, options, raw_to_torch, torch_to_f64
 
 pytestmark = pytest.mark.gpu
 
@@ -72,7 +72,7 @@ def test_multi_parity_shapes(shape, min_range):
     case = workloads.make_multi_case("multi_shape", 7100 + len(lens) + q, dtype, lens, q, hq, hkv, d, bs)
     dc = DeviceCase(case)
     dc.write_all()
-    with env(PA_MULTI_MIN_RANGE=min_range):
+    with options(PA_MULTI_MIN_RANGE=min_range):
         out = _run(dc, case)
     assert_parity(out, _ref(case), dtype)
     dc.close()
@@ -90,7 +90,7 @@ def test_multi_parity_pass_groups(shape, pass_group, waves):
     case = workloads.make_multi_case("multi_shape", 7100 + len(lens) + q, dtype, lens, q, hq, hkv, d, bs)
     dc = DeviceCase(case)
     dc.write_all()
-    with env(PA_MULTI_PASS_GROUP=pass_group, PA_MULTI_MIN_RANGE=1, PA_MULTI_WAVES=waves):
+    with options(PA_MULTI_PASS_GROUP=pass_group, PA_MULTI_MIN_RANGE=1, PA_MULTI_WAVES=waves):
         out = _run(dc, case)
     assert_parity(out, _ref(case), dtype)
     dc.close()
@@ -178,7 +178,7 @@ def test_multi_parity_fp8_pools(shape, min_range, waves):
                                                                   q, hq, hkv, d, bs))
     dc = DeviceCase(case)
     dc.write_all()
-    with env(PA_MULTI_MIN_RANGE=min_range, PA_MULTI_WAVES=waves):
+    with options(PA_MULTI_MIN_RANGE=min_range, PA_MULTI_WAVES=waves):
         out = _run(dc, case)
     assert_parity(out, _ref(case), dtype)
     dc.close()
@@ -195,7 +195,7 @@ def test_multi_parity_e5m2_pools(shape, min_range):
                                                                   q, hq, hkv, d, bs), kv_format="e5m2")
     dc = DeviceCase(case)
     dc.write_all()
-    with env(PA_MULTI_MIN_RANGE=min_range):
+    with options(PA_MULTI_MIN_RANGE=min_range):
         out = _run(dc, case)
     assert_parity(out, _ref(case), dtype)
     dc.close()

@@ -11,7 +11,7 @@ import torch
 
 import oracle
 import workloads
-from gpu_support import (DeviceCase, assert_parity, env, oracle_reference, raw_bits, raw_to_torch,
+from gpu_support import (DeviceCase, assert_parity, options, oracle_reference, raw_bits, raw_to_torch,
                          torch_bits, torch_to_f64)
 
 pytestmark = pytest.mark.gpu
@@ -119,7 +119,7 @@ def test_decode_parity_full_config(name, kernel):
     case, (_, _, _, ref) = reference(name, CONFIGS[name])
     dc = DeviceCase(case)
     dc.write_all()
-    with env(PA_FORCE_VALU="1" if kernel == "valu" else None):
+    with options(PA_FORCE_VALU="1" if kernel == "valu" else None):
         out = dc.decode()
     err = assert_parity(out, ref, case.dtype)
     print(f"{name} [{kernel}] parity error {err:.3e}")
@@ -131,7 +131,7 @@ def test_decode_partition_sizes(partition):
     case, (_, _, _, ref) = reference("embedded_1p1b", CONFIGS["embedded_1p1b"])
     dc = DeviceCase(case)
     dc.write_all()
-    with env(PA_PARTITION_TOKENS=partition):
+    with options(PA_PARTITION_TOKENS=partition):
         out = dc.decode()
     assert_parity(out, ref, case.dtype)
     dc.close()
@@ -161,7 +161,7 @@ def test_decode_ragged_shapes(shape, kernel):
     _, _, _, ref = oracle_reference(case)
     dc = DeviceCase(case)
     dc.write_all()
-    with env(PA_FORCE_VALU="1" if kernel == "valu" else None, PA_PARTITION_TOKENS=256):
+    with options(PA_FORCE_VALU="1" if kernel == "valu" else None, PA_PARTITION_TOKENS=256):
         out = dc.decode()
     assert_parity(out, ref, dtype)
     for b, n in enumerate(lens):
@@ -176,7 +176,7 @@ def test_single_token_is_v0_bit_exact(dtype, kernel):
     case = workloads.make_paged_case("n1", 99, dtype, [1, 1, 1, 1], 16, 2, 128, 16)
     dc = DeviceCase(case)
     dc.write_all()
-    with env(PA_FORCE_VALU="1" if kernel == "valu" else None):
+    with options(PA_FORCE_VALU="1" if kernel == "valu" else None):
         out = dc.decode()
     got = torch_bits(out, dtype)
     for b in range(4):
@@ -278,7 +278,7 @@ def test_ring_parity_set_both_kernels_agree_with_oracle():
     dc.write_all()
     outs = {}
     for kernel in ("auto", "valu"):
-        with env(PA_FORCE_VALU="1" if kernel == "valu" else None):
+        with options(PA_FORCE_VALU="1" if kernel == "valu" else None):
             outs[kernel] = torch_to_f64(dc.decode())
         assert_parity(torch.from_numpy(outs[kernel]), ref, "f16")
     dc.close()
@@ -363,7 +363,7 @@ def test_ring_small_groups(hq, hkv, kernel):
     _, _, _, ref = oracle_reference(case)
     dc = DeviceCase(case)
     dc.write_all()
-    with env(PA_FORCE_VALU="1" if kernel == "valu" else None):
+    with options(PA_FORCE_VALU="1" if kernel == "valu" else None):
         out = dc.decode(max_context_len=100_000)
     assert_parity(out, ref, "f16")
     dc.close()
