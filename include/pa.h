@@ -433,6 +433,26 @@ int pa_decode_append(pa_pool *pool, void *out, const void *query, const void *ke
                      int32_t max_context_len, float scale, const pa_ring *ring, void *workspace,
                      size_t workspace_bytes, void *stream);
 
+/* Device: pa_decode_append for callers that cannot allocate memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): no workspace argument, and no hipMalloc, hipFree or other
+ * allocating call.  The split-K partials and the tile schedule go to a
+ * scratch array of pa_decode_noalloc_scratch_bytes() bytes (32 MiB) that
+ * the library holds in device memory, one per GPU, from its first use on
+ * that GPU until the process ends.  The call needs exactly the workspace
+ * that pa_decode_workspace_bytes (same pool, num_seqs, num_q_heads,
+ * max_context_len and ring) reports; above the scratch size it returns
+ * PA_ERR_NOMEM and enqueues nothing.  Every call on one GPU shares that
+ * GPU's array (it keeps the last call's contents; the kernels need no
+ * initialised contents): calls that overlap in time on one GPU, on
+ * different streams or threads, race on it and give unspecified results.
+ * Other arguments, results and errors are those of pa_decode_append. */
+int pa_decode_append_noalloc(pa_pool *pool, void *out, const void *query, const void *key,
+                             const void *value, const int32_t *slot_mapping, const int32_t *block_tables,
+                             int32_t max_blocks_per_seq, const int32_t *context_lens, int32_t num_seqs,
+                             int32_t num_q_heads, int32_t max_context_len, float scale, const pa_ring *ring,
+                             void *stream);
+size_t pa_decode_noalloc_scratch_bytes(void);
 
 /* Device: debug checks of the device-resident inputs that pa_decode,
  * pa_decode_append and pa_reshape_and_cache trust without checking (their

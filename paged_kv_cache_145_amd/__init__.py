@@ -18,6 +18,7 @@ from ._lib import PaRing
 __all__ = [
     "PaError", "Pool", "Ring", "ring_slot", "compute_slot_mapping", "reshape_and_cache",
     "decode_workspace_bytes", "rope_table_bytes", "rope_table_init", "decode", "decode_append",
+    "decode_append_noalloc", "decode_noalloc_scratch_bytes",
     "check_decode_inputs", "DTYPES",
     "block_hashes", "copy_blocks", "set_option", "decode_multi_workspace_bytes", "decode_multi", "Batcher",
 ]
@@ -397,6 +398,23 @@ def decode_append(pool: Pool, out, query, key, value, slot_mapping, block_tables
         _dev_ptr(block_tables, "block_tables"), int(block_tables.shape[1]),
         _dev_ptr(context_lens, "context_lens"), b, query.shape[1], int(max_context_len), float(scale),
         _ring_ptr(ring), ws_ptr, ws_bytes, _stream_ptr(stream)), "pa_decode_append")
+
+
+def decode_append_noalloc(pool: Pool, out, query, key, value, slot_mapping, block_tables, context_lens,
+                          max_context_len: int, scale: float, ring: Optional[Ring] = None, stream=None) -> None:
+    """``decode_append`` without a workspace: the library's per-GPU scratch
+    array holds the split-K partials (see pa_decode_append_noalloc)."""
+    b = _check_append(pool, out, query, key, value, slot_mapping, block_tables, context_lens, ring)
+    _check(_lib.load().pa_decode_append_noalloc(
+        pool.handle, _dev_ptr(out, "out"), _dev_ptr(query, "query"), _dev_ptr(key, "key"),
+        _dev_ptr(value, "value"), _dev_ptr(slot_mapping, "slot_mapping"),
+        _dev_ptr(block_tables, "block_tables"), int(block_tables.shape[1]),
+        _dev_ptr(context_lens, "context_lens"), b, query.shape[1], int(max_context_len), float(scale),
+        _ring_ptr(ring), _stream_ptr(stream)), "pa_decode_append_noalloc")
+
+
+def decode_noalloc_scratch_bytes() -> int:
+    return int(_lib.load().pa_decode_noalloc_scratch_bytes())
 
 
 def check_decode_inputs(pool: Pool, block_tables, context_lens, max_context_len: int,

@@ -103,6 +103,9 @@ SIGNATURES = {
                                               _p, _p]),
     "pa_status_str": (ctypes.c_char_p, [ctypes.c_int]),
     "pa_last_hip_error": (ctypes.c_char_p, []),
+    "pa_decode_append_noalloc": (ctypes.c_int, [_p, _p, _p, _p, _p, _p, _p, _i32, _p, _i32, _i32, _i32,
+                                                ctypes.c_float, ctypes.POINTER(PaRing), _p]),
+    "pa_decode_noalloc_scratch_bytes": (_sz, []),
     "pa_set_option": (ctypes.c_int, [ctypes.c_int, _i32]),
     "pa_get_option": (_i32, [ctypes.c_int]),
 }

@@ -5,6 +5,7 @@
 #include <cstring>
 #include <algorithm>
 #include <atomic>
+#include <mutex>
 #include <string>
 
 #include "launch.h"
@@ -350,6 +351,7 @@ int pa_rope_table_init(float *table, int32_t capacity, int32_t head_dim, float r
   return pa::hip_status(pa::launch_rope_table_init(table, capacity, head_dim, rope_base,
                                                    static_cast<hipStream_t>(stream)));
 }
+
 }  // extern "C"
 
 namespace pa {
@@ -465,6 +467,53 @@ int decode_impl(pa_pool *pool, void *out, const void *query, const int32_t *bloc
 }  // namespace
 }  // namespace pa
 
+// ------------------------------------------------------------------------
+// Scratch of the no-allocation entry point.  Device memory the library
+// owns: each GPU the library runs on holds one copy of this array until the
+// process ends.  Host code never uses the array's name as an address (on
+// the host it is only a stand-in for the symbol); it uses the per-device
+// address that hipGetSymbolAddress returns.
+// ------------------------------------------------------------------------
+namespace pa {
+namespace {
+constexpr size_t kScratchBytes = size_t(32) << 20;
+}  // namespace
+}  // namespace pa
+
+static __device__ __align__(256) unsigned char scratch[pa::kScratchBytes];
+
+namespace pa {
+namespace {
+
+constexpr int kMaxScratchDevices = 64;
+std::atomic<void *> g_scratch_addr[kMaxScratchDevices];
+std::mutex g_scratch_mu;
+
+// Device address of the current device's scratch array, looked up once per
+// device (with that device current) and kept.
+int scratch_address(void **addr) {
+  int dev = 0;
+  const hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_status(e);
+  if (dev < 0 || dev >= kMaxScratchDevices) return PA_ERR_UNSUPPORTED;
+  void *p = g_scratch_addr[dev].load(std::memory_order_acquire);
+  if (p == nullptr) {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    p = g_scratch_addr[dev].load(std::memory_order_relaxed);
+    if (p == nullptr) {
+      const hipError_t es = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+      if (es != hipSuccess) return hip_status(es);
+      if (p == nullptr) return PA_ERR_HIP;
+      g_scratch_addr[dev].store(p, std::memory_order_release);
+    }
+  }
+  *addr = p;
+  return PA_OK;
+}
+
+}  // namespace
+}  // namespace pa
+
 extern "C" {
 
 int pa_decode(pa_pool *pool, void *out, const void *query, const int32_t *block_tables,
@@ -490,6 +539,27 @@ int pa_decode_append(pa_pool *pool, void *out, const void *query, const void *ke
   return pa::decode_impl(pool, out, query, block_tables, max_blocks_per_seq, context_lens, num_seqs,
                          num_q_heads, max_context_len, scale, ring, workspace, workspace_bytes, stream,
                          &app);
+}
+
+size_t pa_decode_noalloc_scratch_bytes(void) { return pa::kScratchBytes; }
+
+int pa_decode_append_noalloc(pa_pool *pool, void *out, const void *query, const void *key,
+                             const void *value, const int32_t *slot_mapping, const int32_t *block_tables,
+                             int32_t max_blocks_per_seq, const int32_t *context_lens, int32_t num_seqs,
+                             int32_t num_q_heads, int32_t max_context_len, float scale, const pa_ring *ring,
+                             void *stream) {
+  if (pool == nullptr || num_seqs < 0 || num_q_heads <= 0 || max_context_len < 0) return PA_ERR_INVAL;
+  if (num_seqs == 0) return PA_OK;
+  if (!pa::ring_valid(ring)) return PA_ERR_INVAL;
+  // the same workspace the allocating form needs must fit the scratch array
+  const size_t need = pa_decode_workspace_bytes(pool, num_seqs, num_q_heads, max_context_len, ring);
+  if (need > pa::kScratchBytes) return PA_ERR_NOMEM;
+  void *ws = nullptr;
+  const int rc = pa::scratch_address(&ws);
+  if (rc != PA_OK) return rc;
+  return pa_decode_append(pool, out, query, key, value, slot_mapping, block_tables, max_blocks_per_seq,
+                          context_lens, num_seqs, num_q_heads, max_context_len, scale, ring, ws,
+                          pa::kScratchBytes, stream);
 }
 
 }  // extern "C"
