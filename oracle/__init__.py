@@ -62,6 +62,7 @@ from .paged_attention import (  # noqa: F401
     attention_one_group,
     decode,
     decode_multi,
+    decode_verify_ring,
     reshape_and_cache,
     reshape_and_cache_,
     build_pools,

@@ -250,6 +250,66 @@ def decode_multi(query, k_pool, v_pool, block_tables, context_lens, scale, dtype
     return out
 
 
+def decode_verify_ring(query, draft_keys, draft_values, k_pool, v_pool, block_tables, context_lens, scale,
+                       dtype, block_size, ring, kv_dtype=None, k_scale=None, v_scale=None) -> np.ndarray:
+    """Speculative verification over the sink + ring cache (float64 output
+    [B, q_len, Hq, D]).
+
+    Page "wzjinhao.cn/news/69573": the target model scores a step of draft
+    tokens in one pass (section "嵌入式流式推理的访存墙与投机瓶颈") over the
+    sink + ring cache of section "环形上下文与注意力沉淀机制", and the
+    drafts it rejects are rolled back.  Reading: stream b has committed
+    positions 0..n-1 (n = context_lens[b]) in the ring; draft i, at position
+    n + i, has its query row query[b, i] and its K/V rows draft_keys[b, i],
+    draft_values[b, i] (query dtype), which are not in the cache.  Row i is
+    the single-token ring decode that sequential decoding would give for
+    draft i: over the ring as it would be after writing drafts 0..i at their
+    slots (an 8-bit pool holds their codes), with cache-order RoPE.  The
+    pools themselves are not changed, so rejected drafts leave nothing to
+    undo.
+    """
+    q_all = to_f64(query, dtype)
+    b_count, q_len, hq, d = q_all.shape
+    hkv = k_pool.shape[2]
+    if hq % hkv != 0:
+        raise ValueError("Hq must be a multiple of Hkv")
+    group = hq // hkv
+    kv8 = kv_dtype in fp8.KV_FORMATS
+    out = np.zeros((b_count, q_len, hq, d), dtype=np.float64)
+    for b in range(b_count):
+        n = int(context_lens[b])
+        if kv8:  # a written draft holds its codes
+            fmt = fp8.KV_FORMATS[kv_dtype]
+            dk = fp8.dequantize_rows(quantize_for_cache(draft_keys[b], dtype, k_scale, kv_dtype), k_scale, fmt)
+            dv = fp8.dequantize_rows(quantize_for_cache(draft_values[b], dtype, v_scale, kv_dtype), v_scale, fmt)
+        else:
+            dk, dv = to_f64(draft_keys[b], dtype), to_f64(draft_values[b], dtype)
+        for i in range(q_len):
+            total = n + i + 1  # positions written once draft i is
+            order = ring_cache_order(total, ring.sink, ring.window)
+            keys = np.empty((len(order), hkv, d))
+            vals = np.empty((len(order), hkv, d))
+            for j, r in enumerate(order):
+                pos = ring_writer(r, total, ring.sink, ring.window)
+                if pos >= n:  # a draft of this step
+                    keys[j], vals[j] = dk[pos - n], dv[pos - n]
+                    continue
+                kr = gather_rows(k_pool, block_tables[b], [r], block_size)
+                vr = gather_rows(v_pool, block_tables[b], [r], block_size)
+                if kv8:
+                    keys[j] = fp8.dequantize_rows(kr, k_scale, fp8.KV_FORMATS[kv_dtype])[0]
+                    vals[j] = fp8.dequantize_rows(vr, v_scale, fp8.KV_FORMATS[kv_dtype])[0]
+                else:
+                    keys[j], vals[j] = to_f64(kr, dtype)[0], to_f64(vr, dtype)[0]
+            length = len(order)
+            keys = rope_rotate_half(keys, np.arange(length)[:, None], ring.rope_base)
+            q_i = rope_rotate_half(q_all[b, i], length - 1, ring.rope_base)
+            for g in range(hkv):
+                heads = slice(g * group, (g + 1) * group)
+                out[b, i, heads] = attention_one_group(q_i[heads], keys[:, g, :], vals[:, g, :], scale)
+    return out
+
+
 # ---------------------------------------------------------------------------
 # write side
 # ---------------------------------------------------------------------------

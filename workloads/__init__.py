@@ -128,6 +128,12 @@ class DecodeCase:
     # prefill): query is then [B, q_len, Hq, D] and the last q_len positions
     # of each sequence are its new tokens; None for single-token decode
     q_len: Optional[int] = None
+    # speculative verification over the sink + ring cache: the q_len draft
+    # rows [B, q_len, Hkv, D] (raw, the query dtype) of positions
+    # context_lens[b] .. context_lens[b] + q_len - 1, which are not in the
+    # cache (context_lens counts the committed positions only)
+    draft_keys: Optional[np.ndarray] = None
+    draft_values: Optional[np.ndarray] = None
 
     @property
     def num_seqs(self) -> int:
@@ -433,6 +439,55 @@ def config_sink_ring(lengths=None, seed_offset: int = 5, pad_with_minus_one: boo
         scale=1.0 / math.sqrt(head_dim), context_lens=lens.astype(np.int32),
         block_tables=tables, query=query, writes=writes,
         ring=RingSpec(sink, window, 10000.0), pad_block=pad,
+    )
+
+
+RING_VERIFY_LENGTHS = [0] + RING_PARITY_LENGTHS
+
+
+def config_ring_verify(lengths=None, q_len: int = 5, seed_offset: int = 15, sink: int = 4, window: int = 1020,
+                       block_size: int = 16, num_q_heads: int = 12, num_kv_heads: int = 2,
+                       head_dim: int = 128, dtype: str = "f16", pad_with_minus_one: bool = False) -> DecodeCase:
+    """Speculative verification over the sink + ring cache (the sink + ring
+    workload's shape): each stream has committed positions 0..n-1 (only the
+    survivors written), and q_len draft tokens at positions n..n+q_len-1
+    whose K/V rows are inputs, not cache contents.  Committed rows and
+    drafts come from ``default_rng([seed, b, p])`` for position p, so any of
+    them can be regenerated alone.  The query holds the drafts' q_len query
+    rows.  Default q_len 5: a step of 4 drafts plus the last accepted token."""
+    seed = SEED_BASE + seed_offset
+    lens = np.asarray(RING_VERIFY_LENGTHS if lengths is None else lengths, dtype=np.int64)
+    batch = lens.size
+    cap = sink + window
+    bps_cap = _ceil_div(cap, block_size)
+    rng = np.random.Generator(np.random.PCG64(seed))
+    nblk = math.ceil(1.1 * bps_cap * batch)
+    tables, pad = _placement_tables(rng, [bps_cap] * batch, nblk, bps_cap, pad_with_minus_one)
+    query = draw_values(rng, (batch, q_len, num_q_heads, head_dim), dtype)
+    writes = []
+    dk = np.empty((batch, q_len, num_kv_heads, head_dim), dtype=query.dtype)
+    dv = np.empty_like(dk)
+    for b in range(batch):
+        n = int(lens[b])
+        pos = ring_survivor_positions(n, sink, window)
+        ks = np.empty((pos.size, num_kv_heads, head_dim), dtype=query.dtype)
+        vs = np.empty_like(ks)
+        for i, p in enumerate(pos):
+            r = np.random.default_rng([seed, b, int(p)])
+            ks[i] = draw_values(r, (num_kv_heads, head_dim), dtype)
+            vs[i] = draw_values(r, (num_kv_heads, head_dim), dtype)
+        writes.append(WriteChunk(b, pos, ks, vs))
+        for i in range(q_len):
+            r = np.random.default_rng([seed, b, n + i])
+            dk[b, i] = draw_values(r, (num_kv_heads, head_dim), dtype)
+            dv[b, i] = draw_values(r, (num_kv_heads, head_dim), dtype)
+    return DecodeCase(
+        name="ring_verify", seed=seed, dtype=dtype, num_blocks=nblk, block_size=block_size,
+        num_kv_heads=num_kv_heads, num_q_heads=num_q_heads, head_dim=head_dim,
+        scale=1.0 / math.sqrt(head_dim), context_lens=lens.astype(np.int32),
+        block_tables=tables, query=query, writes=writes,
+        ring=RingSpec(sink, window, 10000.0), pad_block=pad, q_len=q_len,
+        draft_keys=dk, draft_values=dv,
     )
 
 
