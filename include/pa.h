@@ -506,6 +506,35 @@ int pa_decode_multi(pa_pool *pool, void *out, const void *query, const int32_t *
                     int32_t q_len, int32_t num_q_heads, int32_t max_context_len, float scale,
                     void *workspace, size_t workspace_bytes, void *stream);
 
+/* Device: speculative verification over the sink + ring cache [P3,
+ * "嵌入式流式推理的访存墙与投机瓶颈": the target model scores a step of draft
+ * tokens in one pass; "环形上下文与注意力沉淀机制": the sink + ring cache and
+ * its cache-order RoPE; "C++ 环形 KV 缓存管理内核实现": drafts that are
+ * rejected are rolled back].  Stream b holds its committed positions
+ * 0..n_b-1 in the ring (n_b = context_lens[b], clamped to [0,
+ * max_context_len]); its q_len draft tokens sit at positions n_b..n_b+q_len-1
+ * with query rows query[b, i] ([B, q_len, Hq, D]) and K/V rows
+ * draft_key[b, i], draft_value[b, i] ([B, q_len, Hkv, D]), all in the
+ * pool's dtype and un-rotated.  out[b, i] ([B, q_len, Hq, D]) is what
+ * decoding draft i alone would give after drafts 0..i had been written to
+ * their ring slots: the single-token ring decode over that cache.  The
+ * drafts are never written: the cache is read only, so after the caller
+ * accepts a_b drafts it stores them with pa_reshape_and_cache at the ring
+ * slots of positions n_b..n_b+a_b-1 and the rejected ones leave nothing to
+ * undo.  1 <= q_len <= 16; ring is required and its RoPE table must cover
+ * sink + window + q_len - 1 positions (rope_capacity) at the pool's head
+ * size (PA_ERR_INVAL otherwise); f16/bf16 pools only (PA_ERR_UNSUPPORTED
+ * otherwise).  workspace: pa_decode_verify_ring_workspace_bytes(pool,
+ * num_seqs, q_len, num_q_heads) bytes, 256-byte aligned, no initialisation
+ * needed.  Other arguments and errors as pa_decode_multi. */
+int pa_decode_verify_ring(pa_pool *pool, void *out, const void *query, const void *draft_key,
+                          const void *draft_value, const int32_t *block_tables, int32_t max_blocks_per_seq,
+                          const int32_t *context_lens, int32_t num_seqs, int32_t q_len, int32_t num_q_heads,
+                          int32_t max_context_len, float scale, const pa_ring *ring, void *workspace,
+                          size_t workspace_bytes, void *stream);
+size_t pa_decode_verify_ring_workspace_bytes(const pa_pool *pool, int32_t num_seqs, int32_t q_len,
+                                             int32_t num_q_heads);
+
 /* Name of a status code (static string). */
 const char *pa_status_str(int status);
 

@@ -21,6 +21,7 @@ __all__ = [
     "decode_append_noalloc", "decode_noalloc_scratch_bytes",
     "check_decode_inputs", "DTYPES",
     "block_hashes", "copy_blocks", "set_option", "decode_multi_workspace_bytes", "decode_multi", "Batcher",
+    "decode_verify_ring", "decode_verify_ring_workspace_bytes",
 ]
 
 DTYPES = {"f32": _lib.PA_F32, "f16": _lib.PA_F16, "bf16": _lib.PA_BF16}
@@ -459,6 +460,39 @@ def decode_multi(pool: Pool, out, query, block_tables, context_lens, max_context
         _dev_ptr(block_tables, "block_tables"), int(block_tables.shape[1]),
         _dev_ptr(context_lens, "context_lens"), b, ql, hq, int(max_context_len), float(scale),
         ws_ptr, ws_bytes, _stream_ptr(stream)), "pa_decode_multi")
+
+
+def decode_verify_ring_workspace_bytes(pool: Pool, num_seqs: int, q_len: int, num_q_heads: int) -> int:
+    return int(_lib.load().pa_decode_verify_ring_workspace_bytes(pool.handle, num_seqs, q_len, num_q_heads))
+
+
+def decode_verify_ring(pool: Pool, out, query, draft_key, draft_value, block_tables, context_lens,
+                       max_context_len: int, scale: float, ring: Ring, workspace=None, stream=None) -> None:
+    """Speculative verification over the sink + ring cache: ``query``/``out``
+    [B, q_len, Hq, D], the drafts' K/V rows ``draft_key``/``draft_value``
+    [B, q_len, Hkv, D]; context_lens [B] counts committed positions only.
+    The cache is only read (device tensors, async)."""
+    b, ql, hq, d = query.shape
+    if tuple(out.shape) != (b, ql, hq, d) or d != pool.head_dim:
+        raise ValueError("out/query must be [B, q_len, Hq, D] with D = the pool's head size")
+    if query.dtype != pool.act_dtype or out.dtype != pool.act_dtype:
+        raise ValueError("query/out dtype must match the pool")
+    if tuple(draft_key.shape) != (b, ql, pool.num_kv_heads, d) or draft_key.shape != draft_value.shape:
+        raise ValueError("draft_key/draft_value must be [B, q_len, Hkv, D]")
+    if draft_key.dtype != pool.act_dtype or draft_value.dtype != pool.act_dtype:
+        raise ValueError("draft_key/draft_value dtype must match the pool")
+    if ring is None:
+        raise ValueError("ring verification needs the ring")
+    _check_tables(pool, block_tables, context_lens, b, ring)
+    ws_ptr, ws_bytes = None, 0
+    if workspace is not None:
+        ws_ptr = _dev_ptr(workspace, "workspace")
+        ws_bytes = workspace.numel() * workspace.element_size()
+    _check(_lib.load().pa_decode_verify_ring(
+        pool.handle, _dev_ptr(out, "out"), _dev_ptr(query, "query"), _dev_ptr(draft_key, "draft_key"),
+        _dev_ptr(draft_value, "draft_value"), _dev_ptr(block_tables, "block_tables"), int(block_tables.shape[1]),
+        _dev_ptr(context_lens, "context_lens"), b, ql, hq, int(max_context_len), float(scale), _ring_ptr(ring),
+        ws_ptr, ws_bytes, _stream_ptr(stream)), "pa_decode_verify_ring")
 
 
 class Batcher:

@@ -107,7 +107,8 @@ struct MultiLayout {
 
 // Sizes of one launch slice (at most kMaxMultiSeqsHost (sequence, pass
 // group) pairs); slices run one after another and reuse the workspace.
-MultiLayout multi_layout(const pa_pool *pool, int32_t num_seqs, int32_t q_len, int32_t num_q_heads) {
+MultiLayout multi_layout(const pa_pool *pool, int32_t num_seqs, int32_t q_len, int32_t num_q_heads,
+                         bool ring = false) {
   MultiLayout m{};
   const int hkv = pool->num_kv_heads;
   const int group = num_q_heads / hkv;
@@ -120,7 +121,7 @@ MultiLayout multi_layout(const pa_pool *pool, int32_t num_seqs, int32_t q_len, i
   const int forced_w = option(PA_OPT_MULTI_WAVES);
   m.waves = (forced_w == 1 || forced_w == 2) ? forced_w
             : (pool->kv_fp8 || rows > 3 * 16 * max_mt) ? 2 : 1;
-  const int wave_mt = m.waves == 2 ? 2 : max_mt;
+  const int wave_mt = ring ? kMultiMaxRowTilesRing(m.waves) : m.waves == 2 ? 2 : max_mt;
   const int forced_mt = option(PA_OPT_MULTI_ROW_TILES);
   m.mt = (int)std::min<int64_t>(forced_mt >= 1 && forced_mt <= wave_mt ? forced_mt : wave_mt, ceil_div(rows, 16));
   m.pass_rows = 16 * m.mt;
@@ -144,6 +145,103 @@ MultiLayout multi_layout(const pa_pool *pool, int32_t num_seqs, int32_t q_len, i
 }
 
 constexpr int kMaxMultiQLen = 4096;
+
+// Multi-token decode (ring == nullptr: new tokens already cached) and
+// speculative verification over the sink + ring cache (ring != nullptr:
+// drafts read from draft_k / draft_v).
+int multi_impl(pa_pool *pool, void *out, const void *query, const void *draft_k, const void *draft_v,
+               const int32_t *block_tables, int32_t max_blocks_per_seq, const int32_t *context_lens,
+               int32_t num_seqs, int32_t q_len, int32_t num_q_heads, int32_t max_context_len, float scale,
+               const pa_ring *ring, void *workspace, size_t workspace_bytes, void *stream) {
+  if (pool == nullptr || num_seqs < 0 || q_len < 1 || q_len > pa::kMaxMultiQLen || num_q_heads <= 0 ||
+      max_context_len < 0 || max_blocks_per_seq <= 0)
+    return PA_ERR_INVAL;
+  if (num_q_heads % pool->num_kv_heads != 0) return PA_ERR_INVAL;
+  const int group = num_q_heads / pool->num_kv_heads;
+  // one launch slice must hold every pass of a sequence
+  if (pa::ceil_div((int64_t)q_len * group, 16 * pa::kMultiMaxRowTiles(pool->head_dim)) >
+      pa::kMaxMultiSeqsHost)
+    return PA_ERR_UNSUPPORTED;
+  if (pool->dtype != PA_F16 && pool->dtype != PA_BF16) return PA_ERR_UNSUPPORTED;
+  if (ring != nullptr && pool->kv_fp8) return PA_ERR_UNSUPPORTED;
+  if (num_seqs == 0) return PA_OK;
+  if (out == nullptr || query == nullptr || block_tables == nullptr || context_lens == nullptr)
+    return PA_ERR_INVAL;
+  if (!pa::aligned16(out) || !pa::aligned16(query)) return PA_ERR_INVAL;
+  if ((reinterpret_cast<uintptr_t>(block_tables) | reinterpret_cast<uintptr_t>(context_lens)) & 3u)
+    return PA_ERR_INVAL;
+  if (ring == nullptr) {
+    if (max_context_len > (int64_t)max_blocks_per_seq * pool->block_size) return PA_ERR_INVAL;
+  } else {
+    // the table covers the ring's slots; the RoPE table covers the drafts'
+    // rotations (up to S + W + q_len - 2) at the pool's head size
+    if ((int64_t)ring->sink + ring->window > (int64_t)max_blocks_per_seq * pool->block_size) return PA_ERR_INVAL;
+    if (ring->rope_table == nullptr || !pa::aligned16(ring->rope_table)) return PA_ERR_INVAL;
+    if ((int64_t)ring->rope_capacity < (int64_t)ring->sink + ring->window + q_len - 1 ||
+        ring->rope_head_dim != pool->head_dim)
+      return PA_ERR_INVAL;
+    if (!pa::aligned16(draft_k) || !pa::aligned16(draft_v)) return PA_ERR_INVAL;
+  }
+  if (!(scale == scale)) return PA_ERR_INVAL;
+  const pa::MultiLayout m = pa::multi_layout(pool, num_seqs, q_len, num_q_heads, ring != nullptr);
+  if (workspace == nullptr || workspace_bytes < m.total) return PA_ERR_NOMEM;
+  if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return PA_ERR_INVAL;
+
+  pa::MultiArgs a{};
+  a.k_cache = pool->k_cache;
+  a.v_cache = pool->v_cache;
+  char *ws = static_cast<char *>(workspace);
+  a.ws_sched = reinterpret_cast<int32_t *>(ws);
+  a.ws_ml = reinterpret_cast<float *>(ws + m.sched_bytes);
+  a.ws_o = reinterpret_cast<float *>(ws + m.sched_bytes + m.ml_bytes);
+  a.kv_block_stride = (int64_t)pool->block_size * pool->num_kv_heads * pool->head_dim;
+  a.num_blocks = pool->num_blocks;
+  a.max_context = max_context_len;
+  a.max_blocks_per_seq = max_blocks_per_seq;
+  a.num_q_heads = num_q_heads;
+  a.num_kv_heads = pool->num_kv_heads;
+  a.group = group;
+  a.q_len = q_len;
+  a.rows = q_len * group;
+  a.pass_rows = m.pass_rows;
+  a.passes = m.passes;
+  a.pass_group = m.pass_group;
+  a.pgroups = m.pgroups;
+  a.groups = m.groups;
+  const int forced_range = pa::option(PA_OPT_MULTI_MIN_RANGE);
+  a.min_range_tiles = forced_range >= 1 ? forced_range : 4;
+  a.block_shift = pa::log2_exact(pool->block_size);
+  a.scale_log2 = scale * pa::kLog2eHost;
+  if (ring != nullptr) {
+    a.rope = ring->rope_table;
+    a.ring_sink = ring->sink;
+    a.ring_window = ring->window;
+  }
+  if (pool->kv_fp8)
+    for (int h = 0; h < pool->num_kv_heads; ++h) {
+      a.kv_scale.k[h] = pool->k_scale[h];
+      a.kv_scale.v[h] = pool->v_scale[h];
+    }
+  const int64_t row_elems = (int64_t)q_len * num_q_heads * pool->head_dim;
+  const int esize = pa::dtype_bytes(pool->dtype);
+  const int grid = m.grid;
+  for (int32_t s0 = 0; s0 < num_seqs; s0 += m.seqs_per_launch) {
+    a.num_seqs = std::min(m.seqs_per_launch, num_seqs - s0);
+    a.out = static_cast<char *>(out) + s0 * row_elems * esize;
+    a.query = static_cast<const char *>(query) + s0 * row_elems * esize;
+    a.block_tables = block_tables + (int64_t)s0 * max_blocks_per_seq;
+    a.context_lens = context_lens + s0;
+    if (ring != nullptr) {
+      const int64_t drow = (int64_t)q_len * pool->num_kv_heads * pool->head_dim * esize;
+      a.draft_k = static_cast<const char *>(draft_k) + s0 * drow;
+      a.draft_v = static_cast<const char *>(draft_v) + s0 * drow;
+    }
+    const int rc = pa::hip_status(pa::launch_decode_multi(a, pool->dtype, pool->head_dim, pa::kv8_format(pool), m.waves,
+                                                          grid, static_cast<hipStream_t>(stream), ring != nullptr));
+    if (rc != PA_OK) return rc;
+  }
+  return PA_OK;
+}
 
 }  // namespace
 
@@ -242,72 +340,30 @@ int pa_decode_multi(pa_pool *pool, void *out, const void *query, const int32_t *
                     int32_t max_blocks_per_seq, const int32_t *context_lens, int32_t num_seqs,
                     int32_t q_len, int32_t num_q_heads, int32_t max_context_len, float scale,
                     void *workspace, size_t workspace_bytes, void *stream) {
-  if (pool == nullptr || num_seqs < 0 || q_len < 1 || q_len > pa::kMaxMultiQLen || num_q_heads <= 0 ||
-      max_context_len < 0 || max_blocks_per_seq <= 0)
-    return PA_ERR_INVAL;
-  if (num_q_heads % pool->num_kv_heads != 0) return PA_ERR_INVAL;
-  const int group = num_q_heads / pool->num_kv_heads;
-  // one launch slice must hold every pass of a sequence
-  if (pa::ceil_div((int64_t)q_len * group, 16 * pa::kMultiMaxRowTiles(pool->head_dim)) >
-      pa::kMaxMultiSeqsHost)
-    return PA_ERR_UNSUPPORTED;
-  if (pool->dtype != PA_F16 && pool->dtype != PA_BF16) return PA_ERR_UNSUPPORTED;
-  if (num_seqs == 0) return PA_OK;
-  if (out == nullptr || query == nullptr || block_tables == nullptr || context_lens == nullptr)
-    return PA_ERR_INVAL;
-  if (!pa::aligned16(out) || !pa::aligned16(query)) return PA_ERR_INVAL;
-  if ((reinterpret_cast<uintptr_t>(block_tables) | reinterpret_cast<uintptr_t>(context_lens)) & 3u)
-    return PA_ERR_INVAL;
-  if (max_context_len > (int64_t)max_blocks_per_seq * pool->block_size) return PA_ERR_INVAL;
-  if (!(scale == scale)) return PA_ERR_INVAL;
-  const pa::MultiLayout m = pa::multi_layout(pool, num_seqs, q_len, num_q_heads);
-  if (workspace == nullptr || workspace_bytes < m.total) return PA_ERR_NOMEM;
-  if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return PA_ERR_INVAL;
+  return pa::multi_impl(pool, out, query, nullptr, nullptr, block_tables, max_blocks_per_seq, context_lens,
+                        num_seqs, q_len, num_q_heads, max_context_len, scale, nullptr, workspace, workspace_bytes,
+                        stream);
+}
 
-  pa::MultiArgs a{};
-  a.k_cache = pool->k_cache;
-  a.v_cache = pool->v_cache;
-  char *ws = static_cast<char *>(workspace);
-  a.ws_sched = reinterpret_cast<int32_t *>(ws);
-  a.ws_ml = reinterpret_cast<float *>(ws + m.sched_bytes);
-  a.ws_o = reinterpret_cast<float *>(ws + m.sched_bytes + m.ml_bytes);
-  a.kv_block_stride = (int64_t)pool->block_size * pool->num_kv_heads * pool->head_dim;
-  a.num_blocks = pool->num_blocks;
-  a.max_context = max_context_len;
-  a.max_blocks_per_seq = max_blocks_per_seq;
-  a.num_q_heads = num_q_heads;
-  a.num_kv_heads = pool->num_kv_heads;
-  a.group = group;
-  a.q_len = q_len;
-  a.rows = q_len * group;
-  a.pass_rows = m.pass_rows;
-  a.passes = m.passes;
-  a.pass_group = m.pass_group;
-  a.pgroups = m.pgroups;
-  a.groups = m.groups;
-  const int forced_range = pa::option(PA_OPT_MULTI_MIN_RANGE);
-  a.min_range_tiles = forced_range >= 1 ? forced_range : 4;
-  a.block_shift = pa::log2_exact(pool->block_size);
-  a.scale_log2 = scale * pa::kLog2eHost;
-  if (pool->kv_fp8)
-    for (int h = 0; h < pool->num_kv_heads; ++h) {
-      a.kv_scale.k[h] = pool->k_scale[h];
-      a.kv_scale.v[h] = pool->v_scale[h];
-    }
-  const int64_t row_elems = (int64_t)q_len * num_q_heads * pool->head_dim;
-  const int esize = pa::dtype_bytes(pool->dtype);
-  const int grid = m.grid;
-  for (int32_t s0 = 0; s0 < num_seqs; s0 += m.seqs_per_launch) {
-    a.num_seqs = std::min(m.seqs_per_launch, num_seqs - s0);
-    a.out = static_cast<char *>(out) + s0 * row_elems * esize;
-    a.query = static_cast<const char *>(query) + s0 * row_elems * esize;
-    a.block_tables = block_tables + (int64_t)s0 * max_blocks_per_seq;
-    a.context_lens = context_lens + s0;
-    const int rc = pa::hip_status(pa::launch_decode_multi(a, pool->dtype, pool->head_dim, pa::kv8_format(pool), m.waves,
-                                                          grid, static_cast<hipStream_t>(stream)));
-    if (rc != PA_OK) return rc;
-  }
-  return PA_OK;
+size_t pa_decode_verify_ring_workspace_bytes(const pa_pool *pool, int32_t num_seqs, int32_t q_len,
+                                             int32_t num_q_heads) {
+  if (pool == nullptr || num_seqs <= 0 || q_len < 1 || q_len > pa::kMaxVerifyDrafts || num_q_heads <= 0 ||
+      num_q_heads % pool->num_kv_heads != 0)
+    return 0;
+  return pa::multi_layout(pool, num_seqs, q_len, num_q_heads, true).total;
+}
+
+int pa_decode_verify_ring(pa_pool *pool, void *out, const void *query, const void *draft_key,
+                          const void *draft_value, const int32_t *block_tables, int32_t max_blocks_per_seq,
+                          const int32_t *context_lens, int32_t num_seqs, int32_t q_len, int32_t num_q_heads,
+                          int32_t max_context_len, float scale, const pa_ring *ring, void *workspace,
+                          size_t workspace_bytes, void *stream) {
+  if (ring == nullptr || !pa::ring_valid(ring)) return PA_ERR_INVAL;
+  if (q_len < 1 || q_len > pa::kMaxVerifyDrafts) return PA_ERR_INVAL;
+  if (draft_key == nullptr || draft_value == nullptr) return num_seqs == 0 ? PA_OK : PA_ERR_INVAL;
+  return pa::multi_impl(pool, out, query, draft_key, draft_value, block_tables, max_blocks_per_seq, context_lens,
+                        num_seqs, q_len, num_q_heads, max_context_len, scale, ring, workspace, workspace_bytes,
+                        stream);
 }
 
 size_t pa_decode_workspace_bytes(const pa_pool *pool, int32_t num_seqs, int32_t num_q_heads,

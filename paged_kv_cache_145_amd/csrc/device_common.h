@@ -240,6 +240,39 @@ __device__ __forceinline__ uint2 fp8x4_to_16(uint32_t v) {
   return make_uint2(code_pair_to_16<T, F, false>(v), code_pair_to_16<T, F, true>(v));
 }
 
+// ------------------------------------------------------------- RoPE ---
+// Rotate-half RoPE on a 16-bit fragment held as KB 16-byte chunks where
+// chunk kb covers d = 32 kb + 8 grp + [0, 8); chunk kb + KB/2 holds the
+// partner elements d + D/2.  `cs` points at the (cos, sin) row of the angle.
+template <class T, int KB>
+__device__ __forceinline__ void rope_frag16(uint4 (&f)[KB], const float *cs, int grp) {
+#pragma unroll
+  for (int kb = 0; kb < KB / 2; ++kb) {
+    const float4 *c4 = reinterpret_cast<const float4 *>(cs + 2 * (32 * kb + 8 * grp));
+    float c[8], s[8];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float4 v = c4[i];
+      c[2 * i] = v.x;
+      s[2 * i] = v.y;
+      c[2 * i + 1] = v.z;
+      s[2 * i + 1] = v.w;
+    }
+    uint16_t lo[8], hi[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float x = T::to_float(half_of(f[kb], e));
+      const float y = T::to_float(half_of(f[kb + KB / 2], e));
+      lo[e] = T::from_float(x * c[e] - y * s[e]);
+      hi[e] = T::from_float(x * s[e] + y * c[e]);
+    }
+    f[kb] = make_uint4(pack2(lo[0], lo[1]), pack2(lo[2], lo[3]), pack2(lo[4], lo[5]),
+                       pack2(lo[6], lo[7]));
+    f[kb + KB / 2] = make_uint4(pack2(hi[0], hi[1]), pack2(hi[2], hi[3]), pack2(hi[4], hi[5]),
+                                pack2(hi[6], hi[7]));
+  }
+}
+
 }  // namespace pa
 
 #endif  // PA_DEVICE_COMMON_H_

@@ -103,6 +103,16 @@ struct MultiArgs {
   int32_t block_shift;
   float scale_log2;
   KvScales kv_scale;  // 8-bit pools: dequantisation scales per KV head
+  // Speculative verification over the sink + ring cache: context_lens holds
+  // the committed positions n; the q_len drafts' K/V rows [B, q_len, Hkv, D]
+  // come from draft_k / draft_v (not the cache) as one extra tile per
+  // sequence; rope is the float2 (cos, sin) table of at least
+  // sink + window + q_len - 1 positions.
+  const void *draft_k;
+  const void *draft_v;
+  const float *rope;
+  int32_t ring_sink;
+  int32_t ring_window;
 };
 
 // CUs of the current device: the multi-token kernel's persistent grid is
@@ -111,6 +121,10 @@ int multi_grid();
 // Row tiles of 16 query rows one wave holds: registers allow four at
 // D = 64 and three at D = 128 (with a four-deep load pipeline).
 constexpr int kMultiMaxRowTiles(int head_dim) { return head_dim == 128 ? 3 : 4; }
+// Ring verification keeps a second (sink-rotated) query copy in registers:
+// at most two row tiles with one wave per SIMD, one with two.
+constexpr int kMultiMaxRowTilesRing(int waves) { return waves == 2 ? 1 : 2; }
+constexpr int kMaxVerifyDrafts = 16;  // drafts of one ring verification (one key tile)
 
 enum class DecodeKernel { kMfma, kValu };
 
@@ -135,7 +149,7 @@ hipError_t launch_decode(const DecodeArgs &a, pa_dtype dtype, int head_dim, bool
                          DecodeChoice choice, int num_seqs, hipStream_t stream);
 
 hipError_t launch_decode_multi(const MultiArgs &a, pa_dtype dtype, int head_dim, int kv8, int waves,
-                               int grid, hipStream_t stream);
+                               int grid, hipStream_t stream, bool ring = false);
 
 hipError_t launch_reshape_and_cache(pa_dtype dtype, void *k_cache, void *v_cache,
                                     const void *key, const void *value,

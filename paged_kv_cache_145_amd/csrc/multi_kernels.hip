@@ -26,6 +26,19 @@
 // partials in slots ((group + v) * Hkv + g) * PG + w, merged by
 // decode_multi_reduce_kernel.
 //
+// Ring mode (RING, speculative verification over the sink + ring cache):
+// context_lens holds the committed positions n, the resident keys are the
+// ring slots 0..L-1 (L = min(n, S + W)) read through the block table, and
+// the q_len drafts (positions n..n+q_len-1) are one more tile read from the
+// draft K/V buffers, never from the cache.  Row i (draft i, at p = n + i)
+// gives what decoding the drafts one at a time would: it sees the sinks,
+// the committed window keys its own write would not evict (positions
+// >= p + 1 - W) and drafts i + 1 - W .. i.  RoPE keeps the cache's
+// relative distances without re-rotating per row: keys are rotated by
+// J = pos for sinks and pos - off otherwise (off = max(0, n + 1 - S - W)),
+// the row's query by p - off for window keys and by min(p, S + W - 1) for
+// sinks (a second score MFMA, only on tiles that hold sinks).
+//
 // Per 16-token tile:
 //   S[token][row] = K_tile . Q^T with v_mfma_f32_16x16x32 (A = the lane's
 //   own K row fragment, B = query rows); lane l gets S[4(l/16)+j][l%16];
@@ -124,7 +137,7 @@ __device__ __forceinline__ int mq_active_groups(const MultiArgs &a, int total) {
 // Tile schedule of the launch: s_tfirst[v] = tiles of virtual sequences
 // before v, s_kvend[v] = key positions the rows of v's pass group see.  Work-group 0 also
 // publishes s_tfirst to the workspace for the merge kernel.
-__device__ int mq_schedule(const MultiArgs &a, int *s_tfirst, int *s_kvend, int *s_wsum) {
+__device__ int mq_schedule(const MultiArgs &a, int *s_tfirst, int *s_kvend, int *s_wsum, bool ring) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int nv = a.num_seqs * a.pgroups;
   int carry = 0;
@@ -133,11 +146,17 @@ __device__ int mq_schedule(const MultiArgs &a, int *s_tfirst, int *s_kvend, int 
     int n = 0;
     if (v < nv) {
       const int b = v / a.pgroups;
-      const int last = min(a.passes - 1, (v - b * a.pgroups) * a.pass_group + a.pass_group - 1);
-      int row0, row_end, kv_end;  // the group's last pass sees the most keys
-      mq_pass(a, mq_len(a, b), last, row0, row_end, kv_end);
-      s_kvend[v] = kv_end;
-      n = (kv_end + kTileTokens - 1) / kTileTokens;
+      if (ring) {  // committed ring slots, then the draft tile
+        const int L = min(mq_len(a, b), a.ring_sink + a.ring_window);
+        s_kvend[v] = L;
+        n = (L + kTileTokens - 1) / kTileTokens + 1;
+      } else {
+        const int last = min(a.passes - 1, (v - b * a.pgroups) * a.pass_group + a.pass_group - 1);
+        int row0, row_end, kv_end;  // the group's last pass sees the most keys
+        mq_pass(a, mq_len(a, b), last, row0, row_end, kv_end);
+        s_kvend[v] = kv_end;
+        n = (kv_end + kTileTokens - 1) / kTileTokens;
+      }
     }
     int x = n;  // inclusive scan within the wave
 #pragma unroll
@@ -169,11 +188,14 @@ __device__ int mq_schedule(const MultiArgs &a, int *s_tfirst, int *s_kvend, int 
 // the A operands of two score MFMAs, and the query fragments follow that
 // dimension order; codes widen exactly to 16-bit values before the MFMAs and
 // the LDS tile.
-template <class T, int D, int MT, int KVF, int W>
+template <class T, int D, int MT, int KVF, int W, bool RING>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(W, W)))
 void decode_multi_kernel(MultiArgs a) {
   constexpr bool KV8 = KVF != 0;
-  constexpr int kMqQSlots = kMqQSlotsFor<W>;
+  static_assert(!(KV8 && RING), "ring verification reads 16-bit pools");
+  // ring mode keeps a second, sink-rotated copy of each query fragment
+  constexpr int kMqQSlots = RING ? 1 : kMqQSlotsFor<W>;
+  constexpr int kQCopies = RING ? 2 : 1;
   constexpr int KB = D / 32;  // score MFMAs per row tile and key tile
   constexpr int EV = D / 16;  // V elements per lane per row
   constexpr int NB = D / 16;  // output MFMAs per row tile (16 dims each)
@@ -188,10 +210,10 @@ void decode_multi_kernel(MultiArgs a) {
   __shared__ int s_kvend[kMaxMqSeqs];
   __shared__ int s_wsum[kMqWaves];
   __shared__ __align__(16) char s_vt[kMqWaves][MqLds<D>::kVBytes];
-  __shared__ uint4 s_q[kMqWaves][kMqQSlots * QF * kWave];  // query fragments, lane-major
+  __shared__ uint4 s_q[kMqWaves][kQCopies * kMqQSlots * QF * kWave];  // query fragments, lane-major
 
   const int nv = a.num_seqs * a.pgroups;
-  const int total = mq_schedule(a, s_tfirst, s_kvend, s_wsum);
+  const int total = mq_schedule(a, s_tfirst, s_kvend, s_wsum, RING);
   const int hkv = a.num_kv_heads, G = a.group, ql = a.q_len, PG = a.pass_group;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -227,9 +249,17 @@ void decode_multi_kernel(MultiArgs a) {
   f32x4 acc[MT][NB];
   float m_run[MT], l_part[MT];
   int limit[MT];  // last key position this lane's row sees in each row tile (-1: none)
+                  // (ring: the row's draft index i, -1: none)
+  int lo_pos[MT];  // ring: oldest window position the row sees (p + 1 - W)
   uint4 qf[MT][KB];
+  uint4 qfs[RING ? MT : 1][RING ? KB : 1];  // ring: the sink-rotated copy
   int seg_row0 = 0, seg_row_end = 0;
   bool seg_whole = false;
+  // ring: committed length n, resident slots L, rotation offset, the slot
+  // of the newest committed position, whether sink rotations differ
+  int seg_n = 0, seg_L = 0, seg_off = 0, seg_rn = 0;
+  bool seg_dual = false;
+  const int S_ = RING ? a.ring_sink : 0, W_ = RING ? a.ring_window : 1;
 
   // Staged metadata of a chunk of up to 64 tiles (lane i: tile c0 + i),
   // read back with readlane.
@@ -253,10 +283,13 @@ void decode_multi_kernel(MultiArgs a) {
       tt = y - s_tfirst[lo];
       const int tiles = s_tfirst[lo + 1] - s_tfirst[lo];
       const int b = lo / a.pgroups;
-      blk = a.block_tables[(int64_t)b * a.max_blocks_per_seq + ((kTileTokens * tt) >> a.block_shift)];
-      blk = min(max(blk, 0), a.num_blocks - 1);
-      tvalid = min(kTileTokens, s_kvend[lo] - kTileTokens * tt);
-      tflag = (tt == 0 ? 1 : 0) | (tt == tiles - 1 ? 2 : 0);
+      const bool draft = RING && tt == tiles - 1;
+      if (!draft) {
+        blk = a.block_tables[(int64_t)b * a.max_blocks_per_seq + ((kTileTokens * tt) >> a.block_shift)];
+        blk = min(max(blk, 0), a.num_blocks - 1);
+      }
+      tvalid = draft ? ql : min(kTileTokens, s_kvend[lo] - kTileTokens * tt);
+      tflag = (tt == 0 ? 1 : 0) | (tt == tiles - 1 ? 2 : 0) | (draft ? 4 : 0);
     }
     // tiles that open a segment get a query slot in LDS; the chunk ends
     // before its (kMqQSlots + 1)-th opening tile
@@ -270,6 +303,7 @@ void decode_multi_kernel(MultiArgs a) {
     }
     tslot = opens && lane < cnt ? __popcll(m & ((1ull << lane) - 1)) : 0;
     uint4 qtmp[kMqQSlots][QF];
+    uint4 qsink[RING ? kMqQSlots : 1][RING ? QF : 1];
     unsigned long long mm = m;
 #pragma unroll
     for (int s2 = 0; s2 < kMqQSlots; ++s2) {
@@ -290,13 +324,31 @@ void decode_multi_kernel(MultiArgs a) {
         for (int kb = 0; kb < KB; ++kb)
           qtmp[s2][mt * KB + kb] =
               ok ? *reinterpret_cast<const uint4 *>(q + q_dim(kb)) : make_uint4(0u, 0u, 0u, 0u);
+        if constexpr (RING) {
+          // window copy rotated by p - off, sink copy by min(p, S + W - 1)
+          const int n = mq_len(a, b);
+          const int p = n + qi;
+          const int off = max(0, n + 1 - S_ - W_);
+          uint4 fw[KB], fs[KB];
+#pragma unroll
+          for (int kb = 0; kb < KB; ++kb) fw[kb] = fs[kb] = qtmp[s2][mt * KB + kb];
+          rope_frag16<T, KB>(fw, a.rope + (int64_t)(p - off) * D, grp);
+          rope_frag16<T, KB>(fs, a.rope + (int64_t)min(p, S_ + W_ - 1) * D, grp);
+#pragma unroll
+          for (int kb = 0; kb < KB; ++kb) {
+            qtmp[s2][mt * KB + kb] = fw[kb];
+            qsink[s2][mt * KB + kb] = fs[kb];
+          }
+        }
       }
       mm &= mm - 1;
     }
     if (lane < cnt) {
-      const int64_t off = ((int64_t)blk * a.kv_block_stride +
-                           (int64_t)((kTileTokens * tt) & bmask) * row_stride + (int64_t)g * D) *
-                          (int64_t)KVB;
+      // the draft tile's rows are those of the draft buffers
+      const int64_t off =
+          (tflag & 4) ? (((int64_t)(tv / a.pgroups) * ql * hkv + g) * D) * (int64_t)KVB
+                      : ((int64_t)blk * a.kv_block_stride + (int64_t)((kTileTokens * tt) & bmask) * row_stride +
+                         (int64_t)g * D) * (int64_t)KVB;
       toff_lo = (int)(uint32_t)off;
       toff_hi = (int)(off >> 32);
       tnrec = (int)(((tvalid - 1) * row_stride + D) * (int64_t)KVB);  // tvalid >= 1 here
@@ -305,6 +357,12 @@ void decode_multi_kernel(MultiArgs a) {
     for (int s2 = 0; s2 < kMqQSlots; ++s2)
 #pragma unroll
       for (int f = 0; f < QF; ++f) qs[(s2 * QF + f) * kWave + lane] = qtmp[s2][f];
+    if constexpr (RING) {
+#pragma unroll
+      for (int s2 = 0; s2 < kMqQSlots; ++s2)
+#pragma unroll
+        for (int f = 0; f < QF; ++f) qs[((kMqQSlots + s2) * QF + f) * kWave + lane] = qsink[s2][f];
+    }
   };
 
   // Loads of staged tile j (j >= cnt: empty record range, no memory access).
@@ -312,10 +370,11 @@ void decode_multi_kernel(MultiArgs a) {
     const int jj = min(j, kWave - 1);
     const uint64_t off = ((uint64_t)(uint32_t)rd(toff_hi, jj) << 32) | (uint32_t)rd(toff_lo, jj);
     const int nrec = j < cnt ? rd(tnrec, jj) : 0;
-    const auto kr = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<char *>(static_cast<const char *>(a.k_cache) + off), (short)0, nrec, kBufferWord3);
-    const auto vr = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<char *>(static_cast<const char *>(a.v_cache) + off), (short)0, nrec, kBufferWord3);
+    const bool draft = RING && (rd(tflag, jj) & 4);
+    const char *kbase = static_cast<const char *>(draft ? a.draft_k : a.k_cache);
+    const char *vbase = static_cast<const char *>(draft ? a.draft_v : a.v_cache);
+    const auto kr = __builtin_amdgcn_make_buffer_rsrc(const_cast<char *>(kbase + off), (short)0, nrec, kBufferWord3);
+    const auto vr = __builtin_amdgcn_make_buffer_rsrc(const_cast<char *>(vbase + off), (short)0, nrec, kBufferWord3);
 #pragma unroll
     for (int kb = 0; kb < KLD; ++kb) k[kb] = buffer_load16(kr, k_off + 64 * kb);
 #pragma unroll
@@ -335,10 +394,26 @@ void decode_multi_kernel(MultiArgs a) {
     const int L = mq_len(a, b);
     int kv_end;
     mq_pass(a, L, (v - b * a.pgroups) * PG + w, seg_row0, seg_row_end, kv_end);  // no rows past the last pass
+    if constexpr (RING) {
+      seg_n = L;
+      seg_L = min(L, S_ + W_);
+      seg_off = max(0, L + 1 - S_ - W_);
+      seg_rn = L > S_ ? S_ + (L - 1 - S_) % W_ : L - 1;
+      seg_dual = L + ql > S_ + W_;
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) qfs[mt][kb] = qs[((kMqQSlots + slot) * QF + mt * KB + kb) * kWave + lane];
+    }
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
       const int r = seg_row0 + 16 * mt + row16;
-      limit[mt] = r < seg_row_end ? L - ql + r / G : -1;
+      if constexpr (RING) {
+        limit[mt] = r < seg_row_end ? r / G : -1;
+        lo_pos[mt] = L + r / G + 1 - W_;
+      } else {
+        limit[mt] = r < seg_row_end ? L - ql + r / G : -1;
+      }
       m_run[mt] = -INFINITY;
       l_part[mt] = 0.f;
 #pragma unroll
@@ -366,6 +441,21 @@ void decode_multi_kernel(MultiArgs a) {
       for (int tau = 0; tau < 4; ++tau) vf[tau] = vraw[tau];
     }
     const int kp0 = kTileTokens * rd(tt, j) + 4 * grp;  // key position of S element 0
+    // ring: position of a committed key held by slot r (r < L)
+    auto slot_pos = [&](int r) {
+      if (r < S_ || seg_n <= S_ + W_) return r;
+      int d = seg_rn - r;
+      d += d < 0 ? W_ : 0;
+      return seg_n - 1 - d;
+    };
+    const bool dtile = RING && (rd(tflag, j) & 4);
+    if constexpr (RING) {
+      // rotate this lane's key (row16 of the tile) by J
+      const int r = kTileTokens * rd(tt, j) + row16;
+      const int pos = dtile ? (row16 < ql ? seg_n + row16 : 0) : (r < seg_L ? slot_pos(r) : 0);
+      const int jrot = pos < S_ ? pos : pos - seg_off;
+      rope_frag16<T, KB>(kf, a.rope + (int64_t)max(jrot, 0) * D, grp);
+    }
     f32x4 sv[MT];
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
@@ -373,6 +463,24 @@ void decode_multi_kernel(MultiArgs a) {
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb) sacc = T::mfma_16x16x32(kf[kb], qf[mt][kb], sacc);
       sv[mt] = sacc;
+    }
+    if constexpr (RING) {
+      // sink keys take the sink-rotated query (only tiles holding sinks, and
+      // only when the two rotations differ)
+      const bool has_sink = dtile ? seg_n < S_ : kTileTokens * rd(tt, j) < S_;
+      if (seg_dual && has_sink) {
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+          f32x4 sacc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int kb = 0; kb < KB; ++kb) sacc = T::mfma_16x16x32(kf[kb], qfs[mt][kb], sacc);
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int pos = dtile ? seg_n + 4 * grp + r : kp0 + r;  // sink keys: position = slot
+            if (pos < S_) sv[mt][r] = sacc[r];
+          }
+        }
+      }
     }
     // V rows past the keys the pass sees were loaded as zeros, so a zero
     // weight never meets a NaN sentinel; rows before hold written values.
@@ -387,7 +495,21 @@ void decode_multi_kernel(MultiArgs a) {
     for (int mt = 0; mt < MT; ++mt) {
       float sc[4];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) sc[r] = (kp0 + r <= limit[mt]) ? sv[mt][r] * sl2 : -INFINITY;
+      for (int r = 0; r < 4; ++r) {
+        bool vis;
+        if constexpr (RING) {
+          if (dtile) {  // draft d: causal, and not evicted by the row's own write
+            const int d = 4 * grp + r;
+            vis = d < ql && d <= limit[mt] && (seg_n + d < S_ || seg_n + d >= lo_pos[mt]);
+          } else {
+            const int rs = kp0 + r;
+            vis = limit[mt] >= 0 && rs < seg_L && (rs < S_ || slot_pos(rs) >= lo_pos[mt]);
+          }
+        } else {
+          vis = kp0 + r <= limit[mt];
+        }
+        sc[r] = vis ? sv[mt][r] * sl2 : -INFINITY;
+      }
       const float lmax = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
       if (__any(lmax > m_run[mt] + kMqRescaleSlack)) {
         float tmax = fmaxf(lmax, __shfl_xor(lmax, 16));
@@ -578,9 +700,9 @@ __global__ __launch_bounds__(256) void decode_multi_reduce_kernel(MultiArgs a) {
   out[3] = T::from_float(acc.w * inv);
 }
 
-template <class T, int D, int MT, int KVF, int W>
+template <class T, int D, int MT, int KVF, int W, bool RING>
 hipError_t launch_mt(const MultiArgs &a, int grid, hipStream_t stream) {
-  hipLaunchKernelGGL((decode_multi_kernel<T, D, MT, KVF, W>), dim3(grid), dim3(kMqWaves * kWave), 0, stream, a);
+  hipLaunchKernelGGL((decode_multi_kernel<T, D, MT, KVF, W, RING>), dim3(grid), dim3(kMqWaves * kWave), 0, stream, a);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   constexpr int rpb = 256 / (D / 4);
@@ -590,31 +712,37 @@ hipError_t launch_mt(const MultiArgs &a, int grid, hipStream_t stream) {
   return hipGetLastError();
 }
 
-template <class T, int D, int KVF>
+template <class T, int D, int KVF, bool RING>
 hipError_t launch_d(const MultiArgs &a, int mt, int waves, int grid, hipStream_t stream) {
-  if (waves == 2) return mt == 1 ? launch_mt<T, D, 1, KVF, 2>(a, grid, stream)
-                                 : launch_mt<T, D, 2, KVF, 2>(a, grid, stream);
+  if constexpr (RING) {  // row tiles per wave: see kMultiMaxRowTilesRing
+    if (waves == 2) return mt == 1 ? launch_mt<T, D, 1, KVF, 2, true>(a, grid, stream) : hipErrorInvalidValue;
+    if (mt > 2) return hipErrorInvalidValue;
+    return mt == 1 ? launch_mt<T, D, 1, KVF, 1, true>(a, grid, stream) : launch_mt<T, D, 2, KVF, 1, true>(a, grid, stream);
+  }
+  if (waves == 2) return mt == 1 ? launch_mt<T, D, 1, KVF, 2, RING>(a, grid, stream)
+                                 : launch_mt<T, D, 2, KVF, 2, RING>(a, grid, stream);
   switch (mt) {
-    case 1: return launch_mt<T, D, 1, KVF, 1>(a, grid, stream);
-    case 2: return launch_mt<T, D, 2, KVF, 1>(a, grid, stream);
-    case 3: return launch_mt<T, D, 3, KVF, 1>(a, grid, stream);
-    default: return launch_mt<T, D, kMultiMaxRowTiles(D), KVF, 1>(a, grid, stream);
+    case 1: return launch_mt<T, D, 1, KVF, 1, RING>(a, grid, stream);
+    case 2: return launch_mt<T, D, 2, KVF, 1, RING>(a, grid, stream);
+    case 3: return launch_mt<T, D, 3, KVF, 1, RING>(a, grid, stream);
+    default: return launch_mt<T, D, kMultiMaxRowTiles(D), KVF, 1, RING>(a, grid, stream);
   }
 }
 
-template <class T, int KVF>
+template <class T, int KVF, bool RING>
 hipError_t launch_h(const MultiArgs &a, int head_dim, int mt, int waves, int grid, hipStream_t stream) {
-  return head_dim == 128 ? launch_d<T, 128, KVF>(a, mt, waves, grid, stream)
-                         : launch_d<T, 64, KVF>(a, mt, waves, grid, stream);
+  return head_dim == 128 ? launch_d<T, 128, KVF, RING>(a, mt, waves, grid, stream)
+                         : launch_d<T, 64, KVF, RING>(a, mt, waves, grid, stream);
 }
 
 template <class T>
 hipError_t launch_t(const MultiArgs &a, int head_dim, int kv8, int mt, int waves, int grid,
-                    hipStream_t stream) {
+                    hipStream_t stream, bool ring) {
+  if (ring) return kv8 == 0 ? launch_h<T, 0, true>(a, head_dim, mt, waves, grid, stream) : hipErrorInvalidValue;
   switch (kv8) {
-    case 0: return launch_h<T, 0>(a, head_dim, mt, waves, grid, stream);
-    case kKvE4M3: return launch_h<T, kKvE4M3>(a, head_dim, mt, waves, grid, stream);
-    case kKvE5M2: return launch_h<T, kKvE5M2>(a, head_dim, mt, waves, grid, stream);
+    case 0: return launch_h<T, 0, false>(a, head_dim, mt, waves, grid, stream);
+    case kKvE4M3: return launch_h<T, kKvE4M3, false>(a, head_dim, mt, waves, grid, stream);
+    case kKvE5M2: return launch_h<T, kKvE5M2, false>(a, head_dim, mt, waves, grid, stream);
     default: return hipErrorInvalidValue;
   }
 }
@@ -633,10 +761,10 @@ int multi_grid() {
 }
 
 hipError_t launch_decode_multi(const MultiArgs &a, pa_dtype dtype, int head_dim, int kv8, int waves,
-                               int grid, hipStream_t stream) {
+                               int grid, hipStream_t stream, bool ring) {
   const int mt = a.pass_rows / 16;
-  if (dtype == PA_BF16) return launch_t<BF16>(a, head_dim, kv8, mt, waves, grid, stream);
-  return launch_t<F16>(a, head_dim, kv8, mt, waves, grid, stream);
+  if (dtype == PA_BF16) return launch_t<BF16>(a, head_dim, kv8, mt, waves, grid, stream, ring);
+  return launch_t<F16>(a, head_dim, kv8, mt, waves, grid, stream, ring);
 }
 
 }  // namespace pa

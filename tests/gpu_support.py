@@ -54,7 +54,7 @@ def options(**kv):
 class DeviceCase:
     """A workload resident on cuda:0: pools filled by the library's writes."""
 
-    def __init__(self, case: workloads.DecodeCase, device: str = "cuda:0"):
+    def __init__(self, case: workloads.DecodeCase, device: str = "cuda:0", rope_extra: int = 0):
         self.case = case
         self.device = device
         dt = case.dtype
@@ -78,11 +78,13 @@ class DeviceCase:
             self.pool = pk.Pool(self.k_cache, self.v_cache, case.block_size)
         self.ring = None
         if case.ring is not None:
-            cap = case.ring.sink + case.ring.window
+            # rope_extra: positions beyond sink + window (ring verification
+            # rotates drafts up to q_len - 1 past them)
+            cap = case.ring.sink + case.ring.window + rope_extra
             nbytes = pk.rope_table_bytes(cap, case.head_dim)
             table = torch.empty(nbytes // 4, dtype=torch.float32, device=device)
             pk.rope_table_init(table, cap, case.head_dim, case.ring.rope_base)
-            self.ring = pk.Ring(case.ring.sink, case.ring.window, case.ring.rope_base, table)
+            self.ring = pk.Ring(case.ring.sink, case.ring.window, case.ring.rope_base, table, capacity=cap)
         self.block_tables = torch.from_numpy(np.ascontiguousarray(case.block_tables, dtype=np.int32)).to(device)
         self.context_lens = torch.from_numpy(np.ascontiguousarray(case.context_lens, dtype=np.int32)).to(device)
         self.query = raw_to_torch(case.query, dt).to(device)
