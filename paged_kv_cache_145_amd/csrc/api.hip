@@ -430,8 +430,7 @@ int decode_impl(pa_pool *pool, void *out, const void *query, const int32_t *bloc
   if (num_q_heads % pool->num_kv_heads != 0) return PA_ERR_INVAL;
   const int group = num_q_heads / pool->num_kv_heads;
   if (!pa::ring_valid(ring)) return PA_ERR_INVAL;
-  if (pool->kv_fp8 &&
-      (ring != nullptr || pa::choose_decode_kernel(pool->dtype, group).kernel != pa::DecodeKernel::kMfma))
+  if (pool->kv_fp8 && pa::choose_decode_kernel(pool->dtype, group).kernel != pa::DecodeKernel::kMfma)
     return PA_ERR_UNSUPPORTED;
   if (num_seqs == 0) return PA_OK;
   if (out == nullptr || query == nullptr || block_tables == nullptr || context_lens == nullptr)

@@ -16,10 +16,11 @@
 //    order so RoPE keeps relative distances as the ring slides.
 //
 // Work decomposition (MI355X-first, not the pages' CUDA design):
-//  * decode_mfma_kernel (16-bit K/V, GQA group 4..16): stream-K over
-//    16-token tiles, one work-group of 4 waves per CU, one KV head per
-//    wave; both contractions on MFMA; a separate combine kernel merges the
-//    partials of sequences cut by a range boundary.
+//  * decode_mfma_kernel (16-bit K/V or 8-bit codes, GQA group 1..16, plain
+//    or sink + ring): stream-K over 16-token tiles, one work-group of 4
+//    waves per CU (two on 8-bit pools), one KV head per wave; both
+//    contractions on MFMA; a separate combine kernel merges the partials
+//    of sequences cut by a range boundary.
 //  * decode_valu_kernel (any dtype, any group): persistent work-groups over
 //    (partition, KV head, head chunk, sequence) items with VALU dot
 //    products; decode_reduce_kernel merges partitions.
@@ -366,8 +367,8 @@ __device__ __forceinline__ void locate_tile(const int *s_tfirst, int num_seqs, i
 // 16-bit pools: one wave per SIMD (a memory-bound wave paired with an older
 // neighbour falls behind it).  8-bit pools halve the bytes per tile and the
 // per-tile arithmetic then dominates, so two waves per SIMD overlap it.
-// APP: the launch also stores each sequence's new token (16-bit pools, no
-// ring); a separate instantiation, so plain decode carries none of it.
+// APP: the launch also stores each sequence's new token (8-bit pools: its
+// codes); a separate instantiation, so plain decode carries none of it.
 // KVF: 0 for 16-bit pools, else the 8-bit format (kKvE4M3 or kKvE5M2).
 template <class T, int D, bool RING, int KVF, bool APP = false>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, KVF != 0 ? 2 : 1)))
@@ -382,7 +383,6 @@ void decode_mfma_kernel(DecodeArgs a) {
   // 8-bit pools (KV8): one byte per K/V element.  A lane's 16-byte K load
   // then carries 16 dimensions, the A operands of two score MFMAs; the
   // query fragments follow the same dimension order.
-  static_assert(!(KV8 && RING), "8-bit pools have no ring mode");
   constexpr int kQSlots = kQSlotsFor<KV8>;
   constexpr int KVB = KV8 ? 1 : (int)sizeof(st);  // bytes per K/V element
   constexpr int KLD = KV8 ? D / 64 : KB;          // 16-byte K loads per lane per tile
@@ -612,7 +612,10 @@ void decode_mfma_kernel(DecodeArgs a) {
     const int slot = rd(tslot, j);
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) qf[kb] = qs[(slot * KB + kb) * kWave + lane];
-    if constexpr (RING) rope_frag16<T, KB>(qf, a.rope + (int64_t)(s_len[b] - 1) * D, grp);
+    if constexpr (RING) {
+      if constexpr (KV8) rope_frag16_kv8<T, D>(qf, a.rope + (int64_t)(s_len[b] - 1) * D, grp);
+      else rope_frag16<T, KB>(qf, a.rope + (int64_t)(s_len[b] - 1) * D, grp);
+    }
     m_run = -INFINITY;
     l_part = 0.f;
 #pragma unroll
@@ -646,7 +649,8 @@ void decode_mfma_kernel(DecodeArgs a) {
       const int n = a.context_lens[b];
       const int r = kTileTokens * t + row16;
       const int jc = (j < cnt && r < L) ? ring_cache_index(r, n, a.ring_sink, a.ring_window) : 0;
-      rope_frag16<T, KB>(kf, a.rope + (int64_t)jc * D, grp);
+      if constexpr (KV8) rope_frag16_kv8<T, D>(kf, a.rope + (int64_t)jc * D, grp);
+      else rope_frag16<T, KB>(kf, a.rope + (int64_t)jc * D, grp);
     }
     f32x4 s = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -1142,8 +1146,7 @@ hipError_t launch_typed(const DecodeArgs &a, DecodeChoice choice, hipStream_t st
     if (choice.kernel == DecodeKernel::kMfma) {
       const int grid = mfma_grid<T, D, RING, KVF>(a.num_kv_heads);
       if (a.app_key != nullptr) {
-        if constexpr (RING && KV8) return hipErrorInvalidValue;
-        else hipLaunchKernelGGL((decode_mfma_kernel<T, D, RING, KVF, true>), dim3(grid), block, 0, stream, a);
+        hipLaunchKernelGGL((decode_mfma_kernel<T, D, RING, KVF, true>), dim3(grid), block, 0, stream, a);
       } else {
         hipLaunchKernelGGL((decode_mfma_kernel<T, D, RING, KVF>), dim3(grid), block, 0, stream, a);
       }
@@ -1191,7 +1194,13 @@ hipError_t launch_dtype(const DecodeArgs &a, int head_dim, bool ring, int kv8,
                         DecodeChoice choice, hipStream_t stream) {
   if constexpr (T::kBytes == 2) {
     if (kv8 == kKvE4M3 || kv8 == kKvE5M2) {
-      if (ring) return hipErrorInvalidValue;
+      if (ring) {
+        if (kv8 == kKvE5M2)
+          return head_dim == 128 ? launch_typed<T, 128, true, kKvE5M2>(a, choice, stream)
+                                 : launch_typed<T, 64, true, kKvE5M2>(a, choice, stream);
+        return head_dim == 128 ? launch_typed<T, 128, true, kKvE4M3>(a, choice, stream)
+                               : launch_typed<T, 64, true, kKvE4M3>(a, choice, stream);
+      }
       if (kv8 == kKvE5M2)
         return head_dim == 128 ? launch_typed<T, 128, false, kKvE5M2>(a, choice, stream)
                                : launch_typed<T, 64, false, kKvE5M2>(a, choice, stream);
@@ -1215,10 +1224,8 @@ int mfma_waves_t(int head_dim, int num_kv_heads) {
 
 template <class T, bool RING>
 int mfma_waves_r(int head_dim, int kv8, int num_kv_heads) {
-  if constexpr (!RING) {
-    if (kv8 == kKvE4M3) return mfma_waves_t<T, false, kKvE4M3>(head_dim, num_kv_heads);
-    if (kv8 == kKvE5M2) return mfma_waves_t<T, false, kKvE5M2>(head_dim, num_kv_heads);
-  }
+  if (kv8 == kKvE4M3) return mfma_waves_t<T, RING, kKvE4M3>(head_dim, num_kv_heads);
+  if (kv8 == kKvE5M2) return mfma_waves_t<T, RING, kKvE5M2>(head_dim, num_kv_heads);
   return mfma_waves_t<T, RING, 0>(head_dim, num_kv_heads);
 }
 

@@ -273,6 +273,54 @@ __device__ __forceinline__ void rope_frag16(uint4 (&f)[KB], const float *cs, int
   }
 }
 
+// The same rotation on fragments in the dimension order of 8-bit pools,
+// where chunk kb covers d = 64 (kb / 2) + 16 grp + 8 (kb % 2) + [0, 8) (a
+// lane's 16-byte load of codes is 16 consecutive dimensions).  D = 128: the
+// partner d + 64 is chunk kb + 2 of the same lane.  D = 64: the partner
+// d +- 32 is the same chunk of lane ^ 32 (grp ^ 2).
+template <class T, int D>
+__device__ __forceinline__ void rope_frag16_kv8(uint4 (&f)[D / 32], const float *cs, int grp) {
+  constexpr int KB = D / 32;
+  auto rotate = [&](uint4 &own, const uint4 &partner, int d0, float sign) {
+    const float4 *c4 = reinterpret_cast<const float4 *>(cs + 2 * d0);
+    float c[8], s[8];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float4 v = c4[i];
+      c[2 * i] = v.x;
+      s[2 * i] = v.y;
+      c[2 * i + 1] = v.z;
+      s[2 * i + 1] = v.w;
+    }
+    uint16_t r[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+      r[e] = T::from_float(T::to_float(half_of(own, e)) * c[e] + sign * T::to_float(half_of(partner, e)) * s[e]);
+    own = make_uint4(pack2(r[0], r[1]), pack2(r[2], r[3]), pack2(r[4], r[5]), pack2(r[6], r[7]));
+  };
+  if constexpr (D == 128) {
+#pragma unroll
+    for (int kb = 0; kb < KB / 2; ++kb) {
+      const uint4 lo = f[kb], hi = f[kb + KB / 2];
+      const int d0 = 16 * grp + 8 * kb;  // angle index of element 0 (d < D / 2)
+      rotate(f[kb], hi, d0, -1.f);
+      rotate(f[kb + KB / 2], lo, d0, 1.f);
+    }
+  } else {
+    static_assert(D == 64, "head size");
+    const bool low = grp < 2;
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) {
+      uint4 partner;
+      partner.x = __shfl_xor(f[kb].x, 32);
+      partner.y = __shfl_xor(f[kb].y, 32);
+      partner.z = __shfl_xor(f[kb].z, 32);
+      partner.w = __shfl_xor(f[kb].w, 32);
+      rotate(f[kb], partner, 16 * (grp & 1) + 8 * kb, low ? -1.f : 1.f);
+    }
+  }
+}
+
 }  // namespace pa
 
 #endif  // PA_DEVICE_COMMON_H_

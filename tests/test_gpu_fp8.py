@@ -144,18 +144,11 @@ def test_fp8_relabelling_bit_identical():
 def test_fp8_unsupported_combinations_are_rejected():
     case = workloads.FP8_CONFIGS["tiny_fp8"]()
     dc = DeviceCase(case)
-    out = torch.empty((case.num_seqs, case.num_q_heads, case.head_dim), dtype=torch.bfloat16, device="cuda")
     # a group above 16 has no 8-bit kernel
     q1 = torch.zeros((case.num_seqs, 32 * case.num_kv_heads, case.head_dim), dtype=torch.bfloat16, device="cuda")
     o1 = torch.empty_like(q1)
     with pytest.raises(pk.PaError) as e:
         pk.decode(dc.pool, o1, q1, dc.block_tables, dc.context_lens, int(case.context_lens.max()), 0.1)
-    assert e.value.status == -5
-    # the ring cache is not combined with 8-bit pools
-    table = torch.empty(pk.rope_table_bytes(64, case.head_dim) // 4, dtype=torch.float32, device="cuda")
-    ring = pk.Ring(4, 60, 10000.0, table)
-    with pytest.raises(pk.PaError) as e:
-        pk.decode(dc.pool, out, dc.query, dc.block_tables, dc.context_lens, 64, 0.1, ring=ring)
     assert e.value.status == -5
     dc.close()
 
@@ -174,3 +167,31 @@ def test_fp8_small_groups(hq, hkv, d, kv_format):
     assert_parity(out, ref, case.dtype)
     assert np.all(out.float().cpu().numpy()[4] == 0)
     dc.close()
+
+
+RING_FP8 = [("e4m3", 128, 12, 2), ("e5m2", 128, 12, 2), ("e4m3", 64, 8, 2), ("e5m2", 64, 4, 4)]
+
+
+@pytest.mark.parametrize("kv_format,d,hq,hkv", RING_FP8, ids=lambda v: str(v))
+@pytest.mark.parametrize("lengths", ["parity", "timing"])
+def test_fp8_ring_parity(kv_format, d, hq, hkv, lengths):
+    """8-bit pools in sink + ring mode: codes widened, then rotated by cache
+    order (D 64 rotates across lanes, D 128 within a lane)."""
+    lens = None if lengths == "parity" else workloads.ring_timing_lengths()
+    case = workloads.config_sink_ring_fp8(kv_format, lens, d, hq, hkv)
+    print(f"fp8 ring {kv_format} D{d} Hq{hq} Hkv{hkv} {lengths}", flush=True)
+    _, _, _, ref = oracle_reference(case)
+    dc = DeviceCase(case)
+    dc.write_all()
+    out = dc.decode()
+    assert_parity(out, ref, case.dtype)
+    dc.close()
+
+
+@pytest.mark.parametrize("kv_format", ["e4m3", "e5m2"])
+def test_fp8_ring_append_step(kv_format):
+    """The one-call step on 8-bit ring pools: the staging wave quantises the
+    newest token into its ring slot and the call equals write-then-decode."""
+    from test_gpu_append import _check
+
+    _check(workloads.config_sink_ring_fp8(kv_format, [1, 4, 5, 1023, 1024, 1025, 2045, 99_999]))

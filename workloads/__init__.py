@@ -599,11 +599,24 @@ MULTI_CONFIGS = {
 }
 
 
+def config_sink_ring_fp8(kv_format: str = "e4m3", lengths=None, head_dim: int = 128,
+                         num_q_heads: int = 12, num_kv_heads: int = 2) -> DecodeCase:
+    """The sink + ring workload on 8-bit pools (f16 activations written as
+    E4M3 or E5M2 codes with per-head scales)."""
+    case = config_sink_ring(lengths=lengths, head_dim=head_dim, num_q_heads=num_q_heads,
+                            num_kv_heads=num_kv_heads)
+    case.kv_dtype = "fp8_" + kv_format
+    case.k_scale, case.v_scale = fp8_scales(case.num_kv_heads)
+    case.name = f"sink_ring_{kv_format}"
+    return case
+
+
 FP8_CONFIGS = {
     "tiny_fp8": config_tiny_fp8,
     "embedded_1p1b_fp8": config_embedded_1p1b_fp8,
     "llama70b_b64_fp8": config_llama70b_fp8,
     "llama70b_b64_e5m2": config_llama70b_e5m2,
+    "sink_ring_fp8": config_sink_ring_fp8,
 }
 
 
