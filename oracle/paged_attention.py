@@ -232,18 +232,22 @@ def decode_multi(query, k_pool, v_pool, block_tables, context_lens, scale, dtype
     out = np.zeros((b_count, q_len, hq, d), dtype=np.float64)
     for b in range(b_count):
         n_ctx = int(context_lens[b])
+        if n_ctx <= 0:
+            continue
+        # the sequence's keys in logical order, gathered once; token i sees a prefix
+        idx = np.arange(n_ctx)
+        if kv_dtype in fp8.KV_FORMATS:
+            fmt = fp8.KV_FORMATS[kv_dtype]
+            keys_all = fp8.dequantize_rows(gather_rows(k_pool, block_tables[b], idx, block_size), k_scale, fmt)
+            vals_all = fp8.dequantize_rows(gather_rows(v_pool, block_tables[b], idx, block_size), v_scale, fmt)
+        else:
+            keys_all = to_f64(gather_rows(k_pool, block_tables[b], idx, block_size), dtype)
+            vals_all = to_f64(gather_rows(v_pool, block_tables[b], idx, block_size), dtype)
         for i in range(q_len):
             n = n_ctx - q_len + i + 1  # keys visible to new token i
             if n <= 0:
                 continue
-            idx = np.arange(n)
-            if kv_dtype in fp8.KV_FORMATS:
-                fmt = fp8.KV_FORMATS[kv_dtype]
-                keys = fp8.dequantize_rows(gather_rows(k_pool, block_tables[b], idx, block_size), k_scale, fmt)
-                vals = fp8.dequantize_rows(gather_rows(v_pool, block_tables[b], idx, block_size), v_scale, fmt)
-            else:
-                keys = to_f64(gather_rows(k_pool, block_tables[b], idx, block_size), dtype)
-                vals = to_f64(gather_rows(v_pool, block_tables[b], idx, block_size), dtype)
+            keys, vals = keys_all[:n], vals_all[:n]
             for g in range(hkv):
                 heads = slice(g * group, (g + 1) * group)
                 out[b, i, heads] = attention_one_group(q_all[b, i, heads], keys[:, g, :], vals[:, g, :], scale)

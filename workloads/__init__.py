@@ -522,8 +522,6 @@ def config_fp8(base=None, kv_format: str = "e4m3", **kw) -> DecodeCase:
     if kv_format not in ("e4m3", "e5m2"):
         raise ValueError(f"unknown 8-bit format {kv_format!r}")
     case = (base or config_llama70b)(**kw)
-    if case.ring is not None:
-        raise ValueError("8-bit KV storage is not combined with the ring cache")
     if case.dtype == "f32":
         case = _requantise_f32(case)
     case.kv_dtype = "fp8_" + kv_format
