@@ -535,6 +535,17 @@ int pa_decode_verify_ring(pa_pool *pool, void *out, const void *query, const voi
 size_t pa_decode_verify_ring_workspace_bytes(const pa_pool *pool, int32_t num_seqs, int32_t q_len,
                                              int32_t num_q_heads);
 
+/* Device: a streaming-read probe, a measurement aid outside the attention
+ * path (the pages define no such operation).  Reads `bytes` (a nonzero
+ * multiple of 16) at src (16-byte aligned) with the non-temporal 16-byte
+ * loads the decode kernels use for K/V, four work-groups per CU; work-group
+ * w stores the XOR of the 32-bit words it read to checksums[w], so the
+ * caller-owned checksums array must hold 4096 uint32 (the XOR of all
+ * entries is the XOR of every word of the buffer).  Timing it gives the
+ * practical read ceiling the decode's HBM fraction is compared against.
+ * PA_ERR_INVAL for bad pointers or sizes. */
+int pa_read_probe(const void *src, size_t bytes, uint32_t *checksums, void *stream);
+
 /* Name of a status code (static string). */
 const char *pa_status_str(int status);
 

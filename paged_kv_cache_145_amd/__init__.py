@@ -20,7 +20,7 @@ __all__ = [
     "decode_workspace_bytes", "rope_table_bytes", "rope_table_init", "decode", "decode_append",
     "decode_append_noalloc", "decode_noalloc_scratch_bytes",
     "check_decode_inputs", "DTYPES",
-    "block_hashes", "copy_blocks", "set_option", "decode_multi_workspace_bytes", "decode_multi", "Batcher",
+    "block_hashes", "copy_blocks", "set_option", "read_probe", "decode_multi_workspace_bytes", "decode_multi", "Batcher",
     "decode_verify_ring", "decode_verify_ring_workspace_bytes",
 ]
 
@@ -286,6 +286,20 @@ def set_option(name: str, value: int) -> int:
     old = int(lib.pa_get_option(opt))
     _check(lib.pa_set_option(opt, int(value)), "pa_set_option")
     return old
+
+
+READ_PROBE_CHECKSUMS = 4096
+
+
+def read_probe(src, checksums, stream=None) -> None:
+    """Streaming-read probe over the bytes of device tensor ``src``
+    (measurement aid); ``checksums`` is a device int32/uint32 tensor of
+    4096 entries receiving per-work-group XOR checksums."""
+    nbytes = src.numel() * src.element_size()
+    if checksums.numel() * checksums.element_size() < 4 * READ_PROBE_CHECKSUMS:
+        raise ValueError("checksums must hold 4096 32-bit words")
+    _check(_lib.load().pa_read_probe(_dev_ptr(src, "src"), nbytes, _dev_ptr(checksums, "checksums"),
+                                     _stream_ptr(stream)), "pa_read_probe")
 
 
 def ring_slot(pos: int, sink: int, window: int) -> int:

@@ -109,6 +109,7 @@ SIGNATURES = {
     "pa_decode_verify_ring": (ctypes.c_int, [_p, _p, _p, _p, _p, _p, _i32, _p, _i32, _i32, _i32, _i32,
                                              ctypes.c_float, ctypes.POINTER(PaRing), _p, _sz, _p]),
     "pa_decode_verify_ring_workspace_bytes": (_sz, [_p, _i32, _i32, _i32]),
+    "pa_read_probe": (ctypes.c_int, [_p, _sz, _p, _p]),
     "pa_set_option": (ctypes.c_int, [ctypes.c_int, _i32]),
     "pa_get_option": (_i32, [ctypes.c_int]),
 }

@@ -400,6 +400,14 @@ int pa_check_decode_inputs(const pa_pool *pool, const int32_t *block_tables, int
       counts, static_cast<hipStream_t>(stream)));
 }
 
+int pa_read_probe(const void *src, size_t bytes, uint32_t *checksums, void *stream) {
+  if (src == nullptr || checksums == nullptr || bytes == 0 || (bytes & 15) != 0) return PA_ERR_INVAL;
+  if (!pa::aligned16(src) || (reinterpret_cast<uintptr_t>(checksums) & 3u) != 0) return PA_ERR_INVAL;
+  // four work-groups per CU
+  const int grid = std::min(pa::kReadProbeMaxGrid, 4 * pa::multi_grid());
+  return pa::hip_status(pa::launch_read_probe(src, (int64_t)bytes, checksums, grid, static_cast<hipStream_t>(stream)));
+}
+
 int pa_rope_table_init(float *table, int32_t capacity, int32_t head_dim, float rope_base,
                        void *stream) {
   if (table == nullptr || capacity <= 0 || (head_dim != 64 && head_dim != 128)) return PA_ERR_INVAL;

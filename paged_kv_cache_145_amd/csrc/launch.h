@@ -181,6 +181,11 @@ hipError_t launch_check_inputs(const int32_t *block_tables, int32_t max_blocks_p
 hipError_t launch_rope_table_init(float *table, int32_t capacity, int32_t head_dim,
                                   float rope_base, hipStream_t stream);
 
+// Streaming-read probe: grid work-groups read `bytes` (a multiple of 16) and
+// store one XOR checksum each to out[0 .. grid).
+constexpr int kReadProbeMaxGrid = 4096;
+hipError_t launch_read_probe(const void *src, int64_t bytes, uint32_t *out, int grid, hipStream_t stream);
+
 }  // namespace pa
 
 #endif  // PA_LAUNCH_H_

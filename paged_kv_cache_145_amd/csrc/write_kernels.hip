@@ -236,6 +236,41 @@ hipError_t launch_check_inputs(const int32_t *block_tables, int32_t max_blocks_p
   return hipGetLastError();
 }
 
+// Streaming-read probe (a measurement aid, not part of the attention path):
+// work-group w reads the 16-byte pieces w * U * 256 + u * 256 + t, stepping
+// by the grid, with the same non-temporal loads the decode uses for K/V,
+// and stores the XOR of every 32-bit word it read to out[w].
+constexpr int kProbeUnroll = 8;
+__global__ __launch_bounds__(256) void read_probe_kernel(const char *src, int64_t pieces, uint32_t *out) {
+  const int64_t step = (int64_t)gridDim.x * kProbeUnroll * 256;
+  u32x4 acc = {0u, 0u, 0u, 0u};
+  for (int64_t p0 = (int64_t)blockIdx.x * kProbeUnroll * 256; p0 < pieces; p0 += step) {
+    // one descriptor per round keeps every offset below 2^31 bytes
+    const int64_t left = pieces - p0;
+    const int nrec = (int)(16 * (left < kProbeUnroll * 256 ? left : (int64_t)kProbeUnroll * 256));
+    const auto r = __builtin_amdgcn_make_buffer_rsrc(const_cast<char *>(src + 16 * p0), (short)0, nrec,
+                                                     kBufferWord3);
+    u32x4 v[kProbeUnroll];
+#pragma unroll
+    for (int u = 0; u < kProbeUnroll; ++u)
+      v[u] = __builtin_bit_cast(u32x4, buffer_load16<kCacheStream>(r, 16 * (u * 256 + (int)threadIdx.x)));
+#pragma unroll
+    for (int u = 0; u < kProbeUnroll; ++u) acc ^= v[u];
+  }
+  uint32_t x = acc.x ^ acc.y ^ acc.z ^ acc.w;
+  for (int off = 32; off >= 1; off >>= 1) x ^= __shfl_xor(x, off);
+  __shared__ uint32_t s_x[4];
+  if ((threadIdx.x & 63) == 0) s_x[threadIdx.x >> 6] = x;
+  __syncthreads();
+  if (threadIdx.x == 0) out[blockIdx.x] = s_x[0] ^ s_x[1] ^ s_x[2] ^ s_x[3];
+}
+
+hipError_t launch_read_probe(const void *src, int64_t bytes, uint32_t *out, int grid, hipStream_t stream) {
+  hipLaunchKernelGGL(read_probe_kernel, dim3(grid), dim3(256), 0, stream, static_cast<const char *>(src),
+                     bytes / 16, out);
+  return hipGetLastError();
+}
+
 hipError_t launch_rope_table_init(float *table, int32_t capacity, int32_t head_dim,
                                   float rope_base, hipStream_t stream) {
   const int64_t total = (int64_t)capacity * (head_dim / 2);
