@@ -579,8 +579,15 @@ void decode_mfma_kernel(DecodeArgs a) {
         app_load(ends, arow, aslot, absel);
         app_store(arow, aslot, absel);
       }
-      // keep the chunk's tile loads after the stores
-      __asm__ volatile("" ::: "memory");
+      // The tile loads that follow read rows other lanes of this wave just
+      // stored.  Lanes are separate threads, so a wavefront-scope
+      // acquire-release fence orders the stores before the loads.  It
+      // emits no instruction on gfx9 parts: a wavefront's vector memory
+      // operations are performed in program order, so a later load of an
+      // address the wave stored to returns the stored value (LLVM AMDGPU
+      // memory model, wavefront scope); the fence only keeps the compiler
+      // from moving the loads above the stores.
+      __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
     }
 #pragma unroll
     for (int s2 = 0; s2 < kQSlots; ++s2)

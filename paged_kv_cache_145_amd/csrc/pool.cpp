@@ -1,13 +1,16 @@
 // Host side of the paged KV cache: pool description, block allocator with
 // reference counts, ring slot equation and slot mapping.  Plain C++17, no HIP.
 //
-// Allocation order follows the free-bitmap allocator of "端侧 SLM 显存保活术…"
-// (sheratonhq.com/news/141880), section "嵌入式轻量 Block 分配器设计": the
-// lowest free id is taken first (word scan + count trailing zeros) and -1
-// reports exhaustion.  Reference counts and release at the last reference
-// follow "Ollama的内存管理策略…" (xdnf.cn/news/5086), section
-// "三、KV Cache内存管理的工程实现"; misuse that page leaves unchecked
-// (release of a free block) is an error here.
+// Allocation order is that of "端侧 SLM 显存保活术…" (sheratonhq.com/news/141880),
+// section "嵌入式轻量 Block 分配器设计": a new block is the lowest free id, and
+// -1 reports an exhausted pool.  The free set is kept as a two-level bitmap:
+// leaf word w has bit i set when block 64 w + i is free, and bit w of the
+// summary words is set when leaf word w has any free block, so the lowest
+// free id is found by reading one summary word per 4,096 blocks.
+// Reference counts and release at the last reference follow
+// "Ollama的内存管理策略…" (xdnf.cn/news/5086), section
+// "三、KV Cache内存管理的工程实现"; misuse that page leaves unchecked (release
+// of a free block) is an error here.
 #include <cstring>
 #include <new>
 
@@ -18,18 +21,18 @@
 namespace pa {
 
 int32_t alloc_block_locked(pa_pool *pool) {
-  for (size_t w = 0; w < pool->free_bits.size(); ++w) {
-    const uint64_t bits = pool->free_bits[w];
-    if (bits != 0) {
-      const int bit = __builtin_ctzll(bits);
-      pool->free_bits[w] = bits & ~(1ull << bit);
-      const int32_t id = (int32_t)(w * 64 + (size_t)bit);
-      pool->refcount[(size_t)id] = 1;
-      pool->used += 1;
-      return id;
-    }
-  }
-  return -1;
+  // lowest leaf word with a free block, then its lowest free block
+  size_t s = 0;
+  while (s < pool->free_summary.size() && pool->free_summary[s] == 0) ++s;
+  if (s == pool->free_summary.size()) return -1;
+  const size_t w = s * 64 + (size_t)__builtin_ctzll(pool->free_summary[s]);
+  uint64_t &leaf = pool->free_bits[w];
+  const int32_t id = (int32_t)(w * 64 + (size_t)__builtin_ctzll(leaf));
+  leaf &= leaf - 1;  // that block is taken
+  if (leaf == 0) pool->free_summary[s] &= ~(1ull << (w % 64));
+  pool->refcount[(size_t)id] = 1;
+  pool->used += 1;
+  return id;
 }
 
 void add_ref_locked(pa_pool *pool, int32_t block_id) {
@@ -43,7 +46,9 @@ void drop_ref_locked(pa_pool *pool, int32_t block_id) {
   rc -= 1;
   if (rc == 1) pool->shared -= 1;
   if (rc == 0) {
-    pool->free_bits[(size_t)block_id / 64] |= 1ull << (block_id % 64);
+    const size_t w = (size_t)block_id / 64;
+    pool->free_bits[w] |= 1ull << (block_id % 64);
+    pool->free_summary[w / 64] |= 1ull << (w % 64);
     pool->used -= 1;
   }
 }
@@ -84,10 +89,12 @@ int pa_create_pool(pa_pool **out, int32_t num_blocks, int32_t block_size, int32_
   p->k_cache = k_cache;
   p->v_cache = v_cache;
   try {
+    // every block starts free
     const size_t words = (size_t)pa::ceil_div(num_blocks, 64);
-    p->free_bits.assign(words, ~0ull);
-    const int tail = num_blocks % 64;
-    if (tail != 0) p->free_bits[words - 1] = (1ull << tail) - 1ull;
+    p->free_bits.assign(words, 0ull);
+    for (int32_t b = 0; b < num_blocks; ++b) p->free_bits[(size_t)b / 64] |= 1ull << (b % 64);
+    p->free_summary.assign((size_t)pa::ceil_div((int64_t)words, 64), 0ull);
+    for (size_t w = 0; w < words; ++w) p->free_summary[w / 64] |= 1ull << (w % 64);
     p->refcount.assign((size_t)num_blocks, 0);
     p->prefix.block_entry.assign((size_t)num_blocks, -1);
   } catch (...) {

@@ -60,7 +60,8 @@ struct pa_pool {
   // Allocator: one bit per block (1 = free), scanned lowest word first with a
   // count-trailing-zeros step, plus a reference count per block.
   mutable std::mutex mu;
-  std::vector<uint64_t> free_bits;
+  std::vector<uint64_t> free_bits;     // bit b % 64 of word b / 64: block b is free
+  std::vector<uint64_t> free_summary;  // bit w % 64 of word w / 64: free_bits[w] != 0
   std::vector<int32_t> refcount;
   int32_t used;
   int32_t shared;

@@ -426,3 +426,24 @@ def test_ring_verify_argument_validation(lib):
     assert call(good, pool=f32) == -5
     lib.pa_destroy_pool(f32)
     lib.pa_destroy_pool(h)
+
+
+def test_allocator_lowest_free_id_across_summary_words(lib):
+    """A pool of 10,000 blocks (several 4,096-block summary words): blocks come
+    out in id order, freed ids come back lowest first, exhaustion gives -1,
+    and the model allocator agrees step by step."""
+    n = 10_000
+    h = fake_pool(lib, n, 16, 2, 128, 1)
+    model = BlockAllocatorModel(n)
+    assert [lib.pa_alloc_block(h) for _ in range(n)] == list(range(n))
+    for _ in range(n):
+        model.alloc()
+    assert lib.pa_alloc_block(h) == -1 and model.alloc() == -1
+    freed = [9999, 4096, 4095, 8191, 8192, 63, 64, 0]
+    for b in freed:
+        assert lib.pa_decref_block(h, b) == 0
+        model.decref(b)
+    got = [lib.pa_alloc_block(h) for _ in range(len(freed) + 1)]
+    want = [model.alloc() for _ in range(len(freed) + 1)]
+    assert got == want == sorted(freed) + [-1]
+    lib.pa_destroy_pool(h)
