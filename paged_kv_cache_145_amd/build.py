@@ -28,6 +28,10 @@ HIP_FLAGS = [
     f"--offload-arch={ARCH}",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-munsafe-fp-atomics",
+    # MFMA accumulators in ordinary VGPRs: with the accumulation registers
+    # (AGPRs) the compiler copied the multi-token kernel's 96 output
+    # accumulators out and back on every key tile
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
 ]
 
 

@@ -694,8 +694,7 @@ void decode_mfma_kernel(DecodeArgs a) {
 #pragma unroll
     for (int tau = 0; tau < 4; ++tau)
       *reinterpret_cast<vchunk *>(vt + (4 * grp + tau) * kVRow + sizeof(vchunk) * row16) = vf[tau];
-    const uint2 pa = make_uint2(pack2(T::from_float(pj[0]), T::from_float(pj[1])),
-                                pack2(T::from_float(pj[2]), T::from_float(pj[3])));
+    const uint2 pa = make_uint2(T::pack_pair(pj[0], pj[1]), T::pack_pair(pj[2], pj[3]));
     const char *vr = vt + (4 * grp + (row16 >> 2)) * kVRow + 8 * (row16 & 3);
     uint2 vtr[NB];
 #pragma unroll

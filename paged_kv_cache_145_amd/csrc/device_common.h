@@ -18,6 +18,9 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr int kWave = 64;
@@ -41,6 +44,10 @@ struct F16 {
   }
   static __device__ __forceinline__ uint16_t from_float(float x) {
     return __builtin_bit_cast(uint16_t, (_Float16)x);  // round to nearest even
+  }
+  // from_float of two values, lo in bits 0..15 (one v_cvt_pk_f16_f32)
+  static __device__ __forceinline__ uint32_t pack_pair(float lo, float hi) {
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){lo, hi}, f16x2));
   }
   static __device__ __forceinline__ f32x4 mfma_16x16x32(uint4 a, uint4 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a),
@@ -72,6 +79,10 @@ struct BF16 {
   }
   static __device__ __forceinline__ uint16_t from_float(float x) {
     return __builtin_bit_cast(uint16_t, (__bf16)x);  // round to nearest even
+  }
+  // from_float of two values, lo in bits 0..15 (one v_cvt_pk_bf16_f32)
+  static __device__ __forceinline__ uint32_t pack_pair(float lo, float hi) {
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){lo, hi}, bf16x2));
   }
   static __device__ __forceinline__ f32x4 mfma_16x16x32(uint4 a, uint4 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),

@@ -73,15 +73,17 @@ struct MqV;
 template <>
 struct MqV<128> {
   typedef uint4 type;
+  template <int P>
   static __device__ __forceinline__ uint4 load(__amdgpu_buffer_rsrc_t r, int off) {
-    return buffer_load16(r, off);
+    return buffer_load16<P>(r, off);
   }
 };
 template <>
 struct MqV<64> {
   typedef uint2 type;
+  template <int P>
   static __device__ __forceinline__ uint2 load(__amdgpu_buffer_rsrc_t r, int off) {
-    return buffer_load8(r, off);
+    return buffer_load8<P>(r, off);
   }
 };
 
@@ -92,8 +94,9 @@ struct MqV8;
 template <>
 struct MqV8<128> {
   typedef uint2 type;
+  template <int P>
   static __device__ __forceinline__ uint2 load(__amdgpu_buffer_rsrc_t r, int off) {
-    return buffer_load8(r, off);
+    return buffer_load8<P>(r, off);
   }
   template <class T, int F>
   static __device__ __forceinline__ uint4 widen(const uint2 &v) { return fp8x8_to_16<T, F>(v); }
@@ -101,8 +104,9 @@ struct MqV8<128> {
 template <>
 struct MqV8<64> {
   typedef uint32_t type;
+  template <int P>
   static __device__ __forceinline__ uint32_t load(__amdgpu_buffer_rsrc_t r, int off) {
-    return buffer_load4(r, off);
+    return buffer_load4<P>(r, off);
   }
   template <class T, int F>
   static __device__ __forceinline__ uint2 widen(const uint32_t &v) { return fp8x4_to_16<T, F>(v); }
@@ -188,10 +192,15 @@ __device__ int mq_schedule(const MultiArgs &a, int *s_tfirst, int *s_kvend, int 
 // the A operands of two score MFMAs, and the query fragments follow that
 // dimension order; codes widen exactly to 16-bit values before the MFMAs and
 // the LDS tile.
-template <class T, int D, int MT, int KVF, int W, bool RING>
+// NT: the call makes one pass per (sequence, KV head), so each K/V row is
+// read once and its loads carry the non-temporal hint.  Calls with several
+// passes re-read a head's tiles from L2 (the passes of a work-group share
+// them), which the hint would defeat.
+template <class T, int D, int MT, int KVF, int W, bool RING, bool NT>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(W, W)))
 void decode_multi_kernel(MultiArgs a) {
   constexpr bool KV8 = KVF != 0;
+  constexpr int kPolicy = NT ? kCacheStream : kCacheNormal;
   static_assert(!(KV8 && RING), "ring verification reads 16-bit pools");
   // ring mode keeps a second, sink-rotated copy of each query fragment
   constexpr int kMqQSlots = RING ? 1 : kMqQSlotsFor<W>;
@@ -249,6 +258,9 @@ void decode_multi_kernel(MultiArgs a) {
   f32x4 acc[MT][NB];
   float m_run[MT], l_part[MT];
   int limit[MT];  // last key position this lane's row sees in each row tile (-1: none)
+  // smallest limit over the valid rows of each row tile (wave-uniform; INT_MAX
+  // when the tile holds none): key tiles wholly at or below it need no mask
+  int lim_lo[MT];
                   // (ring: the row's draft index i, -1: none)
   int lo_pos[MT];  // ring: oldest window position the row sees (p + 1 - W)
   uint4 qf[MT][KB];
@@ -376,11 +388,11 @@ void decode_multi_kernel(MultiArgs a) {
     const auto kr = __builtin_amdgcn_make_buffer_rsrc(const_cast<char *>(kbase + off), (short)0, nrec, kBufferWord3);
     const auto vr = __builtin_amdgcn_make_buffer_rsrc(const_cast<char *>(vbase + off), (short)0, nrec, kBufferWord3);
 #pragma unroll
-    for (int kb = 0; kb < KLD; ++kb) k[kb] = buffer_load16(kr, k_off + 64 * kb);
+    for (int kb = 0; kb < KLD; ++kb) k[kb] = buffer_load16<kPolicy>(kr, k_off + 64 * kb);
 #pragma unroll
     for (int tau = 0; tau < 4; ++tau) {
-      if constexpr (KV8) v[tau] = MqV8<D>::load(vr, v_off[tau]);
-      else v[tau] = MqV<D>::load(vr, v_off[tau]);
+      if constexpr (KV8) v[tau] = MqV8<D>::template load<kPolicy>(vr, v_off[tau]);
+      else v[tau] = MqV<D>::template load<kPolicy>(vr, v_off[tau]);
     }
   };
 
@@ -413,6 +425,8 @@ void decode_multi_kernel(MultiArgs a) {
         lo_pos[mt] = L + r / G + 1 - W_;
       } else {
         limit[mt] = r < seg_row_end ? L - ql + r / G : -1;
+        const int r0 = seg_row0 + 16 * mt;
+        lim_lo[mt] = __builtin_amdgcn_readfirstlane(r0 < seg_row_end ? L - ql + r0 / G : INT_MAX);
       }
       m_run[mt] = -INFINITY;
       l_part[mt] = 0.f;
@@ -494,6 +508,16 @@ void decode_multi_kernel(MultiArgs a) {
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
       float sc[4];
+      if constexpr (!RING) {
+        // Rows that see the whole tile need no mask; padding rows (past the
+        // pass's last) are never stored, so they may see any finite score.
+#pragma unroll
+        for (int r = 0; r < 4; ++r) sc[r] = sv[mt][r] * sl2;
+        if (kTileTokens * rd(tt, j) + kTileTokens - 1 > lim_lo[mt]) {
+#pragma unroll
+          for (int r = 0; r < 4; ++r) sc[r] = kp0 + r <= limit[mt] ? sc[r] : -INFINITY;
+        }
+      } else {
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         bool vis;
@@ -505,10 +529,9 @@ void decode_multi_kernel(MultiArgs a) {
             const int rs = kp0 + r;
             vis = limit[mt] >= 0 && rs < seg_L && (rs < S_ || slot_pos(rs) >= lo_pos[mt]);
           }
-        } else {
-          vis = kp0 + r <= limit[mt];
         }
         sc[r] = vis ? sv[mt][r] * sl2 : -INFINITY;
+      }
       }
       const float lmax = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
       if (__any(lmax > m_run[mt] + kMqRescaleSlack)) {
@@ -532,8 +555,7 @@ void decode_multi_kernel(MultiArgs a) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) pj[r] = fast_exp2(sc[r] - m_ref);
       l_part[mt] += (pj[0] + pj[1]) + (pj[2] + pj[3]);
-      const uint2 pa = make_uint2(pack2(T::from_float(pj[0]), T::from_float(pj[1])),
-                                  pack2(T::from_float(pj[2]), T::from_float(pj[3])));
+      const uint2 pa = make_uint2(T::pack_pair(pj[0], pj[1]), T::pack_pair(pj[2], pj[3]));
 #pragma unroll
       for (int jb = 0; jb < NB; ++jb) acc[mt][jb] = T::mfma_16x16x16(pa, vtr[jb], acc[mt][jb]);
     }
@@ -702,7 +724,14 @@ __global__ __launch_bounds__(256) void decode_multi_reduce_kernel(MultiArgs a) {
 
 template <class T, int D, int MT, int KVF, int W, bool RING>
 hipError_t launch_mt(const MultiArgs &a, int grid, hipStream_t stream) {
-  hipLaunchKernelGGL((decode_multi_kernel<T, D, MT, KVF, W, RING>), dim3(grid), dim3(kMqWaves * kWave), 0, stream, a);
+  // one pass per (sequence, KV head): each K/V row is read once (W = 1 only:
+  // the two-wave configuration serves calls with several passes)
+  if (W == 1 && a.passes == 1)
+    hipLaunchKernelGGL((decode_multi_kernel<T, D, MT, KVF, W, RING, W == 1>), dim3(grid), dim3(kMqWaves * kWave), 0,
+                       stream, a);
+  else
+    hipLaunchKernelGGL((decode_multi_kernel<T, D, MT, KVF, W, RING, false>), dim3(grid), dim3(kMqWaves * kWave), 0,
+                       stream, a);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   constexpr int rpb = 256 / (D / 4);
@@ -718,14 +747,15 @@ hipError_t launch_d(const MultiArgs &a, int mt, int waves, int grid, hipStream_t
     if (waves == 2) return mt == 1 ? launch_mt<T, D, 1, KVF, 2, true>(a, grid, stream) : hipErrorInvalidValue;
     if (mt > 2) return hipErrorInvalidValue;
     return mt == 1 ? launch_mt<T, D, 1, KVF, 1, true>(a, grid, stream) : launch_mt<T, D, 2, KVF, 1, true>(a, grid, stream);
-  }
-  if (waves == 2) return mt == 1 ? launch_mt<T, D, 1, KVF, 2, RING>(a, grid, stream)
-                                 : launch_mt<T, D, 2, KVF, 2, RING>(a, grid, stream);
-  switch (mt) {
-    case 1: return launch_mt<T, D, 1, KVF, 1, RING>(a, grid, stream);
-    case 2: return launch_mt<T, D, 2, KVF, 1, RING>(a, grid, stream);
-    case 3: return launch_mt<T, D, 3, KVF, 1, RING>(a, grid, stream);
-    default: return launch_mt<T, D, kMultiMaxRowTiles(D), KVF, 1, RING>(a, grid, stream);
+  } else {
+    if (waves == 2) return mt == 1 ? launch_mt<T, D, 1, KVF, 2, false>(a, grid, stream)
+                                   : launch_mt<T, D, 2, KVF, 2, false>(a, grid, stream);
+    switch (mt) {
+      case 1: return launch_mt<T, D, 1, KVF, 1, false>(a, grid, stream);
+      case 2: return launch_mt<T, D, 2, KVF, 1, false>(a, grid, stream);
+      case 3: return launch_mt<T, D, 3, KVF, 1, false>(a, grid, stream);
+      default: return launch_mt<T, D, kMultiMaxRowTiles(D), KVF, 1, false>(a, grid, stream);
+    }
   }
 }
 
