@@ -445,8 +445,18 @@ def multi_costs(case) -> dict:
     s_kv = 1 if workloads_is_kv8(case.kv_dtype) else s
     lens = case.context_lens.astype(np.int64)
     row = case.num_kv_heads * case.head_dim * 2 * s_kv
-    kv = int(lens.sum()) * row
     qo = case.num_seqs * case.q_len * case.num_q_heads * case.head_dim * 2 * s
+    if case.ring is not None:
+        # ring verification: the resident rows (at most S + W) and the drafts'
+        # rows (inputs, query dtype); draft i sees min(n + i + 1, S + W) keys
+        cap = case.ring.sink + case.ring.window
+        res = np.minimum(lens, cap)
+        kv = int(res.sum()) * row + case.num_seqs * case.q_len * case.num_kv_heads * case.head_dim * 2 * s
+        tables = int(sum(-(-int(n) // case.block_size) for n in res)) * 4 + case.num_seqs * 4
+        keys_seen = sum(min(int(n) + i + 1, cap) for n in lens for i in range(case.q_len))
+        flops = 4 * case.head_dim * case.num_q_heads * keys_seen
+        return {"bytes": kv + qo + tables, "flops": flops, "tokens": int(res.sum())}
+    kv = int(lens.sum()) * row
     tables = int(sum(-(-int(n) // case.block_size) for n in lens)) * 4 + case.num_seqs * 4
     keys_seen = sum(max(0, int(n) - case.q_len + i + 1) for n in lens for i in range(case.q_len))
     flops = 4 * case.head_dim * case.num_q_heads * keys_seen
@@ -481,20 +491,35 @@ def measure_multi(args) -> int:
     else:
         k, v = _nan_pools(workloads, torch, shape, case.dtype, dev)
         pool = pk.Pool(k, v, case.block_size)
+    ring = None
+    if case.ring is not None:  # verification over the sink + ring cache (drafts rotated up to q_len - 1 past it)
+        cap = case.ring.sink + case.ring.window + case.q_len
+        table = torch.empty(pk.rope_table_bytes(cap, case.head_dim) // 4, dtype=torch.float32, device=dev)
+        pk.rope_table_init(table, cap, case.head_dim, case.ring.rope_base)
+        ring = pk.Ring(case.ring.sink, case.ring.window, case.ring.rope_base, table, capacity=cap)
     for ch in case.writes:
         sid = np.full(ch.positions.shape, ch.seq, dtype=np.int32)
-        slots = pk.compute_slot_mapping(pool, case.block_tables, sid, ch.positions)
+        slots = pk.compute_slot_mapping(pool, case.block_tables, sid, ch.positions, ring)
         pk.reshape_and_cache(pool, to_dev(ch.keys), to_dev(ch.values), torch.from_numpy(slots).to(dev))
     query = to_dev(case.query)
     tables = torch.from_numpy(case.block_tables).to(dev)
     lens = torch.from_numpy(case.context_lens).to(dev)
     mcl = int(case.context_lens.max())
     out = torch.empty(tuple(case.query.shape), dtype=tdt, device=dev)
-    ws = torch.empty(max(pk.decode_multi_workspace_bytes(pool, case.num_seqs, case.q_len, case.num_q_heads, mcl), 1),
-                     dtype=torch.uint8, device=dev)
+    if ring is not None:
+        dk, dv = to_dev(case.draft_keys), to_dev(case.draft_values)
+        ws = torch.empty(max(pk.decode_verify_ring_workspace_bytes(pool, case.num_seqs, case.q_len,
+                                                                   case.num_q_heads), 1),
+                         dtype=torch.uint8, device=dev)
 
-    def call():
-        pk.decode_multi(pool, out, query, tables, lens, mcl, case.scale, workspace=ws)
+        def call():
+            pk.decode_verify_ring(pool, out, query, dk, dv, tables, lens, mcl, case.scale, ring, workspace=ws)
+    else:
+        ws = torch.empty(max(pk.decode_multi_workspace_bytes(pool, case.num_seqs, case.q_len, case.num_q_heads,
+                                                             mcl), 1), dtype=torch.uint8, device=dev)
+
+        def call():
+            pk.decode_multi(pool, out, query, tables, lens, mcl, case.scale, workspace=ws)
 
     for _ in range(args.warmup):
         call()
@@ -554,14 +579,21 @@ def multi_cpu_baseline(case, max_rows: int = 800) -> dict:
     except ImportError:  # pragma: no cover
         threadpool_limits = None
     nseq = max(1, min(case.num_seqs, max_rows // case.q_len))
+    if case.ring is not None:  # each verified row rebuilds its ring: a smaller sample
+        nseq = max(1, min(case.num_seqs, 16))
     kp, vp, _ = oracle.build_pools(case)
     ctx = threadpool_limits(limits=1) if threadpool_limits else None
     if ctx:
         ctx.__enter__()
     try:
         t0, c0 = time.perf_counter(), time.process_time()
-        oracle.decode_multi(case.query[:nseq], kp, vp, case.block_tables[:nseq], case.context_lens[:nseq],
-                            case.scale, case.dtype, case.block_size, case.q_len)
+        if case.ring is not None:
+            oracle.decode_verify_ring(case.query[:nseq], case.draft_keys[:nseq], case.draft_values[:nseq], kp, vp,
+                                      case.block_tables[:nseq], case.context_lens[:nseq], case.scale, case.dtype,
+                                      case.block_size, case.ring)
+        else:
+            oracle.decode_multi(case.query[:nseq], kp, vp, case.block_tables[:nseq], case.context_lens[:nseq],
+                                case.scale, case.dtype, case.block_size, case.q_len)
         wall = time.perf_counter() - t0
     finally:
         if ctx:
@@ -569,7 +601,8 @@ def multi_cpu_baseline(case, max_rows: int = 800) -> dict:
     cores = max(1, round((time.process_time() - c0) / wall))
     rows = nseq * case.q_len
     return {"value": round(rows / wall, 2), "unit": "tokens/s", "cores": cores, "kind": "oracle",
-            "sample": f"the new tokens of the first {nseq} sequences ({rows} rows), fp64 gather + softmax, "
+            "sample": f"the new tokens of the first {nseq} sequences ({rows} rows), fp64 gather + softmax"
+                      f"{' (ring verification)' if case.ring is not None else ''}, "
                       f"{wall:.2f} s"}
 
 

@@ -594,6 +594,10 @@ MULTI_CONFIGS = {
     # resolved at call time: config_fp8 is defined further down
     "spec_verify_llama70b_fp8": lambda: config_fp8(config_spec_verify_llama70b),
     "spec_verify_llama70b_e5m2": lambda: config_fp8(config_spec_verify_llama70b, kv_format="e5m2"),
+    # verification over the sink + ring cache: the edge lengths, and the
+    # timing set (16 full windows at distinct ring phases near 100k)
+    "ring_verify": lambda: config_ring_verify(),
+    "ring_verify_timing": lambda: config_ring_verify(lengths=ring_timing_lengths()),
 }
 
 
