@@ -59,11 +59,13 @@ constexpr int kMaxMqSeqs = kMaxMultiSeqsHost;  // virtual sequences per launch
 constexpr float kMqRescaleSlack = 8.0f;        // log2 units the running max may lag
 // Two configurations.  W = 1 (one wave per SIMD, up to three row tiles, a
 // four-deep load pipeline): memory-bound calls such as draft verification.
-// W = 2 (two waves per SIMD, at most two row tiles, two stages, one query
-// slot, so two work-groups fit a CU): calls with many row passes, where a
-// second wave hides the per-tile MFMA -> softmax -> MFMA chain.
-template <int W>
-constexpr int kMqStagesFor = W == 2 ? 2 : 4;  // depth of the per-wave tile pipeline
+// W = 2 (two waves per SIMD, up to three row tiles, one query slot, so two
+// work-groups fit a CU): calls with many row passes, where a second wave
+// hides the per-tile MFMA -> softmax -> MFMA chain.  Three row tiles fill
+// the 256 registers a wave then has with a single load stage (two spill);
+// one or two row tiles keep two stages.
+template <int W, int MT>
+constexpr int kMqStagesFor = W == 2 ? (MT >= 3 ? 1 : 2) : 4;  // depth of the per-wave tile pipeline
 template <int W>
 constexpr int kMqQSlotsFor = W == 2 ? 1 : 2;  // segment-opening tiles per staged chunk
 
@@ -611,7 +613,7 @@ void decode_multi_kernel(MultiArgs a) {
   // S register buffers: tile j is consumed from buffer j % S while the next
   // S - 1 tiles are in flight.  Loads are unconditional (empty past cnt) so
   // every step sees the same loads in flight and the same wait counts.
-  constexpr int S = kMqStagesFor<W>;
+  constexpr int S = kMqStagesFor<W, MT>;
   uint4 kbuf[S][KLD];
   vload vbuf[S][4];
   for (int start = xbeg; start < xend; start += cnt) {
@@ -749,7 +751,8 @@ hipError_t launch_d(const MultiArgs &a, int mt, int waves, int grid, hipStream_t
     return mt == 1 ? launch_mt<T, D, 1, KVF, 1, true>(a, grid, stream) : launch_mt<T, D, 2, KVF, 1, true>(a, grid, stream);
   } else {
     if (waves == 2) return mt == 1 ? launch_mt<T, D, 1, KVF, 2, false>(a, grid, stream)
-                                   : launch_mt<T, D, 2, KVF, 2, false>(a, grid, stream);
+                           : mt == 2 ? launch_mt<T, D, 2, KVF, 2, false>(a, grid, stream)
+                                     : launch_mt<T, D, 3, KVF, 2, false>(a, grid, stream);
     switch (mt) {
       case 1: return launch_mt<T, D, 1, KVF, 1, false>(a, grid, stream);
       case 2: return launch_mt<T, D, 2, KVF, 1, false>(a, grid, stream);
