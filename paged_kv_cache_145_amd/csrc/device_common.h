@@ -154,8 +154,11 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ uint2 lds_read_tr16_b64(const void *lds_addr) {
   typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+  // an address-space cast, not an integer round trip, so that the compiler
+  // still sees which LDS object is read (its waits for loads that write
+  // LDS directly then name only that object)
   const s16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-      (lds_s16x4 *)(__attribute__((address_space(3))) char *)(uintptr_t)lds_addr);
+      (lds_s16x4 *)(__attribute__((address_space(3))) const char *)lds_addr);
   return __builtin_bit_cast(uint2, r);
 }
 

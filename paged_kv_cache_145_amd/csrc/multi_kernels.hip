@@ -198,12 +198,20 @@ __device__ int mq_schedule(const MultiArgs &a, int *s_tfirst, int *s_kvend, int 
 // read once and its loads carry the non-temporal hint.  Calls with several
 // passes re-read a head's tiles from L2 (the passes of a work-group share
 // them), which the hint would defeat.
-template <class T, int D, int MT, int KVF, int W, bool RING, bool NT>
+// SH: the four waves of a work-group are four passes of one KV head (pass
+// group 4), so they walk the same key tiles.  Each tile's K and V then come
+// into LDS once for the work-group, a quarter per wave with buffer loads
+// that write LDS directly (no registers), kShDepth tiles ahead, one barrier
+// per tile; the waves read K fragments and transposed V from there, and a
+// segment's query fragments straight from memory.  16-bit pools, D = 128,
+// two waves per SIMD (chunked prefill).
+template <class T, int D, int MT, int KVF, int W, bool RING, bool NT, bool SH = false>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(W, W)))
 void decode_multi_kernel(MultiArgs a) {
   constexpr bool KV8 = KVF != 0;
   constexpr int kPolicy = NT ? kCacheStream : kCacheNormal;
   static_assert(!(KV8 && RING), "ring verification reads 16-bit pools");
+  static_assert(!SH || (!KV8 && !RING && D == 128 && W == 2), "shared tiles: 16-bit pools, D 128, two waves");
   // ring mode keeps a second, sink-rotated copy of each query fragment
   constexpr int kMqQSlots = RING ? 1 : kMqQSlotsFor<W>;
   constexpr int kQCopies = RING ? 2 : 1;
@@ -220,8 +228,25 @@ void decode_multi_kernel(MultiArgs a) {
   __shared__ int s_tfirst[kMaxMqSeqs + 1];
   __shared__ int s_kvend[kMaxMqSeqs];
   __shared__ int s_wsum[kMqWaves];
-  __shared__ __align__(16) char s_vt[kMqWaves][MqLds<D>::kVBytes];
-  __shared__ uint4 s_q[kMqWaves][kQCopies * kMqQSlots * QF * kWave];  // query fragments, lane-major
+  __shared__ __align__(16) char s_vt[SH ? 1 : kMqWaves][SH ? 16 : MqLds<D>::kVBytes];
+  // SH: [buffer][K rows | V rows], rows of D * 2 bytes without padding; the
+  // 16-byte pieces of row r are stored permuted (K: piece p at p ^ r, V: at
+  // p ^ 2 (r mod 4)) so that the fragment and transposing reads of one
+  // instruction fall in distinct banks
+  // SH layout of one buffer: K then V, each four groups (one per loading
+  // wave q) of rows q, q + 4, q + 8, q + 12 at 256-byte strides; group q
+  // starts at q * kShGroup, 32 bytes past a multiple of 128, so the rows
+  // that one fragment or transposing read touches fall in distinct banks.
+  // K rows also swap 16-byte pieces within each 64-byte quarter (piece
+  // 4 c + e at 4 c + (e ^ (row / 4 mod 2))).  A lane's K fragments and V
+  // reads are then one address plus constant offsets.
+  constexpr int kShGroup = 4 * D * 2 + 32;       // 1056 bytes
+  constexpr int kShHalf = 4 * kShGroup;          // K or V of one tile
+  constexpr int kShBuf = 2 * kShHalf;
+  constexpr int kShDepth = 3;                    // tiles in flight ahead of the one consumed
+  static_assert(kShDepth == 3, "the consuming loop below is unrolled for four buffers");
+  __shared__ __align__(16) char s_kv[SH ? (kShDepth + 1) * kShBuf : 16];
+  __shared__ uint4 s_q[SH ? 1 : kMqWaves][SH ? 1 : kQCopies * kMqQSlots * QF * kWave];  // query fragments, lane-major
 
   const int nv = a.num_seqs * a.pgroups;
   const int total = mq_schedule(a, s_tfirst, s_kvend, s_wsum, RING);
@@ -243,8 +268,15 @@ void decode_multi_kernel(MultiArgs a) {
 
   const int64_t row_stride = (int64_t)hkv * D;  // elements between token rows
   const int bmask = (1 << a.block_shift) - 1;
-  char *vt = s_vt[wave];
-  uint4 *qs = s_q[wave];
+  char *vt = s_vt[SH ? 0 : wave];
+  // SH: LDS byte addresses of this lane's first K fragment and first
+  // transposing V read in buffer 0 (row row16 = 4 g + q: group q, row g)
+  const uint32_t sh_lds = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char *)s_kv;
+  const uint32_t sh_k = sh_lds + (row16 & 3) * kShGroup + (row16 >> 2) * (D * 2) +
+                        16 * (grp ^ ((row16 >> 2) & 1));
+  const uint32_t sh_v = sh_lds + kShHalf + (row16 >> 2) * kShGroup + grp * (D * 2) + 8 * (row16 & 3);
+  uint32_t sh_off = 0;  // SH: byte offset of the consumed tile's buffer
+  uint4 *qs = s_q[SH ? 0 : wave];
   const int k_off = (int)((row16 * row_stride + (KV8 ? 16 : 8) * grp) * (int64_t)KVB);
   // query dimension of element 0 of score MFMA kb's fragment in this lane
   auto q_dim = [&](int kb) { return KV8 ? 64 * (kb >> 1) + 16 * grp + 8 * (kb & 1) : 32 * kb + 8 * grp; };
@@ -309,6 +341,7 @@ void decode_multi_kernel(MultiArgs a) {
     // before its (kMqQSlots + 1)-th opening tile
     const bool opens = lane < cnt && ((tflag & 1) || c0 + lane == xbeg);
     unsigned long long m = __ballot(opens);
+    if (SH) m = 0;  // segments load their query fragments themselves
     if (__popcll(m) > kMqQSlots) {
       unsigned long long r = m;
       for (int i = 0; i < kMqQSlots; ++i) r &= r - 1;
@@ -367,10 +400,12 @@ void decode_multi_kernel(MultiArgs a) {
       toff_hi = (int)(off >> 32);
       tnrec = (int)(((tvalid - 1) * row_stride + D) * (int64_t)KVB);  // tvalid >= 1 here
     }
+    if constexpr (!SH) {
 #pragma unroll
-    for (int s2 = 0; s2 < kMqQSlots; ++s2)
+      for (int s2 = 0; s2 < kMqQSlots; ++s2)
 #pragma unroll
-      for (int f = 0; f < QF; ++f) qs[(s2 * QF + f) * kWave + lane] = qtmp[s2][f];
+        for (int f = 0; f < QF; ++f) qs[(s2 * QF + f) * kWave + lane] = qtmp[s2][f];
+    }
     if constexpr (RING) {
 #pragma unroll
       for (int s2 = 0; s2 < kMqQSlots; ++s2)
@@ -398,12 +433,58 @@ void decode_multi_kernel(MultiArgs a) {
     }
   };
 
+  // SH: this wave's quarter of staged tile j (rows 4 wave .. 4 wave + 3 of
+  // K and of V) into LDS buffer buf; rows past the tile's valid ones fall
+  // outside the record range and are written as zeros.
+  auto dma_tile = [&](int j, char *buf) {
+    if constexpr (SH) {
+      // j >= cnt: an empty record (writes zeros into a free buffer), so that
+      // every step has the same loads in flight
+      const int jj = min(j, kWave - 1);
+      const uint64_t off = ((uint64_t)(uint32_t)rd(toff_hi, jj) << 32) | (uint32_t)rd(toff_lo, jj);
+      const int nrec = j < cnt ? rd(tnrec, jj) : 0;
+      const auto kr = __builtin_amdgcn_make_buffer_rsrc(
+          const_cast<char *>(static_cast<const char *>(a.k_cache) + off), (short)0, nrec, kBufferWord3);
+      const auto vr = __builtin_amdgcn_make_buffer_rsrc(
+          const_cast<char *>(static_cast<const char *>(a.v_cache) + off), (short)0, nrec, kBufferWord3);
+      // this wave's group: rows 4 g + wave (g = lane / 16), lane's slot s
+      const int gq = lane >> 4, slot = lane & 15;
+      const int rbytes = (int)((4 * gq + wave) * row_stride * 2);
+      const int kpiece = (slot & 12) | ((slot & 3) ^ (gq & 1));
+      char *kd = buf + wave * kShGroup;
+      char *vd = buf + kShHalf + wave * kShGroup;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(kr, (__attribute__((address_space(3))) void *)kd, 16,
+                                               rbytes + (kpiece << 4), 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(vr, (__attribute__((address_space(3))) void *)vd, 16,
+                                               rbytes + (slot << 4), 0, 0, 0);
+    }
+  };
+
   auto begin_segment = [&](int j, int v, bool whole) {
-    const int slot = rd(tslot, j);
+    if constexpr (SH) {
+      // this wave's pass of virtual sequence v (rows past its last load zeros)
+      const int bq = v / a.pgroups;
+      const int p = (v - bq * a.pgroups) * PG + w;
+      const int row_end = min(a.rows, (p + 1) * a.pass_rows);
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
+      for (int mt = 0; mt < MT; ++mt) {
+        const int r = p * a.pass_rows + 16 * mt + row16;
+        const bool ok = r < row_end;
+        const int qi = ok ? r / G : 0;
+        const int h = ok ? r - qi * G : 0;
+        const st *q = static_cast<const st *>(a.query) +
+                      (((int64_t)bq * ql + qi) * a.num_q_heads + (int64_t)g * G + h) * D;
 #pragma unroll
-      for (int kb = 0; kb < KB; ++kb) qf[mt][kb] = qs[(slot * QF + mt * KB + kb) * kWave + lane];
+        for (int kb = 0; kb < KB; ++kb)
+          qf[mt][kb] = ok ? *reinterpret_cast<const uint4 *>(q + q_dim(kb)) : make_uint4(0u, 0u, 0u, 0u);
+      }
+    } else {
+      const int slot = rd(tslot, j);
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) qf[mt][kb] = qs[(slot * QF + mt * KB + kb) * kWave + lane];
+    }
     const int b = v / a.pgroups;
     const int L = mq_len(a, b);
     int kv_end;
@@ -417,7 +498,7 @@ void decode_multi_kernel(MultiArgs a) {
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-        for (int kb = 0; kb < KB; ++kb) qfs[mt][kb] = qs[((kMqQSlots + slot) * QF + mt * KB + kb) * kWave + lane];
+        for (int kb = 0; kb < KB; ++kb) qfs[mt][kb] = qs[((kMqQSlots + rd(tslot, j)) * QF + mt * KB + kb) * kWave + lane];
     }
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
@@ -442,7 +523,40 @@ void decode_multi_kernel(MultiArgs a) {
   auto process_tile = [&](int j, const uint4 (&kraw)[KLD], const vload (&vraw)[4]) {
     uint4 kf[KB];
     vchunk vf[4];
-    if constexpr (KV8) {
+    // SH: V, already transposed, comes with the K fragments (below)
+    typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+    u32x2 shv[SH ? NB : 1];
+    if constexpr (SH) {
+      // One asm block reads the tile's K fragments and transposed V and waits
+      // for its own reads.  The compiler sees no LDS read of the buffers that
+      // the tile loads write, so it adds no waits for those loads of its own
+      // (the explicit wait and barrier before this tile order them).
+      static_assert(KB == 4 && NB == 8, "SH reads are written for D = 128");
+      const uint32_t ka = sh_k + sh_off, va = sh_v + sh_off;
+      u32x4 k0, k1, k2, k3;
+      asm volatile(
+          "ds_read_b128 %0, %12\n\t"
+          "ds_read_b128 %1, %12 offset:64\n\t"
+          "ds_read_b128 %2, %12 offset:128\n\t"
+          "ds_read_b128 %3, %12 offset:192\n\t"
+          "ds_read_b64_tr_b16 %4, %13\n\t"
+          "ds_read_b64_tr_b16 %5, %13 offset:32\n\t"
+          "ds_read_b64_tr_b16 %6, %13 offset:64\n\t"
+          "ds_read_b64_tr_b16 %7, %13 offset:96\n\t"
+          "ds_read_b64_tr_b16 %8, %13 offset:128\n\t"
+          "ds_read_b64_tr_b16 %9, %13 offset:160\n\t"
+          "ds_read_b64_tr_b16 %10, %13 offset:192\n\t"
+          "ds_read_b64_tr_b16 %11, %13 offset:224\n\t"
+          "s_waitcnt lgkmcnt(0)"
+          : "=&v"(k0), "=&v"(k1), "=&v"(k2), "=&v"(k3), "=&v"(shv[0]), "=&v"(shv[1]), "=&v"(shv[2]),
+            "=&v"(shv[3]), "=&v"(shv[4]), "=&v"(shv[5]), "=&v"(shv[6]), "=&v"(shv[7])
+          : "v"(ka), "v"(va)
+          : "memory");
+      kf[0] = __builtin_bit_cast(uint4, k0);
+      kf[1] = __builtin_bit_cast(uint4, k1);
+      kf[2] = __builtin_bit_cast(uint4, k2);
+      kf[3] = __builtin_bit_cast(uint4, k3);
+    } else if constexpr (KV8) {
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb) {
         const uint4 w8 = kraw[kb >> 1];
@@ -500,13 +614,18 @@ void decode_multi_kernel(MultiArgs a) {
     }
     // V rows past the keys the pass sees were loaded as zeros, so a zero
     // weight never meets a NaN sentinel; rows before hold written values.
-#pragma unroll
-    for (int tau = 0; tau < 4; ++tau)
-      *reinterpret_cast<vchunk *>(vt + (4 * grp + tau) * kVRow + sizeof(vchunk) * row16) = vf[tau];
-    const char *vr = vt + (4 * grp + (row16 >> 2)) * kVRow + 8 * (row16 & 3);
     uint2 vtr[NB];
+    if constexpr (SH) {
 #pragma unroll
-    for (int jb = 0; jb < NB; ++jb) vtr[jb] = lds_read_tr16_b64(vr + 32 * jb);
+      for (int jb = 0; jb < NB; ++jb) vtr[jb] = __builtin_bit_cast(uint2, shv[jb]);
+    } else {
+#pragma unroll
+      for (int tau = 0; tau < 4; ++tau)
+        *reinterpret_cast<vchunk *>(vt + (4 * grp + tau) * kVRow + sizeof(vchunk) * row16) = vf[tau];
+      const char *vr = vt + (4 * grp + (row16 >> 2)) * kVRow + 8 * (row16 & 3);
+#pragma unroll
+      for (int jb = 0; jb < NB; ++jb) vtr[jb] = lds_read_tr16_b64(vr + 32 * jb);
+    }
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
       float sc[4];
@@ -613,6 +732,46 @@ void decode_multi_kernel(MultiArgs a) {
   // S register buffers: tile j is consumed from buffer j % S while the next
   // S - 1 tiles are in flight.  Loads are unconditional (empty past cnt) so
   // every step sees the same loads in flight and the same wait counts.
+  if constexpr (SH) {
+    // Tile j of a chunk sits in buffer j mod 4.  Per tile: this wave's loads
+    // of tile j done (two loads per tile, issued in order, those of the
+    // kShDepth - 1 later tiles may still be in flight), a barrier (every
+    // quarter of tile j in LDS, every wave done with tile j - 1), the loads
+    // of tile j + kShDepth into the buffer tile j - 1 used, then tile j.
+    // The four waves share the range and the chunking, so they meet the
+    // same barriers.  Stores (segment ends) are drained before the next
+    // wait, so the count below covers only the tile loads.
+    constexpr int kVmWait = 2 * (kShDepth - 1);  // vmcnt field of s_waitcnt (< 16)
+    constexpr int kWaitImm = kVmWait | (0x7 << 4) | (0xF << 8);  // expcnt, lgkmcnt unchanged
+    uint4 kd[KLD];
+    vload vd[4];
+    auto sh_step = [&](int j, int cur, int next) {
+      if (j >= cnt) return;  // wave-uniform
+      __builtin_amdgcn_s_waitcnt(kWaitImm);
+      // a bare barrier: __syncthreads() adds a release fence, which waits
+      // for every load in flight (the next tiles' too); LDS needs none
+      __builtin_amdgcn_s_barrier();
+      dma_tile(j + kShDepth, s_kv + next * kShBuf);
+      sh_off = cur * kShBuf;
+      const bool ends = (rd(tflag, j) & 2) || c0 + j == xend - 1;
+      step(j, kd, vd);
+      if (ends) __builtin_amdgcn_s_waitcnt(0);  // this segment's stores
+    };
+    for (int start = xbeg; start < xend; start += cnt) {
+      stage(start);  // sets cnt
+      __syncthreads();  // the previous chunk's tiles are consumed
+      dma_tile(0, s_kv);
+      dma_tile(1, s_kv + kShBuf);
+      dma_tile(2, s_kv + 2 * kShBuf);
+      for (int j = 0; j < cnt; j += 4) {
+        sh_step(j, 0, 3);
+        sh_step(j + 1, 1, 0);
+        sh_step(j + 2, 2, 1);
+        sh_step(j + 3, 3, 2);
+      }
+    }
+    return;
+  }
   constexpr int S = kMqStagesFor<W, MT>;
   uint4 kbuf[S][KLD];
   vload vbuf[S][4];
@@ -728,9 +887,13 @@ template <class T, int D, int MT, int KVF, int W, bool RING>
 hipError_t launch_mt(const MultiArgs &a, int grid, hipStream_t stream) {
   // one pass per (sequence, KV head): each K/V row is read once (W = 1 only:
   // the two-wave configuration serves calls with several passes)
+  constexpr bool kCanShare = W == 2 && KVF == 0 && !RING && D == 128;
   if (W == 1 && a.passes == 1)
     hipLaunchKernelGGL((decode_multi_kernel<T, D, MT, KVF, W, RING, W == 1>), dim3(grid), dim3(kMqWaves * kWave), 0,
                        stream, a);
+  else if (kCanShare && a.pass_group == kMqWaves)
+    hipLaunchKernelGGL((decode_multi_kernel<T, D, MT, KVF, W, RING, false, kCanShare>), dim3(grid),
+                       dim3(kMqWaves * kWave), 0, stream, a);
   else
     hipLaunchKernelGGL((decode_multi_kernel<T, D, MT, KVF, W, RING, false>), dim3(grid), dim3(kMqWaves * kWave), 0,
                        stream, a);
