@@ -725,15 +725,17 @@ void decode_mfma_kernel(DecodeArgs a) {
         }
       }
     } else {
+      // the partial's normalised rows are stored in the activation type, like
+      // the output (their (m, l) stay fp32)
       const int64_t slot = ((int64_t)grp_id + b) * hkv + g;
-      float *po = a.ws_o + slot * G * D;
+      st *po = reinterpret_cast<st *>(a.ws_o) + slot * G * D;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int h = 4 * grp + r;
         if (h < G) {
           const float inv = vscale / lh[r];
 #pragma unroll
-          for (int e = 0; e < NB; ++e) po[h * D + 16 * e + row16] = acc[e][r] * inv;
+          for (int e = 0; e < NB; ++e) po[h * D + 16 * e + row16] = T::from_float(acc[e][r] * inv);
         }
       }
       if (grp == 0 && row16 < G) {
@@ -809,14 +811,14 @@ __global__ __launch_bounds__(256) void decode_streamk_reduce_kernel(DecodeArgs a
   float den = 0.f, mx = -INFINITY;
   for (int s0 = 0; s0 < nseg; s0 += kWave) {  // chunks of 64 segments, online rescale
     const int cnt = min(kWave, nseg - s0);
-    const float *rows = a.ws_o + ((slot0 + (int64_t)s0 * hkv) * G + h) * D + lane;
+    const st *rows = reinterpret_cast<const st *>(a.ws_o) + ((slot0 + (int64_t)s0 * hkv) * G + h) * D + lane;
     // the rows of the first 8 segments are requested together with the
     // (m, l) pairs (indices clamped into the chunk; extra copies unused)
     float v[8][DPL];
 #pragma unroll
     for (int u = 0; u < 8; ++u)
 #pragma unroll
-      for (int k = 0; k < DPL; ++k) v[u][k] = rows[min(u, cnt - 1) * rstride + k * kWave];
+      for (int k = 0; k < DPL; ++k) v[u][k] = T::to_float(rows[min(u, cnt - 1) * rstride + k * kWave]);
     float ms = -INFINITY, ls = 0.f;
     if (lane < cnt) {
       const int64_t slot = slot0 + (int64_t)(s0 + lane) * hkv;
@@ -846,7 +848,7 @@ __global__ __launch_bounds__(256) void decode_streamk_reduce_kernel(DecodeArgs a
 #pragma unroll
       for (int u = 0; u < 8; ++u)
 #pragma unroll
-        for (int k = 0; k < DPL; ++k) v[u][k] = rows[min(j + u, cnt - 1) * rstride + k * kWave];
+        for (int k = 0; k < DPL; ++k) v[u][k] = T::to_float(rows[min(j + u, cnt - 1) * rstride + k * kWave]);
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
         if (j + u < cnt) {

@@ -36,9 +36,10 @@ struct DecodeArgs {
   const void *v_cache;
   const int32_t *block_tables;
   const int32_t *context_lens;
-  // split-K partials.  MFMA kernel: slots [waves + B * Hkv][G][D] and
-  // [..][G][2]; VALU kernel: [B][Hq][max_parts][D] and [..][2].
-  float *ws_o;   // partition-normalised outputs
+  // split-K partials.  MFMA kernel: slots [waves + B * Hkv][G][D] in the
+  // activation type and [..][G][2]; VALU kernel: [B][Hq][max_parts][D] fp32
+  // and [..][2].
+  float *ws_o;   // partition-normalised outputs (see above for the type)
   float *ws_ml;  // (running max in log2 units, sum)
   int32_t *ws_sched;  // MFMA kernel: tile prefix per sequence [B + 1]
   // Append mode (MFMA kernel, plain paging): the new token of each
@@ -79,8 +80,8 @@ struct MultiArgs {
   const int32_t *block_tables;
   const int32_t *context_lens;
   // stream-K partials: slots [(groups + B * pgroups) * Hkv * pass_group]
-  // [pass_rows][D] and [..][pass_rows][2]; tile prefix per (sequence, pass
-  // group) [B * pgroups + 1]
+  // [pass_rows][D] in the activation type and [..][pass_rows][2] fp32; tile
+  // prefix per (sequence, pass group) [B * pgroups + 1]
   float *ws_o;
   float *ws_ml;
   int32_t *ws_sched;

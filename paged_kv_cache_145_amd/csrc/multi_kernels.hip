@@ -707,9 +707,10 @@ void decode_multi_kernel(MultiArgs a) {
 #pragma unroll
           for (int e = 0; e < NB; ++e) out[16 * e + row16] = T::from_float(acc[mt][e][r] * inv);
         } else {
-          float *po = a.ws_o + (slot * a.pass_rows + (rr - seg_row0)) * D;
+          // normalised partial rows in the activation type ((m, l) fp32)
+          st *po = reinterpret_cast<st *>(a.ws_o) + (slot * a.pass_rows + (rr - seg_row0)) * D;
 #pragma unroll
-          for (int e = 0; e < NB; ++e) po[16 * e + row16] = acc[mt][e][r] * inv;
+          for (int e = 0; e < NB; ++e) po[16 * e + row16] = T::from_float(acc[mt][e][r] * inv);
         }
       }
       if (!whole && grp == 0) {
@@ -840,7 +841,9 @@ __global__ __launch_bounds__(256) void decode_multi_reduce_kernel(MultiArgs a) {
           const int64_t r = r0 + (int64_t)(k0 - ga + u) * rstep;
           mk[u] = a.ws_ml[r * 2];
           lk[u] = a.ws_ml[r * 2 + 1];
-          ok[u] = reinterpret_cast<const float4 *>(a.ws_o + r * D)[q4];
+          const uint2 w2 = reinterpret_cast<const uint2 *>(reinterpret_cast<const st *>(a.ws_o) + r * D)[q4];
+          ok[u] = make_float4(T::to_float((st)(w2.x & 0xffffu)), T::to_float((st)(w2.x >> 16)),
+                              T::to_float((st)(w2.y & 0xffffu)), T::to_float((st)(w2.y >> 16)));
         } else {
           mk[u] = -INFINITY;
           lk[u] = 0.f;
