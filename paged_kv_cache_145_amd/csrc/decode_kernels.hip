@@ -792,10 +792,11 @@ __global__ __launch_bounds__(256) void decode_streamk_reduce_kernel(DecodeArgs a
   if (h >= G) return;
   const int t0 = a.ws_sched[b], t1 = a.ws_sched[b + 1];
   const int total = a.ws_sched[a.num_seqs];
-  st *out = static_cast<st *>(a.out) + ((int64_t)b * a.num_q_heads + g * G + h) * D + lane;
+  // lane holds DPL adjacent elements (one 4-byte access at D = 128)
+  st *out = static_cast<st *>(a.out) + ((int64_t)b * a.num_q_heads + g * G + h) * D + DPL * lane;
   if (t1 == t0) {
 #pragma unroll
-    for (int k = 0; k < DPL; ++k) out[k * kWave] = T::from_float(0.f);
+    for (int k = 0; k < DPL; ++k) out[k] = T::from_float(0.f);
     return;
   }
   const int active = active_groups(a, total, groups);
@@ -811,14 +812,14 @@ __global__ __launch_bounds__(256) void decode_streamk_reduce_kernel(DecodeArgs a
   float den = 0.f, mx = -INFINITY;
   for (int s0 = 0; s0 < nseg; s0 += kWave) {  // chunks of 64 segments, online rescale
     const int cnt = min(kWave, nseg - s0);
-    const st *rows = reinterpret_cast<const st *>(a.ws_o) + ((slot0 + (int64_t)s0 * hkv) * G + h) * D + lane;
+    const st *rows = reinterpret_cast<const st *>(a.ws_o) + ((slot0 + (int64_t)s0 * hkv) * G + h) * D + DPL * lane;
     // the rows of the first 8 segments are requested together with the
     // (m, l) pairs (indices clamped into the chunk; extra copies unused)
     float v[8][DPL];
 #pragma unroll
     for (int u = 0; u < 8; ++u)
 #pragma unroll
-      for (int k = 0; k < DPL; ++k) v[u][k] = T::to_float(rows[min(u, cnt - 1) * rstride + k * kWave]);
+      for (int k = 0; k < DPL; ++k) v[u][k] = T::to_float(rows[min(u, cnt - 1) * rstride + k]);
     float ms = -INFINITY, ls = 0.f;
     if (lane < cnt) {
       const int64_t slot = slot0 + (int64_t)(s0 + lane) * hkv;
@@ -848,7 +849,7 @@ __global__ __launch_bounds__(256) void decode_streamk_reduce_kernel(DecodeArgs a
 #pragma unroll
       for (int u = 0; u < 8; ++u)
 #pragma unroll
-        for (int k = 0; k < DPL; ++k) v[u][k] = T::to_float(rows[min(j + u, cnt - 1) * rstride + k * kWave]);
+        for (int k = 0; k < DPL; ++k) v[u][k] = T::to_float(rows[min(j + u, cnt - 1) * rstride + k]);
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
         if (j + u < cnt) {
@@ -862,7 +863,7 @@ __global__ __launch_bounds__(256) void decode_streamk_reduce_kernel(DecodeArgs a
   }
   const float inv = 1.f / den;
 #pragma unroll
-  for (int k = 0; k < DPL; ++k) out[k * kWave] = T::from_float(num[k] * inv);
+  for (int k = 0; k < DPL; ++k) out[k] = T::from_float(num[k] * inv);
 }
 
 // ---------------------------------------------------------------------------

@@ -58,14 +58,16 @@ constexpr int kMqWaves = 4;
 constexpr int kMaxMqSeqs = kMaxMultiSeqsHost;  // virtual sequences per launch
 constexpr float kMqRescaleSlack = 8.0f;        // log2 units the running max may lag
 // Two configurations.  W = 1 (one wave per SIMD, up to three row tiles, a
-// four-deep load pipeline): memory-bound calls such as draft verification.
+// two-deep load pipeline: verification of the 70B-shaped batch 102.3 us
+// against 103.4 at three stages, 104.4 at four, 106-109 at six): memory-bound
+// calls such as draft verification.
 // W = 2 (two waves per SIMD, up to three row tiles, one query slot, so two
 // work-groups fit a CU): calls with many row passes, where a second wave
 // hides the per-tile MFMA -> softmax -> MFMA chain.  Three row tiles fill
 // the 256 registers a wave then has with a single load stage (two spill);
 // one or two row tiles keep two stages.
 template <int W, int MT>
-constexpr int kMqStagesFor = W == 2 ? (MT >= 3 ? 1 : 2) : 4;  // depth of the per-wave tile pipeline
+constexpr int kMqStagesFor = (W == 2 && MT >= 3) ? 1 : 2;  // depth of the per-wave tile pipeline
 template <int W>
 constexpr int kMqQSlotsFor = W == 2 ? 1 : 2;  // segment-opening tiles per staged chunk
 
