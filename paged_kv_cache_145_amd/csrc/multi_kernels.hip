@@ -836,20 +836,20 @@ __global__ __launch_bounds__(256) void decode_multi_reduce_kernel(MultiArgs a) {
     for (int k0 = ga; k0 <= gb; k0 += kWin) {
       const int cnt = min(kWin, gb - k0 + 1);
       float mk[kWin], lk[kWin];
-      float4 ok[kWin];
+      // rows stay raw (four 16-bit values) until they are used, so that no
+      // conversion waits on a load before the window's other loads issue
+      uint2 okr[kWin];
 #pragma unroll
       for (int u = 0; u < kWin; ++u) {
         if (u < cnt) {
           const int64_t r = r0 + (int64_t)(k0 - ga + u) * rstep;
           mk[u] = a.ws_ml[r * 2];
           lk[u] = a.ws_ml[r * 2 + 1];
-          const uint2 w2 = reinterpret_cast<const uint2 *>(reinterpret_cast<const st *>(a.ws_o) + r * D)[q4];
-          ok[u] = make_float4(T::to_float((st)(w2.x & 0xffffu)), T::to_float((st)(w2.x >> 16)),
-                              T::to_float((st)(w2.y & 0xffffu)), T::to_float((st)(w2.y >> 16)));
+          okr[u] = reinterpret_cast<const uint2 *>(reinterpret_cast<const st *>(a.ws_o) + r * D)[q4];
         } else {
           mk[u] = -INFINITY;
           lk[u] = 0.f;
-          ok[u] = make_float4(0.f, 0.f, 0.f, 0.f);
+          okr[u] = make_uint2(0u, 0u);
         }
       }
       float m_new = m_max;
@@ -869,10 +869,10 @@ __global__ __launch_bounds__(256) void decode_multi_reduce_kernel(MultiArgs a) {
         if (u < cnt) {
           const float wk = lk[u] > 0.f ? lk[u] * fast_exp2(mk[u] - m_max) : 0.f;
           wsum += wk;
-          acc.x += wk * ok[u].x;
-          acc.y += wk * ok[u].y;
-          acc.z += wk * ok[u].z;
-          acc.w += wk * ok[u].w;
+          acc.x += wk * T::to_float((st)(okr[u].x & 0xffffu));
+          acc.y += wk * T::to_float((st)(okr[u].x >> 16));
+          acc.z += wk * T::to_float((st)(okr[u].y & 0xffffu));
+          acc.w += wk * T::to_float((st)(okr[u].y >> 16));
         }
       }
     }
