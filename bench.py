@@ -184,6 +184,107 @@ def _oracle_run(case, threads: int, min_seconds: float, max_repeats: int) -> dic
             "seconds_per_call": round(t, 4)}
 
 
+# Per-wave timeline records of the measurement build (the layout the decode
+# kernels write after the workspace's other parts): main kernel 8 uint64 per
+# wave for up to 8192 waves, combine kernel 2 uint64 per wave for up to 65536.
+TIMELINE_WAVES, TIMELINE_COMBINE_WAVES = 8192, 65536
+TIMELINE_BYTES = TIMELINE_WAVES * 64 + TIMELINE_COMBINE_WAVES * 16
+TIMELINE_TICK_US = 0.01  # s_memrealtime runs at 100 MHz
+
+
+def wave_timeline(torch, dev, decode, ws, ws_bytes: int, calls: int, config: str, fused: bool) -> dict:
+    """Per-wave timeline of ``calls`` decode calls on the measurement build:
+    when the waves enter, have the tile schedule, consume their first tile
+    and end streaming, per XCD, and when the combine kernel's waves enter
+    and finish merging, all relative to the first wave's entry (µs)."""
+    base = ws_bytes - TIMELINE_BYTES
+    region = ws[base:ws_bytes]
+    scrub = torch.ones(1 << 28, dtype=torch.float32, device=dev)
+    per_call = []
+    for c in range(calls):
+        cold = c < (calls + 1) // 2
+        region.zero_()
+        if cold:
+            scrub.sum()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        decode()
+        e1.record()
+        e1.synchronize()
+        rec = region.view(torch.int64).cpu().numpy().view(np.uint64)
+        main = rec[: TIMELINE_WAVES * 8].reshape(TIMELINE_WAVES, 8)
+        main = main[main[:, 6] == 1]
+        comb = rec[TIMELINE_WAVES * 8:].reshape(TIMELINE_COMBINE_WAVES, 2)
+        comb = comb[comb[:, 0] != 0]
+        t0 = int(main[:, 0].min())
+
+        def us(x):
+            return (np.asarray(x, dtype=np.float64) - t0) * TIMELINE_TICK_US
+
+        entry, sched, first, end = us(main[:, 0]), us(main[:, 1]), us(main[:, 2]), us(main[:, 3])
+        tiles = (main[:, 4] >> np.uint64(32)).astype(np.int64)
+        segs = (main[:, 4] & np.uint64(0xFFFFFFFF)).astype(np.int64)
+        xcc = main[:, 5].astype(np.int64)
+        merged = (comb[:, 1] >> np.uint64(63)) == 1
+        c_entry = us(comb[:, 0])
+        c_exit = us(comb[merged, 1] & np.uint64((1 << 63) - 1))
+        stream = end - first
+        row = {
+            "cold": cold, "call_us_events": round(e0.elapsed_time(e1) * 1e3, 2), "waves": int(main.shape[0]),
+            "entry_spread_us": round(float(entry.max()), 2),
+            "schedule_ready_us": {"median": round(float(np.median(sched)), 2), "max": round(float(sched.max()), 2)},
+            "first_tile_us": {"median": round(float(np.median(first)), 2), "max": round(float(first.max()), 2)},
+            "stream_end_us": {"p10": round(float(np.percentile(end, 10)), 2), "median": round(float(np.median(end)), 2),
+                              "p90": round(float(np.percentile(end, 90)), 2), "max": round(float(end.max()), 2)},
+            "xcd_mean_end_us": [round(float(end[xcc == x].mean()), 2) if np.any(xcc == x) else None
+                                for x in range(8)],
+            "tiles_per_wave": {"min": int(tiles.min()), "max": int(tiles.max())},
+            "segments_per_wave": {"median": float(np.median(segs)), "max": int(segs.max())},
+            # does a wave that begins more segments end later?
+            "corr_end_vs_segments": round(float(np.corrcoef(end, segs)[0, 1]), 3) if segs.std() > 0 else None,
+            "corr_stream_vs_segments": (round(float(np.corrcoef(stream, segs)[0, 1]), 3)
+                                        if segs.std() > 0 else None),
+            "combine": {
+                "first_entry_us": round(float(c_entry.min()), 2) if c_entry.size else None,
+                "gap_after_last_stream_end_us": round(float(c_entry.min() - end.max()), 2) if c_entry.size else None,
+                "merging_waves": int(merged.sum()),
+                "merge_end_median_us": round(float(np.median(c_exit)), 2) if c_exit.size else None,
+                "merge_end_max_us": round(float(c_exit.max()), 2) if c_exit.size else None,
+            },
+        }
+        per_call.append(row)
+    del scrub
+
+    def med(rows, *keys):
+        vals = []
+        for r in rows:
+            v = r
+            for k in keys:
+                v = v[k]
+            vals.append(v)
+        return round(float(np.median(vals)), 2)
+
+    summary = {}
+    for label, rows in (("cold", [r for r in per_call if r["cold"]]), ("hot", [r for r in per_call if not r["cold"]])):
+        if not rows:
+            continue
+        summary[label] = {
+            "calls": len(rows),
+            "call_us_events": med(rows, "call_us_events"),
+            "schedule_ready_us": med(rows, "schedule_ready_us", "median"),
+            "first_tile_median_us": med(rows, "first_tile_us", "median"),
+            "stream_end_median_us": med(rows, "stream_end_us", "median"),
+            "stream_end_max_us": med(rows, "stream_end_us", "max"),
+            "combine_gap_us": med(rows, "combine", "gap_after_last_stream_end_us"),
+            "merge_end_max_us": med(rows, "combine", "merge_end_max_us"),
+        }
+    return {"timeline": config, "kernel": "decode_mfma_kernel" + (" (append variant)" if fused else "") +
+            " + decode_streamk_reduce_kernel, measurement build (PA_WAVE_TIMELINE)",
+            "clock": "s_memrealtime, 100 MHz, microseconds from the first wave's entry",
+            "summary": summary, "calls": per_call}
+
+
 def read_ceiling(torch, dev, calls: int = 20) -> dict:
     """Plain streaming-read ceiling of this machine: the library's read probe
     (non-temporal 16-byte loads, four work-groups per CU) over 1 GiB, median
@@ -771,6 +872,9 @@ def main() -> int:
                          "(admission, tail copies, shared-prefix decode, bulk block copy); multi: "
                          "multi-token decode on --config spec_verify_llama70b (default) or chunked_prefill; "
                          "batching: the continuous-batching driver looping over schedule, writes and decode")
+    ap.add_argument("--timeline", type=int, default=0, metavar="CALLS",
+                    help="load the measurement build and print the per-wave timeline of this many decode "
+                         "calls (half after a 1 GiB scrub, half back to back) instead of timing steps")
     ap.add_argument("--traffic-command", default="",
                     help="the profiling command line recorded with --write-traffic")
     args = ap.parse_args()
@@ -797,6 +901,11 @@ def main() -> int:
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         return 2
+    if args.timeline > 0:
+        if args.measure != "decode":
+            print("--timeline covers the single-token decode", file=sys.stderr)
+            return 2
+        _lib.use_timeline_build()
     _lib.load()
     if args.measure == "prefix":
         return measure_prefix(args)
@@ -880,6 +989,17 @@ def main() -> int:
 
     # algorithmic bytes of the call the events bracket
     call_bytes = ab["decode"] + (ab["write_out"] if fused else 0)
+
+    if args.timeline > 0:
+        if not mfma:
+            print("--timeline covers the stream-K (MFMA) decode", file=sys.stderr)
+            return 2
+        for _ in range(args.warmup):
+            decode()
+        print(json.dumps(wave_timeline(torch, dev, decode, ws, ws_bytes, args.timeline, args.config, fused)),
+              flush=True)
+        pool.close()
+        return 0
 
     if args.profile_calls > 0:
         for _ in range(args.profile_calls):

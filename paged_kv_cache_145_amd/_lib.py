@@ -33,7 +33,7 @@ class PaPrefixStats(ctypes.Structure):
 
 # kernel-configuration overrides (pa_set_option), for tests and measurements
 PA_OPTIONS = {"PA_FORCE_VALU": 0, "PA_PARTITION_TOKENS": 1, "PA_MULTI_WAVES": 2, "PA_MULTI_ROW_TILES": 3,
-              "PA_MULTI_PASS_GROUP": 4, "PA_MULTI_MIN_RANGE": 5}
+              "PA_MULTI_PASS_GROUP": 4, "PA_MULTI_MIN_RANGE": 5, "PA_DECODE_SEQ_COST": 6}
 
 PA_PREFIX_TAIL = 1
 PA_PREFIX_RESIDENT = 2
@@ -115,6 +115,17 @@ SIGNATURES = {
 }
 
 _LIB = None
+
+
+def use_timeline_build() -> None:
+    """Load the measurement build (``libpa_mi355x_timeline.so``: the same
+    library with per-wave timeline stamps in the stream-K decode) instead of
+    the product library.  Must precede the first load."""
+    global LIB_NAME, LIB_PATH
+    if _LIB is not None:
+        raise RuntimeError("the library is already loaded")
+    LIB_NAME = "libpa_mi355x_timeline.so"
+    LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), LIB_NAME)
 
 
 def load() -> ctypes.CDLL:

@@ -18,6 +18,11 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(ROOT, "_build")
 LIB_NAME = "libpa_mi355x.so"
 LIB_PATH = os.path.join(PKG, LIB_NAME)
+# Measurement build: the same library with per-wave timeline stamps in the
+# stream-K decode (PA_WAVE_TIMELINE); only `bench.py --timeline` loads it.
+TIMELINE_LIB_NAME = "libpa_mi355x_timeline.so"
+TIMELINE_LIB_PATH = os.path.join(PKG, TIMELINE_LIB_NAME)
+TIMELINE_SOURCES = ["decode_kernels.hip", "api.hip"]  # the files the define changes
 
 HIP_SOURCES = ["decode_kernels.hip", "multi_kernels.hip", "write_kernels.hip", "api.hip"]
 CPP_SOURCES = ["pool.cpp", "prefix.cpp", "batching.cpp"]
@@ -51,25 +56,41 @@ def _run(cmd, verbose):
     return proc
 
 
+def _link(hipcc, objs, path, verbose):
+    tmp = path + ".tmp"
+    _run([hipcc, "-shared", f"--offload-arch={ARCH}", *objs, "-o", tmp], verbose)
+    os.replace(tmp, path)
+
+
 def build(verbose: bool = False, jobs: int = 4) -> str:
-    """Compile every source and link ``libpa_mi355x.so``; returns its path."""
+    """Compile every source and link ``libpa_mi355x.so`` and the timeline
+    measurement library; returns the product library's path."""
     hipcc = _hipcc()
-    os.makedirs(BUILD_DIR, exist_ok=True)
+    tl_dir = os.path.join(BUILD_DIR, "timeline")
+    os.makedirs(tl_dir, exist_ok=True)
     cmds = []
     objs = []
+    tl_objs = []
     for src in HIP_SOURCES:
         obj = os.path.join(BUILD_DIR, src + ".o")
         cmds.append([hipcc, *COMMON, *HIP_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj])
         objs.append(obj)
+        if src in TIMELINE_SOURCES:
+            tl_obj = os.path.join(tl_dir, src + ".o")
+            cmds.append([hipcc, *COMMON, *HIP_FLAGS, "-DPA_WAVE_TIMELINE", "-c", os.path.join(CSRC, src),
+                         "-o", tl_obj])
+            tl_objs.append(tl_obj)
+        else:
+            tl_objs.append(obj)
     for src in CPP_SOURCES:
         obj = os.path.join(BUILD_DIR, src + ".o")
         cmds.append([hipcc, *COMMON, "-x", "c++", "-c", os.path.join(CSRC, src), "-o", obj])
         objs.append(obj)
+        tl_objs.append(obj)
     with concurrent.futures.ThreadPoolExecutor(max_workers=max(1, jobs)) as ex:
         list(ex.map(lambda c: _run(c, verbose), cmds))
-    tmp = LIB_PATH + ".tmp"
-    _run([hipcc, "-shared", f"--offload-arch={ARCH}", *objs, "-o", tmp], verbose)
-    os.replace(tmp, LIB_PATH)
+    _link(hipcc, objs, LIB_PATH, verbose)
+    _link(hipcc, tl_objs, TIMELINE_LIB_PATH, verbose)
     return LIB_PATH
 
 

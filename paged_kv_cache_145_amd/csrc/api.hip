@@ -48,7 +48,8 @@ struct OptionInit {
   OptionInit() {
     static const char *const names[PA_OPT_COUNT] = {"PA_FORCE_VALU",      "PA_PARTITION_TOKENS",
                                                     "PA_MULTI_WAVES",     "PA_MULTI_ROW_TILES",
-                                                    "PA_MULTI_PASS_GROUP", "PA_MULTI_MIN_RANGE"};
+                                                    "PA_MULTI_PASS_GROUP", "PA_MULTI_MIN_RANGE",
+                                                    "PA_DECODE_SEQ_COST"};
     for (int i = 0; i < PA_OPT_COUNT; ++i) g_options[i].store(env_int(names[i], 0));
   }
 } g_option_init;
@@ -87,6 +88,9 @@ WorkspaceLayout workspace_layout(const pa_pool *pool, int32_t num_seqs, int32_t 
     w.ml_bytes = round_up(slots * group * 2 * sizeof(float), 256);
     w.o_bytes = round_up(slots * group * pool->head_dim * sizeof(float), 256);
     w.total = w.sched_bytes + w.ml_bytes + w.o_bytes;
+#ifdef PA_WAVE_TIMELINE
+    w.total += kTimelineBytes;  // measurement build: per-wave records after the partials
+#endif
     return w;
   }
   if (w.max_parts <= 1) {
@@ -480,6 +484,9 @@ int decode_impl(pa_pool *pool, void *out, const void *query, const int32_t *bloc
   a.ws_sched = w.sched_bytes > 0 ? reinterpret_cast<int32_t *>(ws) : nullptr;
   a.ws_ml = w.ml_bytes > 0 ? reinterpret_cast<float *>(ws + w.sched_bytes) : nullptr;
   a.ws_o = w.o_bytes > 0 ? reinterpret_cast<float *>(ws + w.sched_bytes + w.ml_bytes) : nullptr;
+#ifdef PA_WAVE_TIMELINE
+  if (w.o_bytes > 0) a.timeline = reinterpret_cast<uint64_t *>(ws + w.sched_bytes + w.ml_bytes + w.o_bytes);
+#endif
   a.rope = ring ? ring->rope_table : nullptr;
   a.kv_block_stride = (int64_t)pool->block_size * pool->num_kv_heads * pool->head_dim;
   a.num_seqs = num_seqs;
@@ -495,6 +502,12 @@ int decode_impl(pa_pool *pool, void *out, const void *query, const int32_t *bloc
   // Plain tiles are cheap, so short ranges lose to start-up and merging;
   // ring tiles also rotate every key and gain from spreading out.
   a.min_range_tiles = ring ? 1 : 4;
+  // Stream-K ranges weigh each sequence as this many extra tiles (its start
+  // and end: staging, query fragments, output or partial rows).  Measured
+  // on the 70B-shaped batch: 8-bit pools 52.0 -> 48.9 us per call at 5
+  // (costs 4-6 equal, 9 worse), 16-bit pools 74.1 -> 73.7 us at 1.
+  const int forced_cost = pa::option(PA_OPT_DECODE_SEQ_COST);
+  a.seq_cost = forced_cost >= 1 ? forced_cost - 1 : pool->kv_fp8 ? 5 : 1;
   a.ring_sink = ring ? ring->sink : 0;
   a.ring_window = ring ? ring->window : 1;
   a.scale_log2 = scale * pa::kLog2eHost;

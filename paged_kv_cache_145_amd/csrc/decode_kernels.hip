@@ -38,6 +38,14 @@ namespace pa {
 namespace {
 
 constexpr int kNW = kDecodeWaves;
+
+#ifdef PA_WAVE_TIMELINE
+// Measurement build only: the real-time counter (100 MHz, the same on every
+// XCD) and the XCC id of the executing wave (hardware register XCC_ID, bits
+// 3:0).
+__device__ __forceinline__ uint64_t tl_now() { return __builtin_amdgcn_s_memrealtime(); }
+__device__ __forceinline__ uint64_t tl_xcc() { return (uint64_t)(__builtin_amdgcn_s_getreg((3 << 11) | 20) & 15); }
+#endif
 // A new tile maximum must exceed the running reference by this many log2
 // units before the accumulators are rescaled; weights stay <= 2^8.
 constexpr float kRescaleSlack = 8.0f;
@@ -350,6 +358,32 @@ __device__ __forceinline__ int active_groups(const DecodeArgs &a, int total_tile
   return max(1, min(groups, (total_tiles + m - 1) / m));
 }
 
+// Cost-weighted stream-K ranges.  Sequence b weighs its tiles plus `cost`
+// tiles' worth of work for its start and end, so the weighted position of
+// its tile t is W(b) + cost + t with W(b) = s_tfirst[b] + cost * b (strictly
+// increasing in b when cost > 0).  Group q takes the tiles whose weighted
+// position lies in [q * per, (q + 1) * per): a range that opens many short
+// sequences gets fewer tiles.  Every boundary depends only on the lengths,
+// the cost and the grid, so the combine order stays fixed.  cost = 0 gives
+// ranges of equal tile counts.
+__device__ __forceinline__ int64_t weighted_total(int total, int num_seqs, int cost) {
+  return (int64_t)total + (int64_t)cost * num_seqs;
+}
+
+// First tile whose weighted position is >= target (total if none).
+__device__ __forceinline__ int weighted_tile(const int *s_tfirst, int num_seqs, int total, int cost,
+                                             int64_t target) {
+  if (target >= weighted_total(total, num_seqs, cost)) return total;
+  int lo = 0, hi = num_seqs;  // largest b < num_seqs with W(b) <= target
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if ((int64_t)s_tfirst[mid] + (int64_t)cost * mid <= target) lo = mid;
+    else hi = mid;
+  }
+  const int64_t off = target - ((int64_t)s_tfirst[lo] + (int64_t)cost * lo) - cost;
+  return s_tfirst[lo] + (off > 0 ? (int)off : 0);
+}
+
 // (b, t) of flattened tile y (y < s_tfirst[num_seqs]).
 __device__ __forceinline__ void locate_tile(const int *s_tfirst, int num_seqs, int y, int &b,
                                             int &t, int &tiles) {
@@ -395,7 +429,15 @@ void decode_mfma_kernel(DecodeArgs a) {
   __shared__ __align__(16) char s_vtiles[kNW][MfmaLds<D>::kVBytes];
   __shared__ uint4 s_q[kNW][kQSlots * KB * kWave];  // query fragments, lane-major
 
+#ifdef PA_WAVE_TIMELINE
+  const uint64_t tl_entry = tl_now();
+#endif
   const int total = build_tile_schedule(a, RING, s_tfirst, s_len, s_wsum, (RING && APP) ? s_newslot : nullptr);
+#ifdef PA_WAVE_TIMELINE
+  const uint64_t tl_sched = tl_now();
+  uint64_t tl_first = 0;
+  int tl_segs = 0;
+#endif
   const int hkv = a.num_kv_heads;
   const int G = a.group;
   const int lane = threadIdx.x & 63;
@@ -406,9 +448,9 @@ void decode_mfma_kernel(DecodeArgs a) {
   const int grp_id = gw / hkv;  // tile range of this wave
   const int g = gw - grp_id * hkv;  // KV head of this wave
   if (grp_id >= groups) return;
-  const int per = (total + groups - 1) / groups;
-  const int xbeg = grp_id * per;
-  const int xend = min(total, xbeg + per);
+  const int64_t per = (weighted_total(total, a.num_seqs, a.seq_cost) + groups - 1) / groups;
+  const int xbeg = weighted_tile(s_tfirst, a.num_seqs, total, a.seq_cost, grp_id * per);
+  const int xend = weighted_tile(s_tfirst, a.num_seqs, total, a.seq_cost, (grp_id + 1) * per);
   if (xbeg >= xend) return;  // no barriers follow
   const int hq0 = g * G;
   const int64_t head_off = (int64_t)g * D;
@@ -756,6 +798,10 @@ void decode_mfma_kernel(DecodeArgs a) {
       const int b = rd(tb, j), flag = rd(tflag, j);
       if ((flag & 1) || c0 + j == xbeg) begin_segment(j, b, (flag & 1) != 0);
       process_tile(j, kc, vc);
+#ifdef PA_WAVE_TIMELINE
+      if (tl_first == 0) tl_first = tl_now();
+      tl_segs += ((flag & 1) || c0 + j == xbeg) ? 1 : 0;
+#endif
       const bool last = c0 + j == xend - 1;
       if ((flag & 2) || last) end_segment(b, (flag & 2) != 0);
     }
@@ -771,6 +817,20 @@ void decode_mfma_kernel(DecodeArgs a) {
         step(j + u, kbuf[u], vbuf[u], kbuf[(u + S - 1) % S], vbuf[(u + S - 1) % S]);
     }
   }
+#ifdef PA_WAVE_TIMELINE
+  const uint64_t tl_end = tl_now();
+  if (lane == 0 && a.timeline != nullptr && gw < kTimelineWaves) {
+    uint64_t *r = a.timeline + (int64_t)gw * 8;
+    r[0] = tl_entry;
+    r[1] = tl_sched;
+    r[2] = tl_first;
+    r[3] = tl_end;
+    r[4] = ((uint64_t)(xend - xbeg) << 32) | (uint32_t)tl_segs;
+    r[5] = tl_xcc();
+    r[6] = 1;
+    r[7] = blockIdx.x;
+  }
+#endif
 }
 
 // ---------------------------------------------------------------------------
@@ -790,6 +850,14 @@ __global__ __launch_bounds__(256) void decode_streamk_reduce_kernel(DecodeArgs a
   const int g = blockIdx.y, b = blockIdx.z;
   const int hkv = a.num_kv_heads, G = a.group;
   if (h >= G) return;
+#ifdef PA_WAVE_TIMELINE
+  const int64_t tl_cw =
+      (((int64_t)blockIdx.z * gridDim.y + blockIdx.y) * gridDim.x + blockIdx.x) * kNW + (threadIdx.x >> 6);
+  uint64_t *tl_rec = (a.timeline != nullptr && tl_cw < kTimelineCombineWaves)
+                         ? a.timeline + (int64_t)kTimelineWaves * 8 + tl_cw * 2
+                         : nullptr;
+  if (tl_rec != nullptr && lane == 0) tl_rec[0] = tl_now();
+#endif
   const int t0 = a.ws_sched[b], t1 = a.ws_sched[b + 1];
   const int total = a.ws_sched[a.num_seqs];
   // lane holds DPL adjacent elements (one 4-byte access at D = 128)
@@ -800,8 +868,9 @@ __global__ __launch_bounds__(256) void decode_streamk_reduce_kernel(DecodeArgs a
     return;
   }
   const int active = active_groups(a, total, groups);
-  const int per = (total + active - 1) / active;
-  const int q_lo = t0 / per, q_hi = (t1 - 1) / per;
+  const int64_t per = (weighted_total(total, a.num_seqs, a.seq_cost) + active - 1) / active;
+  const int64_t w0 = (int64_t)t0 + (int64_t)a.seq_cost * (b + 1);  // weighted position of tile 0
+  const int q_lo = (int)(w0 / per), q_hi = (int)((w0 + (t1 - t0) - 1) / per);
   if (q_lo == q_hi) return;
   const int nseg = q_hi - q_lo + 1;
   const int64_t slot0 = ((int64_t)q_lo + b) * hkv + g;  // slot of segment s: slot0 + s * hkv
@@ -864,6 +933,9 @@ __global__ __launch_bounds__(256) void decode_streamk_reduce_kernel(DecodeArgs a
   const float inv = 1.f / den;
 #pragma unroll
   for (int k = 0; k < DPL; ++k) out[k] = T::from_float(num[k] * inv);
+#ifdef PA_WAVE_TIMELINE
+  if (tl_rec != nullptr && lane == 0) tl_rec[1] = tl_now() | (1ull << 63);
+#endif
 }
 
 // ---------------------------------------------------------------------------

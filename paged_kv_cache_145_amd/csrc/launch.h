@@ -63,12 +63,30 @@ struct DecodeArgs {
   int32_t partition_tokens;
   int32_t max_parts;
   int32_t min_range_tiles;  // MFMA kernel: shortest stream-K range worth a group
+  int32_t seq_cost;         // MFMA kernel: extra cost of a sequence in its range, in tiles
   int32_t ring_sink;
   int32_t ring_window;
   float scale_log2;  // scale * log2(e)
   KvScales kv_scale;  // 8-bit pools: dequantisation scales per KV head
   KvScales kv_inv;    // 8-bit pools in append mode: fp32(1 / scale), as the cache write uses
+  uint64_t *timeline;  // measurement build only (PA_WAVE_TIMELINE), else null and unused
 };
+
+// Per-wave timeline of the stream-K decode, compiled only into the
+// measurement library (PA_WAVE_TIMELINE; the product library has none of
+// it).  The records sit after the workspace's other parts:
+//   main kernel, wave gw < kTimelineWaves: 8 uint64 at gw * 8:
+//     [0] entry stamp, [1] tile schedule ready, [2] first tile consumed,
+//     [3] streaming end, [4] (tiles << 32) | segments begun, [5] XCC id,
+//     [6] 1 (record valid), [7] work-group id
+//   combine kernel, wave cw < kTimelineCombineWaves: 2 uint64 at
+//     kTimelineWaves * 8 + cw * 2: [0] entry stamp, [1] exit stamp with
+//     bit 63 set when the wave merged a cut sequence.
+// Stamps are s_memrealtime counts (100 MHz).  Waves that exit before
+// streaming (no range) leave their record untouched.
+constexpr int kTimelineWaves = 8192;
+constexpr int kTimelineCombineWaves = 65536;
+constexpr size_t kTimelineBytes = (size_t)kTimelineWaves * 8 * 8 + (size_t)kTimelineCombineWaves * 2 * 8;
 
 // Multi-token decode (several new tokens per sequence, causal).
 constexpr int kMaxMultiSeqsHost = 1024;  // (sequence, pass group) pairs per launch slice

@@ -14,8 +14,8 @@ import torch
 
 import paged_kv_cache_145_amd as pk
 import workloads
-from gpu_support import (TORCH_DTYPES, DeviceCase, INT_VIEW, assert_parity, oracle_reference, raw_to_torch,
-                         torch_bits)
+from gpu_support import (TORCH_DTYPES, DeviceCase, INT_VIEW, assert_parity, options, oracle_reference,
+                         raw_to_torch, torch_bits)
 
 pytestmark = pytest.mark.gpu
 
@@ -206,3 +206,14 @@ def test_append_rejects_misaligned_inputs():
     assert e.value.status == -1
     dc.close()
     full.close()
+
+
+@pytest.mark.parametrize("cost", [2, 6])
+def test_append_cost_weighted_ranges(cost):
+    """The one-call step with cost-weighted stream-K ranges equals the two
+    calls bit for bit (both under the same ranges) and the oracle."""
+    print(f"append llama70b b64, sequence cost {cost}", flush=True)
+    with options(PA_DECODE_SEQ_COST=cost + 1):
+        _check(workloads.config_llama70b())
+        _check(workloads.make_paged_case("append_cost", 8700 + cost, "bf16", [0, 1, 2, 15, 16, 17, 33, 700],
+                                         32, 4, 128, 16))

@@ -15,7 +15,7 @@ import torch
 import oracle
 import paged_kv_cache_145_amd as pk
 import workloads
-from gpu_support import DeviceCase, assert_parity, oracle_reference
+from gpu_support import DeviceCase, assert_parity, options, oracle_reference, torch_bits
 
 pytestmark = pytest.mark.gpu
 
@@ -195,3 +195,20 @@ def test_fp8_ring_append_step(kv_format):
     from test_gpu_append import _check
 
     _check(workloads.config_sink_ring_fp8(kv_format, [1, 4, 5, 1023, 1024, 1025, 2045, 99_999]))
+
+
+@pytest.mark.parametrize("cost", [2, 6])
+@pytest.mark.parametrize("name", ["llama70b_b64_fp8", "llama70b_b64_e5m2"])
+def test_fp8_decode_cost_weighted_ranges(name, cost):
+    """8-bit pools under cost-weighted stream-K ranges: the oracle's result,
+    repeated bit for bit."""
+    case = _case(name)
+    dc = DeviceCase(case)
+    dc.write_all()
+    with options(PA_DECODE_SEQ_COST=cost + 1):
+        out = dc.decode()
+        again = dc.decode()
+    _, _, _, ref = oracle_reference(case)
+    assert_parity(out, ref, case.dtype)
+    assert np.array_equal(torch_bits(out, case.dtype), torch_bits(again, case.dtype))
+    dc.close()

@@ -409,3 +409,58 @@ def test_input_checks_count_exactly_the_planted_errors(ring):
     torch.cuda.synchronize()
     assert counts.cpu().tolist() == [2, 2, 1, 0]
     dc.close()
+
+
+# ------------------------------------------------- cost-weighted stream-K ranges
+
+COST_SHAPES = [
+    # dtype, Hq, Hkv, D, bs, lengths: short and empty sequences between long ones
+    ("bf16", 32, 4, 128, 16, [0, 1, 2, 15, 16, 17, 33, 700, 2900, 0, 5, 9000, 3]),
+    ("f16", 8, 8, 64, 64, [1, 64, 65, 1500, 33, 0]),
+    ("bf16", 16, 1, 128, 16, [3, 20000, 1, 1, 1]),
+]
+
+
+@pytest.mark.parametrize("cost", [1, 3, 8, 40])
+@pytest.mark.parametrize("shape", COST_SHAPES, ids=lambda s: f"{s[0]}-G{s[1] // s[2]}-D{s[3]}-n{len(s[5])}")
+def test_decode_cost_weighted_ranges(shape, cost):
+    """Stream-K ranges that weigh every sequence as `cost` extra tiles give
+    the oracle's result, repeat bit for bit, and stay bit-identical under
+    block relabelling (the boundaries depend only on lengths, cost and
+    grid)."""
+    dtype, hq, hkv, d, bs, lens = shape
+    case = workloads.make_paged_case("cost", 7300 + hq + d, dtype, lens, hq, hkv, d, bs)
+    _, _, _, ref = oracle_reference(case)
+    dc = DeviceCase(case)
+    dc.write_all()
+    perm = np.random.default_rng(cost).permutation(case.num_blocks)
+    case2 = workloads.DecodeCase(**{**case.__dict__})
+    case2.block_tables = np.where(case.block_tables >= 0, perm[np.maximum(case.block_tables, 0)],
+                                  case.block_tables).astype(np.int32)
+    dc2 = DeviceCase(case2)
+    dc2.write_all()
+    with options(PA_DECODE_SEQ_COST=cost + 1):
+        out = dc.decode()
+        again = dc.decode()
+        moved = dc2.decode()
+    assert_parity(out, ref, dtype)
+    bits = torch_bits(out, dtype)
+    assert np.array_equal(bits, torch_bits(again, dtype))
+    assert np.array_equal(bits, torch_bits(moved, dtype))
+    for b, n in enumerate(lens):
+        if n == 0:
+            assert np.all(bits[b] == 0)
+    dc.close()
+    dc2.close()
+
+
+@pytest.mark.parametrize("cost", [2, 6])
+@pytest.mark.parametrize("name", ["llama70b_b64", "shared_prefix", "sink_ring"])
+def test_decode_cost_weighted_ranges_full_config(name, cost):
+    case, (_, _, _, ref) = reference(name, CONFIGS[name])
+    dc = DeviceCase(case)
+    dc.write_all()
+    with options(PA_DECODE_SEQ_COST=cost + 1):
+        out = dc.decode()
+    assert_parity(out, ref, case.dtype)
+    dc.close()
