@@ -190,6 +190,7 @@ def _oracle_run(case, threads: int, min_seconds: float, max_repeats: int) -> dic
 TIMELINE_WAVES, TIMELINE_COMBINE_WAVES = 8192, 65536
 TIMELINE_BYTES = TIMELINE_WAVES * 64 + TIMELINE_COMBINE_WAVES * 16
 TIMELINE_TICK_US = 0.01  # s_memrealtime runs at 100 MHz
+TIMELINE_RECORDS = []  # raw records of each call, for callers that analyse them further
 
 
 def wave_timeline(torch, dev, decode, ws, ws_bytes: int, calls: int, config: str, fused: bool) -> dict:
@@ -213,6 +214,7 @@ def wave_timeline(torch, dev, decode, ws, ws_bytes: int, calls: int, config: str
         e1.record()
         e1.synchronize()
         rec = region.view(torch.int64).cpu().numpy().view(np.uint64)
+        TIMELINE_RECORDS.append(rec.copy())
         main = rec[: TIMELINE_WAVES * 8].reshape(TIMELINE_WAVES, 8)
         main = main[main[:, 6] == 1]
         comb = rec[TIMELINE_WAVES * 8:].reshape(TIMELINE_COMBINE_WAVES, 2)

@@ -565,6 +565,8 @@ const char *pa_last_hip_error(void);
  *   PA_OPT_DECODE_SEQ_COST   single-token stream-K decode: the extra work a
  *                            sequence brings to the range that holds it, in
  *                            16-token tiles, plus one (1: none)
+ *   PA_OPT_MULTI_SEQ_COST    multi-token decode: the same for a (sequence,
+ *                            pass group), plus one (1: none)
  * Options change the kernel choice and the workspace size: set them before
  * pa_*_workspace_bytes and keep them until the matching call has been
  * enqueued.  pa_set_option returns PA_ERR_INVAL for an unknown option or a
@@ -577,7 +579,8 @@ typedef enum {
   PA_OPT_MULTI_PASS_GROUP = 4,
   PA_OPT_MULTI_MIN_RANGE = 5,
   PA_OPT_DECODE_SEQ_COST = 6,
-  PA_OPT_COUNT = 7
+  PA_OPT_MULTI_SEQ_COST = 7,
+  PA_OPT_COUNT = 8
 } pa_option;
 int pa_set_option(pa_option opt, int32_t value);
 int32_t pa_get_option(pa_option opt);

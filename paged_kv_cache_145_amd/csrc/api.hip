@@ -49,7 +49,7 @@ struct OptionInit {
     static const char *const names[PA_OPT_COUNT] = {"PA_FORCE_VALU",      "PA_PARTITION_TOKENS",
                                                     "PA_MULTI_WAVES",     "PA_MULTI_ROW_TILES",
                                                     "PA_MULTI_PASS_GROUP", "PA_MULTI_MIN_RANGE",
-                                                    "PA_DECODE_SEQ_COST"};
+                                                    "PA_DECODE_SEQ_COST", "PA_MULTI_SEQ_COST"};
     for (int i = 0; i < PA_OPT_COUNT; ++i) g_options[i].store(env_int(names[i], 0));
   }
 } g_option_init;
@@ -216,6 +216,13 @@ int multi_impl(pa_pool *pool, void *out, const void *query, const void *draft_k,
   a.groups = m.groups;
   const int forced_range = pa::option(PA_OPT_MULTI_MIN_RANGE);
   a.min_range_tiles = forced_range >= 1 ? forced_range : 4;
+  // Stream-K ranges weigh each (sequence, pass group) as this many extra
+  // tiles (staging its query rows, writing its output or partial rows).
+  // Measured: verification of the 70B-shaped batch 101.7 -> 93.5 us at 6
+  // (4: 94.6, 12: 96.9), E4M3 pools 80.5 -> 67.5 us at 8, chunked prefill
+  // 211.6 -> 181.0 us at 6, ring verification 36.1 -> 33.6 us.
+  const int forced_cost = pa::option(PA_OPT_MULTI_SEQ_COST);
+  a.seq_cost = forced_cost >= 1 ? forced_cost - 1 : pool->kv_fp8 ? 8 : 6;
   a.block_shift = pa::log2_exact(pool->block_size);
   a.scale_log2 = scale * pa::kLog2eHost;
   if (ring != nullptr) {

@@ -254,6 +254,32 @@ __device__ __forceinline__ uint2 fp8x4_to_16(uint32_t v) {
   return make_uint2(code_pair_to_16<T, F, false>(v), code_pair_to_16<T, F, true>(v));
 }
 
+// Cost-weighted stream-K ranges (single- and multi-token decode).  Sequence
+// (or virtual sequence) b weighs its tiles plus `cost` tiles' worth of work
+// for its start and end, so the weighted position of its tile t is W(b) + cost + t with W(b) = s_tfirst[b] + cost * b (strictly
+// increasing in b when cost > 0).  Group q takes the tiles whose weighted
+// position lies in [q * per, (q + 1) * per): a range that opens many short
+// sequences gets fewer tiles.  Every boundary depends only on the lengths,
+// the cost and the grid, so the combine order stays fixed.  cost = 0 gives
+// ranges of equal tile counts.
+__device__ __forceinline__ int64_t weighted_total(int total, int num_seqs, int cost) {
+  return (int64_t)total + (int64_t)cost * num_seqs;
+}
+
+// First tile whose weighted position is >= target (total if none).
+__device__ __forceinline__ int weighted_tile(const int *s_tfirst, int num_seqs, int total, int cost,
+                                             int64_t target) {
+  if (target >= weighted_total(total, num_seqs, cost)) return total;
+  int lo = 0, hi = num_seqs;  // largest b < num_seqs with W(b) <= target
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if ((int64_t)s_tfirst[mid] + (int64_t)cost * mid <= target) lo = mid;
+    else hi = mid;
+  }
+  const int64_t off = target - ((int64_t)s_tfirst[lo] + (int64_t)cost * lo) - cost;
+  return s_tfirst[lo] + (off > 0 ? (int)off : 0);
+}
+
 // ------------------------------------------------------------- RoPE ---
 // Rotate-half RoPE on a 16-bit fragment held as KB 16-byte chunks where
 // chunk kb covers d = 32 kb + 8 grp + [0, 8); chunk kb + KB/2 holds the

@@ -119,6 +119,7 @@ struct MultiArgs {
   int32_t pgroups;    // ceil(passes / pass_group)
   int32_t groups;     // wave groups (Hkv * pass_group waves each) of the grid
   int32_t min_range_tiles;
+  int32_t seq_cost;   // extra cost of a (sequence, pass group) in its range, in tiles
   int32_t block_shift;
   float scale_log2;
   KvScales kv_scale;  // 8-bit pools: dequantisation scales per KV head

@@ -263,9 +263,9 @@ void decode_multi_kernel(MultiArgs a) {
   const int g = within / PG;           // KV head of this wave
   const int w = within - g * PG;       // pass of each pass group
   if (grp_id >= groups) return;        // no barriers follow
-  const int per = (total + groups - 1) / groups;
-  const int xbeg = grp_id * per;
-  const int xend = min(total, xbeg + per);
+  const int64_t per = (weighted_total(total, nv, a.seq_cost) + groups - 1) / groups;
+  const int xbeg = weighted_tile(s_tfirst, nv, total, a.seq_cost, grp_id * per);
+  const int xend = weighted_tile(s_tfirst, nv, total, a.seq_cost, (grp_id + 1) * per);
   if (xbeg >= xend) return;
 
   const int64_t row_stride = (int64_t)hkv * D;  // elements between token rows
@@ -814,8 +814,9 @@ __global__ __launch_bounds__(256) void decode_multi_reduce_kernel(MultiArgs a) {
   const int total = a.ws_sched[nv];
   const int t0 = a.ws_sched[v], t1 = a.ws_sched[v + 1];
   const int groups = mq_active_groups(a, total);
-  const int per = (total + groups - 1) / groups;
-  const int ga = t1 > t0 ? t0 / per : 0, gb = t1 > t0 ? (t1 - 1) / per : 0;
+  const int64_t per = (weighted_total(total, nv, a.seq_cost) + groups - 1) / groups;
+  const int64_t w0 = (int64_t)t0 + (int64_t)a.seq_cost * (v + 1);  // weighted position of tile 0
+  const int ga = t1 > t0 ? (int)(w0 / per) : 0, gb = t1 > t0 ? (int)((w0 + (t1 - t0) - 1) / per) : 0;
   if (t1 > t0 && ga == gb) return;  // written by the main kernel
   const int row0 = pass * a.pass_rows;
   const int row_end = min(a.rows, row0 + a.pass_rows);

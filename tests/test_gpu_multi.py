@@ -241,3 +241,23 @@ def test_more_sequences_than_one_launch_slice():
                                 case.dtype, case.block_size)
             assert_parity(single, ref, case.dtype)
         dc.close()
+
+
+@pytest.mark.parametrize("cost", [1, 4, 30])
+@pytest.mark.parametrize("pass_group", [1, 4])
+@pytest.mark.parametrize("shape", SHAPES[:5], ids=[f"s{i}" for i in range(5)])
+def test_multi_cost_weighted_ranges(shape, pass_group, cost):
+    """Stream-K ranges that weigh each (sequence, pass group) as `cost` extra
+    tiles: the oracle's result, repeated bit for bit, with short ranges so
+    that many pieces are merged."""
+    dtype, lens, q, hq, hkv, d, bs = shape
+    print(f"multi shape {shape} pass_group={pass_group} cost={cost}", flush=True)
+    case = workloads.make_multi_case("multi_shape", 7100 + len(lens) + q, dtype, lens, q, hq, hkv, d, bs)
+    dc = DeviceCase(case)
+    dc.write_all()
+    with options(PA_MULTI_SEQ_COST=cost + 1, PA_MULTI_PASS_GROUP=pass_group, PA_MULTI_MIN_RANGE=1):
+        out = _run(dc, case)
+        again = _run(dc, case)
+    assert_parity(out, _ref(case), dtype)
+    assert torch.equal(out.view(torch.int16), again.view(torch.int16))
+    dc.close()

@@ -13,7 +13,7 @@ import torch
 import oracle
 import paged_kv_cache_145_amd as pk
 import workloads
-from gpu_support import INT_VIEW, TORCH_DTYPES, DeviceCase, assert_parity, raw_to_torch, torch_bits
+from gpu_support import INT_VIEW, TORCH_DTYPES, DeviceCase, assert_parity, options, raw_to_torch, torch_bits
 
 pytestmark = pytest.mark.gpu
 
@@ -139,4 +139,19 @@ def test_ring_verify_rejects_a_short_rope_table():
     dc = DeviceCase(case)  # table holds only sink + window positions
     with pytest.raises(pk.PaError, match="INVAL"):
         _verify(dc, case)
+    dc.close()
+
+
+@pytest.mark.parametrize("cost", [2, 9])
+def test_ring_verify_cost_weighted_ranges(cost):
+    """Ring verification under cost-weighted stream-K ranges (short ranges,
+    so the edge lengths are cut and merged)."""
+    case = CASES[list(CASES)[0]]()
+    ref = _ref(case)
+    dc = DeviceCase(case, rope_extra=DRAFT_ROPE)
+    dc.write_all()
+    with options(PA_MULTI_SEQ_COST=cost + 1, PA_MULTI_MIN_RANGE=1):
+        out = _verify(dc, case)
+    assert_parity(out.reshape(case.num_seqs * case.q_len, case.num_q_heads, case.head_dim),
+                  ref.reshape(-1, case.num_q_heads, case.head_dim), case.dtype)
     dc.close()
