@@ -795,12 +795,21 @@ void decode_multi_kernel(MultiArgs a) {
 // Merge of the passes whose virtual sequence was cut by range boundaries:
 // out = sum_k w_k o_k / sum_k w_k, w_k = l_k 2^(m_k - max m), over the
 // groups k that covered it, in group order; virtual sequences with no tile
-// get zero rows.  A thread owns one row and four output dimensions.
+// get zero rows.  A thread owns one row and eight output dimensions (one
+// 16-byte load per segment), so a work-group covers 16 rows at D = 128 and
+// the grid of a verification batch fits the chip in one round.
+template <int D>
+struct MqMerge {
+  static constexpr int kPerThread = 8;             // output elements per thread
+  static constexpr int kThreadsPerRow = D / kPerThread;
+  static constexpr int kRowsPerBlock = 256 / kThreadsPerRow;
+};
+
 template <class T, int D>
 __global__ __launch_bounds__(256) void decode_multi_reduce_kernel(MultiArgs a) {
   typedef typename T::storage st;
-  constexpr int QPR = D / 4;      // threads per row
-  constexpr int RPB = 256 / QPR;  // rows per work-group
+  constexpr int QPR = MqMerge<D>::kThreadsPerRow;
+  constexpr int RPB = MqMerge<D>::kRowsPerBlock;
   const int bpv = (a.pass_rows + RPB - 1) / RPB;  // work-groups per (sequence, pass, head)
   const int rb = blockIdx.x % bpv;
   const int g = (blockIdx.x / bpv) % a.num_kv_heads;
@@ -821,10 +830,12 @@ __global__ __launch_bounds__(256) void decode_multi_reduce_kernel(MultiArgs a) {
   const int row0 = pass * a.pass_rows;
   const int row_end = min(a.rows, row0 + a.pass_rows);
   const int row = rb * RPB + (int)threadIdx.x / QPR;
-  const int q4 = (int)threadIdx.x % QPR;
+  const int q8 = (int)threadIdx.x % QPR;
   if (row0 + row >= row_end) return;  // no barriers follow
   float wsum = 0.f;
-  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  float acc[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) acc[e] = 0.f;
   if (t1 > t0) {
     // Segments k = ga..gb in windows of kWin: every (m, l) pair and row of a
     // window is requested before the first is used (one round trip per
@@ -837,20 +848,20 @@ __global__ __launch_bounds__(256) void decode_multi_reduce_kernel(MultiArgs a) {
     for (int k0 = ga; k0 <= gb; k0 += kWin) {
       const int cnt = min(kWin, gb - k0 + 1);
       float mk[kWin], lk[kWin];
-      // rows stay raw (four 16-bit values) until they are used, so that no
+      // rows stay raw (eight 16-bit values) until they are used, so that no
       // conversion waits on a load before the window's other loads issue
-      uint2 okr[kWin];
+      uint4 okr[kWin];
 #pragma unroll
       for (int u = 0; u < kWin; ++u) {
         if (u < cnt) {
           const int64_t r = r0 + (int64_t)(k0 - ga + u) * rstep;
           mk[u] = a.ws_ml[r * 2];
           lk[u] = a.ws_ml[r * 2 + 1];
-          okr[u] = reinterpret_cast<const uint2 *>(reinterpret_cast<const st *>(a.ws_o) + r * D)[q4];
+          okr[u] = reinterpret_cast<const uint4 *>(reinterpret_cast<const st *>(a.ws_o) + r * D)[q8];
         } else {
           mk[u] = -INFINITY;
           lk[u] = 0.f;
-          okr[u] = make_uint2(0u, 0u);
+          okr[u] = make_uint4(0u, 0u, 0u, 0u);
         }
       }
       float m_new = m_max;
@@ -859,10 +870,8 @@ __global__ __launch_bounds__(256) void decode_multi_reduce_kernel(MultiArgs a) {
       if (k0 > ga && m_new > m_max) {
         const float f = fast_exp2(m_max - m_new);
         wsum *= f;
-        acc.x *= f;
-        acc.y *= f;
-        acc.z *= f;
-        acc.w *= f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[e] *= f;
       }
       m_max = m_new;
 #pragma unroll
@@ -870,10 +879,8 @@ __global__ __launch_bounds__(256) void decode_multi_reduce_kernel(MultiArgs a) {
         if (u < cnt) {
           const float wk = lk[u] > 0.f ? lk[u] * fast_exp2(mk[u] - m_max) : 0.f;
           wsum += wk;
-          acc.x += wk * T::to_float((st)(okr[u].x & 0xffffu));
-          acc.y += wk * T::to_float((st)(okr[u].x >> 16));
-          acc.z += wk * T::to_float((st)(okr[u].y & 0xffffu));
-          acc.w += wk * T::to_float((st)(okr[u].y >> 16));
+#pragma unroll
+          for (int e = 0; e < 8; ++e) acc[e] += wk * T::to_float(half_of(okr[u], e));
         }
       }
     }
@@ -882,11 +889,10 @@ __global__ __launch_bounds__(256) void decode_multi_reduce_kernel(MultiArgs a) {
   const int rr = row0 + row;
   const int i = rr / a.group, h = rr - (rr / a.group) * a.group;
   st *out = static_cast<st *>(a.out) +
-            (((int64_t)b * a.q_len + i) * a.num_q_heads + (int64_t)g * a.group + h) * D + 4 * q4;
-  out[0] = T::from_float(acc.x * inv);
-  out[1] = T::from_float(acc.y * inv);
-  out[2] = T::from_float(acc.z * inv);
-  out[3] = T::from_float(acc.w * inv);
+            (((int64_t)b * a.q_len + i) * a.num_q_heads + (int64_t)g * a.group + h) * D + 8 * q8;
+  *reinterpret_cast<uint4 *>(out) =
+      make_uint4(T::pack_pair(acc[0] * inv, acc[1] * inv), T::pack_pair(acc[2] * inv, acc[3] * inv),
+                 T::pack_pair(acc[4] * inv, acc[5] * inv), T::pack_pair(acc[6] * inv, acc[7] * inv));
 }
 
 template <class T, int D, int MT, int KVF, int W, bool RING>
@@ -905,7 +911,7 @@ hipError_t launch_mt(const MultiArgs &a, int grid, hipStream_t stream) {
                        stream, a);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
-  constexpr int rpb = 256 / (D / 4);
+  constexpr int rpb = MqMerge<D>::kRowsPerBlock;
   const int bpv = (a.pass_rows + rpb - 1) / rpb;
   hipLaunchKernelGGL((decode_multi_reduce_kernel<T, D>),
                      dim3((unsigned)(a.num_seqs * a.passes * a.num_kv_heads * bpv)), dim3(256), 0, stream, a);
