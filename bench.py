@@ -193,7 +193,7 @@ TIMELINE_TICK_US = 0.01  # s_memrealtime runs at 100 MHz
 TIMELINE_RECORDS = []  # raw records of each call, for callers that analyse them further
 
 
-def wave_timeline(torch, dev, decode, ws, ws_bytes: int, calls: int, config: str, fused: bool) -> dict:
+def wave_timeline(torch, dev, decode, ws, ws_bytes: int, calls: int, config: str, kernel: str) -> dict:
     """Per-wave timeline of ``calls`` decode calls on the measurement build:
     when the waves enter, have the tile schedule, consume their first tile
     and end streaming, per XCD, and when the combine kernel's waves enter
@@ -281,8 +281,7 @@ def wave_timeline(torch, dev, decode, ws, ws_bytes: int, calls: int, config: str
             "combine_gap_us": med(rows, "combine", "gap_after_last_stream_end_us"),
             "merge_end_max_us": med(rows, "combine", "merge_end_max_us"),
         }
-    return {"timeline": config, "kernel": "decode_mfma_kernel" + (" (append variant)" if fused else "") +
-            " + decode_streamk_reduce_kernel, measurement build (PA_WAVE_TIMELINE)",
+    return {"timeline": config, "kernel": kernel + ", measurement build (PA_WAVE_TIMELINE)",
             "clock": "s_memrealtime, 100 MHz, microseconds from the first wave's entry",
             "summary": summary, "calls": per_call}
 
@@ -627,6 +626,11 @@ def measure_multi(args) -> int:
     for _ in range(args.warmup):
         call()
     torch.cuda.synchronize()
+    if args.timeline > 0:
+        print(json.dumps(wave_timeline(torch, dev, call, ws, ws.numel(), args.timeline, args.config,
+                                       kernel="decode_multi_kernel + decode_multi_reduce_kernel")), flush=True)
+        pool.close()
+        return 0
     t0 = time.perf_counter()
     mean_us, med_us = _event_us(torch, call, args.steps)
     wall = time.perf_counter() - t0
@@ -876,7 +880,8 @@ def main() -> int:
                          "batching: the continuous-batching driver looping over schedule, writes and decode")
     ap.add_argument("--timeline", type=int, default=0, metavar="CALLS",
                     help="load the measurement build and print the per-wave timeline of this many decode "
-                         "calls (half after a 1 GiB scrub, half back to back) instead of timing steps")
+                         "calls (half after a 1 GiB scrub, half back to back) instead of timing steps "
+                         "(single-token decode, or --measure multi)")
     ap.add_argument("--traffic-command", default="",
                     help="the profiling command line recorded with --write-traffic")
     args = ap.parse_args()
@@ -904,8 +909,8 @@ def main() -> int:
         print("bench.py needs a GPU", file=sys.stderr)
         return 2
     if args.timeline > 0:
-        if args.measure != "decode":
-            print("--timeline covers the single-token decode", file=sys.stderr)
+        if args.measure not in ("decode", "multi"):
+            print("--timeline covers the single- and multi-token decode", file=sys.stderr)
             return 2
         _lib.use_timeline_build()
     _lib.load()
@@ -998,7 +1003,9 @@ def main() -> int:
             return 2
         for _ in range(args.warmup):
             decode()
-        print(json.dumps(wave_timeline(torch, dev, decode, ws, ws_bytes, args.timeline, args.config, fused)),
+        kernel = ("decode_mfma_kernel" + (" (append variant)" if fused else "") +
+                  " + decode_streamk_reduce_kernel")
+        print(json.dumps(wave_timeline(torch, dev, decode, ws, ws_bytes, args.timeline, args.config, kernel)),
               flush=True)
         pool.close()
         return 0

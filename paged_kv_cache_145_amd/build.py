@@ -19,10 +19,11 @@ BUILD_DIR = os.path.join(ROOT, "_build")
 LIB_NAME = "libpa_mi355x.so"
 LIB_PATH = os.path.join(PKG, LIB_NAME)
 # Measurement build: the same library with per-wave timeline stamps in the
-# stream-K decode (PA_WAVE_TIMELINE); only `bench.py --timeline` loads it.
+# stream-K decode kernels (PA_WAVE_TIMELINE); only `bench.py --timeline`
+# loads it.
 TIMELINE_LIB_NAME = "libpa_mi355x_timeline.so"
 TIMELINE_LIB_PATH = os.path.join(PKG, TIMELINE_LIB_NAME)
-TIMELINE_SOURCES = ["decode_kernels.hip", "api.hip"]  # the files the define changes
+TIMELINE_SOURCES = ["decode_kernels.hip", "multi_kernels.hip", "api.hip"]  # the files the define changes
 
 HIP_SOURCES = ["decode_kernels.hip", "multi_kernels.hip", "write_kernels.hip", "api.hip"]
 CPP_SOURCES = ["pool.cpp", "prefix.cpp", "batching.cpp"]

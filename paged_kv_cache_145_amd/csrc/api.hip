@@ -147,6 +147,9 @@ MultiLayout multi_layout(const pa_pool *pool, int32_t num_seqs, int32_t q_len, i
   m.ml_bytes = round_up(rows_total * 2 * sizeof(float), 256);
   m.o_bytes = round_up(rows_total * pool->head_dim * sizeof(float), 256);
   m.total = m.sched_bytes + m.ml_bytes + m.o_bytes;
+#ifdef PA_WAVE_TIMELINE
+  m.total += kTimelineBytes;  // measurement build: per-wave records after the partials
+#endif
   return m;
 }
 
@@ -200,6 +203,9 @@ int multi_impl(pa_pool *pool, void *out, const void *query, const void *draft_k,
   a.ws_sched = reinterpret_cast<int32_t *>(ws);
   a.ws_ml = reinterpret_cast<float *>(ws + m.sched_bytes);
   a.ws_o = reinterpret_cast<float *>(ws + m.sched_bytes + m.ml_bytes);
+#ifdef PA_WAVE_TIMELINE
+  a.timeline = reinterpret_cast<uint64_t *>(ws + m.sched_bytes + m.ml_bytes + m.o_bytes);
+#endif
   a.kv_block_stride = (int64_t)pool->block_size * pool->num_kv_heads * pool->head_dim;
   a.num_blocks = pool->num_blocks;
   a.max_context = max_context_len;

@@ -39,13 +39,6 @@ namespace {
 
 constexpr int kNW = kDecodeWaves;
 
-#ifdef PA_WAVE_TIMELINE
-// Measurement build only: the real-time counter (100 MHz, the same on every
-// XCD) and the XCC id of the executing wave (hardware register XCC_ID, bits
-// 3:0).
-__device__ __forceinline__ uint64_t tl_now() { return __builtin_amdgcn_s_memrealtime(); }
-__device__ __forceinline__ uint64_t tl_xcc() { return (uint64_t)(__builtin_amdgcn_s_getreg((3 << 11) | 20) & 15); }
-#endif
 // A new tile maximum must exceed the running reference by this many log2
 // units before the accumulators are rescaled; weights stay <= 2^8.
 constexpr float kRescaleSlack = 8.0f;

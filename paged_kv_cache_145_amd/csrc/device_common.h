@@ -254,6 +254,14 @@ __device__ __forceinline__ uint2 fp8x4_to_16(uint32_t v) {
   return make_uint2(code_pair_to_16<T, F, false>(v), code_pair_to_16<T, F, true>(v));
 }
 
+#ifdef PA_WAVE_TIMELINE
+// Measurement build only: the real-time counter (100 MHz, the same on every
+// XCD) and the XCC id of the executing wave (hardware register XCC_ID, bits
+// 3:0).
+__device__ __forceinline__ uint64_t tl_now() { return __builtin_amdgcn_s_memrealtime(); }
+__device__ __forceinline__ uint64_t tl_xcc() { return (uint64_t)(__builtin_amdgcn_s_getreg((3 << 11) | 20) & 15); }
+#endif
+
 // Cost-weighted stream-K ranges (single- and multi-token decode).  Sequence
 // (or virtual sequence) b weighs its tiles plus `cost` tiles' worth of work
 // for its start and end, so the weighted position of its tile t is W(b) + cost + t with W(b) = s_tfirst[b] + cost * b (strictly

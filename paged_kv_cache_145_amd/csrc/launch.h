@@ -72,7 +72,7 @@ struct DecodeArgs {
   uint64_t *timeline;  // measurement build only (PA_WAVE_TIMELINE), else null and unused
 };
 
-// Per-wave timeline of the stream-K decode, compiled only into the
+// Per-wave timeline of the stream-K decode (single- and multi-token), compiled only into the
 // measurement library (PA_WAVE_TIMELINE; the product library has none of
 // it).  The records sit after the workspace's other parts:
 //   main kernel, wave gw < kTimelineWaves: 8 uint64 at gw * 8:
@@ -120,6 +120,7 @@ struct MultiArgs {
   int32_t groups;     // wave groups (Hkv * pass_group waves each) of the grid
   int32_t min_range_tiles;
   int32_t seq_cost;   // extra cost of a (sequence, pass group) in its range, in tiles
+  uint64_t *timeline;  // measurement build only (PA_WAVE_TIMELINE), else null and unused
   int32_t block_shift;
   float scale_log2;
   KvScales kv_scale;  // 8-bit pools: dequantisation scales per KV head

@@ -251,7 +251,15 @@ void decode_multi_kernel(MultiArgs a) {
   __shared__ uint4 s_q[SH ? 1 : kMqWaves][SH ? 1 : kQCopies * kMqQSlots * QF * kWave];  // query fragments, lane-major
 
   const int nv = a.num_seqs * a.pgroups;
+#ifdef PA_WAVE_TIMELINE
+  const uint64_t tl_entry = tl_now();
+#endif
   const int total = mq_schedule(a, s_tfirst, s_kvend, s_wsum, RING);
+#ifdef PA_WAVE_TIMELINE
+  const uint64_t tl_sched = tl_now();
+  uint64_t tl_first = 0;
+  int tl_segs = 0;
+#endif
   const int hkv = a.num_kv_heads, G = a.group, ql = a.q_len, PG = a.pass_group;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -314,6 +322,10 @@ void decode_multi_kernel(MultiArgs a) {
   auto rd = [&](int x, int j) { return __builtin_amdgcn_readlane(x, j); };
   int tv = 0, tt = 0, tvalid = 0, tflag = 0, toff_lo = 0, toff_hi = 0, tnrec = 0, tslot = 0;
   int c0 = 0, cnt = 0;
+  // query fragments of the staged chunk's opening tiles, between their loads
+  // (stage) and their LDS stores (stage_lds)
+  uint4 qtmp[kMqQSlots][QF];
+  uint4 qsink[RING ? kMqQSlots : 1][RING ? QF : 1];
   auto stage = [&](int start) {
     c0 = start;
     cnt = min(kWave, xend - start);
@@ -351,8 +363,6 @@ void decode_multi_kernel(MultiArgs a) {
       m &= (1ull << cnt) - 1;
     }
     tslot = opens && lane < cnt ? __popcll(m & ((1ull << lane) - 1)) : 0;
-    uint4 qtmp[kMqQSlots][QF];
-    uint4 qsink[RING ? kMqQSlots : 1][RING ? QF : 1];
     unsigned long long mm = m;
 #pragma unroll
     for (int s2 = 0; s2 < kMqQSlots; ++s2) {
@@ -402,6 +412,10 @@ void decode_multi_kernel(MultiArgs a) {
       toff_hi = (int)(off >> 32);
       tnrec = (int)(((tvalid - 1) * row_stride + D) * (int64_t)KVB);  // tvalid >= 1 here
     }
+  };
+  // The staged query fragments go to LDS after the chunk's first tile loads
+  // have been issued, so those loads overlap the query's arrival.
+  auto stage_lds = [&]() {
     if constexpr (!SH) {
 #pragma unroll
       for (int s2 = 0; s2 < kMqQSlots; ++s2)
@@ -729,7 +743,29 @@ void decode_multi_kernel(MultiArgs a) {
     const int v = rd(tv, j), flag = rd(tflag, j);
     if ((flag & 1) || c0 + j == xbeg) begin_segment(j, v, (flag & 1) != 0);
     process_tile(j, kc, vc);
+#ifdef PA_WAVE_TIMELINE
+    if (tl_first == 0) tl_first = tl_now();
+    tl_segs += ((flag & 1) || c0 + j == xbeg) ? 1 : 0;
+#endif
     if ((flag & 2) || c0 + j == xend - 1) end_segment(v, (flag & 2) != 0);
+  };
+
+  // measurement build: this wave's timeline record
+  auto tl_finish = [&]() {
+#ifdef PA_WAVE_TIMELINE
+    const uint64_t tl_end = tl_now();
+    if (lane == 0 && a.timeline != nullptr && gw < kTimelineWaves) {
+      uint64_t *r = a.timeline + (int64_t)gw * 8;
+      r[0] = tl_entry;
+      r[1] = tl_sched;
+      r[2] = tl_first;
+      r[3] = tl_end;
+      r[4] = ((uint64_t)(xend - xbeg) << 32) | (uint32_t)tl_segs;
+      r[5] = tl_xcc();
+      r[6] = 1;
+      r[7] = blockIdx.x;
+    }
+#endif
   };
 
   // S register buffers: tile j is consumed from buffer j % S while the next
@@ -762,6 +798,7 @@ void decode_multi_kernel(MultiArgs a) {
     };
     for (int start = xbeg; start < xend; start += cnt) {
       stage(start);  // sets cnt
+      stage_lds();
       __syncthreads();  // the previous chunk's tiles are consumed
       dma_tile(0, s_kv);
       dma_tile(1, s_kv + kShBuf);
@@ -773,6 +810,7 @@ void decode_multi_kernel(MultiArgs a) {
         sh_step(j + 3, 3, 2);
       }
     }
+    tl_finish();
     return;
   }
   constexpr int S = kMqStagesFor<W, MT>;
@@ -782,6 +820,7 @@ void decode_multi_kernel(MultiArgs a) {
     stage(start);  // sets cnt
 #pragma unroll
     for (int u = 0; u < S - 1; ++u) load_tile(u, kbuf[u], vbuf[u]);
+    stage_lds();
     for (int j = 0; j < cnt; j += S) {
 #pragma unroll
       for (int u = 0; u < S; ++u) {
@@ -790,6 +829,7 @@ void decode_multi_kernel(MultiArgs a) {
       }
     }
   }
+  tl_finish();
 }
 
 // Merge of the passes whose virtual sequence was cut by range boundaries:
@@ -811,6 +851,13 @@ __global__ __launch_bounds__(256) void decode_multi_reduce_kernel(MultiArgs a) {
   constexpr int QPR = MqMerge<D>::kThreadsPerRow;
   constexpr int RPB = MqMerge<D>::kRowsPerBlock;
   const int bpv = (a.pass_rows + RPB - 1) / RPB;  // work-groups per (sequence, pass, head)
+#ifdef PA_WAVE_TIMELINE
+  const int64_t tl_cw = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  uint64_t *tl_rec = (a.timeline != nullptr && tl_cw < kTimelineCombineWaves)
+                         ? a.timeline + (int64_t)kTimelineWaves * 8 + tl_cw * 2
+                         : nullptr;
+  if (tl_rec != nullptr && (threadIdx.x & 63) == 0) tl_rec[0] = tl_now();
+#endif
   const int rb = blockIdx.x % bpv;
   const int g = (blockIdx.x / bpv) % a.num_kv_heads;
   const int bp = blockIdx.x / (bpv * a.num_kv_heads);  // b * passes + pass
@@ -893,6 +940,9 @@ __global__ __launch_bounds__(256) void decode_multi_reduce_kernel(MultiArgs a) {
   *reinterpret_cast<uint4 *>(out) =
       make_uint4(T::pack_pair(acc[0] * inv, acc[1] * inv), T::pack_pair(acc[2] * inv, acc[3] * inv),
                  T::pack_pair(acc[4] * inv, acc[5] * inv), T::pack_pair(acc[6] * inv, acc[7] * inv));
+#ifdef PA_WAVE_TIMELINE
+  if (tl_rec != nullptr && (threadIdx.x & 63) == 0) tl_rec[1] = tl_now() | (1ull << 63);
+#endif
 }
 
 template <class T, int D, int MT, int KVF, int W, bool RING>
