@@ -567,6 +567,10 @@ const char *pa_last_hip_error(void);
  *                            16-token tiles, plus one (1: none)
  *   PA_OPT_MULTI_SEQ_COST    multi-token decode: the same for a (sequence,
  *                            pass group), plus one (1: none)
+ *   PA_OPT_YOUNG_SHARE       stream-K kernels that run two work-groups per
+ *                            CU: range size of the second work-group of a
+ *                            CU relative to the first, in thousandths
+ *                            (1000: equal)
  * Options change the kernel choice and the workspace size: set them before
  * pa_*_workspace_bytes and keep them until the matching call has been
  * enqueued.  pa_set_option returns PA_ERR_INVAL for an unknown option or a
@@ -580,7 +584,8 @@ typedef enum {
   PA_OPT_MULTI_MIN_RANGE = 5,
   PA_OPT_DECODE_SEQ_COST = 6,
   PA_OPT_MULTI_SEQ_COST = 7,
-  PA_OPT_COUNT = 8
+  PA_OPT_YOUNG_SHARE = 8,
+  PA_OPT_COUNT = 9
 } pa_option;
 int pa_set_option(pa_option opt, int32_t value);
 int32_t pa_get_option(pa_option opt);

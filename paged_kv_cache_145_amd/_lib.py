@@ -34,7 +34,7 @@ class PaPrefixStats(ctypes.Structure):
 # kernel-configuration overrides (pa_set_option), for tests and measurements
 PA_OPTIONS = {"PA_FORCE_VALU": 0, "PA_PARTITION_TOKENS": 1, "PA_MULTI_WAVES": 2, "PA_MULTI_ROW_TILES": 3,
               "PA_MULTI_PASS_GROUP": 4, "PA_MULTI_MIN_RANGE": 5, "PA_DECODE_SEQ_COST": 6,
-              "PA_MULTI_SEQ_COST": 7}
+              "PA_MULTI_SEQ_COST": 7, "PA_YOUNG_SHARE": 8}
 
 PA_PREFIX_TAIL = 1
 PA_PREFIX_RESIDENT = 2

@@ -49,7 +49,8 @@ struct OptionInit {
     static const char *const names[PA_OPT_COUNT] = {"PA_FORCE_VALU",      "PA_PARTITION_TOKENS",
                                                     "PA_MULTI_WAVES",     "PA_MULTI_ROW_TILES",
                                                     "PA_MULTI_PASS_GROUP", "PA_MULTI_MIN_RANGE",
-                                                    "PA_DECODE_SEQ_COST", "PA_MULTI_SEQ_COST"};
+                                                    "PA_DECODE_SEQ_COST", "PA_MULTI_SEQ_COST",
+                                                    "PA_YOUNG_SHARE"};
     for (int i = 0; i < PA_OPT_COUNT; ++i) g_options[i].store(env_int(names[i], 0));
   }
 } g_option_init;
@@ -220,6 +221,18 @@ int multi_impl(pa_pool *pool, void *out, const void *query, const void *draft_k,
   a.pass_group = m.pass_group;
   a.pgroups = m.pgroups;
   a.groups = m.groups;
+  // With two work-groups per CU, the groups past the first work-group of
+  // every CU run second on their CU (their waves issue behind the first
+  // work-group's) and get 0.8 of the others' ranges: chunked prefill
+  // 176.1 -> 168.8 us, E4M3 verification 67.0 -> 65.2 us (0.9: 172.9 /
+  // 66.0, 0.7: 173.5 / 65.4, 0.6: 181.2 / 67.8).
+  {
+    const int wpg = pool->num_kv_heads * m.pass_group;  // waves per group
+    const int cus = pa::multi_grid();
+    a.young_from = m.grid > cus ? (int)pa::ceil_div((int64_t)cus * 4, wpg) : m.groups;
+    const int forced_share = pa::option(PA_OPT_YOUNG_SHARE);
+    a.young_share = forced_share >= 1 ? std::min(1024, forced_share * 1024 / 1000) : 819;
+  }
   const int forced_range = pa::option(PA_OPT_MULTI_MIN_RANGE);
   a.min_range_tiles = forced_range >= 1 ? forced_range : 4;
   // Stream-K ranges weigh each (sequence, pass group) as this many extra
@@ -521,6 +534,11 @@ int decode_impl(pa_pool *pool, void *out, const void *query, const int32_t *bloc
   // (costs 4-6 equal, 9 worse), 16-bit pools 74.1 -> 73.7 us at 1.
   const int forced_cost = pa::option(PA_OPT_DECODE_SEQ_COST);
   a.seq_cost = forced_cost >= 1 ? forced_cost - 1 : pool->kv_fp8 ? 5 : 1;
+  // two work-groups per CU (8-bit pools): the second one's share of a range
+  // (memory-bound there: 0.9-0.95 measured no faster than equal ranges)
+  const int forced_share = pa::option(PA_OPT_YOUNG_SHARE);
+  a.young_share = forced_share >= 1 ? std::min(1024, forced_share * 1024 / 1000) : 1024;
+  a.young_from = INT32_MAX;  // set by the launcher, which knows the grid
   a.ring_sink = ring ? ring->sink : 0;
   a.ring_window = ring ? ring->window : 1;
   a.scale_log2 = scale * pa::kLog2eHost;

@@ -415,9 +415,9 @@ void decode_mfma_kernel(DecodeArgs a) {
   const int grp_id = gw / hkv;  // tile range of this wave
   const int g = gw - grp_id * hkv;  // KV head of this wave
   if (grp_id >= groups) return;
-  const int64_t per = (weighted_total(total, a.num_seqs, a.seq_cost) + groups - 1) / groups;
-  const int xbeg = weighted_tile(s_tfirst, a.num_seqs, total, a.seq_cost, grp_id * per);
-  const int xend = weighted_tile(s_tfirst, a.num_seqs, total, a.seq_cost, (grp_id + 1) * per);
+  const RangeSplit rs = range_split(weighted_total(total, a.num_seqs, a.seq_cost), groups, a.young_from, a.young_share);
+  const int xbeg = weighted_tile(s_tfirst, a.num_seqs, total, a.seq_cost, range_start(rs, grp_id));
+  const int xend = weighted_tile(s_tfirst, a.num_seqs, total, a.seq_cost, range_start(rs, grp_id + 1));
   if (xbeg >= xend) return;  // no barriers follow
   const int hq0 = g * G;
   const int64_t head_off = (int64_t)g * D;
@@ -835,9 +835,9 @@ __global__ __launch_bounds__(256) void decode_streamk_reduce_kernel(DecodeArgs a
     return;
   }
   const int active = active_groups(a, total, groups);
-  const int64_t per = (weighted_total(total, a.num_seqs, a.seq_cost) + active - 1) / active;
+  const RangeSplit rs = range_split(weighted_total(total, a.num_seqs, a.seq_cost), active, a.young_from, a.young_share);
   const int64_t w0 = (int64_t)t0 + (int64_t)a.seq_cost * (b + 1);  // weighted position of tile 0
-  const int q_lo = (int)(w0 / per), q_hi = (int)((w0 + (t1 - t0) - 1) / per);
+  const int q_lo = range_of(rs, w0), q_hi = range_of(rs, w0 + (t1 - t0) - 1);
   if (q_lo == q_hi) return;
   const int nseg = q_hi - q_lo + 1;
   const int64_t slot0 = ((int64_t)q_lo + b) * hkv + g;  // slot of segment s: slot0 + s * hkv
@@ -1193,16 +1193,21 @@ hipError_t launch_typed(const DecodeArgs &a, DecodeChoice choice, hipStream_t st
   if constexpr (T::kBytes == 2) {
     if (choice.kernel == DecodeKernel::kMfma) {
       const int grid = mfma_grid<T, D, RING, KVF>(a.num_kv_heads);
-      if (a.app_key != nullptr) {
-        hipLaunchKernelGGL((decode_mfma_kernel<T, D, RING, KVF, true>), dim3(grid), block, 0, stream, a);
+      // groups whose first wave lies past the first work-group of every CU
+      // run second on their CU
+      DecodeArgs b = a;
+      const int cus = multi_grid();
+      b.young_from = grid > cus ? (cus * kNW + b.num_kv_heads - 1) / b.num_kv_heads : INT32_MAX;
+      if (b.app_key != nullptr) {
+        hipLaunchKernelGGL((decode_mfma_kernel<T, D, RING, KVF, true>), dim3(grid), block, 0, stream, b);
       } else {
-        hipLaunchKernelGGL((decode_mfma_kernel<T, D, RING, KVF>), dim3(grid), block, 0, stream, a);
+        hipLaunchKernelGGL((decode_mfma_kernel<T, D, RING, KVF>), dim3(grid), block, 0, stream, b);
       }
       hipError_t err = hipGetLastError();
       if (err != hipSuccess) return err;
       hipLaunchKernelGGL((decode_streamk_reduce_kernel<T, D>),
-                         dim3((a.group + kNW - 1) / kNW, a.num_kv_heads, a.num_seqs), block, 0, stream,
-                         a, (grid * kNW) / a.num_kv_heads);
+                         dim3((b.group + kNW - 1) / kNW, b.num_kv_heads, b.num_seqs), block, 0, stream,
+                         b, (grid * kNW) / b.num_kv_heads);
       return hipGetLastError();
     }
   }

@@ -274,6 +274,44 @@ __device__ __forceinline__ int64_t weighted_total(int total, int num_seqs, int c
   return (int64_t)total + (int64_t)cost * num_seqs;
 }
 
+// Range sizes when a kernel runs two work-groups per CU.  Work-groups are
+// dispatched in index order, one per CU first, so the groups q >= young_from
+// (the second work-group of their CU) issue behind the first one and stream
+// more slowly; their ranges are young_share / 1024 of the others'.  Group q
+// covers weighted positions [range_start(q), range_start(q + 1)); every
+// boundary still depends only on the lengths, the costs and the grid.
+struct RangeSplit {
+  int64_t per, per_young;
+  int young_from;
+};
+
+__device__ __forceinline__ RangeSplit range_split(int64_t wtotal, int groups, int young_from, int young_share) {
+  RangeSplit r;
+  r.young_from = min(max(young_from, 0), groups);
+  const int ny = groups - r.young_from;
+  if (ny == 0 || young_share >= 1024 || young_share <= 0) {
+    r.per = (wtotal + groups - 1) / groups;
+    r.per_young = r.per;
+    r.young_from = groups;
+  } else {
+    const int64_t den = (int64_t)r.young_from * 1024 + (int64_t)ny * young_share;
+    r.per = max((int64_t)1, (wtotal * 1024 + den - 1) / den);
+    r.per_young = max((int64_t)1, (r.per * young_share + 1023) / 1024);
+  }
+  return r;
+}
+
+__device__ __forceinline__ int64_t range_start(const RangeSplit &r, int q) {
+  return q <= r.young_from ? (int64_t)q * r.per
+                           : (int64_t)r.young_from * r.per + (int64_t)(q - r.young_from) * r.per_young;
+}
+
+// The group whose range holds weighted position x.
+__device__ __forceinline__ int range_of(const RangeSplit &r, int64_t x) {
+  const int64_t yo = (int64_t)r.young_from * r.per;
+  return x < yo ? (int)(x / r.per) : r.young_from + (int)((x - yo) / r.per_young);
+}
+
 // First tile whose weighted position is >= target (total if none).
 __device__ __forceinline__ int weighted_tile(const int *s_tfirst, int num_seqs, int total, int cost,
                                              int64_t target) {

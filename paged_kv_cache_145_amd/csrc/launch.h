@@ -64,6 +64,8 @@ struct DecodeArgs {
   int32_t max_parts;
   int32_t min_range_tiles;  // MFMA kernel: shortest stream-K range worth a group
   int32_t seq_cost;         // MFMA kernel: extra cost of a sequence in its range, in tiles
+  int32_t young_from;       // MFMA kernel: first group run as its CU's second work-group
+  int32_t young_share;      // MFMA kernel: their range size relative to the others, / 1024
   int32_t ring_sink;
   int32_t ring_window;
   float scale_log2;  // scale * log2(e)
@@ -120,6 +122,8 @@ struct MultiArgs {
   int32_t groups;     // wave groups (Hkv * pass_group waves each) of the grid
   int32_t min_range_tiles;
   int32_t seq_cost;   // extra cost of a (sequence, pass group) in its range, in tiles
+  int32_t young_from;  // first group run as its CU's second work-group (W = 2)
+  int32_t young_share; // their range size relative to the others, / 1024
   uint64_t *timeline;  // measurement build only (PA_WAVE_TIMELINE), else null and unused
   int32_t block_shift;
   float scale_log2;

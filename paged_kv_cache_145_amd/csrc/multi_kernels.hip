@@ -46,6 +46,7 @@
 //   through a per-wave LDS tile and returns as B operands through
 //   transposing LDS reads, shared by the MT row tiles.
 #include <algorithm>
+#include <atomic>
 #include <type_traits>
 
 #include "device_common.h"
@@ -271,9 +272,9 @@ void decode_multi_kernel(MultiArgs a) {
   const int g = within / PG;           // KV head of this wave
   const int w = within - g * PG;       // pass of each pass group
   if (grp_id >= groups) return;        // no barriers follow
-  const int64_t per = (weighted_total(total, nv, a.seq_cost) + groups - 1) / groups;
-  const int xbeg = weighted_tile(s_tfirst, nv, total, a.seq_cost, grp_id * per);
-  const int xend = weighted_tile(s_tfirst, nv, total, a.seq_cost, (grp_id + 1) * per);
+  const RangeSplit rs = range_split(weighted_total(total, nv, a.seq_cost), groups, a.young_from, a.young_share);
+  const int xbeg = weighted_tile(s_tfirst, nv, total, a.seq_cost, range_start(rs, grp_id));
+  const int xend = weighted_tile(s_tfirst, nv, total, a.seq_cost, range_start(rs, grp_id + 1));
   if (xbeg >= xend) return;
 
   const int64_t row_stride = (int64_t)hkv * D;  // elements between token rows
@@ -870,9 +871,9 @@ __global__ __launch_bounds__(256) void decode_multi_reduce_kernel(MultiArgs a) {
   const int total = a.ws_sched[nv];
   const int t0 = a.ws_sched[v], t1 = a.ws_sched[v + 1];
   const int groups = mq_active_groups(a, total);
-  const int64_t per = (weighted_total(total, nv, a.seq_cost) + groups - 1) / groups;
+  const RangeSplit rs = range_split(weighted_total(total, nv, a.seq_cost), groups, a.young_from, a.young_share);
   const int64_t w0 = (int64_t)t0 + (int64_t)a.seq_cost * (v + 1);  // weighted position of tile 0
-  const int ga = t1 > t0 ? (int)(w0 / per) : 0, gb = t1 > t0 ? (int)((w0 + (t1 - t0) - 1) / per) : 0;
+  const int ga = t1 > t0 ? range_of(rs, w0) : 0, gb = t1 > t0 ? range_of(rs, w0 + (t1 - t0) - 1) : 0;
   if (t1 > t0 && ga == gb) return;  // written by the main kernel
   const int row0 = pass * a.pass_rows;
   const int row_end = min(a.rows, row0 + a.pass_rows);
@@ -1012,9 +1013,16 @@ hipError_t launch_t(const MultiArgs &a, int head_dim, int kv8, int mt, int waves
 int multi_grid() {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) dev = 0;
+  static std::atomic<int> cached[64];  // CU count per device, looked up once
+  const bool slot = dev >= 0 && dev < 64;
+  if (slot) {
+    const int c = cached[dev].load(std::memory_order_relaxed);
+    if (c > 0) return c;
+  }
   int cus = 0;
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
     cus = 256;
+  if (slot) cached[dev].store(cus, std::memory_order_relaxed);
   return cus;
 }
 

@@ -212,3 +212,23 @@ def test_fp8_decode_cost_weighted_ranges(name, cost):
     assert_parity(out, ref, case.dtype)
     assert np.array_equal(torch_bits(out, case.dtype), torch_bits(again, case.dtype))
     dc.close()
+
+
+@pytest.mark.parametrize("share", [400, 900])
+def test_fp8_decode_young_share_ranges(share):
+    """8-bit pools run two work-groups per CU; the second one's shorter
+    ranges give the oracle's result, repeated bit for bit, also on ragged
+    lengths with empty sequences."""
+    for case in (_case("llama70b_b64_fp8"),
+                 workloads.config_fp8(lambda: workloads.make_paged_case("young", 8800, "bf16",
+                                                                        [0, 1, 17, 300, 0, 5000, 2], 32, 4,
+                                                                        128, 16))):
+        dc = DeviceCase(case)
+        dc.write_all()
+        with options(PA_YOUNG_SHARE=share, PA_DECODE_SEQ_COST=4):
+            out = dc.decode()
+            again = dc.decode()
+        _, _, _, ref = oracle_reference(case)
+        assert_parity(out, ref, case.dtype)
+        assert np.array_equal(torch_bits(out, case.dtype), torch_bits(again, case.dtype))
+        dc.close()

@@ -261,3 +261,35 @@ def test_multi_cost_weighted_ranges(shape, pass_group, cost):
     assert_parity(out, _ref(case), dtype)
     assert torch.equal(out.view(torch.int16), again.view(torch.int16))
     dc.close()
+
+
+@pytest.mark.parametrize("share", [300, 700, 950])
+@pytest.mark.parametrize("shape", SHAPES[:5], ids=[f"s{i}" for i in range(5)])
+def test_multi_young_share_ranges(shape, share):
+    """Two waves per SIMD (two work-groups per CU) with the second
+    work-group's ranges shortened: the oracle's result, repeated bit for
+    bit."""
+    dtype, lens, q, hq, hkv, d, bs = shape
+    print(f"multi shape {shape} young share {share}", flush=True)
+    case = workloads.make_multi_case("multi_shape", 7100 + len(lens) + q, dtype, lens, q, hq, hkv, d, bs)
+    dc = DeviceCase(case)
+    dc.write_all()
+    with options(PA_YOUNG_SHARE=share, PA_MULTI_WAVES=2, PA_MULTI_MIN_RANGE=1):
+        out = _run(dc, case)
+        again = _run(dc, case)
+    assert_parity(out, _ref(case), dtype)
+    assert torch.equal(out.view(torch.int16), again.view(torch.int16))
+    dc.close()
+
+
+@pytest.mark.parametrize("share", [500, 850])
+def test_chunked_prefill_young_share(share):
+    case = workloads.config_chunked_prefill()
+    print(f"chunked prefill young share {share}", flush=True)
+    dc = DeviceCase(case)
+    dc.write_all()
+    with options(PA_YOUNG_SHARE=share):
+        out = _run(dc, case)
+    ref = _ref(case)
+    assert_parity(out, ref, case.dtype)
+    dc.close()
