@@ -238,10 +238,12 @@ int multi_impl(pa_pool *pool, void *out, const void *query, const void *draft_k,
   // Stream-K ranges weigh each (sequence, pass group) as this many extra
   // tiles (staging its query rows, writing its output or partial rows).
   // Measured: verification of the 70B-shaped batch 101.7 -> 93.5 us at 6
-  // (4: 94.6, 12: 96.9), E4M3 pools 80.5 -> 67.5 us at 8, chunked prefill
-  // 211.6 -> 181.0 us at 6, ring verification 36.1 -> 33.6 us.
+  // (4: 94.6, 12: 96.9), chunked prefill 211.6 -> 181.0 us, ring
+  // verification 36.1 -> 33.6 us; with the later kernels costs 5-8 are
+  // within noise for both, and E4M3 verification takes 63.6 us at 6
+  // against 65.9 at 8.
   const int forced_cost = pa::option(PA_OPT_MULTI_SEQ_COST);
-  a.seq_cost = forced_cost >= 1 ? forced_cost - 1 : pool->kv_fp8 ? 8 : 6;
+  a.seq_cost = forced_cost >= 1 ? forced_cost - 1 : 6;
   a.block_shift = pa::log2_exact(pool->block_size);
   a.scale_log2 = scale * pa::kLog2eHost;
   if (ring != nullptr) {
