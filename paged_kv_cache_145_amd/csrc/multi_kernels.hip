@@ -837,13 +837,17 @@ void decode_multi_kernel(MultiArgs a) {
 // out = sum_k w_k o_k / sum_k w_k, w_k = l_k 2^(m_k - max m), over the
 // groups k that covered it, in group order; virtual sequences with no tile
 // get zero rows.  A thread owns one row and eight output dimensions (one
-// 16-byte load per segment), so a work-group covers 16 rows at D = 128 and
-// the grid of a verification batch fits the chip in one round.
+// 16-byte load per segment), so a work-group covers a block of 16 rows at
+// D = 128.  The grid holds as many work-groups as the CUs keep resident at
+// the kernel's register count, each looping over row blocks, rather than one
+// work-group per block: dispatching a work-group per block cost verification
+// of the 70B-shaped batch about 1 us per call.
 template <int D>
 struct MqMerge {
   static constexpr int kPerThread = 8;             // output elements per thread
   static constexpr int kThreadsPerRow = D / kPerThread;
   static constexpr int kRowsPerBlock = 256 / kThreadsPerRow;
+  static constexpr int kGroupsPerCu = 4;           // resident at up to 128 VGPRs
 };
 
 template <class T, int D>
@@ -851,7 +855,7 @@ __global__ __launch_bounds__(256) void decode_multi_reduce_kernel(MultiArgs a) {
   typedef typename T::storage st;
   constexpr int QPR = MqMerge<D>::kThreadsPerRow;
   constexpr int RPB = MqMerge<D>::kRowsPerBlock;
-  const int bpv = (a.pass_rows + RPB - 1) / RPB;  // work-groups per (sequence, pass, head)
+  const int bpv = (a.pass_rows + RPB - 1) / RPB;  // row blocks per (sequence, pass, head)
 #ifdef PA_WAVE_TIMELINE
   const int64_t tl_cw = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   uint64_t *tl_rec = (a.timeline != nullptr && tl_cw < kTimelineCombineWaves)
@@ -859,91 +863,97 @@ __global__ __launch_bounds__(256) void decode_multi_reduce_kernel(MultiArgs a) {
                          : nullptr;
   if (tl_rec != nullptr && (threadIdx.x & 63) == 0) tl_rec[0] = tl_now();
 #endif
-  const int rb = blockIdx.x % bpv;
-  const int g = (blockIdx.x / bpv) % a.num_kv_heads;
-  const int bp = blockIdx.x / (bpv * a.num_kv_heads);  // b * passes + pass
-  const int b = bp / a.passes;
-  const int pass = bp - b * a.passes;
   const int PG = a.pass_group;
-  const int v = b * a.pgroups + pass / PG;
-  const int w = pass - (pass / PG) * PG;
   const int nv = a.num_seqs * a.pgroups;
   const int total = a.ws_sched[nv];
-  const int t0 = a.ws_sched[v], t1 = a.ws_sched[v + 1];
   const int groups = mq_active_groups(a, total);
   const RangeSplit rs = range_split(weighted_total(total, nv, a.seq_cost), groups, a.young_from, a.young_share);
-  const int64_t w0 = (int64_t)t0 + (int64_t)a.seq_cost * (v + 1);  // weighted position of tile 0
-  const int ga = t1 > t0 ? range_of(rs, w0) : 0, gb = t1 > t0 ? range_of(rs, w0 + (t1 - t0) - 1) : 0;
-  if (t1 > t0 && ga == gb) return;  // written by the main kernel
-  const int row0 = pass * a.pass_rows;
-  const int row_end = min(a.rows, row0 + a.pass_rows);
-  const int row = rb * RPB + (int)threadIdx.x / QPR;
-  const int q8 = (int)threadIdx.x % QPR;
-  if (row0 + row >= row_end) return;  // no barriers follow
-  float wsum = 0.f;
-  float acc[8];
+  // item blk: (sequence, pass, KV head, block of RPB rows); returns early when
+  // the main kernel wrote the rows (no barriers follow)
+  auto item = [&](int blk) {
+    const int rb = blk % bpv;
+    const int g = (blk / bpv) % a.num_kv_heads;
+    const int bp = blk / (bpv * a.num_kv_heads);  // b * passes + pass
+    const int b = bp / a.passes;
+    const int pass = bp - b * a.passes;
+    const int v = b * a.pgroups + pass / PG;
+    const int w = pass - (pass / PG) * PG;
+    const int t0 = a.ws_sched[v], t1 = a.ws_sched[v + 1];
+    const int64_t w0 = (int64_t)t0 + (int64_t)a.seq_cost * (v + 1);  // weighted position of tile 0
+    const int ga = t1 > t0 ? range_of(rs, w0) : 0, gb = t1 > t0 ? range_of(rs, w0 + (t1 - t0) - 1) : 0;
+    if (t1 > t0 && ga == gb) return;  // written by the main kernel
+    const int row0 = pass * a.pass_rows;
+    const int row_end = min(a.rows, row0 + a.pass_rows);
+    const int row = rb * RPB + (int)threadIdx.x / QPR;
+    const int q8 = (int)threadIdx.x % QPR;
+    if (row0 + row >= row_end) return;
+    float wsum = 0.f;
+    float acc[8];
 #pragma unroll
-  for (int e = 0; e < 8; ++e) acc[e] = 0.f;
-  if (t1 > t0) {
-    // Segments k = ga..gb in windows of kWin: every (m, l) pair and row of a
-    // window is requested before the first is used (one round trip per
-    // window, not one per segment); windows after the first rescale the
-    // running sums to the new maximum.
-    constexpr int kWin = 16;
-    const int64_t rstep = (int64_t)a.num_kv_heads * PG * a.pass_rows;  // rows between segments
-    const int64_t r0 = ((((int64_t)ga + v) * a.num_kv_heads + g) * PG + w) * a.pass_rows + row;
-    float m_max = -INFINITY;
-    for (int k0 = ga; k0 <= gb; k0 += kWin) {
-      const int cnt = min(kWin, gb - k0 + 1);
-      float mk[kWin], lk[kWin];
-      // rows stay raw (eight 16-bit values) until they are used, so that no
-      // conversion waits on a load before the window's other loads issue
-      uint4 okr[kWin];
+    for (int e = 0; e < 8; ++e) acc[e] = 0.f;
+    if (t1 > t0) {
+      // Segments k = ga..gb in windows of kWin: every (m, l) pair and row of a
+      // window is requested before the first is used (one round trip per
+      // window, not one per segment); windows after the first rescale the
+      // running sums to the new maximum.
+      constexpr int kWin = 16;
+      const int64_t rstep = (int64_t)a.num_kv_heads * PG * a.pass_rows;  // rows between segments
+      const int64_t r0 = ((((int64_t)ga + v) * a.num_kv_heads + g) * PG + w) * a.pass_rows + row;
+      float m_max = -INFINITY;
+      for (int k0 = ga; k0 <= gb; k0 += kWin) {
+        const int cnt = min(kWin, gb - k0 + 1);
+        float mk[kWin], lk[kWin];
+        // rows stay raw (eight 16-bit values) until they are used, so that no
+        // conversion waits on a load before the window's other loads issue
+        uint4 okr[kWin];
 #pragma unroll
-      for (int u = 0; u < kWin; ++u) {
-        if (u < cnt) {
-          const int64_t r = r0 + (int64_t)(k0 - ga + u) * rstep;
-          mk[u] = a.ws_ml[r * 2];
-          lk[u] = a.ws_ml[r * 2 + 1];
-          okr[u] = reinterpret_cast<const uint4 *>(reinterpret_cast<const st *>(a.ws_o) + r * D)[q8];
-        } else {
-          mk[u] = -INFINITY;
-          lk[u] = 0.f;
-          okr[u] = make_uint4(0u, 0u, 0u, 0u);
+        for (int u = 0; u < kWin; ++u) {
+          if (u < cnt) {
+            const int64_t r = r0 + (int64_t)(k0 - ga + u) * rstep;
+            mk[u] = a.ws_ml[r * 2];
+            lk[u] = a.ws_ml[r * 2 + 1];
+            okr[u] = reinterpret_cast<const uint4 *>(reinterpret_cast<const st *>(a.ws_o) + r * D)[q8];
+          } else {
+            mk[u] = -INFINITY;
+            lk[u] = 0.f;
+            okr[u] = make_uint4(0u, 0u, 0u, 0u);
+          }
         }
-      }
-      float m_new = m_max;
+        float m_new = m_max;
 #pragma unroll
-      for (int u = 0; u < kWin; ++u) m_new = fmaxf(m_new, mk[u]);
-      if (k0 > ga && m_new > m_max) {
-        const float f = fast_exp2(m_max - m_new);
-        wsum *= f;
+        for (int u = 0; u < kWin; ++u) m_new = fmaxf(m_new, mk[u]);
+        if (k0 > ga && m_new > m_max) {
+          const float f = fast_exp2(m_max - m_new);
+          wsum *= f;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) acc[e] *= f;
-      }
-      m_max = m_new;
+          for (int e = 0; e < 8; ++e) acc[e] *= f;
+        }
+        m_max = m_new;
 #pragma unroll
-      for (int u = 0; u < kWin; ++u) {
-        if (u < cnt) {
-          const float wk = lk[u] > 0.f ? lk[u] * fast_exp2(mk[u] - m_max) : 0.f;
-          wsum += wk;
+        for (int u = 0; u < kWin; ++u) {
+          if (u < cnt) {
+            const float wk = lk[u] > 0.f ? lk[u] * fast_exp2(mk[u] - m_max) : 0.f;
+            wsum += wk;
 #pragma unroll
-          for (int e = 0; e < 8; ++e) acc[e] += wk * T::to_float(half_of(okr[u], e));
+            for (int e = 0; e < 8; ++e) acc[e] += wk * T::to_float(half_of(okr[u], e));
+          }
         }
       }
     }
-  }
-  const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
-  const int rr = row0 + row;
-  const int i = rr / a.group, h = rr - (rr / a.group) * a.group;
-  st *out = static_cast<st *>(a.out) +
-            (((int64_t)b * a.q_len + i) * a.num_q_heads + (int64_t)g * a.group + h) * D + 8 * q8;
-  *reinterpret_cast<uint4 *>(out) =
-      make_uint4(T::pack_pair(acc[0] * inv, acc[1] * inv), T::pack_pair(acc[2] * inv, acc[3] * inv),
-                 T::pack_pair(acc[4] * inv, acc[5] * inv), T::pack_pair(acc[6] * inv, acc[7] * inv));
+    const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
+    const int rr = row0 + row;
+    const int i = rr / a.group, h = rr - (rr / a.group) * a.group;
+    st *out = static_cast<st *>(a.out) +
+              (((int64_t)b * a.q_len + i) * a.num_q_heads + (int64_t)g * a.group + h) * D + 8 * q8;
+    *reinterpret_cast<uint4 *>(out) =
+        make_uint4(T::pack_pair(acc[0] * inv, acc[1] * inv), T::pack_pair(acc[2] * inv, acc[3] * inv),
+                   T::pack_pair(acc[4] * inv, acc[5] * inv), T::pack_pair(acc[6] * inv, acc[7] * inv));
 #ifdef PA_WAVE_TIMELINE
-  if (tl_rec != nullptr && (threadIdx.x & 63) == 0) tl_rec[1] = tl_now() | (1ull << 63);
+    if (tl_rec != nullptr && (threadIdx.x & 63) == 0) tl_rec[1] = tl_now() | (1ull << 63);
 #endif
+  };
+  const int items = a.num_seqs * a.passes * a.num_kv_heads * bpv;
+  for (int blk = blockIdx.x; blk < items; blk += gridDim.x) item(blk);
 }
 
 template <class T, int D, int MT, int KVF, int W, bool RING>
@@ -964,8 +974,10 @@ hipError_t launch_mt(const MultiArgs &a, int grid, hipStream_t stream) {
   if (err != hipSuccess) return err;
   constexpr int rpb = MqMerge<D>::kRowsPerBlock;
   const int bpv = (a.pass_rows + rpb - 1) / rpb;
+  const int items = a.num_seqs * a.passes * a.num_kv_heads * bpv;
   hipLaunchKernelGGL((decode_multi_reduce_kernel<T, D>),
-                     dim3((unsigned)(a.num_seqs * a.passes * a.num_kv_heads * bpv)), dim3(256), 0, stream, a);
+                     dim3((unsigned)std::min(items, MqMerge<D>::kGroupsPerCu * multi_grid())), dim3(256), 0, stream,
+                     a);
   return hipGetLastError();
 }
 
