@@ -239,11 +239,13 @@ int multi_impl(pa_pool *pool, void *out, const void *query, const void *draft_k,
   // tiles (staging its query rows, writing its output or partial rows).
   // Measured: verification of the 70B-shaped batch 101.7 -> 93.5 us at 6
   // (4: 94.6, 12: 96.9), chunked prefill 211.6 -> 181.0 us, ring
-  // verification 36.1 -> 33.6 us; with the later kernels costs 5-8 are
-  // within noise for both, and E4M3 verification takes 63.6 us at 6
-  // against 65.9 at 8.
+  // verification 36.1 -> 33.6 us.  On the current kernels one wave per
+  // SIMD takes 5 (verification 88.4 us at 6, 87.2 at 5, 88.7 at 4; ring
+  // verification 0.2 us faster) and two waves per SIMD 6 (chunked prefill
+  // 165.8 us against 173.1 at 5; E4M3 verification 63.6 us against 65.9
+  // at 8).
   const int forced_cost = pa::option(PA_OPT_MULTI_SEQ_COST);
-  a.seq_cost = forced_cost >= 1 ? forced_cost - 1 : 6;
+  a.seq_cost = forced_cost >= 1 ? forced_cost - 1 : m.waves == 1 ? 5 : 6;
   a.block_shift = pa::log2_exact(pool->block_size);
   a.scale_log2 = scale * pa::kLog2eHost;
   if (ring != nullptr) {
